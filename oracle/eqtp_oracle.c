@@ -1,0 +1,428 @@
+/*
+ * eqtp_oracle.c -- plain fp64 CPU oracle for the equivariant message-passing
+ * convolution (spherical harmonics -> Clebsch-Gordan tensor product -> sum into
+ * the destination node), the per-l channel linear and the standalone
+ * spherical harmonics.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the CPU
+ * baseline leg of the benchmark may load this library.  It shares no code,
+ * header, table or generator with the HIP library: every constant here
+ * (Legendre recursion, Racah formula, complex->real change of basis, path
+ * enumeration) is computed from its textbook definition at run time.
+ *
+ * Everything is computed in double precision from the caller's float32
+ * inputs, in the plain loop order of the definition, with no blocking, fusion
+ * or reordering.
+ *
+ * Sources (the Batmobile page, "Batmobile CUDA kernel optimisation: a 10-20x
+ * acceleration strategy for equivariant graph neural networks"):
+ *   - section "equivariant GNN compute bottleneck": the core operation is real
+ *     spherical harmonics of the edge direction, a Clebsch-Gordan tensor
+ *     product with the source node's features, and message passing;
+ *   - section "2. register intermediate computation": real SH of the unit edge
+ *     vector; Y00 = 0.28209479177387814, Y10 = 0.4886025119029199*nz,
+ *     Y11c = -0.4886025119029199*nx, Y11s = -0.4886025119029199*ny, in that
+ *     declaration order (which fixes the Condon-Shortley phase and the
+ *     per-l component order l0, l1c, l1s, l2c, l2s, ...); higher orders "are
+ *     handled the same way";
+ *   - section "1. compile-time constants": Clebsch-Gordan coefficients indexed
+ *     by a path index (34 entries, i.e. every (l1,l2,l3<=3) triangle triple);
+ *   - section "3. operator fusion": edge vectors [E,3], node features
+ *     [N,C,16], source indices [E]; one message per edge.
+ * Readings where the page is silent (all stated in the design notes):
+ *   path weights are per path and per channel (channel-wise "uvu" product),
+ *   messages are summed into dst with no normalisation, a zero-length edge
+ *   vector gives Y = (Y00, 0, ..., 0), the radial basis is
+ *   sin(n pi r / r_c) / r times the p=6 polynomial envelope, the linear has
+ *   no bias, and odd (l1+l2+l3) real coefficients (purely imaginary in this
+ *   basis) are represented by their imaginary part.
+ */
+#include <complex.h>
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define OR_MAX_L 12
+
+/* ------------------------------------------------------------------------ */
+/* factorials                                                                */
+/* ------------------------------------------------------------------------ */
+static double fact(int n) {
+  double f = 1.0;
+  for (int i = 2; i <= n; ++i) f *= (double)i;
+  return f;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Real spherical harmonics                                                  */
+/* ------------------------------------------------------------------------ */
+
+/* Associated Legendre function P_l^m(z), m >= 0, including the
+ * Condon-Shortley phase (-1)^m, by the standard three-term recursion in l. */
+static double legendre_p(int l, int m, double z) {
+  double s = sqrt(fmax(0.0, 1.0 - z * z));
+  double pmm = 1.0; /* P_m^m = (-1)^m (2m-1)!! s^m */
+  for (int i = 1; i <= m; ++i) pmm *= -(double)(2 * i - 1) * s;
+  if (l == m) return pmm;
+  double pm1 = z * (double)(2 * m + 1) * pmm; /* P_{m+1}^m */
+  if (l == m + 1) return pm1;
+  double pl = 0.0;
+  for (int ll = m + 2; ll <= l; ++ll) {
+    pl = ((double)(2 * ll - 1) * z * pm1 - (double)(ll + m - 1) * pmm) / (double)(ll - m);
+    pmm = pm1;
+    pm1 = pl;
+  }
+  return pl;
+}
+
+/* Index of a real component inside the (lmax+1)^2 vector, in the page's
+ * declaration order: per l, first m=0, then (cos, sin) for m = 1..l. */
+static int comp_index(int l, int m, int is_sin) {
+  if (m == 0) return l * l;
+  return l * l + 2 * m - 1 + is_sin;
+}
+
+/* Y[(lmax+1)^2] of direction (x,y,z) (not necessarily unit).  Orthonormal on
+ * the sphere; Y_l0 = N P_l(cos t); Y_lm,c/s = sqrt2 N_lm P_l^m(cos t) cos/sin(m phi)
+ * with N_lm = sqrt((2l+1)/(4 pi) (l-m)!/(l+m)!). */
+static void real_sh(int lmax, double x, double y, double z, double* Y) {
+  double r = sqrt(x * x + y * y + z * z);
+  int K = (lmax + 1) * (lmax + 1);
+  for (int k = 0; k < K; ++k) Y[k] = 0.0;
+  Y[0] = sqrt(1.0 / (4.0 * M_PI));
+  if (r == 0.0) return; /* zero-length edge: only the l=0 component survives */
+  double ct = z / r;
+  if (ct > 1.0) ct = 1.0;
+  if (ct < -1.0) ct = -1.0;
+  double phi = atan2(y, x);
+  for (int l = 0; l <= lmax; ++l) {
+    for (int m = 0; m <= l; ++m) {
+      double n = sqrt((2.0 * l + 1.0) / (4.0 * M_PI) * fact(l - m) / fact(l + m));
+      double p = legendre_p(l, m, ct);
+      if (m == 0) {
+        Y[comp_index(l, 0, 0)] = n * p;
+      } else {
+        Y[comp_index(l, m, 0)] = sqrt(2.0) * n * p * cos((double)m * phi);
+        Y[comp_index(l, m, 1)] = sqrt(2.0) * n * p * sin((double)m * phi);
+      }
+    }
+  }
+}
+
+int oracle_sh_f64(int64_t E, const double* vec, int lmax, double* Y) {
+  if (lmax < 0 || lmax > OR_MAX_L || E < 0) return 1;
+  int K = (lmax + 1) * (lmax + 1);
+  for (int64_t e = 0; e < E; ++e) real_sh(lmax, vec[3 * e], vec[3 * e + 1], vec[3 * e + 2], Y + e * K);
+  return 0;
+}
+
+/* float32 inputs are widened exactly to double first. */
+static double* widen(const float* a, int64_t n) {
+  double* d = (double*)malloc(sizeof(double) * (n > 0 ? n : 1));
+  for (int64_t i = 0; i < n; ++i) d[i] = (double)a[i];
+  return d;
+}
+
+int oracle_sh(int64_t E, const float* vec, int lmax, double* Y) {
+  if (E < 0) return 1;
+  double* v = widen(vec, 3 * E);
+  int rc = oracle_sh_f64(E, v, lmax, Y);
+  free(v);
+  return rc;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Clebsch-Gordan coefficients                                               */
+/* ------------------------------------------------------------------------ */
+
+/* <l1 m1 l2 m2 | l3 m3> by the Racah formula (integer angular momenta). */
+double oracle_cg_complex(int l1, int m1, int l2, int m2, int l3, int m3) {
+  if (m3 != m1 + m2) return 0.0;
+  if (l3 < abs(l1 - l2) || l3 > l1 + l2) return 0.0;
+  if (abs(m1) > l1 || abs(m2) > l2 || abs(m3) > l3) return 0.0;
+  double pre = sqrt((2.0 * l3 + 1.0) * fact(l1 + l2 - l3) * fact(l1 - l2 + l3) * fact(-l1 + l2 + l3) /
+                    fact(l1 + l2 + l3 + 1));
+  pre *= sqrt(fact(l1 + m1) * fact(l1 - m1) * fact(l2 + m2) * fact(l2 - m2) * fact(l3 + m3) * fact(l3 - m3));
+  double sum = 0.0;
+  for (int k = 0; k <= l1 + l2 + l3; ++k) {
+    int a = l1 + l2 - l3 - k, b = l1 - m1 - k, c = l2 + m2 - k;
+    int d = l3 - l2 + m1 + k, e = l3 - l1 - m2 + k;
+    if (a < 0 || b < 0 || c < 0 || d < 0 || e < 0) continue;
+    double den = fact(k) * fact(a) * fact(b) * fact(c) * fact(d) * fact(e);
+    sum += ((k & 1) ? -1.0 : 1.0) / den;
+  }
+  return pre * sum;
+}
+
+/* Row mu (page order within l) of the unitary U_l that maps complex SH to
+ * real SH: Yreal_mu = sum_m U[mu][m] Y_l^m.  Fills u[2l+1] indexed by m+l. */
+static void u_row(int l, int mu, double complex* u) {
+  for (int i = 0; i < 2 * l + 1; ++i) u[i] = 0.0;
+  if (mu == 0) {
+    u[l] = 1.0;
+    return;
+  }
+  int m = (mu + 1) / 2;
+  int is_sin = (mu % 2 == 0);
+  double sgn = (m & 1) ? -1.0 : 1.0;
+  double h = 1.0 / sqrt(2.0);
+  if (!is_sin) {
+    u[l + m] = h;
+    u[l - m] = sgn * h;
+  } else {
+    u[l + m] = -I * h;
+    u[l - m] = I * sgn * h;
+  }
+}
+
+/* Real-basis coefficients C[mu1][mu2][mu3] for one (l1,l2,l3) triple, with
+ * mu in page order.  C = sum U_l3[mu3,m3] <l1m1 l2m2|l3m3> conj(U_l1[mu1,m1])
+ * conj(U_l2[mu2,m2]).  For even l1+l2+l3 the result is real; for odd it is
+ * purely imaginary and its imaginary part is returned.  Returns -1 if the
+ * triple is not allowed, else 0 (real) or 1 (imaginary part taken).  If
+ * max_discard is non-NULL it receives the largest magnitude of the discarded
+ * (should-be-zero) part. */
+int oracle_cg_real(int l1, int l2, int l3, double* out, double* max_discard) {
+  if (l1 < 0 || l2 < 0 || l3 < 0 || l1 > OR_MAX_L || l2 > OR_MAX_L || l3 > OR_MAX_L) return -1;
+  if (l3 < abs(l1 - l2) || l3 > l1 + l2) return -1;
+  int n1 = 2 * l1 + 1, n2 = 2 * l2 + 1, n3 = 2 * l3 + 1;
+  int odd = (l1 + l2 + l3) & 1;
+  double complex u1[2 * OR_MAX_L + 1], u2[2 * OR_MAX_L + 1], u3[2 * OR_MAX_L + 1];
+  double disc = 0.0;
+  for (int a = 0; a < n1; ++a) {
+    u_row(l1, a, u1);
+    for (int b = 0; b < n2; ++b) {
+      u_row(l2, b, u2);
+      for (int c = 0; c < n3; ++c) {
+        u_row(l3, c, u3);
+        double complex s = 0.0;
+        for (int m1 = -l1; m1 <= l1; ++m1)
+          for (int m2 = -l2; m2 <= l2; ++m2) {
+            int m3 = m1 + m2;
+            if (m3 < -l3 || m3 > l3) continue;
+            double cg = oracle_cg_complex(l1, m1, l2, m2, l3, m3);
+            s += u3[l3 + m3] * cg * conj(u1[l1 + m1]) * conj(u2[l2 + m2]);
+          }
+        double keep = odd ? cimag(s) : creal(s);
+        double drop = odd ? creal(s) : cimag(s);
+        if (fabs(drop) > disc) disc = fabs(drop);
+        out[(a * n2 + b) * n3 + c] = keep;
+      }
+    }
+  }
+  if (max_discard) *max_discard = disc;
+  return odd;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Path sets                                                                 */
+/* ------------------------------------------------------------------------ */
+
+/* Paths (l1 = feature l, l2 = SH l, l3 = output l), all <= lmax, triangle
+ * allowed; path_set 0 additionally requires l1+l2+l3 even (parity
+ * respecting).  Canonical order: lexicographic in (l1,l2,l3). Returns P. */
+int oracle_paths(int lmax, int path_set, int32_t* l1l2l3) {
+  if (lmax < 0 || lmax > OR_MAX_L || (path_set != 0 && path_set != 1)) return -1;
+  int P = 0;
+  for (int l1 = 0; l1 <= lmax; ++l1)
+    for (int l2 = 0; l2 <= lmax; ++l2)
+      for (int l3 = 0; l3 <= lmax; ++l3) {
+        if (l3 < abs(l1 - l2) || l3 > l1 + l2) continue;
+        if (path_set == 0 && ((l1 + l2 + l3) & 1)) continue;
+        if (l1l2l3) {
+          l1l2l3[3 * P] = l1;
+          l1l2l3[3 * P + 1] = l2;
+          l1l2l3[3 * P + 2] = l3;
+        }
+        ++P;
+      }
+  return P;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Radial weights                                                            */
+/* ------------------------------------------------------------------------ */
+
+/* Polynomial envelope with p = 6: u(d) = 1 - 28 d^6 + 48 d^7 - 21 d^8 for
+ * d < 1, else 0. */
+double oracle_envelope(double d) {
+  if (d >= 1.0) return 0.0;
+  double d6 = d * d * d * d * d * d;
+  return 1.0 - 28.0 * d6 + 48.0 * d6 * d - 21.0 * d6 * d * d;
+}
+
+/* Radial basis R_n(r) = sin(n pi r / r_c) / r * u(r / r_c), n = 1..n_basis;
+ * at r = 0 the limit n pi / r_c is used. */
+void oracle_radial_basis(double r, double r_cut, int n_basis, double* R) {
+  double u = oracle_envelope(r / r_cut);
+  for (int n = 1; n <= n_basis; ++n) {
+    double b = (r == 0.0) ? (double)n * M_PI / r_cut : sin((double)n * M_PI * r / r_cut) / r;
+    R[n - 1] = b * u;
+  }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Convolution                                                               */
+/* ------------------------------------------------------------------------ */
+
+/* out[n, c, l3 mu3] = sum_{e: dst_e = n} sum_{p=(l1,l2,l3)} w_e[p,c]
+ *                     sum_{mu1,mu2} C^p[mu1,mu2,mu3] x[src_e, c, l1 mu1] Y_{l2 mu2}(vec_e)
+ * weight_mode 0: w_e[p,c] = w[p*C + c]   (w is [P, C])
+ * weight_mode 1: w_e[p,c] = sum_n R_n(|vec_e|) w[n*P*C + p*C + c]   (w is [n_basis, P*C])
+ * x is [N, C, K] float32, out is [N, C, K] float64 and is overwritten.
+ * Edges are taken in the order given; dst need not be sorted.
+ * Returns 0 on success, nonzero on bad arguments. */
+int oracle_conv_f64(int64_t N, int64_t E, int lmax, int C, int path_set, int weight_mode, double r_cut,
+                    int n_basis, const double* vec, const int32_t* src, const int32_t* dst, const double* x,
+                    const double* w, double* out) {
+  if (lmax < 0 || lmax > OR_MAX_L || C <= 0 || N < 0 || E < 0) return 1;
+  if (weight_mode != 0 && weight_mode != 1) return 1;
+  if (weight_mode == 1 && (n_basis <= 0 || n_basis > 64 || !(r_cut > 0.0))) return 1;
+  int K = (lmax + 1) * (lmax + 1);
+  int P = oracle_paths(lmax, path_set, NULL);
+  if (P <= 0) return 1;
+  int32_t* paths = (int32_t*)malloc(sizeof(int32_t) * 3 * P);
+  oracle_paths(lmax, path_set, paths);
+  /* dense real CG block per path */
+  double** cg = (double**)malloc(sizeof(double*) * P);
+  for (int p = 0; p < P; ++p) {
+    int l1 = paths[3 * p], l2 = paths[3 * p + 1], l3 = paths[3 * p + 2];
+    cg[p] = (double*)malloc(sizeof(double) * (2 * l1 + 1) * (2 * l2 + 1) * (2 * l3 + 1));
+    oracle_cg_real(l1, l2, l3, cg[p], NULL);
+  }
+  for (int64_t i = 0; i < N * C * K; ++i) out[i] = 0.0;
+  double* Y = (double*)malloc(sizeof(double) * K);
+  double* we = (double*)malloc(sizeof(double) * P * C);
+  double R[64];
+  int rc = 0;
+  for (int64_t e = 0; e < E; ++e) {
+    int64_t s = src[e], d = dst[e];
+    if (s < 0 || s >= N || d < 0 || d >= N) {
+      rc = 2;
+      break;
+    }
+    double vx = vec[3 * e], vy = vec[3 * e + 1], vz = vec[3 * e + 2];
+    /* 1. spherical harmonics of the edge direction */
+    real_sh(lmax, vx, vy, vz, Y);
+    /* 2. per-edge path weights */
+    if (weight_mode == 0) {
+      for (int i = 0; i < P * C; ++i) we[i] = w[i];
+    } else {
+      double r = sqrt(vx * vx + vy * vy + vz * vz);
+      oracle_radial_basis(r, r_cut, n_basis, R);
+      for (int i = 0; i < P * C; ++i) {
+        double acc = 0.0;
+        for (int n = 0; n < n_basis; ++n) acc += R[n] * w[(int64_t)n * P * C + i];
+        we[i] = acc;
+      }
+    }
+    /* 3. tensor product with the source features, summed into dst */
+    for (int p = 0; p < P; ++p) {
+      int l1 = paths[3 * p], l2 = paths[3 * p + 1], l3 = paths[3 * p + 2];
+      int n1 = 2 * l1 + 1, n2 = 2 * l2 + 1, n3 = 2 * l3 + 1;
+      for (int a = 0; a < n1; ++a)
+        for (int b = 0; b < n2; ++b)
+          for (int c3 = 0; c3 < n3; ++c3) {
+            double coef = cg[p][(a * n2 + b) * n3 + c3];
+            if (coef == 0.0) continue;
+            double cy = coef * Y[l2 * l2 + b];
+            for (int ch = 0; ch < C; ++ch) {
+              double xv = x[(s * C + ch) * K + l1 * l1 + a];
+              out[(d * C + ch) * K + l3 * l3 + c3] += we[p * C + ch] * cy * xv;
+            }
+          }
+    }
+  }
+  free(Y);
+  free(we);
+  for (int p = 0; p < P; ++p) free(cg[p]);
+  free(cg);
+  free(paths);
+  return rc;
+}
+
+/* float32 entry point: inputs widened exactly to double, then the f64 core. */
+int oracle_conv(int64_t N, int64_t E, int lmax, int C, int path_set, int weight_mode, double r_cut,
+                int n_basis, const float* vec, const int32_t* src, const int32_t* dst, const float* x,
+                const float* w, double* out) {
+  if (lmax < 0 || lmax > OR_MAX_L || C <= 0 || N < 0 || E < 0) return 1;
+  int K = (lmax + 1) * (lmax + 1);
+  int P = oracle_paths(lmax, path_set, NULL);
+  if (P <= 0) return 1;
+  int64_t nw = (weight_mode == 1) ? (int64_t)n_basis * P * C : (int64_t)P * C;
+  if (weight_mode == 1 && (n_basis <= 0 || n_basis > 64)) return 1;
+  double* v = widen(vec, 3 * E);
+  double* xx = widen(x, N * C * K);
+  double* ww = widen(w, nw);
+  int rc = oracle_conv_f64(N, E, lmax, C, path_set, weight_mode, r_cut, n_basis, v, src, dst, xx, ww, out);
+  free(v);
+  free(xx);
+  free(ww);
+  return rc;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Per-l channel linear                                                      */
+/* ------------------------------------------------------------------------ */
+
+/* Round a float32 to the nearest bfloat16 (ties to even) and return it as a
+ * float32 value.  NaN is kept as a quiet NaN. */
+static float round_bf16(float f) {
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) {
+    u |= 0x00400000u;
+    u &= 0xffff0000u;
+  } else {
+    uint32_t lsb = (u >> 16) & 1u;
+    u += 0x7fffu + lsb;
+    u &= 0xffff0000u;
+  }
+  float r;
+  memcpy(&r, &u, 4);
+  return r;
+}
+
+float oracle_round_bf16(float f) { return round_bf16(f); }
+
+/* out[n, c', l mu] = sum_c W[l, c', c] h[n, c, l mu] in double precision. */
+int oracle_linear_f64(int64_t N, int C, int lmax, const double* h, const double* W, double* out) {
+  if (lmax < 0 || lmax > OR_MAX_L || C <= 0 || N < 0) return 1;
+  int K = (lmax + 1) * (lmax + 1);
+  for (int64_t n = 0; n < N; ++n)
+    for (int l = 0; l <= lmax; ++l)
+      for (int mu = l * l; mu < (l + 1) * (l + 1); ++mu)
+        for (int co = 0; co < C; ++co) {
+          double acc = 0.0;
+          for (int ci = 0; ci < C; ++ci) acc += W[((int64_t)l * C + co) * C + ci] * h[(n * C + ci) * K + mu];
+          out[(n * C + co) * K + mu] = acc;
+        }
+  return 0;
+}
+
+/* out[n, c', l mu] = sum_c W[l, c', c] h[n, c, l mu], W is [lmax+1, C, C]
+ * (output channel major).  If bf16 != 0 both h and W are first rounded to
+ * bfloat16 (round to nearest even), as the bf16 matrix-core mode consumes
+ * them; products and sums are then exact/fp64 here. */
+int oracle_linear(int64_t N, int C, int lmax, int bf16, const float* h, const float* W, double* out) {
+  if (lmax < 0 || lmax > OR_MAX_L || C <= 0 || N < 0) return 1;
+  int K = (lmax + 1) * (lmax + 1);
+  for (int64_t n = 0; n < N; ++n)
+    for (int l = 0; l <= lmax; ++l)
+      for (int mu = l * l; mu < (l + 1) * (l + 1); ++mu)
+        for (int co = 0; co < C; ++co) {
+          double acc = 0.0;
+          for (int ci = 0; ci < C; ++ci) {
+            float wv = W[((int64_t)l * C + co) * C + ci];
+            float hv = h[(n * C + ci) * K + mu];
+            if (bf16) {
+              wv = round_bf16(wv);
+              hv = round_bf16(hv);
+            }
+            acc += (double)wv * (double)hv;
+          }
+          out[(n * C + co) * K + mu] = acc;
+        }
+  return 0;
+}
