@@ -1,0 +1,220 @@
+#!/usr/bin/env python3
+"""Throughput of the fused equivariant convolution on one MI355X.
+
+One step = the whole hot path over one batch of the workload: the fused
+spherical harmonics -> Clebsch-Gordan product -> destination sum
+(eqtp_conv_fused), then the per-l channel linear (eqtp_linear).  The default
+workload is "mid": 10,000 atoms in a periodic box at 0.1 atoms/A^3, radius
+cut-off 4 A (266,116 directed edges), lmax 3, C = 64, parity path set (23
+paths, 353 coefficients), bf16-operand 64x64 linear.  Inputs are synthetic
+(seeded) and resident in device memory before timing starts.
+
+Prints one JSON line (see the "metric" field); diagnostics go to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+PEAK_FP32_TFLOPS = 157.3       # MI355X fp32 (matrix and packed vector)
+METRIC = "edges/sec fused SH+CG-TP+aggregate (10k atoms, C=64, L=3); % of roofline"
+
+WORKLOAD_TEXT = {
+    "typical": "typical: 1000 atoms, periodic 0.1/A^3, k=20 nearest, L=3, C=32, conv + fp32 32x32 per-l linear",
+    "mid": "mid: 10k atoms, periodic 0.1/A^3, r_c=4 A, L=3, C=64, conv + bf16 64x64 per-l linear",
+    "large": "large: 100k atoms, periodic 0.1/A^3, r_c=5 A, L=3, C=32, conv (dst-sorted)",
+    "radial": "radial: 50k atoms, periodic 0.1/A^3, r_c=5 A, L=3, C=128, radial-weighted conv",
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def count_terms(lmax, path_set):
+    """Non-zero coupling coefficients (2*nnz*C flops per edge) from the library's table."""
+    import re
+
+    inc = os.path.join(ROOT, "spherical_harmonic_cg_amd", "csrc", "generated", "cg_tables.inc")
+    tag = "L%d_%s" % (lmax, "parity" if path_set == 0 else "so3")
+    m = re.search(r"constexpr int kNumTerms_%s = (\d+);" % tag, open(inc).read())
+    return int(m.group(1))
+
+
+def cpu_baseline(wl, budget_s):
+    """The fp64 oracle on the same workload, on the host (it is single-threaded).
+
+    Bounded sample: a first run over 200 destination rows sizes the sample so
+    that the timed run takes about ``budget_s`` seconds (the whole workload if
+    it fits)."""
+    import oracle
+
+    def run(rows):
+        e = int(wl.row_ptr[rows])
+        t = time.perf_counter()
+        h = oracle.conv(wl.N, wl.vec[:e], wl.src[:e], wl.dst[:e], wl.x, wl.weights, wl.lmax,
+                        path_set=wl.path_set, weight_mode=wl.weight_mode, r_cut=wl.r_cut)
+        if wl.w_lin is not None:
+            oracle.linear(h[:rows].astype(np.float32), wl.w_lin, wl.lmax, bf16=wl.linear_bf16)
+        return time.perf_counter() - t, e
+
+    probe_rows = min(wl.N, 200)
+    dt, e = run(probe_rows)
+    per_edge = dt / max(e, 1)
+    rows = wl.N
+    if per_edge * wl.E > budget_s:
+        rows = int(np.searchsorted(wl.row_ptr, budget_s / per_edge))
+        rows = max(probe_rows, min(rows, wl.N))
+    dt, e = run(rows)
+    return {"value": round(e / dt, 1), "unit": "edges/s", "cores": 1, "kind": "oracle",
+            "sample": "fp64 oracle, one thread, on the first %d of %d destination rows (%d of %d edges) of the "
+                      "same workload: conv%s, %.1f s" % (rows, wl.N, e, wl.E,
+                                                         " + per-l linear" if wl.w_lin is not None else "", dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="mid", choices=sorted(WORKLOAD_TEXT))
+    ap.add_argument("--algo", type=int, default=0, help="0 auto, 1 node/matrix cores, 2 edge/vector ALUs")
+    ap.add_argument("--unsorted", action="store_true", help="random edge order (atomic path)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget-s", type=float, default=15.0)
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="after timing, run one 256 MiB device copy (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path (a split into CSR "
+              "row ranges with a halo exchange of source features is not built); run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import spherical_harmonic_cg_amd as eq
+    from spherical_harmonic_cg_amd import synth
+
+    if not torch.cuda.is_available():
+        log("no GPU visible")
+        sys.exit(1)
+    eq.load_library()
+    torch.cuda.set_device(0)
+
+    t_gen = time.perf_counter()
+    wl = synth.make_config(args.config)
+    log("workload %s: N=%d E=%d C=%d lmax=%d P=%d (generated in %.1fs)" % (wl.name, wl.N, wl.E, wl.C, wl.lmax,
+                                                                            wl.P, time.perf_counter() - t_gen))
+    dev = torch.device("cuda:0")
+    T = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    if args.unsorted:
+        pvec, psrc, pdst = synth.random_permutation(wl)
+        vec, src, dst, row_ptr = T(pvec), T(psrc), T(pdst), None
+    else:
+        vec, src, dst, row_ptr = T(wl.vec), T(wl.src), None, T(wl.row_ptr)
+    x = T(wl.x)
+    w = T(wl.weights)
+    out = torch.empty_like(x)
+    w_lin = T(wl.w_lin) if wl.w_lin is not None else None
+    out2 = torch.empty_like(x) if w_lin is not None else None
+    lin_dtype = eq.EQTP_BF16 if wl.linear_bf16 else eq.EQTP_F32
+    stream = torch.cuda.current_stream()
+
+    def conv():
+        eq.eqtp_conv_fused(vec, src, x, w, wl.lmax, row_ptr=row_ptr, dst=dst, path_set=wl.path_set,
+                           weight_mode=wl.weight_mode, r_cut=wl.r_cut, algo=args.algo, out=out)
+
+    def linear():
+        if w_lin is not None:
+            eq.eqtp_linear(out, w_lin, wl.lmax, lin_dtype, out=out2)
+
+    for _ in range(args.warmup):
+        conv()
+        linear()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(K):
+        ev[i][0].record(stream)
+        conv()
+        ev[i][1].record(stream)
+        linear()
+        ev[i][2].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_start.elapsed_time(t_end)
+    conv_ms = np.array([a.elapsed_time(b) for a, b, _ in ev])
+    lin_ms = np.array([b.elapsed_time(c) for _, b, c in ev])
+    ms_per_step = total_ms / K
+    log("timed %d steps: %.4f ms/step (events), wall %.4f ms/step; conv avg %.4f ms (p10 %.4f p90 %.4f), "
+        "linear avg %.4f ms" % (K, ms_per_step, 1e3 * wall / K, conv_ms.mean(), np.percentile(conv_ms, 10),
+                                np.percentile(conv_ms, 90), lin_ms.mean()))
+
+    if args.calib_copy:
+        a = torch.empty(64 << 20, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        a.fill_(1.0)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        log("calibration copy: 256 MiB read + 256 MiB written")
+
+    edges_per_s = wl.E / (ms_per_step * 1e-3)
+    nnz = count_terms(wl.lmax, wl.path_set)
+    flop_edge = 2 * nnz * wl.C + (2 * 8 * wl.P * wl.C if wl.weight_mode == 1 else 0)
+    conv_s = float(conv_ms.mean()) * 1e-3
+    achieved_tflops = flop_edge * wl.E / conv_s / 1e12
+    roofline = {"bound": "mfma", "achieved": round(achieved_tflops, 3), "peak": PEAK_FP32_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved_tflops / PEAK_FP32_TFLOPS, 4), "traffic": None}
+    alg_bytes = 2 * wl.N * wl.C * wl.K * 4 + wl.E * 16 + (wl.N + 1) * 4 + wl.weights.size * 4
+    log("conv: %.3e counted flop (2*nnz*C per edge), %.1f MB algorithmic bytes -> %.1f GB/s" % (
+        flop_edge * wl.E, alg_bytes / 1e6, alg_bytes / conv_s / 1e9))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, args.cpu_budget_s)
+        log("cpu baseline: %.1f edges/s (%s)" % (cpu["value"], cpu["sample"]))
+
+    rec = {
+        "metric": METRIC,
+        "value": round(edges_per_s, 1),
+        "unit": "edges/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD_TEXT[args.config] + (" (random edge order)" if args.unsorted else ""),
+                   "atoms": wl.N, "edges": wl.E, "channels": wl.C, "lmax": wl.lmax, "paths": wl.P,
+                   "coupling_nnz": nnz, "algo": args.algo},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,173 @@
+/*
+ * eqtp.h -- C ABI of the MI355X (gfx950) equivariant convolution library.
+ *
+ * The library computes, on one GPU, the hot path of an equivariant
+ * message-passing convolution as the Batmobile page describes it ("Batmobile
+ * CUDA kernel optimisation: a 10-20x acceleration strategy for equivariant
+ * graph neural networks"):
+ *   section "equivariant GNN compute bottleneck" -- real spherical harmonics
+ *     of each edge direction, a Clebsch-Gordan tensor product with the source
+ *     node's features, and message passing into the destination node;
+ *   section "2. register intermediate computation" -- the harmonics for
+ *     l <= 3 of the normalised edge vector, components per l in the order
+ *     l0, l1c, l1s, l2c, l2s, ... (Y00, Y10, Y11c, Y11s first);
+ *   section "1. compile-time constants" -- coupling coefficients compiled
+ *     into the kernels, indexed by path;
+ *   section "3. operator fusion" -- edge vectors [E,3], node features
+ *     [N,C,16], source indices [E]; every edge vector read once.
+ *
+ * Conventions shared by every entry point
+ *   - All pointers not marked "host" are device pointers allocated and owned
+ *     by the caller.  The library allocates no device memory, performs no
+ *     host<->device copies and never synchronises.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Work is enqueued on it and the call returns immediately.
+ *   - Return value: EQTP_OK (0) or an error code.  Argument errors are
+ *     detected on the host before anything is launched (no partial writes).
+ *     A failed launch returns EQTP_EHIP.  Device faults surface at the
+ *     caller's next synchronisation.
+ *   - Functions are thread-safe; the library keeps no mutable state.
+ *   - Feature vectors use layout [N, C, K] with K = (lmax+1)^2: each
+ *     channel's K components are contiguous, in the component order above.
+ *   - Indices (src, dst, row_ptr) are int32.  Out-of-range index values are
+ *     clamped inside the kernels so that no access leaves the buffers; the
+ *     result for such inputs is unspecified.
+ */
+#ifndef EQTP_H
+#define EQTP_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define EQTP_OK 0
+#define EQTP_EINVAL 1       /* bad argument (null pointer, size, alignment, enum) */
+#define EQTP_EUNSUPPORTED 2 /* valid request this build does not implement */
+#define EQTP_EHIP 3         /* the HIP runtime reported an error at launch */
+
+/* coupling path sets (paths are (l1 = feature l, l2 = harmonic l, l3 = output l)) */
+#define EQTP_PATHS_PARITY 0 /* l1+l2+l3 even: 23 paths at lmax 3, 11 at lmax 2 */
+#define EQTP_PATHS_SO3 1    /* every triangle-allowed triple: 34 at lmax 3, 15 at lmax 2 */
+
+/* how the per-path, per-channel weights are given */
+#define EQTP_W_FIXED 0  /* weights fp32 [P, C], shared by every edge */
+#define EQTP_W_RADIAL 1 /* weights fp32 [n_basis, P*C]; per edge w_e[p,c] = sum_n R_n(r_e) W[n, p*C+c] */
+
+/* edge order */
+#define EQTP_EDGES_DST_SORTED 0 /* edges grouped by dst; row_ptr[N+1] gives each node's range */
+#define EQTP_EDGES_UNSORTED 1   /* any order; dst[E] given; results summed with atomics */
+
+/* algorithm for sorted edges with fixed weights (others always use the edge kernel) */
+#define EQTP_ALGO_AUTO 0
+#define EQTP_ALGO_NODE_MFMA 1 /* per node: outer-product sums on matrix cores, then the coupling */
+#define EQTP_ALGO_EDGE_VALU 2 /* per edge: harmonics, coupling and product on the vector ALUs */
+
+/* operand precision of the channel linear */
+#define EQTP_F32 0
+#define EQTP_BF16 1
+
+/*
+ * Number of coupling paths P for (lmax, path_set), or a negative status.
+ * lmax in [0, 3].
+ */
+int eqtp_num_paths(int lmax, int path_set);
+
+/*
+ * Writes the path list in canonical order (lexicographic in (l1, l2, l3)) to
+ * the host array l1l2l3 [P, 3].  Returns P or a negative status.  The weight
+ * rows of eqtp_conv_fused follow this order.
+ */
+int eqtp_path_table(int lmax, int path_set, int32_t* l1l2l3 /* host */);
+
+/*
+ * Real spherical harmonics of edge vectors (Batmobile page, section
+ * "2. register intermediate computation").
+ *   vec [E, 3] fp32, any length; a zero vector gives (Y00, 0, ..., 0).
+ *   Y   [E, (lmax+1)^2] fp32 output, 16-byte aligned; fully overwritten.
+ *   lmax in [0, 3]; 0 <= E < 2^31.
+ * Orthonormal harmonics with the Condon-Shortley phase:
+ *   Y00 = 0.28209479177387814, Y10 = 0.4886025119029199 z,
+ *   Y11c = -0.4886025119029199 x, Y11s = -0.4886025119029199 y (unit vector),
+ *   Y_lm,c / Y_lm,s = sqrt2 Re / Im of the complex harmonic.
+ */
+int eqtp_sh(const float* vec, int64_t E, int lmax, float* Y, void* stream);
+
+typedef struct eqtp_conv_desc {
+  int32_t struct_size; /* = sizeof(eqtp_conv_desc) */
+  int32_t lmax;        /* 0..3 */
+  int32_t C;           /* channels: 8, 16, 32, 64 or 128 */
+  int32_t path_set;    /* EQTP_PATHS_* */
+  int32_t weight_mode; /* EQTP_W_* */
+  int32_t edge_order;  /* EQTP_EDGES_* */
+  int32_t algo;        /* EQTP_ALGO_* */
+  float r_cut;         /* radial mode: cut-off radius (> 0) */
+  int32_t n_basis;     /* radial mode: number of radial functions, must be 8 */
+} eqtp_conv_desc;
+
+/*
+ * Fused convolution: spherical harmonics -> coupling with the source
+ * features -> sum into the destination node (Batmobile page, sections
+ * "2." and "3."):
+ *   out[n, c, l3 m3] = sum_{e : dst_e = n} sum_{p = (l1,l2,l3)} w_e[p, c]
+ *                      sum_{m1, m2} C^p[m1, m2, m3] x[src_e, c, l1 m1] Y_{l2 m2}(vec_e)
+ * with real-basis coupling coefficients C^p (odd l1+l2+l3 paths of the SO3
+ * set use the imaginary part of the purely imaginary real-basis block).
+ *   d        host descriptor (read during the call only).
+ *   N, E     nodes and edges, 0 <= N, E < 2^31 (E > 0 requires N > 0).
+ *   vec      [E, 3] fp32 edge vectors.
+ *   src      [E] int32 source node of each edge.
+ *   dst      [E] int32 destination node; required for EQTP_EDGES_UNSORTED,
+ *            ignored (may be NULL) for EQTP_EDGES_DST_SORTED.
+ *   row_ptr  [N+1] int32 CSR row pointers over dst-sorted edges
+ *            (row_ptr[0] = 0, row_ptr[N] = E, non-decreasing); required for
+ *            EQTP_EDGES_DST_SORTED, ignored for EQTP_EDGES_UNSORTED.
+ *   x        [N, C, K] fp32 node features, 16-byte aligned.
+ *   weights  EQTP_W_FIXED: [P, C] fp32; EQTP_W_RADIAL: [8, P*C] fp32 with
+ *            R_n(r) = sin(n pi r / r_cut) / r * u(r / r_cut), n = 1..8,
+ *            u(d) = 1 - 28 d^6 + 48 d^7 - 21 d^8 for d < 1, else 0
+ *            (limit n pi / r_cut at r = 0).
+ *   out      [N, C, K] fp32, 16-byte aligned, fully overwritten (nodes with
+ *            no incoming edge get zeros); must not alias any input.
+ * Sorted edges: deterministic (bit-identical from run to run).  Unsorted
+ * edges: summation order varies from run to run.
+ */
+int eqtp_conv_fused(const eqtp_conv_desc* d, int64_t N, int64_t E, const float* vec, const int32_t* src,
+                    const int32_t* dst, const int32_t* row_ptr, const float* x, const float* weights, float* out,
+                    void* stream);
+
+/*
+ * Per-l channel linear (channel mixing inside each irrep, no bias):
+ *   out[n, c', l m] = sum_c W[l, c', c] h[n, c, l m]
+ *   h    [N, C, K] fp32, 16-byte aligned.
+ *   W    [lmax+1, C, C] fp32 (output-channel major), 16-byte aligned.
+ *   out  [N, C, K] fp32, 16-byte aligned, fully overwritten; no aliasing.
+ *   dtype EQTP_F32: fp32 matrix-core products; EQTP_BF16: h and W are
+ *   rounded to bfloat16 (nearest even) on load and the products are
+ *   accumulated in fp32 on the bf16 matrix cores.
+ *   C in {8, 16, 32, 64, 128}, lmax in [0, 3], 0 <= N < 2^31.
+ */
+int eqtp_linear(int64_t N, int C, int lmax, int dtype, const float* h, const float* W, float* out, void* stream);
+
+/* Static description of a status code (never NULL). */
+const char* eqtp_status_string(int status);
+
+/*
+ * Test-only: walks the dst-sorted edges with exactly the row -> wave ->
+ * lane -> step schedule that eqtp_conv_fused uses for the given (C, lmax,
+ * algo) and, instead of the tensor product, counts the edges each node
+ * receives and sums their src indices:
+ *   count   [N] int32 output, src_sum [N] int64 output (fully overwritten).
+ * algo: EQTP_ALGO_NODE_MFMA or EQTP_ALGO_EDGE_VALU.  Other arguments as in
+ * eqtp_conv_fused.
+ */
+int eqtp_test_segment_probe(const int32_t* row_ptr, const int32_t* src, int64_t N, int64_t E, int C, int lmax,
+                            int algo, int32_t* count, int64_t* src_sum, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EQTP_H */

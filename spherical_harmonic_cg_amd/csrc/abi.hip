@@ -1,0 +1,156 @@
+// abi.hip -- the extern "C" entry points declared in include/eqtp.h:
+// argument validation, kernel selection and launch on the caller's stream.
+#include <stdint.h>
+
+#include "../../include/eqtp.h"
+#include "eqtp_device.hpp"
+#include "eqtp_kernels.hpp"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+bool valid_c(int C) { return C == 8 || C == 16 || C == 32 || C == 64 || C == 128; }
+constexpr int64_t kMaxIndex = (int64_t(1) << 31) - 1;
+
+int num_paths_host(int lmax, int path_set) {
+  static const int parity[4] = {eqtp_gen::kNumPaths_L0_parity, eqtp_gen::kNumPaths_L1_parity,
+                                eqtp_gen::kNumPaths_L2_parity, eqtp_gen::kNumPaths_L3_parity};
+  static const int so3[4] = {eqtp_gen::kNumPaths_L0_so3, eqtp_gen::kNumPaths_L1_so3, eqtp_gen::kNumPaths_L2_so3,
+                             eqtp_gen::kNumPaths_L3_so3};
+  if (lmax < 0 || lmax > 3) return -EQTP_EUNSUPPORTED;
+  if (path_set == EQTP_PATHS_PARITY) return parity[lmax];
+  if (path_set == EQTP_PATHS_SO3) return so3[lmax];
+  return -EQTP_EINVAL;
+}
+
+const eqtp_gen::PathLs* path_list(int lmax, int path_set) {
+  static const eqtp_gen::PathLs* parity[4] = {eqtp_gen::kPaths_L0_parity, eqtp_gen::kPaths_L1_parity,
+                                              eqtp_gen::kPaths_L2_parity, eqtp_gen::kPaths_L3_parity};
+  static const eqtp_gen::PathLs* so3[4] = {eqtp_gen::kPaths_L0_so3, eqtp_gen::kPaths_L1_so3,
+                                           eqtp_gen::kPaths_L2_so3, eqtp_gen::kPaths_L3_so3};
+  return path_set == EQTP_PATHS_PARITY ? parity[lmax] : so3[lmax];
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? EQTP_OK : EQTP_EHIP; }
+
+}  // namespace
+
+extern "C" {
+
+int eqtp_num_paths(int lmax, int path_set) { return num_paths_host(lmax, path_set); }
+
+int eqtp_path_table(int lmax, int path_set, int32_t* l1l2l3) {
+  const int P = num_paths_host(lmax, path_set);
+  if (P < 0) return P;
+  if (!l1l2l3) return -EQTP_EINVAL;
+  const eqtp_gen::PathLs* pl = path_list(lmax, path_set);
+  for (int p = 0; p < P; ++p) {
+    l1l2l3[3 * p] = pl[p].l1;
+    l1l2l3[3 * p + 1] = pl[p].l2;
+    l1l2l3[3 * p + 2] = pl[p].l3;
+  }
+  return P;
+}
+
+int eqtp_sh(const float* vec, int64_t E, int lmax, float* Y, void* stream) {
+  if (lmax < 0 || lmax > 3) return lmax < 0 ? EQTP_EINVAL : EQTP_EUNSUPPORTED;
+  if (E < 0 || E > kMaxIndex) return EQTP_EINVAL;
+  if (E == 0) return EQTP_OK;
+  if (!vec || !Y || !aligned4(vec) || !aligned16(Y)) return EQTP_EINVAL;
+  return status_of(eqtp::launch_sh(vec, E, lmax, Y, (hipStream_t)stream));
+}
+
+int eqtp_conv_fused(const eqtp_conv_desc* d, int64_t N, int64_t E, const float* vec, const int32_t* src,
+                    const int32_t* dst, const int32_t* row_ptr, const float* x, const float* weights, float* out,
+                    void* stream) {
+  if (!d || d->struct_size != (int32_t)sizeof(eqtp_conv_desc)) return EQTP_EINVAL;
+  if (d->lmax < 0) return EQTP_EINVAL;
+  if (d->lmax > 3) return EQTP_EUNSUPPORTED;
+  if (d->path_set != EQTP_PATHS_PARITY && d->path_set != EQTP_PATHS_SO3) return EQTP_EINVAL;
+  if (d->weight_mode != EQTP_W_FIXED && d->weight_mode != EQTP_W_RADIAL) return EQTP_EINVAL;
+  if (d->edge_order != EQTP_EDGES_DST_SORTED && d->edge_order != EQTP_EDGES_UNSORTED) return EQTP_EINVAL;
+  if (d->algo != EQTP_ALGO_AUTO && d->algo != EQTP_ALGO_NODE_MFMA && d->algo != EQTP_ALGO_EDGE_VALU)
+    return EQTP_EINVAL;
+  if (d->C <= 0) return EQTP_EINVAL;
+  if (!valid_c(d->C)) return EQTP_EUNSUPPORTED;
+  if (d->weight_mode == EQTP_W_RADIAL) {
+    if (!(d->r_cut > 0.0f)) return EQTP_EINVAL;
+    if (d->n_basis != 8) return EQTP_EUNSUPPORTED;
+  }
+  if (N < 0 || E < 0 || N > kMaxIndex || E > kMaxIndex) return EQTP_EINVAL;
+  if (E > 0 && N == 0) return EQTP_EINVAL;
+  // the node-factored algorithm needs per-node sums of edge-independent weights
+  const bool node_ok = d->edge_order == EQTP_EDGES_DST_SORTED && d->weight_mode == EQTP_W_FIXED;
+  if (d->algo == EQTP_ALGO_NODE_MFMA && !node_ok) return EQTP_EUNSUPPORTED;
+  if (N == 0) return EQTP_OK;
+  if (!x || !out || !weights || !aligned16(x) || !aligned16(out) || !aligned4(weights)) return EQTP_EINVAL;
+  if (E > 0) {
+    if (!vec || !src || !aligned4(vec) || !aligned4(src)) return EQTP_EINVAL;
+  }
+  if (d->edge_order == EQTP_EDGES_DST_SORTED) {
+    if (!row_ptr || !aligned4(row_ptr)) return EQTP_EINVAL;
+  } else if (E > 0) {
+    if (!dst || !aligned4(dst)) return EQTP_EINVAL;
+  }
+  eqtp::ConvArgs a;
+  a.N = N;
+  a.E = E;
+  a.lmax = d->lmax;
+  a.C = d->C;
+  a.path_set = d->path_set;
+  a.weight_mode = d->weight_mode;
+  a.edge_order = d->edge_order;
+  a.r_cut = d->r_cut;
+  a.vec = vec;
+  a.src = src;
+  a.dst = dst;
+  a.row_ptr = row_ptr;
+  a.x = x;
+  a.w = weights;
+  a.out = out;
+  a.stream = (hipStream_t)stream;
+  const bool use_node = node_ok && d->algo != EQTP_ALGO_EDGE_VALU;
+  return status_of(use_node ? eqtp::launch_conv_node(a) : eqtp::launch_conv_edge(a));
+}
+
+int eqtp_linear(int64_t N, int C, int lmax, int dtype, const float* h, const float* W, float* out, void* stream) {
+  if (lmax < 0 || C <= 0 || N < 0 || N > kMaxIndex) return EQTP_EINVAL;
+  if (lmax > 3 || !valid_c(C)) return EQTP_EUNSUPPORTED;
+  if (dtype != EQTP_F32 && dtype != EQTP_BF16) return EQTP_EINVAL;
+  if (N == 0) return EQTP_OK;
+  if (!h || !W || !out || !aligned16(h) || !aligned16(W) || !aligned16(out)) return EQTP_EINVAL;
+  return status_of(eqtp::launch_linear(N, C, lmax, dtype == EQTP_BF16, h, W, out, (hipStream_t)stream));
+}
+
+const char* eqtp_status_string(int status) {
+  switch (status) {
+    case EQTP_OK: return "EQTP_OK: success";
+    case EQTP_EINVAL: return "EQTP_EINVAL: invalid argument";
+    case EQTP_EUNSUPPORTED: return "EQTP_EUNSUPPORTED: request not supported by this build";
+    case EQTP_EHIP: return "EQTP_EHIP: HIP runtime error at launch";
+    default: return "unknown status";
+  }
+}
+
+int eqtp_test_segment_probe(const int32_t* row_ptr, const int32_t* src, int64_t N, int64_t E, int C, int lmax,
+                            int algo, int32_t* count, int64_t* src_sum, void* stream) {
+  if (N < 0 || E < 0 || N > kMaxIndex || E > kMaxIndex || (E > 0 && N == 0)) return EQTP_EINVAL;
+  if (lmax < 0 || lmax > 3 || !valid_c(C)) return EQTP_EUNSUPPORTED;
+  if (algo != EQTP_ALGO_NODE_MFMA && algo != EQTP_ALGO_EDGE_VALU) return EQTP_EINVAL;
+  if (N == 0) return EQTP_OK;
+  if (!row_ptr || !count || !src_sum || (E > 0 && !src)) return EQTP_EINVAL;
+  eqtp::ProbeArgs a;
+  a.N = N;
+  a.E = E;
+  a.C = C;
+  a.lmax = lmax;
+  a.row_ptr = row_ptr;
+  a.src = src;
+  a.count = count;
+  a.src_sum = reinterpret_cast<long long*>(src_sum);
+  a.stream = (hipStream_t)stream;
+  return status_of(algo == EQTP_ALGO_NODE_MFMA ? eqtp::launch_probe_node(a) : eqtp::launch_probe_edge(a));
+}
+
+}  // extern "C"

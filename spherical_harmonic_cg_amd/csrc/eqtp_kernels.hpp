@@ -1,0 +1,44 @@
+// eqtp_kernels.hpp -- host-side launch interface between the C ABI and the
+// kernels.  Arguments are validated by the ABI layer before these are called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+namespace eqtp {
+
+struct ConvArgs {
+  int64_t N, E;
+  int lmax, C, path_set, weight_mode, edge_order;
+  float r_cut;
+  const float* vec;
+  const int32_t* src;
+  const int32_t* dst;
+  const int32_t* row_ptr;
+  const float* x;
+  const float* w;
+  float* out;
+  hipStream_t stream;
+};
+
+struct ProbeArgs {
+  int64_t N, E;
+  int C, lmax;
+  const int32_t* row_ptr;
+  const int32_t* src;
+  int32_t* count;
+  long long* src_sum;
+  hipStream_t stream;
+};
+
+hipError_t launch_sh(const float* vec, int64_t E, int lmax, float* Y, hipStream_t stream);
+hipError_t launch_conv_node(const ConvArgs& a);   // sorted edges, fixed weights, matrix cores
+hipError_t launch_conv_edge(const ConvArgs& a);   // any order / weights, vector ALUs
+hipError_t launch_probe_node(const ProbeArgs& a);
+hipError_t launch_probe_edge(const ProbeArgs& a);
+hipError_t launch_linear(int64_t N, int C, int lmax, int bf16, const float* h, const float* W, float* out,
+                         hipStream_t stream);
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t stream);
+
+}  // namespace eqtp

@@ -1,0 +1,209 @@
+"""Python binding of the C ABI in include/eqtp.h (argument marshalling only).
+
+Every function has the name of the C entry point it calls.  Tensors are
+PyTorch tensors on the current HIP device; work is enqueued on
+``torch.cuda.current_stream()`` and nothing is synchronised.  All arithmetic
+runs in the HIP library: if ``libeqtp.so`` has not been built, the first call
+raises -- there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libeqtp.so")
+
+EQTP_OK, EQTP_EINVAL, EQTP_EUNSUPPORTED, EQTP_EHIP = 0, 1, 2, 3
+EQTP_PATHS_PARITY, EQTP_PATHS_SO3 = 0, 1
+EQTP_W_FIXED, EQTP_W_RADIAL = 0, 1
+EQTP_EDGES_DST_SORTED, EQTP_EDGES_UNSORTED = 0, 1
+EQTP_ALGO_AUTO, EQTP_ALGO_NODE_MFMA, EQTP_ALGO_EDGE_VALU = 0, 1, 2
+EQTP_F32, EQTP_BF16 = 0, 1
+
+EXPORTED = ("eqtp_num_paths", "eqtp_path_table", "eqtp_sh", "eqtp_conv_fused", "eqtp_linear",
+            "eqtp_status_string", "eqtp_test_segment_probe")
+
+
+class EqtpError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__("%s: %s" % (where, eqtp_status_string(status)))
+
+
+class _ConvDesc(ctypes.Structure):
+    _fields_ = [("struct_size", ctypes.c_int32), ("lmax", ctypes.c_int32), ("C", ctypes.c_int32),
+                ("path_set", ctypes.c_int32), ("weight_mode", ctypes.c_int32), ("edge_order", ctypes.c_int32),
+                ("algo", ctypes.c_int32), ("r_cut", ctypes.c_float), ("n_basis", ctypes.c_int32)]
+
+
+_lib = None
+_lock = threading.Lock()
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libeqtp.so (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(path):
+                raise RuntimeError("HIP library %s not built; run `python -m spherical_harmonic_cg_amd.build`" % path)
+            lib = ctypes.CDLL(path)
+            vp, i32, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+            lib.eqtp_num_paths.argtypes = [i32, i32]
+            lib.eqtp_num_paths.restype = i32
+            lib.eqtp_path_table.argtypes = [i32, i32, vp]
+            lib.eqtp_path_table.restype = i32
+            lib.eqtp_sh.argtypes = [vp, i64, i32, vp, vp]
+            lib.eqtp_sh.restype = i32
+            lib.eqtp_conv_fused.argtypes = [ctypes.POINTER(_ConvDesc), i64, i64, vp, vp, vp, vp, vp, vp, vp, vp]
+            lib.eqtp_conv_fused.restype = i32
+            lib.eqtp_linear.argtypes = [i64, i32, i32, i32, vp, vp, vp, vp]
+            lib.eqtp_linear.restype = i32
+            lib.eqtp_status_string.argtypes = [i32]
+            lib.eqtp_status_string.restype = ctypes.c_char_p
+            lib.eqtp_test_segment_probe.argtypes = [vp, vp, i64, i64, i32, i32, i32, vp, vp, vp]
+            lib.eqtp_test_segment_probe.restype = i32
+            _lib = lib
+    return _lib
+
+
+def _stream():
+    import torch
+
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None and t.numel() > 0 else ctypes.c_void_p(0)
+
+
+def _check(t, name, dtype, shape=None):
+    import torch
+
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be on the GPU" % name)
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+
+
+def _raise(rc, where):
+    if rc != EQTP_OK:
+        raise EqtpError(rc, where)
+
+
+def eqtp_status_string(status: int) -> str:
+    return load_library().eqtp_status_string(int(status)).decode()
+
+
+def eqtp_num_paths(lmax: int, path_set: int = EQTP_PATHS_PARITY) -> int:
+    P = load_library().eqtp_num_paths(lmax, path_set)
+    if P < 0:
+        raise EqtpError(-P, "eqtp_num_paths")
+    return P
+
+
+def eqtp_path_table(lmax: int, path_set: int = EQTP_PATHS_PARITY) -> np.ndarray:
+    P = eqtp_num_paths(lmax, path_set)
+    out = np.zeros((P, 3), dtype=np.int32)
+    rc = load_library().eqtp_path_table(lmax, path_set, out.ctypes.data_as(ctypes.c_void_p))
+    if rc < 0:
+        raise EqtpError(-rc, "eqtp_path_table")
+    return out
+
+
+def eqtp_sh(vec, lmax: int, Y=None):
+    """Y [E, (lmax+1)^2] fp32 = real spherical harmonics of vec [E, 3] fp32."""
+    import torch
+
+    _check(vec, "vec", torch.float32)
+    E = vec.shape[0]
+    if vec.dim() != 2 or vec.shape[1] != 3:
+        raise ValueError("vec must be [E, 3]")
+    K = (lmax + 1) ** 2
+    if Y is None:
+        Y = torch.empty((E, K), dtype=torch.float32, device=vec.device)
+    _check(Y, "Y", torch.float32, (E, K))
+    _raise(load_library().eqtp_sh(_ptr(vec), E, lmax, _ptr(Y), _stream()), "eqtp_sh")
+    return Y
+
+
+def eqtp_conv_fused(vec, src, x, weights, lmax: int, row_ptr=None, dst=None, path_set: int = EQTP_PATHS_PARITY,
+                    weight_mode: int = EQTP_W_FIXED, r_cut: float = 0.0, n_basis: int = 8,
+                    algo: int = EQTP_ALGO_AUTO, out=None):
+    """out [N, C, K] = fused harmonics -> coupling -> sum into dst.
+
+    Give ``row_ptr`` [N+1] for dst-sorted edges, or ``dst`` [E] for any order
+    (atomic accumulation).  ``weights`` is [P, C] (fixed) or [8, P*C] (radial).
+    """
+    import torch
+
+    _check(x, "x", torch.float32)
+    if x.dim() != 3:
+        raise ValueError("x must be [N, C, K]")
+    N, C, K = x.shape
+    if K != (lmax + 1) ** 2:
+        raise ValueError("x has %d components, lmax %d needs %d" % (K, lmax, (lmax + 1) ** 2))
+    _check(vec, "vec", torch.float32)
+    E = vec.shape[0]
+    _check(src, "src", torch.int32, (E,))
+    _check(weights, "weights", torch.float32)
+    if (row_ptr is None) == (dst is None):
+        raise ValueError("give exactly one of row_ptr (dst-sorted edges) or dst (any order)")
+    if row_ptr is not None:
+        _check(row_ptr, "row_ptr", torch.int32, (N + 1,))
+        order = EQTP_EDGES_DST_SORTED
+    else:
+        _check(dst, "dst", torch.int32, (E,))
+        order = EQTP_EDGES_UNSORTED
+    P = eqtp_num_paths(lmax, path_set)
+    wshape = (P, C) if weight_mode == EQTP_W_FIXED else (n_basis, P * C)
+    if tuple(weights.shape) != wshape:
+        raise ValueError("weights has shape %s, expected %s" % (tuple(weights.shape), wshape))
+    if out is None:
+        out = torch.empty_like(x)
+    _check(out, "out", torch.float32, (N, C, K))
+    d = _ConvDesc(ctypes.sizeof(_ConvDesc), lmax, C, path_set, weight_mode, order, algo, float(r_cut), n_basis)
+    rc = load_library().eqtp_conv_fused(ctypes.byref(d), N, E, _ptr(vec), _ptr(src), _ptr(dst), _ptr(row_ptr),
+                                        _ptr(x), _ptr(weights), _ptr(out), _stream())
+    _raise(rc, "eqtp_conv_fused")
+    return out
+
+
+def eqtp_linear(h, W, lmax: int, dtype: int = EQTP_F32, out=None):
+    """out[n, c', l m] = sum_c W[l, c', c] h[n, c, l m]; dtype EQTP_F32 or EQTP_BF16 operands."""
+    import torch
+
+    _check(h, "h", torch.float32)
+    N, C, K = h.shape
+    _check(W, "W", torch.float32, (lmax + 1, C, C))
+    if out is None:
+        out = torch.empty_like(h)
+    _check(out, "out", torch.float32, (N, C, K))
+    _raise(load_library().eqtp_linear(N, C, lmax, dtype, _ptr(h), _ptr(W), _ptr(out), _stream()), "eqtp_linear")
+    return out
+
+
+def eqtp_test_segment_probe(row_ptr, src, C: int, lmax: int, algo: int = EQTP_ALGO_NODE_MFMA):
+    """(count [N] int32, src_sum [N] int64) walked with the conv kernel's schedule."""
+    import torch
+
+    _check(row_ptr, "row_ptr", torch.int32)
+    _check(src, "src", torch.int32)
+    N = row_ptr.shape[0] - 1
+    E = src.shape[0]
+    count = torch.empty(N, dtype=torch.int32, device=row_ptr.device)
+    src_sum = torch.empty(N, dtype=torch.int64, device=row_ptr.device)
+    rc = load_library().eqtp_test_segment_probe(_ptr(row_ptr), _ptr(src), N, E, C, lmax, algo, _ptr(count),
+                                                _ptr(src_sum), _stream())
+    _raise(rc, "eqtp_test_segment_probe")
+    return count, src_sum

@@ -222,10 +222,10 @@ def make_config(name: str, seed: int = 2026) -> Workload:
 
 def random_permutation(wl: Workload, seed: int = 2026):
     """A seeded random edge order (for the unsorted / atomic path): returns
-    (src, dst, vec) permuted."""
+    (vec, src, dst) permuted, in the argument order of the convolution."""
     rng = np.random.default_rng(np.random.SeedSequence([seed, 99]))
     perm = rng.permutation(wl.E)
-    return wl.src[perm].copy(), wl.dst[perm].copy(), wl.vec[perm].copy()
+    return wl.vec[perm].copy(), wl.src[perm].copy(), wl.dst[perm].copy()
 
 
 def small_graph(n: int, e_per_row: int, C: int, lmax: int, seed: int, path_set: int = 0,

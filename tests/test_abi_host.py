@@ -1,0 +1,120 @@
+"""The C-ABI library loads and exports every function include/eqtp.h
+declares; host-only entry points and argument validation (no kernel
+launches: every call here is rejected or answered before any HIP call)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "eqtp.h")
+
+
+def _lib():
+    from spherical_harmonic_cg_amd import eqtp
+
+    if not os.path.exists(eqtp.LIB_PATH):
+        pytest.skip("libeqtp.so not built")
+    return eqtp
+
+
+def _declared():
+    txt = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const char\*|int)\s+(eqtp_\w+)\s*\(", txt, re.M)))
+
+
+def test_header_declares_the_binding_names():
+    from spherical_harmonic_cg_amd import eqtp
+
+    assert _declared() == sorted(eqtp.EXPORTED)
+
+
+def test_every_declared_symbol_is_exported():
+    e = _lib()
+    lib = ctypes.CDLL(e.LIB_PATH)
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_num_paths_and_table_match_oracle():
+    e = _lib()
+    for L in range(4):
+        for ps in (0, 1):
+            assert e.eqtp_num_paths(L, ps) == len(oracle.paths(L, ps))
+            np.testing.assert_array_equal(e.eqtp_path_table(L, ps), oracle.paths(L, ps))
+    lib = e.load_library()
+    assert lib.eqtp_num_paths(4, 0) == -e.EQTP_EUNSUPPORTED
+    assert lib.eqtp_num_paths(3, 7) == -e.EQTP_EINVAL
+
+
+def test_status_strings():
+    e = _lib()
+    for s in range(5):
+        assert isinstance(e.eqtp_status_string(s), str)
+    assert e.eqtp_status_string(1).startswith("EQTP_EINVAL")
+
+
+def _desc(e, **kw):
+    d = dict(lmax=3, C=64, path_set=0, weight_mode=0, edge_order=0, algo=0, r_cut=0.0, n_basis=8)
+    d.update(kw)
+    return e._ConvDesc(ctypes.sizeof(e._ConvDesc), d["lmax"], d["C"], d["path_set"], d["weight_mode"],
+                       d["edge_order"], d["algo"], d["r_cut"], d["n_basis"])
+
+
+FAKE = ctypes.c_void_p(0x10000)  # never dereferenced: every call below is rejected first
+NULL = ctypes.c_void_p(0)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(lmax=4), 2), (dict(lmax=-1), 1), (dict(C=48), 2), (dict(C=0), 1), (dict(path_set=3), 1),
+    (dict(weight_mode=2), 1), (dict(edge_order=5), 1), (dict(algo=9), 1),
+    (dict(weight_mode=1, r_cut=0.0), 1), (dict(weight_mode=1, r_cut=5.0, n_basis=6), 2),
+    (dict(weight_mode=1, r_cut=5.0, algo=1), 2), (dict(edge_order=1, algo=1), 2),
+])
+def test_conv_descriptor_validation(kw, want):
+    e = _lib()
+    lib = e.load_library()
+    d = _desc(e, **kw)
+    rc = lib.eqtp_conv_fused(ctypes.byref(d), 10, 20, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, NULL)
+    assert rc == want
+
+
+def test_conv_pointer_and_size_validation():
+    e = _lib()
+    lib = e.load_library()
+    d = _desc(e)
+    call = lambda N, E, vec, src, dst, rp, x, w, out: lib.eqtp_conv_fused(ctypes.byref(d), N, E, vec, src, dst, rp,
+                                                                          x, w, out, NULL)
+    assert call(10, 20, FAKE, FAKE, NULL, FAKE, NULL, FAKE, FAKE) == 1      # x missing
+    assert call(10, 20, FAKE, FAKE, NULL, NULL, FAKE, FAKE, FAKE) == 1      # row_ptr missing (sorted)
+    assert call(10, 20, NULL, FAKE, NULL, FAKE, FAKE, FAKE, FAKE) == 1      # vec missing
+    assert call(-1, 20, FAKE, FAKE, NULL, FAKE, FAKE, FAKE, FAKE) == 1      # negative N
+    assert call(0, 20, FAKE, FAKE, NULL, FAKE, FAKE, FAKE, FAKE) == 1       # edges without nodes
+    assert call(1 << 31, 0, FAKE, FAKE, NULL, FAKE, FAKE, FAKE, FAKE) == 1  # too many nodes
+    mis = ctypes.c_void_p(0x10004)
+    assert call(10, 20, FAKE, FAKE, NULL, FAKE, mis, FAKE, FAKE) == 1       # x not 16-byte aligned
+    assert call(0, 0, NULL, NULL, NULL, NULL, NULL, NULL, NULL) == 0        # empty problem: nothing to do
+    du = _desc(e, edge_order=1)
+    assert lib.eqtp_conv_fused(ctypes.byref(du), 10, 20, FAKE, FAKE, NULL, NULL, FAKE, FAKE, FAKE, NULL) == 1
+    bad = _desc(e)
+    bad.struct_size = 4
+    assert lib.eqtp_conv_fused(ctypes.byref(bad), 10, 20, FAKE, FAKE, NULL, FAKE, FAKE, FAKE, FAKE, NULL) == 1
+
+
+def test_sh_and_linear_validation():
+    e = _lib()
+    lib = e.load_library()
+    assert lib.eqtp_sh(FAKE, 10, 4, FAKE, NULL) == 2
+    assert lib.eqtp_sh(FAKE, -1, 3, FAKE, NULL) == 1
+    assert lib.eqtp_sh(NULL, 10, 3, FAKE, NULL) == 1
+    assert lib.eqtp_sh(FAKE, 10, 3, ctypes.c_void_p(0x10008), NULL) == 1
+    assert lib.eqtp_sh(NULL, 0, 3, NULL, NULL) == 0
+    assert lib.eqtp_linear(10, 64, 3, 2, FAKE, FAKE, FAKE, NULL) == 1
+    assert lib.eqtp_linear(10, 48, 3, 0, FAKE, FAKE, FAKE, NULL) == 2
+    assert lib.eqtp_linear(10, 64, 3, 0, NULL, FAKE, FAKE, NULL) == 1
+    assert lib.eqtp_linear(0, 64, 3, 0, NULL, NULL, NULL, NULL) == 0
+    assert lib.eqtp_test_segment_probe(FAKE, FAKE, 10, 20, 64, 3, 0, FAKE, FAKE, NULL) == 1
