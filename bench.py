@@ -50,6 +50,37 @@ def count_terms(lmax, path_set):
     return int(m.group(1))
 
 
+KERNEL_SOURCES = ("spherical_harmonic_cg_amd/csrc/conv_node.hip", "spherical_harmonic_cg_amd/csrc/eqtp_device.hpp",
+                  "spherical_harmonic_cg_amd/csrc/generated/cg_tables.inc")
+
+
+def kernel_source_hash():
+    import hashlib
+
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, rel), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(config, atom_order, unsorted, algo):
+    """HBM-side bytes per launch of the conv kernel from the committed counter
+    summary (profiles/traffic.json), or None when that summary was taken on
+    different kernel sources or another workload."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))
+    except ValueError:
+        return None
+    key = "%s/%s/%s/%d" % (config, atom_order, "unsorted" if unsorted else "sorted", algo)
+    ent = rec.get(key)
+    if not ent or ent.get("source_sha256_16") != kernel_source_hash():
+        return None
+    return ent["read_bytes"] + ent["write_bytes"]
+
+
 def cpu_baseline(wl, budget_s):
     """The fp64 oracle on the same workload, on the host (it is single-threaded).
 
@@ -89,6 +120,8 @@ def main():
     ap.add_argument("--config", default="mid", choices=sorted(WORKLOAD_TEXT))
     ap.add_argument("--algo", type=int, default=0, help="0 auto, 1 node/matrix cores, 2 edge/vector ALUs")
     ap.add_argument("--unsorted", action="store_true", help="random edge order (atomic path)")
+    ap.add_argument("--atom-order", default="generation", choices=("generation", "cell"),
+                    help="'cell': spatially coherent atom numbering (a labelled extra, not the headline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
     ap.add_argument("--calib-copy", action="store_true",
@@ -113,7 +146,7 @@ def main():
     torch.cuda.set_device(0)
 
     t_gen = time.perf_counter()
-    wl = synth.make_config(args.config)
+    wl = synth.make_config(args.config, atom_order=args.atom_order)
     log("workload %s: N=%d E=%d C=%d lmax=%d P=%d (generated in %.1fs)" % (wl.name, wl.N, wl.E, wl.C, wl.lmax,
                                                                             wl.P, time.perf_counter() - t_gen))
     dev = torch.device("cuda:0")
@@ -184,7 +217,8 @@ def main():
     conv_s = float(conv_ms.mean()) * 1e-3
     achieved_tflops = flop_edge * wl.E / conv_s / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved_tflops, 3), "peak": PEAK_FP32_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved_tflops / PEAK_FP32_TFLOPS, 4), "traffic": None}
+                "unit": "TFLOP/s", "frac": round(achieved_tflops / PEAK_FP32_TFLOPS, 4),
+                "traffic": measured_traffic(args.config, args.atom_order, args.unsorted, args.algo)}
     alg_bytes = 2 * wl.N * wl.C * wl.K * 4 + wl.E * 16 + (wl.N + 1) * 4 + wl.weights.size * 4
     log("conv: %.3e counted flop (2*nnz*C per edge), %.1f MB algorithmic bytes -> %.1f GB/s" % (
         flop_edge * wl.E, alg_bytes / 1e6, alg_bytes / conv_s / 1e9))
@@ -207,7 +241,8 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": WORKLOAD_TEXT[args.config] + (" (random edge order)" if args.unsorted else ""),
+        "config": {"workload": WORKLOAD_TEXT[args.config] + (" (random edge order)" if args.unsorted else "")
+                   + (" (cell-sorted atom numbering)" if args.atom_order == "cell" else ""),
                    "atoms": wl.N, "edges": wl.E, "channels": wl.C, "lmax": wl.lmax, "paths": wl.P,
                    "coupling_nnz": nnz, "algo": args.algo},
         "roofline": roofline,

@@ -33,113 +33,213 @@ namespace eqtp {
 template <int L, int C>
 struct NodeCfg {
   static constexpr int K = num_comp(L);
-  static constexpr int NW = C >= 16 ? C / 16 : 1;        // waves per workgroup
-  static constexpr int CW = C >= 16 ? 16 : C;            // channels per wave
-  static constexpr int GS = (K * K) % 2 ? K * K : K * K + 1;  // LDS floats per channel (odd)
-  static constexpr int SLICE = CW * GS;                  // LDS floats per wave's G slice
+  static constexpr int CW = C >= 16 ? 16 : C;            // channels per wave (MFMA columns in use)
+  static constexpr int NBLK = C / CW;                    // channel blocks per row
+  // G row per channel: K*K floats padded to a multiple of 4 (16-byte rows) with
+  // stride = 4 (mod 32) words, so 8 lanes' 16-byte accesses hit distinct banks
+  static constexpr int GS = ((K * K + 3) / 4 * 4) % 32 == 4 ? (K * K + 3) / 4 * 4
+                                                          : ((K * K + 3) / 4 * 4 + 31) / 32 * 32 + 4;
+  static constexpr int SLICE = CW * GS;                  // G slice (floats)
   static constexpr int STG = 64 * 16 + 64;               // staging: Y[64][16] + src[64]
-  static constexpr bool STG_IN_SLICE = SLICE >= STG;
-  static constexpr int LDS = NW * SLICE + (STG_IN_SLICE ? 0 : NW * STG);
-  static constexpr int CB = C > 64 ? C / 64 : 1;         // 64-channel blocks in the epilogue
-  static constexpr int NG = NW / CB;                     // output-component groups
-  static constexpr int THREADS = NW * kWave;
-  static_assert(C * K <= LDS, "output tile must fit in LDS");
-  static_assert(LDS * 4 <= 160 * 1024, "LDS budget");
+  static constexpr int LDS = SLICE > STG ? SLICE : STG;  // staging and G share the wave's LDS
+  static constexpr int THREADS = kWave;                  // one independent wavefront per workgroup
+  static constexpr int PF = 3;                           // gather steps in flight
+  static_assert(LDS * 4 <= 64 * 1024, "LDS budget");
 };
 
-// One row -> wave -> lane -> step walk.  Calls stage(cb, cnt) once per chunk
-// of up to 64 edges; for every 4-edge step of the chunk, load(el) issues the
-// step's memory reads (el = this lane's edge slot 0..63 in the staging area)
-// and compute(data) consumes them.  Loads run one step ahead of compute.
-template <class Stage, class Load, class Compute>
-__device__ __forceinline__ void node_row_walk(int e_beg, int e_end, Stage&& stage, Load&& load, Compute&& compute) {
+// The task schedule shared by the convolution and its test probe.
+//   * Task t = (row t / NBLK, channel block t % NBLK); persistent wavefronts
+//     take t = blockIdx.x, blockIdx.x + gridDim.x, ...  The next task's CSR
+//     bounds and first 64 edges (vector, source) are loaded while the current
+//     one runs.
+//   * A row's edges are staged 64 at a time (stage(valid, vx, vy, vz, s):
+//     lane i holds edge i of the chunk) and consumed in 4-edge steps: lane l
+//     takes slot 4*step + l/16.  load(slot, live) issues a step's reads and
+//     compute(data) consumes them; PF steps are kept in flight in a ring.
+//     Loads are issued unconditionally (steps past the end are "not live" and
+//     read nothing), so the wait for a step covers that step's loads only.
+//   * task_end(row, blk) runs after each task (the epilogue).
+// BUF: edge vectors and sources come through raw buffer loads (< 4 GiB).
+template <int PF, int NBLK, bool BUF, class Stage, class Load, class Compute, class TaskEnd>
+__device__ __forceinline__ void node_tasks(int N, int E, const int* __restrict__ row_ptr, const float* __restrict__ vec,
+                                           const int* __restrict__ src, Stage&& stage, Load&& load,
+                                           Compute&& compute, TaskEnd&& task_end) {
   const int lane = threadIdx.x & 63;
   const int kq = lane >> 4;
-  for (int cb = e_beg; cb < e_end; cb += 64) {
-    const int cnt = min(64, e_end - cb);
-    stage(cb, cnt);
-    wave_lds_sync();
-    const int nsteps = (cnt + 3) >> 2;
-    auto cur = load(kq);
-    for (int st = 0; st < nsteps; ++st) {
-      decltype(cur) nxt = cur;
-      if (st + 1 < nsteps) nxt = load((st + 1) * 4 + kq);
-      compute(cur);
-      cur = nxt;
+  const long long ntasks = (long long)N * NBLK;
+  const rsrc_t rvec = make_rsrc(vec, vec != nullptr ? (uint64_t)E * 12u : 0u);
+  const rsrc_t rsrc = make_rsrc(src, (uint64_t)E * 4u);
+  auto bounds = [&](long long t, int& b, int& e) {
+    const int r = (int)(t / NBLK);
+    b = 0;
+    e = 0;
+    if (E > 0) {
+      b = min(max(row_ptr[r], 0), E);
+      e = min(max(row_ptr[r + 1], b), E);
     }
+  };
+  auto edge_in = [&](int b, int e, int i, float& vx, float& vy, float& vz, int& s, bool& valid) {
+    valid = b + i < e;
+    if constexpr (BUF) {
+      const uint32_t k = valid ? (uint32_t)(b + i) : 0u;
+      const uint32_t ov = valid ? 12u * k : kOutOfRange;
+      vx = buf_f32(rvec, ov);
+      vy = buf_f32(rvec, ov + 4u);
+      vz = buf_f32(rvec, ov + 8u);
+      s = clamp_index(buf_i32(rsrc, valid ? 4u * k : kOutOfRange), N);
+    } else {
+      const int k = valid ? b + i : 0;
+      vx = vy = vz = 0.0f;
+      s = 0;
+      if (valid) {
+        if (vec != nullptr) {
+          vx = vec[3 * k];
+          vy = vec[3 * k + 1];
+          vz = vec[3 * k + 2];
+        }
+        s = clamp_index(src[k], N);
+      }
+    }
+  };
+  long long t = blockIdx.x;
+  if (t >= ntasks) return;
+  int e_beg, e_end;
+  bounds(t, e_beg, e_end);
+  float pvx, pvy, pvz;
+  int ps;
+  bool pvalid;
+  edge_in(e_beg, e_end, lane, pvx, pvy, pvz, ps, pvalid);
+  while (true) {
+    const long long tn = t + gridDim.x;
+    int nb = 0, ne = 0;
+    if (tn < ntasks) bounds(tn, nb, ne);
+    bool next_loaded = false;
+    float qvx = 0.f, qvy = 0.f, qvz = 0.f;
+    int qs = 0;
+    bool qvalid = false;
+    for (int cb = e_beg; cb < e_end; cb += 64) {
+      const int cnt = min(64, e_end - cb);
+      if (cb != e_beg) edge_in(cb, e_end, lane, pvx, pvy, pvz, ps, pvalid);
+      stage(pvalid, pvx, pvy, pvz, ps);
+      wave_lds_sync();
+      const int nsteps = (cnt + 3) >> 2;
+      decltype(load(0, true)) ring[PF];
+#pragma unroll
+      for (int q = 0; q < PF; ++q) ring[q] = load(4 * min(q, 15) + kq, q < nsteps);
+      if (!next_loaded) {
+        edge_in(nb, ne, lane, qvx, qvy, qvz, qs, qvalid);
+        next_loaded = true;
+      }
+      for (int base = 0; base < nsteps; base += PF) {
+#pragma unroll
+        for (int q = 0; q < PF; ++q) {
+          if (base + q < nsteps) compute(ring[q]);
+          const int st = base + q + PF;
+          ring[q] = load(4 * min(st, 15) + kq, st < nsteps);
+        }
+      }
+      wave_lds_sync();
+    }
+    if (!next_loaded) edge_in(nb, ne, lane, qvx, qvy, qvz, qs, qvalid);
+    task_end((int)(t / NBLK), (int)(t % NBLK));
     wave_lds_sync();
+    if (tn >= ntasks) break;
+    t = tn;
+    e_beg = nb;
+    e_end = ne;
+    pvx = qvx;
+    pvy = qvy;
+    pvz = qvz;
+    ps = qs;
+    pvalid = qvalid;
   }
 }
 
-template <int L, int PS, int C>
-__global__ __launch_bounds__((NodeCfg<L, C>::THREADS)) void conv_node_kernel(int N, int E,
-                                                                           const int* __restrict__ row_ptr,
-                                                                           const float* __restrict__ vec,
-                                                                           const int* __restrict__ src,
-                                                                           const float* __restrict__ x,
-                                                                           const float* __restrict__ w,
-                                                                           float* __restrict__ out) {
+template <int L, int PS, int C, bool BUF>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void conv_node_kernel(
+    int N, int E, const int* __restrict__ row_ptr, const float* __restrict__ vec, const int* __restrict__ src,
+    const float* __restrict__ x, const float* __restrict__ w, float* __restrict__ out) {
   using Cfg = NodeCfg<L, C>;
   using T = Tables<L, PS>;
   constexpr int K = Cfg::K;
   __shared__ __attribute__((aligned(16))) float lds[Cfg::LDS];
 
   const int lane = threadIdx.x & 63;
-  const int wv = threadIdx.x >> 6;
-  const int row = blockIdx.x;
-  int e_beg = 0, e_end = 0;
-  if (E > 0) {
-    e_beg = min(max(row_ptr[row], 0), E);
-    e_end = min(max(row_ptr[row + 1], e_beg), E);
-  }
+  float* ystg = lds;
+  int* sstg = reinterpret_cast<int*>(lds + 64 * 16);
+  const rsrc_t rx = make_rsrc(x, (uint64_t)N * C * K * 4u);
 
-  float* slice = lds + wv * Cfg::SLICE;
-  float* ystg = Cfg::STG_IN_SLICE ? slice : lds + Cfg::NW * Cfg::SLICE + wv * Cfg::STG;
-  int* sstg = reinterpret_cast<int*>(ystg + 64 * 16);
-
-  const int cl = lane & 15;                  // column of the MFMA tile = channel within the wave
+  const int cl = lane & 15;  // MFMA column = channel within the block
   const bool c_ok = cl < Cfg::CW;
-  const int c_load = wv * Cfg::CW + (c_ok ? cl : 0);
 
   f4 acc[K];
 #pragma unroll
   for (int k = 0; k < K; ++k) acc[k] = f4{0.f, 0.f, 0.f, 0.f};
+  int c_base = (int)(blockIdx.x % Cfg::NBLK) * Cfg::CW;  // first channel of the current task's block
 
-  auto stage = [&](int cb, int cnt) {
-    const bool valid = lane < cnt;
-    const int e = cb + (valid ? lane : 0);
-    const float vx = vec[3 * e + 0], vy = vec[3 * e + 1], vz = vec[3 * e + 2];
-    const int s = clamp_index(src[e], N);
+  auto stage = [&](bool valid, float vx, float vy, float vz, int s) {
     float Y[16];
     sh_eval<L>(vx, vy, vz, Y);
     const float m = valid ? 1.0f : 0.0f;  // padding slots contribute nothing
     f4* yd = reinterpret_cast<f4*>(ystg + lane * 16);
 #pragma unroll
     for (int q = 0; q < 4; ++q) yd[q] = f4{m * Y[4 * q], m * Y[4 * q + 1], m * Y[4 * q + 2], m * Y[4 * q + 3]};
-    sstg[lane] = s;
+    sstg[lane] = valid ? s : -1;  // -1: the slot's gather reads nothing
   };
 
+  // B operand columns.  K = 16: column n = lane%16 stands for (channel
+  // 4j + n/4, components 4(n%4)..4(n%4)+3) of channel group j, so one 16-byte
+  // load per lane and j reads 256 contiguous bytes per edge (4 channels x 16
+  // components); MFMA (j, q) then accumulates G[4j + n/4][4(n%4) + q][mu2].
+  // Other K: column n = channel n, one MFMA per component.
   struct StepData {
     float a;
     float xv[K];
   };
-  auto load = [&](int el) {
+  auto load = [&](int el, bool live) {
     StepData d;
-    d.a = ystg[el * 16 + cl];
     const int s = sstg[el];
-    const float* xp = x + ((size_t)s * C + c_load) * K;
-    if constexpr (K % 4 == 0) {
+    const bool ok = live && s >= 0;
+    d.a = live ? ystg[el * 16 + cl] : 0.0f;
+    if constexpr (K == 16) {
 #pragma unroll
-      for (int q = 0; q < K / 4; ++q) {
-        const f4 t = c_ok ? reinterpret_cast<const f4*>(xp)[q] : f4{0.f, 0.f, 0.f, 0.f};
-        d.xv[4 * q] = t[0];
-        d.xv[4 * q + 1] = t[1];
-        d.xv[4 * q + 2] = t[2];
-        d.xv[4 * q + 3] = t[3];
+      for (int j = 0; j < 4; ++j) {
+        const int cw = 4 * j + (cl >> 2);
+        const bool v = ok && cw < Cfg::CW;
+        f4 t;
+        if constexpr (BUF) {
+          const uint32_t off = v ? (uint32_t)((((size_t)s * C + c_base + cw) * K + 4 * (cl & 3)) * 4) : kOutOfRange;
+          t = buf_f4(rx, off);
+        } else {
+          t = v ? *reinterpret_cast<const f4*>(x + ((size_t)s * C + c_base + cw) * K + 4 * (cl & 3))
+                : f4{0.f, 0.f, 0.f, 0.f};
+        }
+        d.xv[4 * j] = t[0];
+        d.xv[4 * j + 1] = t[1];
+        d.xv[4 * j + 2] = t[2];
+        d.xv[4 * j + 3] = t[3];
       }
     } else {
+      const bool v = ok && c_ok;
+      const size_t e0 = ((size_t)(v ? s : 0) * C + c_base + (c_ok ? cl : 0)) * K;
+      if constexpr (K % 4 == 0) {
 #pragma unroll
-      for (int k = 0; k < K; ++k) d.xv[k] = c_ok ? xp[k] : 0.0f;
+        for (int q = 0; q < K / 4; ++q) {
+          f4 t;
+          if constexpr (BUF) t = buf_f4(rx, v ? (uint32_t)((e0 + 4 * q) * 4) : kOutOfRange);
+          else t = v ? *reinterpret_cast<const f4*>(x + e0 + 4 * q) : f4{0.f, 0.f, 0.f, 0.f};
+          d.xv[4 * q] = t[0];
+          d.xv[4 * q + 1] = t[1];
+          d.xv[4 * q + 2] = t[2];
+          d.xv[4 * q + 3] = t[3];
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+          if constexpr (BUF) d.xv[k] = buf_f32(rx, v ? (uint32_t)((e0 + k) * 4) : kOutOfRange);
+          else d.xv[k] = v ? x[e0 + k] : 0.0f;
+        }
+      }
     }
     return d;
   };
@@ -148,129 +248,153 @@ __global__ __launch_bounds__((NodeCfg<L, C>::THREADS)) void conv_node_kernel(int
     for (int k = 0; k < K; ++k) acc[k] = __builtin_amdgcn_mfma_f32_16x16x4f32(d.a, d.xv[k], acc[k], 0, 0, 0);
   };
 
-  node_row_walk(e_beg, e_end, stage, load, compute);
+  auto task_end = [&](int row, int blk) {
+    // G[c][mu1][mu2] -> LDS (over the staging area), one 16-byte store per
+    // accumulator: lane (cl, kq) holds mu2 = 4 kq + v of
+    //   K = 16: acc[4j + q] -> channel 4j + cl/4, mu1 = 4(cl%4) + q;
+    //   else:   acc[k]      -> channel cl, mu1 = k.
+    if constexpr (K == 16) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int cw = 4 * j + (cl >> 2);
+        if (cw < Cfg::CW) {
+          float* gc = lds + cw * Cfg::GS;
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            *reinterpret_cast<f4*>(gc + (4 * (cl & 3) + q) * K + 4 * (lane >> 4)) = acc[4 * j + q];
+        }
+      }
+    } else if (c_ok) {
+      float* gc = lds + cl * Cfg::GS;
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        if constexpr (K % 4 == 0) {
+          *reinterpret_cast<f4*>(gc + k * K + 4 * (lane >> 4)) = acc[k];
+        } else {
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int mu2 = 4 * (lane >> 4) + v;
+            if (mu2 < K) gc[k * K + mu2] = acc[k][v];
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < K; ++k) acc[k] = f4{0.f, 0.f, 0.f, 0.f};
+    wave_lds_sync();
+    // coupling for channel c = blk*CW + lane (lanes < CW), all output components
+    if (lane < Cfg::CW) {
+      const int c = blk * Cfg::CW + lane;
+      const float* gc = lds + lane * Cfg::GS;
+      float wr[T::P];
+#pragma unroll
+      for (int p = 0; p < T::P; ++p) wr[p] = w[p * C + c];
+      float ov[K];
+#pragma unroll
+      for (int k = 0; k < K; ++k) ov[k] = 0.0f;
+      float t = 0.0f;
+      static_for<0, T::NT>([&](auto ii) {
+        constexpr int i = decltype(ii)::value;
+        constexpr eqtp_gen::CgTerm tm = T::by_out[i];
+        constexpr bool first = (i == 0) || T::by_out[i - 1].p != tm.p || T::by_out[i - 1].mu3 != tm.mu3;
+        constexpr bool last = (i + 1 == T::NT) || T::by_out[i + 1].p != tm.p || T::by_out[i + 1].mu3 != tm.mu3;
+        const float g = gc[tm.mu1 * K + tm.mu2];
+        t = first ? tm.c * g : fmaf(tm.c, g, t);
+        if constexpr (last) ov[tm.mu3] = fmaf(wr[tm.p], t, ov[tm.mu3]);
+      });
+      float* op = out + ((size_t)row * C + c) * K;
+      if constexpr (K % 4 == 0) {
+#pragma unroll
+        for (int q = 0; q < K / 4; ++q)
+          reinterpret_cast<f4*>(op)[q] = f4{ov[4 * q], ov[4 * q + 1], ov[4 * q + 2], ov[4 * q + 3]};
+      } else {
+#pragma unroll
+        for (int k = 0; k < K; ++k) op[k] = ov[k];
+      }
+    }
+  };
 
-  // G[c][mu1][mu2] -> LDS.  Lane l holds G[16w + l%16][mu1][mu2 = 4(l/16) + v].
-  if (c_ok) {
-    float* gc = slice + cl * Cfg::GS;
-#pragma unroll
-    for (int k = 0; k < K; ++k)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int mu2 = 4 * (lane >> 4) + v;
-        if (mu2 < K) gc[k * K + mu2] = acc[k][v];
-      }
-  }
-  __syncthreads();
-
-  // Epilogue: wave -> (64-channel block, output-component group); lane = channel.
-  const int cblk = wv % Cfg::CB;
-  const int grp = wv / Cfg::CB;
-  const int c = cblk * 64 + lane;
-  float ov[K];
-#pragma unroll
-  for (int k = 0; k < K; ++k) ov[k] = 0.0f;
-  if (c < C) {
-    const float* gc = lds + c * Cfg::GS;
-    float wr[T::P];
-#pragma unroll
-    for (int p = 0; p < T::P; ++p) wr[p] = w[p * C + c];
-    static_for<0, Cfg::NG>([&](auto gi) {
-      constexpr int G = decltype(gi)::value;
-      constexpr int TB = term_begin_for_mu3<L, PS>(group_mu3_begin<L, PS>(Cfg::NG, G));
-      constexpr int TE = term_begin_for_mu3<L, PS>(group_mu3_begin<L, PS>(Cfg::NG, G + 1));
-      if (grp == G) {
-        float t = 0.0f;
-        static_for<TB, TE>([&](auto ii) {
-          constexpr int i = decltype(ii)::value;
-          constexpr eqtp_gen::CgTerm tm = T::by_out[i];
-          constexpr bool first = (i == TB) || T::by_out[i - 1].p != tm.p || T::by_out[i - 1].mu3 != tm.mu3;
-          constexpr bool last = (i + 1 == TE) || T::by_out[i + 1].p != tm.p || T::by_out[i + 1].mu3 != tm.mu3;
-          const float g = gc[tm.mu1 * K + tm.mu2];
-          t = first ? tm.c * g : fmaf(tm.c, g, t);
-          if constexpr (last) ov[tm.mu3] = fmaf(wr[tm.p], t, ov[tm.mu3]);
-        });
-      }
-    });
-  }
-  __syncthreads();
-  // Output tile [C][K] in LDS (this wave's component group only), then a
-  // coalesced store of the row.
-  if (c < C) {
-    static_for<0, Cfg::NG>([&](auto gi) {
-      constexpr int G = decltype(gi)::value;
-      constexpr int MB = group_mu3_begin<L, PS>(Cfg::NG, G);
-      constexpr int ME = group_mu3_begin<L, PS>(Cfg::NG, G + 1);
-      if (grp == G) {
-#pragma unroll
-        for (int k = MB; k < ME; ++k) lds[c * K + k] = ov[k];
-      }
-    });
-  }
-  __syncthreads();
-  f4* orow = reinterpret_cast<f4*>(out + (size_t)row * C * K);
-  const f4* trow = reinterpret_cast<const f4*>(lds);
-  for (int i = threadIdx.x; i < C * K / 4; i += Cfg::THREADS) orow[i] = trow[i];
+  // load() needs the channel block of the current task: advance it after each task
+  node_tasks<Cfg::PF, Cfg::NBLK, BUF>(
+      N, E, row_ptr, vec, src, stage, load, compute,
+      [&](int row, int blk) {
+        task_end(row, blk);
+        // next task's block (tasks advance by gridDim.x)
+        const long long tn = (long long)row * Cfg::NBLK + blk + gridDim.x;
+        c_base = (int)(tn % Cfg::NBLK) * Cfg::CW;
+      });
 }
-
-// Test-only twin of the walk above: the same launch shape, staging and step
-// schedule, counting edges and summing source indices per row.
+// Test-only twin: the same launch shape and node_tasks schedule, counting
+// edges and summing source indices per row instead of the product (channel
+// block 0 of each row reports).
 template <int L, int C>
-__global__ __launch_bounds__((NodeCfg<L, C>::THREADS)) void probe_node_kernel(int N, int E,
-                                                                            const int* __restrict__ row_ptr,
-                                                                            const int* __restrict__ src,
-                                                                            int* __restrict__ count,
-                                                                            long long* __restrict__ src_sum) {
+__global__ __launch_bounds__(64) void probe_node_kernel(int N, int E, const int* __restrict__ row_ptr,
+                                                        const float* __restrict__ vec, const int* __restrict__ src,
+                                                        int* __restrict__ count, long long* __restrict__ src_sum) {
   using Cfg = NodeCfg<L, C>;
   __shared__ __attribute__((aligned(16))) float lds[Cfg::LDS];
   const int lane = threadIdx.x & 63;
-  const int wv = threadIdx.x >> 6;
-  const int row = blockIdx.x;
-  int e_beg = 0, e_end = 0;
-  if (E > 0) {
-    e_beg = min(max(row_ptr[row], 0), E);
-    e_end = min(max(row_ptr[row + 1], e_beg), E);
-  }
-  float* slice = lds + wv * Cfg::SLICE;
-  float* ystg = Cfg::STG_IN_SLICE ? slice : lds + Cfg::NW * Cfg::SLICE + wv * Cfg::STG;
-  int* sstg = reinterpret_cast<int*>(ystg + 64 * 16);
+  float* ystg = lds;
+  int* sstg = reinterpret_cast<int*>(lds + 64 * 16);
   int cnt_acc = 0;
   long long sum_acc = 0;
-  auto stage = [&](int cb, int cnt) {
-    const bool valid = lane < cnt;
-    const int e = cb + (valid ? lane : 0);
+  auto stage = [&](bool valid, float, float, float, int s) {
     ystg[lane * 16] = valid ? 1.0f : 0.0f;  // the "harmonic" flags real slots
-    sstg[lane] = clamp_index(src[e], N);
+    sstg[lane] = s;
   };
   struct StepData {
     bool real;
     int s;
   };
-  auto load = [&](int el) { return StepData{ystg[el * 16] != 0.0f, sstg[el]}; };
+  auto load = [&](int el, bool live) { return StepData{live && ystg[el * 16] != 0.0f, sstg[el]}; };
   auto compute = [&](const StepData& d) {
     if ((lane & 15) == 0 && d.real) {
       cnt_acc += 1;
       sum_acc += d.s;
     }
   };
-  node_row_walk(e_beg, e_end, stage, load, compute);
-  // lanes 0, 16, 32, 48 hold partial results; fold them
-  for (int off = 16; off < 64; off <<= 1) {
-    cnt_acc += __shfl_xor(cnt_acc, off);
-    sum_acc += __shfl_xor(sum_acc, off);
-  }
-  if (wv == 0 && lane == 0) {
-    count[row] = cnt_acc;
-    src_sum[row] = sum_acc;
-  }
+  auto task_end = [&](int row, int blk) {
+    // lanes 0, 16, 32, 48 hold partial results; fold them
+    for (int off = 16; off < 64; off <<= 1) {
+      cnt_acc += __shfl_xor(cnt_acc, off);
+      sum_acc += __shfl_xor(sum_acc, off);
+    }
+    if (blk == 0 && lane == 0) {
+      count[row] = cnt_acc;
+      src_sum[row] = sum_acc;
+    }
+    cnt_acc = 0;
+    sum_acc = 0;
+  };
+  node_tasks<Cfg::PF, Cfg::NBLK, true>(N, E, row_ptr, vec, src, stage, load, compute, task_end);
+}
+
+static int num_cus() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 256;
+  return n;
+}
+
+// persistent single-wave workgroups: two per SIMD
+template <int L, int C>
+static unsigned node_grid(int64_t N) {
+  const int64_t tasks = N * NodeCfg<L, C>::NBLK;
+  const int64_t g = (int64_t)num_cus() * 8;
+  return (unsigned)(tasks < g ? tasks : g);
 }
 
 template <int L, int PS, int C>
 static hipError_t launch_node(const ConvArgs& a) {
   using Cfg = NodeCfg<L, C>;
   if (a.N == 0) return hipSuccess;
-  hipLaunchKernelGGL((conv_node_kernel<L, PS, C>), dim3((unsigned)a.N), dim3(Cfg::THREADS), 0, a.stream, (int)a.N,
-                     (int)a.E, a.row_ptr, a.vec, a.src, a.x, a.w, a.out);
+  const bool buf = (uint64_t)a.N * C * Cfg::K * 4u <= kMaxBufferBytes && (uint64_t)a.E * 12u <= kMaxBufferBytes;
+  if (buf)
+    hipLaunchKernelGGL((conv_node_kernel<L, PS, C, true>), dim3(node_grid<L, C>(a.N)), dim3(Cfg::THREADS), 0,
+                       a.stream, (int)a.N, (int)a.E, a.row_ptr, a.vec, a.src, a.x, a.w, a.out);
+  else
+    hipLaunchKernelGGL((conv_node_kernel<L, PS, C, false>), dim3(node_grid<L, C>(a.N)), dim3(Cfg::THREADS), 0,
+                       a.stream, (int)a.N, (int)a.E, a.row_ptr, a.vec, a.src, a.x, a.w, a.out);
   return hipGetLastError();
 }
 
@@ -278,8 +402,8 @@ template <int L, int C>
 static hipError_t launch_probe_node(const ProbeArgs& a) {
   using Cfg = NodeCfg<L, C>;
   if (a.N == 0) return hipSuccess;
-  hipLaunchKernelGGL((probe_node_kernel<L, C>), dim3((unsigned)a.N), dim3(Cfg::THREADS), 0, a.stream, (int)a.N,
-                     (int)a.E, a.row_ptr, a.src, a.count, a.src_sum);
+  hipLaunchKernelGGL((probe_node_kernel<L, C>), dim3(node_grid<L, C>(a.N)), dim3(Cfg::THREADS), 0, a.stream,
+                     (int)a.N, (int)a.E, a.row_ptr, (const float*)nullptr, a.src, a.count, a.src_sum);
   return hipGetLastError();
 }
 

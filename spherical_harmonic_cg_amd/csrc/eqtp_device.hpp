@@ -177,6 +177,30 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// ---------------------------------------------------------------------------
+// Raw buffer loads.  A load whose byte offset falls outside the resource
+// returns zeros without touching memory, so masked loads need no branch and
+// the compiler can count outstanding loads statically (which a branch around
+// each load prevents).  Resources cover < 4 GiB; callers check the size.
+// ---------------------------------------------------------------------------
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t kOutOfRange = 0xFFFFFFF0u;   // any offset at or past the end reads as zero
+constexpr uint64_t kMaxBufferBytes = 0xFFFF0000ull;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint64_t bytes) {
+  // word 3 of a gfx9 buffer resource: 32-bit data format, no swizzle
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)(uint32_t)bytes, 0x00020000);
+}
+__device__ __forceinline__ f4 buf_f4(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+__device__ __forceinline__ float buf_f32(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+}
+__device__ __forceinline__ int buf_i32(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(int, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+}
+
 // Round-to-nearest-even float -> bfloat16.
 __device__ __forceinline__ __bf16 to_bf16(float f) { return (__bf16)f; }
 

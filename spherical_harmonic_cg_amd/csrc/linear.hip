@@ -2,143 +2,266 @@
 // on the matrix cores (the one dense contraction of the path).
 //
 // A workgroup (4 waves) takes 16 consecutive nodes -- one contiguous
-// 16*C*K-float block of h -- loads it coalesced and stores it in LDS
-// transposed to [m][node][c].  Work items are (component m, 16-row tile of
-// output channels); for each, the 16x16 output tile D[c'][node] is
-//   fp32 mode: sum over 16-channel blocks of 4 v_mfma_f32_16x16x4_f32, lane
-//              (i = l%16, k = l/16) supplying W[c'0+i][ci0+4k+s] and
-//              h[node i][ci0+4k+s][m] for s = 0..3 (one 16-byte read each);
-//   bf16 mode: sum over 32-channel blocks of v_mfma_f32_16x16x32_bf16 with
-//              8 consecutive input channels per lane, both operands rounded
-//              to bfloat16 (nearest even) as they are loaded.
-// Results wait in registers until every wave is done with the input tile,
-// then go through LDS (reusing it) to a coalesced store.  Bytes per node:
-// 8 C K (read h, write out); flops 2 C^2 K: bound by HBM bandwidth.
+// 16*C*K-float block of h.  It stages, in the operand type (bf16 or fp32):
+//   * W as [l][c'][c] with rows padded so that the 16-byte operand reads of
+//     16 consecutive rows fall in distinct LDS banks (when it fits in LDS;
+//     otherwise the A operands are read from global memory, L2-resident);
+//   * the h tile transposed to [m][node][c] (two channels per thread, plane
+//     stride padded to spread the m-planes of a store over banks).
+// Work units are (4 consecutive components m, 16 output channels); for each,
+// the 16x16 tiles D[c'][node] come from v_mfma_f32_16x16x32_bf16 (bf16 mode:
+// operands rounded to nearest-even bf16 when staged, fp32 accumulation) or
+// v_mfma_f32_16x16x4_f32 (fp32 mode).  Lane (i, k) holds D[c'0+4k+v][node i]
+// for the four m of the unit, i.e. out[node i][c'][m..m+3].  When every wave
+// is done, the (dead) input staging is reused as the fp32 output tile in the
+// global layout and the tile leaves with coalesced 16-byte stores.  Bytes per
+// node: 8 C K (h once, out once); flops 2 C^2 K: bound by HBM bandwidth.
 #include "eqtp_device.hpp"
 #include "eqtp_kernels.hpp"
 
 namespace eqtp {
 
+template <bool BF16>
+struct LinOp;
+template <>
+struct LinOp<true> {
+  typedef __bf16 T;
+  static constexpr int KSTEP = 32;  // input channels per MFMA
+  static constexpr int PAD = 8;     // row padding (elements): 16 bytes
+};
+template <>
+struct LinOp<false> {
+  typedef float T;
+  static constexpr int KSTEP = 16;  // four 16x16x4 MFMAs per 16 input channels
+  static constexpr int PAD = 4;
+};
+
 template <int L, int C, bool BF16>
 struct LinCfg {
+  using Op = LinOp<BF16>;
+  typedef typename Op::T T;
   static constexpr int K = num_comp(L);
-  static constexpr int TN = 16;                  // nodes per workgroup
-  static constexpr int CS = C + 4;               // LDS row stride (floats), 16-byte aligned
-  static constexpr int CT = (C + 15) / 16;       // output channel tiles
-  static constexpr int ITEMS = K * CT;
+  static constexpr int TN = 16;                      // nodes per workgroup (MFMA columns)
+  static constexpr int RS = C + Op::PAD;             // LDS row stride (elements)
+  static constexpr int ES = (int)sizeof(T);
+  // m-plane stride in 4-byte words: TN rows plus 4 words (keeps 16-byte alignment; planes 4 apart land
+  // 16 banks apart)
+  static constexpr int PLANE_W = (TN * RS * ES) / 4 + 4;
+  static constexpr int PLANE = PLANE_W * 4 / ES;     // in elements
+  static constexpr int H_ELEMS = K * PLANE;
+  static constexpr int W_ELEMS = (L + 1) * C * RS;
+  static constexpr int LDS_BYTES_FULL = (H_ELEMS + W_ELEMS) * ES;
+  static constexpr bool W_LDS = LDS_BYTES_FULL <= 160 * 1024;
+  static constexpr int NS = C * K + 4;              // output tile node stride (floats)
+  static constexpr int OUT_FLOATS = TN * NS;
+  static constexpr int LDS_ELEMS_IN = H_ELEMS + (W_LDS ? W_ELEMS : 0);
+  static constexpr int LDS_BYTES = LDS_ELEMS_IN * ES > OUT_FLOATS * 4 ? LDS_ELEMS_IN * ES : OUT_FLOATS * 4;
+  static constexpr int CT = (C + 15) / 16;           // 16-row output channel tiles
+  static constexpr int MQ = (K + 3) / 4;             // component quads
+  static constexpr int UNITS = MQ * CT;
   static constexpr int WAVES = 4;
-  static constexpr int IPW = (ITEMS + WAVES - 1) / WAVES;
-  static constexpr int LDS_IN = K * TN * CS;
-  static constexpr int LDS_OUT = TN * C * K;
-  static constexpr int LDS = LDS_IN > LDS_OUT ? LDS_IN : LDS_OUT;
-  static_assert(LDS * 4 <= 160 * 1024, "LDS budget");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+  static_assert(C % 8 == 0, "channels must be a multiple of 8");
 };
 
 __device__ __forceinline__ int l_of(int m) { return m >= 9 ? 3 : (m >= 4 ? 2 : (m >= 1 ? 1 : 0)); }
+
+template <class T>
+__device__ __forceinline__ T to_op(float f);
+template <>
+__device__ __forceinline__ __bf16 to_op<__bf16>(float f) { return to_bf16(f); }
+template <>
+__device__ __forceinline__ float to_op<float>(float f) { return f; }
 
 template <int L, int C, bool BF16>
 __global__ __launch_bounds__(256) void linear_kernel(int N, const float* __restrict__ h, const float* __restrict__ W,
                                                      float* __restrict__ out) {
   using Cfg = LinCfg<L, C, BF16>;
+  using Op = typename Cfg::Op;
+  typedef typename Cfg::T T;
   constexpr int K = Cfg::K;
   constexpr int TN = Cfg::TN;
-  constexpr int CS = Cfg::CS;
-  __shared__ __attribute__((aligned(16))) float lds[Cfg::LDS];
-  const int lane = threadIdx.x & 63;
-  const int wv = threadIdx.x >> 6;
+  constexpr int RS = Cfg::RS;
+  __shared__ __attribute__((aligned(16))) unsigned char lds_raw[Cfg::LDS_BYTES];
+  T* hT = reinterpret_cast<T*>(lds_raw);   // [K][PLANE]: plane m holds rows node*RS + c
+  T* Wl = hT + Cfg::H_ELEMS;               // [L+1][C][RS]
+  float* otile = reinterpret_cast<float*>(lds_raw);  // after the products: [node][NS] output tile
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
   const int n0 = blockIdx.x * TN;
   const int nv = min(TN, N - n0);
   const size_t base = (size_t)n0 * C * K;
 
-  // 1. tile load, transposed into lds[m][node][c]
-  for (int f = threadIdx.x; f < TN * C * K; f += 256) {
-    const int n = f / (C * K);
-    const int rem = f - n * (C * K);
-    const int c = rem / K;
-    const int m = rem - c * K;
-    lds[(m * TN + n) * CS + c] = n < nv ? h[base + f] : 0.0f;
+  // 1. stage W (once per workgroup) and the h tile: every global load is
+  //    issued before the first LDS store so their latencies overlap.
+  constexpr int WF4 = Cfg::W_LDS ? (L + 1) * C * C / 4 : 0;
+  constexpr int W_IT = (WF4 + 255) / 256;
+  constexpr int HU = (K % 4 == 0) ? TN * (C / 2) * (K / 4) : 0;  // (node, channel pair, m quad) units
+  constexpr int H_IT = (HU + 255) / 256;
+  f4 wbuf[W_IT > 0 ? W_IT : 1];
+  f4 ha[H_IT > 0 ? H_IT : 1], hb[H_IT > 0 ? H_IT : 1];
+#pragma unroll
+  for (int it = 0; it < W_IT; ++it) {
+    const int i = tid + it * 256;
+    wbuf[it] = i < WF4 ? reinterpret_cast<const f4*>(W)[i] : f4{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll
+  for (int it = 0; it < H_IT; ++it) {
+    const int u = tid + it * 256;
+    const int mq = u % (K / 4 > 0 ? K / 4 : 1);
+    const int cp = (u / (K / 4 > 0 ? K / 4 : 1)) % (C / 2);
+    const int n = u / ((K / 4 > 0 ? K / 4 : 1) * (C / 2));
+    ha[it] = hb[it] = f4{0.f, 0.f, 0.f, 0.f};
+    if (u < HU && n < nv) {
+      const float* src = h + base + ((size_t)n * C + 2 * cp) * K + 4 * mq;
+      ha[it] = *reinterpret_cast<const f4*>(src);
+      hb[it] = *reinterpret_cast<const f4*>(src + K);
+    }
+  }
+#pragma unroll
+  for (int it = 0; it < W_IT; ++it) {
+    const int i = tid + it * 256;
+    if (i < WF4) {
+      const int e = 4 * i;
+      const int row = e / C, c = e - row * C;  // row = l*C + c'
+      T* d = Wl + row * RS + c;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) d[j] = to_op<T>(wbuf[it][j]);
+    }
+  }
+#pragma unroll
+  for (int it = 0; it < H_IT; ++it) {
+    const int u = tid + it * 256;
+    if (u < HU) {
+      const int mq = u % (K / 4 > 0 ? K / 4 : 1);
+      const int cp = (u / (K / 4 > 0 ? K / 4 : 1)) % (C / 2);
+      const int n = u / ((K / 4 > 0 ? K / 4 : 1) * (C / 2));
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        T* d = hT + (4 * mq + q) * Cfg::PLANE + n * RS + 2 * cp;
+        d[0] = to_op<T>(ha[it][q]);
+        d[1] = to_op<T>(hb[it][q]);
+      }
+    }
+  }
+  if constexpr (K % 4 != 0) {
+    for (int f = tid; f < TN * C * K; f += 256) {
+      const int n = f / (C * K);
+      const int rem = f - n * (C * K);
+      const int c = rem / K;
+      const int m = rem - c * K;
+      hT[m * Cfg::PLANE + n * RS + c] = to_op<T>(n < nv ? h[base + f] : 0.0f);
+    }
   }
   __syncthreads();
 
-  // 2. matrix-core products; results held in registers
+  // 2. units (m quad, output tile) -> MFMA; results wait in registers
   const int i16 = lane & 15;
   const int kq = lane >> 4;
-  f4 res[Cfg::IPW];
+  constexpr int UPW = (Cfg::UNITS + Cfg::WAVES - 1) / Cfg::WAVES;  // units per wave
+  f4 res[UPW][4];
 #pragma unroll
-  for (int q = 0; q < Cfg::IPW; ++q) {
-    res[q] = f4{0.f, 0.f, 0.f, 0.f};
-    const int item = wv + q * Cfg::WAVES;
-    if (item < Cfg::ITEMS) {
-      const int m = item / Cfg::CT;
-      const int ct = item - m * Cfg::CT;
+  for (int uu = 0; uu < UPW; ++uu) {
+    const int unit = wv + uu * Cfg::WAVES;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) res[uu][q] = f4{0.f, 0.f, 0.f, 0.f};
+    if (unit >= Cfg::UNITS) continue;
+    const int mq = unit / Cfg::CT;
+    const int ct = unit - mq * Cfg::CT;
+    const int co = ct * 16 + i16;  // A row supplied by this lane
+    const bool co_ok = co < C;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int m = 4 * mq + q;
+      if (m >= K) continue;
       const int l = l_of(m);
-      const int co = ct * 16 + i16;  // output channel supplied by this lane (A rows)
-      const bool co_ok = co < C;
-      const float* wrow = W + ((size_t)l * C + (co_ok ? co : 0)) * C;
-      const float* hrow = lds + (m * TN + i16) * CS;
+      const T* hrow = hT + m * Cfg::PLANE + i16 * RS;
       f4 acc = f4{0.f, 0.f, 0.f, 0.f};
-      if constexpr (!BF16) {
-#pragma unroll
-        for (int ci0 = 0; ci0 < C; ci0 += 16) {
-          const int cb = ci0 + 4 * kq;
-          f4 a4 = f4{0.f, 0.f, 0.f, 0.f}, b4 = f4{0.f, 0.f, 0.f, 0.f};
-          if (cb < C) {
-            if (co_ok) a4 = *reinterpret_cast<const f4*>(wrow + cb);
-            b4 = *reinterpret_cast<const f4*>(hrow + cb);
-          }
-#pragma unroll
-          for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[s], b4[s], acc, 0, 0, 0);
-        }
-      } else {
+      if constexpr (BF16) {
 #pragma unroll
         for (int ci0 = 0; ci0 < C; ci0 += 32) {
           const int cb = ci0 + 8 * kq;
           bf16x8 a8, b8;
-          f4 a0 = f4{0.f, 0.f, 0.f, 0.f}, a1 = a0, b0 = a0, b1 = a0;
           if (cb < C) {
-            if (co_ok) {
-              a0 = *reinterpret_cast<const f4*>(wrow + cb);
-              a1 = *reinterpret_cast<const f4*>(wrow + cb + 4);
-            }
-            b0 = *reinterpret_cast<const f4*>(hrow + cb);
-            b1 = *reinterpret_cast<const f4*>(hrow + cb + 4);
-          }
+            b8 = *reinterpret_cast<const bf16x8*>(hrow + cb);
+            if constexpr (Cfg::W_LDS) {
+              a8 = *reinterpret_cast<const bf16x8*>(Wl + (l * C + (co_ok ? co : 0)) * RS + cb);
+            } else {
+              const float* wr = W + ((size_t)l * C + (co_ok ? co : 0)) * C + cb;
+              const f4 w0 = *reinterpret_cast<const f4*>(wr), w1 = *reinterpret_cast<const f4*>(wr + 4);
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            a8[j] = to_bf16(a0[j]);
-            a8[4 + j] = to_bf16(a1[j]);
-            b8[j] = to_bf16(b0[j]);
-            b8[4 + j] = to_bf16(b1[j]);
+              for (int j = 0; j < 4; ++j) {
+                a8[j] = to_bf16(w0[j]);
+                a8[4 + j] = to_bf16(w1[j]);
+              }
+            }
+            if (!co_ok) {
+#pragma unroll
+              for (int j = 0; j < 8; ++j) a8[j] = (__bf16)0.0f;
+            }
+          } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              a8[j] = (__bf16)0.0f;
+              b8[j] = (__bf16)0.0f;
+            }
           }
           acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a8, b8, acc, 0, 0, 0);
         }
+      } else {
+#pragma unroll
+        for (int ci0 = 0; ci0 < C; ci0 += 16) {
+          const int cb = ci0 + 4 * kq;
+          f4 a4 = f4{0.f, 0.f, 0.f, 0.f}, b4 = a4;
+          if (cb < C) {
+            b4 = *reinterpret_cast<const f4*>(hrow + cb);
+            if (co_ok) {
+              if constexpr (Cfg::W_LDS) a4 = *reinterpret_cast<const f4*>(Wl + (l * C + co) * RS + cb);
+              else a4 = *reinterpret_cast<const f4*>(W + ((size_t)l * C + co) * C + cb);
+            }
+          }
+#pragma unroll
+          for (int s4 = 0; s4 < 4; ++s4) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[s4], b4[s4], acc, 0, 0, 0);
+        }
       }
-      res[q] = acc;
+      res[uu][q] = acc;
+    }
+  }
+  __syncthreads();  // inputs are dead: the LDS now holds the output tile
+
+  // 3. lane (i16, kq): out[node i16][ct*16 + 4kq + v][4mq + q] = res[q][v] -> LDS tile (global layout,
+  //    node stride padded by 4 words so 8 lanes' 16-byte writes hit distinct banks)
+#pragma unroll
+  for (int uu = 0; uu < UPW; ++uu) {
+    const int unit = wv + uu * Cfg::WAVES;
+    if (unit >= Cfg::UNITS) continue;
+    const int mq = unit / Cfg::CT;
+    const int ct = unit - mq * Cfg::CT;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int c2 = ct * 16 + 4 * kq + v;
+      if (c2 >= C) continue;
+      float* op = otile + i16 * Cfg::NS + c2 * K + 4 * mq;
+      if constexpr (K % 4 == 0) {
+        *reinterpret_cast<f4*>(op) = f4{res[uu][0][v], res[uu][1][v], res[uu][2][v], res[uu][3][v]};
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (4 * mq + q < K) op[q] = res[uu][q][v];
+      }
     }
   }
   __syncthreads();
 
-  // 3. D[c' = ct*16 + 4 kq + v][node = i16] -> lds[node][c'][m] (global layout)
-#pragma unroll
-  for (int q = 0; q < Cfg::IPW; ++q) {
-    const int item = wv + q * Cfg::WAVES;
-    if (item < Cfg::ITEMS) {
-      const int m = item / Cfg::CT;
-      const int ct = item - m * Cfg::CT;
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int co = ct * 16 + 4 * kq + v;
-        if (co < C) lds[(i16 * C + co) * K + m] = res[q][v];
-      }
-    }
-  }
-  __syncthreads();
-
-  // 4. coalesced store of the valid nodes
-  const int nf4 = nv * C * K / 4;
+  // 4. coalesced 16-byte stores of the valid nodes
+  constexpr int CK4 = C * K / 4;
   f4* ob = reinterpret_cast<f4*>(out + base);
-  const f4* tb = reinterpret_cast<const f4*>(lds);
-  for (int i = threadIdx.x; i < nf4; i += 256) ob[i] = tb[i];
+  for (int i = tid; i < nv * CK4; i += 256) {
+    const int n = i / CK4;
+    const int j = i - n * CK4;
+    ob[i] = *reinterpret_cast<const f4*>(otile + n * Cfg::NS + 4 * j);
+  }
 }
 
 template <int L, int C, bool BF16>

@@ -182,11 +182,36 @@ def _finish(name, pos, box, src, dst, lmax, C, rng_feat, rng_w, rng_extra, path_
 CONFIG_NAMES = ("tiny", "typical", "mid", "large", "radial")
 
 
-def make_config(name: str, seed: int = 2026) -> Workload:
-    """Build one of the five named workloads (see the module docstring)."""
+def cell_order(pos: np.ndarray, box: float, cell: float) -> np.ndarray:
+    """Permutation that numbers atoms by the Morton (Z-order) index of their
+    cubic cell of side ~``cell`` -- a spatially coherent numbering."""
+    n_side = max(1, int(box // cell))
+    ijk = np.clip(np.floor(np.mod(pos, box) / (box / n_side)).astype(np.int64), 0, n_side - 1)
+    code = np.zeros(pos.shape[0], dtype=np.int64)
+    for bit in range(21):
+        for d in range(3):
+            code |= ((ijk[:, d] >> bit) & 1) << (3 * bit + d)
+    return np.argsort(code, kind="stable")
+
+
+def make_config(name: str, seed: int = 2026, atom_order: str = "generation") -> Workload:
+    """Build one of the five named workloads (see the module docstring).
+
+    ``atom_order="cell"`` renumbers the atoms of a periodic workload along a
+    Morton curve over cells of side 2 A before the graph is built (a
+    spatially coherent numbering, for comparison only); the default keeps the
+    generation order, in which atom numbers carry no spatial information."""
     k = CONFIG_NAMES.index(name) + 1
     ss = np.random.SeedSequence([seed, k]).spawn(4)
     rng_pos, rng_feat, rng_w, rng_extra = (np.random.default_rng(s) for s in ss)
+    if atom_order not in ("generation", "cell"):
+        raise ValueError(atom_order)
+
+    def place(n, box):
+        pos = rng_pos.uniform(0.0, box, size=(n, 3))
+        if atom_order == "cell":
+            pos = pos[cell_order(pos, box, 2.0)]
+        return pos
     if name == "tiny":
         n, box_side = 64, 6.0
         pos = rng_pos.uniform(0.0, box_side, size=(n, 3))
@@ -195,26 +220,26 @@ def make_config(name: str, seed: int = 2026) -> Workload:
     if name == "typical":
         n = 1000
         box = (n / DENSITY) ** (1.0 / 3.0)
-        pos = rng_pos.uniform(0.0, box, size=(n, 3))
+        pos = place(n, box)
         src, dst = knn_edges(pos, 20, box)
         return _finish(name, pos, box, src, dst, 3, 32, rng_feat, rng_w, rng_extra, linear=True)
     if name == "mid":
         n = 10000
         box = (n / DENSITY) ** (1.0 / 3.0)
-        pos = rng_pos.uniform(0.0, box, size=(n, 3))
+        pos = place(n, box)
         src, dst = radius_edges(pos, 4.0, box)
         return _finish(name, pos, box, src, dst, 3, 64, rng_feat, rng_w, rng_extra, r_cut=4.0, linear=True,
                        linear_bf16=True)
     if name == "large":
         n = 100000
         box = (n / DENSITY) ** (1.0 / 3.0)
-        pos = rng_pos.uniform(0.0, box, size=(n, 3))
+        pos = place(n, box)
         src, dst = radius_edges(pos, 5.0, box)
         return _finish(name, pos, box, src, dst, 3, 32, rng_feat, rng_w, rng_extra, r_cut=5.0)
     if name == "radial":
         n = 50000
         box = (n / DENSITY) ** (1.0 / 3.0)
-        pos = rng_pos.uniform(0.0, box, size=(n, 3))
+        pos = place(n, box)
         src, dst = radius_edges(pos, 5.0, box)
         return _finish(name, pos, box, src, dst, 3, 128, rng_feat, rng_w, rng_extra, r_cut=5.0, radial=True)
     raise KeyError(name)

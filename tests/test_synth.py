@@ -55,3 +55,15 @@ def test_num_paths():
     assert synth.num_paths(0, 0) == 1 and synth.num_paths(1, 0) == 4
     assert synth.num_paths(3, 0) == 23 and synth.num_paths(3, 1) == 34
     assert synth.num_paths(2, 0) == 11 and synth.num_paths(2, 1) == 15
+
+
+def test_cell_order_is_a_renumbering():
+    """The cell-sorted numbering is a permutation of the same atoms: same edge
+    count and the same sorted multiset of edge lengths."""
+    a = synth.make_config("typical")
+    b = synth.make_config("typical", atom_order="cell")
+    assert a.E == b.E
+    la = np.sort(np.linalg.norm(a.vec.astype(np.float64), axis=1))
+    lb = np.sort(np.linalg.norm(b.vec.astype(np.float64), axis=1))
+    np.testing.assert_allclose(la, lb, rtol=1e-6)
+    assert np.abs(b.src.astype(int) - b.dst).mean() < np.abs(a.src.astype(int) - a.dst).mean()
