@@ -63,7 +63,7 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def measured_traffic(config, atom_order, unsorted, algo):
+def measured_traffic(config, atom_order, unsorted, algo, path_set="parity"):
     """HBM-side bytes per launch of the conv kernel from the committed counter
     summary (profiles/traffic.json), or None when that summary was taken on
     different kernel sources or another workload."""
@@ -75,6 +75,8 @@ def measured_traffic(config, atom_order, unsorted, algo):
     except ValueError:
         return None
     key = "%s/%s/%s/%d" % (config, atom_order, "unsorted" if unsorted else "sorted", algo)
+    if path_set != "parity":
+        key += "/" + path_set
     ent = rec.get(key)
     if not ent or ent.get("source_sha256_16") != kernel_source_hash():
         return None
@@ -122,6 +124,8 @@ def main():
     ap.add_argument("--unsorted", action="store_true", help="random edge order (atomic path)")
     ap.add_argument("--atom-order", default="generation", choices=("generation", "cell"),
                     help="'cell': spatially coherent atom numbering (a labelled extra, not the headline)")
+    ap.add_argument("--path-set", default="parity", choices=("parity", "so3"),
+                    help="'so3': the 34-path SO(3) set (a labelled extra, not the headline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
     ap.add_argument("--calib-copy", action="store_true",
@@ -146,7 +150,8 @@ def main():
     torch.cuda.set_device(0)
 
     t_gen = time.perf_counter()
-    wl = synth.make_config(args.config, atom_order=args.atom_order)
+    wl = synth.make_config(args.config, atom_order=args.atom_order,
+                           path_set=1 if args.path_set == "so3" else 0)
     log("workload %s: N=%d E=%d C=%d lmax=%d P=%d (generated in %.1fs)" % (wl.name, wl.N, wl.E, wl.C, wl.lmax,
                                                                             wl.P, time.perf_counter() - t_gen))
     dev = torch.device("cuda:0")
@@ -218,7 +223,7 @@ def main():
     achieved_tflops = flop_edge * wl.E / conv_s / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved_tflops, 3), "peak": PEAK_FP32_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved_tflops / PEAK_FP32_TFLOPS, 4),
-                "traffic": measured_traffic(args.config, args.atom_order, args.unsorted, args.algo)}
+                "traffic": measured_traffic(args.config, args.atom_order, args.unsorted, args.algo, args.path_set)}
     alg_bytes = 2 * wl.N * wl.C * wl.K * 4 + wl.E * 16 + (wl.N + 1) * 4 + wl.weights.size * 4
     log("conv: %.3e counted flop (2*nnz*C per edge), %.1f MB algorithmic bytes -> %.1f GB/s" % (
         flop_edge * wl.E, alg_bytes / 1e6, alg_bytes / conv_s / 1e9))
@@ -242,7 +247,8 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": WORKLOAD_TEXT[args.config] + (" (random edge order)" if args.unsorted else "")
-                   + (" (cell-sorted atom numbering)" if args.atom_order == "cell" else ""),
+                   + (" (cell-sorted atom numbering)" if args.atom_order == "cell" else "")
+                   + (" (SO(3) path set)" if args.path_set == "so3" else ""),
                    "atoms": wl.N, "edges": wl.E, "channels": wl.C, "lmax": wl.lmax, "paths": wl.P,
                    "coupling_nnz": nnz, "algo": args.algo},
         "roofline": roofline,

@@ -178,21 +178,38 @@ __global__ __launch_bounds__(EdgeCfg<C>::THREADS) void conv_edge_kernel(int N, i
       }
     }
   } else {
+    // The wave's G messages (G*C*K = 64*CPL*K floats, one contiguous C*K
+    // block per edge) go through LDS so that atomic instruction i covers
+    // floats 64i .. 64i+63: 256 contiguous bytes (two cache lines) instead of
+    // one float per 64-byte channel row.
+    constexpr int MSG = C * K;               // floats per edge message
+    constexpr int NI = Cfg::CPL * K;         // atomic instructions per wave and round
+    __shared__ float xch[Cfg::WAVES][kWave * NI];
+    __shared__ int xdst[Cfg::WAVES][Cfg::G];
+    float* const xw = xch[wv];
     const long long base = ((long long)blockIdx.x * Cfg::WAVES + wv) * Cfg::EPW;
     const int e_end = (int)min((long long)E, base + Cfg::EPW);
-    for (int e = (int)base + g; e < e_end; e += Cfg::G) {
+    for (int e0 = (int)base; e0 < e_end; e0 += Cfg::G) {  // wave-uniform rounds of G edges
+      const int e = e0 + g;
+      const bool valid = e < e_end;
 #pragma unroll
       for (int j = 0; j < Cfg::CPL; ++j)
 #pragma unroll
         for (int k = 0; k < K; ++k) acc[j][k] = 0.0f;
-      M::run(e, N, cl, vec, src, x, w, wreg, inv_rc, acc);
-      const int d = clamp_index(dst[e], N);
+      if (valid) M::run(e, N, cl, vec, src, x, w, wreg, inv_rc, acc);
 #pragma unroll
-      for (int j = 0; j < Cfg::CPL; ++j) {
-        float* op = out + ((size_t)d * C + cl + j * Cfg::CL) * K;
+      for (int j = 0; j < Cfg::CPL; ++j)
 #pragma unroll
-        for (int k = 0; k < K; ++k) unsafeAtomicAdd(op + k, acc[j][k]);  // hardware fp32 atomic (coarse-grained memory)
+        for (int k = 0; k < K; ++k) xw[(g * C + cl + j * Cfg::CL) * K + k] = acc[j][k];
+      if (cl == 0) xdst[wv][g] = valid ? clamp_index(dst[e], N) : -1;  // -1: no edge in this slot
+      wave_lds_sync();
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int f = kWave * i + lane;      // float index in the wave's messages
+        const int d = xdst[wv][f / MSG];
+        if (d >= 0) unsafeAtomicAdd(out + (size_t)d * MSG + f % MSG, xw[f]);  // hardware fp32 atomic
       }
+      wave_lds_sync();
     }
   }
 }

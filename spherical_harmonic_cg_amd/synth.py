@@ -194,13 +194,15 @@ def cell_order(pos: np.ndarray, box: float, cell: float) -> np.ndarray:
     return np.argsort(code, kind="stable")
 
 
-def make_config(name: str, seed: int = 2026, atom_order: str = "generation") -> Workload:
+def make_config(name: str, seed: int = 2026, atom_order: str = "generation", path_set: int = 0) -> Workload:
     """Build one of the five named workloads (see the module docstring).
 
     ``atom_order="cell"`` renumbers the atoms of a periodic workload along a
     Morton curve over cells of side 2 A before the graph is built (a
     spatially coherent numbering, for comparison only); the default keeps the
-    generation order, in which atom numbers carry no spatial information."""
+    generation order, in which atom numbers carry no spatial information.
+    ``path_set=1`` draws the path weights for the 34-path SO(3) set instead of
+    the 23 parity-respecting paths (lmax 3; same graph and features)."""
     k = CONFIG_NAMES.index(name) + 1
     ss = np.random.SeedSequence([seed, k]).spawn(4)
     rng_pos, rng_feat, rng_w, rng_extra = (np.random.default_rng(s) for s in ss)
@@ -216,32 +218,33 @@ def make_config(name: str, seed: int = 2026, atom_order: str = "generation") -> 
         n, box_side = 64, 6.0
         pos = rng_pos.uniform(0.0, box_side, size=(n, 3))
         src, dst = radius_edges_bruteforce(pos, 3.0, None)
-        return _finish(name, pos, None, src, dst, 2, 8, rng_feat, rng_w, rng_extra, r_cut=3.0)
+        return _finish(name, pos, None, src, dst, 2, 8, rng_feat, rng_w, rng_extra, r_cut=3.0, path_set=path_set)
     if name == "typical":
         n = 1000
         box = (n / DENSITY) ** (1.0 / 3.0)
         pos = place(n, box)
         src, dst = knn_edges(pos, 20, box)
-        return _finish(name, pos, box, src, dst, 3, 32, rng_feat, rng_w, rng_extra, linear=True)
+        return _finish(name, pos, box, src, dst, 3, 32, rng_feat, rng_w, rng_extra, linear=True, path_set=path_set)
     if name == "mid":
         n = 10000
         box = (n / DENSITY) ** (1.0 / 3.0)
         pos = place(n, box)
         src, dst = radius_edges(pos, 4.0, box)
         return _finish(name, pos, box, src, dst, 3, 64, rng_feat, rng_w, rng_extra, r_cut=4.0, linear=True,
-                       linear_bf16=True)
+                       linear_bf16=True, path_set=path_set)
     if name == "large":
         n = 100000
         box = (n / DENSITY) ** (1.0 / 3.0)
         pos = place(n, box)
         src, dst = radius_edges(pos, 5.0, box)
-        return _finish(name, pos, box, src, dst, 3, 32, rng_feat, rng_w, rng_extra, r_cut=5.0)
+        return _finish(name, pos, box, src, dst, 3, 32, rng_feat, rng_w, rng_extra, r_cut=5.0, path_set=path_set)
     if name == "radial":
         n = 50000
         box = (n / DENSITY) ** (1.0 / 3.0)
         pos = place(n, box)
         src, dst = radius_edges(pos, 5.0, box)
-        return _finish(name, pos, box, src, dst, 3, 128, rng_feat, rng_w, rng_extra, r_cut=5.0, radial=True)
+        return _finish(name, pos, box, src, dst, 3, 128, rng_feat, rng_w, rng_extra, r_cut=5.0, radial=True,
+                       path_set=path_set)
     raise KeyError(name)
 
 
