@@ -69,6 +69,12 @@ def _load():
             lib.oracle_round_bf16.restype = ctypes.c_float
             lib.oracle_linear.argtypes = [i64, i32, i32, i32, vp, vp, vp]
             lib.oracle_linear.restype = i32
+            lib.oracle_sh_grad_f64.argtypes = [i64, vp, i32, vp, vp]
+            lib.oracle_sh_grad_f64.restype = i32
+            lib.oracle_conv_backward.argtypes = [i64, i64, i32, i32, i32] + [vp] * 9
+            lib.oracle_conv_backward.restype = i32
+            lib.oracle_conv_backward_f64.argtypes = [i64, i64, i32, i32, i32] + [vp] * 9
+            lib.oracle_conv_backward_f64.restype = i32
             _lib = lib
     return _lib
 
@@ -208,3 +214,44 @@ def linear(h, W, lmax: int, bf16: bool = False) -> np.ndarray:
     if lib.oracle_linear(N, C, lmax, 1 if bf16 else 0, _p(hh), _p(WW), _p(out)) != 0:
         raise ValueError("oracle_linear failed")
     return out
+
+
+def sh_grad(vec, lmax: int):
+    """(Y [E, K], G [E, K, 3]) from the polynomial route of oracle_sh_grad_f64:
+    the harmonics again and their gradient with respect to the edge vector."""
+    lib = _load()
+    v = _f64(vec).reshape(-1, 3)
+    K = (lmax + 1) ** 2
+    Y = np.empty((v.shape[0], K), dtype=np.float64)
+    G = np.empty((v.shape[0], K, 3), dtype=np.float64)
+    if lib.oracle_sh_grad_f64(v.shape[0], _p(v), lmax, _p(Y), _p(G)) != 0:
+        raise ValueError("oracle_sh_grad_f64: bad arguments")
+    return Y, G
+
+
+def conv_backward(N, vec, src, dst, x, w, gout, lmax, path_set=PATHS_PARITY):
+    """(gx [N,C,K], gw [P,C], gvec [E,3]) fp64: gradients of sum(gout * out)
+    for the fixed-weight convolution (see oracle_conv_backward in the C source).
+
+    float64 ``x`` selects the double entry point (vec, w, gout taken as float64)."""
+    lib = _load()
+    is64 = np.asarray(x).dtype == np.float64
+    cast = _f64 if is64 else _f32
+    v = cast(vec).reshape(-1, 3)
+    s = _i32(src)
+    d = _i32(dst)
+    xx, ww, gg = cast(x), cast(w), cast(gout)
+    E = v.shape[0]
+    C = xx.shape[1]
+    K = (lmax + 1) ** 2
+    P = paths(lmax, path_set).shape[0]
+    if xx.shape != (N, C, K) or gg.shape != (N, C, K) or ww.shape != (P, C) or s.shape != (E,) or d.shape != (E,):
+        raise ValueError("shape mismatch")
+    gx = np.empty((N, C, K), dtype=np.float64)
+    gw = np.empty((P, C), dtype=np.float64)
+    gv = np.empty((E, 3), dtype=np.float64)
+    fn = lib.oracle_conv_backward_f64 if is64 else lib.oracle_conv_backward
+    rc = fn(N, E, lmax, C, path_set, _p(v), _p(s), _p(d), _p(xx), _p(ww), _p(gg), _p(gx), _p(gw), _p(gv))
+    if rc != 0:
+        raise ValueError("oracle_conv_backward failed (rc=%d)" % rc)
+    return gx, gw, gv

@@ -363,6 +363,207 @@ int oracle_conv(int64_t N, int64_t E, int lmax, int C, int path_set, int weight_
 }
 
 /* ------------------------------------------------------------------------ */
+/* Gradients of the convolution (fixed weights)                              */
+/* ------------------------------------------------------------------------ */
+
+/* Coefficients a[0..l] of the Legendre polynomial P_l(z) = sum_k a_k z^k from
+ * the explicit sum P_l(z) = 2^-l sum_j (-1)^j C(l,j) C(2l-2j,l) z^(l-2j). */
+static void legendre_coeffs(int l, double* a) {
+  for (int k = 0; k <= l; ++k) a[k] = 0.0;
+  for (int j = 0; 2 * j <= l; ++j) {
+    double c = fact(l) / (fact(j) * fact(l - j)) * fact(2 * l - 2 * j) / (fact(l) * fact(l - 2 * j));
+    a[l - 2 * j] += ((j & 1) ? -c : c) / pow(2.0, (double)l);
+  }
+}
+
+/* m-th derivative of P_l at z (zero for m > l). */
+static double legendre_deriv(int l, int m, double z) {
+  double a[OR_MAX_L + 2];
+  if (m > l) return 0.0;
+  legendre_coeffs(l, a);
+  double v = 0.0;
+  for (int k = l; k >= m; --k) {
+    double c = a[k];
+    for (int i = 0; i < m; ++i) c *= (double)(k - i); /* d^m/dz^m z^k */
+    v = v * z + c;
+  }
+  /* Horner above ran over k = l..m with powers shifted by m */
+  return v;
+}
+
+/* Real spherical harmonics and their gradient with respect to the (not
+ * normalised) vector v, by a second route independent of real_sh: on the unit
+ * sphere u = v/|v| = (x, y, z),
+ *   Y_l0     = N_l0 P_l(z),
+ *   Y_lm,c/s = sqrt2 N_lm (-1)^m P_l^(m)(z) Re/Im (x + i y)^m,   m = 1..l,
+ * (P_l^(m): m-th derivative of the Legendre polynomial; (-1)^m is the
+ * Condon-Shortley phase).  These are polynomials in (x, y, z); their gradient
+ * g_u is taken componentwise and projected on the sphere's tangent plane:
+ * dY/dv = (g_u - u (u . g_u)) / |v|.  G[k*3 + a] = dY_k/dv_a.  A zero vector
+ * gives Y = (Y00, 0, ...) and G = 0 (Y is constant there by the reading of
+ * the zero-length edge). */
+static void real_sh_grad(int lmax, double vx, double vy, double vz, double* Y, double* G) {
+  int K = (lmax + 1) * (lmax + 1);
+  for (int k = 0; k < K; ++k) {
+    Y[k] = 0.0;
+    G[3 * k] = G[3 * k + 1] = G[3 * k + 2] = 0.0;
+  }
+  Y[0] = sqrt(1.0 / (4.0 * M_PI));
+  double r = sqrt(vx * vx + vy * vy + vz * vz);
+  if (r == 0.0) return;
+  double u[3] = {vx / r, vy / r, vz / r};
+  double A[OR_MAX_L + 1], B[OR_MAX_L + 1]; /* (x + i y)^m = A_m + i B_m */
+  A[0] = 1.0;
+  B[0] = 0.0;
+  for (int m = 1; m <= lmax; ++m) {
+    A[m] = u[0] * A[m - 1] - u[1] * B[m - 1];
+    B[m] = u[0] * B[m - 1] + u[1] * A[m - 1];
+  }
+  for (int l = 0; l <= lmax; ++l) {
+    for (int m = 0; m <= l; ++m) {
+      double n = sqrt((2.0 * l + 1.0) / (4.0 * M_PI) * fact(l - m) / fact(l + m));
+      double D = legendre_deriv(l, m, u[2]), D1 = legendre_deriv(l, m + 1, u[2]);
+      double fc, fs, gc[3], gs[3];
+      if (m == 0) {
+        fc = n * D;
+        gc[0] = 0.0;
+        gc[1] = 0.0;
+        gc[2] = n * D1;
+        fs = 0.0;
+        gs[0] = gs[1] = gs[2] = 0.0;
+      } else {
+        double pre = sqrt(2.0) * n * ((m & 1) ? -1.0 : 1.0);
+        fc = pre * D * A[m];
+        fs = pre * D * B[m];
+        /* d/dx (x+iy)^m = m (x+iy)^(m-1), d/dy (x+iy)^m = i m (x+iy)^(m-1) */
+        gc[0] = pre * D * m * A[m - 1];
+        gc[1] = -pre * D * m * B[m - 1];
+        gc[2] = pre * D1 * A[m];
+        gs[0] = pre * D * m * B[m - 1];
+        gs[1] = pre * D * m * A[m - 1];
+        gs[2] = pre * D1 * B[m];
+      }
+      for (int t = 0; t < 2; ++t) {
+        if (m == 0 && t == 1) break;
+        int k = comp_index(l, m, t);
+        double* g = t ? gs : gc;
+        Y[k] = t ? fs : fc;
+        double ug = u[0] * g[0] + u[1] * g[1] + u[2] * g[2];
+        for (int a = 0; a < 3; ++a) G[3 * k + a] = (g[a] - u[a] * ug) / r;
+      }
+    }
+  }
+}
+
+int oracle_sh_grad_f64(int64_t E, const double* vec, int lmax, double* Y, double* G) {
+  if (lmax < 0 || lmax > OR_MAX_L || E < 0) return 1;
+  int K = (lmax + 1) * (lmax + 1);
+  for (int64_t e = 0; e < E; ++e)
+    real_sh_grad(lmax, vec[3 * e], vec[3 * e + 1], vec[3 * e + 2], Y + e * K, G + e * K * 3);
+  return 0;
+}
+
+/* Gradients of L = sum_{n,c,k} gout[n,c,k] out[n,c,k] for the fixed-weight
+ * convolution (weight_mode 0) of oracle_conv_f64, written out from its
+ * definition term by term:
+ *   gx[s,c,l1 m1] = sum_{e: src_e = s} sum_p w[p,c] sum C^p[m1,m2,m3] Y_e[l2 m2] gout[dst_e,c,l3 m3]
+ *   gw[p,c]       = sum_e sum C^p[m1,m2,m3] x[src_e,c,l1 m1] Y_e[l2 m2] gout[dst_e,c,l3 m3]
+ *   gvec[e]       = sum_k dL/dY_e[k] * dY_k/dvec_e,
+ *   dL/dY_e[l2 m2] = sum_c sum_p w[p,c] sum C^p[m1,m2,m3] x[src_e,c,l1 m1] gout[dst_e,c,l3 m3].
+ * Y comes from real_sh (as in the forward), dY/dvec from real_sh_grad.
+ * Any of gx [N,C,K], gw [P,C], gvec [E,3] may be NULL; the others are
+ * overwritten.  Returns 0 on success. */
+int oracle_conv_backward_f64(int64_t N, int64_t E, int lmax, int C, int path_set, const double* vec,
+                             const int32_t* src, const int32_t* dst, const double* x, const double* w,
+                             const double* gout, double* gx, double* gw, double* gvec) {
+  if (lmax < 0 || lmax > OR_MAX_L || C <= 0 || N < 0 || E < 0) return 1;
+  int K = (lmax + 1) * (lmax + 1);
+  int P = oracle_paths(lmax, path_set, NULL);
+  if (P <= 0) return 1;
+  int32_t* paths = (int32_t*)malloc(sizeof(int32_t) * 3 * P);
+  oracle_paths(lmax, path_set, paths);
+  double** cg = (double**)malloc(sizeof(double*) * P);
+  for (int p = 0; p < P; ++p) {
+    int l1 = paths[3 * p], l2 = paths[3 * p + 1], l3 = paths[3 * p + 2];
+    cg[p] = (double*)malloc(sizeof(double) * (2 * l1 + 1) * (2 * l2 + 1) * (2 * l3 + 1));
+    oracle_cg_real(l1, l2, l3, cg[p], NULL);
+  }
+  if (gx)
+    for (int64_t i = 0; i < N * C * K; ++i) gx[i] = 0.0;
+  if (gw)
+    for (int64_t i = 0; i < (int64_t)P * C; ++i) gw[i] = 0.0;
+  double* Y = (double*)malloc(sizeof(double) * K);
+  double* Y2 = (double*)malloc(sizeof(double) * K);
+  double* G = (double*)malloc(sizeof(double) * K * 3);
+  double* dY = (double*)malloc(sizeof(double) * K);
+  int rc = 0;
+  for (int64_t e = 0; e < E; ++e) {
+    int64_t s = src[e], d = dst[e];
+    if (s < 0 || s >= N || d < 0 || d >= N) {
+      rc = 2;
+      break;
+    }
+    double vx = vec[3 * e], vy = vec[3 * e + 1], vz = vec[3 * e + 2];
+    real_sh(lmax, vx, vy, vz, Y);
+    real_sh_grad(lmax, vx, vy, vz, Y2, G);
+    for (int k = 0; k < K; ++k) dY[k] = 0.0;
+    for (int p = 0; p < P; ++p) {
+      int l1 = paths[3 * p], l2 = paths[3 * p + 1], l3 = paths[3 * p + 2];
+      int n1 = 2 * l1 + 1, n2 = 2 * l2 + 1, n3 = 2 * l3 + 1;
+      for (int a = 0; a < n1; ++a)
+        for (int b = 0; b < n2; ++b)
+          for (int c3 = 0; c3 < n3; ++c3) {
+            double coef = cg[p][(a * n2 + b) * n3 + c3];
+            if (coef == 0.0) continue;
+            for (int ch = 0; ch < C; ++ch) {
+              double xv = x[(s * C + ch) * K + l1 * l1 + a];
+              double gv = gout[(d * C + ch) * K + l3 * l3 + c3];
+              double wv = w[p * C + ch];
+              double yv = Y[l2 * l2 + b];
+              if (gx) gx[(s * C + ch) * K + l1 * l1 + a] += wv * coef * yv * gv;
+              if (gw) gw[p * C + ch] += coef * xv * yv * gv;
+              dY[l2 * l2 + b] += wv * coef * xv * gv;
+            }
+          }
+    }
+    if (gvec)
+      for (int a = 0; a < 3; ++a) {
+        double acc = 0.0;
+        for (int k = 0; k < K; ++k) acc += dY[k] * G[3 * k + a];
+        gvec[3 * e + a] = acc;
+      }
+  }
+  free(Y);
+  free(Y2);
+  free(G);
+  free(dY);
+  for (int p = 0; p < P; ++p) free(cg[p]);
+  free(cg);
+  free(paths);
+  return rc;
+}
+
+/* float32 entry point: inputs widened exactly to double. */
+int oracle_conv_backward(int64_t N, int64_t E, int lmax, int C, int path_set, const float* vec,
+                         const int32_t* src, const int32_t* dst, const float* x, const float* w,
+                         const float* gout, double* gx, double* gw, double* gvec) {
+  if (lmax < 0 || lmax > OR_MAX_L || C <= 0 || N < 0 || E < 0) return 1;
+  int K = (lmax + 1) * (lmax + 1);
+  int P = oracle_paths(lmax, path_set, NULL);
+  if (P <= 0) return 1;
+  double* v = widen(vec, 3 * E);
+  double* xx = widen(x, N * C * K);
+  double* ww = widen(w, (int64_t)P * C);
+  double* gg = widen(gout, N * C * K);
+  int rc = oracle_conv_backward_f64(N, E, lmax, C, path_set, v, src, dst, xx, ww, gg, gx, gw, gvec);
+  free(v);
+  free(xx);
+  free(ww);
+  free(gg);
+  return rc;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Per-l channel linear                                                      */
 /* ------------------------------------------------------------------------ */
 

@@ -1,0 +1,130 @@
+"""Pins for the oracle's gradients of the convolution (CPU only).
+
+The gradient formulas in oracle_conv_backward are checked against facts that
+do not use them:
+  * the harmonics gradient against central differences of the forward
+    harmonics (a different route: Legendre functions and atan2), against
+    tangency (Y depends on the direction only) and 1/|v| scaling;
+  * dL/dx by the adjoint identity: L is linear in x, so <gx, dx> equals
+    <gout, conv(dx)> exactly for any dx;
+  * dL/dw by linearity in w the same way;
+  * dL/dvec by central differences of the forward oracle in fp64.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from spherical_harmonic_cg_amd import synth
+
+
+def _L(N, vec, src, dst, x, w, gout, lmax, ps):
+    out = oracle.conv(N, vec, src, dst, x, w, lmax, path_set=ps)
+    return float(np.sum(gout * out))
+
+
+def _case(lmax, ps, seed, C=3, n=7, deg=4, zero_vec_edges=0):
+    wl = synth.small_graph(n, deg, C, lmax, seed, path_set=ps, zero_vec_edges=zero_vec_edges)
+    rng = np.random.default_rng(seed + 101)
+    f64 = lambda a: np.asarray(a, dtype=np.float64)
+    gout = rng.standard_normal((wl.N, C, (lmax + 1) ** 2))
+    return wl.N, f64(wl.vec), wl.src, wl.dst, f64(wl.x), f64(wl.w), gout
+
+
+@pytest.mark.parametrize("lmax", [0, 1, 2, 3])
+def test_sh_grad_second_route_values(lmax):
+    rng = np.random.default_rng(3)
+    v = np.concatenate([rng.standard_normal((40, 3)) * rng.uniform(0.1, 5.0, (40, 1)),
+                        np.array([[0, 0, 2.0], [0, 0, -1.5], [3.0, 0, 0], [0, -1, 0]])])
+    Y, _ = oracle.sh_grad(v, lmax)
+    np.testing.assert_allclose(Y, oracle.sh(v, lmax), rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("lmax", [1, 2, 3])
+def test_sh_grad_finite_differences(lmax):
+    rng = np.random.default_rng(5 + lmax)
+    v = rng.standard_normal((30, 3)) * rng.uniform(0.3, 4.0, (30, 1))
+    _, G = oracle.sh_grad(v, lmax)
+    h = 1e-6
+    for a in range(3):
+        d = np.zeros(3)
+        d[a] = h
+        fd = (oracle.sh(v + d, lmax) - oracle.sh(v - d, lmax)) / (2 * h)
+        np.testing.assert_allclose(G[:, :, a], fd, rtol=0, atol=2e-8 * max(1.0, np.abs(fd).max()))
+
+
+def test_sh_grad_tangent_and_scaling():
+    rng = np.random.default_rng(11)
+    v = rng.standard_normal((25, 3))
+    _, G = oracle.sh_grad(v, 3)
+    assert np.abs(np.einsum("eka,ea->ek", G, v)).max() < 1e-13
+    _, G2 = oracle.sh_grad(2.5 * v, 3)
+    np.testing.assert_allclose(G2, G / 2.5, rtol=0, atol=1e-13)
+
+
+def test_sh_grad_zero_vector():
+    Y, G = oracle.sh_grad(np.zeros((1, 3)), 3)
+    assert Y[0, 0] == pytest.approx(0.28209479177387814, abs=1e-16)
+    assert np.all(Y[0, 1:] == 0.0) and np.all(G == 0.0)
+
+
+@pytest.mark.parametrize("lmax,ps", [(1, 0), (2, 0), (3, 0), (2, 1), (3, 1)])
+def test_backward_x_adjoint(lmax, ps):
+    N, vec, src, dst, x, w, gout = _case(lmax, ps, 21 + lmax)
+    gx, _, _ = oracle.conv_backward(N, vec, src, dst, x, w, gout, lmax, ps)
+    rng = np.random.default_rng(7)
+    for _ in range(3):
+        dx = rng.standard_normal(x.shape)
+        lhs = float(np.sum(gx * dx))
+        rhs = _L(N, vec, src, dst, dx, w, gout, lmax, ps)
+        assert abs(lhs - rhs) <= 1e-12 * max(1.0, abs(rhs))
+
+
+@pytest.mark.parametrize("lmax,ps", [(1, 0), (3, 0), (3, 1)])
+def test_backward_w_linear(lmax, ps):
+    N, vec, src, dst, x, w, gout = _case(lmax, ps, 31 + lmax)
+    _, gw, _ = oracle.conv_backward(N, vec, src, dst, x, w, gout, lmax, ps)
+    rng = np.random.default_rng(8)
+    for _ in range(3):
+        dw = rng.standard_normal(w.shape)
+        lhs = float(np.sum(gw * dw))
+        rhs = _L(N, vec, src, dst, x, dw, gout, lmax, ps)
+        assert abs(lhs - rhs) <= 1e-12 * max(1.0, abs(rhs))
+
+
+@pytest.mark.parametrize("lmax,ps", [(1, 0), (2, 0), (3, 0), (3, 1)])
+def test_backward_vec_finite_differences(lmax, ps):
+    N, vec, src, dst, x, w, gout = _case(lmax, ps, 41 + lmax)
+    _, _, gv = oracle.conv_backward(N, vec, src, dst, x, w, gout, lmax, ps)
+    rng = np.random.default_rng(9)
+    h = 1e-5
+    for _ in range(3):
+        d = rng.standard_normal(vec.shape)
+        fd = (_L(N, vec + h * d, src, dst, x, w, gout, lmax, ps) - _L(N, vec - h * d, src, dst, x, w, gout, lmax, ps)) / (2 * h)
+        lhs = float(np.sum(gv * d))
+        assert abs(lhs - fd) <= 1e-7 * max(1.0, abs(fd))
+    # edge by edge: each edge's gradient moves only its own term
+    for e in range(0, vec.shape[0], max(1, vec.shape[0] // 5)):
+        for a in range(3):
+            d = np.zeros_like(vec)
+            d[e, a] = 1.0
+            fd = (_L(N, vec + h * d, src, dst, x, w, gout, lmax, ps) - _L(N, vec - h * d, src, dst, x, w, gout, lmax, ps)) / (2 * h)
+            assert abs(gv[e, a] - fd) <= 1e-7 * max(1.0, abs(fd))
+
+
+def test_backward_zero_length_edge():
+    N, vec, src, dst, x, w, gout = _case(3, 0, 51, zero_vec_edges=2)
+    assert np.all(vec[:2] == 0.0)
+    gx, gw, gv = oracle.conv_backward(N, vec, src, dst, x, w, gout, 3, 0)
+    assert np.all(gv[:2] == 0.0)
+    dx = np.random.default_rng(1).standard_normal(x.shape)
+    assert abs(np.sum(gx * dx) - _L(N, vec, src, dst, dx, w, gout, 3, 0)) < 1e-11
+
+
+def test_backward_float32_entry_matches_widened():
+    wl = synth.small_graph(6, 5, 4, 3, 61)
+    gout = np.random.default_rng(2).standard_normal((wl.N, 4, 16)).astype(np.float32)
+    a = oracle.conv_backward(wl.N, wl.vec, wl.src, wl.dst, wl.x, wl.w, gout, 3)
+    b = oracle.conv_backward(wl.N, wl.vec.astype(np.float64), wl.src, wl.dst, wl.x.astype(np.float64),
+                             wl.w.astype(np.float64), gout.astype(np.float64), 3)
+    for u, v in zip(a, b):
+        assert np.array_equal(u, v)
