@@ -139,6 +139,33 @@ int eqtp_conv_fused(const eqtp_conv_desc* d, int64_t N, int64_t E, const float* 
                     void* stream);
 
 /*
+ * Gradients of the fused convolution with fixed weights: for a scalar loss L
+ * with grad_out = dL/dout,
+ *   grad_x[s, c, l1 m1] = sum_{e: src_e = s} sum_p w[p, c] sum_{m2, m3} C^p[m1, m2, m3] Y_{l2 m2}(vec_e)
+ *                         grad_out[dst_e, c, l3 m3]
+ *   grad_w[p, c]        = sum_e sum_{m1, m2, m3} C^p x[src_e, c, l1 m1] Y_{l2 m2}(vec_e) grad_out[dst_e, c, l3 m3]
+ *   grad_vec[e]         = sum_{l2 m2} dL/dY_{l2 m2}(vec_e) * dY_{l2 m2}/dvec_e
+ * (the forces of an interatomic potential are built from grad_vec; the page
+ * names a PyTorch autograd function with a backward as the integration path,
+ * section "extension possibilities").  A zero-length edge vector has
+ * grad_vec = 0.
+ *   d, N, E, vec, src, dst, row_ptr, x, weights: as for eqtp_conv_fused;
+ *            d->weight_mode must be EQTP_W_FIXED (radial weights:
+ *            EQTP_EUNSUPPORTED); d->algo is ignored.
+ *   grad_out [N, C, K] fp32.
+ *   grad_x   [N, C, K] fp32, 16-byte aligned, or NULL (not computed).
+ *   grad_w   [P, C] fp32, or NULL.
+ *   grad_vec [E, 3] fp32, or NULL.
+ * Each requested output is fully overwritten; outputs must not alias inputs
+ * or each other.  grad_x and grad_w are sums of fp32 atomics (their
+ * summation order varies from run to run); grad_vec is written once per
+ * edge.  Errors as for eqtp_conv_fused.
+ */
+int eqtp_conv_backward(const eqtp_conv_desc* d, int64_t N, int64_t E, const float* vec, const int32_t* src,
+                       const int32_t* dst, const int32_t* row_ptr, const float* x, const float* weights,
+                       const float* grad_out, float* grad_x, float* grad_w, float* grad_vec, void* stream);
+
+/*
  * Per-l channel linear (channel mixing inside each irrep, no bias):
  *   out[n, c', l m] = sum_c W[l, c', c] h[n, c, l m]
  *   h    [N, C, K] fp32, 16-byte aligned.

@@ -114,6 +114,50 @@ int eqtp_conv_fused(const eqtp_conv_desc* d, int64_t N, int64_t E, const float* 
   return status_of(use_node ? eqtp::launch_conv_node(a) : eqtp::launch_conv_edge(a));
 }
 
+int eqtp_conv_backward(const eqtp_conv_desc* d, int64_t N, int64_t E, const float* vec, const int32_t* src,
+                       const int32_t* dst, const int32_t* row_ptr, const float* x, const float* weights,
+                       const float* grad_out, float* grad_x, float* grad_w, float* grad_vec, void* stream) {
+  if (!d || d->struct_size != (int32_t)sizeof(eqtp_conv_desc)) return EQTP_EINVAL;
+  if (d->lmax < 0) return EQTP_EINVAL;
+  if (d->lmax > 3) return EQTP_EUNSUPPORTED;
+  if (d->path_set != EQTP_PATHS_PARITY && d->path_set != EQTP_PATHS_SO3) return EQTP_EINVAL;
+  if (d->weight_mode != EQTP_W_FIXED && d->weight_mode != EQTP_W_RADIAL) return EQTP_EINVAL;
+  if (d->edge_order != EQTP_EDGES_DST_SORTED && d->edge_order != EQTP_EDGES_UNSORTED) return EQTP_EINVAL;
+  if (d->C <= 0) return EQTP_EINVAL;
+  if (!valid_c(d->C)) return EQTP_EUNSUPPORTED;
+  if (d->weight_mode == EQTP_W_RADIAL) return EQTP_EUNSUPPORTED;
+  if (N < 0 || E < 0 || N > kMaxIndex || E > kMaxIndex) return EQTP_EINVAL;
+  if (E > 0 && N == 0) return EQTP_EINVAL;
+  if (!grad_x && !grad_w && !grad_vec) return EQTP_EINVAL;
+  if (grad_x && !aligned16(grad_x)) return EQTP_EINVAL;
+  if ((grad_w && !aligned4(grad_w)) || (grad_vec && !aligned4(grad_vec))) return EQTP_EINVAL;
+  if (!weights || !aligned4(weights)) return EQTP_EINVAL;
+  if (N > 0 && (!x || !grad_out || !aligned4(x) || !aligned4(grad_out))) return EQTP_EINVAL;
+  if (E > 0) {
+    if (!vec || !src || !aligned4(vec) || !aligned4(src)) return EQTP_EINVAL;
+    if (d->edge_order == EQTP_EDGES_UNSORTED && (!dst || !aligned4(dst))) return EQTP_EINVAL;
+  }
+  if (d->edge_order == EQTP_EDGES_DST_SORTED && N > 0 && (!row_ptr || !aligned4(row_ptr))) return EQTP_EINVAL;
+  eqtp::BwdArgs a;
+  a.N = N;
+  a.E = E;
+  a.lmax = d->lmax;
+  a.C = d->C;
+  a.path_set = d->path_set;
+  a.vec = vec;
+  a.src = src;
+  a.dst = d->edge_order == EQTP_EDGES_UNSORTED ? dst : nullptr;
+  a.row_ptr = d->edge_order == EQTP_EDGES_DST_SORTED ? row_ptr : nullptr;
+  a.x = x;
+  a.w = weights;
+  a.gout = grad_out;
+  a.gx = grad_x;
+  a.gw = grad_w;
+  a.gvec = grad_vec;
+  a.stream = (hipStream_t)stream;
+  return status_of(eqtp::launch_conv_backward(a));
+}
+
 int eqtp_linear(int64_t N, int C, int lmax, int dtype, const float* h, const float* W, float* out, void* stream) {
   if (lmax < 0 || C <= 0 || N < 0 || N > kMaxIndex) return EQTP_EINVAL;
   if (lmax > 3 || !valid_c(C)) return EQTP_EUNSUPPORTED;

@@ -1,0 +1,243 @@
+// conv_bwd.hip -- gradients of the fused convolution with fixed path weights,
+// evaluated edge by edge on the vector ALUs.
+//
+// Forward (Batmobile page, sections "2. register intermediate computation" and
+// "3. operator fusion", with the destination sum):
+//   out[n,c,mu3] = sum_{e: dst_e = n} sum_p w[p,c] sum_{mu1,mu2} C^p[mu1,mu2,mu3] x[src_e,c,mu1] Y_mu2(vec_e).
+// For L = sum gout * out, per edge e = (s -> d) and channel c:
+//   s1[p,mu1] = sum_{mu2,mu3} C^p Y[mu2] gout[d,c,mu3]
+//     -> grad_x[s,c,mu1] += w[p,c] s1,   grad_w[p,c] += x[s,c,mu1] s1
+//   s2[p,mu2] = sum_{mu1,mu3} C^p x[s,c,mu1] gout[d,c,mu3]
+//     -> dL/dY_e[mu2] += w[p,c] s2 (summed over channels)
+//   grad_vec[e] = sum_mu2 dL/dY_e[mu2] dY_mu2/dvec_e   (sh_grad_eval).
+// The two sums walk the constexpr coupling table in (path, mu1) and (path,
+// mu2) order so each partial sum is a contiguous run of immediates.
+//
+// Lane mapping as in the per-edge forward: lane = channel (C <= 64: 64/C edges
+// per round, one per lane group; C = 128: two channels per lane).
+//   * dst-sorted edges (row_ptr): one wavefront per destination row, so the
+//     row's gout block is read once;
+//   * unsorted edges (dst): each wave takes a contiguous run of edges.
+// grad_x is a scatter into sources: a round's per-lane contributions are
+// exchanged through LDS and added with fp32 atomics covering 256 contiguous
+// bytes per instruction.  grad_w is accumulated in registers over all the
+// wave's edges and added once per wave.  grad_vec is written per edge.
+#include "eqtp_device.hpp"
+#include "eqtp_kernels.hpp"
+
+namespace eqtp {
+
+template <int C>
+struct BwdCfg {
+  static constexpr int CPL = C > 64 ? C / 64 : 1;  // channels per lane
+  static constexpr int CL = C / CPL;               // lanes per edge group
+  static constexpr int G = kWave / CL;             // edge groups per wave
+  static constexpr int WAVES = 4;
+  static constexpr int THREADS = WAVES * kWave;
+  static constexpr int EPW = 16 * G;               // edges per wave, unsorted mode
+};
+
+template <int L, int PS, int C, bool SORTED>
+__global__ __launch_bounds__(BwdCfg<C>::THREADS) void conv_bwd_kernel(
+    int N, int E, const int* __restrict__ row_ptr, const float* __restrict__ vec, const int* __restrict__ src,
+    const int* __restrict__ dst, const float* __restrict__ x, const float* __restrict__ w,
+    const float* __restrict__ gout, float* __restrict__ gx, float* __restrict__ gw, float* __restrict__ gvec) {
+  using Cfg = BwdCfg<C>;
+  using T = Tables<L, PS>;
+  using O1 = TermOrder<L, PS, 1>;
+  using O2 = TermOrder<L, PS, 2>;
+  constexpr int K = num_comp(L);
+  constexpr int P = T::P;
+  constexpr int MSG = C * K;         // floats per node block
+  constexpr int NI = Cfg::CPL * K;   // atomic instructions per wave and round
+  __shared__ float xch[Cfg::WAVES][kWave * NI];
+  __shared__ int xsrc[Cfg::WAVES][Cfg::G];
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int g = lane / Cfg::CL;
+  const int cl = lane % Cfg::CL;
+  float* const xw = xch[wv];
+
+  float wreg[Cfg::CPL][P];
+  float gwacc[Cfg::CPL][P];
+#pragma unroll
+  for (int j = 0; j < Cfg::CPL; ++j)
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      wreg[j][p] = w[p * C + cl + j * Cfg::CL];
+      gwacc[j][p] = 0.0f;
+    }
+
+  float gv[Cfg::CPL][K];  // gout[d, channel, :]
+  auto load_g = [&](int d) {
+#pragma unroll
+    for (int j = 0; j < Cfg::CPL; ++j)
+#pragma unroll
+      for (int k = 0; k < K; ++k) gv[j][k] = gout[((size_t)d * C + cl + j * Cfg::CL) * K + k];
+  };
+
+  // one round: lane group g handles edge e (if valid)
+  auto round = [&](int e, bool valid) {
+    float mx[Cfg::CPL][K];
+    float dy[16];
+#pragma unroll
+    for (int j = 0; j < Cfg::CPL; ++j)
+#pragma unroll
+      for (int k = 0; k < K; ++k) mx[j][k] = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) dy[k] = 0.0f;
+    float Y[16], Gm[16][3];
+    int s = -1;
+    if (valid) {
+      s = clamp_index(src[e], N);
+      sh_grad_eval<L>(vec[3 * e], vec[3 * e + 1], vec[3 * e + 2], Y, Gm);
+      if constexpr (!SORTED) load_g(clamp_index(dst[e], N));
+#pragma unroll
+      for (int j = 0; j < Cfg::CPL; ++j) {
+        float xv[K];
+#pragma unroll
+        for (int k = 0; k < K; ++k) xv[k] = x[((size_t)s * C + cl + j * Cfg::CL) * K + k];
+        // (path, mu1) runs: grad_x and grad_w
+        float s1 = 0.0f;
+        static_for<0, T::NT>([&](auto jj) {
+          constexpr int q = decltype(jj)::value;
+          constexpr eqtp_gen::CgTerm tm = O1::term(q);
+          const float yg = Y[tm.mu2] * gv[j][tm.mu3];
+          s1 = O1::first(q) ? tm.c * yg : fmaf(tm.c, yg, s1);
+          if constexpr (O1::last(q)) {
+            mx[j][tm.mu1] = fmaf(wreg[j][tm.p], s1, mx[j][tm.mu1]);
+            gwacc[j][tm.p] = fmaf(xv[tm.mu1], s1, gwacc[j][tm.p]);
+          }
+        });
+        // (path, mu2) runs: dL/dY
+        float s2 = 0.0f;
+        static_for<0, T::NT>([&](auto jj) {
+          constexpr int q = decltype(jj)::value;
+          constexpr eqtp_gen::CgTerm tm = O2::term(q);
+          const float xg = xv[tm.mu1] * gv[j][tm.mu3];
+          s2 = O2::first(q) ? tm.c * xg : fmaf(tm.c, xg, s2);
+          if constexpr (O2::last(q)) dy[tm.mu2] = fmaf(wreg[j][tm.p], s2, dy[tm.mu2]);
+        });
+      }
+    }
+    // grad_x: exchange the round's contributions so that atomic instruction i
+    // adds floats 64i .. 64i+63 of the wave's G source blocks
+    if (gx != nullptr) {
+#pragma unroll
+      for (int j = 0; j < Cfg::CPL; ++j)
+#pragma unroll
+        for (int k = 0; k < K; ++k) xw[(g * C + cl + j * Cfg::CL) * K + k] = mx[j][k];
+      if (cl == 0) xsrc[wv][g] = s;  // -1: no edge in this slot
+      wave_lds_sync();
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int f = kWave * i + lane;
+        const int sd = xsrc[wv][f / MSG];
+        if (sd >= 0) unsafeAtomicAdd(gx + (size_t)sd * MSG + f % MSG, xw[f]);
+      }
+      wave_lds_sync();
+    }
+    // grad_vec: sum dL/dY over the group's channels (its CL lanes)
+    if (gvec != nullptr) {
+#pragma unroll
+      for (int off = 1; off < Cfg::CL; off <<= 1)
+#pragma unroll
+        for (int k = 0; k < K; ++k) dy[k] += __shfl_xor(dy[k], off);
+      if (valid && cl == 0) {
+        float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f;
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+          a0 = fmaf(dy[k], Gm[k][0], a0);
+          a1 = fmaf(dy[k], Gm[k][1], a1);
+          a2 = fmaf(dy[k], Gm[k][2], a2);
+        }
+        gvec[3 * (size_t)e] = a0;
+        gvec[3 * (size_t)e + 1] = a1;
+        gvec[3 * (size_t)e + 2] = a2;
+      }
+    }
+  };
+
+  if constexpr (SORTED) {
+    const int row = blockIdx.x * Cfg::WAVES + wv;
+    if (row >= N) return;
+    int e_beg = 0, e_end = 0;
+    if (E > 0) {
+      e_beg = min(max(row_ptr[row], 0), E);
+      e_end = min(max(row_ptr[row + 1], e_beg), E);
+    }
+    if (e_beg == e_end) return;
+    load_g(row);
+    for (int e0 = e_beg; e0 < e_end; e0 += Cfg::G) round(e0 + g, e0 + g < e_end);  // wave-uniform rounds
+  } else {
+    const long long base = ((long long)blockIdx.x * Cfg::WAVES + wv) * Cfg::EPW;
+    if (base >= E) return;
+    const int e_end = (int)min((long long)E, base + Cfg::EPW);
+    for (int e0 = (int)base; e0 < e_end; e0 += Cfg::G) round(e0 + g, e0 + g < e_end);
+  }
+  // grad_w: combine the lane groups, then one atomic per (path, channel)
+  if (gw != nullptr) {
+#pragma unroll
+    for (int off = Cfg::CL; off < kWave; off <<= 1)
+#pragma unroll
+      for (int j = 0; j < Cfg::CPL; ++j)
+#pragma unroll
+        for (int p = 0; p < P; ++p) gwacc[j][p] += __shfl_xor(gwacc[j][p], off);
+    if (g == 0) {
+#pragma unroll
+      for (int j = 0; j < Cfg::CPL; ++j)
+#pragma unroll
+        for (int p = 0; p < P; ++p) unsafeAtomicAdd(gw + p * C + cl + j * Cfg::CL, gwacc[j][p]);
+    }
+  }
+}
+
+template <int L, int PS, int C>
+static hipError_t launch_bwd_t(const BwdArgs& a) {
+  using Cfg = BwdCfg<C>;
+  constexpr int K = num_comp(L);
+  hipError_t err;
+  if (a.gx && a.N > 0 && (err = launch_fill_zero(a.gx, a.N * C * K, a.stream)) != hipSuccess) return err;
+  if (a.gw && (err = launch_fill_zero(a.gw, (int64_t)Tables<L, PS>::P * C, a.stream)) != hipSuccess) return err;
+  if (a.gvec && a.E > 0 && (err = launch_fill_zero(a.gvec, a.E * 3, a.stream)) != hipSuccess) return err;
+  if (a.N == 0 || a.E == 0) return hipSuccess;
+  if (a.row_ptr != nullptr) {
+    const unsigned blocks = (unsigned)((a.N + Cfg::WAVES - 1) / Cfg::WAVES);
+    hipLaunchKernelGGL((conv_bwd_kernel<L, PS, C, true>), dim3(blocks), dim3(Cfg::THREADS), 0, a.stream, (int)a.N,
+                       (int)a.E, a.row_ptr, a.vec, a.src, a.dst, a.x, a.w, a.gout, a.gx, a.gw, a.gvec);
+  } else {
+    const long long per_block = (long long)Cfg::WAVES * Cfg::EPW;
+    const unsigned blocks = (unsigned)((a.E + per_block - 1) / per_block);
+    hipLaunchKernelGGL((conv_bwd_kernel<L, PS, C, false>), dim3(blocks), dim3(Cfg::THREADS), 0, a.stream,
+                       (int)a.N, (int)a.E, a.row_ptr, a.vec, a.src, a.dst, a.x, a.w, a.gout, a.gx, a.gw, a.gvec);
+  }
+  return hipGetLastError();
+}
+
+template <int L, int PS>
+static hipError_t dispatch_bwd_c(const BwdArgs& a) {
+  switch (a.C) {
+    case 8: return launch_bwd_t<L, PS, 8>(a);
+    case 16: return launch_bwd_t<L, PS, 16>(a);
+    case 32: return launch_bwd_t<L, PS, 32>(a);
+    case 64: return launch_bwd_t<L, PS, 64>(a);
+    case 128: return launch_bwd_t<L, PS, 128>(a);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_conv_backward(const BwdArgs& a) {
+  switch (a.lmax * 2 + a.path_set) {
+    case 0: return dispatch_bwd_c<0, 0>(a);
+    case 1: return dispatch_bwd_c<0, 1>(a);
+    case 2: return dispatch_bwd_c<1, 0>(a);
+    case 3: return dispatch_bwd_c<1, 1>(a);
+    case 4: return dispatch_bwd_c<2, 0>(a);
+    case 5: return dispatch_bwd_c<2, 1>(a);
+    case 6: return dispatch_bwd_c<3, 0>(a);
+    case 7: return dispatch_bwd_c<3, 1>(a);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace eqtp

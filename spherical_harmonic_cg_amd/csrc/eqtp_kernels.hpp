@@ -32,6 +32,22 @@ struct ProbeArgs {
   hipStream_t stream;
 };
 
+struct BwdArgs {
+  int64_t N, E;
+  int lmax, C, path_set;
+  const float* vec;
+  const int32_t* src;
+  const int32_t* dst;      // unsorted edges (row_ptr == nullptr)
+  const int32_t* row_ptr;  // dst-sorted edges
+  const float* x;
+  const float* w;
+  const float* gout;
+  float* gx;    // or nullptr
+  float* gw;    // or nullptr
+  float* gvec;  // or nullptr
+  hipStream_t stream;
+};
+
 hipError_t launch_sh(const float* vec, int64_t E, int lmax, float* Y, hipStream_t stream);
 hipError_t launch_conv_node(const ConvArgs& a);   // sorted edges, fixed weights, matrix cores
 hipError_t launch_conv_edge(const ConvArgs& a);   // any order / weights, vector ALUs
@@ -40,5 +56,6 @@ hipError_t launch_probe_edge(const ProbeArgs& a);
 hipError_t launch_linear(int64_t N, int C, int lmax, int bf16, const float* h, const float* W, float* out,
                          hipStream_t stream);
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t stream);
+hipError_t launch_conv_backward(const BwdArgs& a);   // fixed weights, vector ALUs
 
 }  // namespace eqtp

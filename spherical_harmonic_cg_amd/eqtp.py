@@ -24,7 +24,7 @@ EQTP_EDGES_DST_SORTED, EQTP_EDGES_UNSORTED = 0, 1
 EQTP_ALGO_AUTO, EQTP_ALGO_NODE_MFMA, EQTP_ALGO_EDGE_VALU = 0, 1, 2
 EQTP_F32, EQTP_BF16 = 0, 1
 
-EXPORTED = ("eqtp_num_paths", "eqtp_path_table", "eqtp_sh", "eqtp_conv_fused", "eqtp_linear",
+EXPORTED = ("eqtp_num_paths", "eqtp_path_table", "eqtp_sh", "eqtp_conv_fused", "eqtp_conv_backward", "eqtp_linear",
             "eqtp_status_string", "eqtp_test_segment_probe")
 
 
@@ -61,6 +61,8 @@ def load_library(path: str = LIB_PATH):
             lib.eqtp_sh.restype = i32
             lib.eqtp_conv_fused.argtypes = [ctypes.POINTER(_ConvDesc), i64, i64, vp, vp, vp, vp, vp, vp, vp, vp]
             lib.eqtp_conv_fused.restype = i32
+            lib.eqtp_conv_backward.argtypes = [ctypes.POINTER(_ConvDesc), i64, i64] + [vp] * 11
+            lib.eqtp_conv_backward.restype = i32
             lib.eqtp_linear.argtypes = [i64, i32, i32, i32, vp, vp, vp, vp]
             lib.eqtp_linear.restype = i32
             lib.eqtp_status_string.argtypes = [i32]
@@ -177,6 +179,46 @@ def eqtp_conv_fused(vec, src, x, weights, lmax: int, row_ptr=None, dst=None, pat
                                         _ptr(x), _ptr(weights), _ptr(out), _stream())
     _raise(rc, "eqtp_conv_fused")
     return out
+
+
+def eqtp_conv_backward(vec, src, x, weights, grad_out, lmax: int, row_ptr=None, dst=None,
+                       path_set: int = EQTP_PATHS_PARITY, need_x: bool = True, need_w: bool = True,
+                       need_vec: bool = True):
+    """(grad_x [N,C,K] | None, grad_w [P,C] | None, grad_vec [E,3] | None) of
+    sum(grad_out * eqtp_conv_fused(...)) for fixed weights [P, C]."""
+    import torch
+
+    _check(x, "x", torch.float32)
+    if x.dim() != 3:
+        raise ValueError("x must be [N, C, K]")
+    N, C, K = x.shape
+    if K != (lmax + 1) ** 2:
+        raise ValueError("x has %d components, lmax %d needs %d" % (K, lmax, (lmax + 1) ** 2))
+    _check(grad_out, "grad_out", torch.float32, (N, C, K))
+    _check(vec, "vec", torch.float32)
+    E = vec.shape[0]
+    _check(src, "src", torch.int32, (E,))
+    if (row_ptr is None) == (dst is None):
+        raise ValueError("give exactly one of row_ptr (dst-sorted edges) or dst (any order)")
+    if row_ptr is not None:
+        _check(row_ptr, "row_ptr", torch.int32, (N + 1,))
+        order = EQTP_EDGES_DST_SORTED
+    else:
+        _check(dst, "dst", torch.int32, (E,))
+        order = EQTP_EDGES_UNSORTED
+    P = eqtp_num_paths(lmax, path_set)
+    _check(weights, "weights", torch.float32, (P, C))
+    if not (need_x or need_w or need_vec):
+        raise ValueError("request at least one gradient")
+    gx = torch.empty_like(x) if need_x else None
+    gw = torch.empty_like(weights) if need_w else None
+    gv = torch.empty((E, 3), dtype=torch.float32, device=x.device) if need_vec else None
+    d = _ConvDesc(ctypes.sizeof(_ConvDesc), lmax, C, path_set, EQTP_W_FIXED, order, EQTP_ALGO_AUTO, 0.0, 8)
+    rc = load_library().eqtp_conv_backward(ctypes.byref(d), N, E, _ptr(vec), _ptr(src), _ptr(dst), _ptr(row_ptr),
+                                           _ptr(x), _ptr(weights), _ptr(grad_out), _ptr(gx), _ptr(gw), _ptr(gv),
+                                           _stream())
+    _raise(rc, "eqtp_conv_backward")
+    return gx, gw, gv
 
 
 def eqtp_linear(h, W, lmax: int, dtype: int = EQTP_F32, out=None):

@@ -118,3 +118,28 @@ def test_sh_and_linear_validation():
     assert lib.eqtp_linear(10, 64, 3, 0, NULL, FAKE, FAKE, NULL) == 1
     assert lib.eqtp_linear(0, 64, 3, 0, NULL, NULL, NULL, NULL) == 0
     assert lib.eqtp_test_segment_probe(FAKE, FAKE, 10, 20, 64, 3, 0, FAKE, FAKE, NULL) == 1
+
+
+def test_conv_backward_validation():
+    e = _lib()
+    lib = e.load_library()
+
+    def call(d, N=10, E=20, vec=FAKE, src=FAKE, dst=NULL, rp=FAKE, x=FAKE, w=FAKE, g=FAKE, gx=FAKE, gw=FAKE,
+             gv=FAKE):
+        return lib.eqtp_conv_backward(ctypes.byref(d), N, E, vec, src, dst, rp, x, w, g, gx, gw, gv, NULL)
+
+    assert call(_desc(e, weight_mode=1, r_cut=5.0)) == 2                 # radial weights: not implemented
+    assert call(_desc(e, lmax=4)) == 2
+    assert call(_desc(e, C=48)) == 2
+    assert call(_desc(e, path_set=2)) == 1
+    assert call(_desc(e), gx=NULL, gw=NULL, gv=NULL) == 1                 # nothing requested
+    assert call(_desc(e), x=NULL) == 1
+    assert call(_desc(e), g=NULL) == 1
+    assert call(_desc(e), vec=NULL) == 1
+    assert call(_desc(e), rp=NULL) == 1                                   # sorted without row_ptr
+    assert call(_desc(e, edge_order=1), rp=NULL) == 1                     # unsorted without dst
+    assert call(_desc(e), gx=ctypes.c_void_p(0x10004)) == 1               # grad_x not 16-byte aligned
+    assert call(_desc(e), N=0) == 1                                       # edges without nodes
+    bad = _desc(e)
+    bad.struct_size = 8
+    assert call(bad) == 1
