@@ -27,6 +27,92 @@
 
 namespace eqtp {
 
+// ---------------------------------------------------------------------------
+// Gradient of the real harmonics with respect to the (unnormalised) edge
+// vector: G[k][a] = dY_k / dvec_a.  Each Y_k of sh_eval is a polynomial p_k in the
+// unit vector u = vec/|vec|; its gradient in u (written out per component
+// below) is projected onto the sphere's tangent plane and divided by |vec|:
+// G = (grad p - u (u . grad p)) / |vec|.  A zero vector gives G = 0 (Y is
+// constant there).  Y is returned as by sh_eval.
+// ---------------------------------------------------------------------------
+template <int L>
+__device__ __forceinline__ void sh_grad_eval(float vx, float vy, float vz, float (&Y)[16], float (&G)[16][3]) {
+  using namespace eqtp_gen;
+  sh_eval<L>(vx, vy, vz, Y);
+  const float r2 = vx * vx + vy * vy + vz * vz;
+  const bool nz = r2 > 0.0f;
+  const float inv = nz ? rsqrtf(r2) : 0.0f;
+  const float x = vx * inv, y = vy * inv, z = vz * inv;
+  float g[16][3];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) g[k][0] = g[k][1] = g[k][2] = 0.0f;
+  if constexpr (L >= 1) {
+    g[1][2] = kShC1;
+    g[2][0] = -kShC1;
+    g[3][1] = -kShC1;
+  }
+  if constexpr (L >= 2) {
+    g[4][2] = 6.0f * kShC20 * z;
+    g[5][0] = -kShC21 * z;
+    g[5][2] = -kShC21 * x;
+    g[6][1] = -kShC21 * z;
+    g[6][2] = -kShC21 * y;
+    g[7][0] = 2.0f * kShC22 * x;
+    g[7][1] = -2.0f * kShC22 * y;
+    g[8][0] = 2.0f * kShC22 * y;
+    g[8][1] = 2.0f * kShC22 * x;
+  }
+  if constexpr (L >= 3) {
+    const float zz = z * z, d = x * x - y * y;
+    g[9][2] = kShC30 * (15.0f * zz - 3.0f);
+    g[10][0] = -kShC31 * (5.0f * zz - 1.0f);
+    g[10][2] = -10.0f * kShC31 * x * z;
+    g[11][1] = -kShC31 * (5.0f * zz - 1.0f);
+    g[11][2] = -10.0f * kShC31 * y * z;
+    g[12][0] = 2.0f * kShC32 * x * z;
+    g[12][1] = -2.0f * kShC32 * y * z;
+    g[12][2] = kShC32 * d;
+    g[13][0] = 2.0f * kShC32 * y * z;
+    g[13][1] = 2.0f * kShC32 * x * z;
+    g[13][2] = 2.0f * kShC32 * x * y;
+    g[14][0] = -3.0f * kShC33 * d;
+    g[14][1] = 6.0f * kShC33 * x * y;
+    g[15][0] = -6.0f * kShC33 * x * y;
+    g[15][1] = -3.0f * kShC33 * d;
+  }
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const float ug = x * g[k][0] + y * g[k][1] + z * g[k][2];
+    G[k][0] = (g[k][0] - x * ug) * inv;
+    G[k][1] = (g[k][1] - y * ug) * inv;
+    G[k][2] = (g[k][2] - z * ug) * inv;
+  }
+}
+
+// by_out positions ordered by a (path, component) key, stably: KEY 1 sorts by
+// (p, mu1), KEY 2 by (p, mu2).  Runs of equal key are contiguous.
+template <int L, int PS, int KEY>
+struct TermOrder {
+  using T = Tables<L, PS>;
+  struct Idx {
+    short v[T::NT > 0 ? T::NT : 1];
+  };
+  static constexpr int key(int i) { return T::by_out[i].p * 16 + (KEY == 1 ? T::by_out[i].mu1 : T::by_out[i].mu2); }
+  static constexpr Idx make() {  // stable counting sort by key
+    Idx a{};
+    int pos[64 * 16 + 1] = {};
+    for (int i = 0; i < T::NT; ++i) pos[key(i) + 1]++;
+    for (int kk = 0; kk < 64 * 16; ++kk) pos[kk + 1] += pos[kk];
+    for (int i = 0; i < T::NT; ++i) a.v[pos[key(i)]++] = (short)i;
+    return a;
+  }
+  static constexpr Idx order = make();
+  static constexpr const eqtp_gen::CgTerm& term(int j) { return T::by_out[order.v[j]]; }
+  static constexpr bool first(int j) { return j == 0 || key(order.v[j - 1]) != key(order.v[j]); }
+  static constexpr bool last(int j) { return j + 1 == T::NT || key(order.v[j + 1]) != key(order.v[j]); }
+};
+
+
 template <int C>
 struct BwdCfg {
   static constexpr int CPL = C > 64 ? C / 64 : 1;  // channels per lane
