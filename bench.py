@@ -128,6 +128,8 @@ def main():
                     help="'so3': the 34-path SO(3) set (a labelled extra, not the headline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
+    ap.add_argument("--backward", action="store_true",
+                    help="also time eqtp_conv_backward (all three gradients) on the same inputs (an extra field)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="after timing, run one 256 MiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -207,6 +209,33 @@ def main():
         "linear avg %.4f ms" % (K, ms_per_step, 1e3 * wall / K, conv_ms.mean(), np.percentile(conv_ms, 10),
                                 np.percentile(conv_ms, 90), lin_ms.mean()))
 
+    backward = None
+    if args.backward:
+        if wl.weight_mode != 0:
+            log("backward: fixed weights only; skipped for this workload")
+        else:
+            gout = torch.randn_like(x)
+            bkw = dict(dst=dst) if args.unsorted else dict(row_ptr=row_ptr)
+
+            def bwd():
+                eq.eqtp_conv_backward(vec, src, x, w, gout, wl.lmax, path_set=wl.path_set, **bkw)
+
+            for _ in range(max(3, args.warmup // 4)):
+                bwd()
+            torch.cuda.synchronize()
+            kb = max(5, K // 4)
+            b0 = torch.cuda.Event(enable_timing=True)
+            b1 = torch.cuda.Event(enable_timing=True)
+            b0.record(stream)
+            for _ in range(kb):
+                bwd()
+            b1.record(stream)
+            torch.cuda.synchronize()
+            bms = b0.elapsed_time(b1) / kb
+            backward = {"ms": round(bms, 5), "edges_per_s": round(wl.E / (bms * 1e-3), 1), "launches": kb,
+                        "what": "grad_x, grad_w and grad_vec of the conv (one launch of eqtp_conv_backward)"}
+            log("backward: %.4f ms (%.3e edges/s)" % (bms, wl.E / (bms * 1e-3)))
+
     if args.calib_copy:
         a = torch.empty(64 << 20, dtype=torch.float32, device=dev)
         b = torch.empty_like(a)
@@ -254,6 +283,8 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
+    if backward is not None:
+        rec["backward"] = backward
     print(json.dumps(rec), flush=True)
 
 

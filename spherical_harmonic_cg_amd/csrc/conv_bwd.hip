@@ -162,74 +162,116 @@ __global__ __launch_bounds__(BwdCfg<C>::THREADS) void conv_bwd_kernel(
       for (int k = 0; k < K; ++k) gv[j][k] = gout[((size_t)d * C + cl + j * Cfg::CL) * K + k];
   };
 
-  // one round: lane group g handles edge e (if valid)
-  auto round = [&](int e, bool valid) {
-    float mx[Cfg::CPL][K];
-    float dy[16];
+  // An edge's inputs, loaded one round ahead of their use.  Invalid slots
+  // load an in-range edge (their results are discarded), so the loads carry
+  // no branches.
+  struct EdgeIn {
+    float vx, vy, vz;
+    int s;
+    float xv[Cfg::CPL][K];
+    float gd[SORTED ? 1 : Cfg::CPL][K];  // gout of the destination (unsorted edges)
+  };
+  auto fetch = [&](int e, bool valid, int e_alt) {
+    EdgeIn in;
+    const int ec = valid ? e : e_alt;
+    in.vx = vec[3 * ec];
+    in.vy = vec[3 * ec + 1];
+    in.vz = vec[3 * ec + 2];
+    in.s = clamp_index(src[ec], N);
 #pragma unroll
     for (int j = 0; j < Cfg::CPL; ++j)
 #pragma unroll
-      for (int k = 0; k < K; ++k) mx[j][k] = 0.0f;
-#pragma unroll
-    for (int k = 0; k < 16; ++k) dy[k] = 0.0f;
-    float Y[16], Gm[16][3];
-    int s = -1;
-    if (valid) {
-      s = clamp_index(src[e], N);
-      sh_grad_eval<L>(vec[3 * e], vec[3 * e + 1], vec[3 * e + 2], Y, Gm);
-      if constexpr (!SORTED) load_g(clamp_index(dst[e], N));
-#pragma unroll
-      for (int j = 0; j < Cfg::CPL; ++j) {
-        float xv[K];
-#pragma unroll
-        for (int k = 0; k < K; ++k) xv[k] = x[((size_t)s * C + cl + j * Cfg::CL) * K + k];
-        // (path, mu1) runs: grad_x and grad_w
-        float s1 = 0.0f;
-        static_for<0, T::NT>([&](auto jj) {
-          constexpr int q = decltype(jj)::value;
-          constexpr eqtp_gen::CgTerm tm = O1::term(q);
-          const float yg = Y[tm.mu2] * gv[j][tm.mu3];
-          s1 = O1::first(q) ? tm.c * yg : fmaf(tm.c, yg, s1);
-          if constexpr (O1::last(q)) {
-            mx[j][tm.mu1] = fmaf(wreg[j][tm.p], s1, mx[j][tm.mu1]);
-            gwacc[j][tm.p] = fmaf(xv[tm.mu1], s1, gwacc[j][tm.p]);
-          }
-        });
-        // (path, mu2) runs: dL/dY
-        float s2 = 0.0f;
-        static_for<0, T::NT>([&](auto jj) {
-          constexpr int q = decltype(jj)::value;
-          constexpr eqtp_gen::CgTerm tm = O2::term(q);
-          const float xg = xv[tm.mu1] * gv[j][tm.mu3];
-          s2 = O2::first(q) ? tm.c * xg : fmaf(tm.c, xg, s2);
-          if constexpr (O2::last(q)) dy[tm.mu2] = fmaf(wreg[j][tm.p], s2, dy[tm.mu2]);
-        });
-      }
-    }
-    // grad_x: exchange the round's contributions so that atomic instruction i
-    // adds floats 64i .. 64i+63 of the wave's G source blocks
-    if (gx != nullptr) {
+      for (int k = 0; k < K; ++k) in.xv[j][k] = x[((size_t)in.s * C + cl + j * Cfg::CL) * K + k];
+    if constexpr (!SORTED) {
+      const int d = clamp_index(dst[ec], N);
 #pragma unroll
       for (int j = 0; j < Cfg::CPL; ++j)
 #pragma unroll
-        for (int k = 0; k < K; ++k) xw[(g * C + cl + j * Cfg::CL) * K + k] = mx[j][k];
-      if (cl == 0) xsrc[wv][g] = s;  // -1: no edge in this slot
-      wave_lds_sync();
-#pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        const int f = kWave * i + lane;
-        const int sd = xsrc[wv][f / MSG];
-        if (sd >= 0) unsafeAtomicAdd(gx + (size_t)sd * MSG + f % MSG, xw[f]);
-      }
-      wave_lds_sync();
+        for (int k = 0; k < K; ++k) in.gd[j][k] = gout[((size_t)d * C + cl + j * Cfg::CL) * K + k];
     }
-    // grad_vec: sum dL/dY over the group's channels (its CL lanes)
+    return in;
+  };
+
+  // one round: lane group g handles edge e (if valid) with inputs in.  The
+  // (path, mu1) pass and the grad_x exchange finish before the (path, mu2)
+  // pass starts, so their accumulators are never live together.
+  auto round = [&](int e, bool valid, const EdgeIn& in) {
+    float Y[16];
+    if (valid) sh_eval<L>(in.vx, in.vy, in.vz, Y);
+    {
+      float mx[Cfg::CPL][K];
+#pragma unroll
+      for (int j = 0; j < Cfg::CPL; ++j)
+#pragma unroll
+        for (int k = 0; k < K; ++k) mx[j][k] = 0.0f;
+      if (valid) {
+#pragma unroll
+        for (int j = 0; j < Cfg::CPL; ++j) {
+          const float(&gj)[K] = SORTED ? gv[j] : in.gd[SORTED ? 0 : j];
+          // (path, mu1) runs: grad_x and grad_w
+          float s1 = 0.0f;
+          static_for<0, T::NT>([&](auto jj) {
+            constexpr int q = decltype(jj)::value;
+            constexpr eqtp_gen::CgTerm tm = O1::term(q);
+            // (c * Y) * g per term: no product shared between terms, so no long-lived common subexpressions
+            const float cy = tm.c * Y[tm.mu2];
+            s1 = O1::first(q) ? cy * gj[tm.mu3] : fmaf(cy, gj[tm.mu3], s1);
+            if constexpr (O1::last(q)) {
+              mx[j][tm.mu1] = fmaf(wreg[j][tm.p], s1, mx[j][tm.mu1]);
+              gwacc[j][tm.p] = fmaf(in.xv[j][tm.mu1], s1, gwacc[j][tm.p]);
+              __builtin_amdgcn_sched_barrier(0);  // keep runs apart: bounded live temporaries
+            }
+          });
+        }
+      }
+      // grad_x: exchange the round's contributions so that atomic instruction
+      // i adds floats 64i .. 64i+63 of the wave's G source blocks
+      if (gx != nullptr) {
+#pragma unroll
+        for (int j = 0; j < Cfg::CPL; ++j)
+#pragma unroll
+          for (int k = 0; k < K; ++k) xw[(g * C + cl + j * Cfg::CL) * K + k] = mx[j][k];
+        if (cl == 0) xsrc[wv][g] = valid ? in.s : -1;  // -1: no edge in this slot
+        wave_lds_sync();
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+          const int f = kWave * i + lane;
+          const int sd = xsrc[wv][f / MSG];
+          if (sd >= 0) unsafeAtomicAdd(gx + (size_t)sd * MSG + f % MSG, xw[f]);
+        }
+        wave_lds_sync();
+      }
+    }
     if (gvec != nullptr) {
+      float dy[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) dy[k] = 0.0f;
+      if (valid) {
+#pragma unroll
+        for (int j = 0; j < Cfg::CPL; ++j) {
+          const float(&gj)[K] = SORTED ? gv[j] : in.gd[SORTED ? 0 : j];
+          // (path, mu2) runs: dL/dY
+          float s2 = 0.0f;
+          static_for<0, T::NT>([&](auto jj) {
+            constexpr int q = decltype(jj)::value;
+            constexpr eqtp_gen::CgTerm tm = O2::term(q);
+            const float cx = tm.c * in.xv[j][tm.mu1];
+            s2 = O2::first(q) ? cx * gj[tm.mu3] : fmaf(cx, gj[tm.mu3], s2);
+            if constexpr (O2::last(q)) {
+              dy[tm.mu2] = fmaf(wreg[j][tm.p], s2, dy[tm.mu2]);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          });
+        }
+      }
+      // grad_vec: sum dL/dY over the group's channels (its CL lanes)
 #pragma unroll
       for (int off = 1; off < Cfg::CL; off <<= 1)
 #pragma unroll
         for (int k = 0; k < K; ++k) dy[k] += __shfl_xor(dy[k], off);
       if (valid && cl == 0) {
+        float Y2[16], Gm[16][3];
+        sh_grad_eval<L>(in.vx, in.vy, in.vz, Y2, Gm);
         float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f;
 #pragma unroll
         for (int k = 0; k < K; ++k) {
@@ -244,6 +286,18 @@ __global__ __launch_bounds__(BwdCfg<C>::THREADS) void conv_bwd_kernel(
     }
   };
 
+  // wave-uniform rounds over [e_first, e_last); the next round's inputs are
+  // fetched before the current round's arithmetic
+  auto walk = [&](int e_first, int e_last) {
+    EdgeIn cur = fetch(e_first + g, e_first + g < e_last, e_first);
+    for (int e0 = e_first; e0 < e_last; e0 += Cfg::G) {
+      const int e = e0 + g;
+      const EdgeIn nxt = fetch(e + Cfg::G, e + Cfg::G < e_last, e_first);
+      round(e, e < e_last, cur);
+      cur = nxt;
+    }
+  };
+
   if constexpr (SORTED) {
     const int row = blockIdx.x * Cfg::WAVES + wv;
     if (row >= N) return;
@@ -254,12 +308,11 @@ __global__ __launch_bounds__(BwdCfg<C>::THREADS) void conv_bwd_kernel(
     }
     if (e_beg == e_end) return;
     load_g(row);
-    for (int e0 = e_beg; e0 < e_end; e0 += Cfg::G) round(e0 + g, e0 + g < e_end);  // wave-uniform rounds
+    walk(e_beg, e_end);
   } else {
     const long long base = ((long long)blockIdx.x * Cfg::WAVES + wv) * Cfg::EPW;
     if (base >= E) return;
-    const int e_end = (int)min((long long)E, base + Cfg::EPW);
-    for (int e0 = (int)base; e0 < e_end; e0 += Cfg::G) round(e0 + g, e0 + g < e_end);
+    walk((int)base, (int)min((long long)E, base + Cfg::EPW));
   }
   // grad_w: combine the lane groups, then one atomic per (path, channel)
   if (gw != nullptr) {
