@@ -69,6 +69,10 @@ def _load():
             lib.oracle_round_bf16.restype = ctypes.c_float
             lib.oracle_linear.argtypes = [i64, i32, i32, i32, vp, vp, vp]
             lib.oracle_linear.restype = i32
+            lib.oracle_messages.argtypes = [i64, i64, i32, i32, i32, i32, f64, i32, vp, vp, vp, vp, vp]
+            lib.oracle_messages.restype = i32
+            lib.oracle_messages_f64.argtypes = [i64, i64, i32, i32, i32, i32, f64, i32, vp, vp, vp, vp, vp]
+            lib.oracle_messages_f64.restype = i32
             lib.oracle_sh_grad_f64.argtypes = [i64, vp, i32, vp, vp]
             lib.oracle_sh_grad_f64.restype = i32
             lib.oracle_conv_backward.argtypes = [i64, i64, i32, i32, i32] + [vp] * 9
@@ -255,3 +259,26 @@ def conv_backward(N, vec, src, dst, x, w, gout, lmax, path_set=PATHS_PARITY):
     if rc != 0:
         raise ValueError("oracle_conv_backward failed (rc=%d)" % rc)
     return gx, gw, gv
+
+
+def messages(N, vec, src, x, w, lmax, path_set=PATHS_PARITY, weight_mode=0, r_cut=0.0, n_basis=8) -> np.ndarray:
+    """fp64 per-edge messages [E, C, (lmax+1)^2] (see oracle_messages in the C source); float64 ``x``
+    selects the double entry point."""
+    lib = _load()
+    is64 = np.asarray(x).dtype == np.float64
+    cast = _f64 if is64 else _f32
+    v = cast(vec).reshape(-1, 3)
+    s = _i32(src)
+    xx = cast(x)
+    ww = cast(w)
+    E = v.shape[0]
+    C = xx.shape[1]
+    K = (lmax + 1) ** 2
+    if xx.shape != (N, C, K) or s.shape != (E,):
+        raise ValueError("shape mismatch")
+    out = np.empty((E, C, K), dtype=np.float64)
+    fn = lib.oracle_messages_f64 if is64 else lib.oracle_messages
+    rc = fn(N, E, lmax, C, path_set, weight_mode, float(r_cut), n_basis, _p(v), _p(s), _p(xx), _p(ww), _p(out))
+    if rc != 0:
+        raise ValueError("oracle_messages failed (rc=%d)" % rc)
+    return out

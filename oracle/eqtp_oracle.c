@@ -342,6 +342,92 @@ int oracle_conv_f64(int64_t N, int64_t E, int lmax, int C, int path_set, int wei
   return rc;
 }
 
+/* Per-edge messages (the Batmobile page's fused kernel output, section "3.
+ * operator fusion": one [C, K] message per edge, no destination sum):
+ *   msg[e, c, l3 m3] = sum_p w_e[p,c] sum_{m1,m2} C^p[m1,m2,m3] x[src_e, c, l1 m1] Y_{l2 m2}(vec_e)
+ * with w_e as in oracle_conv_f64.  msg is [E, C, K] float64, overwritten. */
+int oracle_messages_f64(int64_t N, int64_t E, int lmax, int C, int path_set, int weight_mode, double r_cut,
+                        int n_basis, const double* vec, const int32_t* src, const double* x, const double* w,
+                        double* msg) {
+  if (lmax < 0 || lmax > OR_MAX_L || C <= 0 || N < 0 || E < 0) return 1;
+  if (weight_mode != 0 && weight_mode != 1) return 1;
+  if (weight_mode == 1 && (n_basis <= 0 || n_basis > 64 || !(r_cut > 0.0))) return 1;
+  int K = (lmax + 1) * (lmax + 1);
+  int P = oracle_paths(lmax, path_set, NULL);
+  if (P <= 0) return 1;
+  int32_t* paths = (int32_t*)malloc(sizeof(int32_t) * 3 * P);
+  oracle_paths(lmax, path_set, paths);
+  double** cg = (double**)malloc(sizeof(double*) * P);
+  for (int p = 0; p < P; ++p) {
+    int l1 = paths[3 * p], l2 = paths[3 * p + 1], l3 = paths[3 * p + 2];
+    cg[p] = (double*)malloc(sizeof(double) * (2 * l1 + 1) * (2 * l2 + 1) * (2 * l3 + 1));
+    oracle_cg_real(l1, l2, l3, cg[p], NULL);
+  }
+  for (int64_t i = 0; i < E * C * K; ++i) msg[i] = 0.0;
+  double* Y = (double*)malloc(sizeof(double) * K);
+  double* we = (double*)malloc(sizeof(double) * P * C);
+  double R[64];
+  int rc = 0;
+  for (int64_t e = 0; e < E; ++e) {
+    int64_t s = src[e];
+    if (s < 0 || s >= N) {
+      rc = 2;
+      break;
+    }
+    double vx = vec[3 * e], vy = vec[3 * e + 1], vz = vec[3 * e + 2];
+    real_sh(lmax, vx, vy, vz, Y);
+    if (weight_mode == 0) {
+      for (int i = 0; i < P * C; ++i) we[i] = w[i];
+    } else {
+      double r = sqrt(vx * vx + vy * vy + vz * vz);
+      oracle_radial_basis(r, r_cut, n_basis, R);
+      for (int i = 0; i < P * C; ++i) {
+        double acc = 0.0;
+        for (int n = 0; n < n_basis; ++n) acc += R[n] * w[(int64_t)n * P * C + i];
+        we[i] = acc;
+      }
+    }
+    for (int p = 0; p < P; ++p) {
+      int l1 = paths[3 * p], l2 = paths[3 * p + 1], l3 = paths[3 * p + 2];
+      int n1 = 2 * l1 + 1, n2 = 2 * l2 + 1, n3 = 2 * l3 + 1;
+      for (int a = 0; a < n1; ++a)
+        for (int b = 0; b < n2; ++b)
+          for (int c3 = 0; c3 < n3; ++c3) {
+            double coef = cg[p][(a * n2 + b) * n3 + c3];
+            if (coef == 0.0) continue;
+            double cy = coef * Y[l2 * l2 + b];
+            for (int ch = 0; ch < C; ++ch)
+              msg[(e * C + ch) * K + l3 * l3 + c3] += we[p * C + ch] * cy * x[(s * C + ch) * K + l1 * l1 + a];
+          }
+    }
+  }
+  free(Y);
+  free(we);
+  for (int p = 0; p < P; ++p) free(cg[p]);
+  free(cg);
+  free(paths);
+  return rc;
+}
+
+int oracle_messages(int64_t N, int64_t E, int lmax, int C, int path_set, int weight_mode, double r_cut,
+                    int n_basis, const float* vec, const int32_t* src, const float* x, const float* w,
+                    double* msg) {
+  if (lmax < 0 || lmax > OR_MAX_L || C <= 0 || N < 0 || E < 0) return 1;
+  int K = (lmax + 1) * (lmax + 1);
+  int P = oracle_paths(lmax, path_set, NULL);
+  if (P <= 0) return 1;
+  if (weight_mode == 1 && (n_basis <= 0 || n_basis > 64)) return 1;
+  int64_t nw = (weight_mode == 1) ? (int64_t)n_basis * P * C : (int64_t)P * C;
+  double* v = widen(vec, 3 * E);
+  double* xx = widen(x, N * C * K);
+  double* ww = widen(w, nw);
+  int rc = oracle_messages_f64(N, E, lmax, C, path_set, weight_mode, r_cut, n_basis, v, src, xx, ww, msg);
+  free(v);
+  free(xx);
+  free(ww);
+  return rc;
+}
+
 /* float32 entry point: inputs widened exactly to double, then the f64 core. */
 int oracle_conv(int64_t N, int64_t E, int lmax, int C, int path_set, int weight_mode, double r_cut,
                 int n_basis, const float* vec, const int32_t* src, const int32_t* dst, const float* x,

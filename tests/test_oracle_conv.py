@@ -374,3 +374,29 @@ def test_linear_bf16_mode():
     ref = oracle.linear(oracle.round_bf16(h).astype(np.float64), oracle.round_bf16(W).astype(np.float64), lmax)
     np.testing.assert_allclose(got, ref, atol=1e-12)
     assert np.abs(got - oracle.linear(h, W, lmax)).max() > 1e-4
+
+
+# ----------------------------------------------------------------------------
+# per-edge messages (the page's fused kernel output, no destination sum)
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("lmax,ps,radial", [(1, 0, False), (2, 0, False), (3, 0, False), (3, 1, False),
+                                            (3, 0, True), (2, 1, True)])
+def test_messages_sum_to_the_convolution(lmax, ps, radial):
+    wl = synth.small_graph(9, 5, 3, lmax, 700 + lmax, path_set=ps, radial=radial)
+    w = wl.w_rad if radial else wl.w
+    kw = dict(path_set=ps, weight_mode=1 if radial else 0, r_cut=wl.r_cut)
+    msg = oracle.messages(wl.N, wl.vec, wl.src, wl.x, w, lmax, **kw)
+    out = oracle.conv(wl.N, wl.vec, wl.src, wl.dst, wl.x, w, lmax, **kw)
+    summed = np.zeros_like(out)
+    np.add.at(summed, wl.dst, msg)
+    np.testing.assert_allclose(summed, out, rtol=0, atol=1e-12 * max(1.0, np.abs(out).max()))
+
+
+def test_messages_single_edge_graph_is_the_convolution_row():
+    # one edge into its own node: the message is that node's convolution output
+    wl = synth.small_graph(6, 4, 4, 3, 711)
+    for e in (0, 3, wl.src.shape[0] - 1):
+        msg = oracle.messages(wl.N, wl.vec[e:e + 1], wl.src[e:e + 1], wl.x, wl.w, 3)
+        out = oracle.conv(wl.N, wl.vec[e:e + 1], wl.src[e:e + 1], np.array([0], np.int32), wl.x, wl.w, 3)
+        np.testing.assert_allclose(msg[0], out[0], rtol=0, atol=1e-13)
