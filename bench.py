@@ -130,6 +130,8 @@ def main():
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
     ap.add_argument("--backward", action="store_true",
                     help="also time eqtp_conv_backward (all three gradients) on the same inputs (an extra field)")
+    ap.add_argument("--messages", action="store_true",
+                    help="also time eqtp_conv_messages (per-edge [E,C,K] output, the page's kernel) (an extra field)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="after timing, run one 256 MiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -236,6 +238,34 @@ def main():
                         "what": "grad_x, grad_w and grad_vec of the conv (one launch of eqtp_conv_backward)"}
             log("backward: %.4f ms (%.3e edges/s)" % (bms, wl.E / (bms * 1e-3)))
 
+    messages = None
+    if args.messages:
+        msg_out = torch.empty((wl.E, wl.C, wl.K), dtype=torch.float32, device=dev)
+
+        def msg():
+            eq.eqtp_conv_messages(vec, src, x, w, wl.lmax, path_set=wl.path_set, weight_mode=wl.weight_mode,
+                                  r_cut=wl.r_cut, out=msg_out)
+
+        for _ in range(3):
+            msg()
+        torch.cuda.synchronize()
+        km = max(5, K // 4)
+        m0 = torch.cuda.Event(enable_timing=True)
+        m1 = torch.cuda.Event(enable_timing=True)
+        m0.record(stream)
+        for _ in range(km):
+            msg()
+        m1.record(stream)
+        torch.cuda.synchronize()
+        mms = m0.elapsed_time(m1) / km
+        wbytes = wl.E * wl.C * wl.K * 4
+        messages = {"ms": round(mms, 5), "edges_per_s": round(wl.E / (mms * 1e-3), 1), "launches": km,
+                    "write_GBps": round(wbytes / (mms * 1e-3) / 1e9, 1),
+                    "what": "per-edge messages [E,C,K] (one launch of eqtp_conv_messages)"}
+        del msg_out
+        log("messages: %.4f ms (%.3e edges/s, %.0f GB/s written)" % (mms, wl.E / (mms * 1e-3),
+                                                                      wbytes / (mms * 1e-3) / 1e9))
+
     if args.calib_copy:
         a = torch.empty(64 << 20, dtype=torch.float32, device=dev)
         b = torch.empty_like(a)
@@ -285,6 +315,8 @@ def main():
     }
     if backward is not None:
         rec["backward"] = backward
+    if messages is not None:
+        rec["messages"] = messages
     print(json.dumps(rec), flush=True)
 
 

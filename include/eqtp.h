@@ -139,6 +139,19 @@ int eqtp_conv_fused(const eqtp_conv_desc* d, int64_t N, int64_t E, const float* 
                     void* stream);
 
 /*
+ * Per-edge messages, without the destination sum (the page's fused kernel,
+ * section "3. operator fusion": edge vectors [E,3], node features [N,C,16],
+ * source indices [E] in, messages [E,C,16] out):
+ *   messages[e, c, l3 m3] = sum_p w_e[p, c] sum_{m1, m2} C^p[m1, m2, m3] x[src_e, c, l1 m1] Y_{l2 m2}(vec_e)
+ * d: lmax, C, path_set, weight_mode, r_cut, n_basis as for eqtp_conv_fused
+ * (edge_order and algo are ignored); N, E, vec, src, x, weights as there.
+ *   messages [E, C, K] fp32, 16-byte aligned, fully overwritten; must not
+ *            alias an input.  Deterministic.
+ */
+int eqtp_conv_messages(const eqtp_conv_desc* d, int64_t N, int64_t E, const float* vec, const int32_t* src,
+                       const float* x, const float* weights, float* messages, void* stream);
+
+/*
  * Gradients of the fused convolution with fixed weights: for a scalar loss L
  * with grad_out = dL/dout,
  *   grad_x[s, c, l1 m1] = sum_{e: src_e = s} sum_p w[p, c] sum_{m2, m3} C^p[m1, m2, m3] Y_{l2 m2}(vec_e)

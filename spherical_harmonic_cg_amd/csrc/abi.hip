@@ -114,6 +114,45 @@ int eqtp_conv_fused(const eqtp_conv_desc* d, int64_t N, int64_t E, const float* 
   return status_of(use_node ? eqtp::launch_conv_node(a) : eqtp::launch_conv_edge(a));
 }
 
+int eqtp_conv_messages(const eqtp_conv_desc* d, int64_t N, int64_t E, const float* vec, const int32_t* src,
+                       const float* x, const float* weights, float* messages, void* stream) {
+  if (!d || d->struct_size != (int32_t)sizeof(eqtp_conv_desc)) return EQTP_EINVAL;
+  if (d->lmax < 0) return EQTP_EINVAL;
+  if (d->lmax > 3) return EQTP_EUNSUPPORTED;
+  if (d->path_set != EQTP_PATHS_PARITY && d->path_set != EQTP_PATHS_SO3) return EQTP_EINVAL;
+  if (d->weight_mode != EQTP_W_FIXED && d->weight_mode != EQTP_W_RADIAL) return EQTP_EINVAL;
+  if (d->C <= 0) return EQTP_EINVAL;
+  if (!valid_c(d->C)) return EQTP_EUNSUPPORTED;
+  if (d->weight_mode == EQTP_W_RADIAL) {
+    if (!(d->r_cut > 0.0f)) return EQTP_EINVAL;
+    if (d->n_basis != 8) return EQTP_EUNSUPPORTED;
+  }
+  if (N < 0 || E < 0 || N > kMaxIndex || E > kMaxIndex) return EQTP_EINVAL;
+  if (E > 0 && N == 0) return EQTP_EINVAL;
+  if (E == 0) return EQTP_OK;
+  if (!vec || !src || !x || !weights || !messages) return EQTP_EINVAL;
+  if (!aligned4(vec) || !aligned4(src) || !aligned4(weights) || !aligned16(x) || !aligned16(messages))
+    return EQTP_EINVAL;
+  eqtp::ConvArgs a;
+  a.N = N;
+  a.E = E;
+  a.lmax = d->lmax;
+  a.C = d->C;
+  a.path_set = d->path_set;
+  a.weight_mode = d->weight_mode;
+  a.edge_order = EQTP_EDGES_UNSORTED;
+  a.r_cut = d->r_cut;
+  a.vec = vec;
+  a.src = src;
+  a.dst = nullptr;
+  a.row_ptr = nullptr;
+  a.x = x;
+  a.w = weights;
+  a.out = messages;
+  a.stream = (hipStream_t)stream;
+  return status_of(eqtp::launch_conv_messages(a));
+}
+
 int eqtp_conv_backward(const eqtp_conv_desc* d, int64_t N, int64_t E, const float* vec, const int32_t* src,
                        const int32_t* dst, const int32_t* row_ptr, const float* x, const float* weights,
                        const float* grad_out, float* grad_x, float* grad_w, float* grad_vec, void* stream) {

@@ -214,6 +214,92 @@ __global__ __launch_bounds__(EdgeCfg<C>::THREADS) void conv_edge_kernel(int N, i
   }
 }
 
+// Per-edge messages without the destination sum (the page's fused kernel
+// output, section "3. operator fusion"): msg[e, c, :] for every edge, lane =
+// channel; a wave's store of one edge covers its C*K*4 contiguous bytes.
+template <int L, int PS, int C, bool RADIAL>
+__global__ __launch_bounds__(EdgeCfg<C>::THREADS) void conv_msg_kernel(int N, int E, const float* __restrict__ vec,
+                                                                       const int* __restrict__ src,
+                                                                       const float* __restrict__ x,
+                                                                       const float* __restrict__ w,
+                                                                       float* __restrict__ msg, float inv_rc) {
+  using Cfg = EdgeCfg<C>;
+  using T = Tables<L, PS>;
+  using M = EdgeMsg<L, PS, C, RADIAL>;
+  constexpr int K = num_comp(L);
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int g = lane / Cfg::CL;
+  const int cl = lane % Cfg::CL;
+  float wreg[Cfg::CPL][T::P];
+  if constexpr (!RADIAL) {
+#pragma unroll
+    for (int j = 0; j < Cfg::CPL; ++j)
+#pragma unroll
+      for (int p = 0; p < T::P; ++p) wreg[j][p] = w[p * C + cl + j * Cfg::CL];
+  }
+  const long long base = ((long long)blockIdx.x * Cfg::WAVES + wv) * Cfg::EPW;
+  const int e_end = (int)min((long long)E, base + Cfg::EPW);
+  for (int e = (int)base + g; e < e_end; e += Cfg::G) {
+    float acc[Cfg::CPL][K];
+#pragma unroll
+    for (int j = 0; j < Cfg::CPL; ++j)
+#pragma unroll
+      for (int k = 0; k < K; ++k) acc[j][k] = 0.0f;
+    M::run(e, N, cl, vec, src, x, w, wreg, inv_rc, acc);
+#pragma unroll
+    for (int j = 0; j < Cfg::CPL; ++j) {
+      float* op = msg + ((size_t)e * C + cl + j * Cfg::CL) * K;
+      if constexpr (K % 4 == 0) {
+#pragma unroll
+        for (int q = 0; q < K / 4; ++q)
+          reinterpret_cast<f4*>(op)[q] = f4{acc[j][4 * q], acc[j][4 * q + 1], acc[j][4 * q + 2], acc[j][4 * q + 3]};
+      } else {
+#pragma unroll
+        for (int k = 0; k < K; ++k) op[k] = acc[j][k];
+      }
+    }
+  }
+}
+
+template <int L, int PS, int C, bool RADIAL>
+static hipError_t launch_msg_t(const ConvArgs& a) {
+  using Cfg = EdgeCfg<C>;
+  if (a.E == 0) return hipSuccess;
+  const long long per_block = (long long)Cfg::WAVES * Cfg::EPW;
+  const unsigned blocks = (unsigned)((a.E + per_block - 1) / per_block);
+  hipLaunchKernelGGL((conv_msg_kernel<L, PS, C, RADIAL>), dim3(blocks), dim3(Cfg::THREADS), 0, a.stream, (int)a.N,
+                     (int)a.E, a.vec, a.src, a.x, a.w, a.out, RADIAL ? 1.0f / a.r_cut : 0.0f);
+  return hipGetLastError();
+}
+
+template <int L, int PS>
+static hipError_t dispatch_msg_c(const ConvArgs& a) {
+  const bool radial = a.weight_mode == 1;
+  switch (a.C) {
+    case 8: return radial ? launch_msg_t<L, PS, 8, true>(a) : launch_msg_t<L, PS, 8, false>(a);
+    case 16: return radial ? launch_msg_t<L, PS, 16, true>(a) : launch_msg_t<L, PS, 16, false>(a);
+    case 32: return radial ? launch_msg_t<L, PS, 32, true>(a) : launch_msg_t<L, PS, 32, false>(a);
+    case 64: return radial ? launch_msg_t<L, PS, 64, true>(a) : launch_msg_t<L, PS, 64, false>(a);
+    case 128: return radial ? launch_msg_t<L, PS, 128, true>(a) : launch_msg_t<L, PS, 128, false>(a);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_conv_messages(const ConvArgs& a) {
+  switch (a.lmax * 2 + a.path_set) {
+    case 0: return dispatch_msg_c<0, 0>(a);
+    case 1: return dispatch_msg_c<0, 1>(a);
+    case 2: return dispatch_msg_c<1, 0>(a);
+    case 3: return dispatch_msg_c<1, 1>(a);
+    case 4: return dispatch_msg_c<2, 0>(a);
+    case 5: return dispatch_msg_c<2, 1>(a);
+    case 6: return dispatch_msg_c<3, 0>(a);
+    case 7: return dispatch_msg_c<3, 1>(a);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 // Test-only twin of the sorted walk: same launch shape, row -> wave and
 // edge -> lane-group dealing, and the same cross-lane combine.
 template <int C>

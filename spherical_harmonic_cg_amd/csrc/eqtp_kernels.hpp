@@ -51,6 +51,7 @@ struct BwdArgs {
 hipError_t launch_sh(const float* vec, int64_t E, int lmax, float* Y, hipStream_t stream);
 hipError_t launch_conv_node(const ConvArgs& a);   // sorted edges, fixed weights, matrix cores
 hipError_t launch_conv_edge(const ConvArgs& a);   // any order / weights, vector ALUs
+hipError_t launch_conv_messages(const ConvArgs& a);  // per-edge messages into out [E, C, K]
 hipError_t launch_probe_node(const ProbeArgs& a);
 hipError_t launch_probe_edge(const ProbeArgs& a);
 hipError_t launch_linear(int64_t N, int C, int lmax, int bf16, const float* h, const float* W, float* out,

@@ -24,7 +24,8 @@ EQTP_EDGES_DST_SORTED, EQTP_EDGES_UNSORTED = 0, 1
 EQTP_ALGO_AUTO, EQTP_ALGO_NODE_MFMA, EQTP_ALGO_EDGE_VALU = 0, 1, 2
 EQTP_F32, EQTP_BF16 = 0, 1
 
-EXPORTED = ("eqtp_num_paths", "eqtp_path_table", "eqtp_sh", "eqtp_conv_fused", "eqtp_conv_backward", "eqtp_linear",
+EXPORTED = ("eqtp_num_paths", "eqtp_path_table", "eqtp_sh", "eqtp_conv_fused", "eqtp_conv_messages",
+            "eqtp_conv_backward", "eqtp_linear",
             "eqtp_status_string", "eqtp_test_segment_probe")
 
 
@@ -61,6 +62,8 @@ def load_library(path: str = LIB_PATH):
             lib.eqtp_sh.restype = i32
             lib.eqtp_conv_fused.argtypes = [ctypes.POINTER(_ConvDesc), i64, i64, vp, vp, vp, vp, vp, vp, vp, vp]
             lib.eqtp_conv_fused.restype = i32
+            lib.eqtp_conv_messages.argtypes = [ctypes.POINTER(_ConvDesc), i64, i64] + [vp] * 6
+            lib.eqtp_conv_messages.restype = i32
             lib.eqtp_conv_backward.argtypes = [ctypes.POINTER(_ConvDesc), i64, i64] + [vp] * 11
             lib.eqtp_conv_backward.restype = i32
             lib.eqtp_linear.argtypes = [i64, i32, i32, i32, vp, vp, vp, vp]
@@ -178,6 +181,34 @@ def eqtp_conv_fused(vec, src, x, weights, lmax: int, row_ptr=None, dst=None, pat
     rc = load_library().eqtp_conv_fused(ctypes.byref(d), N, E, _ptr(vec), _ptr(src), _ptr(dst), _ptr(row_ptr),
                                         _ptr(x), _ptr(weights), _ptr(out), _stream())
     _raise(rc, "eqtp_conv_fused")
+    return out
+
+
+def eqtp_conv_messages(vec, src, x, weights, lmax: int, path_set: int = EQTP_PATHS_PARITY,
+                       weight_mode: int = EQTP_W_FIXED, r_cut: float = 0.0, n_basis: int = 8, out=None):
+    """messages [E, C, K]: one message per edge, no destination sum."""
+    import torch
+
+    _check(x, "x", torch.float32)
+    if x.dim() != 3:
+        raise ValueError("x must be [N, C, K]")
+    N, C, K = x.shape
+    if K != (lmax + 1) ** 2:
+        raise ValueError("x has %d components, lmax %d needs %d" % (K, lmax, (lmax + 1) ** 2))
+    _check(vec, "vec", torch.float32)
+    E = vec.shape[0]
+    _check(src, "src", torch.int32, (E,))
+    P = eqtp_num_paths(lmax, path_set)
+    wshape = (P, C) if weight_mode == EQTP_W_FIXED else (n_basis, P * C)
+    _check(weights, "weights", torch.float32, wshape)
+    if out is None:
+        out = torch.empty((E, C, K), dtype=torch.float32, device=x.device)
+    _check(out, "out", torch.float32, (E, C, K))
+    d = _ConvDesc(ctypes.sizeof(_ConvDesc), lmax, C, path_set, weight_mode, EQTP_EDGES_UNSORTED, EQTP_ALGO_AUTO,
+                  float(r_cut), n_basis)
+    rc = load_library().eqtp_conv_messages(ctypes.byref(d), N, E, _ptr(vec), _ptr(src), _ptr(x), _ptr(weights),
+                                           _ptr(out), _stream())
+    _raise(rc, "eqtp_conv_messages")
     return out
 
 

@@ -143,3 +143,21 @@ def test_conv_backward_validation():
     bad = _desc(e)
     bad.struct_size = 8
     assert call(bad) == 1
+
+
+def test_conv_messages_validation():
+    e = _lib()
+    lib = e.load_library()
+
+    def call(d, N=10, E=20, vec=FAKE, src=FAKE, x=FAKE, w=FAKE, m=FAKE):
+        return lib.eqtp_conv_messages(ctypes.byref(d), N, E, vec, src, x, w, m, NULL)
+
+    assert call(_desc(e, lmax=4)) == 2
+    assert call(_desc(e, C=24)) == 2
+    assert call(_desc(e, weight_mode=1, r_cut=0.0)) == 1
+    assert call(_desc(e, weight_mode=1, r_cut=4.0, n_basis=4)) == 2
+    assert call(_desc(e), m=NULL) == 1
+    assert call(_desc(e), x=NULL) == 1
+    assert call(_desc(e), m=ctypes.c_void_p(0x10008)) == 1               # messages not 16-byte aligned
+    assert call(_desc(e), N=0) == 1                                       # edges without nodes
+    assert call(_desc(e), E=0, vec=NULL, src=NULL, m=NULL) == 0           # no edges: nothing to do
