@@ -63,7 +63,7 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def measured_traffic(config, atom_order, unsorted, algo, path_set="parity"):
+def measured_traffic(config, atom_order, unsorted, algo, path_set="parity", x_bf16=False):
     """HBM-side bytes per launch of the conv kernel from the committed counter
     summary (profiles/traffic.json), or None when that summary was taken on
     different kernel sources or another workload."""
@@ -77,6 +77,8 @@ def measured_traffic(config, atom_order, unsorted, algo, path_set="parity"):
     key = "%s/%s/%s/%d" % (config, atom_order, "unsorted" if unsorted else "sorted", algo)
     if path_set != "parity":
         key += "/" + path_set
+    if x_bf16:
+        key += "/xbf16"
     ent = rec.get(key)
     if not ent or ent.get("source_sha256_16") != kernel_source_hash():
         return None
@@ -126,6 +128,8 @@ def main():
                     help="'cell': spatially coherent atom numbering (a labelled extra, not the headline)")
     ap.add_argument("--path-set", default="parity", choices=("parity", "so3"),
                     help="'so3': the 34-path SO(3) set (a labelled extra, not the headline)")
+    ap.add_argument("--x-bf16", action="store_true",
+                    help="bfloat16 node features (a labelled extra: halves the gathered bytes)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
     ap.add_argument("--backward", action="store_true",
@@ -166,10 +170,12 @@ def main():
     else:
         vec, src, dst, row_ptr = T(wl.vec), T(wl.src), None, T(wl.row_ptr)
     x = T(wl.x)
+    if args.x_bf16:
+        x = x.to(torch.bfloat16)
     w = T(wl.weights)
-    out = torch.empty_like(x)
+    out = torch.empty(x.shape, dtype=torch.float32, device=dev)
     w_lin = T(wl.w_lin) if wl.w_lin is not None else None
-    out2 = torch.empty_like(x) if w_lin is not None else None
+    out2 = torch.empty_like(out) if w_lin is not None else None
     lin_dtype = eq.EQTP_BF16 if wl.linear_bf16 else eq.EQTP_F32
     stream = torch.cuda.current_stream()
 
@@ -213,10 +219,10 @@ def main():
 
     backward = None
     if args.backward:
-        if wl.weight_mode != 0:
-            log("backward: fixed weights only; skipped for this workload")
+        if wl.weight_mode != 0 or args.x_bf16:
+            log("backward: fp32 features and fixed weights only; skipped for this workload")
         else:
-            gout = torch.randn_like(x)
+            gout = torch.randn(out.shape, dtype=torch.float32, device=dev)
             bkw = dict(dst=dst) if args.unsorted else dict(row_ptr=row_ptr)
 
             def bwd():
@@ -239,7 +245,9 @@ def main():
             log("backward: %.4f ms (%.3e edges/s)" % (bms, wl.E / (bms * 1e-3)))
 
     messages = None
-    if args.messages:
+    if args.messages and args.x_bf16:
+        log("messages: fp32 features only; skipped")
+    elif args.messages:
         msg_out = torch.empty((wl.E, wl.C, wl.K), dtype=torch.float32, device=dev)
 
         def msg():
@@ -282,7 +290,8 @@ def main():
     achieved_tflops = flop_edge * wl.E / conv_s / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved_tflops, 3), "peak": PEAK_FP32_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved_tflops / PEAK_FP32_TFLOPS, 4),
-                "traffic": measured_traffic(args.config, args.atom_order, args.unsorted, args.algo, args.path_set)}
+                "traffic": measured_traffic(args.config, args.atom_order, args.unsorted, args.algo, args.path_set,
+                                            args.x_bf16)}
     alg_bytes = 2 * wl.N * wl.C * wl.K * 4 + wl.E * 16 + (wl.N + 1) * 4 + wl.weights.size * 4
     log("conv: %.3e counted flop (2*nnz*C per edge), %.1f MB algorithmic bytes -> %.1f GB/s" % (
         flop_edge * wl.E, alg_bytes / 1e6, alg_bytes / conv_s / 1e9))
@@ -307,7 +316,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": WORKLOAD_TEXT[args.config] + (" (random edge order)" if args.unsorted else "")
                    + (" (cell-sorted atom numbering)" if args.atom_order == "cell" else "")
-                   + (" (SO(3) path set)" if args.path_set == "so3" else ""),
+                   + (" (SO(3) path set)" if args.path_set == "so3" else "")
+                   + (" (bfloat16 node features)" if args.x_bf16 else ""),
                    "atoms": wl.N, "edges": wl.E, "channels": wl.C, "lmax": wl.lmax, "paths": wl.P,
                    "coupling_nnz": nnz, "algo": args.algo},
         "roofline": roofline,

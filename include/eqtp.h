@@ -105,7 +105,14 @@ typedef struct eqtp_conv_desc {
   int32_t algo;        /* EQTP_ALGO_* */
   float r_cut;         /* radial mode: cut-off radius (> 0) */
   int32_t n_basis;     /* radial mode: number of radial functions, must be 8 */
+  int32_t x_dtype;     /* EQTP_F32 (default) or EQTP_BF16: x holds bfloat16 features,
+                          same [N, C, K] layout, 2 bytes each (eqtp_conv_fused with
+                          dst-sorted edges and fixed weights only).  A descriptor whose
+                          struct_size ends before this field is read as EQTP_F32. */
 } eqtp_conv_desc;
+
+/* struct_size of a descriptor without the x_dtype field (still accepted) */
+#define EQTP_CONV_DESC_SIZE_V1 36
 
 /*
  * Fused convolution: spherical harmonics -> coupling with the source
@@ -124,7 +131,10 @@ typedef struct eqtp_conv_desc {
  *   row_ptr  [N+1] int32 CSR row pointers over dst-sorted edges
  *            (row_ptr[0] = 0, row_ptr[N] = E, non-decreasing); required for
  *            EQTP_EDGES_DST_SORTED, ignored for EQTP_EDGES_UNSORTED.
- *   x        [N, C, K] fp32 node features, 16-byte aligned.
+ *   x        [N, C, K] node features, 16-byte aligned: fp32, or bfloat16 when
+ *            d->x_dtype = EQTP_BF16 (then d->algo must not be
+ *            EQTP_ALGO_EDGE_VALU, and unsorted edges or radial weights give
+ *            EQTP_EUNSUPPORTED); accumulation is fp32 either way.
  *   weights  EQTP_W_FIXED: [P, C] fp32; EQTP_W_RADIAL: [8, P*C] fp32 with
  *            R_n(r) = sin(n pi r / r_cut) / r * u(r / r_cut), n = 1..8,
  *            u(d) = 1 - 28 d^6 + 48 d^7 - 21 d^8 for d < 1, else 0
@@ -135,7 +145,7 @@ typedef struct eqtp_conv_desc {
  * edges: summation order varies from run to run.
  */
 int eqtp_conv_fused(const eqtp_conv_desc* d, int64_t N, int64_t E, const float* vec, const int32_t* src,
-                    const int32_t* dst, const int32_t* row_ptr, const float* x, const float* weights, float* out,
+                    const int32_t* dst, const int32_t* row_ptr, const void* x, const float* weights, float* out,
                     void* stream);
 
 /*

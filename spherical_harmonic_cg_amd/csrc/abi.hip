@@ -1,5 +1,6 @@
 // abi.hip -- the extern "C" entry points declared in include/eqtp.h:
 // argument validation, kernel selection and launch on the caller's stream.
+#include <stddef.h>
 #include <stdint.h>
 
 #include "../../include/eqtp.h"
@@ -11,6 +12,16 @@ namespace {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 bool valid_c(int C) { return C == 8 || C == 16 || C == 32 || C == 64 || C == 128; }
+
+static_assert(offsetof(eqtp_conv_desc, x_dtype) == EQTP_CONV_DESC_SIZE_V1, "descriptor layout");
+
+// descriptor version check: the current size, or the size before x_dtype
+bool desc_ok(const eqtp_conv_desc* d) {
+  return d && (d->struct_size == (int32_t)sizeof(eqtp_conv_desc) || d->struct_size == EQTP_CONV_DESC_SIZE_V1);
+}
+int desc_x_dtype(const eqtp_conv_desc* d) {
+  return d->struct_size >= (int32_t)sizeof(eqtp_conv_desc) ? d->x_dtype : EQTP_F32;
+}
 constexpr int64_t kMaxIndex = (int64_t(1) << 31) - 1;
 
 int num_paths_host(int lmax, int path_set) {
@@ -62,9 +73,11 @@ int eqtp_sh(const float* vec, int64_t E, int lmax, float* Y, void* stream) {
 }
 
 int eqtp_conv_fused(const eqtp_conv_desc* d, int64_t N, int64_t E, const float* vec, const int32_t* src,
-                    const int32_t* dst, const int32_t* row_ptr, const float* x, const float* weights, float* out,
+                    const int32_t* dst, const int32_t* row_ptr, const void* x, const float* weights, float* out,
                     void* stream) {
-  if (!d || d->struct_size != (int32_t)sizeof(eqtp_conv_desc)) return EQTP_EINVAL;
+  if (!desc_ok(d)) return EQTP_EINVAL;
+  const int x_dtype = desc_x_dtype(d);
+  if (x_dtype != EQTP_F32 && x_dtype != EQTP_BF16) return EQTP_EINVAL;
   if (d->lmax < 0) return EQTP_EINVAL;
   if (d->lmax > 3) return EQTP_EUNSUPPORTED;
   if (d->path_set != EQTP_PATHS_PARITY && d->path_set != EQTP_PATHS_SO3) return EQTP_EINVAL;
@@ -83,6 +96,7 @@ int eqtp_conv_fused(const eqtp_conv_desc* d, int64_t N, int64_t E, const float* 
   // the node-factored algorithm needs per-node sums of edge-independent weights
   const bool node_ok = d->edge_order == EQTP_EDGES_DST_SORTED && d->weight_mode == EQTP_W_FIXED;
   if (d->algo == EQTP_ALGO_NODE_MFMA && !node_ok) return EQTP_EUNSUPPORTED;
+  if (x_dtype == EQTP_BF16 && (!node_ok || d->algo == EQTP_ALGO_EDGE_VALU)) return EQTP_EUNSUPPORTED;
   if (N == 0) return EQTP_OK;
   if (!x || !out || !weights || !aligned16(x) || !aligned16(out) || !aligned4(weights)) return EQTP_EINVAL;
   if (E > 0) {
@@ -106,7 +120,8 @@ int eqtp_conv_fused(const eqtp_conv_desc* d, int64_t N, int64_t E, const float* 
   a.src = src;
   a.dst = dst;
   a.row_ptr = row_ptr;
-  a.x = x;
+  a.x = static_cast<const float*>(x);
+  a.x_bf16 = x_dtype == EQTP_BF16;
   a.w = weights;
   a.out = out;
   a.stream = (hipStream_t)stream;
@@ -116,7 +131,8 @@ int eqtp_conv_fused(const eqtp_conv_desc* d, int64_t N, int64_t E, const float* 
 
 int eqtp_conv_messages(const eqtp_conv_desc* d, int64_t N, int64_t E, const float* vec, const int32_t* src,
                        const float* x, const float* weights, float* messages, void* stream) {
-  if (!d || d->struct_size != (int32_t)sizeof(eqtp_conv_desc)) return EQTP_EINVAL;
+  if (!desc_ok(d)) return EQTP_EINVAL;
+  if (desc_x_dtype(d) != EQTP_F32) return desc_x_dtype(d) == EQTP_BF16 ? EQTP_EUNSUPPORTED : EQTP_EINVAL;
   if (d->lmax < 0) return EQTP_EINVAL;
   if (d->lmax > 3) return EQTP_EUNSUPPORTED;
   if (d->path_set != EQTP_PATHS_PARITY && d->path_set != EQTP_PATHS_SO3) return EQTP_EINVAL;
@@ -156,7 +172,8 @@ int eqtp_conv_messages(const eqtp_conv_desc* d, int64_t N, int64_t E, const floa
 int eqtp_conv_backward(const eqtp_conv_desc* d, int64_t N, int64_t E, const float* vec, const int32_t* src,
                        const int32_t* dst, const int32_t* row_ptr, const float* x, const float* weights,
                        const float* grad_out, float* grad_x, float* grad_w, float* grad_vec, void* stream) {
-  if (!d || d->struct_size != (int32_t)sizeof(eqtp_conv_desc)) return EQTP_EINVAL;
+  if (!desc_ok(d)) return EQTP_EINVAL;
+  if (desc_x_dtype(d) != EQTP_F32) return desc_x_dtype(d) == EQTP_BF16 ? EQTP_EUNSUPPORTED : EQTP_EINVAL;
   if (d->lmax < 0) return EQTP_EINVAL;
   if (d->lmax > 3) return EQTP_EUNSUPPORTED;
   if (d->path_set != EQTP_PATHS_PARITY && d->path_set != EQTP_PATHS_SO3) return EQTP_EINVAL;

@@ -155,10 +155,12 @@ __device__ __forceinline__ void node_tasks(int N, int E, const int* __restrict__
   }
 }
 
-template <int L, int PS, int C, bool BUF>
+// XB: the node features are bfloat16 (widened to fp32 on load: a bf16 value
+// is the upper half of the fp32 with the same bits), halving the gather.
+template <int L, int PS, int C, bool BUF, bool XB>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void conv_node_kernel(
     int N, int E, const int* __restrict__ row_ptr, const float* __restrict__ vec, const int* __restrict__ src,
-    const float* __restrict__ x, const float* __restrict__ w, float* __restrict__ out) {
+    const void* __restrict__ xp, const float* __restrict__ w, float* __restrict__ out) {
   using Cfg = NodeCfg<L, C>;
   using T = Tables<L, PS>;
   constexpr int K = Cfg::K;
@@ -167,7 +169,41 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void co
   const int lane = threadIdx.x & 63;
   float* ystg = lds;
   int* sstg = reinterpret_cast<int*>(lds + 64 * 16);
-  const rsrc_t rx = make_rsrc(x, (uint64_t)N * C * K * 4u);
+  constexpr uint32_t XS = XB ? 2u : 4u;  // bytes per feature element
+  const rsrc_t rx = make_rsrc(xp, (uint64_t)N * C * K * XS);
+  const float* const x = static_cast<const float*>(xp);
+  const uint16_t* const xh = static_cast<const uint16_t*>(xp);
+  // 4 consecutive features from element index i, or 1 (zeros when !v)
+  auto ld4 = [&](size_t i, bool v) -> f4 {
+    if constexpr (XB) {
+      uint32_t d0 = 0, d1 = 0;
+      if constexpr (BUF) {
+        const auto t = __builtin_amdgcn_raw_buffer_load_b64(rx, v ? (int)(uint32_t)(i * 2) : (int)kOutOfRange, 0, 0);
+        d0 = t[0];
+        d1 = t[1];
+      } else if (v) {
+        const uint2 t = *reinterpret_cast<const uint2*>(xh + i);
+        d0 = t.x;
+        d1 = t.y;
+      }
+      return f4{__uint_as_float(d0 << 16), __uint_as_float(d0 & 0xffff0000u), __uint_as_float(d1 << 16),
+                __uint_as_float(d1 & 0xffff0000u)};
+    } else {
+      if constexpr (BUF) return buf_f4(rx, v ? (uint32_t)(i * 4) : kOutOfRange);
+      else return v ? *reinterpret_cast<const f4*>(x + i) : f4{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  auto ld1 = [&](size_t i, bool v) -> float {
+    if constexpr (XB) {
+      uint32_t h = 0;
+      if constexpr (BUF) h = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rx, v ? (int)(uint32_t)(i * 2) : (int)kOutOfRange, 0, 0);
+      else if (v) h = xh[i];
+      return __uint_as_float(h << 16);
+    } else {
+      if constexpr (BUF) return buf_f32(rx, v ? (uint32_t)(i * 4) : kOutOfRange);
+      else return v ? x[i] : 0.0f;
+    }
+  };
 
   const int cl = lane & 15;  // MFMA column = channel within the block
   const bool c_ok = cl < Cfg::CW;
@@ -206,14 +242,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void co
       for (int j = 0; j < 4; ++j) {
         const int cw = 4 * j + (cl >> 2);
         const bool v = ok && cw < Cfg::CW;
-        f4 t;
-        if constexpr (BUF) {
-          const uint32_t off = v ? (uint32_t)((((size_t)s * C + c_base + cw) * K + 4 * (cl & 3)) * 4) : kOutOfRange;
-          t = buf_f4(rx, off);
-        } else {
-          t = v ? *reinterpret_cast<const f4*>(x + ((size_t)s * C + c_base + cw) * K + 4 * (cl & 3))
-                : f4{0.f, 0.f, 0.f, 0.f};
-        }
+        const f4 t = ld4(v ? ((size_t)s * C + c_base + cw) * K + 4 * (cl & 3) : 0, v);
         d.xv[4 * j] = t[0];
         d.xv[4 * j + 1] = t[1];
         d.xv[4 * j + 2] = t[2];
@@ -225,9 +254,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void co
       if constexpr (K % 4 == 0) {
 #pragma unroll
         for (int q = 0; q < K / 4; ++q) {
-          f4 t;
-          if constexpr (BUF) t = buf_f4(rx, v ? (uint32_t)((e0 + 4 * q) * 4) : kOutOfRange);
-          else t = v ? *reinterpret_cast<const f4*>(x + e0 + 4 * q) : f4{0.f, 0.f, 0.f, 0.f};
+          const f4 t = ld4(e0 + 4 * q, v);
           d.xv[4 * q] = t[0];
           d.xv[4 * q + 1] = t[1];
           d.xv[4 * q + 2] = t[2];
@@ -235,10 +262,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void co
         }
       } else {
 #pragma unroll
-        for (int k = 0; k < K; ++k) {
-          if constexpr (BUF) d.xv[k] = buf_f32(rx, v ? (uint32_t)((e0 + k) * 4) : kOutOfRange);
-          else d.xv[k] = v ? x[e0 + k] : 0.0f;
-        }
+        for (int k = 0; k < K; ++k) d.xv[k] = ld1(e0 + k, v);
       }
     }
     return d;
@@ -388,13 +412,24 @@ template <int L, int PS, int C>
 static hipError_t launch_node(const ConvArgs& a) {
   using Cfg = NodeCfg<L, C>;
   if (a.N == 0) return hipSuccess;
-  const bool buf = (uint64_t)a.N * C * Cfg::K * 4u <= kMaxBufferBytes && (uint64_t)a.E * 12u <= kMaxBufferBytes;
-  if (buf)
-    hipLaunchKernelGGL((conv_node_kernel<L, PS, C, true>), dim3(node_grid<L, C>(a.N)), dim3(Cfg::THREADS), 0,
-                       a.stream, (int)a.N, (int)a.E, a.row_ptr, a.vec, a.src, a.x, a.w, a.out);
-  else
-    hipLaunchKernelGGL((conv_node_kernel<L, PS, C, false>), dim3(node_grid<L, C>(a.N)), dim3(Cfg::THREADS), 0,
-                       a.stream, (int)a.N, (int)a.E, a.row_ptr, a.vec, a.src, a.x, a.w, a.out);
+  const uint64_t xs = a.x_bf16 ? 2u : 4u;
+  const bool buf = (uint64_t)a.N * C * Cfg::K * xs <= kMaxBufferBytes && (uint64_t)a.E * 12u <= kMaxBufferBytes;
+  const dim3 grid(node_grid<L, C>(a.N)), block(Cfg::THREADS);
+  if (a.x_bf16) {
+    if (buf)
+      hipLaunchKernelGGL((conv_node_kernel<L, PS, C, true, true>), grid, block, 0, a.stream, (int)a.N, (int)a.E,
+                         a.row_ptr, a.vec, a.src, a.x, a.w, a.out);
+    else
+      hipLaunchKernelGGL((conv_node_kernel<L, PS, C, false, true>), grid, block, 0, a.stream, (int)a.N, (int)a.E,
+                         a.row_ptr, a.vec, a.src, a.x, a.w, a.out);
+  } else {
+    if (buf)
+      hipLaunchKernelGGL((conv_node_kernel<L, PS, C, true, false>), grid, block, 0, a.stream, (int)a.N, (int)a.E,
+                         a.row_ptr, a.vec, a.src, a.x, a.w, a.out);
+    else
+      hipLaunchKernelGGL((conv_node_kernel<L, PS, C, false, false>), grid, block, 0, a.stream, (int)a.N, (int)a.E,
+                         a.row_ptr, a.vec, a.src, a.x, a.w, a.out);
+  }
   return hipGetLastError();
 }
 

@@ -11,6 +11,7 @@ namespace eqtp {
 struct ConvArgs {
   int64_t N, E;
   int lmax, C, path_set, weight_mode, edge_order;
+  int x_bf16 = 0;  // x holds bfloat16 features (node algorithm only)
   float r_cut;
   const float* vec;
   const int32_t* src;

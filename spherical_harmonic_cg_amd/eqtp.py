@@ -38,7 +38,8 @@ class EqtpError(RuntimeError):
 class _ConvDesc(ctypes.Structure):
     _fields_ = [("struct_size", ctypes.c_int32), ("lmax", ctypes.c_int32), ("C", ctypes.c_int32),
                 ("path_set", ctypes.c_int32), ("weight_mode", ctypes.c_int32), ("edge_order", ctypes.c_int32),
-                ("algo", ctypes.c_int32), ("r_cut", ctypes.c_float), ("n_basis", ctypes.c_int32)]
+                ("algo", ctypes.c_int32), ("r_cut", ctypes.c_float), ("n_basis", ctypes.c_int32),
+                ("x_dtype", ctypes.c_int32)]
 
 
 _lib = None
@@ -149,10 +150,13 @@ def eqtp_conv_fused(vec, src, x, weights, lmax: int, row_ptr=None, dst=None, pat
 
     Give ``row_ptr`` [N+1] for dst-sorted edges, or ``dst`` [E] for any order
     (atomic accumulation).  ``weights`` is [P, C] (fixed) or [8, P*C] (radial).
+    ``x`` is float32, or bfloat16 (dst-sorted edges, fixed weights); ``out``
+    is float32.
     """
     import torch
 
-    _check(x, "x", torch.float32)
+    x_dtype = EQTP_BF16 if x.dtype == torch.bfloat16 else EQTP_F32
+    _check(x, "x", torch.bfloat16 if x_dtype == EQTP_BF16 else torch.float32)
     if x.dim() != 3:
         raise ValueError("x must be [N, C, K]")
     N, C, K = x.shape
@@ -175,9 +179,10 @@ def eqtp_conv_fused(vec, src, x, weights, lmax: int, row_ptr=None, dst=None, pat
     if tuple(weights.shape) != wshape:
         raise ValueError("weights has shape %s, expected %s" % (tuple(weights.shape), wshape))
     if out is None:
-        out = torch.empty_like(x)
+        out = torch.empty((N, C, K), dtype=torch.float32, device=x.device)
     _check(out, "out", torch.float32, (N, C, K))
-    d = _ConvDesc(ctypes.sizeof(_ConvDesc), lmax, C, path_set, weight_mode, order, algo, float(r_cut), n_basis)
+    d = _ConvDesc(ctypes.sizeof(_ConvDesc), lmax, C, path_set, weight_mode, order, algo, float(r_cut), n_basis,
+                  x_dtype)
     rc = load_library().eqtp_conv_fused(ctypes.byref(d), N, E, _ptr(vec), _ptr(src), _ptr(dst), _ptr(row_ptr),
                                         _ptr(x), _ptr(weights), _ptr(out), _stream())
     _raise(rc, "eqtp_conv_fused")
@@ -205,7 +210,7 @@ def eqtp_conv_messages(vec, src, x, weights, lmax: int, path_set: int = EQTP_PAT
         out = torch.empty((E, C, K), dtype=torch.float32, device=x.device)
     _check(out, "out", torch.float32, (E, C, K))
     d = _ConvDesc(ctypes.sizeof(_ConvDesc), lmax, C, path_set, weight_mode, EQTP_EDGES_UNSORTED, EQTP_ALGO_AUTO,
-                  float(r_cut), n_basis)
+                  float(r_cut), n_basis, EQTP_F32)
     rc = load_library().eqtp_conv_messages(ctypes.byref(d), N, E, _ptr(vec), _ptr(src), _ptr(x), _ptr(weights),
                                            _ptr(out), _stream())
     _raise(rc, "eqtp_conv_messages")
@@ -244,7 +249,7 @@ def eqtp_conv_backward(vec, src, x, weights, grad_out, lmax: int, row_ptr=None, 
     gx = torch.empty_like(x) if need_x else None
     gw = torch.empty_like(weights) if need_w else None
     gv = torch.empty((E, 3), dtype=torch.float32, device=x.device) if need_vec else None
-    d = _ConvDesc(ctypes.sizeof(_ConvDesc), lmax, C, path_set, EQTP_W_FIXED, order, EQTP_ALGO_AUTO, 0.0, 8)
+    d = _ConvDesc(ctypes.sizeof(_ConvDesc), lmax, C, path_set, EQTP_W_FIXED, order, EQTP_ALGO_AUTO, 0.0, 8, EQTP_F32)
     rc = load_library().eqtp_conv_backward(ctypes.byref(d), N, E, _ptr(vec), _ptr(src), _ptr(dst), _ptr(row_ptr),
                                            _ptr(x), _ptr(weights), _ptr(grad_out), _ptr(gx), _ptr(gw), _ptr(gv),
                                            _stream())

@@ -59,10 +59,10 @@ def test_status_strings():
 
 
 def _desc(e, **kw):
-    d = dict(lmax=3, C=64, path_set=0, weight_mode=0, edge_order=0, algo=0, r_cut=0.0, n_basis=8)
+    d = dict(lmax=3, C=64, path_set=0, weight_mode=0, edge_order=0, algo=0, r_cut=0.0, n_basis=8, x_dtype=0)
     d.update(kw)
     return e._ConvDesc(ctypes.sizeof(e._ConvDesc), d["lmax"], d["C"], d["path_set"], d["weight_mode"],
-                       d["edge_order"], d["algo"], d["r_cut"], d["n_basis"])
+                       d["edge_order"], d["algo"], d["r_cut"], d["n_basis"], d["x_dtype"])
 
 
 FAKE = ctypes.c_void_p(0x10000)  # never dereferenced: every call below is rejected first
@@ -161,3 +161,25 @@ def test_conv_messages_validation():
     assert call(_desc(e), m=ctypes.c_void_p(0x10008)) == 1               # messages not 16-byte aligned
     assert call(_desc(e), N=0) == 1                                       # edges without nodes
     assert call(_desc(e), E=0, vec=NULL, src=NULL, m=NULL) == 0           # no edges: nothing to do
+
+
+def test_descriptor_versions_and_feature_dtype():
+    e = _lib()
+    lib = e.load_library()
+    assert ctypes.sizeof(e._ConvDesc) == 40
+    conv = lambda d, **kw: lib.eqtp_conv_fused(ctypes.byref(d), 10, 20, FAKE, FAKE, kw.get("dst", NULL),
+                                               kw.get("rp", FAKE), FAKE, FAKE, FAKE, NULL)
+    v1 = _desc(e, lmax=4)
+    v1.struct_size = 36  # a descriptor from before the x_dtype field: accepted, read as fp32 features
+    assert conv(v1) == 2
+    v1b = _desc(e, lmax=4, x_dtype=1)
+    v1b.struct_size = 36  # x_dtype lies past struct_size, so it is not read
+    assert conv(v1b) == 2
+    assert conv(_desc(e, x_dtype=7)) == 1
+    assert conv(_desc(e, x_dtype=1, edge_order=1), dst=FAKE, rp=NULL) == 2     # bf16 features: node algorithm only
+    assert conv(_desc(e, x_dtype=1, weight_mode=1, r_cut=4.0)) == 2
+    assert conv(_desc(e, x_dtype=1, algo=2)) == 2
+    bf = _desc(e, x_dtype=1)
+    assert lib.eqtp_conv_messages(ctypes.byref(bf), 10, 20, FAKE, FAKE, FAKE, FAKE, FAKE, NULL) == 2
+    assert lib.eqtp_conv_backward(ctypes.byref(bf), 10, 20, FAKE, FAKE, NULL, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                  FAKE, NULL) == 2
