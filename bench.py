@@ -63,7 +63,7 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def measured_traffic(config, atom_order, unsorted, algo, path_set="parity", x_bf16=False):
+def measured_traffic(config, atom_order, unsorted, algo, path_set="parity", x_bf16=False, sort_edges=False):
     """HBM-side bytes per launch of the conv kernel from the committed counter
     summary (profiles/traffic.json), or None when that summary was taken on
     different kernel sources or another workload."""
@@ -74,7 +74,8 @@ def measured_traffic(config, atom_order, unsorted, algo, path_set="parity", x_bf
         rec = json.load(open(path))
     except ValueError:
         return None
-    key = "%s/%s/%s/%d" % (config, atom_order, "unsorted" if unsorted else "sorted", algo)
+    order = ("unsorted+gpusort" if sort_edges else "unsorted") if unsorted else "sorted"
+    key = "%s/%s/%s/%d" % (config, atom_order, order, algo)
     if path_set != "parity":
         key += "/" + path_set
     if x_bf16:
@@ -124,6 +125,9 @@ def main():
     ap.add_argument("--config", default="mid", choices=sorted(WORKLOAD_TEXT))
     ap.add_argument("--algo", type=int, default=0, help="0 auto, 1 node/matrix cores, 2 edge/vector ALUs")
     ap.add_argument("--unsorted", action="store_true", help="random edge order (atomic path)")
+    ap.add_argument("--sort-edges", action="store_true",
+                    help="with --unsorted: each step groups the edges by destination on the GPU "
+                         "(eqtp_sort_edges) and runs the dst-sorted conv on them, instead of the atomic path")
     ap.add_argument("--atom-order", default="generation", choices=("generation", "cell"),
                     help="'cell': spatially coherent atom numbering (a labelled extra, not the headline)")
     ap.add_argument("--path-set", default="parity", choices=("parity", "so3"),
@@ -140,6 +144,8 @@ def main():
                     help="after timing, run one 256 MiB device copy (counter calibration)")
     args = ap.parse_args()
 
+    if args.sort_edges and not args.unsorted:
+        ap.error("--sort-edges needs --unsorted")
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path (a split into CSR "
               "row ranges with a halo exchange of source features is not built); run with --gpus 1.",
@@ -179,7 +185,21 @@ def main():
     lin_dtype = eq.EQTP_BF16 if wl.linear_bf16 else eq.EQTP_F32
     stream = torch.cuda.current_stream()
 
+    sort_out = None
+    if args.sort_edges:
+        sort_out = (torch.empty(wl.N + 1, dtype=torch.int32, device=dev), torch.empty_like(src),
+                    torch.empty_like(vec), torch.empty_like(src))
+
+    def sort():
+        if sort_out is not None:
+            eq.eqtp_sort_edges(dst, wl.N, vec=vec, src=src, out=sort_out)
+
     def conv():
+        if sort_out is not None:
+            rp_s, _, vec_s, src_s = sort_out
+            eq.eqtp_conv_fused(vec_s, src_s, x, w, wl.lmax, row_ptr=rp_s, path_set=wl.path_set,
+                               weight_mode=wl.weight_mode, r_cut=wl.r_cut, algo=args.algo, out=out)
+            return
         eq.eqtp_conv_fused(vec, src, x, w, wl.lmax, row_ptr=row_ptr, dst=dst, path_set=wl.path_set,
                            weight_mode=wl.weight_mode, r_cut=wl.r_cut, algo=args.algo, out=out)
 
@@ -188,13 +208,13 @@ def main():
             eq.eqtp_linear(out, w_lin, wl.lmax, lin_dtype, out=out2)
 
     for _ in range(args.warmup):
+        sort()
         conv()
         linear()
     torch.cuda.synchronize()
 
     K = args.steps
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-           torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    ev = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(4)) for _ in range(K)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -202,20 +222,25 @@ def main():
     t_start.record(stream)
     for i in range(K):
         ev[i][0].record(stream)
-        conv()
+        sort()
         ev[i][1].record(stream)
-        linear()
+        conv()
         ev[i][2].record(stream)
+        linear()
+        ev[i][3].record(stream)
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     total_ms = t_start.elapsed_time(t_end)
-    conv_ms = np.array([a.elapsed_time(b) for a, b, _ in ev])
-    lin_ms = np.array([b.elapsed_time(c) for _, b, c in ev])
+    sort_ms = np.array([a.elapsed_time(b) for a, b, _, _ in ev])
+    conv_ms = np.array([b.elapsed_time(c) for _, b, c, _ in ev])
+    lin_ms = np.array([c.elapsed_time(d) for _, _, c, d in ev])
     ms_per_step = total_ms / K
     log("timed %d steps: %.4f ms/step (events), wall %.4f ms/step; conv avg %.4f ms (p10 %.4f p90 %.4f), "
         "linear avg %.4f ms" % (K, ms_per_step, 1e3 * wall / K, conv_ms.mean(), np.percentile(conv_ms, 10),
                                 np.percentile(conv_ms, 90), lin_ms.mean()))
+    if sort_out is not None:
+        log("edge sort (eqtp_sort_edges) avg %.4f ms per step, inside the step" % sort_ms.mean())
 
     backward = None
     if args.backward:
@@ -224,9 +249,13 @@ def main():
         else:
             gout = torch.randn(out.shape, dtype=torch.float32, device=dev)
             bkw = dict(dst=dst) if args.unsorted else dict(row_ptr=row_ptr)
+            bvec, bsrc = vec, src
+            if sort_out is not None:
+                bkw = dict(row_ptr=sort_out[0])
+                bvec, bsrc = sort_out[2], sort_out[3]
 
             def bwd():
-                eq.eqtp_conv_backward(vec, src, x, w, gout, wl.lmax, path_set=wl.path_set, **bkw)
+                eq.eqtp_conv_backward(bvec, bsrc, x, w, gout, wl.lmax, path_set=wl.path_set, **bkw)
 
             for _ in range(max(3, args.warmup // 4)):
                 bwd()
@@ -291,7 +320,7 @@ def main():
     roofline = {"bound": "mfma", "achieved": round(achieved_tflops, 3), "peak": PEAK_FP32_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved_tflops / PEAK_FP32_TFLOPS, 4),
                 "traffic": measured_traffic(args.config, args.atom_order, args.unsorted, args.algo, args.path_set,
-                                            args.x_bf16)}
+                                            args.x_bf16, args.sort_edges)}
     alg_bytes = 2 * wl.N * wl.C * wl.K * 4 + wl.E * 16 + (wl.N + 1) * 4 + wl.weights.size * 4
     log("conv: %.3e counted flop (2*nnz*C per edge), %.1f MB algorithmic bytes -> %.1f GB/s" % (
         flop_edge * wl.E, alg_bytes / 1e6, alg_bytes / conv_s / 1e9))
@@ -315,6 +344,7 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": WORKLOAD_TEXT[args.config] + (" (random edge order)" if args.unsorted else "")
+                   + (" (sorted by destination on the GPU inside each step)" if args.sort_edges else "")
                    + (" (cell-sorted atom numbering)" if args.atom_order == "cell" else "")
                    + (" (SO(3) path set)" if args.path_set == "so3" else "")
                    + (" (bfloat16 node features)" if args.x_bf16 else ""),
@@ -323,6 +353,9 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
+    if sort_out is not None:
+        rec["edge_sort"] = {"ms": round(float(sort_ms.mean()), 5),
+                            "what": "eqtp_sort_edges (counting sort by destination), inside ms_per_step"}
     if backward is not None:
         rec["backward"] = backward
     if messages is not None:

@@ -189,6 +189,30 @@ int eqtp_conv_backward(const eqtp_conv_desc* d, int64_t N, int64_t E, const floa
                        const float* grad_out, float* grad_x, float* grad_w, float* grad_vec, void* stream);
 
 /*
+ * Groups edges given in any order by destination node (a counting sort on the
+ * GPU), producing what the dst-sorted convolution takes.  Layout preparation
+ * for the message-passing step that the Batmobile page, section "3. operator
+ * fusion", chains after the tensor product; the sort itself is not on the
+ * page (a plain counting sort by destination).  Outputs:
+ *   row_ptr    [N+1] int32 out: CSR row pointers (row_ptr[N] = E);
+ *   perm       [E] int32 out: perm[i] = index (in the input order) of the
+ *              edge placed at sorted position i;
+ *   vec_sorted [E, 3] fp32 out = vec[perm], or NULL (then vec may be NULL);
+ *   src_sorted [E] int32 out = src[perm], or NULL (then src may be NULL).
+ *   dst        [E] int32 in, 0 <= dst < N (values outside are clamped).
+ * The order of the edges inside a row is unspecified and may differ from call
+ * to call (it follows the order of hardware atomics); everything else is
+ * unique.  No scratch memory: row_ptr serves as the counter array.
+ * 0 <= N < 2^31 - 1, 0 <= E < 2^31, E > 0 requires N > 0; row_ptr is never
+ * NULL (N = 0 writes row_ptr[0] = 0).  dst and perm may be NULL when E = 0.
+ * Returns EQTP_EINVAL for bad sizes, NULL or misaligned pointers (checked
+ * before anything is launched), else the launch status.  Asynchronous on
+ * stream; the caller owns every buffer.
+ */
+int eqtp_sort_edges(int64_t N, int64_t E, const int32_t* dst, const float* vec, const int32_t* src, int32_t* row_ptr,
+                    int32_t* perm, float* vec_sorted, int32_t* src_sorted, void* stream);
+
+/*
  * Per-l channel linear (channel mixing inside each irrep, no bias):
  *   out[n, c', l m] = sum_c W[l, c', c] h[n, c, l m]
  *   h    [N, C, K] fp32, 16-byte aligned.

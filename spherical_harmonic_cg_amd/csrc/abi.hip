@@ -214,6 +214,20 @@ int eqtp_conv_backward(const eqtp_conv_desc* d, int64_t N, int64_t E, const floa
   return status_of(eqtp::launch_conv_backward(a));
 }
 
+int eqtp_sort_edges(int64_t N, int64_t E, const int32_t* dst, const float* vec, const int32_t* src, int32_t* row_ptr,
+                    int32_t* perm, float* vec_sorted, int32_t* src_sorted, void* stream) {
+  if (N < 0 || E < 0 || N > kMaxIndex - 1 || E > kMaxIndex) return EQTP_EINVAL;
+  if (E > 0 && N == 0) return EQTP_EINVAL;
+  if (!row_ptr || !aligned4(row_ptr)) return EQTP_EINVAL;  // N + 1 >= 1 entries, row_ptr[N] = E is always written
+  if (E > 0) {
+    if (!dst || !perm || !aligned4(dst) || !aligned4(perm)) return EQTP_EINVAL;
+    if (vec_sorted && (!vec || !aligned4(vec) || !aligned4(vec_sorted))) return EQTP_EINVAL;
+    if (src_sorted && (!src || !aligned4(src) || !aligned4(src_sorted))) return EQTP_EINVAL;
+  }
+  return status_of(eqtp::launch_sort_edges(N, E, dst, vec, src, row_ptr, perm, vec_sorted, src_sorted,
+                                           (hipStream_t)stream));
+}
+
 int eqtp_linear(int64_t N, int C, int lmax, int dtype, const float* h, const float* W, float* out, void* stream) {
   if (lmax < 0 || C <= 0 || N < 0 || N > kMaxIndex) return EQTP_EINVAL;
   if (lmax > 3 || !valid_c(C)) return EQTP_EUNSUPPORTED;

@@ -59,5 +59,7 @@ hipError_t launch_linear(int64_t N, int C, int lmax, int bf16, const float* h, c
                          hipStream_t stream);
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t stream);
 hipError_t launch_conv_backward(const BwdArgs& a);   // fixed weights, vector ALUs
+hipError_t launch_sort_edges(int64_t N, int64_t E, const int32_t* dst, const float* vec, const int32_t* src,
+                             int32_t* row_ptr, int32_t* perm, float* vec_out, int32_t* src_out, hipStream_t stream);
 
 }  // namespace eqtp

@@ -1,0 +1,122 @@
+// sort.hip -- groups edges given in any order by destination node (a counting
+// sort on the GPU) so that the dst-segmented convolution, which needs CSR row
+// pointers, can run on them instead of the fp32-atomic scatter.
+//
+// No scratch memory: the row-pointer output doubles as the counter array.
+//   1. row_ptr[0..N-1] = 0, then row_ptr[d] += 1 per edge (histogram);
+//   2. one workgroup turns it in place into inclusive sums (row ends) and sets
+//      row_ptr[N] = E;
+//   3. every edge takes slot = atomicSub(&row_ptr[d], 1) - 1, which fills row
+//      d from its end backwards and leaves row_ptr[d] at the row's start.
+// The order of edges inside a row depends on the atomics' order (unspecified).
+#include "eqtp_device.hpp"
+#include "eqtp_kernels.hpp"
+
+namespace eqtp {
+
+constexpr int kScanThreads = 1024;
+
+__global__ __launch_bounds__(256) void zero_i32_kernel(int* __restrict__ p, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0;
+}
+
+__global__ __launch_bounds__(256) void dst_histogram_kernel(const int* __restrict__ dst, int E, int N,
+                                                            int* __restrict__ counts) {
+  for (int e = blockIdx.x * blockDim.x + threadIdx.x; e < E; e += gridDim.x * blockDim.x)
+    atomicAdd(&counts[clamp_index(dst[e], N)], 1);
+}
+
+// In-place inclusive prefix sum of a[0..N-1] by one workgroup, then a[N] = E.
+// The array is walked in tiles of kScanThreads * kScanItems entries: a tile is
+// read coalesced into LDS (padded by one word per kScanItems so that the
+// per-thread reads below do not collide in banks), each thread scans its
+// kScanItems consecutive entries, the per-thread totals are scanned with
+// shuffles inside each wave and through LDS across the waves, the tile is
+// rewritten in LDS and stored coalesced; a running carry links the tiles.
+constexpr int kScanItems = 8;
+constexpr int kScanTile = kScanThreads * kScanItems;
+__device__ __forceinline__ int scan_pad(int i) { return i + i / kScanItems; }
+
+__global__ __launch_bounds__(kScanThreads) void inclusive_scan_kernel(int* __restrict__ a, int N, int E) {
+  __shared__ int tile[kScanTile + kScanTile / kScanItems];
+  __shared__ int wave_tot[kScanThreads / 64];
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  int carry = 0;
+  for (int base = 0; base < N; base += kScanTile) {
+#pragma unroll
+    for (int j = 0; j < kScanItems; ++j) {
+      const int i = base + j * kScanThreads + t;
+      tile[scan_pad(j * kScanThreads + t)] = i < N ? a[i] : 0;
+    }
+    __syncthreads();
+    int v[kScanItems];
+    int sum = 0;
+#pragma unroll
+    for (int k = 0; k < kScanItems; ++k) {
+      sum += tile[scan_pad(t * kScanItems + k)];
+      v[k] = sum;
+    }
+    int incl = sum;  // inclusive scan of the per-thread totals inside the wave
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int u = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += u;
+    }
+    if (lane == 63) wave_tot[wv] = incl;
+    __syncthreads();
+    int before = carry, all = 0;
+#pragma unroll
+    for (int w = 0; w < kScanThreads / 64; ++w) {
+      const int s = wave_tot[w];
+      before += w < wv ? s : 0;
+      all += s;
+    }
+    const int off = before + incl - sum;  // exclusive prefix of this thread's entries
+#pragma unroll
+    for (int k = 0; k < kScanItems; ++k) tile[scan_pad(t * kScanItems + k)] = off + v[k];
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kScanItems; ++j) {
+      const int i = base + j * kScanThreads + t;
+      if (i < N) a[i] = tile[scan_pad(j * kScanThreads + t)];
+    }
+    carry += all;
+    __syncthreads();  // the next tile overwrites tile[] and wave_tot[]
+  }
+  if (t == 0) a[N] = E;
+}
+
+__global__ __launch_bounds__(256) void scatter_by_dst_kernel(const int* __restrict__ dst, const float* __restrict__ vec,
+                                                             const int* __restrict__ src, int E, int N,
+                                                             int* __restrict__ ends, int* __restrict__ perm,
+                                                             float* __restrict__ vec_out, int* __restrict__ src_out) {
+  for (int e = blockIdx.x * blockDim.x + threadIdx.x; e < E; e += gridDim.x * blockDim.x) {
+    const int d = clamp_index(dst[e], N);
+    const int slot = atomicSub(&ends[d], 1) - 1;
+    perm[slot] = e;
+    if (vec_out != nullptr) {
+      vec_out[3 * (size_t)slot] = vec[3 * (size_t)e];
+      vec_out[3 * (size_t)slot + 1] = vec[3 * (size_t)e + 1];
+      vec_out[3 * (size_t)slot + 2] = vec[3 * (size_t)e + 2];
+    }
+    if (src_out != nullptr) src_out[slot] = src[e];
+  }
+}
+
+hipError_t launch_sort_edges(int64_t N, int64_t E, const int32_t* dst, const float* vec, const int32_t* src,
+                             int32_t* row_ptr, int32_t* perm, float* vec_out, int32_t* src_out, hipStream_t stream) {
+  auto grid = [](int64_t n) {
+    int64_t b = (n + 255) / 256;
+    return (unsigned)(b < 1 ? 1 : (b > 8192 ? 8192 : b));
+  };
+  hipLaunchKernelGGL(zero_i32_kernel, dim3(grid(N)), dim3(256), 0, stream, row_ptr, (int)N);
+  if (E > 0)
+    hipLaunchKernelGGL(dst_histogram_kernel, dim3(grid(E)), dim3(256), 0, stream, dst, (int)E, (int)N, row_ptr);
+  hipLaunchKernelGGL(inclusive_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, row_ptr, (int)N, (int)E);
+  if (E > 0)
+    hipLaunchKernelGGL(scatter_by_dst_kernel, dim3(grid(E)), dim3(256), 0, stream, dst, vec, src, (int)E, (int)N,
+                       row_ptr, perm, vec_out, src_out);
+  return hipGetLastError();
+}
+
+}  // namespace eqtp

@@ -25,7 +25,7 @@ EQTP_ALGO_AUTO, EQTP_ALGO_NODE_MFMA, EQTP_ALGO_EDGE_VALU = 0, 1, 2
 EQTP_F32, EQTP_BF16 = 0, 1
 
 EXPORTED = ("eqtp_num_paths", "eqtp_path_table", "eqtp_sh", "eqtp_conv_fused", "eqtp_conv_messages",
-            "eqtp_conv_backward", "eqtp_linear",
+            "eqtp_conv_backward", "eqtp_sort_edges", "eqtp_linear",
             "eqtp_status_string", "eqtp_test_segment_probe")
 
 
@@ -67,6 +67,8 @@ def load_library(path: str = LIB_PATH):
             lib.eqtp_conv_messages.restype = i32
             lib.eqtp_conv_backward.argtypes = [ctypes.POINTER(_ConvDesc), i64, i64] + [vp] * 11
             lib.eqtp_conv_backward.restype = i32
+            lib.eqtp_sort_edges.argtypes = [i64, i64] + [vp] * 8
+            lib.eqtp_sort_edges.restype = i32
             lib.eqtp_linear.argtypes = [i64, i32, i32, i32, vp, vp, vp, vp]
             lib.eqtp_linear.restype = i32
             lib.eqtp_status_string.argtypes = [i32]
@@ -255,6 +257,34 @@ def eqtp_conv_backward(vec, src, x, weights, grad_out, lmax: int, row_ptr=None, 
                                            _stream())
     _raise(rc, "eqtp_conv_backward")
     return gx, gw, gv
+
+
+def eqtp_sort_edges(dst, N: int, vec=None, src=None, out=None):
+    """(row_ptr [N+1], perm [E], vec[perm] | None, src[perm] | None): edges grouped
+    by destination (order inside a row unspecified).  ``out`` may give the four
+    output tensors (the last two None when vec / src are not given)."""
+    import torch
+
+    _check(dst, "dst", torch.int32)
+    E = dst.shape[0]
+    dev = dst.device
+    if out is None:
+        out = (torch.empty(N + 1, dtype=torch.int32, device=dev), torch.empty(E, dtype=torch.int32, device=dev),
+               torch.empty_like(vec) if vec is not None else None, torch.empty_like(src) if src is not None else None)
+    row_ptr, perm, vs, ss = out
+    _check(row_ptr, "row_ptr", torch.int32, (N + 1,))
+    _check(perm, "perm", torch.int32, (E,))
+    if vec is not None:
+        _check(vec, "vec", torch.float32, (E, 3))
+        _check(vs, "vec_sorted", torch.float32, (E, 3))
+    if src is not None:
+        _check(src, "src", torch.int32, (E,))
+        _check(ss, "src_sorted", torch.int32, (E,))
+    rc = load_library().eqtp_sort_edges(N, E, _ptr(dst), _ptr(vec), _ptr(src), _ptr(row_ptr), _ptr(perm),
+                                        _ptr(vs if vec is not None else None), _ptr(ss if src is not None else None),
+                                        _stream())
+    _raise(rc, "eqtp_sort_edges")
+    return row_ptr, perm, (vs if vec is not None else None), (ss if src is not None else None)
 
 
 def eqtp_linear(h, W, lmax: int, dtype: int = EQTP_F32, out=None):

@@ -183,3 +183,19 @@ def test_descriptor_versions_and_feature_dtype():
     assert lib.eqtp_conv_messages(ctypes.byref(bf), 10, 20, FAKE, FAKE, FAKE, FAKE, FAKE, NULL) == 2
     assert lib.eqtp_conv_backward(ctypes.byref(bf), 10, 20, FAKE, FAKE, NULL, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                                   FAKE, NULL) == 2
+
+
+def test_sort_edges_validation():
+    e = _lib()
+    lib = e.load_library()
+    call = lambda N, E, dst=FAKE, vec=NULL, src=NULL, rp=FAKE, perm=FAKE, vs=NULL, ss=NULL: lib.eqtp_sort_edges(
+        N, E, dst, vec, src, rp, perm, vs, ss, NULL)
+    assert call(-1, 5) == 1
+    assert call(0, 5) == 1                 # edges without nodes
+    assert call(10, 5, rp=NULL) == 1
+    assert call(10, 5, dst=NULL) == 1
+    assert call(10, 5, perm=NULL) == 1
+    assert call(10, 5, vs=FAKE) == 1       # sorted vectors requested without input vectors
+    assert call(10, 5, ss=FAKE) == 1
+    assert call(0, 0, dst=NULL, rp=NULL, perm=NULL) == 1  # row_ptr has N + 1 >= 1 entries
+    assert call((1 << 31) - 1, 0) == 1

@@ -1,0 +1,122 @@
+"""GPU counting sort of edges by destination (eqtp_sort_edges, through the C
+ABI) and the dst-sorted convolution run on its output.
+
+Unique results are compared exactly: row_ptr against numpy's bincount +
+cumsum, and vec[perm] / src[perm] against numpy gathers with the GPU's perm.
+The order of edges inside a row is not unique (it follows the hardware
+atomics), so perm is checked for validity: a permutation of 0..E-1 that puts
+row n's edges, and only those, in [row_ptr[n], row_ptr[n+1]).  The
+convolution on the sorted edges is compared with the fp64 oracle on the
+original order to the usual 2e-4 * max|oracle| bar.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from spherical_harmonic_cg_amd import synth
+from test_gpu_parity import TOL, _assert_close, _eq, _np, _oracle_rows, _sample_rows, _say, _t, _wl
+
+pytestmark = pytest.mark.gpu
+
+
+def _check_sort(eq, N, dst, vec=None, src=None):
+    E = dst.shape[0]
+    rp, perm, vs, ss = eq.eqtp_sort_edges(_t(dst), N, vec=_t(vec) if vec is not None else None,
+                                         src=_t(src) if src is not None else None)
+    rp, perm = _np(rp), _np(perm)
+    want_rp = np.concatenate([[0], np.cumsum(np.bincount(dst, minlength=N))]).astype(np.int32)
+    assert rp.dtype == np.int32 and np.array_equal(rp, want_rp), "row_ptr differs"
+    assert perm.shape == (E,)
+    assert np.array_equal(np.sort(perm), np.arange(E, dtype=np.int32)), "perm is not a permutation"
+    deg = np.diff(want_rp)
+    assert np.array_equal(dst[perm], np.repeat(np.arange(N, dtype=np.int32), deg)), "rows hold foreign edges"
+    if vec is not None:
+        assert np.array_equal(_np(vs), vec[perm])
+    if src is not None:
+        assert np.array_equal(_np(ss), src[perm])
+    return rp, perm, vs, ss
+
+
+@pytest.mark.parametrize("N,E,seed", [(1, 1, 0), (1, 500, 1), (7, 3, 2), (100, 1000, 3), (1023, 5000, 4),
+                                      (1024, 4096, 5), (1025, 777, 6), (5000, 2, 7), (40000, 300001, 8)])
+def test_sort_random_destinations(N, E, seed):
+    eq = _eq()
+    rng = np.random.default_rng(seed)
+    dst = rng.integers(0, N, size=E).astype(np.int32)
+    vec = rng.standard_normal((E, 3)).astype(np.float32)
+    src = rng.integers(0, N, size=E).astype(np.int32)
+    _say("sort N=%d E=%d" % (N, E))
+    _check_sort(eq, N, dst, vec, src)
+
+
+def test_sort_skewed_rows():
+    """One hot row with half the edges, many empty rows, first and last rows used."""
+    eq = _eq()
+    rng = np.random.default_rng(11)
+    N, E = 3000, 60000
+    dst = np.where(rng.random(E) < 0.5, 1234, rng.integers(0, N, size=E) // 7 * 7).astype(np.int32)
+    dst[:2] = (0, N - 1)
+    _say("sort skewed N=%d E=%d" % (N, E))
+    _check_sort(eq, N, dst, rng.standard_normal((E, 3)).astype(np.float32), rng.integers(0, N, E).astype(np.int32))
+
+
+def test_sort_without_vec_and_src():
+    eq = _eq()
+    dst = np.random.default_rng(12).integers(0, 50, size=999).astype(np.int32)
+    _say("sort perm only")
+    _, _, vs, ss = _check_sort(eq, 50, dst)
+    assert vs is None and ss is None
+
+
+def test_sort_no_edges():
+    eq = _eq()
+    import torch
+
+    _say("sort no edges")
+    for N in (0, 1, 5000):
+        rp, perm, _, _ = eq.eqtp_sort_edges(torch.zeros(0, dtype=torch.int32, device="cuda"), N)
+        assert np.array_equal(_np(rp), np.zeros(N + 1, dtype=np.int32)) and perm.numel() == 0
+
+
+def test_sort_repeated_calls_reuse_outputs():
+    """The outputs double as the counters: a second call into the same buffers,
+    on different edges, must not see the first call's values."""
+    eq = _eq()
+    rng = np.random.default_rng(13)
+    N = 300
+    d1 = rng.integers(0, N, size=4000).astype(np.int32)
+    d2 = rng.integers(0, N // 2, size=4000).astype(np.int32)
+    _say("sort repeated")
+    rp, perm, _, _ = eq.eqtp_sort_edges(_t(d1), N)
+    eq.eqtp_sort_edges(_t(d2), N, out=(rp, perm, None, None))
+    rp, perm = _np(rp), _np(perm)
+    assert np.array_equal(rp, np.concatenate([[0], np.cumsum(np.bincount(d2, minlength=N))]))
+    assert np.array_equal(d2[perm], np.sort(d2))
+
+
+@pytest.mark.parametrize("lmax,ps,C", [(3, 0, 64), (3, 1, 32), (2, 0, 16), (1, 0, 128), (0, 0, 8)])
+def test_sort_then_conv_small(lmax, ps, C):
+    eq = _eq()
+    wl = synth.small_graph(57, 11, C, lmax, 700 + lmax + C, path_set=ps, empty_rows=(0, 9), long_rows=(4,),
+                           long_len=90, zero_vec_edges=2)
+    pvec, psrc, pdst = synth.random_permutation(wl, seed=5)
+    _say("sort+conv lmax=%d ps=%d C=%d E=%d" % (lmax, ps, C, wl.E))
+    rp, _, vs, ss = _check_sort(eq, wl.N, pdst, pvec, psrc)
+    out = eq.eqtp_conv_fused(vs, ss, _t(wl.x), _t(wl.w), lmax, row_ptr=_t(rp), path_set=ps)
+    ref = oracle.conv(wl.N, wl.vec, wl.src, wl.dst, wl.x, wl.w, lmax, path_set=ps)
+    _assert_close(_np(out), ref, TOL, "sort+conv")
+
+
+@pytest.mark.parametrize("name", ["mid", "large"])
+def test_sort_then_conv_workload(name):
+    """Full-size workloads in random edge order: sort exact, conv on sampled rows."""
+    eq = _eq()
+    wl = _wl(name)
+    pvec, psrc, pdst = synth.random_permutation(wl)
+    _say("sort+conv %s E=%d" % (name, wl.E))
+    rp, _, vs, ss = _check_sort(eq, wl.N, pdst, pvec, psrc)
+    assert np.array_equal(rp, wl.row_ptr)
+    out = _np(eq.eqtp_conv_fused(vs, ss, _t(wl.x), _t(wl.weights), wl.lmax, row_ptr=_t(rp), path_set=wl.path_set,
+                                 weight_mode=wl.weight_mode, r_cut=wl.r_cut))
+    rows = _sample_rows(wl, 60)
+    _assert_close(out[rows], _oracle_rows(wl, rows), TOL, name + " sort+conv")
