@@ -257,21 +257,44 @@ def main():
             def bwd():
                 eq.eqtp_conv_backward(bvec, bsrc, x, w, gout, wl.lmax, path_set=wl.path_set, **bkw)
 
-            for _ in range(max(3, args.warmup // 4)):
-                bwd()
-            torch.cuda.synchronize()
-            kb = max(5, K // 4)
-            b0 = torch.cuda.Event(enable_timing=True)
-            b1 = torch.cuda.Event(enable_timing=True)
-            b0.record(stream)
-            for _ in range(kb):
-                bwd()
-            b1.record(stream)
-            torch.cuda.synchronize()
-            bms = b0.elapsed_time(b1) / kb
-            backward = {"ms": round(bms, 5), "edges_per_s": round(wl.E / (bms * 1e-3), 1), "launches": kb,
-                        "what": "grad_x, grad_w and grad_vec of the conv (one launch of eqtp_conv_backward)"}
-            log("backward: %.4f ms (%.3e edges/s)" % (bms, wl.E / (bms * 1e-3)))
+            # by source: destinations of the CSR, sort by source, grad_x and grad_w on
+            # the matrix cores, grad_vec edge by edge (what the autograd wrapper runs)
+            E_ = wl.E
+            if "row_ptr" in bkw:
+                rows = torch.empty(E_, dtype=torch.int32, device=dev)
+            grp = (torch.empty(wl.N + 1, dtype=torch.int32, device=dev), torch.empty(E_, dtype=torch.int32, device=dev),
+                   torch.empty((E_, 3), dtype=torch.float32, device=dev), torch.empty(E_, dtype=torch.int32, device=dev))
+
+            def bwd_src():
+                d_ = eq.eqtp_edge_rows(bkw["row_ptr"], E_, out=rows) if "row_ptr" in bkw else bkw["dst"]
+                eq.eqtp_sort_edges(bsrc, wl.N, vec=bvec, src=d_, out=grp)
+                eq.eqtp_conv_backward_by_source(grp[2], grp[3], grp[0], x, w, gout, wl.lmax, path_set=wl.path_set)
+                eq.eqtp_conv_backward(bvec, bsrc, x, w, gout, wl.lmax, path_set=wl.path_set, need_x=False,
+                                      need_w=False, need_vec=True, **bkw)
+
+            def timed(fn):
+                for _ in range(max(3, args.warmup // 4)):
+                    fn()
+                torch.cuda.synchronize()
+                kb = max(5, K // 4)
+                b0 = torch.cuda.Event(enable_timing=True)
+                b1 = torch.cuda.Event(enable_timing=True)
+                b0.record(stream)
+                for _ in range(kb):
+                    fn()
+                b1.record(stream)
+                torch.cuda.synchronize()
+                return b0.elapsed_time(b1) / kb, kb
+
+            bms, kb = timed(bwd)
+            sms, _ = timed(bwd_src)
+            backward = {"ms": round(sms, 5), "edges_per_s": round(wl.E / (sms * 1e-3), 1), "launches": kb,
+                        "what": "grad_x, grad_w and grad_vec of the conv: source grouping on the GPU "
+                                "(eqtp_edge_rows + eqtp_sort_edges), eqtp_conv_backward_by_source (grad_x, grad_w), "
+                                "eqtp_conv_backward (grad_vec)",
+                        "edge_path_ms": round(bms, 5),
+                        "edge_path_what": "all three from eqtp_conv_backward (fp32 atomics for grad_x)"}
+            log("backward: by source %.4f ms (%.3e edges/s); edge path %.4f ms" % (sms, wl.E / (sms * 1e-3), bms))
 
     messages = None
     if args.messages and args.x_bf16:

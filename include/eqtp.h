@@ -189,6 +189,41 @@ int eqtp_conv_backward(const eqtp_conv_desc* d, int64_t N, int64_t E, const floa
                        const float* grad_out, float* grad_x, float* grad_w, float* grad_vec, void* stream);
 
 /*
+ * grad_x and grad_w as for eqtp_conv_backward (same formulas, fixed weights),
+ * computed from a copy of the edges grouped by SOURCE node, on the matrix
+ * cores and without atomics on grad_x:
+ *   H_s[c, m3, m2] = sum_{e: src_e = s} grad_out[dst_e, c, m3] Y_m2(vec_e),
+ *   grad_x[s, c, m1] = sum_p w[p, c] sum_{m2, m3} C^p[m1, m2, m3] H_s[c, m3, m2],
+ *   grad_w[p, c] = sum_s sum_{m1} x[s, c, m1] sum_{m2, m3} C^p[m1, m2, m3] H_s[c, m3, m2].
+ *   src_ptr [N+1] int32: CSR over source nodes (src_ptr[N] = E);
+ *   vec_s   [E, 3] fp32 and dst_s [E] int32: each edge's vector (pointing
+ *           from its source to its destination, as in the forward) and its
+ *           destination, in source-grouped order.
+ *   eqtp_sort_edges(N, E, src, vec, dst, src_ptr, perm, vec_s, dst_s, ...)
+ *   produces these from the forward's arrays (eqtp_edge_rows gives dst from
+ *   a dst-sorted CSR).
+ *   x [N, C, K] fp32 16-byte aligned (needed for grad_w only, else may be NULL);
+ *   grad_out [N, C, K] fp32 16-byte aligned; weights [P, C] fp32.
+ *   grad_x [N, C, K] fp32 16-byte aligned, fully overwritten (zeros for nodes
+ *   that are no edge's source), deterministic; or NULL.
+ *   grad_w [P, C] fp32, a sum of fp32 atomics; or NULL.  Not both NULL.
+ * d: lmax, C, path_set, weight_mode (must be EQTP_W_FIXED), x_dtype (must be
+ * EQTP_F32); edge_order and algo are ignored.  Errors as for
+ * eqtp_conv_backward.
+ */
+int eqtp_conv_backward_by_source(const eqtp_conv_desc* d, int64_t N, int64_t E, const float* vec_s,
+                                 const int32_t* dst_s, const int32_t* src_ptr, const float* x, const float* weights,
+                                 const float* grad_out, float* grad_x, float* grad_w, void* stream);
+
+/*
+ * rows[e] = the row n with row_ptr[n] <= e < row_ptr[n+1] (the destination of
+ * each edge of a dst-sorted CSR), for 0 <= e < E.  row_ptr [N+1] int32 as for
+ * eqtp_conv_fused; rows [E] int32 out.  EQTP_EINVAL for bad sizes or
+ * NULL / misaligned pointers when E > 0; asynchronous on stream.
+ */
+int eqtp_edge_rows(int64_t N, int64_t E, const int32_t* row_ptr, int32_t* rows, void* stream);
+
+/*
  * Groups edges given in any order by destination node (a counting sort on the
  * GPU), producing what the dst-sorted convolution takes.  Layout preparation
  * for the message-passing step that the Batmobile page, section "3. operator

@@ -1,8 +1,12 @@
 """PyTorch autograd wrapper of the fused convolution (fixed path weights).
 
-The forward calls eqtp_conv_fused and the backward eqtp_conv_backward; all
-arithmetic runs in the HIP library.  Gradients flow to the edge vectors (for
-forces), the node features and the path weights.
+The forward calls eqtp_conv_fused.  The backward computes
+  * grad_x and grad_w with eqtp_conv_backward_by_source, on a copy of the edges
+    grouped by source node that eqtp_sort_edges builds on the GPU (the adjoint
+    of the node-factored forward, on the matrix cores), and
+  * grad_vec (for forces) with eqtp_conv_backward, edge by edge.
+``grad_x_mode="edge"`` takes all three from eqtp_conv_backward instead.  All
+arithmetic runs in the HIP library; this module only marshals arguments.
 """
 from __future__ import annotations
 
@@ -11,29 +15,55 @@ import torch
 from . import eqtp as _eq
 
 
+def group_by_source(N: int, src, vec, dst=None, row_ptr=None):
+    """(src_ptr [N+1], vec_s [E,3], dst_s [E]): the edges grouped by source node
+    (the input of eqtp_conv_backward_by_source).  Destinations come from dst, or
+    from a dst-sorted CSR (row_ptr)."""
+    E = src.shape[0]
+    if dst is None:
+        dst = _eq.eqtp_edge_rows(row_ptr, E)
+    src_ptr, _, vec_s, dst_s = _eq.eqtp_sort_edges(src, N, vec=vec, src=dst)
+    return src_ptr, vec_s, dst_s
+
+
 class EquivariantConvFunction(torch.autograd.Function):
     """out = conv(vec, x, weights) over dst-sorted (row_ptr) or unsorted (dst) edges."""
 
     @staticmethod
-    def forward(ctx, vec, x, weights, src, row_ptr, dst, lmax, path_set):
+    def forward(ctx, vec, x, weights, src, row_ptr, dst, lmax, path_set, grad_x_mode):
         out = _eq.eqtp_conv_fused(vec, src, x, weights, lmax, row_ptr=row_ptr, dst=dst, path_set=path_set)
         ctx.save_for_backward(vec, x, weights, src, row_ptr, dst)
         ctx.lmax = lmax
         ctx.path_set = path_set
+        ctx.grad_x_mode = grad_x_mode
         return out
 
     @staticmethod
     def backward(ctx, grad_out):
         vec, x, weights, src, row_ptr, dst = ctx.saved_tensors
         need_vec, need_x, need_w = ctx.needs_input_grad[0], ctx.needs_input_grad[1], ctx.needs_input_grad[2]
+        g = grad_out.contiguous()
         gx = gw = gv = None
-        if need_vec or need_x or need_w:
-            gx, gw, gv = _eq.eqtp_conv_backward(vec, src, x, weights, grad_out.contiguous(), ctx.lmax,
-                                                row_ptr=row_ptr, dst=dst, path_set=ctx.path_set, need_x=need_x,
-                                                need_w=need_w, need_vec=need_vec)
-        return gv, gx, gw, None, None, None, None, None
+        if ctx.grad_x_mode == "edge":
+            if need_vec or need_x or need_w:
+                gx, gw, gv = _eq.eqtp_conv_backward(vec, src, x, weights, g, ctx.lmax, row_ptr=row_ptr, dst=dst,
+                                                    path_set=ctx.path_set, need_x=need_x, need_w=need_w,
+                                                    need_vec=need_vec)
+        else:
+            if need_x or need_w:
+                src_ptr, vec_s, dst_s = group_by_source(x.shape[0], src, vec, dst=dst, row_ptr=row_ptr)
+                gx, gw = _eq.eqtp_conv_backward_by_source(vec_s, dst_s, src_ptr, x, weights, g, ctx.lmax,
+                                                          path_set=ctx.path_set, need_x=need_x, need_w=need_w)
+            if need_vec:
+                _, _, gv = _eq.eqtp_conv_backward(vec, src, x, weights, g, ctx.lmax, row_ptr=row_ptr, dst=dst,
+                                                  path_set=ctx.path_set, need_x=False, need_w=False, need_vec=True)
+        return gv, gx, gw, None, None, None, None, None, None
 
 
-def equivariant_conv(vec, x, weights, src, lmax: int, row_ptr=None, dst=None, path_set: int = _eq.EQTP_PATHS_PARITY):
-    """Differentiable fused convolution (see eqtp_conv_fused for the layouts)."""
-    return EquivariantConvFunction.apply(vec, x, weights, src, row_ptr, dst, lmax, path_set)
+def equivariant_conv(vec, x, weights, src, lmax: int, row_ptr=None, dst=None, path_set: int = _eq.EQTP_PATHS_PARITY,
+                     grad_x_mode: str = "by_source"):
+    """Differentiable fused convolution (see eqtp_conv_fused for the layouts).
+    grad_x_mode: "by_source" (default) or "edge" (see the module docstring)."""
+    if grad_x_mode not in ("by_source", "edge"):
+        raise ValueError("grad_x_mode must be 'by_source' or 'edge'")
+    return EquivariantConvFunction.apply(vec, x, weights, src, row_ptr, dst, lmax, path_set, grad_x_mode)

@@ -214,6 +214,54 @@ int eqtp_conv_backward(const eqtp_conv_desc* d, int64_t N, int64_t E, const floa
   return status_of(eqtp::launch_conv_backward(a));
 }
 
+int eqtp_conv_backward_by_source(const eqtp_conv_desc* d, int64_t N, int64_t E, const float* vec_s,
+                                 const int32_t* dst_s, const int32_t* src_ptr, const float* x, const float* weights,
+                                 const float* grad_out, float* grad_x, float* grad_w, void* stream) {
+  if (!desc_ok(d)) return EQTP_EINVAL;
+  if (desc_x_dtype(d) != EQTP_F32) return desc_x_dtype(d) == EQTP_BF16 ? EQTP_EUNSUPPORTED : EQTP_EINVAL;
+  if (d->lmax < 0) return EQTP_EINVAL;
+  if (d->lmax > 3) return EQTP_EUNSUPPORTED;
+  if (d->path_set != EQTP_PATHS_PARITY && d->path_set != EQTP_PATHS_SO3) return EQTP_EINVAL;
+  if (d->weight_mode != EQTP_W_FIXED && d->weight_mode != EQTP_W_RADIAL) return EQTP_EINVAL;
+  if (d->C <= 0) return EQTP_EINVAL;
+  if (!valid_c(d->C)) return EQTP_EUNSUPPORTED;
+  if (d->weight_mode == EQTP_W_RADIAL) return EQTP_EUNSUPPORTED;
+  if (N < 0 || E < 0 || N > kMaxIndex || E > kMaxIndex) return EQTP_EINVAL;
+  if (E > 0 && N == 0) return EQTP_EINVAL;
+  if (!grad_x && !grad_w) return EQTP_EINVAL;
+  if ((grad_x && !aligned16(grad_x)) || (grad_w && !aligned4(grad_w))) return EQTP_EINVAL;
+  if (!weights || !aligned4(weights)) return EQTP_EINVAL;
+  if (N > 0) {
+    if (!grad_out || !aligned16(grad_out) || !src_ptr || !aligned4(src_ptr)) return EQTP_EINVAL;
+    if (grad_w && (!x || !aligned16(x))) return EQTP_EINVAL;
+  }
+  if (E > 0 && (!vec_s || !dst_s || !aligned4(vec_s) || !aligned4(dst_s))) return EQTP_EINVAL;
+  eqtp::BwdArgs a;
+  a.N = N;
+  a.E = E;
+  a.lmax = d->lmax;
+  a.C = d->C;
+  a.path_set = d->path_set;
+  a.vec = vec_s;
+  a.src = nullptr;
+  a.dst = dst_s;
+  a.row_ptr = src_ptr;
+  a.x = x;
+  a.w = weights;
+  a.gout = grad_out;
+  a.gx = grad_x;
+  a.gw = grad_w;
+  a.gvec = nullptr;
+  a.stream = (hipStream_t)stream;
+  return status_of(eqtp::launch_conv_backward_by_source(a));
+}
+
+int eqtp_edge_rows(int64_t N, int64_t E, const int32_t* row_ptr, int32_t* rows, void* stream) {
+  if (N < 0 || E < 0 || N > kMaxIndex || E > kMaxIndex) return EQTP_EINVAL;
+  if (E > 0 && (N == 0 || !row_ptr || !rows || !aligned4(row_ptr) || !aligned4(rows))) return EQTP_EINVAL;
+  return status_of(eqtp::launch_edge_rows(N, E, row_ptr, rows, (hipStream_t)stream));
+}
+
 int eqtp_sort_edges(int64_t N, int64_t E, const int32_t* dst, const float* vec, const int32_t* src, int32_t* row_ptr,
                     int32_t* perm, float* vec_sorted, int32_t* src_sorted, void* stream) {
   if (N < 0 || E < 0 || N > kMaxIndex - 1 || E > kMaxIndex) return EQTP_EINVAL;

@@ -22,6 +22,9 @@
 // exchanged through LDS and added with fp32 atomics covering 256 contiguous
 // bytes per instruction.  grad_w is accumulated in registers over all the
 // wave's edges and added once per wave.  grad_vec is written per edge.
+// The two walks are separate launches (PASS 1: grad_x and grad_w; PASS 2:
+// grad_vec), so that each holds only its own accumulators: one launch doing
+// both needs about 300 registers at lmax 3, which leaves one wave per SIMD.
 #include "eqtp_device.hpp"
 #include "eqtp_kernels.hpp"
 
@@ -123,7 +126,7 @@ struct BwdCfg {
   static constexpr int EPW = 16 * G;               // edges per wave, unsorted mode
 };
 
-template <int L, int PS, int C, bool SORTED>
+template <int L, int PS, int C, bool SORTED, int PASS>
 __global__ __launch_bounds__(BwdCfg<C>::THREADS) void conv_bwd_kernel(
     int N, int E, const int* __restrict__ row_ptr, const float* __restrict__ vec, const int* __restrict__ src,
     const int* __restrict__ dst, const float* __restrict__ x, const float* __restrict__ w,
@@ -144,15 +147,20 @@ __global__ __launch_bounds__(BwdCfg<C>::THREADS) void conv_bwd_kernel(
   const int cl = lane % Cfg::CL;
   float* const xw = xch[wv];
 
+  if constexpr (PASS == 1) {
+    if (gx == nullptr && gw == nullptr) return;
+  } else {
+    if (gvec == nullptr) return;
+  }
   float wreg[Cfg::CPL][P];
-  float gwacc[Cfg::CPL][P];
+  float gwacc[Cfg::CPL][PASS == 1 ? P : 1];
 #pragma unroll
-  for (int j = 0; j < Cfg::CPL; ++j)
+  for (int j = 0; j < Cfg::CPL; ++j) {
 #pragma unroll
-    for (int p = 0; p < P; ++p) {
-      wreg[j][p] = w[p * C + cl + j * Cfg::CL];
-      gwacc[j][p] = 0.0f;
-    }
+    for (int p = 0; p < P; ++p) wreg[j][p] = w[p * C + cl + j * Cfg::CL];
+#pragma unroll
+    for (int p = 0; p < (PASS == 1 ? P : 1); ++p) gwacc[j][p] = 0.0f;
+  }
 
   float gv[Cfg::CPL][K];  // gout[d, channel, :]
   auto load_g = [&](int d) {
@@ -198,7 +206,7 @@ __global__ __launch_bounds__(BwdCfg<C>::THREADS) void conv_bwd_kernel(
   auto round = [&](int e, bool valid, const EdgeIn& in) {
     float Y[16];
     if (valid) sh_eval<L>(in.vx, in.vy, in.vz, Y);
-    {
+    if constexpr (PASS == 1) {
       float mx[Cfg::CPL][K];
 #pragma unroll
       for (int j = 0; j < Cfg::CPL; ++j)
@@ -218,7 +226,7 @@ __global__ __launch_bounds__(BwdCfg<C>::THREADS) void conv_bwd_kernel(
             s1 = O1::first(q) ? cy * gj[tm.mu3] : fmaf(cy, gj[tm.mu3], s1);
             if constexpr (O1::last(q)) {
               mx[j][tm.mu1] = fmaf(wreg[j][tm.p], s1, mx[j][tm.mu1]);
-              gwacc[j][tm.p] = fmaf(in.xv[j][tm.mu1], s1, gwacc[j][tm.p]);
+              if constexpr (PASS == 1) gwacc[j][tm.p] = fmaf(in.xv[j][tm.mu1], s1, gwacc[j][tm.p]);
               __builtin_amdgcn_sched_barrier(0);  // keep runs apart: bounded live temporaries
             }
           });
@@ -242,7 +250,7 @@ __global__ __launch_bounds__(BwdCfg<C>::THREADS) void conv_bwd_kernel(
         wave_lds_sync();
       }
     }
-    if (gvec != nullptr) {
+    if constexpr (PASS == 2) {
       float dy[16];
 #pragma unroll
       for (int k = 0; k < 16; ++k) dy[k] = 0.0f;
@@ -315,18 +323,18 @@ __global__ __launch_bounds__(BwdCfg<C>::THREADS) void conv_bwd_kernel(
     walk((int)base, (int)min((long long)E, base + Cfg::EPW));
   }
   // grad_w: combine the lane groups, then one atomic per (path, channel)
-  if (gw != nullptr) {
+  if (PASS == 1 && gw != nullptr) {
 #pragma unroll
     for (int off = Cfg::CL; off < kWave; off <<= 1)
 #pragma unroll
       for (int j = 0; j < Cfg::CPL; ++j)
 #pragma unroll
-        for (int p = 0; p < P; ++p) gwacc[j][p] += __shfl_xor(gwacc[j][p], off);
+        for (int p = 0; p < (PASS == 1 ? P : 1); ++p) gwacc[j][p] += __shfl_xor(gwacc[j][p], off);
     if (g == 0) {
 #pragma unroll
       for (int j = 0; j < Cfg::CPL; ++j)
 #pragma unroll
-        for (int p = 0; p < P; ++p) unsafeAtomicAdd(gw + p * C + cl + j * Cfg::CL, gwacc[j][p]);
+        for (int p = 0; p < (PASS == 1 ? P : 1); ++p) unsafeAtomicAdd(gw + p * C + cl + j * Cfg::CL, gwacc[j][p]);
     }
   }
 }
@@ -340,15 +348,21 @@ static hipError_t launch_bwd_t(const BwdArgs& a) {
   if (a.gw && (err = launch_fill_zero(a.gw, (int64_t)Tables<L, PS>::P * C, a.stream)) != hipSuccess) return err;
   if (a.gvec && a.E > 0 && (err = launch_fill_zero(a.gvec, a.E * 3, a.stream)) != hipSuccess) return err;
   if (a.N == 0 || a.E == 0) return hipSuccess;
-  if (a.row_ptr != nullptr) {
-    const unsigned blocks = (unsigned)((a.N + Cfg::WAVES - 1) / Cfg::WAVES);
-    hipLaunchKernelGGL((conv_bwd_kernel<L, PS, C, true>), dim3(blocks), dim3(Cfg::THREADS), 0, a.stream, (int)a.N,
-                       (int)a.E, a.row_ptr, a.vec, a.src, a.dst, a.x, a.w, a.gout, a.gx, a.gw, a.gvec);
-  } else {
-    const long long per_block = (long long)Cfg::WAVES * Cfg::EPW;
-    const unsigned blocks = (unsigned)((a.E + per_block - 1) / per_block);
-    hipLaunchKernelGGL((conv_bwd_kernel<L, PS, C, false>), dim3(blocks), dim3(Cfg::THREADS), 0, a.stream,
-                       (int)a.N, (int)a.E, a.row_ptr, a.vec, a.src, a.dst, a.x, a.w, a.gout, a.gx, a.gw, a.gvec);
+  const bool sorted = a.row_ptr != nullptr;
+  const long long per_block = (long long)Cfg::WAVES * Cfg::EPW;
+  const unsigned blocks = sorted ? (unsigned)((a.N + Cfg::WAVES - 1) / Cfg::WAVES)
+                                 : (unsigned)((a.E + per_block - 1) / per_block);
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, dim3(blocks), dim3(Cfg::THREADS), 0, a.stream, (int)a.N, (int)a.E, a.row_ptr, a.vec,
+                       a.src, a.dst, a.x, a.w, a.gout, a.gx, a.gw, a.gvec);
+  };
+  if (a.gx != nullptr || a.gw != nullptr) {
+    if (sorted) go(conv_bwd_kernel<L, PS, C, true, 1>);
+    else go(conv_bwd_kernel<L, PS, C, false, 1>);
+  }
+  if (a.gvec != nullptr) {
+    if (sorted) go(conv_bwd_kernel<L, PS, C, true, 2>);
+    else go(conv_bwd_kernel<L, PS, C, false, 2>);
   }
   return hipGetLastError();
 }

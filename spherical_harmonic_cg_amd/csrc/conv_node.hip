@@ -25,10 +25,46 @@
 //   * After the row, G goes to LDS; every wave then contracts one group of
 //     output components for C lanes = C channels, reading G rows with an odd
 //     stride (no bank conflicts), and the output tile is stored coalesced.
+//
+// The same kernel gives the gradients with respect to x and w (TR = true).
+// For L = sum gout * out, with the edges grouped by source node s:
+//   H_s[c,mu3,mu2]  = sum_{e: src_e = s} gout[dst_e,c,mu3] * Y_mu2(vec_e)
+//   grad_x[s,c,mu1] = sum_p w[p,c] sum_{mu2,mu3} C^p[mu1,mu2,mu3] H_s[c,mu3,mu2]
+//   grad_w[p,c]     = sum_s sum_{mu1} x[s,c,mu1] sum_{mu2,mu3} C^p[mu1,mu2,mu3] H_s[c,mu3,mu2]
+// H_s is the forward's G with gout gathered through dst instead of x through
+// src, and the contraction is the forward's with mu1 and mu3 exchanged
+// (AdjointTables); grad_w reuses each run's partial sum with one more FMA.
 #include "eqtp_device.hpp"
 #include "eqtp_kernels.hpp"
 
 namespace eqtp {
+
+// The coupling with the roles of mu1 and mu3 exchanged (C'^p[mu3,mu2,mu1] =
+// C^p[mu1,mu2,mu3]), listed by (new mu3, p) so that every (p, mu3) run of the
+// contraction below is contiguous.
+template <int L, int PS>
+struct AdjointTables {
+  using B = Tables<L, PS>;
+  static constexpr int P = B::P;
+  static constexpr int NT = B::NT;
+  struct Arr {
+    eqtp_gen::CgTerm v[NT];
+  };
+  static constexpr int key(const eqtp_gen::CgTerm& t) { return t.mu1 * 64 + t.p; }
+  static constexpr Arr make() {  // stable counting sort by key
+    Arr a{};
+    int pos[16 * 64 + 1] = {};
+    for (int i = 0; i < NT; ++i) pos[key(B::by_out[i]) + 1]++;
+    for (int k = 0; k < 16 * 64; ++k) pos[k + 1] += pos[k];
+    for (int i = 0; i < NT; ++i) {
+      const eqtp_gen::CgTerm t = B::by_out[i];
+      a.v[pos[key(t)]++] = eqtp_gen::CgTerm{t.p, t.mu3, t.mu2, t.mu1, t.c};
+    }
+    return a;
+  }
+  static constexpr Arr arr = make();
+  static constexpr const eqtp_gen::CgTerm* by_out = arr.v;
+};
 
 template <int L, int C>
 struct NodeCfg {
@@ -157,12 +193,16 @@ __device__ __forceinline__ void node_tasks(int N, int E, const int* __restrict__
 
 // XB: the node features are bfloat16 (widened to fp32 on load: a bf16 value
 // is the upper half of the fp32 with the same bits), halving the gather.
-template <int L, int PS, int C, bool BUF, bool XB>
+// TR: gradients (see the top of the file): rows are source nodes, src holds
+// each edge's destination, xp is gout, out receives grad_x (may be null) and
+// grad_w (if non-null, zero-filled beforehand) is accumulated from xn = x.
+template <int L, int PS, int C, bool BUF, bool XB, bool TR>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void conv_node_kernel(
     int N, int E, const int* __restrict__ row_ptr, const float* __restrict__ vec, const int* __restrict__ src,
-    const void* __restrict__ xp, const float* __restrict__ w, float* __restrict__ out) {
+    const void* __restrict__ xp, const float* __restrict__ w, float* __restrict__ out, const float* __restrict__ xn,
+    float* __restrict__ gw) {
   using Cfg = NodeCfg<L, C>;
-  using T = Tables<L, PS>;
+  using T = std::conditional_t<TR, AdjointTables<L, PS>, Tables<L, PS>>;
   constexpr int K = Cfg::K;
   __shared__ __attribute__((aligned(16))) float lds[Cfg::LDS];
 
@@ -211,6 +251,15 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void co
   f4 acc[K];
 #pragma unroll
   for (int k = 0; k < K; ++k) acc[k] = f4{0.f, 0.f, 0.f, 0.f};
+  // grad_w partial sums, [P][16] (lane = channel within the block); in LDS
+  // rather than registers, which the contraction needs
+  __shared__ float gwl[TR ? T::P * 16 : 1];
+  if constexpr (TR) {
+    if (lane < 16) {
+#pragma unroll
+      for (int p = 0; p < T::P; ++p) gwl[p * 16 + lane] = 0.0f;
+    }
+  }
   int c_base = (int)(blockIdx.x % Cfg::NBLK) * Cfg::CW;  // first channel of the current task's block
 
   auto stage = [&](bool valid, float vx, float vy, float vz, int s) {
@@ -316,6 +365,28 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void co
       float ov[K];
 #pragma unroll
       for (int k = 0; k < K; ++k) ov[k] = 0.0f;
+      float xs[TR ? K : 1];  // x[row, c, :] for grad_w
+      if constexpr (TR) {
+        const size_t xo = ((size_t)row * C + c) * K;
+        if (xn != nullptr) {
+          if constexpr (K % 4 == 0) {
+#pragma unroll
+            for (int q = 0; q < K / 4; ++q) {
+              const f4 v = *reinterpret_cast<const f4*>(xn + xo + 4 * q);
+              xs[4 * q] = v[0];
+              xs[4 * q + 1] = v[1];
+              xs[4 * q + 2] = v[2];
+              xs[4 * q + 3] = v[3];
+            }
+          } else {
+#pragma unroll
+            for (int k = 0; k < K; ++k) xs[k] = xn[xo + k];
+          }
+        } else {
+#pragma unroll
+          for (int k = 0; k < K; ++k) xs[k] = 0.0f;
+        }
+      }
       float t = 0.0f;
       static_for<0, T::NT>([&](auto ii) {
         constexpr int i = decltype(ii)::value;
@@ -324,8 +395,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void co
         constexpr bool last = (i + 1 == T::NT) || T::by_out[i + 1].p != tm.p || T::by_out[i + 1].mu3 != tm.mu3;
         const float g = gc[tm.mu1 * K + tm.mu2];
         t = first ? tm.c * g : fmaf(tm.c, g, t);
-        if constexpr (last) ov[tm.mu3] = fmaf(wr[tm.p], t, ov[tm.mu3]);
+        if constexpr (last) {
+          ov[tm.mu3] = fmaf(wr[tm.p], t, ov[tm.mu3]);
+          if constexpr (TR) gwl[tm.p * 16 + lane] = fmaf(xs[tm.mu3], t, gwl[tm.p * 16 + lane]);
+        }
       });
+      if (TR && out == nullptr) return;
       float* op = out + ((size_t)row * C + c) * K;
       if constexpr (K % 4 == 0) {
 #pragma unroll
@@ -347,6 +422,15 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void co
         const long long tn = (long long)row * Cfg::NBLK + blk + gridDim.x;
         c_base = (int)(tn % Cfg::NBLK) * Cfg::CW;
       });
+  if constexpr (TR) {
+    // the grid is a multiple of NBLK (node_grid), so every task of this wave
+    // had channel block blockIdx.x % NBLK
+    if (gw != nullptr && lane < Cfg::CW && (long long)blockIdx.x < (long long)N * Cfg::NBLK) {
+      const int c = (int)(blockIdx.x % Cfg::NBLK) * Cfg::CW + lane;
+#pragma unroll
+      for (int p = 0; p < T::P; ++p) unsafeAtomicAdd(gw + p * C + c, gwl[p * 16 + lane]);
+    }
+  }
 }
 // Test-only twin: the same launch shape and node_tasks schedule, counting
 // edges and summing source indices per row instead of the product (channel
@@ -400,11 +484,13 @@ static int num_cus() {
   return n;
 }
 
-// persistent single-wave workgroups: two per SIMD
+// persistent single-wave workgroups: two per SIMD.  The grid is a multiple
+// of NBLK (tasks is, and so is the cap), so a wave keeps one channel block.
 template <int L, int C>
 static unsigned node_grid(int64_t N) {
-  const int64_t tasks = N * NodeCfg<L, C>::NBLK;
-  const int64_t g = (int64_t)num_cus() * 8;
+  constexpr int NB = NodeCfg<L, C>::NBLK;
+  const int64_t tasks = N * NB;
+  const int64_t g = (int64_t)num_cus() * 8 / NB * NB;
   return (unsigned)(tasks < g ? tasks : g);
 }
 
@@ -417,19 +503,36 @@ static hipError_t launch_node(const ConvArgs& a) {
   const dim3 grid(node_grid<L, C>(a.N)), block(Cfg::THREADS);
   if (a.x_bf16) {
     if (buf)
-      hipLaunchKernelGGL((conv_node_kernel<L, PS, C, true, true>), grid, block, 0, a.stream, (int)a.N, (int)a.E,
-                         a.row_ptr, a.vec, a.src, a.x, a.w, a.out);
+      hipLaunchKernelGGL((conv_node_kernel<L, PS, C, true, true, false>), grid, block, 0, a.stream, (int)a.N,
+                         (int)a.E, a.row_ptr, a.vec, a.src, a.x, a.w, a.out, nullptr, nullptr);
     else
-      hipLaunchKernelGGL((conv_node_kernel<L, PS, C, false, true>), grid, block, 0, a.stream, (int)a.N, (int)a.E,
-                         a.row_ptr, a.vec, a.src, a.x, a.w, a.out);
+      hipLaunchKernelGGL((conv_node_kernel<L, PS, C, false, true, false>), grid, block, 0, a.stream, (int)a.N,
+                         (int)a.E, a.row_ptr, a.vec, a.src, a.x, a.w, a.out, nullptr, nullptr);
   } else {
     if (buf)
-      hipLaunchKernelGGL((conv_node_kernel<L, PS, C, true, false>), grid, block, 0, a.stream, (int)a.N, (int)a.E,
-                         a.row_ptr, a.vec, a.src, a.x, a.w, a.out);
+      hipLaunchKernelGGL((conv_node_kernel<L, PS, C, true, false, false>), grid, block, 0, a.stream, (int)a.N,
+                         (int)a.E, a.row_ptr, a.vec, a.src, a.x, a.w, a.out, nullptr, nullptr);
     else
-      hipLaunchKernelGGL((conv_node_kernel<L, PS, C, false, false>), grid, block, 0, a.stream, (int)a.N, (int)a.E,
-                         a.row_ptr, a.vec, a.src, a.x, a.w, a.out);
+      hipLaunchKernelGGL((conv_node_kernel<L, PS, C, false, false, false>), grid, block, 0, a.stream, (int)a.N,
+                         (int)a.E, a.row_ptr, a.vec, a.src, a.x, a.w, a.out, nullptr, nullptr);
   }
+  return hipGetLastError();
+}
+
+template <int L, int PS, int C>
+static hipError_t launch_node_adjoint(const BwdArgs& a) {
+  using Cfg = NodeCfg<L, C>;
+  hipError_t err;
+  if (a.gw && (err = launch_fill_zero(a.gw, (int64_t)Tables<L, PS>::P * C, a.stream)) != hipSuccess) return err;
+  if (a.N == 0) return hipSuccess;
+  const bool buf = (uint64_t)a.N * C * Cfg::K * 4u <= kMaxBufferBytes && (uint64_t)a.E * 12u <= kMaxBufferBytes;
+  const dim3 grid(node_grid<L, C>(a.N)), block(Cfg::THREADS);
+  if (buf)
+    hipLaunchKernelGGL((conv_node_kernel<L, PS, C, true, false, true>), grid, block, 0, a.stream, (int)a.N, (int)a.E,
+                       a.row_ptr, a.vec, a.dst, a.gout, a.w, a.gx, a.x, a.gw);
+  else
+    hipLaunchKernelGGL((conv_node_kernel<L, PS, C, false, false, true>), grid, block, 0, a.stream, (int)a.N,
+                       (int)a.E, a.row_ptr, a.vec, a.dst, a.gout, a.w, a.gx, a.x, a.gw);
   return hipGetLastError();
 }
 
@@ -468,6 +571,25 @@ hipError_t launch_conv_node(const ConvArgs& a) {
     case 5: return dispatch_node_c<2, 1>(a);
     case 6: return dispatch_node_c<3, 0>(a);
     case 7: return dispatch_node_c<3, 1>(a);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int L, int PS>
+static hipError_t dispatch_adjoint_c(const BwdArgs& a) {
+  EQTP_C_SWITCH(a.C, return (launch_node_adjoint<L, PS, CC>(a)))
+}
+
+hipError_t launch_conv_backward_by_source(const BwdArgs& a) {
+  switch (a.lmax * 2 + a.path_set) {
+    case 0: return dispatch_adjoint_c<0, 0>(a);
+    case 1: return dispatch_adjoint_c<0, 1>(a);
+    case 2: return dispatch_adjoint_c<1, 0>(a);
+    case 3: return dispatch_adjoint_c<1, 1>(a);
+    case 4: return dispatch_adjoint_c<2, 0>(a);
+    case 5: return dispatch_adjoint_c<2, 1>(a);
+    case 6: return dispatch_adjoint_c<3, 0>(a);
+    case 7: return dispatch_adjoint_c<3, 1>(a);
     default: return hipErrorInvalidValue;
   }
 }

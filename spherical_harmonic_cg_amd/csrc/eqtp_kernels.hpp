@@ -59,6 +59,10 @@ hipError_t launch_linear(int64_t N, int C, int lmax, int bf16, const float* h, c
                          hipStream_t stream);
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t stream);
 hipError_t launch_conv_backward(const BwdArgs& a);   // fixed weights, vector ALUs
+// grad_x / grad_w on the matrix cores from edges grouped by source: row_ptr =
+// CSR over sources, vec / dst in that order (src unused)
+hipError_t launch_conv_backward_by_source(const BwdArgs& a);
+hipError_t launch_edge_rows(int64_t N, int64_t E, const int32_t* row_ptr, int32_t* rows, hipStream_t stream);
 hipError_t launch_sort_edges(int64_t N, int64_t E, const int32_t* dst, const float* vec, const int32_t* src,
                              int32_t* row_ptr, int32_t* perm, float* vec_out, int32_t* src_out, hipStream_t stream);
 

@@ -103,6 +103,24 @@ __global__ __launch_bounds__(256) void scatter_by_dst_kernel(const int* __restri
   }
 }
 
+// rows[e] = the row of CSR position e (one thread per row, grid-stride)
+__global__ __launch_bounds__(256) void edge_rows_kernel(const int* __restrict__ row_ptr, int N, int E,
+                                                        int* __restrict__ rows) {
+  for (int r = blockIdx.x * blockDim.x + threadIdx.x; r < N; r += gridDim.x * blockDim.x) {
+    const int b = min(max(row_ptr[r], 0), E);
+    const int e = min(max(row_ptr[r + 1], b), E);
+    for (int i = b; i < e; ++i) rows[i] = r;
+  }
+}
+
+hipError_t launch_edge_rows(int64_t N, int64_t E, const int32_t* row_ptr, int32_t* rows, hipStream_t stream) {
+  if (N == 0 || E == 0) return hipSuccess;
+  const int64_t b = (N + 255) / 256;
+  hipLaunchKernelGGL(edge_rows_kernel, dim3((unsigned)(b > 8192 ? 8192 : b)), dim3(256), 0, stream, row_ptr, (int)N,
+                     (int)E, rows);
+  return hipGetLastError();
+}
+
 hipError_t launch_sort_edges(int64_t N, int64_t E, const int32_t* dst, const float* vec, const int32_t* src,
                              int32_t* row_ptr, int32_t* perm, float* vec_out, int32_t* src_out, hipStream_t stream) {
   auto grid = [](int64_t n) {

@@ -25,7 +25,8 @@ EQTP_ALGO_AUTO, EQTP_ALGO_NODE_MFMA, EQTP_ALGO_EDGE_VALU = 0, 1, 2
 EQTP_F32, EQTP_BF16 = 0, 1
 
 EXPORTED = ("eqtp_num_paths", "eqtp_path_table", "eqtp_sh", "eqtp_conv_fused", "eqtp_conv_messages",
-            "eqtp_conv_backward", "eqtp_sort_edges", "eqtp_linear",
+            "eqtp_conv_backward", "eqtp_conv_backward_by_source", "eqtp_edge_rows", "eqtp_sort_edges",
+            "eqtp_linear",
             "eqtp_status_string", "eqtp_test_segment_probe")
 
 
@@ -67,6 +68,10 @@ def load_library(path: str = LIB_PATH):
             lib.eqtp_conv_messages.restype = i32
             lib.eqtp_conv_backward.argtypes = [ctypes.POINTER(_ConvDesc), i64, i64] + [vp] * 11
             lib.eqtp_conv_backward.restype = i32
+            lib.eqtp_conv_backward_by_source.argtypes = [ctypes.POINTER(_ConvDesc), i64, i64] + [vp] * 9
+            lib.eqtp_conv_backward_by_source.restype = i32
+            lib.eqtp_edge_rows.argtypes = [i64, i64, vp, vp, vp]
+            lib.eqtp_edge_rows.restype = i32
             lib.eqtp_sort_edges.argtypes = [i64, i64] + [vp] * 8
             lib.eqtp_sort_edges.restype = i32
             lib.eqtp_linear.argtypes = [i64, i32, i32, i32, vp, vp, vp, vp]
@@ -257,6 +262,53 @@ def eqtp_conv_backward(vec, src, x, weights, grad_out, lmax: int, row_ptr=None, 
                                            _stream())
     _raise(rc, "eqtp_conv_backward")
     return gx, gw, gv
+
+
+def eqtp_conv_backward_by_source(vec_s, dst_s, src_ptr, x, weights, grad_out, lmax: int,
+                                 path_set: int = EQTP_PATHS_PARITY, need_x: bool = True, need_w: bool = True):
+    """(grad_x [N,C,K] | None, grad_w [P,C] | None) from the edges grouped by
+    source node: src_ptr [N+1] CSR over sources, vec_s [E,3] / dst_s [E] in
+    that order (see eqtp_sort_edges)."""
+    import torch
+
+    _check(grad_out, "grad_out", torch.float32)
+    if grad_out.dim() != 3:
+        raise ValueError("grad_out must be [N, C, K]")
+    N, C, K = grad_out.shape
+    if K != (lmax + 1) ** 2:
+        raise ValueError("grad_out has %d components, lmax %d needs %d" % (K, lmax, (lmax + 1) ** 2))
+    _check(vec_s, "vec_s", torch.float32)
+    E = vec_s.shape[0]
+    _check(dst_s, "dst_s", torch.int32, (E,))
+    _check(src_ptr, "src_ptr", torch.int32, (N + 1,))
+    if need_w:
+        _check(x, "x", torch.float32, (N, C, K))
+    P = eqtp_num_paths(lmax, path_set)
+    _check(weights, "weights", torch.float32, (P, C))
+    if not (need_x or need_w):
+        raise ValueError("request at least one gradient")
+    gx = torch.empty_like(grad_out) if need_x else None
+    gw = torch.empty_like(weights) if need_w else None
+    d = _ConvDesc(ctypes.sizeof(_ConvDesc), lmax, C, path_set, EQTP_W_FIXED, EQTP_EDGES_DST_SORTED, EQTP_ALGO_AUTO,
+                  0.0, 8, EQTP_F32)
+    rc = load_library().eqtp_conv_backward_by_source(ctypes.byref(d), N, E, _ptr(vec_s), _ptr(dst_s), _ptr(src_ptr),
+                                                     _ptr(x if need_w else None), _ptr(weights), _ptr(grad_out),
+                                                     _ptr(gx), _ptr(gw), _stream())
+    _raise(rc, "eqtp_conv_backward_by_source")
+    return gx, gw
+
+
+def eqtp_edge_rows(row_ptr, E: int, out=None):
+    """rows [E] int32: the destination row of every edge of a dst-sorted CSR."""
+    import torch
+
+    _check(row_ptr, "row_ptr", torch.int32)
+    N = row_ptr.shape[0] - 1
+    rows = out if out is not None else torch.empty(E, dtype=torch.int32, device=row_ptr.device)
+    _check(rows, "rows", torch.int32, (E,))
+    rc = load_library().eqtp_edge_rows(N, E, _ptr(row_ptr), _ptr(rows), _stream())
+    _raise(rc, "eqtp_edge_rows")
+    return rows
 
 
 def eqtp_sort_edges(dst, N: int, vec=None, src=None, out=None):

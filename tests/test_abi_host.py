@@ -199,3 +199,39 @@ def test_sort_edges_validation():
     assert call(10, 5, ss=FAKE) == 1
     assert call(0, 0, dst=NULL, rp=NULL, perm=NULL) == 1  # row_ptr has N + 1 >= 1 entries
     assert call((1 << 31) - 1, 0) == 1
+
+
+def test_conv_backward_by_source_validation():
+    e = _lib()
+    lib = e.load_library()
+
+    def call(d, N=10, E=20, vec=FAKE, dst=FAKE, sp=FAKE, x=FAKE, w=FAKE, g=FAKE, gx=FAKE, gw=FAKE):
+        return lib.eqtp_conv_backward_by_source(ctypes.byref(d), N, E, vec, dst, sp, x, w, g, gx, gw, NULL)
+
+    assert call(_desc(e, weight_mode=1, r_cut=5.0)) == 2                 # radial weights: not implemented
+    assert call(_desc(e, lmax=4)) == 2
+    assert call(_desc(e, C=48)) == 2
+    assert call(_desc(e, x_dtype=1)) == 2                                  # bf16 features
+    assert call(_desc(e, path_set=2)) == 1
+    assert call(_desc(e), gx=NULL, gw=NULL) == 1                          # nothing requested
+    assert call(_desc(e), x=NULL) == 1                                    # grad_w needs x
+    assert call(_desc(e), g=NULL) == 1
+    assert call(_desc(e), sp=NULL) == 1
+    assert call(_desc(e), vec=NULL) == 1
+    assert call(_desc(e), dst=NULL) == 1
+    assert call(_desc(e), w=NULL) == 1
+    assert call(_desc(e), gx=ctypes.c_void_p(0x10004)) == 1               # grad_x not 16-byte aligned
+    assert call(_desc(e), g=ctypes.c_void_p(0x10004)) == 1                # grad_out not 16-byte aligned
+    assert call(_desc(e), N=0) == 1                                       # edges without nodes
+    assert call(_desc(e), N=-1) == 1
+
+
+def test_edge_rows_validation():
+    e = _lib()
+    lib = e.load_library()
+    assert lib.eqtp_edge_rows(-1, 5, FAKE, FAKE, NULL) == 1
+    assert lib.eqtp_edge_rows(0, 5, FAKE, FAKE, NULL) == 1
+    assert lib.eqtp_edge_rows(10, 5, NULL, FAKE, NULL) == 1
+    assert lib.eqtp_edge_rows(10, 5, FAKE, NULL, NULL) == 1
+    assert lib.eqtp_edge_rows(10, 5, ctypes.c_void_p(0x10002), FAKE, NULL) == 1
+    assert lib.eqtp_edge_rows(10, 0, NULL, NULL, NULL) == 0                # nothing to do, nothing launched

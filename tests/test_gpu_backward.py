@@ -130,3 +130,127 @@ def test_autograd_function_matches_backward_and_oracle():
     out2 = equivariant_conv(vec2, _t(wl.x), _t(wl.w), _t(wl.src), 3, row_ptr=_t(wl.row_ptr))
     (out2 * _t(gout)).sum().backward()
     _assert_close(_np(vec2.grad), ref[2], TOL, "autograd grad_vec only")
+
+
+# ---------------------------------------------------------------------------
+# grad_x and grad_w from the edges grouped by source (eqtp_conv_backward_by_source)
+# ---------------------------------------------------------------------------
+
+def _by_source_numpy(wl):
+    """Source grouping built on the host (stable order), as test input."""
+    order = np.argsort(wl.src, kind="stable")
+    src_ptr = np.concatenate([[0], np.cumsum(np.bincount(wl.src, minlength=wl.N))]).astype(np.int32)
+    return src_ptr, wl.vec[order], wl.dst[order].astype(np.int32)
+
+
+def _check_by_source(eq, wl, gout, grouping, need=(True, True), what=""):
+    ref = oracle.conv_backward(wl.N, wl.vec, wl.src, wl.dst, wl.x, wl.w, gout, wl.lmax, wl.path_set)
+    sp, vs, ds = grouping
+    gx, gw = eq.eqtp_conv_backward_by_source(vs if not isinstance(vs, np.ndarray) else _t(vs),
+                                             ds if not isinstance(ds, np.ndarray) else _t(ds),
+                                             sp if not isinstance(sp, np.ndarray) else _t(sp),
+                                             _t(wl.x), _t(wl.w), _t(gout), wl.lmax, path_set=wl.path_set,
+                                             need_x=need[0], need_w=need[1])
+    if need[0]:
+        _assert_close(_np(gx), ref[0], TOL, what + " grad_x")
+    else:
+        assert gx is None
+    if need[1]:
+        _assert_close(_np(gw), ref[1], TOL, what + " grad_w")
+    else:
+        assert gw is None
+
+
+@pytest.mark.parametrize("lmax", [0, 1, 2, 3])
+@pytest.mark.parametrize("ps", [0, 1])
+@pytest.mark.parametrize("C", [8, 16, 32, 64, 128])
+def test_backward_by_source_small(lmax, ps, C):
+    eq = _eq()
+    wl = synth.small_graph(37, 9, C, lmax, 900 + lmax * 10 + C, path_set=ps, empty_rows=(3,), long_rows=(5,),
+                           long_len=70, zero_vec_edges=1)
+    # a source with many outgoing edges (> 64: several staging chunks) and one with none
+    wl.src[: 80] = 11
+    wl.src[wl.src == 2] = 12
+    _say("backward by source lmax=%d ps=%d C=%d E=%d" % (lmax, ps, C, wl.src.shape[0]))
+    _check_by_source(eq, wl, _gout(wl, 17), _by_source_numpy(wl), what="by source L%d ps%d C%d" % (lmax, ps, C))
+
+
+@pytest.mark.parametrize("need", [(True, False), (False, True)])
+def test_backward_by_source_partial(need):
+    eq = _eq()
+    wl = synth.small_graph(23, 8, 32, 3, 78)
+    _say("backward by source partial %s" % (need,))
+    _check_by_source(eq, wl, _gout(wl, 18), _by_source_numpy(wl), need=need, what="by source partial")
+
+
+@pytest.mark.parametrize("from_rows", [True, False])
+def test_backward_by_source_gpu_grouping(from_rows):
+    """Grouping built on the GPU: eqtp_edge_rows (from the dst-sorted CSR) or
+    the dst array, then eqtp_sort_edges keyed by source."""
+    eq = _eq()
+    from spherical_harmonic_cg_amd.autograd import group_by_source
+
+    wl = synth.make_config("typical")
+    _say("backward by source, GPU grouping (from_rows=%s) E=%d" % (from_rows, wl.src.shape[0]))
+    if from_rows:
+        rows = eq.eqtp_edge_rows(_t(wl.row_ptr), wl.src.shape[0])
+        assert np.array_equal(_np(rows), wl.dst)
+        grouping = group_by_source(wl.N, _t(wl.src), _t(wl.vec), row_ptr=_t(wl.row_ptr))
+    else:
+        grouping = group_by_source(wl.N, _t(wl.src), _t(wl.vec), dst=_t(wl.dst))
+    _check_by_source(eq, wl, _gout(wl, 19), grouping, what="by source typical")
+
+
+def test_backward_by_source_mid():
+    eq = _eq()
+    from spherical_harmonic_cg_amd.autograd import group_by_source
+
+    wl = synth.make_config("mid")
+    _say("backward by source mid E=%d" % wl.src.shape[0])
+    grouping = group_by_source(wl.N, _t(wl.src), _t(wl.vec), row_ptr=_t(wl.row_ptr))
+    _check_by_source(eq, wl, _gout(wl, 20), grouping, what="by source mid")
+
+
+def test_backward_by_source_no_edges():
+    eq = _eq()
+    import torch
+
+    N, C = 6, 32
+    g = torch.randn(N, C, 16, device="cuda")
+    x = torch.randn(N, C, 16, device="cuda")
+    w = torch.randn(23, C, device="cuda")
+    _say("backward by source, no edges")
+    gx, gw = eq.eqtp_conv_backward_by_source(torch.zeros(0, 3, device="cuda"),
+                                             torch.zeros(0, dtype=torch.int32, device="cuda"),
+                                             torch.zeros(N + 1, dtype=torch.int32, device="cuda"), x, w, g, 3)
+    assert float(_np(gx).__abs__().max()) == 0.0 and float(_np(gw).__abs__().max()) == 0.0
+
+
+def test_edge_rows_exact():
+    eq = _eq()
+    wl = synth.small_graph(300, 7, 8, 1, 5, empty_rows=(0, 17, 299), long_rows=(40,), long_len=200)
+    _say("edge rows")
+    assert np.array_equal(_np(eq.eqtp_edge_rows(_t(wl.row_ptr), wl.src.shape[0])), wl.dst)
+
+
+@pytest.mark.parametrize("mode", ["by_source", "edge"])
+@pytest.mark.parametrize("csr", [True, False])
+def test_autograd_modes(mode, csr):
+    import torch
+
+    eq = _eq()
+    from spherical_harmonic_cg_amd.autograd import equivariant_conv
+
+    wl = synth.small_graph(29, 9, 64, 3, 123, zero_vec_edges=1)
+    gout = _gout(wl, 21)
+    kw = dict(row_ptr=_t(wl.row_ptr)) if csr else dict(dst=_t(wl.dst))
+    vec = _t(wl.vec).requires_grad_(True)
+    x = _t(wl.x).requires_grad_(True)
+    w = _t(wl.w).requires_grad_(True)
+    _say("autograd mode=%s csr=%s" % (mode, csr))
+    out = equivariant_conv(vec, x, w, _t(wl.src), 3, grad_x_mode=mode, **kw)
+    (out * _t(gout)).sum().backward()
+    ref = oracle.conv_backward(wl.N, wl.vec, wl.src, wl.dst, wl.x, wl.w, gout, 3)
+    _assert_close(_np(x.grad), ref[0], TOL, "autograd %s grad_x" % mode)
+    _assert_close(_np(w.grad), ref[1], TOL, "autograd %s grad_w" % mode)
+    _assert_close(_np(vec.grad), ref[2], TOL, "autograd %s grad_vec" % mode)
