@@ -60,10 +60,17 @@ extern "C" {
 #define EQTP_EDGES_DST_SORTED 0 /* edges grouped by dst; row_ptr[N+1] gives each node's range */
 #define EQTP_EDGES_UNSORTED 1   /* any order; dst[E] given; results summed with atomics */
 
-/* algorithm for sorted edges with fixed weights (others always use the edge kernel) */
+/* algorithm of eqtp_conv_fused.  AUTO: NODE_MFMA for dst-sorted edges with
+   fixed weights and lmax <= 3, EDGE_VALU for other lmax <= 3 cases, EDGE_SO2
+   for lmax 4..6. */
 #define EQTP_ALGO_AUTO 0
 #define EQTP_ALGO_NODE_MFMA 1 /* per node: outer-product sums on matrix cores, then the coupling */
 #define EQTP_ALGO_EDGE_VALU 2 /* per edge: harmonics, coupling and product on the vector ALUs */
+#define EQTP_ALGO_EDGE_SO2 3  /* per edge in the edge-aligned frame (E2Former-V2 page, section 2.1,
+                                 "EAAS"): rotate x[src] so that the edge is the z axis, where the
+                                 harmonics keep only m = 0 and the coupling is a sparse re-indexing,
+                                 rotate back; vector ALUs; fixed weights, fp32 features; lmax 0..6
+                                 (C = 128 up to lmax 4).  Same result as the coupling form. */
 
 /* operand precision of the channel linear */
 #define EQTP_F32 0
@@ -71,7 +78,8 @@ extern "C" {
 
 /*
  * Number of coupling paths P for (lmax, path_set), or a negative status.
- * lmax in [0, 3].
+ * lmax in [0, 6] (above 3 only eqtp_conv_fused with EQTP_ALGO_EDGE_SO2 or
+ * EQTP_ALGO_AUTO takes it).
  */
 int eqtp_num_paths(int lmax, int path_set);
 
@@ -97,7 +105,7 @@ int eqtp_sh(const float* vec, int64_t E, int lmax, float* Y, void* stream);
 
 typedef struct eqtp_conv_desc {
   int32_t struct_size; /* = sizeof(eqtp_conv_desc) */
-  int32_t lmax;        /* 0..3 */
+  int32_t lmax;        /* 0..3; 4..6 with EQTP_ALGO_EDGE_SO2 / EQTP_ALGO_AUTO */
   int32_t C;           /* channels: 8, 16, 32, 64 or 128 */
   int32_t path_set;    /* EQTP_PATHS_* */
   int32_t weight_mode; /* EQTP_W_* */
@@ -143,6 +151,8 @@ typedef struct eqtp_conv_desc {
  *            no incoming edge get zeros); must not alias any input.
  * Sorted edges: deterministic (bit-identical from run to run).  Unsorted
  * edges: summation order varies from run to run.
+ * lmax 4..6 (EQTP_ALGO_EDGE_SO2): fixed weights and fp32 features only
+ * (EQTP_EUNSUPPORTED otherwise), C = 128 up to lmax 4; both edge orders.
  */
 int eqtp_conv_fused(const eqtp_conv_desc* d, int64_t N, int64_t E, const float* vec, const int32_t* src,
                     const int32_t* dst, const int32_t* row_ptr, const void* x, const float* weights, float* out,

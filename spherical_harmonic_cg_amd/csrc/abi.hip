@@ -6,6 +6,7 @@
 #include "../../include/eqtp.h"
 #include "eqtp_device.hpp"
 #include "eqtp_kernels.hpp"
+#include "generated/so2_tables.inc"
 
 namespace {
 
@@ -24,22 +25,34 @@ int desc_x_dtype(const eqtp_conv_desc* d) {
 }
 constexpr int64_t kMaxIndex = (int64_t(1) << 31) - 1;
 
+// path counts and lists for lmax 0..6 (the same canonical order in both
+// generated tables; lmax <= 3 also has the coupling-form tables)
 int num_paths_host(int lmax, int path_set) {
-  static const int parity[4] = {eqtp_gen::kNumPaths_L0_parity, eqtp_gen::kNumPaths_L1_parity,
-                                eqtp_gen::kNumPaths_L2_parity, eqtp_gen::kNumPaths_L3_parity};
-  static const int so3[4] = {eqtp_gen::kNumPaths_L0_so3, eqtp_gen::kNumPaths_L1_so3, eqtp_gen::kNumPaths_L2_so3,
-                             eqtp_gen::kNumPaths_L3_so3};
-  if (lmax < 0 || lmax > 3) return -EQTP_EUNSUPPORTED;
+  static const int parity[7] = {eqtp_gen::kSo2NumPaths_L0_parity, eqtp_gen::kSo2NumPaths_L1_parity,
+                                eqtp_gen::kSo2NumPaths_L2_parity, eqtp_gen::kSo2NumPaths_L3_parity,
+                                eqtp_gen::kSo2NumPaths_L4_parity, eqtp_gen::kSo2NumPaths_L5_parity,
+                                eqtp_gen::kSo2NumPaths_L6_parity};
+  static const int so3[7] = {eqtp_gen::kSo2NumPaths_L0_so3, eqtp_gen::kSo2NumPaths_L1_so3,
+                             eqtp_gen::kSo2NumPaths_L2_so3, eqtp_gen::kSo2NumPaths_L3_so3,
+                             eqtp_gen::kSo2NumPaths_L4_so3, eqtp_gen::kSo2NumPaths_L5_so3,
+                             eqtp_gen::kSo2NumPaths_L6_so3};
+  static_assert(eqtp_gen::kSo2NumPaths_L3_parity == eqtp_gen::kNumPaths_L3_parity, "path tables");
+  static_assert(eqtp_gen::kSo2NumPaths_L3_so3 == eqtp_gen::kNumPaths_L3_so3, "path tables");
+  if (lmax < 0 || lmax > eqtp::kSo2MaxL) return -EQTP_EUNSUPPORTED;
   if (path_set == EQTP_PATHS_PARITY) return parity[lmax];
   if (path_set == EQTP_PATHS_SO3) return so3[lmax];
   return -EQTP_EINVAL;
 }
 
 const eqtp_gen::PathLs* path_list(int lmax, int path_set) {
-  static const eqtp_gen::PathLs* parity[4] = {eqtp_gen::kPaths_L0_parity, eqtp_gen::kPaths_L1_parity,
-                                              eqtp_gen::kPaths_L2_parity, eqtp_gen::kPaths_L3_parity};
-  static const eqtp_gen::PathLs* so3[4] = {eqtp_gen::kPaths_L0_so3, eqtp_gen::kPaths_L1_so3,
-                                           eqtp_gen::kPaths_L2_so3, eqtp_gen::kPaths_L3_so3};
+  static const eqtp_gen::PathLs* parity[7] = {eqtp_gen::kSo2Paths_L0_parity, eqtp_gen::kSo2Paths_L1_parity,
+                                              eqtp_gen::kSo2Paths_L2_parity, eqtp_gen::kSo2Paths_L3_parity,
+                                              eqtp_gen::kSo2Paths_L4_parity, eqtp_gen::kSo2Paths_L5_parity,
+                                              eqtp_gen::kSo2Paths_L6_parity};
+  static const eqtp_gen::PathLs* so3[7] = {eqtp_gen::kSo2Paths_L0_so3, eqtp_gen::kSo2Paths_L1_so3,
+                                           eqtp_gen::kSo2Paths_L2_so3, eqtp_gen::kSo2Paths_L3_so3,
+                                           eqtp_gen::kSo2Paths_L4_so3, eqtp_gen::kSo2Paths_L5_so3,
+                                           eqtp_gen::kSo2Paths_L6_so3};
   return path_set == EQTP_PATHS_PARITY ? parity[lmax] : so3[lmax];
 }
 
@@ -79,14 +92,20 @@ int eqtp_conv_fused(const eqtp_conv_desc* d, int64_t N, int64_t E, const float* 
   const int x_dtype = desc_x_dtype(d);
   if (x_dtype != EQTP_F32 && x_dtype != EQTP_BF16) return EQTP_EINVAL;
   if (d->lmax < 0) return EQTP_EINVAL;
-  if (d->lmax > 3) return EQTP_EUNSUPPORTED;
+  if (d->lmax > eqtp::kSo2MaxL) return EQTP_EUNSUPPORTED;
   if (d->path_set != EQTP_PATHS_PARITY && d->path_set != EQTP_PATHS_SO3) return EQTP_EINVAL;
   if (d->weight_mode != EQTP_W_FIXED && d->weight_mode != EQTP_W_RADIAL) return EQTP_EINVAL;
   if (d->edge_order != EQTP_EDGES_DST_SORTED && d->edge_order != EQTP_EDGES_UNSORTED) return EQTP_EINVAL;
-  if (d->algo != EQTP_ALGO_AUTO && d->algo != EQTP_ALGO_NODE_MFMA && d->algo != EQTP_ALGO_EDGE_VALU)
+  if (d->algo != EQTP_ALGO_AUTO && d->algo != EQTP_ALGO_NODE_MFMA && d->algo != EQTP_ALGO_EDGE_VALU &&
+      d->algo != EQTP_ALGO_EDGE_SO2)
     return EQTP_EINVAL;
   if (d->C <= 0) return EQTP_EINVAL;
   if (!valid_c(d->C)) return EQTP_EUNSUPPORTED;
+  // lmax above 3 exists only in the edge-aligned form
+  const bool use_so2 = d->algo == EQTP_ALGO_EDGE_SO2 || (d->algo == EQTP_ALGO_AUTO && d->lmax > 3);
+  if (d->lmax > 3 && !use_so2) return EQTP_EUNSUPPORTED;
+  if (use_so2 && (d->weight_mode != EQTP_W_FIXED || x_dtype != EQTP_F32)) return EQTP_EUNSUPPORTED;
+  if (use_so2 && d->C == 128 && d->lmax > eqtp::kSo2MaxLC128) return EQTP_EUNSUPPORTED;
   if (d->weight_mode == EQTP_W_RADIAL) {
     if (!(d->r_cut > 0.0f)) return EQTP_EINVAL;
     if (d->n_basis != 8) return EQTP_EUNSUPPORTED;
@@ -125,6 +144,7 @@ int eqtp_conv_fused(const eqtp_conv_desc* d, int64_t N, int64_t E, const float* 
   a.w = weights;
   a.out = out;
   a.stream = (hipStream_t)stream;
+  if (use_so2) return status_of(eqtp::launch_conv_so2(a));
   const bool use_node = node_ok && d->algo != EQTP_ALGO_EDGE_VALU;
   return status_of(use_node ? eqtp::launch_conv_node(a) : eqtp::launch_conv_edge(a));
 }

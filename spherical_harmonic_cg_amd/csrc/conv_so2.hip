@@ -1,0 +1,337 @@
+// conv_so2.hip -- the fused convolution in the edge-aligned (SO(2)) form, for
+// lmax up to 6 (E2Former-V2 page, section 2.1 "derivation of EAAS").
+//
+// It computes what the Clebsch-Gordan form computes (Batmobile page, sections
+// "2. register intermediate computation" and "3. operator fusion"):
+//   out[n,c,mu3] = sum_{e: dst_e = n} sum_p w[p,c] sum_{mu1,mu2} C^p[mu1,mu2,mu3] x[src_e,c,mu1] Y_mu2(vec_e),
+// by the equivariance of the coupling: with a rotation R_e that takes the
+// edge direction to the z axis and D(R) its action on the real harmonics
+// (Y(R u) = D(R) Y(u)),
+//   message_e = D(R_e)^T  P(D(R_e) x[src_e]),
+// where P is the coupling with the harmonics of the z axis, which are zero
+// except for m = 0: each output component receives only input components of
+// the same |m| (the page's sparse re-indexing; 624 terms instead of 6460 at
+// lmax 6).  R_e = R_y(-theta) R_z(-phi) for the direction (theta, phi), and
+// D(R_y(b)) = J^T D(R_z(b)) J with the constant J = D(R_x(pi/2)), so
+//   D(R_e)   = J^T Z(-theta) J Z(-phi),   D(R_e)^T = Z(phi) J^T Z(theta) J,
+// where Z(a) rotates every (m cos, m sin) component pair by m a.  No harmonic
+// is evaluated and no per-edge matrix is built: the rotations are two
+// sparse constant matrices (J, J^T: 119 entries up to lmax 6, immediates)
+// and four pair rotations per edge and channel.  Tables and their checks:
+// gen_so2_table.py.
+//
+// A zero edge vector: harmonics of degree > 0 are zero there, so the paths
+// with l2 > 0 are dropped for that edge and the rotation is the identity.
+//
+// Lane mapping as in conv_edge.hip: lane = channel (C <= 64: 64/C edges per
+// wave; C = 128: two channels per lane).  dst-sorted edges: one wave per
+// destination row, lane groups combined with xor shuffles (deterministic);
+// unsorted edges: contiguous edge runs per wave, messages added with fp32
+// atomics after an LDS exchange (256 contiguous bytes per instruction).
+// The path weights are staged once per workgroup in LDS ([P][C]).
+#include "eqtp_device.hpp"
+#include "eqtp_kernels.hpp"
+#include "generated/so2_tables.inc"
+
+namespace eqtp {
+
+template <int L, int PS>
+struct So2Tables;
+
+#define EQTP_SO2(L_, PS_, TAG)                                                     \
+  template <>                                                                      \
+  struct So2Tables<L_, PS_> {                                                      \
+    static constexpr int P = eqtp_gen::kSo2NumPaths_##TAG;                         \
+    static constexpr int NT = eqtp_gen::kSo2NumTerms_##TAG;                        \
+    static constexpr const eqtp_gen::So2Term* terms = eqtp_gen::kSo2Terms_##TAG;   \
+  };
+EQTP_SO2(0, 0, L0_parity)
+EQTP_SO2(1, 0, L1_parity)
+EQTP_SO2(2, 0, L2_parity)
+EQTP_SO2(3, 0, L3_parity)
+EQTP_SO2(4, 0, L4_parity)
+EQTP_SO2(5, 0, L5_parity)
+EQTP_SO2(6, 0, L6_parity)
+EQTP_SO2(0, 1, L0_so3)
+EQTP_SO2(1, 1, L1_so3)
+EQTP_SO2(2, 1, L2_so3)
+EQTP_SO2(3, 1, L3_so3)
+EQTP_SO2(4, 1, L4_so3)
+EQTP_SO2(5, 1, L5_so3)
+EQTP_SO2(6, 1, L6_so3)
+#undef EQTP_SO2
+
+template <int C>
+struct So2Cfg {
+  static constexpr int CPL = C > 64 ? C / 64 : 1;  // channels per lane
+  static constexpr int CL = C / CPL;               // lanes per edge group
+  static constexpr int G = kWave / CL;             // edge groups per wave
+  static constexpr int WAVES = 4;
+  static constexpr int THREADS = WAVES * kWave;
+  static constexpr int EPW = 8 * G;                // edges per wave, unsorted mode
+};
+
+// v <- J v (T = false) or J^T v (T = true) on the first K components
+template <int K, bool T>
+__device__ __forceinline__ void apply_j(float (&v)[K]) {
+  constexpr int NE = T ? eqtp_gen::kJTRowStart[K] : eqtp_gen::kJRowStart[K];
+  float o[K];
+  static_for<0, NE>([&](auto ii) {
+    constexpr int i = decltype(ii)::value;
+    constexpr eqtp_gen::JEntry je = T ? eqtp_gen::kJT[i] : eqtp_gen::kJ[i];
+    constexpr bool first = i == 0 || (T ? eqtp_gen::kJT[i - 1].row : eqtp_gen::kJ[i - 1].row) != je.row;
+    o[je.row] = first ? je.v * v[je.col] : fmaf(je.v, v[je.col], o[je.row]);
+  });
+#pragma unroll
+  for (int k = 0; k < K; ++k) v[k] = o[k];
+}
+
+// v <- Z(a) v: each (m cos, m sin) pair of degree l <= L rotated by m a, with
+// cm[m] = cos(m a), sm[m] = sgn * sin(m a)
+template <int L, int K>
+__device__ __forceinline__ void apply_z(float (&v)[K], const float (&cm)[L + 1], const float (&sm)[L + 1],
+                                        float sgn) {
+#pragma unroll
+  for (int l = 1; l <= L; ++l)
+#pragma unroll
+    for (int m = 1; m <= l; ++m) {
+      const int c = l * l + 2 * m - 1, s = c + 1;
+      const float sn = sgn * sm[m];
+      const float vc = v[c], vs = v[s];
+      v[c] = fmaf(cm[m], vc, -sn * vs);
+      v[s] = fmaf(sn, vc, cm[m] * vs);
+    }
+}
+
+// cos(m a), sin(m a) for m = 0..L from cos a, sin a
+template <int L>
+__device__ __forceinline__ void angle_powers(float c1, float s1, float (&cm)[L + 1], float (&sm)[L + 1]) {
+  cm[0] = 1.0f;
+  sm[0] = 0.0f;
+#pragma unroll
+  for (int m = 1; m <= L; ++m) {
+    cm[m] = fmaf(cm[m - 1], c1, -sm[m - 1] * s1);
+    sm[m] = fmaf(sm[m - 1], c1, cm[m - 1] * s1);
+  }
+}
+
+template <int L, int PS, int C>
+struct So2Msg {
+  using T = So2Tables<L, PS>;
+  using Cfg = So2Cfg<C>;
+  static constexpr int K = num_comp(L);
+
+  // acc[j][:] += message of edge e for channels cl + j*CL; wl = weights [P][C] in LDS
+  __device__ __forceinline__ static void run(int e, int N, int cl, const float* __restrict__ vec,
+                                             const int* __restrict__ src, const float* __restrict__ x,
+                                             const float* wl, float (&acc)[Cfg::CPL][K]) {
+    const float vx = vec[3 * e], vy = vec[3 * e + 1], vz = vec[3 * e + 2];
+    const int s = clamp_index(src[e], N);
+    // edge frame: cos/sin of phi and theta (identity for a zero vector or
+    // along the z axis, where phi is free)
+    const float r2 = vx * vx + vy * vy + vz * vz;
+    const bool nz = r2 > 0.0f;
+    const float inv_r = nz ? rsqrtf(r2) : 0.0f;
+    const float ux = vx * inv_r, uy = vy * inv_r, uz = nz ? vz * inv_r : 1.0f;
+    const float rho2 = ux * ux + uy * uy;
+    const bool tilt = rho2 > 0.0f;
+    const float inv_rho = tilt ? rsqrtf(rho2) : 0.0f;
+    float cp[L + 1], sp[L + 1], ct[L + 1], st[L + 1];
+    angle_powers<L>(tilt ? ux * inv_rho : 1.0f, tilt ? uy * inv_rho : 0.0f, cp, sp);
+    angle_powers<L>(uz, tilt ? rho2 * inv_rho : 0.0f, ct, st);
+    const float keep = nz ? 1.0f : 0.0f;  // paths with l2 > 0 vanish for a zero vector
+
+#pragma unroll
+    for (int j = 0; j < Cfg::CPL; ++j) {
+      float v[K];
+      const float* xp = x + ((size_t)s * C + cl + j * Cfg::CL) * K;
+      if constexpr (K % 4 == 0) {
+#pragma unroll
+        for (int q = 0; q < K / 4; ++q) {
+          const f4 t4 = reinterpret_cast<const f4*>(xp)[q];
+          v[4 * q] = t4[0];
+          v[4 * q + 1] = t4[1];
+          v[4 * q + 2] = t4[2];
+          v[4 * q + 3] = t4[3];
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < K; ++k) v[k] = xp[k];
+      }
+      // into the edge frame: J^T Z(-theta) J Z(-phi)
+      apply_z<L>(v, cp, sp, -1.0f);
+      apply_j<K, false>(v);
+      apply_z<L>(v, ct, st, -1.0f);
+      apply_j<K, true>(v);
+      // sparse coupling, one weight per path, one run per (path, output)
+      float m[K];
+#pragma unroll
+      for (int k = 0; k < K; ++k) m[k] = 0.0f;
+      float wp = 0.0f, t = 0.0f;
+      static_for<0, T::NT>([&](auto ii) {
+        constexpr int i = decltype(ii)::value;
+        constexpr eqtp_gen::So2Term tm = T::terms[i];
+        constexpr bool p_first = i == 0 || T::terms[i - 1].p != tm.p;
+        constexpr bool run_first = p_first || T::terms[i - 1].mu3 != tm.mu3;
+        constexpr bool run_last = i + 1 == T::NT || T::terms[i + 1].p != tm.p || T::terms[i + 1].mu3 != tm.mu3;
+        if constexpr (p_first) {
+          wp = wl[tm.p * C + cl + j * Cfg::CL];
+          if constexpr (tm.l2 > 0) wp *= keep;
+        }
+        t = run_first ? tm.c * v[tm.mu1] : fmaf(tm.c, v[tm.mu1], t);
+        if constexpr (run_last) m[tm.mu3] = fmaf(wp, t, m[tm.mu3]);
+      });
+      // back to the global frame: Z(phi) J^T Z(theta) J, added into acc
+      apply_j<K, false>(m);
+      apply_z<L>(m, ct, st, 1.0f);
+      apply_j<K, true>(m);
+      apply_z<L>(m, cp, sp, 1.0f);
+#pragma unroll
+      for (int k = 0; k < K; ++k) acc[j][k] += m[k];
+    }
+  }
+};
+
+template <int L, int PS, int C, bool ATOMIC>
+__global__ __launch_bounds__(So2Cfg<C>::THREADS) void conv_so2_kernel(int N, int E, const int* __restrict__ row_ptr,
+                                                                      const float* __restrict__ vec,
+                                                                      const int* __restrict__ src,
+                                                                      const int* __restrict__ dst,
+                                                                      const float* __restrict__ x,
+                                                                      const float* __restrict__ w,
+                                                                      float* __restrict__ out) {
+  using Cfg = So2Cfg<C>;
+  using T = So2Tables<L, PS>;
+  using M = So2Msg<L, PS, C>;
+  constexpr int K = num_comp(L);
+  __shared__ float wl[T::P * C];
+  for (int i = threadIdx.x; i < T::P * C; i += Cfg::THREADS) wl[i] = w[i];
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int g = lane / Cfg::CL;
+  const int cl = lane % Cfg::CL;
+
+  float acc[Cfg::CPL][K];
+  if constexpr (!ATOMIC) {
+    const int row = blockIdx.x * Cfg::WAVES + wv;
+    if (row >= N) return;
+    int e_beg = 0, e_end = 0;
+    if (E > 0) {
+      e_beg = min(max(row_ptr[row], 0), E);
+      e_end = min(max(row_ptr[row + 1], e_beg), E);
+    }
+#pragma unroll
+    for (int j = 0; j < Cfg::CPL; ++j)
+#pragma unroll
+      for (int k = 0; k < K; ++k) acc[j][k] = 0.0f;
+    for (int e = e_beg + g; e < e_end; e += Cfg::G) M::run(e, N, cl, vec, src, x, wl, acc);
+#pragma unroll
+    for (int off = Cfg::CL; off < kWave; off <<= 1)
+#pragma unroll
+      for (int j = 0; j < Cfg::CPL; ++j)
+#pragma unroll
+        for (int k = 0; k < K; ++k) acc[j][k] += __shfl_xor(acc[j][k], off);
+    if (g == 0) {
+#pragma unroll
+      for (int j = 0; j < Cfg::CPL; ++j) {
+        float* op = out + ((size_t)row * C + cl + j * Cfg::CL) * K;
+        if constexpr (K % 4 == 0) {
+#pragma unroll
+          for (int q = 0; q < K / 4; ++q)
+            reinterpret_cast<f4*>(op)[q] = f4{acc[j][4 * q], acc[j][4 * q + 1], acc[j][4 * q + 2], acc[j][4 * q + 3]};
+        } else {
+#pragma unroll
+          for (int k = 0; k < K; ++k) op[k] = acc[j][k];
+        }
+      }
+    }
+  } else {
+    constexpr int MSG = C * K;        // floats per edge message
+    constexpr int NI = Cfg::CPL * K;  // atomic instructions per wave and round
+    __shared__ float xch[Cfg::WAVES][kWave * NI];
+    __shared__ int xdst[Cfg::WAVES][Cfg::G];
+    float* const xw = xch[wv];
+    const long long base = ((long long)blockIdx.x * Cfg::WAVES + wv) * Cfg::EPW;
+    const int e_end = (int)min((long long)E, base + Cfg::EPW);
+    for (int e0 = (int)base; e0 < e_end; e0 += Cfg::G) {  // wave-uniform rounds of G edges
+      const int e = e0 + g;
+      const bool valid = e < e_end;
+#pragma unroll
+      for (int j = 0; j < Cfg::CPL; ++j)
+#pragma unroll
+        for (int k = 0; k < K; ++k) acc[j][k] = 0.0f;
+      if (valid) M::run(e, N, cl, vec, src, x, wl, acc);
+#pragma unroll
+      for (int j = 0; j < Cfg::CPL; ++j)
+#pragma unroll
+        for (int k = 0; k < K; ++k) xw[(g * C + cl + j * Cfg::CL) * K + k] = acc[j][k];
+      if (cl == 0) xdst[wv][g] = valid ? clamp_index(dst[e], N) : -1;
+      wave_lds_sync();
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int f = kWave * i + lane;
+        const int d = xdst[wv][f / MSG];
+        if (d >= 0) unsafeAtomicAdd(out + (size_t)d * MSG + f % MSG, xw[f]);
+      }
+      wave_lds_sync();
+    }
+  }
+}
+
+template <int L, int PS, int C>
+static hipError_t launch_so2_t(const ConvArgs& a) {
+  using Cfg = So2Cfg<C>;
+  constexpr int K = num_comp(L);
+  if (a.N == 0) return hipSuccess;
+  if (a.row_ptr != nullptr) {
+    const unsigned blocks = (unsigned)((a.N + Cfg::WAVES - 1) / Cfg::WAVES);
+    hipLaunchKernelGGL((conv_so2_kernel<L, PS, C, false>), dim3(blocks), dim3(Cfg::THREADS), 0, a.stream, (int)a.N,
+                       (int)a.E, a.row_ptr, a.vec, a.src, a.dst, (const float*)a.x, a.w, a.out);
+  } else {
+    hipError_t err = launch_fill_zero(a.out, a.N * C * K, a.stream);
+    if (err != hipSuccess) return err;
+    if (a.E == 0) return hipSuccess;
+    const long long per_block = (long long)Cfg::WAVES * Cfg::EPW;
+    const unsigned blocks = (unsigned)((a.E + per_block - 1) / per_block);
+    hipLaunchKernelGGL((conv_so2_kernel<L, PS, C, true>), dim3(blocks), dim3(Cfg::THREADS), 0, a.stream, (int)a.N,
+                       (int)a.E, a.row_ptr, a.vec, a.src, a.dst, (const float*)a.x, a.w, a.out);
+  }
+  return hipGetLastError();
+}
+
+template <int L, int PS>
+static hipError_t dispatch_so2_c(const ConvArgs& a) {
+  switch (a.C) {
+    case 8: return launch_so2_t<L, PS, 8>(a);
+    case 16: return launch_so2_t<L, PS, 16>(a);
+    case 32: return launch_so2_t<L, PS, 32>(a);
+    case 64: return launch_so2_t<L, PS, 64>(a);
+    case 128:
+      if constexpr (L <= kSo2MaxLC128) return launch_so2_t<L, PS, 128>(a);
+      else return hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_conv_so2(const ConvArgs& a) {
+  switch (a.lmax * 2 + a.path_set) {
+    case 0: return dispatch_so2_c<0, 0>(a);
+    case 1: return dispatch_so2_c<0, 1>(a);
+    case 2: return dispatch_so2_c<1, 0>(a);
+    case 3: return dispatch_so2_c<1, 1>(a);
+    case 4: return dispatch_so2_c<2, 0>(a);
+    case 5: return dispatch_so2_c<2, 1>(a);
+    case 6: return dispatch_so2_c<3, 0>(a);
+    case 7: return dispatch_so2_c<3, 1>(a);
+    case 8: return dispatch_so2_c<4, 0>(a);
+    case 9: return dispatch_so2_c<4, 1>(a);
+    case 10: return dispatch_so2_c<5, 0>(a);
+    case 11: return dispatch_so2_c<5, 1>(a);
+    case 12: return dispatch_so2_c<6, 0>(a);
+    case 13: return dispatch_so2_c<6, 1>(a);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace eqtp

@@ -59,6 +59,10 @@ hipError_t launch_linear(int64_t N, int C, int lmax, int bf16, const float* h, c
                          hipStream_t stream);
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t stream);
 hipError_t launch_conv_backward(const BwdArgs& a);   // fixed weights, vector ALUs
+// edge-aligned (SO(2)) form, lmax 0..6, fixed fp32 weights; C = 128 only up to kSo2MaxLC128
+constexpr int kSo2MaxL = 6;
+constexpr int kSo2MaxLC128 = 4;
+hipError_t launch_conv_so2(const ConvArgs& a);
 // grad_x / grad_w on the matrix cores from edges grouped by source: row_ptr =
 // CSR over sources, vec / dst in that order (src unused)
 hipError_t launch_conv_backward_by_source(const BwdArgs& a);

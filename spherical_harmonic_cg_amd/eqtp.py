@@ -21,7 +21,7 @@ EQTP_OK, EQTP_EINVAL, EQTP_EUNSUPPORTED, EQTP_EHIP = 0, 1, 2, 3
 EQTP_PATHS_PARITY, EQTP_PATHS_SO3 = 0, 1
 EQTP_W_FIXED, EQTP_W_RADIAL = 0, 1
 EQTP_EDGES_DST_SORTED, EQTP_EDGES_UNSORTED = 0, 1
-EQTP_ALGO_AUTO, EQTP_ALGO_NODE_MFMA, EQTP_ALGO_EDGE_VALU = 0, 1, 2
+EQTP_ALGO_AUTO, EQTP_ALGO_NODE_MFMA, EQTP_ALGO_EDGE_VALU, EQTP_ALGO_EDGE_SO2 = 0, 1, 2, 3
 EQTP_F32, EQTP_BF16 = 0, 1
 
 EXPORTED = ("eqtp_num_paths", "eqtp_path_table", "eqtp_sh", "eqtp_conv_fused", "eqtp_conv_messages",

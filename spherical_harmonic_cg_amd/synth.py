@@ -248,6 +248,19 @@ def make_config(name: str, seed: int = 2026, atom_order: str = "generation", pat
     raise KeyError(name)
 
 
+def lmax_graph(lmax: int, C: int, seed: int = 2026, n: int = 2000, r_cut: float = 4.0, path_set: int = 0) -> Workload:
+    """A periodic radius graph like the mid workload (density 0.1 / A^3, r_c =
+    4 A: about 27 neighbours per atom) with n atoms and features of degree up
+    to ``lmax`` (any lmax; for the edge-aligned form above 3)."""
+    ss = np.random.SeedSequence([seed, 100 + lmax, C, n]).spawn(4)
+    rng_pos, rng_feat, rng_w, rng_extra = (np.random.default_rng(s) for s in ss)
+    box = (n / DENSITY) ** (1.0 / 3.0)
+    pos = rng_pos.uniform(0.0, box, size=(n, 3))
+    src, dst = radius_edges(pos, r_cut, box)
+    return _finish("lmax%d" % lmax, pos, box, src, dst, lmax, C, rng_feat, rng_w, rng_extra, r_cut=r_cut,
+                   path_set=path_set)
+
+
 def random_permutation(wl: Workload, seed: int = 2026):
     """A seeded random edge order (for the unsorted / atomic path): returns
     (vec, src, dst) permuted, in the argument order of the convolution."""

@@ -42,12 +42,12 @@ def test_every_declared_symbol_is_exported():
 
 def test_num_paths_and_table_match_oracle():
     e = _lib()
-    for L in range(4):
+    for L in range(7):
         for ps in (0, 1):
             assert e.eqtp_num_paths(L, ps) == len(oracle.paths(L, ps))
             np.testing.assert_array_equal(e.eqtp_path_table(L, ps), oracle.paths(L, ps))
     lib = e.load_library()
-    assert lib.eqtp_num_paths(4, 0) == -e.EQTP_EUNSUPPORTED
+    assert lib.eqtp_num_paths(7, 0) == -e.EQTP_EUNSUPPORTED
     assert lib.eqtp_num_paths(3, 7) == -e.EQTP_EINVAL
 
 
@@ -70,7 +70,9 @@ NULL = ctypes.c_void_p(0)
 
 
 @pytest.mark.parametrize("kw,want", [
-    (dict(lmax=4), 2), (dict(lmax=-1), 1), (dict(C=48), 2), (dict(C=0), 1), (dict(path_set=3), 1),
+    (dict(lmax=7), 2), (dict(lmax=-1), 1), (dict(lmax=4, algo=1), 2), (dict(lmax=4, algo=2), 2),
+    (dict(lmax=4, weight_mode=1, r_cut=5.0), 2), (dict(lmax=4, x_dtype=1), 2), (dict(lmax=5, C=128), 2),
+    (dict(lmax=6, C=128, algo=3), 2), (dict(algo=3, weight_mode=1, r_cut=5.0), 2), (dict(algo=3, x_dtype=1), 2), (dict(C=48), 2), (dict(C=0), 1), (dict(path_set=3), 1),
     (dict(weight_mode=2), 1), (dict(edge_order=5), 1), (dict(algo=9), 1),
     (dict(weight_mode=1, r_cut=0.0), 1), (dict(weight_mode=1, r_cut=5.0, n_basis=6), 2),
     (dict(weight_mode=1, r_cut=5.0, algo=1), 2), (dict(edge_order=1, algo=1), 2),
@@ -169,10 +171,10 @@ def test_descriptor_versions_and_feature_dtype():
     assert ctypes.sizeof(e._ConvDesc) == 40
     conv = lambda d, **kw: lib.eqtp_conv_fused(ctypes.byref(d), 10, 20, FAKE, FAKE, kw.get("dst", NULL),
                                                kw.get("rp", FAKE), FAKE, FAKE, FAKE, NULL)
-    v1 = _desc(e, lmax=4)
+    v1 = _desc(e, lmax=7)
     v1.struct_size = 36  # a descriptor from before the x_dtype field: accepted, read as fp32 features
     assert conv(v1) == 2
-    v1b = _desc(e, lmax=4, x_dtype=1)
+    v1b = _desc(e, lmax=7, x_dtype=1)
     v1b.struct_size = 36  # x_dtype lies past struct_size, so it is not read
     assert conv(v1b) == 2
     assert conv(_desc(e, x_dtype=7)) == 1

@@ -68,7 +68,7 @@ def test_complex_cg_unitarity(l1, l2):
     np.testing.assert_allclose(M @ M.T, np.eye(n), atol=1e-13)
 
 
-@pytest.mark.parametrize("l1,l2", [(0, 3), (1, 2), (2, 2), (3, 3), (3, 2)])
+@pytest.mark.parametrize("l1,l2", [(0, 3), (1, 2), (2, 2), (3, 3), (3, 2), (4, 3), (5, 4), (6, 6), (6, 1)])
 def test_real_cg_unitarity_and_discard(l1, l2):
     """Real-basis blocks for all l3 stack into an orthogonal matrix, and the
     dropped part (imag for even, real for odd l1+l2+l3) vanishes."""
@@ -151,6 +151,32 @@ def test_real_cg_along_z():
                 assert abs(C[c1, 0, s3] + ref) < 1e-14
                 assert abs(C[s1, 0, c3] - ref) < 1e-14
                 assert abs(C[c1, 0, c3]) < 1e-14 and abs(C[s1, 0, s3]) < 1e-14
+
+
+@pytest.mark.parametrize("lmax", [5, 6])
+def test_real_cg_along_z_high_l(lmax):
+    """The along-z reduction for every path with max(l1, l2, l3) = lmax (the
+    blocks the edge-aligned form uses at high degree), against sympy."""
+    for l1, l2, l3 in _triples(lmax):
+        if max(l1, l2, l3) != lmax:
+            continue
+        C = oracle.cg_real(l1, l2, l3)
+        odd = (l1 + l2 + l3) % 2
+        for m in range(0, min(l1, l3) + 1):
+            ref = _sympy_cg(l1, m, l2, 0, l3, m)
+            if m == 0:
+                assert abs(C[0, 0, 0] - (0.0 if odd else ref)) < 1e-13
+                continue
+            c1, s1 = 2 * m - 1, 2 * m
+            if not odd:
+                assert abs(C[c1, 0, c1] - ref) < 1e-13 and abs(C[s1, 0, s1] - ref) < 1e-13
+            else:
+                assert abs(C[c1, 0, s1] + ref) < 1e-13 and abs(C[s1, 0, c1] - ref) < 1e-13
+        # nothing couples different |m| through the m = 0 harmonic
+        for a in range(2 * l1 + 1):
+            for c in range(2 * l3 + 1):
+                if (a + 1) // 2 != (c + 1) // 2:
+                    assert abs(C[a, 0, c]) < 1e-14
 
 
 def test_levi_civita_path():

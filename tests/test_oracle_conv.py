@@ -161,7 +161,8 @@ def _small_problem(lmax, C, seed, radial=False, path_set=0, n=7, e=25):
     return n, vec, src, dst, x, w
 
 
-@pytest.mark.parametrize("lmax,path_set,radial", [(3, 0, False), (3, 1, False), (2, 0, False), (3, 0, True)])
+@pytest.mark.parametrize("lmax,path_set,radial", [(3, 0, False), (3, 1, False), (2, 0, False), (3, 0, True),
+                                                  (4, 1, False), (5, 0, False), (6, 0, False)])
 def test_equivariance(lmax, path_set, radial):
     """conv(R vec, D x) = D conv(vec, x) to 1e-10 (fp64 inputs)."""
     n, vec, src, dst, x, w = _small_problem(lmax, 4, 21, radial, path_set)
