@@ -41,13 +41,36 @@ def log(*a):
 
 
 def count_terms(lmax, path_set):
-    """Non-zero coupling coefficients (2*nnz*C flops per edge) from the library's table."""
+    """Non-zero coupling coefficients (2*nnz*C flops per edge) from the library's tables."""
     import re
 
-    inc = os.path.join(ROOT, "spherical_harmonic_cg_amd", "csrc", "generated", "cg_tables.inc")
+    gen = os.path.join(ROOT, "spherical_harmonic_cg_amd", "csrc", "generated")
     tag = "L%d_%s" % (lmax, "parity" if path_set == 0 else "so3")
-    m = re.search(r"constexpr int kNumTerms_%s = (\d+);" % tag, open(inc).read())
+    m = re.search(r"constexpr int kNumTerms_%s = (\d+);" % tag, open(os.path.join(gen, "cg_tables.inc")).read())
+    if m:
+        return int(m.group(1))
+    m = re.search(r"lmax = %d, %s path set: \d+ paths, \d+ edge-aligned terms \(full coupling: (\d+)\)" % (
+        lmax, "parity" if path_set == 0 else "so3"), open(os.path.join(gen, "so2_tables.inc")).read())
     return int(m.group(1))
+
+
+def so2_ops(lmax, path_set):
+    """Arithmetic instructions per edge and channel of the edge-aligned kernel,
+    from its tables: two frame rotations (4 per (m cos, m sin) pair for each of
+    the two pair rotations, one per non-zero of J and of J^T) and the sparse
+    coupling (one per term plus one per (path, output) run)."""
+    import re
+
+    txt = open(os.path.join(ROOT, "spherical_harmonic_cg_amd", "csrc", "generated", "so2_tables.inc")).read()
+    K = (lmax + 1) ** 2
+    starts = [int(v) for v in re.search(r"kJRowStart\[\d+\] = \{([^}]*)\}", txt).group(1).split(",")]
+    nnz_j = starts[K]
+    pairs = lmax * (lmax + 1) // 2
+    tag = "L%d_%s" % (lmax, "parity" if path_set == 0 else "so3")
+    body = re.search(r"kSo2Terms_%s\[\d+\] = \{(.*?)\n\};" % tag, txt, re.S).group(1)
+    terms = [tuple(int(v) for v in ln.strip().strip("{").split(",")[:3]) for ln in body.strip().splitlines()]
+    runs = len({(p, mu3) for (p, _, mu3) in terms})
+    return 2 * (2 * 4 * pairs + 2 * nnz_j) + len(terms) + runs
 
 
 KERNEL_SOURCES = ("spherical_harmonic_cg_amd/csrc/conv_node.hip", "spherical_harmonic_cg_amd/csrc/eqtp_device.hpp",
@@ -134,6 +157,9 @@ def main():
                     help="'so3': the 34-path SO(3) set (a labelled extra, not the headline)")
     ap.add_argument("--x-bf16", action="store_true",
                     help="bfloat16 node features (a labelled extra: halves the gathered bytes)")
+    ap.add_argument("--lmax", type=int, default=None,
+                    help="instead of --config: the mid graph (10k atoms, r_c=4 A, C=64) with features of degree "
+                         "up to LMAX (4..6 run the edge-aligned kernel; a labelled extra, not the headline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
     ap.add_argument("--backward", action="store_true",
@@ -164,8 +190,11 @@ def main():
     torch.cuda.set_device(0)
 
     t_gen = time.perf_counter()
-    wl = synth.make_config(args.config, atom_order=args.atom_order,
-                           path_set=1 if args.path_set == "so3" else 0)
+    if args.lmax is not None:
+        wl = synth.lmax_graph(args.lmax, 64, seed=2026, n=10000, path_set=1 if args.path_set == "so3" else 0)
+    else:
+        wl = synth.make_config(args.config, atom_order=args.atom_order,
+                               path_set=1 if args.path_set == "so3" else 0)
     log("workload %s: N=%d E=%d C=%d lmax=%d P=%d (generated in %.1fs)" % (wl.name, wl.N, wl.E, wl.C, wl.lmax,
                                                                             wl.P, time.perf_counter() - t_gen))
     dev = torch.device("cuda:0")
@@ -340,10 +369,19 @@ def main():
     flop_edge = 2 * nnz * wl.C + (2 * 8 * wl.P * wl.C if wl.weight_mode == 1 else 0)
     conv_s = float(conv_ms.mean()) * 1e-3
     achieved_tflops = flop_edge * wl.E / conv_s / 1e12
+    cfg_key = args.config if args.lmax is None else "lmax%d" % args.lmax
     roofline = {"bound": "mfma", "achieved": round(achieved_tflops, 3), "peak": PEAK_FP32_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved_tflops / PEAK_FP32_TFLOPS, 4),
-                "traffic": measured_traffic(args.config, args.atom_order, args.unsorted, args.algo, args.path_set,
+                "traffic": measured_traffic(cfg_key, args.atom_order, args.unsorted, args.algo, args.path_set,
                                             args.x_bf16, args.sort_edges)}
+    if args.algo == 3 or wl.lmax > 3:
+        # edge-aligned kernel: vector-ALU bound; flop = 2 per arithmetic instruction lane it executes
+        ops = so2_ops(wl.lmax, wl.path_set)
+        so2_tflops = 2 * ops * wl.C * wl.E / conv_s / 1e12
+        roofline = {"bound": "alu", "achieved": round(so2_tflops, 3), "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(so2_tflops / PEAK_FP32_TFLOPS, 4), "traffic": None,
+                    "counted": "%d arithmetic ops per edge and channel (two frame rotations + sparse coupling), "
+                               "2 flop each; the coupling form would count 2*%d" % (ops, nnz)}
     alg_bytes = 2 * wl.N * wl.C * wl.K * 4 + wl.E * 16 + (wl.N + 1) * 4 + wl.weights.size * 4
     log("conv: %.3e counted flop (2*nnz*C per edge), %.1f MB algorithmic bytes -> %.1f GB/s" % (
         flop_edge * wl.E, alg_bytes / 1e6, alg_bytes / conv_s / 1e9))
@@ -366,7 +404,10 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": WORKLOAD_TEXT[args.config] + (" (random edge order)" if args.unsorted else "")
+        "config": {"workload": (WORKLOAD_TEXT[args.config] if args.lmax is None else
+                                "mid graph at lmax %d: 10k atoms, periodic 0.1/A^3, r_c=4 A, L=%d, C=64, conv"
+                                % (wl.lmax, wl.lmax))
+                   + (" (random edge order)" if args.unsorted else "")
                    + (" (sorted by destination on the GPU inside each step)" if args.sort_edges else "")
                    + (" (cell-sorted atom numbering)" if args.atom_order == "cell" else "")
                    + (" (SO(3) path set)" if args.path_set == "so3" else "")
