@@ -212,6 +212,13 @@ __global__ __launch_bounds__(So2Cfg<C>::THREADS) void conv_so2_kernel(int N, int
   const int g = lane / Cfg::CL;
   const int cl = lane % Cfg::CL;
 
+  constexpr int MSG = C * K;        // floats per edge message
+  constexpr int NI = Cfg::CPL * K;  // floats per lane of one round's messages
+  // sorted rows at lmax >= 4 sum the messages in LDS (the lane's own slots)
+  // rather than in registers, which the rotations and the coupling need
+  constexpr bool LDS_ACC = !ATOMIC && K > 16;
+  constexpr bool XCH = ATOMIC || LDS_ACC;
+  __shared__ float xch[XCH ? Cfg::WAVES : 1][XCH ? kWave * NI : 1];
   float acc[Cfg::CPL][K];
   if constexpr (!ATOMIC) {
     const int row = blockIdx.x * Cfg::WAVES + wv;
@@ -221,17 +228,49 @@ __global__ __launch_bounds__(So2Cfg<C>::THREADS) void conv_so2_kernel(int N, int
       e_beg = min(max(row_ptr[row], 0), E);
       e_end = min(max(row_ptr[row + 1], e_beg), E);
     }
+    if constexpr (LDS_ACC) {
+      float* const xw = xch[wv];
 #pragma unroll
-    for (int j = 0; j < Cfg::CPL; ++j)
+      for (int i = 0; i < NI; ++i) xw[kWave * i + lane] = 0.0f;
+      wave_lds_sync();
+#pragma clang loop unroll(disable)
+      for (int e0 = e_beg; e0 < e_end; e0 += Cfg::G) {  // wave-uniform rounds of G edges
+        const int e = e0 + g;
 #pragma unroll
-      for (int k = 0; k < K; ++k) acc[j][k] = 0.0f;
-    for (int e = e_beg + g; e < e_end; e += Cfg::G) M::run(e, N, cl, vec, src, x, wl, acc);
+        for (int j = 0; j < Cfg::CPL; ++j)
 #pragma unroll
-    for (int off = Cfg::CL; off < kWave; off <<= 1)
+          for (int k = 0; k < K; ++k) acc[j][k] = 0.0f;
+        if (e < e_end) M::run(e, N, cl, vec, src, x, wl, acc);
+        __builtin_amdgcn_sched_barrier(0);  // keep the LDS sums after the message (bounded live range)
+#pragma unroll
+        for (int j = 0; j < Cfg::CPL; ++j)
+#pragma unroll
+          for (int k = 0; k < K; ++k) xw[(g * C + cl + j * Cfg::CL) * K + k] += acc[j][k];
+        wave_lds_sync();
+      }
+      wave_lds_sync();
 #pragma unroll
       for (int j = 0; j < Cfg::CPL; ++j)
 #pragma unroll
-        for (int k = 0; k < K; ++k) acc[j][k] += __shfl_xor(acc[j][k], off);
+        for (int k = 0; k < K; ++k) {
+          float t = 0.0f;
+#pragma unroll
+          for (int gg = 0; gg < Cfg::G; ++gg) t += xw[(gg * C + cl + j * Cfg::CL) * K + k];
+          acc[j][k] = t;
+        }
+    } else {
+#pragma unroll
+      for (int j = 0; j < Cfg::CPL; ++j)
+#pragma unroll
+        for (int k = 0; k < K; ++k) acc[j][k] = 0.0f;
+      for (int e = e_beg + g; e < e_end; e += Cfg::G) M::run(e, N, cl, vec, src, x, wl, acc);
+#pragma unroll
+      for (int off = Cfg::CL; off < kWave; off <<= 1)
+#pragma unroll
+        for (int j = 0; j < Cfg::CPL; ++j)
+#pragma unroll
+          for (int k = 0; k < K; ++k) acc[j][k] += __shfl_xor(acc[j][k], off);
+    }
     if (g == 0) {
 #pragma unroll
       for (int j = 0; j < Cfg::CPL; ++j) {
@@ -247,9 +286,6 @@ __global__ __launch_bounds__(So2Cfg<C>::THREADS) void conv_so2_kernel(int N, int
       }
     }
   } else {
-    constexpr int MSG = C * K;        // floats per edge message
-    constexpr int NI = Cfg::CPL * K;  // atomic instructions per wave and round
-    __shared__ float xch[Cfg::WAVES][kWave * NI];
     __shared__ int xdst[Cfg::WAVES][Cfg::G];
     float* const xw = xch[wv];
     const long long base = ((long long)blockIdx.x * Cfg::WAVES + wv) * Cfg::EPW;
@@ -262,6 +298,7 @@ __global__ __launch_bounds__(So2Cfg<C>::THREADS) void conv_so2_kernel(int N, int
 #pragma unroll
         for (int k = 0; k < K; ++k) acc[j][k] = 0.0f;
       if (valid) M::run(e, N, cl, vec, src, x, wl, acc);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int j = 0; j < Cfg::CPL; ++j)
 #pragma unroll
