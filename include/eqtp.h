@@ -95,7 +95,8 @@ int eqtp_path_table(int lmax, int path_set, int32_t* l1l2l3 /* host */);
  * "2. register intermediate computation").
  *   vec [E, 3] fp32, any length; a zero vector gives (Y00, 0, ..., 0).
  *   Y   [E, (lmax+1)^2] fp32 output, 16-byte aligned; fully overwritten.
- *   lmax in [0, 3]; 0 <= E < 2^31.
+ *   lmax in [0, 6]; 0 <= E < 2^31.  lmax <= 3: closed-form polynomials;
+ *   4..6: the Legendre-derivative recurrence in z times Re/Im (x + i y)^m.
  * Orthonormal harmonics with the Condon-Shortley phase:
  *   Y00 = 0.28209479177387814, Y10 = 0.4886025119029199 z,
  *   Y11c = -0.4886025119029199 x, Y11s = -0.4886025119029199 y (unit vector),
@@ -164,7 +165,9 @@ int eqtp_conv_fused(const eqtp_conv_desc* d, int64_t N, int64_t E, const float* 
  * source indices [E] in, messages [E,C,16] out):
  *   messages[e, c, l3 m3] = sum_p w_e[p, c] sum_{m1, m2} C^p[m1, m2, m3] x[src_e, c, l1 m1] Y_{l2 m2}(vec_e)
  * d: lmax, C, path_set, weight_mode, r_cut, n_basis as for eqtp_conv_fused
- * (edge_order and algo are ignored); N, E, vec, src, x, weights as there.
+ * (edge_order is ignored); N, E, vec, src, x, weights as there.  lmax 4..6,
+ * or d->algo = EQTP_ALGO_EDGE_SO2, use the edge-aligned form (fixed weights
+ * only, C = 128 up to lmax 4); otherwise the coupling form.
  *   messages [E, C, K] fp32, 16-byte aligned, fully overwritten; must not
  *            alias an input.  Deterministic.
  */

@@ -78,7 +78,7 @@ int eqtp_path_table(int lmax, int path_set, int32_t* l1l2l3) {
 }
 
 int eqtp_sh(const float* vec, int64_t E, int lmax, float* Y, void* stream) {
-  if (lmax < 0 || lmax > 3) return lmax < 0 ? EQTP_EINVAL : EQTP_EUNSUPPORTED;
+  if (lmax < 0 || lmax > eqtp::kSo2MaxL) return lmax < 0 ? EQTP_EINVAL : EQTP_EUNSUPPORTED;
   if (E < 0 || E > kMaxIndex) return EQTP_EINVAL;
   if (E == 0) return EQTP_OK;
   if (!vec || !Y || !aligned4(vec) || !aligned16(Y)) return EQTP_EINVAL;
@@ -154,7 +154,11 @@ int eqtp_conv_messages(const eqtp_conv_desc* d, int64_t N, int64_t E, const floa
   if (!desc_ok(d)) return EQTP_EINVAL;
   if (desc_x_dtype(d) != EQTP_F32) return desc_x_dtype(d) == EQTP_BF16 ? EQTP_EUNSUPPORTED : EQTP_EINVAL;
   if (d->lmax < 0) return EQTP_EINVAL;
-  if (d->lmax > 3) return EQTP_EUNSUPPORTED;
+  if (d->lmax > eqtp::kSo2MaxL) return EQTP_EUNSUPPORTED;
+  // lmax above 3 (or algo = EDGE_SO2): the edge-aligned form, fixed weights
+  const bool use_so2 = d->lmax > 3 || d->algo == EQTP_ALGO_EDGE_SO2;
+  if (use_so2 && d->weight_mode != EQTP_W_FIXED) return EQTP_EUNSUPPORTED;
+  if (use_so2 && d->C == 128 && d->lmax > eqtp::kSo2MaxLC128) return EQTP_EUNSUPPORTED;
   if (d->path_set != EQTP_PATHS_PARITY && d->path_set != EQTP_PATHS_SO3) return EQTP_EINVAL;
   if (d->weight_mode != EQTP_W_FIXED && d->weight_mode != EQTP_W_RADIAL) return EQTP_EINVAL;
   if (d->C <= 0) return EQTP_EINVAL;
@@ -186,6 +190,10 @@ int eqtp_conv_messages(const eqtp_conv_desc* d, int64_t N, int64_t E, const floa
   a.w = weights;
   a.out = messages;
   a.stream = (hipStream_t)stream;
+  if (use_so2) {
+    a.messages = 1;
+    return status_of(eqtp::launch_conv_so2(a));
+  }
   return status_of(eqtp::launch_conv_messages(a));
 }
 

@@ -316,11 +316,64 @@ __global__ __launch_bounds__(So2Cfg<C>::THREADS) void conv_so2_kernel(int N, int
   }
 }
 
+// Per-edge messages in the edge-aligned form (the page's fused-kernel output
+// [E, C, K], no destination sum): the wave's store of one edge covers its
+// C*K*4 contiguous bytes.
+template <int L, int PS, int C>
+__global__ __launch_bounds__(So2Cfg<C>::THREADS) void conv_so2_msg_kernel(int N, int E, const float* __restrict__ vec,
+                                                                          const int* __restrict__ src,
+                                                                          const float* __restrict__ x,
+                                                                          const float* __restrict__ w,
+                                                                          float* __restrict__ msg) {
+  using Cfg = So2Cfg<C>;
+  using T = So2Tables<L, PS>;
+  using M = So2Msg<L, PS, C>;
+  constexpr int K = num_comp(L);
+  __shared__ float wl[T::P * C];
+  for (int i = threadIdx.x; i < T::P * C; i += Cfg::THREADS) wl[i] = w[i];
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int g = lane / Cfg::CL;
+  const int cl = lane % Cfg::CL;
+  const long long base = ((long long)blockIdx.x * Cfg::WAVES + wv) * Cfg::EPW;
+  const int e_end = (int)min((long long)E, base + Cfg::EPW);
+#pragma clang loop unroll(disable)
+  for (int e = (int)base + g; e < e_end; e += Cfg::G) {
+    float acc[Cfg::CPL][K];
+#pragma unroll
+    for (int j = 0; j < Cfg::CPL; ++j)
+#pragma unroll
+      for (int k = 0; k < K; ++k) acc[j][k] = 0.0f;
+    M::run(e, N, cl, vec, src, x, wl, acc);
+#pragma unroll
+    for (int j = 0; j < Cfg::CPL; ++j) {
+      float* op = msg + ((size_t)e * C + cl + j * Cfg::CL) * K;
+      if constexpr (K % 4 == 0) {
+#pragma unroll
+        for (int q = 0; q < K / 4; ++q)
+          reinterpret_cast<f4*>(op)[q] = f4{acc[j][4 * q], acc[j][4 * q + 1], acc[j][4 * q + 2], acc[j][4 * q + 3]};
+      } else {
+#pragma unroll
+        for (int k = 0; k < K; ++k) op[k] = acc[j][k];
+      }
+    }
+  }
+}
+
 template <int L, int PS, int C>
 static hipError_t launch_so2_t(const ConvArgs& a) {
   using Cfg = So2Cfg<C>;
   constexpr int K = num_comp(L);
   if (a.N == 0) return hipSuccess;
+  if (a.messages) {
+    if (a.E == 0) return hipSuccess;
+    const long long per_block = (long long)Cfg::WAVES * Cfg::EPW;
+    const unsigned blocks = (unsigned)((a.E + per_block - 1) / per_block);
+    hipLaunchKernelGGL((conv_so2_msg_kernel<L, PS, C>), dim3(blocks), dim3(Cfg::THREADS), 0, a.stream, (int)a.N,
+                       (int)a.E, a.vec, a.src, (const float*)a.x, a.w, a.out);
+    return hipGetLastError();
+  }
   if (a.row_ptr != nullptr) {
     const unsigned blocks = (unsigned)((a.N + Cfg::WAVES - 1) / Cfg::WAVES);
     hipLaunchKernelGGL((conv_so2_kernel<L, PS, C, false>), dim3(blocks), dim3(Cfg::THREADS), 0, a.stream, (int)a.N,

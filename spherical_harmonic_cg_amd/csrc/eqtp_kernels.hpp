@@ -11,7 +11,8 @@ namespace eqtp {
 struct ConvArgs {
   int64_t N, E;
   int lmax, C, path_set, weight_mode, edge_order;
-  int x_bf16 = 0;  // x holds bfloat16 features (node algorithm only)
+  int x_bf16 = 0;
+  int messages = 0;  // edge-aligned kernel: per-edge messages [E, C, K] into out instead of the sum  // x holds bfloat16 features (node algorithm only)
   float r_cut;
   const float* vec;
   const int32_t* src;

@@ -24,6 +24,9 @@ receives at most a couple of input components of the same |m|.
 * Every table is checked here: the rotation property of the harmonics, the
   equivariance of the Clebsch-Gordan tables under D, and that the sparse
   coupling after rotation equals the full coupling for random inputs.
+* Harmonic prefactors for degrees up to 6 (standalone evaluation by the
+  Legendre-derivative recurrence): sqrt((2l+1)/(4 pi) (l-m)!/(l+m)!), times
+  sqrt2 (-1)^m for m > 0.
 """
 from __future__ import annotations
 
@@ -240,6 +243,24 @@ def main(out_path: str = OUT):
     w("};")
     startsT = [next((i for i, e in enumerate(JTent) if e[0] >= r), len(JTent)) for r in range(nrow + 1)]
     w("constexpr short kJTRowStart[%d] = {%s};" % (nrow + 1, ", ".join(str(s) for s in startsT)))
+    w("")
+    # harmonics of degree up to LMAX_SO2 for the standalone evaluation:
+    #   Y_l0 = N_l0 Q_l^0(z),  Y_lm,c/s = sqrt2 (-1)^m N_lm Q_l^m(z) Re/Im (x + i y)^m
+    # with Q_l^m = d^m P_l / dz^m and N_lm = sqrt((2l+1)/(4 pi) (l-m)!/(l+m)!)
+    pi = cg._pi()
+    w("// real-harmonic prefactors A[l][m] (see sh.hip), nearest float32 of the exact value")
+    w("constexpr float kShPrefactor[%d][%d] = {" % (LMAX_SO2 + 1, LMAX_SO2 + 1))
+    for l in range(LMAX_SO2 + 1):
+        vals = []
+        for m in range(LMAX_SO2 + 1):
+            if m > l:
+                vals.append("0.0f")
+                continue
+            n2 = Decimal(2 * l + 1) / (4 * pi) * Decimal(math.factorial(l - m)) / Decimal(math.factorial(l + m))
+            a = n2.sqrt() if m == 0 else (2 * n2).sqrt() * (-1 if m % 2 else 1)
+            vals.append(cg.f32_literal(cg.nearest_f32(a)))
+        w("    {%s}," % ", ".join(vals))
+    w("};")
     w("")
     summary = []
     for path_set, psname in cg.PATH_SETS.items():

@@ -197,8 +197,10 @@ def eqtp_conv_fused(vec, src, x, weights, lmax: int, row_ptr=None, dst=None, pat
 
 
 def eqtp_conv_messages(vec, src, x, weights, lmax: int, path_set: int = EQTP_PATHS_PARITY,
-                       weight_mode: int = EQTP_W_FIXED, r_cut: float = 0.0, n_basis: int = 8, out=None):
-    """messages [E, C, K]: one message per edge, no destination sum."""
+                       weight_mode: int = EQTP_W_FIXED, r_cut: float = 0.0, n_basis: int = 8, out=None,
+                       algo: int = EQTP_ALGO_AUTO):
+    """messages [E, C, K]: one message per edge, no destination sum (lmax 4..6 or
+    algo=EQTP_ALGO_EDGE_SO2: the edge-aligned form)."""
     import torch
 
     _check(x, "x", torch.float32)
@@ -216,7 +218,7 @@ def eqtp_conv_messages(vec, src, x, weights, lmax: int, path_set: int = EQTP_PAT
     if out is None:
         out = torch.empty((E, C, K), dtype=torch.float32, device=x.device)
     _check(out, "out", torch.float32, (E, C, K))
-    d = _ConvDesc(ctypes.sizeof(_ConvDesc), lmax, C, path_set, weight_mode, EQTP_EDGES_UNSORTED, EQTP_ALGO_AUTO,
+    d = _ConvDesc(ctypes.sizeof(_ConvDesc), lmax, C, path_set, weight_mode, EQTP_EDGES_UNSORTED, algo,
                   float(r_cut), n_basis, EQTP_F32)
     rc = load_library().eqtp_conv_messages(ctypes.byref(d), N, E, _ptr(vec), _ptr(src), _ptr(x), _ptr(weights),
                                            _ptr(out), _stream())

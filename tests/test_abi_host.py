@@ -110,7 +110,7 @@ def test_conv_pointer_and_size_validation():
 def test_sh_and_linear_validation():
     e = _lib()
     lib = e.load_library()
-    assert lib.eqtp_sh(FAKE, 10, 4, FAKE, NULL) == 2
+    assert lib.eqtp_sh(FAKE, 10, 7, FAKE, NULL) == 2
     assert lib.eqtp_sh(FAKE, -1, 3, FAKE, NULL) == 1
     assert lib.eqtp_sh(NULL, 10, 3, FAKE, NULL) == 1
     assert lib.eqtp_sh(FAKE, 10, 3, ctypes.c_void_p(0x10008), NULL) == 1
@@ -154,7 +154,11 @@ def test_conv_messages_validation():
     def call(d, N=10, E=20, vec=FAKE, src=FAKE, x=FAKE, w=FAKE, m=FAKE):
         return lib.eqtp_conv_messages(ctypes.byref(d), N, E, vec, src, x, w, m, NULL)
 
-    assert call(_desc(e, lmax=4)) == 2
+    assert call(_desc(e, lmax=7)) == 2
+    assert call(_desc(e, lmax=4, weight_mode=1, r_cut=4.0)) == 2          # edge-aligned form: fixed weights
+    assert call(_desc(e, algo=3, weight_mode=1, r_cut=4.0)) == 2
+    assert call(_desc(e, lmax=5, C=128)) == 2
+    assert call(_desc(e, lmax=5), m=NULL) == 1
     assert call(_desc(e, C=24)) == 2
     assert call(_desc(e, weight_mode=1, r_cut=0.0)) == 1
     assert call(_desc(e, weight_mode=1, r_cut=4.0, n_basis=4)) == 2

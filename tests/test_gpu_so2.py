@@ -111,3 +111,36 @@ def test_so2_lmax6_graph_sampled():
     _assert_close(out[rows], ref, TOL, "so2 L6 sorted")
     outu = _np(_run(eq, wl, True))
     _assert_close(outu[rows], ref, TOL, "so2 L6 unsorted")
+
+
+@pytest.mark.parametrize("L,ps,C", [(4, 0, 32), (5, 1, 16), (6, 0, 64), (6, 1, 8), (4, 1, 128), (3, 0, 64), (2, 1, 32)])
+def test_so2_messages(L, ps, C):
+    """Per-edge messages [E, C, K] in the edge-aligned form (lmax > 3, or
+    algo = EDGE_SO2 at lmax <= 3) against the oracle's messages."""
+    eq = _eq()
+    wl = _graph(L, ps, C, 400 + 10 * L + C + ps, n=11, deg=5)
+    _say("so2 messages L=%d ps=%d C=%d E=%d" % (L, ps, C, wl.src.shape[0]))
+    ref = oracle.messages(wl.N, wl.vec, wl.src, wl.x, wl.w, L, path_set=ps)
+    got = eq.eqtp_conv_messages(_t(wl.vec), _t(wl.src), _t(wl.x), _t(wl.w), L, path_set=ps, algo=SO2)
+    _assert_close(_np(got), ref, TOL, "so2 messages L%d ps%d C%d" % (L, ps, C))
+    if L > 3:  # the default choice at high degree
+        got2 = eq.eqtp_conv_messages(_t(wl.vec), _t(wl.src), _t(wl.x), _t(wl.w), L, path_set=ps)
+        assert np.array_equal(_np(got2), _np(got))
+
+
+@pytest.mark.parametrize("L", [4, 5, 6])
+@pytest.mark.parametrize("E", [1, 255, 256, 257, 5000])
+def test_sh_high_degree(L, E):
+    """Standalone harmonics at degree 4..6 (recurrence) against the oracle's,
+    with zero vectors, the +-z axis and tiny / huge lengths."""
+    eq = _eq()
+    rng = np.random.default_rng(E + 10 * L)
+    v = (rng.standard_normal((E, 3)) * rng.uniform(0.01, 50.0, (E, 1))).astype(np.float32)
+    special = np.array([[0, 0, 0], [0, 0, 3.0], [0, 0, -0.2], [1e-3, 0, 0], [0, -7.0, 0]], np.float32)
+    v[: min(E, 5)] = special[: min(E, 5)]
+    _say("sh high degree L=%d E=%d" % (L, E))
+    got = _np(eq.eqtp_sh(_t(v), L))
+    ref = oracle.sh(v, L)
+    assert np.abs(got - ref).max() <= 2e-5 * max(1.0, np.abs(ref).max())
+    if E >= 1:
+        assert got[0, 0] == np.float32(0.28209479177387814) and np.all(got[0, 1:] == 0.0)
