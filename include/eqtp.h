@@ -187,7 +187,7 @@ int eqtp_conv_messages(const eqtp_conv_desc* d, int64_t N, int64_t E, const floa
  * grad_vec = 0.
  *   d, N, E, vec, src, dst, row_ptr, x, weights: as for eqtp_conv_fused;
  *            d->weight_mode must be EQTP_W_FIXED (radial weights:
- *            EQTP_EUNSUPPORTED); d->algo is ignored.
+ *            EQTP_EUNSUPPORTED).
  *   grad_out [N, C, K] fp32.
  *   grad_x   [N, C, K] fp32, 16-byte aligned, or NULL (not computed).
  *   grad_w   [P, C] fp32, or NULL.
@@ -195,7 +195,10 @@ int eqtp_conv_messages(const eqtp_conv_desc* d, int64_t N, int64_t E, const floa
  * Each requested output is fully overwritten; outputs must not alias inputs
  * or each other.  grad_x and grad_w are sums of fp32 atomics (their
  * summation order varies from run to run); grad_vec is written once per
- * edge.  Errors as for eqtp_conv_fused.
+ * edge.  Errors as for eqtp_conv_fused.  d->algo: for dst-sorted edges,
+ * grad_vec runs on the matrix cores (dL/dY_e = x[src_e] contracted with a
+ * per-node B_d built from grad_out) unless d->algo = EQTP_ALGO_EDGE_VALU,
+ * which walks the coupling per edge on the vector ALUs.
  */
 int eqtp_conv_backward(const eqtp_conv_desc* d, int64_t N, int64_t E, const float* vec, const int32_t* src,
                        const int32_t* dst, const int32_t* row_ptr, const float* x, const float* weights,

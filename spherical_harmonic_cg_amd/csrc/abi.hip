@@ -238,6 +238,7 @@ int eqtp_conv_backward(const eqtp_conv_desc* d, int64_t N, int64_t E, const floa
   a.gx = grad_x;
   a.gw = grad_w;
   a.gvec = grad_vec;
+  a.algo = d->algo;
   a.stream = (hipStream_t)stream;
   return status_of(eqtp::launch_conv_backward(a));
 }

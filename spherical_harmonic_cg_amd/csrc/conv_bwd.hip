@@ -339,6 +339,171 @@ __global__ __launch_bounds__(BwdCfg<C>::THREADS) void conv_bwd_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// grad_vec of dst-sorted rows on the matrix cores.  For the row of node d and
+// an edge e of it, with B_d[c,m1,m2] = sum_p w[p,c] sum_m3 C^p[m1,m2,m3] g[d,c,m3]
+// (edge independent):
+//   dL/dY_e[m2] = sum_{c,m1} x[src_e,c,m1] B_d[c,m1,m2]
+// -- a [16 edges x 256] x [256 x 16] product per 16-channel block on
+// v_mfma_f32_16x16x4_f32 (rows = edges, columns = m2, k = (channel, m1)),
+// 4 MFMAs per edge and block as in the forward.  One wave per row (persistent
+// over rows); per chunk of up to 64 edges and per channel block:
+//   1. lanes 0..15 (one channel each) build B_d in LDS from g[d] with the
+//      coupling walked in (m1, m2, p) order (runs over m3);
+//   2. 16-edge steps: lane (edge i = lane % 16, group kq = lane / 16) loads
+//      x[src_i, c, 4kq .. 4kq+3] for the block's 16 channels and feeds the
+//      MFMAs; dL/dY accumulates across blocks in registers;
+// then dL/dY goes through LDS to one lane per edge, which applies the
+// harmonics' Jacobian (sh_grad_eval) and writes grad_vec.
+// ---------------------------------------------------------------------------
+template <int L, int PS>
+struct TermOrderB {  // stable counting sort of the coupling by (mu1, mu2, p)
+  using T = Tables<L, PS>;
+  struct Idx {
+    short v[T::NT];
+  };
+  static constexpr int key(int i) { return (T::by_out[i].mu1 * 16 + T::by_out[i].mu2) * 64 + T::by_out[i].p; }
+  static constexpr int pair(int i) { return T::by_out[i].mu1 * 16 + T::by_out[i].mu2; }
+  static constexpr Idx make() {
+    Idx a{};
+    int pos[16 * 16 * 64 + 1] = {};
+    for (int i = 0; i < T::NT; ++i) pos[key(i) + 1]++;
+    for (int k = 0; k < 16 * 16 * 64; ++k) pos[k + 1] += pos[k];
+    for (int i = 0; i < T::NT; ++i) a.v[pos[key(i)]++] = (short)i;
+    return a;
+  }
+  static constexpr Idx order = make();
+  static constexpr const eqtp_gen::CgTerm& term(int j) { return T::by_out[order.v[j]]; }
+  static constexpr bool run_first(int j) { return j == 0 || key(order.v[j - 1]) != key(order.v[j]); }
+  static constexpr bool run_last(int j) { return j + 1 == T::NT || key(order.v[j + 1]) != key(order.v[j]); }
+  static constexpr bool pair_first(int j) { return j == 0 || pair(order.v[j - 1]) != pair(order.v[j]); }
+  static constexpr bool pair_last(int j) { return j + 1 == T::NT || pair(order.v[j + 1]) != pair(order.v[j]); }
+  // the run that ends at j is the first run of its (mu1, mu2) pair
+  static constexpr bool run_opens_pair(int j) {
+    while (j > 0 && key(order.v[j - 1]) == key(order.v[j])) --j;
+    return pair_first(j);
+  }
+};
+
+constexpr int kGvBS = 16 * 16 + 4;  // B row per channel (floats): 16-byte rows, stride 4 (mod 64) banks
+
+// slot of row m1 in a channel's B block: rows 4kq + r are rotated by kq within
+// their group of four so that the 16-edge steps' reads (fixed r, kq = 0..3)
+// hit four different 16-bank groups
+__device__ __forceinline__ int gv_slot(int m1) { return (m1 & ~3) | (((m1 & 3) + (m1 >> 2)) & 3); }
+
+template <int L, int PS, int C>
+__global__ __launch_bounds__(64) void gvec_node_kernel(int N, int E, const int* __restrict__ row_ptr,
+                                                       const float* __restrict__ vec, const int* __restrict__ src,
+                                                       const float* __restrict__ x, const float* __restrict__ w,
+                                                       const float* __restrict__ gout, float* __restrict__ gvec) {
+  using T = Tables<L, PS>;
+  using O = TermOrderB<L, PS>;
+  constexpr int K = num_comp(L);
+  constexpr int CW = C >= 16 ? 16 : C;  // channels per block
+  constexpr int NBLK = C / CW;
+  __shared__ __attribute__((aligned(16))) float Bl[16 * kGvBS];  // B of one block; then dL/dY [64][17]
+  __shared__ int sstg[64];
+  const int lane = threadIdx.x & 63;
+  const int i16 = lane & 15;
+  const int kq = lane >> 4;
+  for (int row = blockIdx.x; row < N; row += gridDim.x) {
+    int e_beg = 0, e_end = 0;
+    if (E > 0) {
+      e_beg = min(max(row_ptr[row], 0), E);
+      e_end = min(max(row_ptr[row + 1], e_beg), E);
+    }
+    for (int cb = e_beg; cb < e_end; cb += 64) {
+      const int cnt = min(64, e_end - cb);
+      // stage the chunk: lane i = edge cb + i
+      const bool mine = lane < cnt;
+      const int em = mine ? cb + lane : cb;
+      const float vx = vec[3 * em], vy = vec[3 * em + 1], vz = vec[3 * em + 2];
+      sstg[lane] = mine ? clamp_index(src[em], N) : -1;
+      f4 acc[4];
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) acc[s4] = f4{0.f, 0.f, 0.f, 0.f};
+      for (int blk = 0; blk < NBLK; ++blk) {
+        wave_lds_sync();  // previous block's reads of Bl are done
+        // 1. B_d for this block's channels (all 16 rows zeroed first: rows of
+        //    channels past C stay zero, so the padded MFMA columns add nothing)
+        float* brow = Bl + i16 * kGvBS;
+        if (lane < 16) {
+#pragma unroll
+          for (int q = 0; q < 64; ++q) reinterpret_cast<f4*>(brow)[q] = f4{0.f, 0.f, 0.f, 0.f};
+        }
+        if (lane < CW) {
+          const int c = blk * CW + lane;
+          float gv[16];
+#pragma unroll
+          for (int k = 0; k < 16; ++k) gv[k] = k < K ? gout[((size_t)row * C + c) * K + k] : 0.0f;
+          float wr[T::P];
+#pragma unroll
+          for (int p = 0; p < T::P; ++p) wr[p] = w[p * C + c];
+          float t = 0.0f, b = 0.0f;
+          static_for<0, T::NT>([&](auto jj) {
+            constexpr int j = decltype(jj)::value;
+            constexpr eqtp_gen::CgTerm tm = O::term(j);
+            t = O::run_first(j) ? tm.c * gv[tm.mu3] : fmaf(tm.c, gv[tm.mu3], t);
+            if constexpr (O::run_last(j)) b = O::run_opens_pair(j) ? wr[tm.p] * t : fmaf(wr[tm.p], t, b);
+            if constexpr (O::pair_last(j)) brow[gv_slot(tm.mu1) * 16 + tm.mu2] = b;
+          });
+        }
+        wave_lds_sync();
+        // 2. dL/dY for the chunk's 16-edge steps
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) {
+          if (16 * s4 < cnt) {  // wave-uniform
+            const int sv = sstg[16 * s4 + i16];
+            const bool ok = sv >= 0;
+            f4 xv[16];
+#pragma unroll
+            for (int c = 0; c < 16; ++c) {
+              const bool cok = ok && c < CW;
+              const size_t o = ((size_t)(cok ? sv : 0) * C + blk * CW + (c < CW ? c : 0)) * K;
+              if constexpr (K == 16) {
+                xv[c] = cok ? *reinterpret_cast<const f4*>(x + o + 4 * kq) : f4{0.f, 0.f, 0.f, 0.f};
+              } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) xv[c][r] = (cok && 4 * kq + r < K) ? x[o + 4 * kq + r] : 0.0f;
+              }
+            }
+#pragma unroll
+            for (int c = 0; c < 16; ++c)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const float bv = Bl[c * kGvBS + gv_slot(4 * kq + r) * 16 + i16];
+                acc[s4] = __builtin_amdgcn_mfma_f32_16x16x4f32(xv[c][r], bv, acc[s4], 0, 0, 0);
+              }
+          }
+        }
+      }
+      // 3. dL/dY -> LDS [edge][17]; lane i applies the Jacobian of edge cb + i
+      wave_lds_sync();
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) Bl[(16 * s4 + 4 * kq + v) * 17 + i16] = acc[s4][v];
+      wave_lds_sync();
+      if (mine) {
+        float Y2[16], Gm[16][3];
+        sh_grad_eval<L>(vx, vy, vz, Y2, Gm);
+        float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f;
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+          const float d = Bl[lane * 17 + k];
+          a0 = fmaf(d, Gm[k][0], a0);
+          a1 = fmaf(d, Gm[k][1], a1);
+          a2 = fmaf(d, Gm[k][2], a2);
+        }
+        gvec[3 * (size_t)em] = a0;
+        gvec[3 * (size_t)em + 1] = a1;
+        gvec[3 * (size_t)em + 2] = a2;
+      }
+    }
+  }
+}
+
 template <int L, int PS, int C>
 static hipError_t launch_bwd_t(const BwdArgs& a) {
   using Cfg = BwdCfg<C>;
@@ -361,8 +526,19 @@ static hipError_t launch_bwd_t(const BwdArgs& a) {
     else go(conv_bwd_kernel<L, PS, C, false, 1>);
   }
   if (a.gvec != nullptr) {
-    if (sorted) go(conv_bwd_kernel<L, PS, C, true, 2>);
-    else go(conv_bwd_kernel<L, PS, C, false, 2>);
+    if (sorted && a.algo != 2) {  // matrix cores unless the vector-ALU walk is asked for
+      int dev = 0, cus = 256;
+      if (hipGetDevice(&dev) != hipSuccess ||
+          hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        cus = 256;
+      const int64_t g = (int64_t)cus * 8;
+      hipLaunchKernelGGL((gvec_node_kernel<L, PS, C>), dim3((unsigned)(a.N < g ? a.N : g)), dim3(64), 0, a.stream,
+                         (int)a.N, (int)a.E, a.row_ptr, a.vec, a.src, a.x, a.w, a.gout, a.gvec);
+    } else if (sorted) {
+      go(conv_bwd_kernel<L, PS, C, true, 2>);
+    } else {
+      go(conv_bwd_kernel<L, PS, C, false, 2>);
+    }
   }
   return hipGetLastError();
 }

@@ -47,6 +47,7 @@ struct BwdArgs {
   float* gx;    // or nullptr
   float* gw;    // or nullptr
   float* gvec;  // or nullptr
+  int algo = 0;  // grad_vec of sorted edges: 2 = vector-ALU walk, else matrix cores
   hipStream_t stream;
 };
 

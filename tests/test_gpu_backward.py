@@ -254,3 +254,32 @@ def test_autograd_modes(mode, csr):
     _assert_close(_np(x.grad), ref[0], TOL, "autograd %s grad_x" % mode)
     _assert_close(_np(w.grad), ref[1], TOL, "autograd %s grad_w" % mode)
     _assert_close(_np(vec.grad), ref[2], TOL, "autograd %s grad_vec" % mode)
+
+
+@pytest.mark.parametrize("lmax,ps,C", [(3, 0, 64), (3, 1, 128), (2, 0, 16), (1, 1, 8), (0, 0, 32), (3, 0, 8)])
+def test_grad_vec_both_walks(lmax, ps, C):
+    """grad_vec of dst-sorted edges: the matrix-core kernel (default) and the
+    vector-ALU walk (algo = EDGE_VALU), both against the oracle; rows longer
+    than 64 edges (several chunks) and empty rows included."""
+    eq = _eq()
+    wl = synth.small_graph(31, 12, C, lmax, 610 + lmax + C + ps, path_set=ps, empty_rows=(1, 2), long_rows=(7, 8),
+                           long_len=150, zero_vec_edges=2)
+    gout = _gout(wl, 33)
+    ref = oracle.conv_backward(wl.N, wl.vec, wl.src, wl.dst, wl.x, wl.w, gout, lmax, ps)[2]
+    for algo in (0, 2):
+        _say("grad_vec walk algo=%d lmax=%d ps=%d C=%d" % (algo, lmax, ps, C))
+        _, _, gv = eq.eqtp_conv_backward(_t(wl.vec), _t(wl.src), _t(wl.x), _t(wl.w), _t(gout), lmax,
+                                         row_ptr=_t(wl.row_ptr), path_set=ps, need_x=False, need_w=False,
+                                         algo=algo)
+        _assert_close(_np(gv), ref, TOL, "grad_vec algo %d" % algo)
+
+
+def test_grad_vec_mid_workload():
+    eq = _eq()
+    wl = synth.make_config("mid")
+    gout = _gout(wl, 34)
+    _say("grad_vec mid E=%d" % wl.src.shape[0])
+    ref = oracle.conv_backward(wl.N, wl.vec, wl.src, wl.dst, wl.x, wl.w, gout, 3)[2]
+    _, _, gv = eq.eqtp_conv_backward(_t(wl.vec), _t(wl.src), _t(wl.x), _t(wl.w), _t(gout), 3,
+                                     row_ptr=_t(wl.row_ptr), need_x=False, need_w=False)
+    _assert_close(_np(gv), ref, TOL, "grad_vec mid")
