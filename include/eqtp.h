@@ -272,7 +272,9 @@ int eqtp_sort_edges(int64_t N, int64_t E, const int32_t* dst, const float* vec, 
  *   dtype EQTP_F32: fp32 matrix-core products; EQTP_BF16: h and W are
  *   rounded to bfloat16 (nearest even) on load and the products are
  *   accumulated in fp32 on the bf16 matrix cores.
- *   C in {8, 16, 32, 64, 128}, lmax in [0, 3], 0 <= N < 2^31.
+ *   C in {8, 16, 32, 64, 128}, lmax in [0, 6], 0 <= N < 2^31 (lmax 4..6: a
+ *   4-node tile, 2 at C = 128, with the (node, m) pairs of one degree as
+ *   matrix-core columns).
  */
 int eqtp_linear(int64_t N, int C, int lmax, int dtype, const float* h, const float* W, float* out, void* stream);
 

@@ -307,7 +307,7 @@ int eqtp_sort_edges(int64_t N, int64_t E, const int32_t* dst, const float* vec, 
 
 int eqtp_linear(int64_t N, int C, int lmax, int dtype, const float* h, const float* W, float* out, void* stream) {
   if (lmax < 0 || C <= 0 || N < 0 || N > kMaxIndex) return EQTP_EINVAL;
-  if (lmax > 3 || !valid_c(C)) return EQTP_EUNSUPPORTED;
+  if (lmax > eqtp::kSo2MaxL || !valid_c(C)) return EQTP_EUNSUPPORTED;
   if (dtype != EQTP_F32 && dtype != EQTP_BF16) return EQTP_EINVAL;
   if (N == 0) return EQTP_OK;
   if (!h || !W || !out || !aligned16(h) || !aligned16(W) || !aligned16(out)) return EQTP_EINVAL;

@@ -264,10 +264,145 @@ __global__ __launch_bounds__(256) void linear_kernel(int N, const float* __restr
   }
 }
 
+// ---------------------------------------------------------------------------
+// lmax 4..6: a workgroup takes TN = 4 nodes (their K planes would not fit in
+// LDS with 16 nodes).  MFMA columns are the (node, m) pairs of one degree l
+// (TN (2l+1) of them, in tiles of 16), rows are 16 output channels, k runs
+// over the input channels, so each tile uses the single weight matrix W[l].
+// The h tile is staged transposed to rows (node, m) of C channels (operand
+// type), the results go through LDS to the global layout and leave with
+// coalesced stores.
+// ---------------------------------------------------------------------------
+template <int L, int C, bool BF16>
+struct LinColsCfg {
+  using Op = LinOp<BF16>;
+  typedef typename Op::T T;
+  static constexpr int K = num_comp(L);
+  static constexpr int TN = C >= 128 ? 2 : 4;   // nodes per workgroup
+  static constexpr int RS = C + Op::PAD;        // h row stride (elements): 16-byte rows
+  static constexpr int H_BYTES = (TN * K * RS * (int)sizeof(T) + 15) / 16 * 16;
+  static constexpr int O_BYTES = TN * C * K * 4;
+  static constexpr int LDS_BYTES = H_BYTES + O_BYTES;  // input and output tiles side by side
+  static constexpr int OT = (C + 15) / 16;      // output channel tiles
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+};
+
+template <int L, int C, bool BF16>
+__global__ __launch_bounds__(256) void linear_cols_kernel(int N, const float* __restrict__ h,
+                                                          const float* __restrict__ W, float* __restrict__ out) {
+  using Cfg = LinColsCfg<L, C, BF16>;
+  typedef typename Cfg::T T;
+  constexpr int K = Cfg::K;
+  constexpr int TN = Cfg::TN;
+  constexpr int RS = Cfg::RS;
+  __shared__ __attribute__((aligned(16))) unsigned char lds_raw[Cfg::LDS_BYTES];
+  T* hT = reinterpret_cast<T*>(lds_raw);                              // [(node, m)][RS]
+  float* otile = reinterpret_cast<float*>(lds_raw + Cfg::H_BYTES);    // [node][C][K]
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
+  const int i16 = lane & 15;
+  const int kq = lane >> 4;
+  const int n0 = blockIdx.x * TN;
+  const int nv = min(TN, N - n0);
+  const size_t base = (size_t)n0 * C * K;
+
+  // 1. stage h: element (node, c, m) -> row node*K + m, column c
+  for (int f = tid; f < TN * C * K; f += 256) {
+    const int node = f / (C * K);
+    const int rem = f - node * (C * K);
+    const int c = rem / K;
+    const int m = rem - c * K;
+    hT[(node * K + m) * RS + c] = to_op<T>(node < nv ? h[base + f] : 0.0f);
+  }
+  __syncthreads();
+
+  // 2. units (l, column tile, output tile), dealt round-robin to the waves;
+  //    lane (column i16, group kq) ends with D[co = 16 ot + 4 kq + v][column]
+  int unit = 0;
+  for (int l = 0; l <= L; ++l) {
+    const int width = 2 * l + 1;
+    const int ncol = TN * width;
+    const int ctn = (ncol + 15) / 16;
+    for (int ct = 0; ct < ctn; ++ct) {
+      for (int ot = 0; ot < Cfg::OT; ++ot, ++unit) {
+        if ((unit & 3) != wv) continue;
+        const int n = ct * 16 + i16;  // B column supplied by this lane
+        const bool n_ok = n < ncol;
+        const int node = n_ok ? n / width : 0;
+        const int m = l * l + (n_ok ? n - node * width : 0);
+        const T* hrow = hT + (node * K + m) * RS;
+        const int co = ot * 16 + i16;  // A row supplied by this lane
+        const bool co_ok = co < C;
+        f4 acc = f4{0.f, 0.f, 0.f, 0.f};
+        if constexpr (BF16) {
+#pragma unroll
+          for (int ci0 = 0; ci0 < C; ci0 += 32) {
+            const int cb = ci0 + 8 * kq;
+            bf16x8 a8, b8;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              a8[j] = (__bf16)0.0f;
+              b8[j] = (__bf16)0.0f;
+            }
+            if (cb < C) {
+              if (n_ok) b8 = *reinterpret_cast<const bf16x8*>(hrow + cb);
+              if (co_ok) {
+                const float* wr = W + ((size_t)l * C + co) * C + cb;
+                const f4 w0 = *reinterpret_cast<const f4*>(wr), w1 = *reinterpret_cast<const f4*>(wr + 4);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                  a8[j] = to_bf16(w0[j]);
+                  a8[4 + j] = to_bf16(w1[j]);
+                }
+              }
+            }
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a8, b8, acc, 0, 0, 0);
+          }
+        } else {
+#pragma unroll
+          for (int ci0 = 0; ci0 < C; ci0 += 16) {
+            const int cb = ci0 + 4 * kq;
+            f4 a4 = f4{0.f, 0.f, 0.f, 0.f}, b4 = a4;
+            if (cb < C) {
+              if (n_ok) b4 = *reinterpret_cast<const f4*>(hrow + cb);
+              if (co_ok) a4 = *reinterpret_cast<const f4*>(W + ((size_t)l * C + co) * C + cb);
+            }
+#pragma unroll
+            for (int s4 = 0; s4 < 4; ++s4) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[s4], b4[s4], acc, 0, 0, 0);
+          }
+        }
+        if (n_ok) {
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int c2 = ot * 16 + 4 * kq + v;
+            if (c2 < C) otile[(node * C + c2) * K + m] = acc[v];
+          }
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  // 3. coalesced stores of the valid nodes
+  constexpr int CK = C * K;
+  if constexpr (CK % 4 == 0) {
+    f4* ob = reinterpret_cast<f4*>(out + base);
+    for (int i = tid; i < nv * CK / 4; i += 256) ob[i] = *reinterpret_cast<const f4*>(otile + 4 * i);
+  } else {
+    for (int i = tid; i < nv * CK; i += 256) out[base + i] = otile[i];
+  }
+}
+
 template <int L, int C, bool BF16>
 static hipError_t launch_linear_t(int64_t N, const float* h, const float* W, float* out, hipStream_t stream) {
-  const unsigned blocks = (unsigned)((N + 15) / 16);
-  hipLaunchKernelGGL((linear_kernel<L, C, BF16>), dim3(blocks), dim3(256), 0, stream, (int)N, h, W, out);
+  if constexpr (L <= 3) {
+    const unsigned blocks = (unsigned)((N + 15) / 16);
+    hipLaunchKernelGGL((linear_kernel<L, C, BF16>), dim3(blocks), dim3(256), 0, stream, (int)N, h, W, out);
+  } else {
+    const unsigned blocks = (unsigned)((N + LinColsCfg<L, C, BF16>::TN - 1) / LinColsCfg<L, C, BF16>::TN);
+    hipLaunchKernelGGL((linear_cols_kernel<L, C, BF16>), dim3(blocks), dim3(256), 0, stream, (int)N, h, W, out);
+  }
   return hipGetLastError();
 }
 
@@ -295,6 +430,12 @@ hipError_t launch_linear(int64_t N, int C, int lmax, int bf16, const float* h, c
     case 5: return dispatch_linear_c<2, true>(N, C, h, W, out, stream);
     case 6: return dispatch_linear_c<3, false>(N, C, h, W, out, stream);
     case 7: return dispatch_linear_c<3, true>(N, C, h, W, out, stream);
+    case 8: return dispatch_linear_c<4, false>(N, C, h, W, out, stream);
+    case 9: return dispatch_linear_c<4, true>(N, C, h, W, out, stream);
+    case 10: return dispatch_linear_c<5, false>(N, C, h, W, out, stream);
+    case 11: return dispatch_linear_c<5, true>(N, C, h, W, out, stream);
+    case 12: return dispatch_linear_c<6, false>(N, C, h, W, out, stream);
+    case 13: return dispatch_linear_c<6, true>(N, C, h, W, out, stream);
     default: return hipErrorInvalidValue;
   }
 }

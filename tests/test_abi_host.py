@@ -119,6 +119,7 @@ def test_sh_and_linear_validation():
     assert lib.eqtp_linear(10, 48, 3, 0, FAKE, FAKE, FAKE, NULL) == 2
     assert lib.eqtp_linear(10, 64, 3, 0, NULL, FAKE, FAKE, NULL) == 1
     assert lib.eqtp_linear(0, 64, 3, 0, NULL, NULL, NULL, NULL) == 0
+    assert lib.eqtp_linear(10, 64, 7, 0, FAKE, FAKE, FAKE, NULL) == 2
     assert lib.eqtp_test_segment_probe(FAKE, FAKE, 10, 20, 64, 3, 0, FAKE, FAKE, NULL) == 1
 
 

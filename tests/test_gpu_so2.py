@@ -144,3 +144,21 @@ def test_sh_high_degree(L, E):
     assert np.abs(got - ref).max() <= 2e-5 * max(1.0, np.abs(ref).max())
     if E >= 1:
         assert got[0, 0] == np.float32(0.28209479177387814) and np.all(got[0, 1:] == 0.0)
+
+
+@pytest.mark.parametrize("L", [4, 5, 6])
+@pytest.mark.parametrize("C", [8, 16, 32, 64, 128])
+def test_linear_high_degree(L, C):
+    """The per-l channel linear at lmax 4..6 (column-tiled kernel), fp32 and
+    bf16 operands, node counts that are not multiples of the tile."""
+    eq = _eq()
+    rng = np.random.default_rng(C * 11 + L)
+    N = 37
+    K = (L + 1) ** 2
+    h = rng.standard_normal((N, C, K)).astype(np.float32)
+    W = (rng.standard_normal((L + 1, C, C)) / np.sqrt(C)).astype(np.float32)
+    _say("linear fp32 L=%d C=%d" % (L, C))
+    _assert_close(_np(eq.eqtp_linear(_t(h), _t(W), L, eq.EQTP_F32)), oracle.linear(h, W, L), TOL, "linear fp32")
+    _say("linear bf16 L=%d C=%d" % (L, C))
+    outb = _np(eq.eqtp_linear(_t(h), _t(W), L, eq.EQTP_BF16))
+    _assert_close(outb, oracle.linear(h, W, L, bf16=True), 2e-5, "linear bf16 vs rounded inputs")
