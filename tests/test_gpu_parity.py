@@ -335,6 +335,23 @@ def test_linear(C, L):
     _assert_close(outb, oracle.linear(h, W, L), tol=1e-2, what="linear bf16 vs fp64")
 
 
+@pytest.mark.parametrize("C,L", [(32, 3), (64, 3), (64, 1), (128, 3)])
+def test_linear_many_tiles(C, L):
+    """Enough nodes that every persistent workgroup walks several 16-node tiles (prefetching the
+    next one), with a ragged last tile."""
+    eq = _eq()
+    rng = np.random.default_rng(1000 + C + L)
+    N = 40009 if C <= 64 else 5009  # C = 128 takes one tile per workgroup
+    K = (L + 1) ** 2
+    h = rng.standard_normal((N, C, K)).astype(np.float32)
+    W = (rng.standard_normal((L + 1, C, C)) / np.sqrt(C)).astype(np.float32)
+    for dt, name in ((eq.EQTP_F32, "fp32"), (eq.EQTP_BF16, "bf16")):
+        _say("linear many tiles %s C=%d L=%d N=%d" % (name, C, L, N))
+        out = _np(eq.eqtp_linear(_t(h), _t(W), L, dt))
+        ref = oracle.linear(h, W, L, bf16=(dt == eq.EQTP_BF16))
+        _assert_close(out, ref, tol=2e-4 if dt == eq.EQTP_F32 else 2e-5, what="linear %s many tiles" % name)
+
+
 def test_linear_identity_exact():
     eq = _eq()
     rng = np.random.default_rng(3)
