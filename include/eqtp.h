@@ -61,8 +61,10 @@ extern "C" {
 #define EQTP_EDGES_UNSORTED 1   /* any order; dst[E] given; results summed with atomics */
 
 /* algorithm of eqtp_conv_fused.  AUTO: NODE_MFMA for dst-sorted edges with
-   fixed weights and lmax <= 3, EDGE_VALU for other lmax <= 3 cases, EDGE_SO2
-   for lmax 4..6. */
+   fixed weights and lmax <= 3; EDGE_SO2 for dst-sorted edges with radial
+   weights, fp32 features, lmax <= 3 and C a multiple of 16 (the radial
+   products 8 -> P*C on the matrix cores, 16 edges at a time); EDGE_VALU for
+   other lmax <= 3 cases; EDGE_SO2 for lmax 4..6. */
 #define EQTP_ALGO_AUTO 0
 #define EQTP_ALGO_NODE_MFMA 1 /* per node: outer-product sums on matrix cores, then the coupling */
 #define EQTP_ALGO_EDGE_VALU 2 /* per edge: harmonics, coupling and product on the vector ALUs */
@@ -154,6 +156,8 @@ typedef struct eqtp_conv_desc {
  * edges: summation order varies from run to run.
  * lmax 4..6 (EQTP_ALGO_EDGE_SO2): fixed weights and fp32 features only
  * (EQTP_EUNSUPPORTED otherwise), C = 128 up to lmax 4; both edge orders.
+ * EQTP_ALGO_EDGE_SO2 with radial weights: dst-sorted edges, fp32 features,
+ * lmax <= 3 and C a multiple of 16 only.
  */
 int eqtp_conv_fused(const eqtp_conv_desc* d, int64_t N, int64_t E, const float* vec, const int32_t* src,
                     const int32_t* dst, const int32_t* row_ptr, const void* x, const float* weights, float* out,

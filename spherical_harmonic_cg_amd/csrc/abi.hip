@@ -101,8 +101,14 @@ int eqtp_conv_fused(const eqtp_conv_desc* d, int64_t N, int64_t E, const float* 
     return EQTP_EINVAL;
   if (d->C <= 0) return EQTP_EINVAL;
   if (!valid_c(d->C)) return EQTP_EUNSUPPORTED;
+  // radial weights on dst-sorted edges (lmax <= 3, C a multiple of 16): the edge-aligned form with the
+  // per-edge weights on the matrix cores, unless the per-edge walk (EQTP_ALGO_EDGE_VALU) is asked for
+  const bool radial_so2_ok = d->weight_mode == EQTP_W_RADIAL && d->edge_order == EQTP_EDGES_DST_SORTED &&
+                             d->lmax >= 0 && d->lmax <= 3 && d->C % 16 == 0 && x_dtype == EQTP_F32;
+  const bool use_radial_so2 = radial_so2_ok && (d->algo == EQTP_ALGO_AUTO || d->algo == EQTP_ALGO_EDGE_SO2);
   // lmax above 3 exists only in the edge-aligned form
-  const bool use_so2 = d->algo == EQTP_ALGO_EDGE_SO2 || (d->algo == EQTP_ALGO_AUTO && d->lmax > 3);
+  const bool use_so2 =
+      !use_radial_so2 && (d->algo == EQTP_ALGO_EDGE_SO2 || (d->algo == EQTP_ALGO_AUTO && d->lmax > 3));
   if (d->lmax > 3 && !use_so2) return EQTP_EUNSUPPORTED;
   if (use_so2 && (d->weight_mode != EQTP_W_FIXED || x_dtype != EQTP_F32)) return EQTP_EUNSUPPORTED;
   if (use_so2 && d->C == 128 && d->lmax > eqtp::kSo2MaxLC128) return EQTP_EUNSUPPORTED;
@@ -144,6 +150,7 @@ int eqtp_conv_fused(const eqtp_conv_desc* d, int64_t N, int64_t E, const float* 
   a.w = weights;
   a.out = out;
   a.stream = (hipStream_t)stream;
+  if (use_radial_so2) return status_of(eqtp::launch_conv_so2_radial(a));
   if (use_so2) return status_of(eqtp::launch_conv_so2(a));
   const bool use_node = node_ok && d->algo != EQTP_ALGO_EDGE_VALU;
   return status_of(use_node ? eqtp::launch_conv_node(a) : eqtp::launch_conv_edge(a));

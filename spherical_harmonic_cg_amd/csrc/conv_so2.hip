@@ -29,6 +29,8 @@
 // unsorted edges: contiguous edge runs per wave, messages added with fp32
 // atomics after an LDS exchange (256 contiguous bytes per instruction).
 // The path weights are staged once per workgroup in LDS ([P][C]).
+#include <type_traits>
+
 #include "eqtp_device.hpp"
 #include "eqtp_kernels.hpp"
 #include "generated/so2_tables.inc"
@@ -112,6 +114,85 @@ __device__ __forceinline__ void angle_powers(float c1, float s1, float (&cm)[L +
   for (int m = 1; m <= L; ++m) {
     cm[m] = fmaf(cm[m - 1], c1, -sm[m - 1] * s1);
     sm[m] = fmaf(sm[m - 1], c1, cm[m - 1] * s1);
+  }
+}
+
+// The edge frame of one edge vector: cos/sin of m phi and m theta for the
+// pair rotations (identity for a zero vector or along the z axis, where phi is
+// free), and keep = 0 for a zero vector (paths with l2 > 0 vanish there).
+template <int L>
+struct So2Frame {
+  float cp[L + 1], sp[L + 1], ct[L + 1], st[L + 1];
+  float keep;
+  __device__ __forceinline__ So2Frame(float vx, float vy, float vz) {
+    const float r2 = vx * vx + vy * vy + vz * vz;
+    const bool nz = r2 > 0.0f;
+    const float inv_r = nz ? rsqrtf(r2) : 0.0f;
+    const float ux = vx * inv_r, uy = vy * inv_r, uz = nz ? vz * inv_r : 1.0f;
+    const float rho2 = ux * ux + uy * uy;
+    const bool tilt = rho2 > 0.0f;
+    const float inv_rho = tilt ? rsqrtf(rho2) : 0.0f;
+    angle_powers<L>(tilt ? ux * inv_rho : 1.0f, tilt ? uy * inv_rho : 0.0f, cp, sp);
+    angle_powers<L>(uz, tilt ? rho2 * inv_rho : 0.0f, ct, st);
+    keep = nz ? 1.0f : 0.0f;
+  }
+};
+
+// acc += D(R_e)^T P_w(D(R_e) v) for one channel (the radial kernel below; the
+// fixed-weight kernels keep the same steps inline in So2Msg): v (the source features, K
+// components) is rotated into the edge frame in place, coupled through the
+// sparse table with path weight wfn(p) (dropped for l2 > 0 when the vector is
+// zero), and the result rotated back and added into acc.
+template <int L, int PS, int K, class WFn>
+__device__ __forceinline__ void so2_message(float (&v)[K], const So2Frame<L>& f, WFn&& wfn, float (&acc)[K]) {
+  using T = So2Tables<L, PS>;
+  // into the edge frame: J^T Z(-theta) J Z(-phi)
+  apply_z<L>(v, f.cp, f.sp, -1.0f);
+  apply_j<K, false>(v);
+  apply_z<L>(v, f.ct, f.st, -1.0f);
+  apply_j<K, true>(v);
+  // sparse coupling, one weight per path, one run per (path, output)
+  float m[K];
+#pragma unroll
+  for (int k = 0; k < K; ++k) m[k] = 0.0f;
+  float wp = 0.0f, t = 0.0f;
+  static_for<0, T::NT>([&](auto ii) {
+    constexpr int i = decltype(ii)::value;
+    constexpr eqtp_gen::So2Term tm = T::terms[i];
+    constexpr bool p_first = i == 0 || T::terms[i - 1].p != tm.p;
+    constexpr bool run_first = p_first || T::terms[i - 1].mu3 != tm.mu3;
+    constexpr bool run_last = i + 1 == T::NT || T::terms[i + 1].p != tm.p || T::terms[i + 1].mu3 != tm.mu3;
+    if constexpr (p_first) {
+      wp = wfn(std::integral_constant<int, tm.p>{});
+      if constexpr (tm.l2 > 0) wp *= f.keep;
+    }
+    t = run_first ? tm.c * v[tm.mu1] : fmaf(tm.c, v[tm.mu1], t);
+    if constexpr (run_last) m[tm.mu3] = fmaf(wp, t, m[tm.mu3]);
+  });
+  // back to the global frame: Z(phi) J^T Z(theta) J, added into acc
+  apply_j<K, false>(m);
+  apply_z<L>(m, f.ct, f.st, 1.0f);
+  apply_j<K, true>(m);
+  apply_z<L>(m, f.cp, f.sp, 1.0f);
+#pragma unroll
+  for (int k = 0; k < K; ++k) acc[k] += m[k];
+}
+
+// K consecutive features from xp (16-byte aligned when K % 4 == 0)
+template <int K>
+__device__ __forceinline__ void load_feat(const float* __restrict__ xp, float (&v)[K]) {
+  if constexpr (K % 4 == 0) {
+#pragma unroll
+    for (int q = 0; q < K / 4; ++q) {
+      const f4 t4 = reinterpret_cast<const f4*>(xp)[q];
+      v[4 * q] = t4[0];
+      v[4 * q + 1] = t4[1];
+      v[4 * q + 2] = t4[2];
+      v[4 * q + 3] = t4[3];
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < K; ++k) v[k] = xp[k];
   }
 }
 
@@ -358,6 +439,139 @@ __global__ __launch_bounds__(So2Cfg<C>::THREADS) void conv_so2_msg_kernel(int N,
         for (int k = 0; k < K; ++k) op[k] = acc[j][k];
       }
     }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Radial weights, dst-sorted edges, lmax <= 3, C a multiple of 16.
+// The path weights of an edge are w_e[p,c] = sum_b R_b(|vec_e|) W[b, p*C + c]
+// with the 8 radial functions R_b (eqtp_device.hpp).  For a batch of 16 edges
+// of one row and a block of 16 channels that is a [16 x 8] x [8 x 16] product
+// per path: two v_mfma_f32_16x16x4_f32 with A = R (rows = edges, shared by all
+// paths) and B = W (the workgroup's LDS copy of the block's columns), so W is
+// read once per 16 edges instead of once per edge.  The MFMA leaves w of
+// (edge 4k + i, channel j) in lane (j, k), which is how the rest of the batch
+// runs: lane (j, k) takes the batch's edges 4k .. 4k+3 for channel j through
+// the edge-aligned coupling (rotate in, sparse coupling with w, rotate back)
+// and sums the messages in registers; the four edge groups of a lane's
+// channel are combined with xor shuffles after the row (deterministic).
+// Work unit: one wave per (row, 16-channel block); a workgroup's 4 waves take
+// 4 consecutive rows of one block.
+// ---------------------------------------------------------------------------
+constexpr int kSo2RadialBasis = 8;
+
+template <int L, int PS, int C>
+__global__ __launch_bounds__(256) void conv_so2_radial_kernel(int N, int E, const int* __restrict__ row_ptr,
+                                                              const float* __restrict__ vec,
+                                                              const int* __restrict__ src,
+                                                              const float* __restrict__ x,
+                                                              const float* __restrict__ w, float* __restrict__ out,
+                                                              float inv_rc) {
+  using T = So2Tables<L, PS>;
+  constexpr int K = num_comp(L);
+  constexpr int P = T::P;
+  constexpr int NB = kSo2RadialBasis;
+  constexpr int NBLK = C / 16;
+  static_assert(C % 16 == 0 && L <= 3, "radial edge-aligned kernel: C multiple of 16, lmax <= 3");
+  __shared__ float wl[NB * P * 16];  // [b][p][channel of the block]
+  const int cb = (int)(blockIdx.x % NBLK) * 16;
+  for (int i = threadIdx.x; i < NB * P * 16; i += 256) {
+    const int bp = i >> 4;  // b * P + p
+    wl[i] = w[(size_t)bp * C + cb + (i & 15)];
+  }
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int row = (int)(blockIdx.x / NBLK) * 4 + (threadIdx.x >> 6);
+  if (row >= N) return;
+  const int j = lane & 15;   // channel cb + j; A row (edge e0 + j) for the radial product
+  const int kq = lane >> 4;  // edge group: edges 4 kq .. 4 kq + 3 of each batch; A/B k index
+  int e_beg = 0, e_end = 0;
+  if (E > 0) {
+    e_beg = min(max(row_ptr[row], 0), E);
+    e_end = min(max(row_ptr[row + 1], e_beg), E);
+  }
+  float acc[K];
+#pragma unroll
+  for (int k = 0; k < K; ++k) acc[k] = 0.0f;
+  for (int e0 = e_beg; e0 < e_end; e0 += 16) {
+    // A operand of lane (j, kq): R_{kq}, R_{4+kq} of edge e0 + j (zeros past the row)
+    float a0 = 0.0f, a1 = 0.0f;
+    const int ea = e0 + j;
+    if (ea < e_end) {
+      const float ax = vec[3 * ea], ay = vec[3 * ea + 1], az = vec[3 * ea + 2];
+      float R[NB];
+      radial_basis<NB>(sqrtf(ax * ax + ay * ay + az * az), inv_rc, R);
+      a0 = kq == 0 ? R[0] : (kq == 1 ? R[1] : (kq == 2 ? R[2] : R[3]));
+      a1 = kq == 0 ? R[4] : (kq == 1 ? R[5] : (kq == 2 ? R[6] : R[7]));
+    }
+    // w of edges e0 + 4 kq + i, channel cb + j: wp[p][i]
+    f4 wp[P];
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      wp[p] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, wl[(kq * P + p) * 16 + j], f4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+      wp[p] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, wl[((4 + kq) * P + p) * 16 + j], wp[p], 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = e0 + 4 * kq + i;
+      if (e < e_end) {
+        const So2Frame<L> f(vec[3 * e], vec[3 * e + 1], vec[3 * e + 2]);
+        const int s = clamp_index(src[e], N);
+        float v[K];
+        load_feat<K>(x + ((size_t)s * C + cb + j) * K, v);
+        so2_message<L, PS>(v, f, [&](auto p) { return wp[decltype(p)::value][i]; }, acc);
+      }
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    acc[k] += __shfl_xor(acc[k], 16);
+    acc[k] += __shfl_xor(acc[k], 32);
+  }
+  if (kq == 0) {
+    float* op = out + ((size_t)row * C + cb + j) * K;
+    if constexpr (K % 4 == 0) {
+#pragma unroll
+      for (int q = 0; q < K / 4; ++q)
+        reinterpret_cast<f4*>(op)[q] = f4{acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
+    } else {
+#pragma unroll
+      for (int k = 0; k < K; ++k) op[k] = acc[k];
+    }
+  }
+}
+
+template <int L, int PS, int C>
+static hipError_t launch_so2_radial_t(const ConvArgs& a) {
+  if (a.N == 0) return hipSuccess;
+  const long long blocks = (a.N + 3) / 4 * (C / 16);
+  hipLaunchKernelGGL((conv_so2_radial_kernel<L, PS, C>), dim3((unsigned)blocks), dim3(256), 0, a.stream, (int)a.N,
+                     (int)a.E, a.row_ptr, a.vec, a.src, (const float*)a.x, a.w, a.out, 1.0f / a.r_cut);
+  return hipGetLastError();
+}
+
+template <int L, int PS>
+static hipError_t dispatch_so2_radial_c(const ConvArgs& a) {
+  switch (a.C) {
+    case 16: return launch_so2_radial_t<L, PS, 16>(a);
+    case 32: return launch_so2_radial_t<L, PS, 32>(a);
+    case 64: return launch_so2_radial_t<L, PS, 64>(a);
+    case 128: return launch_so2_radial_t<L, PS, 128>(a);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_conv_so2_radial(const ConvArgs& a) {
+  switch (a.lmax * 2 + a.path_set) {
+    case 0: return dispatch_so2_radial_c<0, 0>(a);
+    case 1: return dispatch_so2_radial_c<0, 1>(a);
+    case 2: return dispatch_so2_radial_c<1, 0>(a);
+    case 3: return dispatch_so2_radial_c<1, 1>(a);
+    case 4: return dispatch_so2_radial_c<2, 0>(a);
+    case 5: return dispatch_so2_radial_c<2, 1>(a);
+    case 6: return dispatch_so2_radial_c<3, 0>(a);
+    case 7: return dispatch_so2_radial_c<3, 1>(a);
+    default: return hipErrorInvalidValue;
   }
 }
 

@@ -65,6 +65,8 @@ hipError_t launch_conv_backward(const BwdArgs& a);   // fixed weights, vector AL
 constexpr int kSo2MaxL = 6;
 constexpr int kSo2MaxLC128 = 4;
 hipError_t launch_conv_so2(const ConvArgs& a);
+// edge-aligned form with radial weights on dst-sorted edges: lmax 0..3, C = 16, 32, 64 or 128
+hipError_t launch_conv_so2_radial(const ConvArgs& a);
 // grad_x / grad_w on the matrix cores from edges grouped by source: row_ptr =
 // CSR over sources, vec / dst in that order (src unused)
 hipError_t launch_conv_backward_by_source(const BwdArgs& a);

@@ -72,7 +72,8 @@ NULL = ctypes.c_void_p(0)
 @pytest.mark.parametrize("kw,want", [
     (dict(lmax=7), 2), (dict(lmax=-1), 1), (dict(lmax=4, algo=1), 2), (dict(lmax=4, algo=2), 2),
     (dict(lmax=4, weight_mode=1, r_cut=5.0), 2), (dict(lmax=4, x_dtype=1), 2), (dict(lmax=5, C=128), 2),
-    (dict(lmax=6, C=128, algo=3), 2), (dict(algo=3, weight_mode=1, r_cut=5.0), 2), (dict(algo=3, x_dtype=1), 2), (dict(C=48), 2), (dict(C=0), 1), (dict(path_set=3), 1),
+    (dict(lmax=6, C=128, algo=3), 2), (dict(algo=3, weight_mode=1, r_cut=5.0, edge_order=1), 2), (dict(algo=3, weight_mode=1, r_cut=5.0, C=8), 2),
+    (dict(lmax=4, algo=3, weight_mode=1, r_cut=5.0), 2), (dict(algo=3, x_dtype=1), 2), (dict(C=48), 2), (dict(C=0), 1), (dict(path_set=3), 1),
     (dict(weight_mode=2), 1), (dict(edge_order=5), 1), (dict(algo=9), 1),
     (dict(weight_mode=1, r_cut=0.0), 1), (dict(weight_mode=1, r_cut=5.0, n_basis=6), 2),
     (dict(weight_mode=1, r_cut=5.0, algo=1), 2), (dict(edge_order=1, algo=1), 2),

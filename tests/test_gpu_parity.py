@@ -233,6 +233,54 @@ def test_conv_small_radial(C, L):
                   what="radial unsorted")
 
 
+RADIAL_CASES = [(C, L, ps) for C in (8, 16, 32, 64, 128) for L in (0, 1, 2, 3) for ps in (0, 1)]
+
+
+@pytest.mark.parametrize("C,L,ps", RADIAL_CASES)
+def test_conv_radial_all_variants(C, L, ps):
+    """Radial weights on dst-sorted edges for every channel count, degree and path set: the edge-aligned
+    kernel with the weights on the matrix cores (algo 0 and 3; C = 8 takes the per-edge walk) and the
+    per-edge walk (algo 2).  Rows of 0, 1, 16, 17 and 70 edges cover empty, full and ragged 16-edge
+    batches; zero vectors and edges beyond the cut-off are mixed in."""
+    eq = _eq()
+    wl = synth.small_graph(n=31, e_per_row=9, C=C, lmax=L, seed=300 + C + 10 * L + 100 * ps, path_set=ps,
+                           radial=True, r_cut=5.0, empty_rows=(0, 30), long_rows=(7,), long_len=70,
+                           zero_vec_edges=2)
+    wl.vec[12:16] *= 1.7  # beyond the cut-off: no contribution
+    g = _gpu_inputs(wl)
+    ref = oracle.conv(wl.N, wl.vec, wl.src, wl.dst, wl.x, wl.w_rad, L, path_set=ps, weight_mode=1, r_cut=5.0)
+    for algo in (0, 2, 3):
+        if algo == 3 and C % 16:
+            continue
+        _say("radial C=%d L=%d ps=%d algo=%d" % (C, L, ps, algo))
+        out = _np(_run_conv(eq, wl, g, algo))
+        _assert_close(out, ref, what="radial C%d L%d ps%d algo%d" % (C, L, ps, algo))
+        assert np.all(out[[0, 30]] == 0.0)
+
+
+def test_conv_radial_batch_edges():
+    """Rows of exactly 1, 15, 16, 17, 31, 32 and 33 edges: around the 16-edge batch of the radial
+    edge-aligned kernel."""
+    eq = _eq()
+    for n_e in (1, 15, 16, 17, 31, 32, 33):
+        wl = synth.small_graph(n=4, e_per_row=n_e, C=32, lmax=3, seed=900 + n_e, radial=True, r_cut=5.0,
+                               long_rows=(0, 1, 2, 3), long_len=n_e)
+        g = _gpu_inputs(wl)
+        ref = oracle.conv(wl.N, wl.vec, wl.src, wl.dst, wl.x, wl.w_rad, 3, weight_mode=1, r_cut=5.0)
+        _say("radial batch edges %d" % n_e)
+        _assert_close(_np(_run_conv(eq, wl, g, 0)), ref, what="radial %d edges per row" % n_e)
+
+
+def test_conv_radial_deterministic():
+    eq = _eq()
+    wl = synth.small_graph(n=40, e_per_row=23, C=64, lmax=3, seed=41, radial=True, r_cut=5.0)
+    g = _gpu_inputs(wl)
+    _say("radial determinism")
+    a = _np(_run_conv(eq, wl, g, 0))
+    b = _np(_run_conv(eq, wl, g, 0))
+    np.testing.assert_array_equal(a, b)
+
+
 def test_conv_long_rows_and_single_node():
     """Rows longer than 64 and 256 edges (several staging chunks), and N = 1."""
     eq = _eq()
