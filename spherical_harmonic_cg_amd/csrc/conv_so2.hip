@@ -449,12 +449,15 @@ __global__ __launch_bounds__(So2Cfg<C>::THREADS) void conv_so2_msg_kernel(int N,
 // of one row and a block of 16 channels that is a [16 x 8] x [8 x 16] product
 // per path: two v_mfma_f32_16x16x4_f32 with A = R (rows = edges, shared by all
 // paths) and B = W (the workgroup's LDS copy of the block's columns), so W is
-// read once per 16 edges instead of once per edge.  The MFMA leaves w of
-// (edge 4k + i, channel j) in lane (j, k), which is how the rest of the batch
-// runs: lane (j, k) takes the batch's edges 4k .. 4k+3 for channel j through
-// the edge-aligned coupling (rotate in, sparse coupling with w, rotate back)
-// and sums the messages in registers; the four edge groups of a lane's
-// channel are combined with xor shuffles after the row (deterministic).
+// read once per 16 edges instead of once per edge.  A's rows are the batch's
+// edges in the order k + 4i of row 4k + i, so the MFMA leaves w of
+// (edge k + 4i, channel j) in lane (j, k), which is how the rest of the batch
+// runs: lane (j, k) takes the batch's edges k, k+4, k+8, k+12 for channel j
+// through the edge-aligned coupling (rotate in, sparse coupling with w,
+// rotate back) and sums the messages in registers.  A row's last, partial
+// batch of n edges then stops after ceil(n/4) of the 4 slots.  The four edge
+// groups of a lane's channel are combined with xor shuffles after the row
+// (deterministic).
 // Work unit: one wave per (row, 16-channel block); a workgroup's 4 waves take
 // 4 consecutive rows of one block.
 // ---------------------------------------------------------------------------
@@ -484,7 +487,7 @@ __global__ __launch_bounds__(256) void conv_so2_radial_kernel(int N, int E, cons
   const int row = (int)(blockIdx.x / NBLK) * 4 + (threadIdx.x >> 6);
   if (row >= N) return;
   const int j = lane & 15;   // channel cb + j; A row (edge e0 + j) for the radial product
-  const int kq = lane >> 4;  // edge group: edges 4 kq .. 4 kq + 3 of each batch; A/B k index
+  const int kq = lane >> 4;  // edge group: edges kq + 4 i of each batch; A/B k index
   int e_beg = 0, e_end = 0;
   if (E > 0) {
     e_beg = min(max(row_ptr[row], 0), E);
@@ -494,9 +497,10 @@ __global__ __launch_bounds__(256) void conv_so2_radial_kernel(int N, int E, cons
 #pragma unroll
   for (int k = 0; k < K; ++k) acc[k] = 0.0f;
   for (int e0 = e_beg; e0 < e_end; e0 += 16) {
-    // A operand of lane (j, kq): R_{kq}, R_{4+kq} of edge e0 + j (zeros past the row)
+    // A operand of lane (j, kq): R_{kq}, R_{4+kq} of the edge of A row j, e0 + (j >> 2) + 4 (j & 3)
+    // (zeros past the row)
     float a0 = 0.0f, a1 = 0.0f;
-    const int ea = e0 + j;
+    const int ea = e0 + ((j >> 2) | ((j & 3) << 2));
     if (ea < e_end) {
       const float ax = vec[3 * ea], ay = vec[3 * ea + 1], az = vec[3 * ea + 2];
       float R[NB];
@@ -504,7 +508,7 @@ __global__ __launch_bounds__(256) void conv_so2_radial_kernel(int N, int E, cons
       a0 = kq == 0 ? R[0] : (kq == 1 ? R[1] : (kq == 2 ? R[2] : R[3]));
       a1 = kq == 0 ? R[4] : (kq == 1 ? R[5] : (kq == 2 ? R[6] : R[7]));
     }
-    // w of edges e0 + 4 kq + i, channel cb + j: wp[p][i]
+    // w of edges e0 + kq + 4 i, channel cb + j: wp[p][i]
     f4 wp[P];
 #pragma unroll
     for (int p = 0; p < P; ++p) {
@@ -513,7 +517,8 @@ __global__ __launch_bounds__(256) void conv_so2_radial_kernel(int N, int E, cons
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int e = e0 + 4 * kq + i;
+      if (e0 + 4 * i >= e_end) break;  // no edge left for any lane (wave-uniform)
+      const int e = e0 + kq + 4 * i;
       if (e < e_end) {
         const So2Frame<L> f(vec[3 * e], vec[3 * e + 1], vec[3 * e + 2]);
         const int s = clamp_index(src[e], N);
