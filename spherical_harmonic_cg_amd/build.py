@@ -32,9 +32,15 @@ FLAGS = [
 ]
 
 
+# per-source additions: the radial edge-aligned kernel consumes its matrix-core
+# results on the vector ALUs, so they are produced in VGPRs (no copies out of
+# the accumulation registers)
+EXTRA_FLAGS = {"conv_so2.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, src.replace(".hip", ".o"))
-    cmd = [HIPCC] + FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC] + FLAGS + EXTRA_FLAGS.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     out = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if "packed-fp32-ops" not in l)
     if r.returncode != 0:

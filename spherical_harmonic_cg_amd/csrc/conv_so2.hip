@@ -136,6 +136,29 @@ struct So2Frame {
     angle_powers<L>(uz, tilt ? rho2 * inv_rho : 0.0f, ct, st);
     keep = nz ? 1.0f : 0.0f;
   }
+  So2Frame() = default;
+  // LDS record of FS floats (16-byte aligned): cp, sp, ct, st, keep
+  static constexpr int FS = (4 * (L + 1) + 1 + 3) / 4 * 4;
+  __device__ __forceinline__ void store(float* __restrict__ f) const {
+#pragma unroll
+    for (int m = 0; m <= L; ++m) {
+      f[m] = cp[m];
+      f[L + 1 + m] = sp[m];
+      f[2 * (L + 1) + m] = ct[m];
+      f[3 * (L + 1) + m] = st[m];
+    }
+    f[4 * (L + 1)] = keep;
+  }
+  __device__ __forceinline__ void load(const float* __restrict__ f) {
+#pragma unroll
+    for (int m = 0; m <= L; ++m) {
+      cp[m] = f[m];
+      sp[m] = f[L + 1 + m];
+      ct[m] = f[2 * (L + 1) + m];
+      st[m] = f[3 * (L + 1) + m];
+    }
+    keep = f[4 * (L + 1)];
+  }
 };
 
 // acc += D(R_e)^T P_w(D(R_e) v) for one channel (the radial kernel below; the
@@ -464,7 +487,7 @@ __global__ __launch_bounds__(So2Cfg<C>::THREADS) void conv_so2_msg_kernel(int N,
 constexpr int kSo2RadialBasis = 8;
 
 template <int L, int PS, int C>
-__global__ __launch_bounds__(256) void conv_so2_radial_kernel(int N, int E, const int* __restrict__ row_ptr,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PS == 0 ? 3 : 2))) void conv_so2_radial_kernel(int N, int E, const int* __restrict__ row_ptr,
                                                               const float* __restrict__ vec,
                                                               const int* __restrict__ src,
                                                               const float* __restrict__ x,
@@ -476,7 +499,10 @@ __global__ __launch_bounds__(256) void conv_so2_radial_kernel(int N, int E, cons
   constexpr int NB = kSo2RadialBasis;
   constexpr int NBLK = C / 16;
   static_assert(C % 16 == 0 && L <= 3, "radial edge-aligned kernel: C multiple of 16, lmax <= 3");
+  using Frame = So2Frame<L>;
   __shared__ float wl[NB * P * 16];  // [b][p][channel of the block]
+  // the current batch's 16 edge frames, per wave (computed once per batch, read by every channel lane)
+  __shared__ __attribute__((aligned(16))) float frm[4][16 * Frame::FS];
   const int cb = (int)(blockIdx.x % NBLK) * 16;
   for (int i = threadIdx.x; i < NB * P * 16; i += 256) {
     const int bp = i >> 4;  // b * P + p
@@ -499,28 +525,40 @@ __global__ __launch_bounds__(256) void conv_so2_radial_kernel(int N, int E, cons
   for (int e0 = e_beg; e0 < e_end; e0 += 16) {
     // A operand of lane (j, kq): R_{kq}, R_{4+kq} of the edge of A row j, e0 + (j >> 2) + 4 (j & 3)
     // (zeros past the row)
+    // and the frame of that edge, written by the lanes of group 0 to the wave's LDS
     float a0 = 0.0f, a1 = 0.0f;
-    const int ea = e0 + ((j >> 2) | ((j & 3) << 2));
+    const int ar = (j >> 2) | ((j & 3) << 2);
+    const int ea = e0 + ar;
+    float ax = 0.0f, ay = 0.0f, az = 0.0f;
     if (ea < e_end) {
-      const float ax = vec[3 * ea], ay = vec[3 * ea + 1], az = vec[3 * ea + 2];
+      ax = vec[3 * ea];
+      ay = vec[3 * ea + 1];
+      az = vec[3 * ea + 2];
       float R[NB];
       radial_basis<NB>(sqrtf(ax * ax + ay * ay + az * az), inv_rc, R);
       a0 = kq == 0 ? R[0] : (kq == 1 ? R[1] : (kq == 2 ? R[2] : R[3]));
       a1 = kq == 0 ? R[4] : (kq == 1 ? R[5] : (kq == 2 ? R[6] : R[7]));
     }
+    float* const wf = frm[threadIdx.x >> 6];
+    wave_lds_sync();  // the previous batch's frames have been read
+    if (kq == 0) Frame(ax, ay, az).store(wf + ar * Frame::FS);
+    wave_lds_sync();
     // w of edges e0 + kq + 4 i, channel cb + j: wp[p][i]
     f4 wp[P];
+    // basis functions 0..3 for every path, then 4..7 accumulated (no back-to-back dependent products)
 #pragma unroll
-    for (int p = 0; p < P; ++p) {
+    for (int p = 0; p < P; ++p)
       wp[p] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, wl[(kq * P + p) * 16 + j], f4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+    for (int p = 0; p < P; ++p)
       wp[p] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, wl[((4 + kq) * P + p) * 16 + j], wp[p], 0, 0, 0);
-    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if (e0 + 4 * i >= e_end) break;  // no edge left for any lane (wave-uniform)
       const int e = e0 + kq + 4 * i;
       if (e < e_end) {
-        const So2Frame<L> f(vec[3 * e], vec[3 * e + 1], vec[3 * e + 2]);
+        Frame f;
+        f.load(wf + (kq + 4 * i) * Frame::FS);
         const int s = clamp_index(src[e], N);
         float v[K];
         load_feat<K>(x + ((size_t)s * C + cb + j) * K, v);
