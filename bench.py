@@ -29,6 +29,7 @@ PEAK_FP32_TFLOPS = 157.3       # MI355X fp32 (matrix and packed vector)
 METRIC = "edges/sec fused SH+CG-TP+aggregate (10k atoms, C=64, L=3); % of roofline"
 
 WORKLOAD_TEXT = {
+    "tiny": "tiny: 64 atoms, 6 A cube (open boundaries), r_c=3 A, both directions, L=2, C=8, conv",
     "typical": "typical: 1000 atoms, periodic 0.1/A^3, k=20 nearest, L=3, C=32, conv + fp32 32x32 per-l linear",
     "mid": "mid: 10k atoms, periodic 0.1/A^3, r_c=4 A, L=3, C=64, conv + bf16 64x64 per-l linear",
     "large": "large: 100k atoms, periodic 0.1/A^3, r_c=5 A, L=3, C=32, conv (dst-sorted)",
