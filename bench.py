@@ -78,11 +78,11 @@ KERNEL_SOURCES = ("spherical_harmonic_cg_amd/csrc/conv_node.hip", "spherical_har
                   "spherical_harmonic_cg_amd/csrc/generated/cg_tables.inc")
 
 
-def kernel_source_hash():
+def kernel_source_hash(sources=KERNEL_SOURCES):
     import hashlib
 
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in sources:
         h.update(open(os.path.join(ROOT, rel), "rb").read())
     return h.hexdigest()[:16]
 
@@ -105,7 +105,8 @@ def measured_traffic(config, atom_order, unsorted, algo, path_set="parity", x_bf
     if x_bf16:
         key += "/xbf16"
     ent = rec.get(key)
-    if not ent or ent.get("source_sha256_16") != kernel_source_hash():
+    # each entry names the sources of the kernel it was taken on (default: the node kernel's)
+    if not ent or ent.get("source_sha256_16") != kernel_source_hash(tuple(ent.get("sources", KERNEL_SOURCES))):
         return None
     return ent["read_bytes"] + ent["write_bytes"]
 
