@@ -503,14 +503,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PS == 0 ? 3
   __shared__ float wl[NB * P * 16];  // [b][p][channel of the block]
   // the current batch's 16 edge frames, per wave (computed once per batch, read by every channel lane)
   __shared__ __attribute__((aligned(16))) float frm[4][16 * Frame::FS];
-  const int cb = (int)(blockIdx.x % NBLK) * 16;
+  // block-major order: the workgroups in flight at any time share one channel
+  // block, so the gathered slice of x (N * 16 * K floats) is what the caches
+  // must hold, not all of x
+  const int ngrp = (N + 3) / 4;
+  const int cb = (int)(blockIdx.x / ngrp) * 16;
   for (int i = threadIdx.x; i < NB * P * 16; i += 256) {
     const int bp = i >> 4;  // b * P + p
     wl[i] = w[(size_t)bp * C + cb + (i & 15)];
   }
   __syncthreads();
   const int lane = threadIdx.x & 63;
-  const int row = (int)(blockIdx.x / NBLK) * 4 + (threadIdx.x >> 6);
+  const int row = (int)(blockIdx.x % ngrp) * 4 + (threadIdx.x >> 6);
   if (row >= N) return;
   const int j = lane & 15;   // channel cb + j; A row (edge e0 + j) for the radial product
   const int kq = lane >> 4;  // edge group: edges kq + 4 i of each batch; A/B k index
