@@ -28,6 +28,8 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_FP32_TFLOPS = 157.3       # MI355X fp32 (matrix and packed vector)
 METRIC = "edges/sec fused SH+CG-TP+aggregate (10k atoms, C=64, L=3); % of roofline"
 
+GRAPH_STEPS = 20  # at most this many steps captured per HIP graph with --graph
+
 WORKLOAD_TEXT = {
     "tiny": "tiny: 64 atoms, 6 A cube (open boundaries), r_c=3 A, both directions, L=2, C=8, conv",
     "typical": "typical: 1000 atoms, periodic 0.1/A^3, k=20 nearest, L=3, C=32, conv + fp32 32x32 per-l linear",
@@ -162,6 +164,8 @@ def main():
     ap.add_argument("--lmax", type=int, default=None,
                     help="instead of --config: the mid graph (10k atoms, r_c=4 A, C=64) with features of degree "
                          "up to LMAX (4..6 run the edge-aligned kernel; a labelled extra, not the headline)")
+    ap.add_argument("--graph", action="store_true",
+                    help="time the step as one captured HIP graph replayed K times (sorted edges, no GPU sort)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
     ap.add_argument("--backward", action="store_true",
@@ -174,6 +178,8 @@ def main():
 
     if args.sort_edges and not args.unsorted:
         ap.error("--sort-edges needs --unsorted")
+    if args.graph and args.unsorted:
+        ap.error("--graph times dst-sorted edges only")
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path (a split into CSR "
               "row ranges with a halo exchange of source features is not built); run with --gpus 1.",
@@ -260,6 +266,39 @@ def main():
     wall = time.perf_counter() - wall0
     total_ms = t_start.elapsed_time(t_end)
     ms_per_step = total_ms / K
+    graph_note = None
+    if args.graph:
+        # the same step captured as a HIP graph, GRAPH_STEPS steps per graph (one graph launch costs about
+        # as much as a few kernel launches, so a one-step graph gains nothing), replayed until K steps ran:
+        # what the step costs without the host's per-launch work (the eager rate is kept in the record)
+        eager_ms = ms_per_step
+        per_graph = max(d for d in range(1, min(GRAPH_STEPS, K) + 1) if K % d == 0)  # exactly K steps
+        reps = K // per_graph
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            conv()
+            linear()
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(per_graph):
+                conv()
+                linear()
+        for _ in range(2):
+            g.replay()
+        torch.cuda.synchronize()
+        t_start.record(stream)
+        for i in range(reps):
+            g.replay()
+        t_end.record(stream)
+        torch.cuda.synchronize()
+        ms_per_step = t_start.elapsed_time(t_end) / (reps * per_graph)
+        graph_note = {"eager_ms_per_step": round(eager_ms, 5), "graph_ms_per_step": round(ms_per_step, 5),
+                      "steps_per_graph": per_graph, "graph_replays": reps}
+        log("graph replay: %.4f ms/step (%d steps per graph, %d replays; eager %.4f)" % (
+            ms_per_step, per_graph, reps, eager_ms))
     # 2. per-launch durations: the same K steps again with an event pair around every launch (the
     #    events add gaps between the kernels, so this pass does not give the step rate)
     ev = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(4)) for _ in range(K)]
@@ -423,7 +462,8 @@ def main():
                    + (" (sorted by destination on the GPU inside each step)" if args.sort_edges else "")
                    + (" (cell-sorted atom numbering)" if args.atom_order == "cell" else "")
                    + (" (SO(3) path set)" if args.path_set == "so3" else "")
-                   + (" (bfloat16 node features)" if args.x_bf16 else ""),
+                   + (" (bfloat16 node features)" if args.x_bf16 else "")
+                   + (" (step replayed as one HIP graph)" if args.graph else ""),
                    "atoms": wl.N, "edges": wl.E, "channels": wl.C, "lmax": wl.lmax, "paths": wl.P,
                    "coupling_nnz": nnz, "algo": args.algo},
         "roofline": roofline,
@@ -432,6 +472,8 @@ def main():
     if sort_out is not None:
         rec["edge_sort"] = {"ms": round(float(sort_ms.mean()), 5),
                             "what": "eqtp_sort_edges (counting sort by destination), inside ms_per_step"}
+    if graph_note is not None:
+        rec["graph"] = graph_note
     if backward is not None:
         rec["backward"] = backward
     if messages is not None:
