@@ -527,11 +527,10 @@ static hipError_t launch_bwd_t(const BwdArgs& a) {
   }
   if (a.gvec != nullptr) {
     if (sorted && a.algo != 2) {  // matrix cores unless the vector-ALU walk is asked for
-      int dev = 0, cus = 256;
-      if (hipGetDevice(&dev) != hipSuccess ||
-          hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-        cus = 256;
-      const int64_t g = (int64_t)cus * 8;
+      // one single-wave workgroup per row (the kernel also walks rows persistently for a smaller grid):
+      // the dispatcher keeps as many resident as registers and LDS allow (9 per CU) and balances rows
+      // of different lengths
+      const int64_t g = (int64_t)1 << 24;
       hipLaunchKernelGGL((gvec_node_kernel<L, PS, C>), dim3((unsigned)(a.N < g ? a.N : g)), dim3(64), 0, a.stream,
                          (int)a.N, (int)a.E, a.row_ptr, a.vec, a.src, a.x, a.w, a.gout, a.gvec);
     } else if (sorted) {
