@@ -32,10 +32,11 @@ FLAGS = [
 ]
 
 
-# per-source additions: the radial edge-aligned kernel consumes its matrix-core
-# results on the vector ALUs, so they are produced in VGPRs (no copies out of
-# the accumulation registers)
-EXTRA_FLAGS = {"conv_so2.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# per-source additions: the radial edge-aligned kernel and the grad_vec kernel
+# consume their matrix-core results on the vector ALUs, so they are produced in
+# VGPRs (no copies out of the accumulation registers)
+EXTRA_FLAGS = {"conv_so2.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+               "conv_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str) -> str:
