@@ -421,11 +421,19 @@ def main():
     conv_s = float(conv_ms.mean()) * 1e-3
     achieved_tflops = flop_edge * wl.E / conv_s / 1e12
     cfg_key = args.config if args.lmax is None else "lmax%d" % args.lmax
-    roofline = {"bound": "mfma", "achieved": round(achieved_tflops, 3), "peak": PEAK_FP32_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved_tflops / PEAK_FP32_TFLOPS, 4),
+    # which kernel ran: the node kernel (fixed weights, dst-sorted, lmax <= 3) is bound by the fp32 matrix
+    # cores; every other form by the fp32 vector ALUs (the radial edge-aligned kernel forms its radial
+    # weights on the matrix cores but spends most of its time in the vector coupling)
+    sorted_edges = not args.unsorted or args.sort_edges
+    node_kernel = wl.weight_mode == 0 and sorted_edges and wl.lmax <= 3 and args.algo in (0, 1)
+    roofline = {"bound": "mfma" if node_kernel else "alu", "achieved": round(achieved_tflops, 3),
+                "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved_tflops / PEAK_FP32_TFLOPS, 4),
                 "traffic": measured_traffic(cfg_key, args.atom_order, args.unsorted, args.algo, args.path_set,
                                             args.x_bf16, args.sort_edges)}
-    if args.algo == 3 or wl.lmax > 3:
+    if wl.weight_mode == 1:
+        roofline["counted"] = ("2*nnz*C coupling flop (nnz=%d) + 2*8*P*C radial flop per edge, whichever form "
+                               "the kernel computes them in" % nnz)
+    elif args.algo == 3 or wl.lmax > 3:
         # edge-aligned kernel: vector-ALU bound; flop = 2 per arithmetic instruction lane it executes
         ops = so2_ops(wl.lmax, wl.path_set)
         so2_tflops = 2 * ops * wl.C * wl.E / conv_s / 1e12
