@@ -137,8 +137,10 @@ struct So2Frame {
     keep = nz ? 1.0f : 0.0f;
   }
   So2Frame() = default;
-  // LDS record of FS floats (16-byte aligned): cp, sp, ct, st, keep
-  static constexpr int FS = (4 * (L + 1) + 1 + 3) / 4 * 4;
+  // LDS record of FS floats (16-byte aligned): cp, sp, ct, st, keep, and one
+  // spare word (SRC) for the caller
+  static constexpr int SRC = 4 * (L + 1) + 1;
+  static constexpr int FS = (SRC + 1 + 3) / 4 * 4;
   __device__ __forceinline__ void store(float* __restrict__ f) const {
 #pragma unroll
     for (int m = 0; m <= L; ++m) {
@@ -529,15 +531,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PS == 0 ? 3
   for (int e0 = e_beg; e0 < e_end; e0 += 16) {
     // A operand of lane (j, kq): R_{kq}, R_{4+kq} of the edge of A row j, e0 + (j >> 2) + 4 (j & 3)
     // (zeros past the row)
-    // and the frame of that edge, written by the lanes of group 0 to the wave's LDS
+    // and the frame and source of that edge, written by the lanes of group 0 to the wave's LDS
     float a0 = 0.0f, a1 = 0.0f;
     const int ar = (j >> 2) | ((j & 3) << 2);
     const int ea = e0 + ar;
     float ax = 0.0f, ay = 0.0f, az = 0.0f;
+    int sa = 0;
     if (ea < e_end) {
       ax = vec[3 * ea];
       ay = vec[3 * ea + 1];
       az = vec[3 * ea + 2];
+      sa = clamp_index(src[ea], N);
       float R[NB];
       radial_basis<NB>(sqrtf(ax * ax + ay * ay + az * az), inv_rc, R);
       a0 = kq == 0 ? R[0] : (kq == 1 ? R[1] : (kq == 2 ? R[2] : R[3]));
@@ -545,7 +549,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PS == 0 ? 3
     }
     float* const wf = frm[threadIdx.x >> 6];
     wave_lds_sync();  // the previous batch's frames have been read
-    if (kq == 0) Frame(ax, ay, az).store(wf + ar * Frame::FS);
+    if (kq == 0) {
+      Frame(ax, ay, az).store(wf + ar * Frame::FS);
+      reinterpret_cast<int*>(wf + ar * Frame::FS)[Frame::SRC] = sa;  // the edge's source, beside its frame
+    }
     wave_lds_sync();
     // w of edges e0 + kq + 4 i, channel cb + j: wp[p][i]
     f4 wp[P];
@@ -563,7 +570,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PS == 0 ? 3
       if (e < e_end) {
         Frame f;
         f.load(wf + (kq + 4 * i) * Frame::FS);
-        const int s = clamp_index(src[e], N);
+        const int s = reinterpret_cast<const int*>(wf + (kq + 4 * i) * Frame::FS)[Frame::SRC];
         float v[K];
         load_feat<K>(x + ((size_t)s * C + cb + j) * K, v);
         so2_message<L, PS>(v, f, [&](auto p) { return wp[decltype(p)::value][i]; }, acc);
