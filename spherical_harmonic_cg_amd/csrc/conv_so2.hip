@@ -482,19 +482,19 @@ __global__ __launch_bounds__(So2Cfg<C>::THREADS) void conv_so2_msg_kernel(int N,
 // rotate back) and sums the messages in registers.  A row's last, partial
 // batch of n edges then stops after ceil(n/4) of the 4 slots.  The four edge
 // groups of a lane's channel are combined with xor shuffles after the row
-// (deterministic).
+// (deterministic).  Each edge's frame (cos/sin of m phi, m theta) and source
+// index are computed once per batch, from the edge vector the lane loads for
+// its A row, and shared through the wave's LDS.
 // Work unit: one wave per (row, 16-channel block); a workgroup's 4 waves take
-// 4 consecutive rows of one block.
+// 4 consecutive rows of one block; workgroups are numbered block-major.  The
+// parity path set fits 168 VGPRs (3 waves per SIMD); the SO(3) set keeps 2.
 // ---------------------------------------------------------------------------
 constexpr int kSo2RadialBasis = 8;
 
 template <int L, int PS, int C>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PS == 0 ? 3 : 2))) void conv_so2_radial_kernel(int N, int E, const int* __restrict__ row_ptr,
-                                                              const float* __restrict__ vec,
-                                                              const int* __restrict__ src,
-                                                              const float* __restrict__ x,
-                                                              const float* __restrict__ w, float* __restrict__ out,
-                                                              float inv_rc) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PS == 0 ? 3 : 2))) void conv_so2_radial_kernel(
+    int N, int E, const int* __restrict__ row_ptr, const float* __restrict__ vec, const int* __restrict__ src,
+    const float* __restrict__ x, const float* __restrict__ w, float* __restrict__ out, float inv_rc) {
   using T = So2Tables<L, PS>;
   constexpr int K = num_comp(L);
   constexpr int P = T::P;
@@ -503,7 +503,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PS == 0 ? 3
   static_assert(C % 16 == 0 && L <= 3, "radial edge-aligned kernel: C multiple of 16, lmax <= 3");
   using Frame = So2Frame<L>;
   __shared__ float wl[NB * P * 16];  // [b][p][channel of the block]
-  // the current batch's 16 edge frames, per wave (computed once per batch, read by every channel lane)
+  // the current batch's 16 edge frames and sources, per wave (computed once per batch, read by every
+  // channel lane)
   __shared__ __attribute__((aligned(16))) float frm[4][16 * Frame::FS];
   // block-major order: the workgroups in flight at any time share one channel
   // block, so the gathered slice of x (N * 16 * K floats) is what the caches
