@@ -89,6 +89,12 @@ def kernel_source_hash(sources=KERNEL_SOURCES):
     return h.hexdigest()[:16]
 
 
+def graph_steps(K):
+    """Steps captured per HIP graph with --graph: the largest divisor of K up to
+    GRAPH_STEPS, so that whole replays run exactly K steps."""
+    return max(d for d in range(1, min(GRAPH_STEPS, K) + 1) if K % d == 0)
+
+
 def measured_traffic(config, atom_order, unsorted, algo, path_set="parity", x_bf16=False, sort_edges=False):
     """HBM-side bytes per launch of the conv kernel from the committed counter
     summary (profiles/traffic.json), or None when that summary was taken on
@@ -272,7 +278,7 @@ def main():
         # as much as a few kernel launches, so a one-step graph gains nothing), replayed until K steps ran:
         # what the step costs without the host's per-launch work (the eager rate is kept in the record)
         eager_ms = ms_per_step
-        per_graph = max(d for d in range(1, min(GRAPH_STEPS, K) + 1) if K % d == 0)  # exactly K steps
+        per_graph = graph_steps(K)
         reps = K // per_graph
         side = torch.cuda.Stream()
         side.wait_stream(stream)
