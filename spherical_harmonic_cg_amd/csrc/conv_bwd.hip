@@ -424,7 +424,27 @@ __global__ __launch_bounds__(64) void gvec_node_kernel(int N, int E, const int* 
 #pragma unroll
       for (int s4 = 0; s4 < 4; ++s4) acc[s4] = f4{0.f, 0.f, 0.f, 0.f};
       for (int blk = 0; blk < NBLK; ++blk) {
-        wave_lds_sync();  // previous block's reads of Bl are done
+        // x[src] of the edges of 16-edge step s4 for this block: lane (edge i16, group kq) holds
+        // components 4kq .. 4kq+3 of the block's 16 channels
+        f4 xv[16];
+        auto load_step = [&](int s4) {
+          const int sv = sstg[16 * s4 + i16];
+          const bool ok = sv >= 0;
+#pragma unroll
+          for (int c = 0; c < 16; ++c) {
+            const bool cok = ok && c < CW;
+            const size_t o = ((size_t)(cok ? sv : 0) * C + blk * CW + (c < CW ? c : 0)) * K;
+            if constexpr (K == 16) {
+              xv[c] = cok ? *reinterpret_cast<const f4*>(x + o + 4 * kq) : f4{0.f, 0.f, 0.f, 0.f};
+            } else {
+#pragma unroll
+              for (int r = 0; r < 4; ++r) xv[c][r] = (cok && 4 * kq + r < K) ? x[o + 4 * kq + r] : 0.0f;
+            }
+          }
+        };
+        wave_lds_sync();  // previous block's reads of Bl are done; sstg is written
+        // the first step's gathers go out before the B_d build, which hides their latency
+        load_step(0);
         // 1. B_d for this block's channels (all 16 rows zeroed first: rows of
         //    channels past C stay zero, so the padded MFMA columns add nothing)
         float* brow = Bl + i16 * kGvBS;
@@ -454,20 +474,7 @@ __global__ __launch_bounds__(64) void gvec_node_kernel(int N, int E, const int* 
 #pragma unroll
         for (int s4 = 0; s4 < 4; ++s4) {
           if (16 * s4 < cnt) {  // wave-uniform
-            const int sv = sstg[16 * s4 + i16];
-            const bool ok = sv >= 0;
-            f4 xv[16];
-#pragma unroll
-            for (int c = 0; c < 16; ++c) {
-              const bool cok = ok && c < CW;
-              const size_t o = ((size_t)(cok ? sv : 0) * C + blk * CW + (c < CW ? c : 0)) * K;
-              if constexpr (K == 16) {
-                xv[c] = cok ? *reinterpret_cast<const f4*>(x + o + 4 * kq) : f4{0.f, 0.f, 0.f, 0.f};
-              } else {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) xv[c][r] = (cok && 4 * kq + r < K) ? x[o + 4 * kq + r] : 0.0f;
-              }
-            }
+            if (s4 > 0) load_step(s4);
 #pragma unroll
             for (int c = 0; c < 16; ++c)
 #pragma unroll
