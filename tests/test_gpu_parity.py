@@ -271,6 +271,18 @@ def test_conv_radial_batch_edges():
         _assert_close(_np(_run_conv(eq, wl, g, 0)), ref, what="radial %d edges per row" % n_e)
 
 
+@pytest.mark.parametrize("n", [1, 2, 3, 5])
+def test_conv_radial_few_nodes(n):
+    """Fewer nodes than a workgroup's four rows (one row group per channel block in the radial
+    edge-aligned kernel's block-major grid), C = 128 (eight channel blocks)."""
+    eq = _eq()
+    wl = synth.small_graph(n=n, e_per_row=19, C=128, lmax=3, seed=1200 + n, radial=True, r_cut=5.0)
+    g = _gpu_inputs(wl)
+    ref = oracle.conv(wl.N, wl.vec, wl.src, wl.dst, wl.x, wl.w_rad, 3, weight_mode=1, r_cut=5.0)
+    _say("radial few nodes n=%d" % n)
+    _assert_close(_np(_run_conv(eq, wl, g, 0)), ref, what="radial n=%d" % n)
+
+
 def test_conv_radial_deterministic():
     eq = _eq()
     wl = synth.small_graph(n=40, e_per_row=23, C=64, lmax=3, seed=41, radial=True, r_cut=5.0)
