@@ -34,6 +34,8 @@
 // H_s is the forward's G with gout gathered through dst instead of x through
 // src, and the contraction is the forward's with mu1 and mu3 exchanged
 // (AdjointTables); grad_w reuses each run's partial sum with one more FMA.
+#include <atomic>
+
 #include "eqtp_device.hpp"
 #include "eqtp_kernels.hpp"
 
@@ -477,10 +479,16 @@ __global__ __launch_bounds__(64) void probe_node_kernel(int N, int E, const int*
   node_tasks<Cfg::PF, Cfg::NBLK, true>(N, E, row_ptr, vec, src, stage, load, compute, task_end);
 }
 
+// compute units of the current device, queried once per device (launches are
+// on the host's hot path for small graphs); racing first queries store the
+// same value
 static int num_cus() {
+  static std::atomic<int> cached[64];
   int dev = 0, n = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (dev >= 0 && dev < 64 && (n = cached[dev].load(std::memory_order_relaxed)) > 0) return n;
   if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 256;
+  if (dev >= 0 && dev < 64) cached[dev].store(n, std::memory_order_relaxed);
   return n;
 }
 
