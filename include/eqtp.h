@@ -26,7 +26,8 @@
  *     detected on the host before anything is launched (no partial writes).
  *     A failed launch returns EQTP_EHIP.  Device faults surface at the
  *     caller's next synchronisation.
- *   - Functions are thread-safe; the library keeps no mutable state.
+ *   - Functions are thread-safe; the only mutable state is a per-device cache
+ *     of the compute-unit count, read once through the HIP runtime.
  *   - Feature vectors use layout [N, C, K] with K = (lmax+1)^2: each
  *     channel's K components are contiguous, in the component order above.
  *   - Indices (src, dst, row_ptr) are int32.  Out-of-range index values are
