@@ -81,7 +81,7 @@ struct NodeCfg {
   static constexpr int STG = 64 * 16 + 64;               // staging: Y[64][16] + src[64]
   static constexpr int LDS = SLICE > STG ? SLICE : STG;  // staging and G share the wave's LDS
   static constexpr int THREADS = kWave;                  // one independent wavefront per workgroup
-  static constexpr int PF = 3;                           // gather steps in flight
+  static constexpr int PF = 2;                           // gather steps in flight
   static_assert(LDS * 4 <= 64 * 1024, "LDS budget");
 };
 
