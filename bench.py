@@ -178,6 +178,8 @@ def main():
                     help="also time eqtp_conv_backward (all three gradients) on the same inputs (an extra field)")
     ap.add_argument("--messages", action="store_true",
                     help="also time eqtp_conv_messages (per-edge [E,C,K] output, the page's kernel) (an extra field)")
+    ap.add_argument("--sh", action="store_true",
+                    help="also time eqtp_sh (standalone harmonics [E,K] of the workload's edges) (an extra field)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="after timing, run one 256 MiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -412,6 +414,28 @@ def main():
         log("messages: %.4f ms (%.3e edges/s, %.0f GB/s written)" % (mms, wl.E / (mms * 1e-3),
                                                                       wbytes / (mms * 1e-3) / 1e9))
 
+    sh = None
+    if args.sh:
+        Y = torch.empty((wl.E, wl.K), dtype=torch.float32, device=dev)
+        for _ in range(3):
+            eq.eqtp_sh(vec, wl.lmax, Y=Y)
+        torch.cuda.synchronize()
+        ks = max(20, K // 2)
+        s0 = torch.cuda.Event(enable_timing=True)
+        s1 = torch.cuda.Event(enable_timing=True)
+        s0.record(stream)
+        for _ in range(ks):
+            eq.eqtp_sh(vec, wl.lmax, Y=Y)
+        s1.record(stream)
+        torch.cuda.synchronize()
+        sms = s0.elapsed_time(s1) / ks
+        sbytes = wl.E * (12 + 4 * wl.K)
+        sh = {"ms": round(sms, 5), "launches": ks, "bytes": sbytes, "GBps": round(sbytes / (sms * 1e-3) / 1e9, 1),
+              "frac_hbm": round(sbytes / (sms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+              "what": "eqtp_sh: 12 B in and 4*K B out per edge, back-to-back launches between two events"}
+        del Y
+        log("sh: %.4f ms (%.0f GB/s, %.3f of HBM peak)" % (sms, sh["GBps"], sh["frac_hbm"]))
+
     if args.calib_copy:
         a = torch.empty(64 << 20, dtype=torch.float32, device=dev)
         b = torch.empty_like(a)
@@ -492,6 +516,8 @@ def main():
         rec["backward"] = backward
     if messages is not None:
         rec["messages"] = messages
+    if sh is not None:
+        rec["sh"] = sh
     print(json.dumps(rec), flush=True)
 
 
