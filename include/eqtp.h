@@ -190,10 +190,10 @@ int eqtp_conv_messages(const eqtp_conv_desc* d, int64_t N, int64_t E, const floa
  * names a PyTorch autograd function with a backward as the integration path,
  * section "extension possibilities").  A zero-length edge vector has
  * grad_vec = 0.
- *   d, N, E, vec, src, dst, row_ptr, x, weights: as for eqtp_conv_fused;
- *            d->weight_mode must be EQTP_W_FIXED (radial weights:
- *            EQTP_EUNSUPPORTED).
- *   grad_out [N, C, K] fp32.
+ *   d, N, E, vec, src, dst, row_ptr, x, weights: as for eqtp_conv_fused
+ *            (x fp32, 16-byte aligned); d->weight_mode must be EQTP_W_FIXED
+ *            (radial weights: EQTP_EUNSUPPORTED).
+ *   grad_out [N, C, K] fp32, 16-byte aligned.
  *   grad_x   [N, C, K] fp32, 16-byte aligned, or NULL (not computed).
  *   grad_w   [P, C] fp32, or NULL.
  *   grad_vec [E, 3] fp32, or NULL.

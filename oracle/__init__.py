@@ -28,10 +28,10 @@ PATHS_SO3 = 1
 
 
 def build(force: bool = False) -> str:
-    """Compile eqtp_oracle.c into liboracle.so (gcc -O2, no fast-math)."""
+    """Compile eqtp_oracle.c into liboracle.so (gcc -O2, no fast-math, OpenMP)."""
     if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
         tmp = _LIB + ".tmp%d" % os.getpid()
-        cmd = ["gcc", "-O2", "-std=c99", "-D_GNU_SOURCE", "-fPIC", "-shared", "-o", tmp, _SRC, "-lm"]
+        cmd = ["gcc", "-O2", "-std=c99", "-D_GNU_SOURCE", "-fopenmp", "-fPIC", "-shared", "-o", tmp, _SRC, "-lm"]
         subprocess.run(cmd, check=True)
         os.replace(tmp, _LIB)
     return _LIB
@@ -79,8 +79,24 @@ def _load():
             lib.oracle_conv_backward.restype = i32
             lib.oracle_conv_backward_f64.argtypes = [i64, i64, i32, i32, i32] + [vp] * 9
             lib.oracle_conv_backward_f64.restype = i32
+            lib.oracle_set_threads.argtypes = [i32]
+            lib.oracle_set_threads.restype = None
+            lib.oracle_num_threads.argtypes = []
+            lib.oracle_num_threads.restype = i32
             _lib = lib
     return _lib
+
+
+def set_threads(n: int = 0) -> None:
+    """Threads for the loops over destination rows, nodes and edges (0 = the
+    OpenMP default: OMP_NUM_THREADS, else every core).  Results do not depend
+    on it."""
+    _load().oracle_set_threads(int(n))
+
+
+def num_threads() -> int:
+    """Threads the parallel loops will use."""
+    return int(_load().oracle_num_threads())
 
 
 def _f32(a):

@@ -12,7 +12,10 @@
  *
  * Everything is computed in double precision from the caller's float32
  * inputs, in the plain loop order of the definition, with no blocking, fusion
- * or reordering.
+ * or reordering.  Loops over independent outputs (destination rows, nodes,
+ * edges) are shared out over OpenMP threads; every output element still
+ * receives its terms in the same order, so the result does not depend on the
+ * thread count (checked bit for bit by the tests).
  *
  * Sources (the Batmobile page, "Batmobile CUDA kernel optimisation: a 10-20x
  * acceleration strategy for equivariant graph neural networks"):
@@ -39,6 +42,9 @@
  */
 #include <complex.h>
 #include <math.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -266,13 +272,102 @@ void oracle_radial_basis(double r, double r_cut, int n_basis, double* R) {
 /* Convolution                                                               */
 /* ------------------------------------------------------------------------ */
 
+/* Worker threads of the loops below that run over independent outputs
+ * (destination rows, nodes, edges); 0 = the OpenMP default (OMP_NUM_THREADS,
+ * else every core of the process).  Splitting the rows over threads changes
+ * no sum: each output element still receives its terms in the same order. */
+static int g_threads = 0;
+
+void oracle_set_threads(int n) { g_threads = n > 0 ? n : 0; }
+
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+  return g_threads > 0 ? g_threads : omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+/* The coupling blocks of every path, dense, from oracle_cg_real. */
+typedef struct {
+  int P;
+  int32_t* paths; /* [P, 3] (l1, l2, l3) */
+  double** cg;    /* cg[p]: [2l1+1][2l2+1][2l3+1] */
+} path_blocks;
+
+static int path_blocks_make(int lmax, int path_set, path_blocks* pb) {
+  pb->P = oracle_paths(lmax, path_set, NULL);
+  if (pb->P <= 0) return 1;
+  pb->paths = (int32_t*)malloc(sizeof(int32_t) * 3 * pb->P);
+  oracle_paths(lmax, path_set, pb->paths);
+  pb->cg = (double**)malloc(sizeof(double*) * pb->P);
+  for (int p = 0; p < pb->P; ++p) {
+    int l1 = pb->paths[3 * p], l2 = pb->paths[3 * p + 1], l3 = pb->paths[3 * p + 2];
+    pb->cg[p] = (double*)malloc(sizeof(double) * (2 * l1 + 1) * (2 * l2 + 1) * (2 * l3 + 1));
+    oracle_cg_real(l1, l2, l3, pb->cg[p], NULL);
+  }
+  return 0;
+}
+
+static void path_blocks_free(path_blocks* pb) {
+  for (int p = 0; p < pb->P; ++p) free(pb->cg[p]);
+  free(pb->cg);
+  free(pb->paths);
+}
+
+/* Adds edge e's message into the C*K values at o (the destination's block, or
+ * the edge's own message block):
+ *   o[c, l3 mu3] += sum_p w_e[p,c] sum_{mu1,mu2} C^p[mu1,mu2,mu3] x[src_e, c, l1 mu1] Y_{l2 mu2}(vec_e)
+ * in the order: harmonics, per-edge path weights, then paths, mu1, mu2, mu3,
+ * channel.  Y [K] and we [P*C] are the caller's work space. */
+static void edge_message_add(const path_blocks* pb, int lmax, int C, int weight_mode, double r_cut, int n_basis,
+                             const double* vec, int64_t e, int64_t s, const double* x, const double* w, double* Y,
+                             double* we, double* o) {
+  int K = (lmax + 1) * (lmax + 1);
+  int P = pb->P;
+  double R[64];
+  double vx = vec[3 * e], vy = vec[3 * e + 1], vz = vec[3 * e + 2];
+  /* 1. spherical harmonics of the edge direction */
+  real_sh(lmax, vx, vy, vz, Y);
+  /* 2. per-edge path weights */
+  if (weight_mode == 0) {
+    for (int i = 0; i < P * C; ++i) we[i] = w[i];
+  } else {
+    double r = sqrt(vx * vx + vy * vy + vz * vz);
+    oracle_radial_basis(r, r_cut, n_basis, R);
+    for (int i = 0; i < P * C; ++i) {
+      double acc = 0.0;
+      for (int n = 0; n < n_basis; ++n) acc += R[n] * w[(int64_t)n * P * C + i];
+      we[i] = acc;
+    }
+  }
+  /* 3. tensor product with the source features */
+  for (int p = 0; p < P; ++p) {
+    int l1 = pb->paths[3 * p], l2 = pb->paths[3 * p + 1], l3 = pb->paths[3 * p + 2];
+    int n1 = 2 * l1 + 1, n2 = 2 * l2 + 1, n3 = 2 * l3 + 1;
+    for (int a = 0; a < n1; ++a)
+      for (int b = 0; b < n2; ++b)
+        for (int c3 = 0; c3 < n3; ++c3) {
+          double coef = pb->cg[p][(a * n2 + b) * n3 + c3];
+          if (coef == 0.0) continue;
+          double cy = coef * Y[l2 * l2 + b];
+          for (int ch = 0; ch < C; ++ch) {
+            double xv = x[(s * C + ch) * K + l1 * l1 + a];
+            o[ch * K + l3 * l3 + c3] += we[p * C + ch] * cy * xv;
+          }
+        }
+  }
+}
+
 /* out[n, c, l3 mu3] = sum_{e: dst_e = n} sum_{p=(l1,l2,l3)} w_e[p,c]
  *                     sum_{mu1,mu2} C^p[mu1,mu2,mu3] x[src_e, c, l1 mu1] Y_{l2 mu2}(vec_e)
  * weight_mode 0: w_e[p,c] = w[p*C + c]   (w is [P, C])
  * weight_mode 1: w_e[p,c] = sum_n R_n(|vec_e|) w[n*P*C + p*C + c]   (w is [n_basis, P*C])
- * x is [N, C, K] float32, out is [N, C, K] float64 and is overwritten.
- * Edges are taken in the order given; dst need not be sorted.
- * Returns 0 on success, nonzero on bad arguments. */
+ * x is [N, C, K], out is [N, C, K] float64 and is overwritten.
+ * Edges may come in any order; each destination receives its edges' messages
+ * in the order given (the edges are grouped by destination, stably, and the
+ * destinations are shared out over the threads).  Returns 0 on success,
+ * 1 on bad arguments, 2 if an index is out of range (out is then all zero). */
 int oracle_conv_f64(int64_t N, int64_t E, int lmax, int C, int path_set, int weight_mode, double r_cut,
                     int n_basis, const double* vec, const int32_t* src, const int32_t* dst, const double* x,
                     const double* w, double* out) {
@@ -280,72 +375,46 @@ int oracle_conv_f64(int64_t N, int64_t E, int lmax, int C, int path_set, int wei
   if (weight_mode != 0 && weight_mode != 1) return 1;
   if (weight_mode == 1 && (n_basis <= 0 || n_basis > 64 || !(r_cut > 0.0))) return 1;
   int K = (lmax + 1) * (lmax + 1);
-  int P = oracle_paths(lmax, path_set, NULL);
-  if (P <= 0) return 1;
-  int32_t* paths = (int32_t*)malloc(sizeof(int32_t) * 3 * P);
-  oracle_paths(lmax, path_set, paths);
-  /* dense real CG block per path */
-  double** cg = (double**)malloc(sizeof(double*) * P);
-  for (int p = 0; p < P; ++p) {
-    int l1 = paths[3 * p], l2 = paths[3 * p + 1], l3 = paths[3 * p + 2];
-    cg[p] = (double*)malloc(sizeof(double) * (2 * l1 + 1) * (2 * l2 + 1) * (2 * l3 + 1));
-    oracle_cg_real(l1, l2, l3, cg[p], NULL);
-  }
   for (int64_t i = 0; i < N * C * K; ++i) out[i] = 0.0;
-  double* Y = (double*)malloc(sizeof(double) * K);
-  double* we = (double*)malloc(sizeof(double) * P * C);
-  double R[64];
-  int rc = 0;
-  for (int64_t e = 0; e < E; ++e) {
-    int64_t s = src[e], d = dst[e];
-    if (s < 0 || s >= N || d < 0 || d >= N) {
-      rc = 2;
-      break;
-    }
-    double vx = vec[3 * e], vy = vec[3 * e + 1], vz = vec[3 * e + 2];
-    /* 1. spherical harmonics of the edge direction */
-    real_sh(lmax, vx, vy, vz, Y);
-    /* 2. per-edge path weights */
-    if (weight_mode == 0) {
-      for (int i = 0; i < P * C; ++i) we[i] = w[i];
-    } else {
-      double r = sqrt(vx * vx + vy * vy + vz * vz);
-      oracle_radial_basis(r, r_cut, n_basis, R);
-      for (int i = 0; i < P * C; ++i) {
-        double acc = 0.0;
-        for (int n = 0; n < n_basis; ++n) acc += R[n] * w[(int64_t)n * P * C + i];
-        we[i] = acc;
+  for (int64_t e = 0; e < E; ++e)
+    if (src[e] < 0 || src[e] >= N || dst[e] < 0 || dst[e] >= N) return 2;
+  path_blocks pb;
+  if (path_blocks_make(lmax, path_set, &pb)) return 1;
+  int P = pb.P;
+  /* edges grouped by destination, in their given order inside each group */
+  int64_t* start = (int64_t*)calloc((size_t)N + 1, sizeof(int64_t));
+  int64_t* order = (int64_t*)malloc(sizeof(int64_t) * (E > 0 ? E : 1));
+  for (int64_t e = 0; e < E; ++e) start[dst[e] + 1]++;
+  for (int64_t n = 0; n < N; ++n) start[n + 1] += start[n];
+  int64_t* fill = (int64_t*)malloc(sizeof(int64_t) * (N > 0 ? N : 1));
+  for (int64_t n = 0; n < N; ++n) fill[n] = start[n];
+  for (int64_t e = 0; e < E; ++e) order[fill[dst[e]]++] = e;
+  free(fill);
+#pragma omp parallel num_threads(oracle_num_threads())
+  {
+    double* Y = (double*)malloc(sizeof(double) * K);
+    double* we = (double*)malloc(sizeof(double) * P * C);
+#pragma omp for schedule(dynamic, 16)
+    for (int64_t n = 0; n < N; ++n)
+      for (int64_t i = start[n]; i < start[n + 1]; ++i) {
+        int64_t e = order[i];
+        edge_message_add(&pb, lmax, C, weight_mode, r_cut, n_basis, vec, e, src[e], x, w, Y, we,
+                         out + n * C * K);
       }
-    }
-    /* 3. tensor product with the source features, summed into dst */
-    for (int p = 0; p < P; ++p) {
-      int l1 = paths[3 * p], l2 = paths[3 * p + 1], l3 = paths[3 * p + 2];
-      int n1 = 2 * l1 + 1, n2 = 2 * l2 + 1, n3 = 2 * l3 + 1;
-      for (int a = 0; a < n1; ++a)
-        for (int b = 0; b < n2; ++b)
-          for (int c3 = 0; c3 < n3; ++c3) {
-            double coef = cg[p][(a * n2 + b) * n3 + c3];
-            if (coef == 0.0) continue;
-            double cy = coef * Y[l2 * l2 + b];
-            for (int ch = 0; ch < C; ++ch) {
-              double xv = x[(s * C + ch) * K + l1 * l1 + a];
-              out[(d * C + ch) * K + l3 * l3 + c3] += we[p * C + ch] * cy * xv;
-            }
-          }
-    }
+    free(Y);
+    free(we);
   }
-  free(Y);
-  free(we);
-  for (int p = 0; p < P; ++p) free(cg[p]);
-  free(cg);
-  free(paths);
-  return rc;
+  free(start);
+  free(order);
+  path_blocks_free(&pb);
+  return 0;
 }
 
 /* Per-edge messages (the Batmobile page's fused kernel output, section "3.
  * operator fusion": one [C, K] message per edge, no destination sum):
  *   msg[e, c, l3 m3] = sum_p w_e[p,c] sum_{m1,m2} C^p[m1,m2,m3] x[src_e, c, l1 m1] Y_{l2 m2}(vec_e)
- * with w_e as in oracle_conv_f64.  msg is [E, C, K] float64, overwritten. */
+ * with w_e as in oracle_conv_f64.  msg is [E, C, K] float64, overwritten.
+ * Returns 2 (msg all zero) if a source index is out of range. */
 int oracle_messages_f64(int64_t N, int64_t E, int lmax, int C, int path_set, int weight_mode, double r_cut,
                         int n_basis, const double* vec, const int32_t* src, const double* x, const double* w,
                         double* msg) {
@@ -353,60 +422,24 @@ int oracle_messages_f64(int64_t N, int64_t E, int lmax, int C, int path_set, int
   if (weight_mode != 0 && weight_mode != 1) return 1;
   if (weight_mode == 1 && (n_basis <= 0 || n_basis > 64 || !(r_cut > 0.0))) return 1;
   int K = (lmax + 1) * (lmax + 1);
-  int P = oracle_paths(lmax, path_set, NULL);
-  if (P <= 0) return 1;
-  int32_t* paths = (int32_t*)malloc(sizeof(int32_t) * 3 * P);
-  oracle_paths(lmax, path_set, paths);
-  double** cg = (double**)malloc(sizeof(double*) * P);
-  for (int p = 0; p < P; ++p) {
-    int l1 = paths[3 * p], l2 = paths[3 * p + 1], l3 = paths[3 * p + 2];
-    cg[p] = (double*)malloc(sizeof(double) * (2 * l1 + 1) * (2 * l2 + 1) * (2 * l3 + 1));
-    oracle_cg_real(l1, l2, l3, cg[p], NULL);
-  }
   for (int64_t i = 0; i < E * C * K; ++i) msg[i] = 0.0;
-  double* Y = (double*)malloc(sizeof(double) * K);
-  double* we = (double*)malloc(sizeof(double) * P * C);
-  double R[64];
-  int rc = 0;
-  for (int64_t e = 0; e < E; ++e) {
-    int64_t s = src[e];
-    if (s < 0 || s >= N) {
-      rc = 2;
-      break;
-    }
-    double vx = vec[3 * e], vy = vec[3 * e + 1], vz = vec[3 * e + 2];
-    real_sh(lmax, vx, vy, vz, Y);
-    if (weight_mode == 0) {
-      for (int i = 0; i < P * C; ++i) we[i] = w[i];
-    } else {
-      double r = sqrt(vx * vx + vy * vy + vz * vz);
-      oracle_radial_basis(r, r_cut, n_basis, R);
-      for (int i = 0; i < P * C; ++i) {
-        double acc = 0.0;
-        for (int n = 0; n < n_basis; ++n) acc += R[n] * w[(int64_t)n * P * C + i];
-        we[i] = acc;
-      }
-    }
-    for (int p = 0; p < P; ++p) {
-      int l1 = paths[3 * p], l2 = paths[3 * p + 1], l3 = paths[3 * p + 2];
-      int n1 = 2 * l1 + 1, n2 = 2 * l2 + 1, n3 = 2 * l3 + 1;
-      for (int a = 0; a < n1; ++a)
-        for (int b = 0; b < n2; ++b)
-          for (int c3 = 0; c3 < n3; ++c3) {
-            double coef = cg[p][(a * n2 + b) * n3 + c3];
-            if (coef == 0.0) continue;
-            double cy = coef * Y[l2 * l2 + b];
-            for (int ch = 0; ch < C; ++ch)
-              msg[(e * C + ch) * K + l3 * l3 + c3] += we[p * C + ch] * cy * x[(s * C + ch) * K + l1 * l1 + a];
-          }
-    }
+  for (int64_t e = 0; e < E; ++e)
+    if (src[e] < 0 || src[e] >= N) return 2;
+  path_blocks pb;
+  if (path_blocks_make(lmax, path_set, &pb)) return 1;
+  int P = pb.P;
+#pragma omp parallel num_threads(oracle_num_threads())
+  {
+    double* Y = (double*)malloc(sizeof(double) * K);
+    double* we = (double*)malloc(sizeof(double) * P * C);
+#pragma omp for schedule(dynamic, 256)
+    for (int64_t e = 0; e < E; ++e)
+      edge_message_add(&pb, lmax, C, weight_mode, r_cut, n_basis, vec, e, src[e], x, w, Y, we, msg + e * C * K);
+    free(Y);
+    free(we);
   }
-  free(Y);
-  free(we);
-  for (int p = 0; p < P; ++p) free(cg[p]);
-  free(cg);
-  free(paths);
-  return rc;
+  path_blocks_free(&pb);
+  return 0;
 }
 
 int oracle_messages(int64_t N, int64_t E, int lmax, int C, int path_set, int weight_mode, double r_cut,
@@ -677,6 +710,7 @@ float oracle_round_bf16(float f) { return round_bf16(f); }
 int oracle_linear_f64(int64_t N, int C, int lmax, const double* h, const double* W, double* out) {
   if (lmax < 0 || lmax > OR_MAX_L || C <= 0 || N < 0) return 1;
   int K = (lmax + 1) * (lmax + 1);
+#pragma omp parallel for schedule(static) num_threads(oracle_num_threads())
   for (int64_t n = 0; n < N; ++n)
     for (int l = 0; l <= lmax; ++l)
       for (int mu = l * l; mu < (l + 1) * (l + 1); ++mu)
@@ -695,6 +729,7 @@ int oracle_linear_f64(int64_t N, int C, int lmax, const double* h, const double*
 int oracle_linear(int64_t N, int C, int lmax, int bf16, const float* h, const float* W, double* out) {
   if (lmax < 0 || lmax > OR_MAX_L || C <= 0 || N < 0) return 1;
   int K = (lmax + 1) * (lmax + 1);
+#pragma omp parallel for schedule(static) num_threads(oracle_num_threads())
   for (int64_t n = 0; n < N; ++n)
     for (int l = 0; l <= lmax; ++l)
       for (int mu = l * l; mu < (l + 1) * (l + 1); ++mu)

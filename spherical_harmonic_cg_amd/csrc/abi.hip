@@ -223,7 +223,7 @@ int eqtp_conv_backward(const eqtp_conv_desc* d, int64_t N, int64_t E, const floa
   if (grad_x && !aligned16(grad_x)) return EQTP_EINVAL;
   if ((grad_w && !aligned4(grad_w)) || (grad_vec && !aligned4(grad_vec))) return EQTP_EINVAL;
   if (!weights || !aligned4(weights)) return EQTP_EINVAL;
-  if (N > 0 && (!x || !grad_out || !aligned4(x) || !aligned4(grad_out))) return EQTP_EINVAL;
+  if (N > 0 && (!x || !grad_out || !aligned16(x) || !aligned16(grad_out))) return EQTP_EINVAL;
   if (E > 0) {
     if (!vec || !src || !aligned4(vec) || !aligned4(src)) return EQTP_EINVAL;
     if (d->edge_order == EQTP_EDGES_UNSORTED && (!dst || !aligned4(dst))) return EQTP_EINVAL;

@@ -182,9 +182,9 @@ __global__ __launch_bounds__(BwdCfg<C>::THREADS) void conv_bwd_kernel(
   auto fetch = [&](int e, bool valid, int e_alt) {
     EdgeIn in;
     const int ec = valid ? e : e_alt;
-    in.vx = vec[3 * ec];
-    in.vy = vec[3 * ec + 1];
-    in.vz = vec[3 * ec + 2];
+    in.vx = vec[3 * (size_t)ec];
+    in.vy = vec[3 * (size_t)ec + 1];
+    in.vz = vec[3 * (size_t)ec + 2];
     in.s = clamp_index(src[ec], N);
 #pragma unroll
     for (int j = 0; j < Cfg::CPL; ++j)
@@ -418,7 +418,7 @@ __global__ __launch_bounds__(64) void gvec_node_kernel(int N, int E, const int* 
       // stage the chunk: lane i = edge cb + i
       const bool mine = lane < cnt;
       const int em = mine ? cb + lane : cb;
-      const float vx = vec[3 * em], vy = vec[3 * em + 1], vz = vec[3 * em + 2];
+      const float vx = vec[3 * (size_t)em], vy = vec[3 * (size_t)em + 1], vz = vec[3 * (size_t)em + 2];
       sstg[lane] = mine ? clamp_index(src[em], N) : -1;
       f4 acc[4];
 #pragma unroll

@@ -48,7 +48,7 @@ struct EdgeMsg {
                                              const int* __restrict__ src, const float* __restrict__ x,
                                              const float* __restrict__ w, const float (&wreg)[Cfg::CPL][T::P],
                                              float inv_rc, float (&acc)[Cfg::CPL][K]) {
-    const float vx = vec[3 * e], vy = vec[3 * e + 1], vz = vec[3 * e + 2];
+    const float vx = vec[3 * (size_t)e], vy = vec[3 * (size_t)e + 1], vz = vec[3 * (size_t)e + 2];
     const int s = clamp_index(src[e], N);
     float Y[16];
     sh_eval<L>(vx, vy, vz, Y);

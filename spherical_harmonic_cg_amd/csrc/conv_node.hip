@@ -14,18 +14,20 @@
 // once per node instead of once per edge, with the coefficients folded into
 // the instruction stream.  Messages never exist in memory.
 //
-// Work decomposition (one workgroup per destination row):
-//   * NW = max(1, C/16) waves; wave w accumulates G for channels 16w..16w+15.
+// Work decomposition: a task is (destination row, block of 16 channels), run by
+// one independent wavefront (a one-wave workgroup); persistent wavefronts walk
+// the task list with a stride that keeps each wave on one channel block.
 //   * The row's edges are staged 64 at a time: lane i loads edge i's vector
-//     and source index (coalesced), evaluates its harmonics and writes them to
-//     the wave's LDS staging area.
+//     and source (coalesced), evaluates its harmonics and writes them, and the
+//     byte offset of the source's channel block, to the wave's LDS.
 //   * Each 4-edge step: lane l feeds A = Y[edge l/16][mu2 = l%16] and, for
-//     each mu1, B = x[src(edge l/16), channel 16w + l%16, mu1] from one
-//     contiguous K-float load per lane.
-//   * After the row, G goes to LDS; every wave then contracts one group of
-//     output components for C lanes = C channels, reading G rows with an odd
-//     stride (no bank conflicts), and the output tile is stored coalesced.
-//
+//     each mu1, B = x[src, channel, mu1] from four 16-byte loads per lane
+//     (16 lanes cover 4 channels x 16 components = 256 contiguous bytes per
+//     edge and load); two steps of loads are kept in flight.
+//   * After the row, G goes to LDS (rows laid out so that the stores are free
+//     of bank conflicts) and lanes 0..15 (= channels) run the whole coupling
+//     with the coefficients as instruction immediates, then store their
+//     64-byte output rows.
 // The same kernel gives the gradients with respect to x and w (TR = true).
 // For L = sum gout * out, with the edges grouped by source node s:
 //   H_s[c,mu3,mu2]  = sum_{e: src_e = s} gout[dst_e,c,mu3] * Y_mu2(vec_e)
@@ -78,7 +80,11 @@ struct NodeCfg {
   static constexpr int GS = ((K * K + 3) / 4 * 4) % 32 == 4 ? (K * K + 3) / 4 * 4
                                                           : ((K * K + 3) / 4 * 4 + 31) / 32 * 32 + 4;
   static constexpr int SLICE = CW * GS;                  // G slice (floats)
-  static constexpr int STG = 64 * 16 + 64;               // staging: Y[64][16] + src[64]
+  static constexpr int YS = 20;                          // staged Y row stride: 16-byte rows on distinct banks
+  static constexpr int STG = 64 * YS + 64;               // staging: Y[64][YS] + src[64]
+  // G row of feature component mu1 (K = 16): rows mu1 and mu1 + 4 on opposite bank halves, so that the
+  // 16-byte stores of 8 consecutive lanes (4 channels x 2 component groups) hit distinct banks
+  static constexpr int grow(int mu1) { return K == 16 ? (mu1 ^ ((mu1 >> 2) & 1)) : mu1; }
   static constexpr int LDS = SLICE > STG ? SLICE : STG;  // staging and G share the wave's LDS
   static constexpr int THREADS = kWave;                  // one independent wavefront per workgroup
   static constexpr int PF = 2;                           // gather steps in flight
@@ -131,9 +137,9 @@ __device__ __forceinline__ void node_tasks(int N, int E, const int* __restrict__
       s = 0;
       if (valid) {
         if (vec != nullptr) {
-          vx = vec[3 * k];
-          vy = vec[3 * k + 1];
-          vz = vec[3 * k + 2];
+          vx = vec[3 * (size_t)k];
+          vy = vec[3 * (size_t)k + 1];
+          vz = vec[3 * (size_t)k + 2];
         }
         s = clamp_index(src[k], N);
       }
@@ -210,7 +216,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void co
 
   const int lane = threadIdx.x & 63;
   float* ystg = lds;
-  int* sstg = reinterpret_cast<int*>(lds + 64 * 16);
+  int* sstg = reinterpret_cast<int*>(lds + 64 * Cfg::YS);
   constexpr uint32_t XS = XB ? 2u : 4u;  // bytes per feature element
   const rsrc_t rx = make_rsrc(xp, (uint64_t)N * C * K * XS);
   const float* const x = static_cast<const float*>(xp);
@@ -247,8 +253,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void co
     }
   };
 
-  const int cl = lane & 15;  // MFMA column = channel within the block
+  const int cl = lane & 15;  // MFMA column
   const bool c_ok = cl < Cfg::CW;
+  // fp32 features in one buffer resource, 16 components, 16-channel blocks: the staging keeps each edge's
+  // gather offset (bytes of its source's channel block) instead of its source index
+  constexpr bool kOffsets = BUF && !XB && K == 16 && Cfg::CW == 16;
 
   f4 acc[K];
 #pragma unroll
@@ -268,16 +277,19 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void co
     float Y[16];
     sh_eval<L>(vx, vy, vz, Y);
     const float m = valid ? 1.0f : 0.0f;  // padding slots contribute nothing
-    f4* yd = reinterpret_cast<f4*>(ystg + lane * 16);
+    f4* yd = reinterpret_cast<f4*>(ystg + lane * Cfg::YS);
 #pragma unroll
     for (int q = 0; q < 4; ++q) yd[q] = f4{m * Y[4 * q], m * Y[4 * q + 1], m * Y[4 * q + 2], m * Y[4 * q + 3]};
-    sstg[lane] = valid ? s : -1;  // -1: the slot's gather reads nothing
+    if constexpr (kOffsets)
+      sstg[lane] = valid ? (int)(((uint32_t)s * C + c_base) * K * 4u) : (int)0xFFFFF000u;  // byte offset or out of range
+    else
+      sstg[lane] = valid ? s : -1;  // -1: the slot's gather reads nothing
   };
 
   // B operand columns.  K = 16: column n = lane%16 stands for (channel
-  // 4j + n/4, components 4(n%4)..4(n%4)+3) of channel group j, so one 16-byte
+  // 4j + n%4, components 4(n/4)..4(n/4)+3) of channel group j, so one 16-byte
   // load per lane and j reads 256 contiguous bytes per edge (4 channels x 16
-  // components); MFMA (j, q) then accumulates G[4j + n/4][4(n%4) + q][mu2].
+  // components); MFMA (j, q) then accumulates G[4j + n%4][4(n/4) + q][mu2].
   // Other K: column n = channel n, one MFMA per component.
   struct StepData {
     float a;
@@ -285,15 +297,28 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void co
   };
   auto load = [&](int el, bool live) {
     StepData d;
+    if constexpr (kOffsets) {
+      const uint32_t o = (live ? (uint32_t)sstg[el] : 0xFFFFF000u) + (uint32_t)(((cl & 3) * K + 4 * (cl >> 2)) * 4);
+      d.a = ystg[el * Cfg::YS + cl];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f4 t = buf_f4(rx, o + (uint32_t)(j * 4 * K * 4));
+        d.xv[4 * j] = t[0];
+        d.xv[4 * j + 1] = t[1];
+        d.xv[4 * j + 2] = t[2];
+        d.xv[4 * j + 3] = t[3];
+      }
+      return d;
+    }
     const int s = sstg[el];
     const bool ok = live && s >= 0;
-    d.a = live ? ystg[el * 16 + cl] : 0.0f;
+    d.a = live ? ystg[el * Cfg::YS + cl] : 0.0f;
     if constexpr (K == 16) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int cw = 4 * j + (cl >> 2);
+        const int cw = 4 * j + (cl & 3);
         const bool v = ok && cw < Cfg::CW;
-        const f4 t = ld4(v ? ((size_t)s * C + c_base + cw) * K + 4 * (cl & 3) : 0, v);
+        const f4 t = ld4(v ? ((size_t)s * C + c_base + cw) * K + 4 * (cl >> 2) : 0, v);
         d.xv[4 * j] = t[0];
         d.xv[4 * j + 1] = t[1];
         d.xv[4 * j + 2] = t[2];
@@ -326,17 +351,17 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void co
   auto task_end = [&](int row, int blk) {
     // G[c][mu1][mu2] -> LDS (over the staging area), one 16-byte store per
     // accumulator: lane (cl, kq) holds mu2 = 4 kq + v of
-    //   K = 16: acc[4j + q] -> channel 4j + cl/4, mu1 = 4(cl%4) + q;
+    //   K = 16: acc[4j + q] -> channel 4j + cl%4, mu1 = 4(cl/4) + q (row grow(mu1));
     //   else:   acc[k]      -> channel cl, mu1 = k.
     if constexpr (K == 16) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int cw = 4 * j + (cl >> 2);
+        const int cw = 4 * j + (cl & 3);
         if (cw < Cfg::CW) {
           float* gc = lds + cw * Cfg::GS;
 #pragma unroll
           for (int q = 0; q < 4; ++q)
-            *reinterpret_cast<f4*>(gc + (4 * (cl & 3) + q) * K + 4 * (lane >> 4)) = acc[4 * j + q];
+            *reinterpret_cast<f4*>(gc + Cfg::grow(4 * (cl >> 2) + q) * K + 4 * (lane >> 4)) = acc[4 * j + q];
         }
       }
     } else if (c_ok) {
@@ -395,7 +420,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void co
         constexpr eqtp_gen::CgTerm tm = T::by_out[i];
         constexpr bool first = (i == 0) || T::by_out[i - 1].p != tm.p || T::by_out[i - 1].mu3 != tm.mu3;
         constexpr bool last = (i + 1 == T::NT) || T::by_out[i + 1].p != tm.p || T::by_out[i + 1].mu3 != tm.mu3;
-        const float g = gc[tm.mu1 * K + tm.mu2];
+        const float g = gc[Cfg::grow(tm.mu1) * K + tm.mu2];
         t = first ? tm.c * g : fmaf(tm.c, g, t);
         if constexpr (last) {
           ov[tm.mu3] = fmaf(wr[tm.p], t, ov[tm.mu3]);
@@ -445,18 +470,18 @@ __global__ __launch_bounds__(64) void probe_node_kernel(int N, int E, const int*
   __shared__ __attribute__((aligned(16))) float lds[Cfg::LDS];
   const int lane = threadIdx.x & 63;
   float* ystg = lds;
-  int* sstg = reinterpret_cast<int*>(lds + 64 * 16);
+  int* sstg = reinterpret_cast<int*>(lds + 64 * Cfg::YS);
   int cnt_acc = 0;
   long long sum_acc = 0;
   auto stage = [&](bool valid, float, float, float, int s) {
-    ystg[lane * 16] = valid ? 1.0f : 0.0f;  // the "harmonic" flags real slots
+    ystg[lane * Cfg::YS] = valid ? 1.0f : 0.0f;  // the "harmonic" flags real slots
     sstg[lane] = s;
   };
   struct StepData {
     bool real;
     int s;
   };
-  auto load = [&](int el, bool live) { return StepData{live && ystg[el * 16] != 0.0f, sstg[el]}; };
+  auto load = [&](int el, bool live) { return StepData{live && ystg[el * Cfg::YS] != 0.0f, sstg[el]}; };
   auto compute = [&](const StepData& d) {
     if ((lane & 15) == 0 && d.real) {
       cnt_acc += 1;

@@ -231,7 +231,7 @@ struct So2Msg {
   __device__ __forceinline__ static void run(int e, int N, int cl, const float* __restrict__ vec,
                                              const int* __restrict__ src, const float* __restrict__ x,
                                              const float* wl, float (&acc)[Cfg::CPL][K]) {
-    const float vx = vec[3 * e], vy = vec[3 * e + 1], vz = vec[3 * e + 2];
+    const float vx = vec[3 * (size_t)e], vy = vec[3 * (size_t)e + 1], vz = vec[3 * (size_t)e + 2];
     const int s = clamp_index(src[e], N);
     // edge frame: cos/sin of phi and theta (identity for a zero vector or
     // along the z axis, where phi is free)
@@ -539,9 +539,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PS == 0 ? 3
     float ax = 0.0f, ay = 0.0f, az = 0.0f;
     int sa = 0;
     if (ea < e_end) {
-      ax = vec[3 * ea];
-      ay = vec[3 * ea + 1];
-      az = vec[3 * ea + 2];
+      ax = vec[3 * (size_t)ea];
+      ay = vec[3 * (size_t)ea + 1];
+      az = vec[3 * (size_t)ea + 2];
       sa = clamp_index(src[ea], N);
       float R[NB];
       radial_basis<NB>(sqrtf(ax * ax + ay * ay + az * az), inv_rc, R);

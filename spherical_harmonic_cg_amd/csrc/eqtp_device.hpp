@@ -58,35 +58,6 @@ __device__ __forceinline__ void static_for(F&& f) {
   if constexpr (E > B) static_for_impl<B>(static_cast<F&&>(f), std::make_integer_sequence<int, E - B>{});
 }
 
-// Contiguous split of the by_out term list into NG groups of whole output
-// components with roughly equal term counts (groups may be empty when NG > K).
-// Returns the first mu3 of group g (g >= NG gives K).
-template <int L, int PS>
-__host__ __device__ constexpr int group_mu3_begin(int NG, int g) {
-  using T = Tables<L, PS>;
-  constexpr int K = num_comp(L);
-  if (g <= 0) return 0;
-  if (g >= NG) return K;
-  int counts[16] = {};
-  for (int i = 0; i < T::NT; ++i) counts[T::by_out[i].mu3]++;
-  const int target = (T::NT * g + NG / 2) / NG;
-  int cum = 0, mu = 0;
-  while (mu < K && cum + counts[mu] / 2 < target) {
-    cum += counts[mu];
-    ++mu;
-  }
-  return mu;
-}
-
-// First by_out term index with mu3 >= mu.
-template <int L, int PS>
-__host__ __device__ constexpr int term_begin_for_mu3(int mu) {
-  using T = Tables<L, PS>;
-  int i = 0;
-  while (i < T::NT && T::by_out[i].mu3 < mu) ++i;
-  return i;
-}
-
 // ---------------------------------------------------------------------------
 // Real spherical harmonics for l <= L of an (unnormalised) edge vector,
 // components in the page order (l0, l1c, l1s, l2c, l2s, ...).  The vector is

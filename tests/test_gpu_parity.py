@@ -57,8 +57,10 @@ def _wl(name):
     return synth.make_config(name)
 
 
-@functools.lru_cache(maxsize=None)
+@functools.lru_cache(maxsize=2)
 def _oracle_full(name):
+    """The oracle over every destination row of the workload (its rows shared out over the host's
+    threads; the result does not depend on the thread count)."""
     wl = _wl(name)
     return oracle.conv(wl.N, wl.vec, wl.src, wl.dst, wl.x, wl.weights, wl.lmax, path_set=wl.path_set,
                        weight_mode=wl.weight_mode, r_cut=wl.r_cut)
@@ -75,26 +77,6 @@ def _run_conv(eq, wl, g, algo, unsorted=False, perm=None):
         vec, src, dst = perm
         return eq.eqtp_conv_fused(_t(vec), _t(src), g["x"], g["w"], dst=_t(dst), **kw)
     return eq.eqtp_conv_fused(g["vec"], g["src"], g["x"], g["w"], row_ptr=g["row_ptr"], **kw)
-
-
-def _oracle_rows(wl, rows):
-    """Oracle output for the given destination rows only (edges of those rows)."""
-    rows = np.asarray(sorted(rows))
-    sel = np.concatenate([np.arange(wl.row_ptr[r], wl.row_ptr[r + 1]) for r in rows])
-    remap = {r: i for i, r in enumerate(rows)}
-    dst = np.array([remap[d] for d in wl.dst[sel]], dtype=np.int32)
-    # keep all source nodes; only the selected rows receive messages
-    out = oracle.conv(wl.N, wl.vec[sel], wl.src[sel], dst, wl.x, wl.weights, wl.lmax, path_set=wl.path_set,
-                      weight_mode=wl.weight_mode, r_cut=wl.r_cut)
-    return out[:len(rows)]
-
-
-def _sample_rows(wl, n, seed=7):
-    rng = np.random.default_rng(seed)
-    deg = np.diff(wl.row_ptr)
-    rows = set(rng.choice(wl.N, size=n, replace=False).tolist())
-    rows |= {0, wl.N - 1, int(np.argmax(deg)), int(np.argmin(deg))}
-    return sorted(rows)
 
 
 # ----------------------------------------------------------------------------
@@ -159,37 +141,48 @@ def test_conv_unsorted_full(name):
     _assert_close(out, _oracle_full(name), what="conv unsorted " + name)
 
 
-def test_conv_large_sorted_and_unsorted_sampled():
-    """Large workload (100k atoms, 5.2M edges): full GPU outputs, oracle on
-    sampled rows (including the longest and shortest)."""
+def test_conv_large_sorted_full():
+    """Large workload (100k atoms, 5.2M edges, C = 32), dst-sorted edges through the
+    node kernel: the whole output tensor against the oracle over every row."""
     eq = _eq()
     wl = _wl("large")
     g = _gpu_inputs(wl)
-    rows = _sample_rows(wl, 150)
-    ref = _oracle_rows(wl, rows)
     _say("conv large sorted node E=%d" % wl.E)
     out = _np(_run_conv(eq, wl, g, 0))
-    _assert_close(out[rows], ref, what="large sorted")
+    _assert_close(out, _oracle_full("large"), what="large sorted")
+
+
+def test_conv_large_unsorted_full():
+    """Large workload with the edges in a seeded random order (fp32 atomics): the whole output
+    tensor against the oracle."""
+    eq = _eq()
+    wl = _wl("large")
+    g = _gpu_inputs(wl)
     _say("conv large unsorted (atomic) E=%d" % wl.E)
     outu = _np(_run_conv(eq, wl, g, 0, unsorted=True, perm=synth.random_permutation(wl)))
-    _assert_close(outu[rows], ref, what="large atomic")
-    # the two complete outputs agree everywhere to the same bar
-    _assert_close(outu, out.astype(np.float64), tol=5e-4, what="large atomic vs sorted")
+    _assert_close(outu, _oracle_full("large"), what="large atomic")
 
 
-def test_conv_radial_sampled():
-    """Radial workload (50k atoms, C=128, per-edge radial weights)."""
+def test_conv_radial_sorted_full():
+    """Radial workload (50k atoms, C = 128, per-edge radial weights), dst-sorted edges through the
+    edge-aligned kernel with the radial products on the matrix cores: the whole output tensor."""
     eq = _eq()
     wl = _wl("radial")
     g = _gpu_inputs(wl)
-    rows = _sample_rows(wl, 60)
-    ref = _oracle_rows(wl, rows)
     _say("conv radial sorted E=%d" % wl.E)
     out = _np(_run_conv(eq, wl, g, 0))
-    _assert_close(out[rows], ref, what="radial sorted")
+    _assert_close(out, _oracle_full("radial"), what="radial sorted")
+
+
+def test_conv_radial_unsorted_full():
+    """Radial workload with the edges in a seeded random order (per-edge walk, fp32 atomics): the
+    whole output tensor."""
+    eq = _eq()
+    wl = _wl("radial")
+    g = _gpu_inputs(wl)
     _say("conv radial unsorted E=%d" % wl.E)
     outu = _np(_run_conv(eq, wl, g, 0, unsorted=True, perm=synth.random_permutation(wl)))
-    _assert_close(outu[rows], ref, what="radial atomic")
+    _assert_close(outu, _oracle_full("radial"), what="radial atomic")
 
 
 # ----------------------------------------------------------------------------

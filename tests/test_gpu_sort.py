@@ -14,7 +14,7 @@ import pytest
 
 import oracle
 from spherical_harmonic_cg_amd import synth
-from test_gpu_parity import TOL, _assert_close, _eq, _np, _oracle_rows, _sample_rows, _say, _t, _wl
+from test_gpu_parity import TOL, _assert_close, _eq, _np, _oracle_full, _say, _t, _wl
 
 pytestmark = pytest.mark.gpu
 
@@ -109,7 +109,7 @@ def test_sort_then_conv_small(lmax, ps, C):
 
 @pytest.mark.parametrize("name", ["mid", "large"])
 def test_sort_then_conv_workload(name):
-    """Full-size workloads in random edge order: sort exact, conv on sampled rows."""
+    """Full-size workloads in random edge order: sort exact, conv on every row against the oracle."""
     eq = _eq()
     wl = _wl(name)
     pvec, psrc, pdst = synth.random_permutation(wl)
@@ -118,5 +118,4 @@ def test_sort_then_conv_workload(name):
     assert np.array_equal(rp, wl.row_ptr)
     out = _np(eq.eqtp_conv_fused(vs, ss, _t(wl.x), _t(wl.weights), wl.lmax, row_ptr=_t(rp), path_set=wl.path_set,
                                  weight_mode=wl.weight_mode, r_cut=wl.r_cut))
-    rows = _sample_rows(wl, 60)
-    _assert_close(out[rows], _oracle_rows(wl, rows), TOL, name + " sort+conv")
+    _assert_close(out, _oracle_full(name), TOL, name + " sort+conv")
