@@ -75,9 +75,12 @@ extern "C" {
                                  rotate back; vector ALUs; fixed weights, fp32 features; lmax 0..6
                                  (C = 128 up to lmax 4).  Same result as the coupling form. */
 
-/* operand precision of the channel linear */
-#define EQTP_F32 0
-#define EQTP_BF16 1
+/* element types: node features (eqtp_conv_desc.x_dtype) and the channel
+   linear's operands (eqtp_linear's dtype) */
+#define EQTP_F32 0      /* fp32 in memory, fp32 arithmetic */
+#define EQTP_BF16 1     /* bfloat16 in memory */
+#define EQTP_F32_BF16 2 /* eqtp_linear only: fp32 in memory, rounded to bfloat16 (nearest even) for the
+                           matrix-core products */
 
 /*
  * Number of coupling paths P for (lmax, path_set), or a negative status.
@@ -269,19 +272,29 @@ int eqtp_sort_edges(int64_t N, int64_t E, const int32_t* dst, const float* vec, 
                     int32_t* perm, float* vec_sorted, int32_t* src_sorted, void* stream);
 
 /*
- * Per-l channel linear (channel mixing inside each irrep, no bias):
+ * Per-l channel linear (channel mixing inside each irrep, no bias), the
+ * channel-wise mixing that follows the convolution: the Batmobile page names
+ * no such layer; its form (a C x C matrix per degree l, applied to every m of
+ * that degree, "bf16 in, fp32 accumulate" on the matrix cores) is this
+ * library's reading of the workload it is measured on.
  *   out[n, c', l m] = sum_c W[l, c', c] h[n, c, l m]
- *   h    [N, C, K] fp32, 16-byte aligned.
- *   W    [lmax+1, C, C] fp32 (output-channel major), 16-byte aligned.
- *   out  [N, C, K] fp32, 16-byte aligned, fully overwritten; no aliasing.
- *   dtype EQTP_F32: fp32 matrix-core products; EQTP_BF16: h and W are
- *   rounded to bfloat16 (nearest even) on load and the products are
- *   accumulated in fp32 on the bf16 matrix cores.
- *   C in {8, 16, 32, 64, 128}, lmax in [0, 6], 0 <= N < 2^31 (lmax 4..6: a
- *   4-node tile, 2 at C = 128, with the (node, m) pairs of one degree as
- *   matrix-core columns).
+ *   dtype    EQTP_F32:      h, W fp32; fp32 matrix-core products.
+ *            EQTP_BF16:     h, W bfloat16 in memory; bf16 matrix-core products,
+ *                           fp32 accumulation.
+ *            EQTP_F32_BF16: h, W fp32 in memory, each value rounded to bf16
+ *                           (nearest even) as it is loaded; bf16 products,
+ *                           fp32 accumulation (for an fp32 h straight from
+ *                           eqtp_conv_fused).
+ *   h    [N, C, K] in the dtype's storage type, 16-byte aligned (read only).
+ *   W    [lmax+1, C, C] (output-channel major) in the same storage type,
+ *        16-byte aligned (read only).
+ *   out  [N, C, K] fp32, 16-byte aligned, fully overwritten; must not alias
+ *        h or W.
+ *   C in {8, 16, 32, 64, 128}, lmax in [0, 6], 0 <= N < 2^31.  Caller-owned
+ *   device buffers; asynchronous on stream; deterministic.  EQTP_EINVAL for
+ *   bad sizes, enums, NULL or misaligned pointers (before any launch).
  */
-int eqtp_linear(int64_t N, int C, int lmax, int dtype, const float* h, const float* W, float* out, void* stream);
+int eqtp_linear(int64_t N, int C, int lmax, int dtype, const void* h, const void* W, float* out, void* stream);
 
 /* Static description of a status code (never NULL). */
 const char* eqtp_status_string(int status);

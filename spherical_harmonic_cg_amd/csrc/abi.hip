@@ -312,13 +312,14 @@ int eqtp_sort_edges(int64_t N, int64_t E, const int32_t* dst, const float* vec, 
                                            (hipStream_t)stream));
 }
 
-int eqtp_linear(int64_t N, int C, int lmax, int dtype, const float* h, const float* W, float* out, void* stream) {
+int eqtp_linear(int64_t N, int C, int lmax, int dtype, const void* h, const void* W, float* out, void* stream) {
   if (lmax < 0 || C <= 0 || N < 0 || N > kMaxIndex) return EQTP_EINVAL;
   if (lmax > eqtp::kSo2MaxL || !valid_c(C)) return EQTP_EUNSUPPORTED;
-  if (dtype != EQTP_F32 && dtype != EQTP_BF16) return EQTP_EINVAL;
+  if (dtype != EQTP_F32 && dtype != EQTP_BF16 && dtype != EQTP_F32_BF16) return EQTP_EINVAL;
   if (N == 0) return EQTP_OK;
   if (!h || !W || !out || !aligned16(h) || !aligned16(W) || !aligned16(out)) return EQTP_EINVAL;
-  return status_of(eqtp::launch_linear(N, C, lmax, dtype == EQTP_BF16, h, W, out, (hipStream_t)stream));
+  const int mode = dtype == EQTP_F32 ? 0 : (dtype == EQTP_BF16 ? 1 : 2);
+  return status_of(eqtp::launch_linear(N, C, lmax, mode, h, W, out, (hipStream_t)stream));
 }
 
 const char* eqtp_status_string(int status) {

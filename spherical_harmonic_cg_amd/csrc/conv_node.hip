@@ -507,7 +507,7 @@ __global__ __launch_bounds__(64) void probe_node_kernel(int N, int E, const int*
 // compute units of the current device, queried once per device (launches are
 // on the host's hot path for small graphs); racing first queries store the
 // same value
-static int num_cus() {
+int num_cus() {
   static std::atomic<int> cached[64];
   int dev = 0, n = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 256;

@@ -57,8 +57,11 @@ hipError_t launch_conv_edge(const ConvArgs& a);   // any order / weights, vector
 hipError_t launch_conv_messages(const ConvArgs& a);  // per-edge messages into out [E, C, K]
 hipError_t launch_probe_node(const ProbeArgs& a);
 hipError_t launch_probe_edge(const ProbeArgs& a);
-hipError_t launch_linear(int64_t N, int C, int lmax, int bf16, const float* h, const float* W, float* out,
+// mode 0: fp32 storage and products; 1: bf16 storage and products; 2: fp32 storage, bf16 products
+hipError_t launch_linear(int64_t N, int C, int lmax, int mode, const void* h, const void* W, float* out,
                          hipStream_t stream);
+// compute units of the current device (cached per device)
+int num_cus();
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t stream);
 hipError_t launch_conv_backward(const BwdArgs& a);   // fixed weights, vector ALUs
 // edge-aligned (SO(2)) form, lmax 0..6, fixed fp32 weights; C = 128 only up to kSo2MaxLC128

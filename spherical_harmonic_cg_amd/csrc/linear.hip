@@ -2,20 +2,22 @@
 // on the matrix cores (the one dense contraction of the path).
 //
 // A workgroup (4 waves) takes 16 consecutive nodes -- one contiguous
-// 16*C*K-float block of h.  It stages, in the operand type (bf16 or fp32):
+// 16*C*K-element block of h, fp32 or bf16 in memory.  It stages, in the
+// operand type (bf16 or fp32):
 //   * W as [l][c'][c] with rows padded so that the 16-byte operand reads of
 //     16 consecutive rows fall in distinct LDS banks (when it fits in LDS;
 //     otherwise the A operands are read from global memory, L2-resident);
 //   * the h tile transposed to [m][node][c] (two channels per thread, plane
 //     stride padded to spread the m-planes of a store over banks).
 // Work units are (4 consecutive components m, 16 output channels); for each,
-// the 16x16 tiles D[c'][node] come from v_mfma_f32_16x16x32_bf16 (bf16 mode:
-// operands rounded to nearest-even bf16 when staged, fp32 accumulation) or
-// v_mfma_f32_16x16x4_f32 (fp32 mode).  Lane (i, k) holds D[c'0+4k+v][node i]
-// for the four m of the unit, i.e. out[node i][c'][m..m+3].  When every wave
-// is done, the (dead) input staging is reused as the fp32 output tile in the
-// global layout and the tile leaves with coalesced 16-byte stores.  Bytes per
-// node: 8 C K (h once, out once); flops 2 C^2 K: bound by HBM bandwidth.
+// the 16x16 tiles D[c'][node] come from v_mfma_f32_16x16x32_bf16 (bf16
+// products: operands held as bf16 in memory, or fp32 rounded to nearest-even
+// bf16 when staged; fp32 accumulation) or v_mfma_f32_16x16x4_f32 (fp32 mode).
+// Lane (i, k) holds D[c'0+4k+v][node i] for the four m of the unit, i.e.
+// out[node i][c'][m..m+3].  When every wave is done, the (dead) input staging
+// is reused as the fp32 output tile in the global layout and the tile leaves
+// with coalesced 16-byte stores.  Bytes per node: C K (h once, 4 or 2 bytes
+// each) + 4 C K (out once); flops 2 C^2 K: bound by HBM bandwidth.
 #include "eqtp_device.hpp"
 #include "eqtp_kernels.hpp"
 
@@ -64,6 +66,15 @@ struct LinCfg {
   static_assert(C % 8 == 0, "channels must be a multiple of 8");
 };
 
+// 4 consecutive stored elements widened to fp32 (one 16-byte or 8-byte load; a bf16 value is the upper
+// half of the fp32 with the same bits)
+__device__ __forceinline__ f4 ld4s(const float* p) { return *reinterpret_cast<const f4*>(p); }
+__device__ __forceinline__ f4 ld4s(const __bf16* p) {
+  const uint2 t = *reinterpret_cast<const uint2*>(p);
+  return f4{__uint_as_float(t.x << 16), __uint_as_float(t.x & 0xffff0000u), __uint_as_float(t.y << 16),
+            __uint_as_float(t.y & 0xffff0000u)};
+}
+
 __device__ __forceinline__ int l_of(int m) { return m >= 9 ? 3 : (m >= 4 ? 2 : (m >= 1 ? 1 : 0)); }
 
 template <class T>
@@ -73,8 +84,9 @@ __device__ __forceinline__ __bf16 to_op<__bf16>(float f) { return to_bf16(f); }
 template <>
 __device__ __forceinline__ float to_op<float>(float f) { return f; }
 
-template <int L, int C, bool BF16>
-__global__ __launch_bounds__(256) void linear_kernel(int N, const float* __restrict__ h, const float* __restrict__ W,
+// S: the element type of h and W in memory (float or __bf16)
+template <int L, int C, bool BF16, class S>
+__global__ __launch_bounds__(256) void linear_kernel(int N, const S* __restrict__ h, const S* __restrict__ W,
                                                      float* __restrict__ out) {
   using Cfg = LinCfg<L, C, BF16>;
   using Op = typename Cfg::Op;
@@ -104,7 +116,7 @@ __global__ __launch_bounds__(256) void linear_kernel(int N, const float* __restr
 #pragma unroll
   for (int it = 0; it < W_IT; ++it) {
     const int i = tid + it * 256;
-    wbuf[it] = i < WF4 ? reinterpret_cast<const f4*>(W)[i] : f4{0.f, 0.f, 0.f, 0.f};
+    wbuf[it] = i < WF4 ? ld4s(W + 4 * i) : f4{0.f, 0.f, 0.f, 0.f};
   }
 #pragma unroll
   for (int it = 0; it < H_IT; ++it) {
@@ -114,9 +126,9 @@ __global__ __launch_bounds__(256) void linear_kernel(int N, const float* __restr
     const int n = u / ((K / 4 > 0 ? K / 4 : 1) * (C / 2));
     ha[it] = hb[it] = f4{0.f, 0.f, 0.f, 0.f};
     if (u < HU && n < nv) {
-      const float* src = h + base + ((size_t)n * C + 2 * cp) * K + 4 * mq;
-      ha[it] = *reinterpret_cast<const f4*>(src);
-      hb[it] = *reinterpret_cast<const f4*>(src + K);
+      const S* src = h + base + ((size_t)n * C + 2 * cp) * K + 4 * mq;
+      ha[it] = ld4s(src);
+      hb[it] = ld4s(src + K);
     }
   }
 #pragma unroll
@@ -151,7 +163,7 @@ __global__ __launch_bounds__(256) void linear_kernel(int N, const float* __restr
       const int rem = f - n * (C * K);
       const int c = rem / K;
       const int m = rem - c * K;
-      hT[m * Cfg::PLANE + n * RS + c] = to_op<T>(n < nv ? h[base + f] : 0.0f);
+      hT[m * Cfg::PLANE + n * RS + c] = to_op<T>(n < nv ? (float)h[base + f] : 0.0f);
     }
   }
   __syncthreads();
@@ -188,8 +200,8 @@ __global__ __launch_bounds__(256) void linear_kernel(int N, const float* __restr
             if constexpr (Cfg::W_LDS) {
               a8 = *reinterpret_cast<const bf16x8*>(Wl + (l * C + (co_ok ? co : 0)) * RS + cb);
             } else {
-              const float* wr = W + ((size_t)l * C + (co_ok ? co : 0)) * C + cb;
-              const f4 w0 = *reinterpret_cast<const f4*>(wr), w1 = *reinterpret_cast<const f4*>(wr + 4);
+              const S* wr = W + ((size_t)l * C + (co_ok ? co : 0)) * C + cb;
+              const f4 w0 = ld4s(wr), w1 = ld4s(wr + 4);
 #pragma unroll
               for (int j = 0; j < 4; ++j) {
                 a8[j] = to_bf16(w0[j]);
@@ -218,7 +230,7 @@ __global__ __launch_bounds__(256) void linear_kernel(int N, const float* __restr
             b4 = *reinterpret_cast<const f4*>(hrow + cb);
             if (co_ok) {
               if constexpr (Cfg::W_LDS) a4 = *reinterpret_cast<const f4*>(Wl + (l * C + co) * RS + cb);
-              else a4 = *reinterpret_cast<const f4*>(W + ((size_t)l * C + co) * C + cb);
+              else a4 = ld4s(W + ((size_t)l * C + co) * C + cb);
             }
           }
 #pragma unroll
@@ -287,9 +299,9 @@ struct LinColsCfg {
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 };
 
-template <int L, int C, bool BF16>
-__global__ __launch_bounds__(256) void linear_cols_kernel(int N, const float* __restrict__ h,
-                                                          const float* __restrict__ W, float* __restrict__ out) {
+template <int L, int C, bool BF16, class S>
+__global__ __launch_bounds__(256) void linear_cols_kernel(int N, const S* __restrict__ h, const S* __restrict__ W,
+                                                          float* __restrict__ out) {
   using Cfg = LinColsCfg<L, C, BF16>;
   typedef typename Cfg::T T;
   constexpr int K = Cfg::K;
@@ -313,7 +325,7 @@ __global__ __launch_bounds__(256) void linear_cols_kernel(int N, const float* __
     const int rem = f - node * (C * K);
     const int c = rem / K;
     const int m = rem - c * K;
-    hT[(node * K + m) * RS + c] = to_op<T>(node < nv ? h[base + f] : 0.0f);
+    hT[(node * K + m) * RS + c] = to_op<T>(node < nv ? (float)h[base + f] : 0.0f);
   }
   __syncthreads();
 
@@ -348,8 +360,8 @@ __global__ __launch_bounds__(256) void linear_cols_kernel(int N, const float* __
             if (cb < C) {
               if (n_ok) b8 = *reinterpret_cast<const bf16x8*>(hrow + cb);
               if (co_ok) {
-                const float* wr = W + ((size_t)l * C + co) * C + cb;
-                const f4 w0 = *reinterpret_cast<const f4*>(wr), w1 = *reinterpret_cast<const f4*>(wr + 4);
+                const S* wr = W + ((size_t)l * C + co) * C + cb;
+                const f4 w0 = ld4s(wr), w1 = ld4s(wr + 4);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                   a8[j] = to_bf16(w0[j]);
@@ -366,7 +378,7 @@ __global__ __launch_bounds__(256) void linear_cols_kernel(int N, const float* __
             f4 a4 = f4{0.f, 0.f, 0.f, 0.f}, b4 = a4;
             if (cb < C) {
               if (n_ok) b4 = *reinterpret_cast<const f4*>(hrow + cb);
-              if (co_ok) a4 = *reinterpret_cast<const f4*>(W + ((size_t)l * C + co) * C + cb);
+              if (co_ok) a4 = ld4s(W + ((size_t)l * C + co) * C + cb);
             }
 #pragma unroll
             for (int s4 = 0; s4 < 4; ++s4) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[s4], b4[s4], acc, 0, 0, 0);
@@ -394,48 +406,53 @@ __global__ __launch_bounds__(256) void linear_cols_kernel(int N, const float* __
   }
 }
 
-template <int L, int C, bool BF16>
-static hipError_t launch_linear_t(int64_t N, const float* h, const float* W, float* out, hipStream_t stream) {
+template <int L, int C, bool BF16, class S>
+static hipError_t launch_linear_t(int64_t N, const void* h, const void* W, float* out, hipStream_t stream) {
+  const S* hs = static_cast<const S*>(h);
+  const S* ws = static_cast<const S*>(W);
   if constexpr (L <= 3) {
     const unsigned blocks = (unsigned)((N + 15) / 16);
-    hipLaunchKernelGGL((linear_kernel<L, C, BF16>), dim3(blocks), dim3(256), 0, stream, (int)N, h, W, out);
+    hipLaunchKernelGGL((linear_kernel<L, C, BF16, S>), dim3(blocks), dim3(256), 0, stream, (int)N, hs, ws, out);
   } else {
     const unsigned blocks = (unsigned)((N + LinColsCfg<L, C, BF16>::TN - 1) / LinColsCfg<L, C, BF16>::TN);
-    hipLaunchKernelGGL((linear_cols_kernel<L, C, BF16>), dim3(blocks), dim3(256), 0, stream, (int)N, h, W, out);
+    hipLaunchKernelGGL((linear_cols_kernel<L, C, BF16, S>), dim3(blocks), dim3(256), 0, stream, (int)N, hs, ws, out);
   }
   return hipGetLastError();
 }
 
-template <int L, bool BF16>
-static hipError_t dispatch_linear_c(int64_t N, int C, const float* h, const float* W, float* out, hipStream_t s) {
+// mode 0: fp32 storage and products; 1: bf16 storage and products; 2: fp32 storage, bf16 products
+template <int L, int C>
+static hipError_t launch_linear_mode(int64_t N, int mode, const void* h, const void* W, float* out, hipStream_t s) {
+  if (mode == 0) return launch_linear_t<L, C, false, float>(N, h, W, out, s);
+  if (mode == 1) return launch_linear_t<L, C, true, __bf16>(N, h, W, out, s);
+  return launch_linear_t<L, C, true, float>(N, h, W, out, s);
+}
+
+template <int L>
+static hipError_t dispatch_linear_c(int64_t N, int C, int mode, const void* h, const void* W, float* out,
+                                    hipStream_t s) {
   switch (C) {
-    case 8: return launch_linear_t<L, 8, BF16>(N, h, W, out, s);
-    case 16: return launch_linear_t<L, 16, BF16>(N, h, W, out, s);
-    case 32: return launch_linear_t<L, 32, BF16>(N, h, W, out, s);
-    case 64: return launch_linear_t<L, 64, BF16>(N, h, W, out, s);
-    case 128: return launch_linear_t<L, 128, BF16>(N, h, W, out, s);
+    case 8: return launch_linear_mode<L, 8>(N, mode, h, W, out, s);
+    case 16: return launch_linear_mode<L, 16>(N, mode, h, W, out, s);
+    case 32: return launch_linear_mode<L, 32>(N, mode, h, W, out, s);
+    case 64: return launch_linear_mode<L, 64>(N, mode, h, W, out, s);
+    case 128: return launch_linear_mode<L, 128>(N, mode, h, W, out, s);
     default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch_linear(int64_t N, int C, int lmax, int bf16, const float* h, const float* W, float* out,
+hipError_t launch_linear(int64_t N, int C, int lmax, int mode, const void* h, const void* W, float* out,
                          hipStream_t stream) {
   if (N == 0) return hipSuccess;
-  switch (lmax * 2 + (bf16 ? 1 : 0)) {
-    case 0: return dispatch_linear_c<0, false>(N, C, h, W, out, stream);
-    case 1: return dispatch_linear_c<0, true>(N, C, h, W, out, stream);
-    case 2: return dispatch_linear_c<1, false>(N, C, h, W, out, stream);
-    case 3: return dispatch_linear_c<1, true>(N, C, h, W, out, stream);
-    case 4: return dispatch_linear_c<2, false>(N, C, h, W, out, stream);
-    case 5: return dispatch_linear_c<2, true>(N, C, h, W, out, stream);
-    case 6: return dispatch_linear_c<3, false>(N, C, h, W, out, stream);
-    case 7: return dispatch_linear_c<3, true>(N, C, h, W, out, stream);
-    case 8: return dispatch_linear_c<4, false>(N, C, h, W, out, stream);
-    case 9: return dispatch_linear_c<4, true>(N, C, h, W, out, stream);
-    case 10: return dispatch_linear_c<5, false>(N, C, h, W, out, stream);
-    case 11: return dispatch_linear_c<5, true>(N, C, h, W, out, stream);
-    case 12: return dispatch_linear_c<6, false>(N, C, h, W, out, stream);
-    case 13: return dispatch_linear_c<6, true>(N, C, h, W, out, stream);
+  if (mode < 0 || mode > 2) return hipErrorInvalidValue;
+  switch (lmax) {
+    case 0: return dispatch_linear_c<0>(N, C, mode, h, W, out, stream);
+    case 1: return dispatch_linear_c<1>(N, C, mode, h, W, out, stream);
+    case 2: return dispatch_linear_c<2>(N, C, mode, h, W, out, stream);
+    case 3: return dispatch_linear_c<3>(N, C, mode, h, W, out, stream);
+    case 4: return dispatch_linear_c<4>(N, C, mode, h, W, out, stream);
+    case 5: return dispatch_linear_c<5>(N, C, mode, h, W, out, stream);
+    case 6: return dispatch_linear_c<6>(N, C, mode, h, W, out, stream);
     default: return hipErrorInvalidValue;
   }
 }

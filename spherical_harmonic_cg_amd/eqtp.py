@@ -22,7 +22,7 @@ EQTP_PATHS_PARITY, EQTP_PATHS_SO3 = 0, 1
 EQTP_W_FIXED, EQTP_W_RADIAL = 0, 1
 EQTP_EDGES_DST_SORTED, EQTP_EDGES_UNSORTED = 0, 1
 EQTP_ALGO_AUTO, EQTP_ALGO_NODE_MFMA, EQTP_ALGO_EDGE_VALU, EQTP_ALGO_EDGE_SO2 = 0, 1, 2, 3
-EQTP_F32, EQTP_BF16 = 0, 1
+EQTP_F32, EQTP_BF16, EQTP_F32_BF16 = 0, 1, 2
 
 EXPORTED = ("eqtp_num_paths", "eqtp_path_table", "eqtp_sh", "eqtp_conv_fused", "eqtp_conv_messages",
             "eqtp_conv_backward", "eqtp_conv_backward_by_source", "eqtp_edge_rows", "eqtp_sort_edges",
@@ -342,16 +342,27 @@ def eqtp_sort_edges(dst, N: int, vec=None, src=None, out=None):
 
 
 def eqtp_linear(h, W, lmax: int, dtype: int = EQTP_F32, out=None):
-    """out[n, c', l m] = sum_c W[l, c', c] h[n, c, l m]; dtype EQTP_F32 or EQTP_BF16 operands."""
+    """out[n, c', l m] = sum_c W[l, c', c] h[n, c, l m] (fp32 out).
+
+    float32 h and W: dtype EQTP_F32 (fp32 products) or EQTP_BF16 / EQTP_F32_BF16 (each value rounded to
+    bf16 for the products; passed to the library as EQTP_F32_BF16).  bfloat16 h and W: bf16 storage and
+    products (EQTP_BF16)."""
     import torch
 
-    _check(h, "h", torch.float32)
+    if h.dtype == torch.bfloat16:
+        if dtype not in (EQTP_BF16, EQTP_F32_BF16):
+            raise ValueError("bfloat16 h needs dtype EQTP_BF16")
+        st, cdt = torch.bfloat16, EQTP_BF16
+    else:
+        st = torch.float32
+        cdt = EQTP_F32 if dtype == EQTP_F32 else EQTP_F32_BF16
+    _check(h, "h", st)
     N, C, K = h.shape
-    _check(W, "W", torch.float32, (lmax + 1, C, C))
+    _check(W, "W", st, (lmax + 1, C, C))
     if out is None:
-        out = torch.empty_like(h)
+        out = torch.empty((N, C, K), dtype=torch.float32, device=h.device)
     _check(out, "out", torch.float32, (N, C, K))
-    _raise(load_library().eqtp_linear(N, C, lmax, dtype, _ptr(h), _ptr(W), _ptr(out), _stream()), "eqtp_linear")
+    _raise(load_library().eqtp_linear(N, C, lmax, cdt, _ptr(h), _ptr(W), _ptr(out), _stream()), "eqtp_linear")
     return out
 
 

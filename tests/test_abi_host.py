@@ -116,7 +116,8 @@ def test_sh_and_linear_validation():
     assert lib.eqtp_sh(NULL, 10, 3, FAKE, NULL) == 1
     assert lib.eqtp_sh(FAKE, 10, 3, ctypes.c_void_p(0x10008), NULL) == 1
     assert lib.eqtp_sh(NULL, 0, 3, NULL, NULL) == 0
-    assert lib.eqtp_linear(10, 64, 3, 2, FAKE, FAKE, FAKE, NULL) == 1
+    assert lib.eqtp_linear(10, 64, 3, 3, FAKE, FAKE, FAKE, NULL) == 1      # unknown dtype
+    assert lib.eqtp_linear(10, 64, 3, 2, FAKE, FAKE, ctypes.c_void_p(0x10008), NULL) == 1  # out misaligned
     assert lib.eqtp_linear(10, 48, 3, 0, FAKE, FAKE, FAKE, NULL) == 2
     assert lib.eqtp_linear(10, 64, 3, 0, NULL, FAKE, FAKE, NULL) == 1
     assert lib.eqtp_linear(0, 64, 3, 0, NULL, NULL, NULL, NULL) == 0

@@ -425,3 +425,46 @@ def test_linear_workloads(name):
     out = _np(eq.eqtp_linear(_t(h), _t(wl.w_lin), wl.lmax, dtype))
     ref = oracle.linear(h, wl.w_lin, wl.lmax)
     _assert_close(out, ref, tol=1e-2 if wl.linear_bf16 else TOL, what="linear " + name)
+
+
+def _bf16_pair(rng, shape, scale=1.0):
+    """A bfloat16 CUDA tensor and the exact float32 values it holds."""
+    import torch
+
+    t = (torch.from_numpy((rng.standard_normal(shape) * scale).astype(np.float32))).to(torch.bfloat16)
+    return t.cuda(), t.float().numpy()
+
+
+@pytest.mark.parametrize("C", [8, 16, 32, 64, 128])
+@pytest.mark.parametrize("L", [0, 1, 2, 3, 4, 6])
+def test_linear_bf16_storage(C, L):
+    """h and W held as bfloat16 in memory (EQTP_BF16): against the oracle on the same bf16 values."""
+    eq = _eq()
+    rng = np.random.default_rng(500 + 7 * C + L)
+    N = 53
+    K = (L + 1) ** 2
+    h, h32 = _bf16_pair(rng, (N, C, K))
+    W, W32 = _bf16_pair(rng, (L + 1, C, C), 1.0 / np.sqrt(C))
+    _say("linear bf16 storage C=%d L=%d" % (C, L))
+    out = _np(eq.eqtp_linear(h, W, L, eq.EQTP_BF16))
+    _assert_close(out, oracle.linear(h32, W32, L), tol=2e-5, what="linear bf16 storage")
+
+
+@pytest.mark.parametrize("C,L", [(64, 3), (32, 3), (128, 3), (64, 2), (16, 1)])
+def test_linear_bf16_many_tiles(C, L):
+    """Enough nodes that every persistent workgroup of the bf16-product kernel walks many 4-node tiles
+    (both register sets of its load ring), a ragged last tile; fp32 storage rounded on load and bf16
+    storage."""
+    eq = _eq()
+    rng = np.random.default_rng(900 + C + L)
+    N = 40009
+    K = (L + 1) ** 2
+    h, h32 = _bf16_pair(rng, (N, C, K))
+    W, W32 = _bf16_pair(rng, (L + 1, C, C), 1.0 / np.sqrt(C))
+    ref = oracle.linear(h32, W32, L)
+    _say("linear bf16 storage many tiles C=%d L=%d" % (C, L))
+    _assert_close(_np(eq.eqtp_linear(h, W, L, eq.EQTP_BF16)), ref, tol=2e-5, what="bf16 storage many tiles")
+    hf = rng.standard_normal((N, C, K)).astype(np.float32)
+    _say("linear fp32 storage bf16 products many tiles C=%d L=%d" % (C, L))
+    out = _np(eq.eqtp_linear(_t(hf), _t(W32), L, eq.EQTP_F32_BF16))
+    _assert_close(out, oracle.linear(hf, W32, L, bf16=True), tol=2e-5, what="fp32 storage bf16 products")
