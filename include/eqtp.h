@@ -121,9 +121,9 @@ typedef struct eqtp_conv_desc {
   float r_cut;         /* radial mode: cut-off radius (> 0) */
   int32_t n_basis;     /* radial mode: number of radial functions, must be 8 */
   int32_t x_dtype;     /* EQTP_F32 (default) or EQTP_BF16: x holds bfloat16 features,
-                          same [N, C, K] layout, 2 bytes each (eqtp_conv_fused with
-                          dst-sorted edges and fixed weights only).  A descriptor whose
-                          struct_size ends before this field is read as EQTP_F32. */
+                          same [N, C, K] layout, 2 bytes each (eqtp_conv_fused at
+                          lmax <= 3).  A descriptor whose struct_size ends before
+                          this field is read as EQTP_F32. */
 } eqtp_conv_desc;
 
 /* struct_size of a descriptor without the x_dtype field (still accepted) */
@@ -147,9 +147,10 @@ typedef struct eqtp_conv_desc {
  *            (row_ptr[0] = 0, row_ptr[N] = E, non-decreasing); required for
  *            EQTP_EDGES_DST_SORTED, ignored for EQTP_EDGES_UNSORTED.
  *   x        [N, C, K] node features, 16-byte aligned: fp32, or bfloat16 when
- *            d->x_dtype = EQTP_BF16 (then d->algo must not be
- *            EQTP_ALGO_EDGE_VALU, and unsorted edges or radial weights give
- *            EQTP_EUNSUPPORTED); accumulation is fp32 either way.
+ *            d->x_dtype = EQTP_BF16 (lmax <= 3; either edge order, fixed or
+ *            radial weights; EQTP_ALGO_EDGE_SO2 gives EQTP_EUNSUPPORTED).  The
+ *            bf16 values are widened exactly; every product, sum and atomic
+ *            add is fp32 either way (out stays fp32).
  *   weights  EQTP_W_FIXED: [P, C] fp32; EQTP_W_RADIAL: [8, P*C] fp32 with
  *            R_n(r) = sin(n pi r / r_cut) / r * u(r / r_cut), n = 1..8,
  *            u(d) = 1 - 28 d^6 + 48 d^7 - 21 d^8 for d < 1, else 0

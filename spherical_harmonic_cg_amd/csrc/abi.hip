@@ -121,7 +121,6 @@ int eqtp_conv_fused(const eqtp_conv_desc* d, int64_t N, int64_t E, const float* 
   // the node-factored algorithm needs per-node sums of edge-independent weights
   const bool node_ok = d->edge_order == EQTP_EDGES_DST_SORTED && d->weight_mode == EQTP_W_FIXED;
   if (d->algo == EQTP_ALGO_NODE_MFMA && !node_ok) return EQTP_EUNSUPPORTED;
-  if (x_dtype == EQTP_BF16 && (!node_ok || d->algo == EQTP_ALGO_EDGE_VALU)) return EQTP_EUNSUPPORTED;
   if (N == 0) return EQTP_OK;
   if (!x || !out || !weights || !aligned16(x) || !aligned16(out) || !aligned4(weights)) return EQTP_EINVAL;
   if (E > 0) {

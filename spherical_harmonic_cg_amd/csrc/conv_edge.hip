@@ -20,6 +20,10 @@
 //     message into out[dst] with global fp32 atomics (out zero-filled first).
 // Radial weights: w_e[p,c] = sum_n R_n(|vec_e|) W[n, p*C + c] with the
 // radial basis of eqtp_device.hpp.
+// XB: the node features are bfloat16 in memory (widened exactly to fp32 on
+// load); every product and sum, and the atomics, stay fp32.
+#include <type_traits>
+
 #include "eqtp_device.hpp"
 #include "eqtp_kernels.hpp"
 
@@ -37,15 +41,16 @@ struct EdgeCfg {
 
 constexpr int kRadialBasis = 8;
 
-template <int L, int PS, int C, bool RADIAL>
+template <int L, int PS, int C, bool RADIAL, bool XB = false>
 struct EdgeMsg {
+  typedef std::conditional_t<XB, __bf16, float> XT;  // element type of x in memory
   using T = Tables<L, PS>;
   using Cfg = EdgeCfg<C>;
   static constexpr int K = num_comp(L);
 
   // acc[j][mu3] += message of edge e for channels cl + j*CL
   __device__ __forceinline__ static void run(int e, int N, int cl, const float* __restrict__ vec,
-                                             const int* __restrict__ src, const float* __restrict__ x,
+                                             const int* __restrict__ src, const XT* __restrict__ x,
                                              const float* __restrict__ w, const float (&wreg)[Cfg::CPL][T::P],
                                              float inv_rc, float (&acc)[Cfg::CPL][K]) {
     const float vx = vec[3 * (size_t)e], vy = vec[3 * (size_t)e + 1], vz = vec[3 * (size_t)e + 2];
@@ -57,8 +62,8 @@ struct EdgeMsg {
     float xv[Cfg::CPL][K];
 #pragma unroll
     for (int j = 0; j < Cfg::CPL; ++j) {
-      const float* xp = x + ((size_t)s * C + cl + j * Cfg::CL) * K;
-      if constexpr (K % 4 == 0) {
+      const XT* xp = x + ((size_t)s * C + cl + j * Cfg::CL) * K;
+      if constexpr (K % 4 == 0 && !XB) {
 #pragma unroll
         for (int q = 0; q < K / 4; ++q) {
           const f4 t4 = reinterpret_cast<const f4*>(xp)[q];
@@ -67,9 +72,19 @@ struct EdgeMsg {
           xv[j][4 * q + 2] = t4[2];
           xv[j][4 * q + 3] = t4[3];
         }
+      } else if constexpr (K % 4 == 0) {
+        // four bf16 values per 8-byte load; a bf16 value is the upper half of the fp32 with the same bits
+#pragma unroll
+        for (int q = 0; q < K / 4; ++q) {
+          const uint2 t2 = reinterpret_cast<const uint2*>(xp)[q];
+          xv[j][4 * q] = __uint_as_float(t2.x << 16);
+          xv[j][4 * q + 1] = __uint_as_float(t2.x & 0xffff0000u);
+          xv[j][4 * q + 2] = __uint_as_float(t2.y << 16);
+          xv[j][4 * q + 3] = __uint_as_float(t2.y & 0xffff0000u);
+        }
       } else {
 #pragma unroll
-        for (int k = 0; k < K; ++k) xv[j][k] = xp[k];
+        for (int k = 0; k < K; ++k) xv[j][k] = (float)xp[k];
       }
     }
     float kacc = 0.0f;
@@ -116,18 +131,14 @@ struct EdgeMsg {
   }
 };
 
-template <int L, int PS, int C, bool RADIAL, bool ATOMIC>
-__global__ __launch_bounds__(EdgeCfg<C>::THREADS) void conv_edge_kernel(int N, int E,
-                                                                        const int* __restrict__ row_ptr,
-                                                                        const float* __restrict__ vec,
-                                                                        const int* __restrict__ src,
-                                                                        const int* __restrict__ dst,
-                                                                        const float* __restrict__ x,
-                                                                        const float* __restrict__ w,
-                                                                        float* __restrict__ out, float inv_rc) {
+template <int L, int PS, int C, bool RADIAL, bool ATOMIC, bool XB>
+__global__ __launch_bounds__(EdgeCfg<C>::THREADS) void conv_edge_kernel(
+    int N, int E, const int* __restrict__ row_ptr, const float* __restrict__ vec, const int* __restrict__ src,
+    const int* __restrict__ dst, const typename EdgeMsg<L, PS, C, RADIAL, XB>::XT* __restrict__ x,
+    const float* __restrict__ w, float* __restrict__ out, float inv_rc) {
   using Cfg = EdgeCfg<C>;
   using T = Tables<L, PS>;
-  using M = EdgeMsg<L, PS, C, RADIAL>;
+  using M = EdgeMsg<L, PS, C, RADIAL, XB>;
   constexpr int K = num_comp(L);
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
@@ -338,9 +349,11 @@ __global__ __launch_bounds__(EdgeCfg<C>::THREADS) void probe_edge_kernel(int N, 
   }
 }
 
-template <int L, int PS, int C, bool RADIAL, bool ATOMIC>
+template <int L, int PS, int C, bool RADIAL, bool ATOMIC, bool XB>
 static hipError_t launch_edge_t(const ConvArgs& a) {
   using Cfg = EdgeCfg<C>;
+  using XT = typename EdgeMsg<L, PS, C, RADIAL, XB>::XT;
+  const XT* x = reinterpret_cast<const XT*>(a.x);
   const float inv_rc = RADIAL ? 1.0f / a.r_cut : 0.0f;
   if constexpr (ATOMIC) {
     if (a.N > 0) {
@@ -350,22 +363,28 @@ static hipError_t launch_edge_t(const ConvArgs& a) {
     if (a.E == 0) return hipSuccess;
     const long long per_block = (long long)Cfg::WAVES * Cfg::EPW;
     const unsigned blocks = (unsigned)((a.E + per_block - 1) / per_block);
-    hipLaunchKernelGGL((conv_edge_kernel<L, PS, C, RADIAL, true>), dim3(blocks), dim3(Cfg::THREADS), 0, a.stream,
-                       (int)a.N, (int)a.E, a.row_ptr, a.vec, a.src, a.dst, a.x, a.w, a.out, inv_rc);
+    hipLaunchKernelGGL((conv_edge_kernel<L, PS, C, RADIAL, true, XB>), dim3(blocks), dim3(Cfg::THREADS), 0,
+                       a.stream, (int)a.N, (int)a.E, a.row_ptr, a.vec, a.src, a.dst, x, a.w, a.out, inv_rc);
   } else {
     if (a.N == 0) return hipSuccess;
     const unsigned blocks = (unsigned)((a.N + Cfg::WAVES - 1) / Cfg::WAVES);
-    hipLaunchKernelGGL((conv_edge_kernel<L, PS, C, RADIAL, false>), dim3(blocks), dim3(Cfg::THREADS), 0,
-                       a.stream, (int)a.N, (int)a.E, a.row_ptr, a.vec, a.src, a.dst, a.x, a.w, a.out, inv_rc);
+    hipLaunchKernelGGL((conv_edge_kernel<L, PS, C, RADIAL, false, XB>), dim3(blocks), dim3(Cfg::THREADS), 0,
+                       a.stream, (int)a.N, (int)a.E, a.row_ptr, a.vec, a.src, a.dst, x, a.w, a.out, inv_rc);
   }
   return hipGetLastError();
 }
 
+template <int L, int PS, int C, bool XB>
+static hipError_t dispatch_edge_mode_x(const ConvArgs& a) {
+  const bool radial = a.weight_mode == 1, atomic = a.edge_order == 1;
+  if (radial)
+    return atomic ? launch_edge_t<L, PS, C, true, true, XB>(a) : launch_edge_t<L, PS, C, true, false, XB>(a);
+  return atomic ? launch_edge_t<L, PS, C, false, true, XB>(a) : launch_edge_t<L, PS, C, false, false, XB>(a);
+}
+
 template <int L, int PS, int C>
 static hipError_t dispatch_edge_mode(const ConvArgs& a) {
-  const bool radial = a.weight_mode == 1, atomic = a.edge_order == 1;
-  if (radial) return atomic ? launch_edge_t<L, PS, C, true, true>(a) : launch_edge_t<L, PS, C, true, false>(a);
-  return atomic ? launch_edge_t<L, PS, C, false, true>(a) : launch_edge_t<L, PS, C, false, false>(a);
+  return a.x_bf16 ? dispatch_edge_mode_x<L, PS, C, true>(a) : dispatch_edge_mode_x<L, PS, C, false>(a);
 }
 
 template <int L, int PS>

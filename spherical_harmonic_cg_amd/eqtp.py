@@ -157,7 +157,7 @@ def eqtp_conv_fused(vec, src, x, weights, lmax: int, row_ptr=None, dst=None, pat
 
     Give ``row_ptr`` [N+1] for dst-sorted edges, or ``dst`` [E] for any order
     (atomic accumulation).  ``weights`` is [P, C] (fixed) or [8, P*C] (radial).
-    ``x`` is float32, or bfloat16 (dst-sorted edges, fixed weights); ``out``
+    ``x`` is float32, or bfloat16 (lmax <= 3, any edge order or weights); ``out``
     is float32.
     """
     import torch
