@@ -195,6 +195,9 @@ def main():
     ap.add_argument("--sort-edges", action="store_true",
                     help="with --unsorted: each step groups the edges by destination on the GPU "
                          "(eqtp_sort_edges) and runs the dst-sorted conv on them, instead of the atomic path")
+    ap.add_argument("--ws", action="store_true",
+                    help="with --unsorted: eqtp_conv_fused_ws, which groups the edges by destination in a "
+                         "workspace (rows in input order) and runs the dst-sorted kernels, inside each step")
     ap.add_argument("--atom-order", default="generation", choices=("generation", "cell"),
                     help="'cell': spatially coherent atom numbering (a labelled extra, not the headline)")
     ap.add_argument("--path-set", default="parity", choices=("parity", "so3"),
@@ -222,6 +225,8 @@ def main():
 
     if args.sort_edges and not args.unsorted:
         ap.error("--sort-edges needs --unsorted")
+    if args.ws and (not args.unsorted or args.sort_edges):
+        ap.error("--ws needs --unsorted (and replaces --sort-edges)")
     if args.graph and args.unsorted:
         ap.error("--graph times dst-sorted edges only")
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -275,7 +280,16 @@ def main():
         if sort_out is not None:
             eq.eqtp_sort_edges(dst, wl.N, vec=vec, src=src, out=sort_out)
 
+    ws_buf = None
+    if args.ws:
+        ws_buf = torch.empty(eq.eqtp_conv_workspace_bytes(wl.N, wl.E, wl.lmax, wl.C, weight_mode=wl.weight_mode,
+                                                          path_set=wl.path_set), dtype=torch.uint8, device=dev)
+
     def conv():
+        if ws_buf is not None:
+            eq.eqtp_conv_fused_ws(vec, src, x, w, wl.lmax, dst=dst, path_set=wl.path_set, weight_mode=wl.weight_mode,
+                                  r_cut=wl.r_cut, algo=args.algo, out=out, workspace=ws_buf)
+            return
         if sort_out is not None:
             rp_s, _, vec_s, src_s = sort_out
             eq.eqtp_conv_fused(vec_s, src_s, x, w, wl.lmax, row_ptr=rp_s, path_set=wl.path_set,
@@ -501,7 +515,7 @@ def main():
     # which kernel ran: the node kernel (fixed weights, dst-sorted, lmax <= 3) is bound by the fp32 matrix
     # cores; every other form by the fp32 vector ALUs (the radial edge-aligned kernel forms its radial
     # weights on the matrix cores but spends most of its time in the vector coupling)
-    sorted_edges = not args.unsorted or args.sort_edges
+    sorted_edges = not args.unsorted or args.sort_edges or args.ws
     node_kernel = wl.weight_mode == 0 and sorted_edges and wl.lmax <= 3 and args.algo in (0, 1)
     roofline = {"bound": "mfma" if node_kernel else "alu", "achieved": round(achieved_tflops, 3),
                 "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved_tflops / PEAK_FP32_TFLOPS, 4),
@@ -546,6 +560,7 @@ def main():
                                 % (wl.lmax, wl.lmax))
                    + (" (random edge order)" if args.unsorted else "")
                    + (" (sorted by destination on the GPU inside each step)" if args.sort_edges else "")
+                   + (" (grouped by destination in a workspace inside each step, eqtp_conv_fused_ws)" if args.ws else "")
                    + (" (cell-sorted atom numbering)" if args.atom_order == "cell" else "")
                    + (" (SO(3) path set)" if args.path_set == "so3" else "")
                    + (" (bfloat16 node features)" if args.x_bf16 else "")

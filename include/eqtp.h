@@ -169,6 +169,39 @@ int eqtp_conv_fused(const eqtp_conv_desc* d, int64_t N, int64_t E, const float* 
                     void* stream);
 
 /*
+ * Bytes of device workspace eqtp_conv_fused_ws needs for (d, N, E): for
+ * EQTP_EDGES_UNSORTED with N > 0, 256-byte aligned regions for row pointers
+ * [N+1], staged edge indices [E], grouped vectors [E,3] and sources [E] (about
+ * 20 bytes per edge); 0 for dst-sorted edges.  Negative status for a bad
+ * descriptor or sizes.
+ */
+int64_t eqtp_conv_workspace_bytes(const eqtp_conv_desc* d, int64_t N, int64_t E);
+
+/*
+ * The fused convolution of eqtp_conv_fused with a caller-given workspace.
+ * Dst-sorted edges: exactly eqtp_conv_fused (the workspace is not touched).
+ * Edges in any order (d->edge_order = EQTP_EDGES_UNSORTED, dst given): the
+ * edges are first grouped by destination in the workspace -- a counting sort
+ * on the GPU whose rows keep the edges' input order, so the grouping does not
+ * depend on the order of hardware atomics -- and the call then runs as for
+ * dst-sorted edges (d->algo as there; row_ptr is ignored).  The result is
+ * deterministic (bit-identical from call to call) and no atomics touch out.
+ * The grouping is layout preparation for the destination sum of the
+ * Batmobile page's section "3. operator fusion"; the page has no sort.
+ *   workspace        device memory of at least eqtp_conv_workspace_bytes(d,
+ *                    N, E) bytes, 16-byte aligned, owned by the caller; its
+ *                    contents on entry do not matter and are overwritten.
+ *   workspace_bytes  its size.
+ * Other arguments, layouts and errors as for eqtp_conv_fused; a missing or
+ * short workspace gives EQTP_EINVAL before any launch.  Asynchronous on
+ * stream; the workspace must not be reused by another call before this one
+ * has finished on the stream.
+ */
+int eqtp_conv_fused_ws(const eqtp_conv_desc* d, int64_t N, int64_t E, const float* vec, const int32_t* src,
+                       const int32_t* dst, const int32_t* row_ptr, const void* x, const float* weights, float* out,
+                       void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
  * Per-edge messages, without the destination sum (the page's fused kernel,
  * section "3. operator fusion": edge vectors [E,3], node features [N,C,16],
  * source indices [E] in, messages [E,C,16] out):

@@ -2,6 +2,7 @@
 // argument validation, kernel selection and launch on the caller's stream.
 #include <stddef.h>
 #include <stdint.h>
+#include <string.h>
 
 #include "../../include/eqtp.h"
 #include "eqtp_device.hpp"
@@ -85,9 +86,14 @@ int eqtp_sh(const float* vec, int64_t E, int lmax, float* Y, void* stream) {
   return status_of(eqtp::launch_sh(vec, E, lmax, Y, (hipStream_t)stream));
 }
 
-int eqtp_conv_fused(const eqtp_conv_desc* d, int64_t N, int64_t E, const float* vec, const int32_t* src,
-                    const int32_t* dst, const int32_t* row_ptr, const void* x, const float* weights, float* out,
-                    void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation and dispatch of the fused convolution; nothing is launched when launch is false.
+int conv_impl(const eqtp_conv_desc* d, int64_t N, int64_t E, const float* vec, const int32_t* src,
+              const int32_t* dst, const int32_t* row_ptr, const void* x, const float* weights, float* out,
+              void* stream, bool launch) {
   if (!desc_ok(d)) return EQTP_EINVAL;
   const int x_dtype = desc_x_dtype(d);
   if (x_dtype != EQTP_F32 && x_dtype != EQTP_BF16) return EQTP_EINVAL;
@@ -149,10 +155,78 @@ int eqtp_conv_fused(const eqtp_conv_desc* d, int64_t N, int64_t E, const float* 
   a.w = weights;
   a.out = out;
   a.stream = (hipStream_t)stream;
+  if (!launch) return EQTP_OK;
   if (use_radial_so2) return status_of(eqtp::launch_conv_so2_radial(a));
   if (use_so2) return status_of(eqtp::launch_conv_so2(a));
   const bool use_node = node_ok && d->algo != EQTP_ALGO_EDGE_VALU;
   return status_of(use_node ? eqtp::launch_conv_node(a) : eqtp::launch_conv_edge(a));
+}
+
+// Workspace of the grouping by destination: row pointers [N+1], the scatter's
+// staged edge indices [E], and the grouped vectors [E,3] and sources [E],
+// each region 256-byte aligned.
+struct WsLayout {
+  size_t staged, vec, src, total;
+};
+WsLayout ws_layout(int64_t N, int64_t E) {
+  auto al = [](int64_t b) { return (size_t)((b + 255) & ~(int64_t)255); };
+  WsLayout w;
+  w.staged = al((N + 1) * 4);
+  w.vec = w.staged + al(E * 4);
+  w.src = w.vec + al(E * 12);
+  w.total = w.src + al(E * 4);
+  return w;
+}
+
+bool groups_edges(const eqtp_conv_desc* d, int64_t N) { return d->edge_order == EQTP_EDGES_UNSORTED && N > 0; }
+
+// eqtp_conv_fused_ws on a given workspace (see include/eqtp.h)
+int conv_ws_impl(const eqtp_conv_desc* d, int64_t N, int64_t E, const float* vec, const int32_t* src,
+                 const int32_t* dst, const int32_t* row_ptr, const void* x, const float* weights, float* out,
+                 void* workspace, int64_t workspace_bytes, void* stream) {
+  if (!desc_ok(d)) return EQTP_EINVAL;
+  if (!groups_edges(d, N)) return conv_impl(d, N, E, vec, src, dst, row_ptr, x, weights, out, stream, true);
+  if (N < 0 || E < 0 || N > kMaxIndex || E > kMaxIndex) return EQTP_EINVAL;
+  const WsLayout L = ws_layout(N, E);
+  if (!workspace || !aligned16(workspace) || workspace_bytes < (int64_t)L.total) return EQTP_EINVAL;
+  if (E > 0 && (!dst || !aligned4(dst))) return EQTP_EINVAL;
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  int32_t* rp = reinterpret_cast<int32_t*>(ws);
+  int32_t* staged = reinterpret_cast<int32_t*>(ws + L.staged);
+  float* vec_s = reinterpret_cast<float*>(ws + L.vec);
+  int32_t* src_s = reinterpret_cast<int32_t*>(ws + L.src);
+  // the call as it runs after the grouping: dst-sorted edges
+  eqtp_conv_desc ds{};
+  memcpy(&ds, d, (size_t)d->struct_size);  // a descriptor of the earlier size ends before x_dtype
+  ds.struct_size = (int32_t)sizeof(eqtp_conv_desc);
+  ds.x_dtype = desc_x_dtype(d);
+  ds.edge_order = EQTP_EDGES_DST_SORTED;
+  int rc = conv_impl(&ds, N, E, vec, src, nullptr, rp, x, weights, out, stream, false);
+  if (rc != EQTP_OK) return rc;
+  rc = status_of(eqtp::launch_sort_edges_ordered(N, E, dst, vec, src, rp, staged, vec_s, src_s, (hipStream_t)stream));
+  if (rc != EQTP_OK) return rc;
+  return conv_impl(&ds, N, E, vec_s, src_s, nullptr, rp, x, weights, out, stream, true);
+}
+
+}  // namespace
+
+extern "C" {
+
+int eqtp_conv_fused(const eqtp_conv_desc* d, int64_t N, int64_t E, const float* vec, const int32_t* src,
+                    const int32_t* dst, const int32_t* row_ptr, const void* x, const float* weights, float* out,
+                    void* stream) {
+  return conv_impl(d, N, E, vec, src, dst, row_ptr, x, weights, out, stream, true);
+}
+
+int64_t eqtp_conv_workspace_bytes(const eqtp_conv_desc* d, int64_t N, int64_t E) {
+  if (!desc_ok(d) || N < 0 || E < 0 || N > kMaxIndex || E > kMaxIndex) return -EQTP_EINVAL;
+  return groups_edges(d, N) ? (int64_t)ws_layout(N, E).total : 0;
+}
+
+int eqtp_conv_fused_ws(const eqtp_conv_desc* d, int64_t N, int64_t E, const float* vec, const int32_t* src,
+                       const int32_t* dst, const int32_t* row_ptr, const void* x, const float* weights, float* out,
+                       void* workspace, int64_t workspace_bytes, void* stream) {
+  return conv_ws_impl(d, N, E, vec, src, dst, row_ptr, x, weights, out, workspace, workspace_bytes, stream);
 }
 
 int eqtp_conv_messages(const eqtp_conv_desc* d, int64_t N, int64_t E, const float* vec, const int32_t* src,

@@ -76,5 +76,9 @@ hipError_t launch_conv_backward_by_source(const BwdArgs& a);
 hipError_t launch_edge_rows(int64_t N, int64_t E, const int32_t* row_ptr, int32_t* rows, hipStream_t stream);
 hipError_t launch_sort_edges(int64_t N, int64_t E, const int32_t* dst, const float* vec, const int32_t* src,
                              int32_t* row_ptr, int32_t* perm, float* vec_out, int32_t* src_out, hipStream_t stream);
+// grouping by destination with each row in input order: staged [E] int32 scratch; vec_out, src_out required
+hipError_t launch_sort_edges_ordered(int64_t N, int64_t E, const int32_t* dst, const float* vec, const int32_t* src,
+                                     int32_t* row_ptr, int32_t* staged, float* vec_out, int32_t* src_out,
+                                     hipStream_t stream);
 
 }  // namespace eqtp

@@ -2,13 +2,21 @@
 // sort on the GPU) so that the dst-segmented convolution, which needs CSR row
 // pointers, can run on them instead of the fp32-atomic scatter.
 //
-// No scratch memory: the row-pointer output doubles as the counter array.
+// eqtp_sort_edges needs no scratch memory: the row-pointer output doubles as
+// the counter array.
 //   1. row_ptr[0..N-1] = 0, then row_ptr[d] += 1 per edge (histogram);
 //   2. one workgroup turns it in place into inclusive sums (row ends) and sets
 //      row_ptr[N] = E;
 //   3. every edge takes slot = atomicSub(&row_ptr[d], 1) - 1, which fills row
-//      d from its end backwards and leaves row_ptr[d] at the row's start.
-// The order of edges inside a row depends on the atomics' order (unspecified).
+//      d from its end backwards and leaves row_ptr[d] at the row's start; the
+//      edge's index (and, for eqtp_sort_edges, its vector and source) goes to
+//      the slot.  The order inside a row follows the atomics.
+// The convolution over edges in any order (eqtp_conv_fused_ws) stages step 3's
+// indices in its workspace and adds
+//   4. one wavefront per row puts the row's indices in increasing order (each
+//      index's rank among the row's indices is its place) and gathers vec and
+//      src in that order: the edges of a row keep their input order, so the
+//      grouping, and the convolution after it, do not depend on the atomics.
 #include "eqtp_device.hpp"
 #include "eqtp_kernels.hpp"
 
@@ -103,6 +111,46 @@ __global__ __launch_bounds__(256) void scatter_by_dst_kernel(const int* __restri
   }
 }
 
+// Step 4: one wavefront per row (persistent waves, rows strided).  Lane i of
+// chunk k holds the row's index at slot 64k + i; its rank is the number of
+// the row's indices below it, counted against each chunk held in a register
+// and broadcast lane by lane.  Indices are distinct (one per edge).  The
+// outputs must not alias `staged`.
+constexpr int kRowWaves = 4;
+__global__ __launch_bounds__(kRowWaves * 64) void row_order_kernel(const int* __restrict__ row_ptr, int N, int E,
+                                                                   const int* __restrict__ staged,
+                                                                   const float* __restrict__ vec,
+                                                                   const int* __restrict__ src,
+                                                                   float* __restrict__ vec_out,
+                                                                   int* __restrict__ src_out) {
+  const int lane = threadIdx.x & 63;
+  const int wave = blockIdx.x * kRowWaves + (threadIdx.x >> 6);
+  const int nwaves = gridDim.x * kRowWaves;
+  for (int r = wave; r < N; r += nwaves) {
+    const int b = min(max(row_ptr[r], 0), E);
+    const int e = min(max(row_ptr[r + 1], b), E);
+    const int len = e - b;
+    for (int c0 = 0; c0 < len; c0 += 64) {
+      const bool mine_ok = c0 + lane < len;
+      const int mine = mine_ok ? staged[b + c0 + lane] : 0;
+      int rank = 0;
+      for (int k0 = 0; k0 < len; k0 += 64) {
+        const int other = k0 + lane < len ? staged[b + k0 + lane] : 0x7fffffff;
+        const int n = min(64, len - k0);
+        for (int j = 0; j < n; ++j) rank += __builtin_amdgcn_readlane(other, j) < mine ? 1 : 0;
+      }
+      if (mine_ok) {
+        const int slot = b + rank;
+        const int ei = clamp_index(mine, E);
+        vec_out[3 * (size_t)slot] = vec[3 * (size_t)ei];
+        vec_out[3 * (size_t)slot + 1] = vec[3 * (size_t)ei + 1];
+        vec_out[3 * (size_t)slot + 2] = vec[3 * (size_t)ei + 2];
+        src_out[slot] = src[ei];
+      }
+    }
+  }
+}
+
 // rows[e] = the row of CSR position e (one thread per row, grid-stride)
 __global__ __launch_bounds__(256) void edge_rows_kernel(const int* __restrict__ row_ptr, int N, int E,
                                                         int* __restrict__ rows) {
@@ -121,19 +169,38 @@ hipError_t launch_edge_rows(int64_t N, int64_t E, const int32_t* row_ptr, int32_
   return hipGetLastError();
 }
 
-hipError_t launch_sort_edges(int64_t N, int64_t E, const int32_t* dst, const float* vec, const int32_t* src,
-                             int32_t* row_ptr, int32_t* perm, float* vec_out, int32_t* src_out, hipStream_t stream) {
-  auto grid = [](int64_t n) {
-    int64_t b = (n + 255) / 256;
-    return (unsigned)(b < 1 ? 1 : (b > 8192 ? 8192 : b));
-  };
-  hipLaunchKernelGGL(zero_i32_kernel, dim3(grid(N)), dim3(256), 0, stream, row_ptr, (int)N);
+static unsigned grid_for(int64_t n) {
+  const int64_t b = (n + 255) / 256;
+  return (unsigned)(b < 1 ? 1 : (b > 8192 ? 8192 : b));
+}
+
+// steps 1-3 (the scatter also writes vec and src when their outputs are given)
+static hipError_t group_by_dst(int64_t N, int64_t E, const int32_t* dst, const float* vec, const int32_t* src,
+                               int32_t* row_ptr, int32_t* perm, float* vec_out, int32_t* src_out, hipStream_t stream) {
+  hipLaunchKernelGGL(zero_i32_kernel, dim3(grid_for(N)), dim3(256), 0, stream, row_ptr, (int)N);
   if (E > 0)
-    hipLaunchKernelGGL(dst_histogram_kernel, dim3(grid(E)), dim3(256), 0, stream, dst, (int)E, (int)N, row_ptr);
+    hipLaunchKernelGGL(dst_histogram_kernel, dim3(grid_for(E)), dim3(256), 0, stream, dst, (int)E, (int)N, row_ptr);
   hipLaunchKernelGGL(inclusive_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, row_ptr, (int)N, (int)E);
   if (E > 0)
-    hipLaunchKernelGGL(scatter_by_dst_kernel, dim3(grid(E)), dim3(256), 0, stream, dst, vec, src, (int)E, (int)N,
+    hipLaunchKernelGGL(scatter_by_dst_kernel, dim3(grid_for(E)), dim3(256), 0, stream, dst, vec, src, (int)E, (int)N,
                        row_ptr, perm, vec_out, src_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_sort_edges(int64_t N, int64_t E, const int32_t* dst, const float* vec, const int32_t* src,
+                             int32_t* row_ptr, int32_t* perm, float* vec_out, int32_t* src_out, hipStream_t stream) {
+  return group_by_dst(N, E, dst, vec, src, row_ptr, perm, vec_out, src_out, stream);
+}
+
+hipError_t launch_sort_edges_ordered(int64_t N, int64_t E, const int32_t* dst, const float* vec, const int32_t* src,
+                                     int32_t* row_ptr, int32_t* staged, float* vec_out, int32_t* src_out,
+                                     hipStream_t stream) {
+  hipError_t err = group_by_dst(N, E, dst, nullptr, nullptr, row_ptr, staged, nullptr, nullptr, stream);
+  if (err != hipSuccess || E == 0) return err;
+  const int64_t rb = (N + kRowWaves - 1) / kRowWaves;
+  const unsigned rgrid = (unsigned)(rb < 1 ? 1 : (rb > 4096 ? 4096 : rb));
+  hipLaunchKernelGGL(row_order_kernel, dim3(rgrid), dim3(kRowWaves * 64), 0, stream, row_ptr, (int)N, (int)E,
+                     staged, vec, src, vec_out, src_out);
   return hipGetLastError();
 }
 

@@ -24,7 +24,8 @@ EQTP_EDGES_DST_SORTED, EQTP_EDGES_UNSORTED = 0, 1
 EQTP_ALGO_AUTO, EQTP_ALGO_NODE_MFMA, EQTP_ALGO_EDGE_VALU, EQTP_ALGO_EDGE_SO2 = 0, 1, 2, 3
 EQTP_F32, EQTP_BF16, EQTP_F32_BF16 = 0, 1, 2
 
-EXPORTED = ("eqtp_num_paths", "eqtp_path_table", "eqtp_sh", "eqtp_conv_fused", "eqtp_conv_messages",
+EXPORTED = ("eqtp_num_paths", "eqtp_path_table", "eqtp_sh", "eqtp_conv_fused", "eqtp_conv_workspace_bytes",
+            "eqtp_conv_fused_ws", "eqtp_conv_messages",
             "eqtp_conv_backward", "eqtp_conv_backward_by_source", "eqtp_edge_rows", "eqtp_sort_edges",
             "eqtp_linear",
             "eqtp_status_string", "eqtp_test_segment_probe")
@@ -64,6 +65,10 @@ def load_library(path: str = LIB_PATH):
             lib.eqtp_sh.restype = i32
             lib.eqtp_conv_fused.argtypes = [ctypes.POINTER(_ConvDesc), i64, i64, vp, vp, vp, vp, vp, vp, vp, vp]
             lib.eqtp_conv_fused.restype = i32
+            lib.eqtp_conv_workspace_bytes.argtypes = [ctypes.POINTER(_ConvDesc), i64, i64]
+            lib.eqtp_conv_workspace_bytes.restype = i64
+            lib.eqtp_conv_fused_ws.argtypes = [ctypes.POINTER(_ConvDesc), i64, i64] + [vp] * 8 + [i64, vp]
+            lib.eqtp_conv_fused_ws.restype = i32
             lib.eqtp_conv_messages.argtypes = [ctypes.POINTER(_ConvDesc), i64, i64] + [vp] * 6
             lib.eqtp_conv_messages.restype = i32
             lib.eqtp_conv_backward.argtypes = [ctypes.POINTER(_ConvDesc), i64, i64] + [vp] * 11
@@ -150,16 +155,8 @@ def eqtp_sh(vec, lmax: int, Y=None):
     return Y
 
 
-def eqtp_conv_fused(vec, src, x, weights, lmax: int, row_ptr=None, dst=None, path_set: int = EQTP_PATHS_PARITY,
-                    weight_mode: int = EQTP_W_FIXED, r_cut: float = 0.0, n_basis: int = 8,
-                    algo: int = EQTP_ALGO_AUTO, out=None):
-    """out [N, C, K] = fused harmonics -> coupling -> sum into dst.
-
-    Give ``row_ptr`` [N+1] for dst-sorted edges, or ``dst`` [E] for any order
-    (atomic accumulation).  ``weights`` is [P, C] (fixed) or [8, P*C] (radial).
-    ``x`` is float32, or bfloat16 (lmax <= 3, any edge order or weights); ``out``
-    is float32.
-    """
+def _conv_args(vec, src, x, weights, lmax, row_ptr, dst, path_set, weight_mode, r_cut, n_basis, algo, out):
+    """Checks the fused convolution's tensors; returns (descriptor, N, E, out)."""
     import torch
 
     x_dtype = EQTP_BF16 if x.dtype == torch.bfloat16 else EQTP_F32
@@ -190,9 +187,58 @@ def eqtp_conv_fused(vec, src, x, weights, lmax: int, row_ptr=None, dst=None, pat
     _check(out, "out", torch.float32, (N, C, K))
     d = _ConvDesc(ctypes.sizeof(_ConvDesc), lmax, C, path_set, weight_mode, order, algo, float(r_cut), n_basis,
                   x_dtype)
+    return d, N, E, out
+
+
+def eqtp_conv_fused(vec, src, x, weights, lmax: int, row_ptr=None, dst=None, path_set: int = EQTP_PATHS_PARITY,
+                    weight_mode: int = EQTP_W_FIXED, r_cut: float = 0.0, n_basis: int = 8,
+                    algo: int = EQTP_ALGO_AUTO, out=None):
+    """out [N, C, K] = fused harmonics -> coupling -> sum into dst.
+
+    Give ``row_ptr`` [N+1] for dst-sorted edges, or ``dst`` [E] for any order
+    (atomic accumulation).  ``weights`` is [P, C] (fixed) or [8, P*C] (radial).
+    ``x`` is float32, or bfloat16 (lmax <= 3, any edge order or weights); ``out``
+    is float32.
+    """
+    d, N, E, out = _conv_args(vec, src, x, weights, lmax, row_ptr, dst, path_set, weight_mode, r_cut, n_basis, algo,
+                              out)
     rc = load_library().eqtp_conv_fused(ctypes.byref(d), N, E, _ptr(vec), _ptr(src), _ptr(dst), _ptr(row_ptr),
                                         _ptr(x), _ptr(weights), _ptr(out), _stream())
     _raise(rc, "eqtp_conv_fused")
+    return out
+
+
+def eqtp_conv_workspace_bytes(N: int, E: int, lmax: int, C: int, edge_order: int = EQTP_EDGES_UNSORTED,
+                              weight_mode: int = EQTP_W_FIXED, path_set: int = EQTP_PATHS_PARITY) -> int:
+    """Device workspace eqtp_conv_fused_ws needs (bytes)."""
+    d = _ConvDesc(ctypes.sizeof(_ConvDesc), lmax, C, path_set, weight_mode, edge_order, EQTP_ALGO_AUTO, 1.0, 8,
+                  EQTP_F32)
+    n = load_library().eqtp_conv_workspace_bytes(ctypes.byref(d), N, E)
+    if n < 0:
+        raise EqtpError(-n, "eqtp_conv_workspace_bytes")
+    return int(n)
+
+
+def eqtp_conv_fused_ws(vec, src, x, weights, lmax: int, row_ptr=None, dst=None, path_set: int = EQTP_PATHS_PARITY,
+                       weight_mode: int = EQTP_W_FIXED, r_cut: float = 0.0, n_basis: int = 8,
+                       algo: int = EQTP_ALGO_AUTO, out=None, workspace=None):
+    """eqtp_conv_fused with a workspace: edges in any order (``dst``) are grouped by destination on the GPU
+    (rows in input order) and summed without atomics.  ``workspace`` is a uint8 CUDA tensor of at least
+    eqtp_conv_workspace_bytes bytes (allocated here if None)."""
+    import torch
+
+    d, N, E, out = _conv_args(vec, src, x, weights, lmax, row_ptr, dst, path_set, weight_mode, r_cut, n_basis, algo,
+                              out)
+    need = load_library().eqtp_conv_workspace_bytes(ctypes.byref(d), N, E)
+    if need < 0:
+        _raise(-need, "eqtp_conv_workspace_bytes")
+    if workspace is None:
+        workspace = torch.empty(max(int(need), 16), dtype=torch.uint8, device=x.device)
+    _check(workspace, "workspace", torch.uint8)
+    rc = load_library().eqtp_conv_fused_ws(ctypes.byref(d), N, E, _ptr(vec), _ptr(src), _ptr(dst), _ptr(row_ptr),
+                                           _ptr(x), _ptr(weights), _ptr(out), _ptr(workspace), workspace.numel(),
+                                           _stream())
+    _raise(rc, "eqtp_conv_fused_ws")
     return out
 
 

@@ -24,7 +24,7 @@ def _lib():
 
 def _declared():
     txt = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:const char\*|int)\s+(eqtp_\w+)\s*\(", txt, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:const char\*|int|int64_t)\s+(eqtp_\w+)\s*\(", txt, re.M)))
 
 
 def test_header_declares_the_binding_names():
@@ -185,9 +185,9 @@ def test_descriptor_versions_and_feature_dtype():
     v1b.struct_size = 36  # x_dtype lies past struct_size, so it is not read
     assert conv(v1b) == 2
     assert conv(_desc(e, x_dtype=7)) == 1
-    assert conv(_desc(e, x_dtype=1, edge_order=1), dst=FAKE, rp=NULL) == 2     # bf16 features: node algorithm only
-    assert conv(_desc(e, x_dtype=1, weight_mode=1, r_cut=4.0)) == 2
-    assert conv(_desc(e, x_dtype=1, algo=2)) == 2
+    assert conv(_desc(e, x_dtype=1, algo=3)) == 2                               # bf16: not the edge-aligned form
+    assert conv(_desc(e, x_dtype=1, lmax=4)) == 2                               # bf16: lmax <= 3 only
+    assert conv(_desc(e, x_dtype=1, weight_mode=1, r_cut=4.0, algo=3)) == 2
     bf = _desc(e, x_dtype=1)
     assert lib.eqtp_conv_messages(ctypes.byref(bf), 10, 20, FAKE, FAKE, FAKE, FAKE, FAKE, NULL) == 2
     assert lib.eqtp_conv_backward(ctypes.byref(bf), 10, 20, FAKE, FAKE, NULL, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
@@ -244,3 +244,22 @@ def test_edge_rows_validation():
     assert lib.eqtp_edge_rows(10, 5, FAKE, NULL, NULL) == 1
     assert lib.eqtp_edge_rows(10, 5, ctypes.c_void_p(0x10002), FAKE, NULL) == 1
     assert lib.eqtp_edge_rows(10, 0, NULL, NULL, NULL) == 0                # nothing to do, nothing launched
+
+
+def test_conv_ws_validation():
+    e = _lib()
+    lib = e.load_library()
+    d = _desc(e, edge_order=1)
+    need = lib.eqtp_conv_workspace_bytes(ctypes.byref(d), 100, 1000)
+    al = lambda b: (b + 255) // 256 * 256
+    assert need == al(101 * 4) + al(1000 * 4) + al(1000 * 12) + al(1000 * 4)
+    assert lib.eqtp_conv_workspace_bytes(ctypes.byref(_desc(e)), 100, 1000) == 0   # dst-sorted: none
+    assert lib.eqtp_conv_workspace_bytes(ctypes.byref(d), -1, 10) == -1
+    assert lib.eqtp_conv_workspace_bytes(ctypes.byref(d), 0, 0) == 0
+    call = lambda ws, nb, dd=d: lib.eqtp_conv_fused_ws(ctypes.byref(dd), 100, 1000, FAKE, FAKE, FAKE, NULL, FAKE,
+                                                        FAKE, FAKE, ws, nb, NULL)
+    assert call(NULL, need) == 1                                  # no workspace
+    assert call(FAKE, need - 1) == 1                              # short workspace
+    assert call(ctypes.c_void_p(0x10008), need) == 1              # misaligned workspace
+    assert lib.eqtp_conv_fused_ws(ctypes.byref(d), 100, 1000, FAKE, FAKE, NULL, NULL, FAKE, FAKE, FAKE, FAKE, need,
+                                  NULL) == 1                      # no dst

@@ -119,3 +119,98 @@ def test_sort_then_conv_workload(name):
     out = _np(eq.eqtp_conv_fused(vs, ss, _t(wl.x), _t(wl.weights), wl.lmax, row_ptr=_t(rp), path_set=wl.path_set,
                                  weight_mode=wl.weight_mode, r_cut=wl.r_cut))
     _assert_close(out, _oracle_full(name), TOL, name + " sort+conv")
+
+
+# ----------------------------------------------------------------------------
+# eqtp_conv_fused_ws: edges in any order, grouped in a workspace (rows in input
+# order), then the dst-sorted kernels
+# ----------------------------------------------------------------------------
+
+def _interleave_rows(wl, seed):
+    """A random interleaving of the rows that keeps every row's edges in their sorted order: the grouping
+    must then give back exactly the dst-sorted edge list."""
+    rng = np.random.default_rng(seed)
+    pos = rng.permutation(wl.E)             # edge i of the sorted list would land at pos[i] ...
+    order = np.empty(wl.E, dtype=np.int64)
+    for r in range(wl.N):                    # ... but each row's slots are refilled in sorted order
+        b, e = wl.row_ptr[r], wl.row_ptr[r + 1]
+        order[np.sort(pos[b:e])] = np.arange(b, e)
+    return wl.vec[order].copy(), wl.src[order].copy(), wl.dst[order].copy()
+
+
+@pytest.mark.parametrize("C,L,radial", [(8, 2, False), (16, 1, False), (32, 3, False), (64, 3, False),
+                                        (128, 3, False), (64, 0, False), (32, 3, True), (128, 3, True),
+                                        (8, 2, True)])
+def test_conv_ws_matches_sorted_bitwise(C, L, radial):
+    """Rows interleaved at random but each in sorted order: the workspace path gives the dst-sorted
+    convolution bit for bit (the grouping restores the sorted list exactly), and two calls agree."""
+    eq = _eq()
+    wl = synth.small_graph(45, 9, C, L, 2000 + C + L, radial=radial, r_cut=5.0, empty_rows=(0, 44),
+                           long_rows=(3,), long_len=150, zero_vec_edges=1)
+    w = wl.w_rad if radial else wl.w
+    kw = dict(weight_mode=1, r_cut=5.0) if radial else {}
+    pvec, psrc, pdst = _interleave_rows(wl, 17)
+    _say("conv ws interleaved C=%d L=%d radial=%d" % (C, L, radial))
+    ref = _np(eq.eqtp_conv_fused(_t(wl.vec), _t(wl.src), _t(wl.x), _t(w), L, row_ptr=_t(wl.row_ptr), **kw))
+    got = _np(eq.eqtp_conv_fused_ws(_t(pvec), _t(psrc), _t(wl.x), _t(w), L, dst=_t(pdst), **kw))
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), "grouped result differs from the sorted one"
+    again = _np(eq.eqtp_conv_fused_ws(_t(pvec), _t(psrc), _t(wl.x), _t(w), L, dst=_t(pdst), **kw))
+    assert np.array_equal(got.view(np.uint32), again.view(np.uint32))
+    orc = oracle.conv(wl.N, wl.vec, wl.src, wl.dst, wl.x, w, L, weight_mode=1 if radial else 0, r_cut=5.0)
+    _assert_close(got, orc, TOL, "conv ws C%d L%d" % (C, L))
+
+
+@pytest.mark.parametrize("C,L,ps", [(C, L, ps) for C in (8, 32, 64, 128) for L in (0, 1, 2, 3) for ps in (0, 1)])
+def test_conv_ws_random_order(C, L, ps):
+    """Edges in a random order: against the oracle, deterministic from call to call, fp32 and bf16 x."""
+    import torch
+
+    eq = _eq()
+    wl = synth.small_graph(40, 11, C, L, 2100 + C + 10 * L + 100 * ps, path_set=ps, empty_rows=(5,),
+                           long_rows=(6, 7), long_len=200, zero_vec_edges=2)
+    pvec, psrc, pdst = synth.random_permutation(wl, seed=3)
+    ref = oracle.conv(wl.N, wl.vec, wl.src, wl.dst, wl.x, wl.w, L, path_set=ps)
+    _say("conv ws random order C=%d L=%d ps=%d" % (C, L, ps))
+    ws = torch.empty(eq.eqtp_conv_workspace_bytes(wl.N, wl.E, L, C), dtype=torch.uint8, device="cuda")
+    a = _np(eq.eqtp_conv_fused_ws(_t(pvec), _t(psrc), _t(wl.x), _t(wl.w), L, dst=_t(pdst), path_set=ps,
+                                  workspace=ws))
+    _assert_close(a, ref, TOL, "conv ws random order")
+    b = _np(eq.eqtp_conv_fused_ws(_t(pvec), _t(psrc), _t(wl.x), _t(wl.w), L, dst=_t(pdst), path_set=ps,
+                                  workspace=ws))
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), "not deterministic"
+    xb = _t(wl.x).to(torch.bfloat16)
+    xr = xb.float().cpu().numpy()
+    got = _np(eq.eqtp_conv_fused_ws(_t(pvec), _t(psrc), xb, _t(wl.w), L, dst=_t(pdst), path_set=ps))
+    _assert_close(got, oracle.conv(wl.N, wl.vec, wl.src, wl.dst, xr, wl.w, L, path_set=ps), TOL, "conv ws bf16 x")
+
+
+def test_conv_ws_no_edges_and_sorted_passthrough():
+    import torch
+
+    eq = _eq()
+    N, C = 9, 32
+    x = torch.randn(N, C, 16, device="cuda")
+    w = torch.randn(23, C, device="cuda")
+    _say("conv ws no edges")
+    out = torch.full_like(x, 7.0)
+    eq.eqtp_conv_fused_ws(torch.zeros((0, 3), device="cuda"), torch.zeros(0, dtype=torch.int32, device="cuda"), x, w,
+                          3, dst=torch.zeros(0, dtype=torch.int32, device="cuda"), out=out)
+    assert np.all(_np(out) == 0.0)
+    assert eq.eqtp_conv_workspace_bytes(N, 100, 3, C, edge_order=eq.EQTP_EDGES_DST_SORTED) == 0
+    wl = synth.small_graph(20, 7, 64, 3, 2200)
+    _say("conv ws sorted pass-through")
+    a = _np(eq.eqtp_conv_fused_ws(_t(wl.vec), _t(wl.src), _t(wl.x), _t(wl.w), 3, row_ptr=_t(wl.row_ptr)))
+    b = _np(eq.eqtp_conv_fused(_t(wl.vec), _t(wl.src), _t(wl.x), _t(wl.w), 3, row_ptr=_t(wl.row_ptr)))
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+@pytest.mark.parametrize("name", ["mid", "large", "radial"])
+def test_conv_ws_workloads(name):
+    """Full-size workloads in random edge order through the workspace path: every row against the oracle."""
+    eq = _eq()
+    wl = _wl(name)
+    pvec, psrc, pdst = synth.random_permutation(wl)
+    _say("conv ws %s E=%d" % (name, wl.E))
+    out = _np(eq.eqtp_conv_fused_ws(_t(pvec), _t(psrc), _t(wl.x), _t(wl.weights), wl.lmax, dst=_t(pdst),
+                                    path_set=wl.path_set, weight_mode=wl.weight_mode, r_cut=wl.r_cut))
+    _assert_close(out, _oracle_full(name), TOL, name + " conv ws")
