@@ -48,6 +48,7 @@ extern "C" {
 #define EQTP_EINVAL 1       /* bad argument (null pointer, size, alignment, enum) */
 #define EQTP_EUNSUPPORTED 2 /* valid request this build does not implement */
 #define EQTP_EHIP 3         /* the HIP runtime reported an error at launch */
+#define EQTP_ETOOLARGE 4    /* eqtp_conv_fused_noalloc: the call needs more than the static scratch */
 
 /* coupling path sets (paths are (l1 = feature l, l2 = harmonic l, l3 = output l)) */
 #define EQTP_PATHS_PARITY 0 /* l1+l2+l3 even: 23 paths at lmax 3, 11 at lmax 2 */
@@ -200,6 +201,24 @@ int64_t eqtp_conv_workspace_bytes(const eqtp_conv_desc* d, int64_t N, int64_t E)
 int eqtp_conv_fused_ws(const eqtp_conv_desc* d, int64_t N, int64_t E, const float* vec, const int32_t* src,
                        const int32_t* dst, const int32_t* row_ptr, const void* x, const float* weights, float* out,
                        void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): exactly
+ * eqtp_conv_fused_ws, with the workspace taken from a static array of the
+ * library (128 MiB per device, reserved while the process runs) instead of
+ * the caller.  The call allocates nothing.  A request whose workspace
+ * (eqtp_conv_workspace_bytes) exceeds 128 MiB -- e.g. more than about six
+ * million edges in any order -- returns EQTP_ETOOLARGE before any launch;
+ * dst-sorted edges need none.  Every call on a device shares that device's
+ * array, so calls that overlap on one device (other streams, other threads)
+ * race and must be serialised by the caller; consecutive calls on one stream
+ * are safe.  The first call on a device looks up the array's address there.
+ * Arguments, layouts, results and other errors as for eqtp_conv_fused_ws.
+ */
+int eqtp_conv_fused_noalloc(const eqtp_conv_desc* d, int64_t N, int64_t E, const float* vec, const int32_t* src,
+                            const int32_t* dst, const int32_t* row_ptr, const void* x, const float* weights,
+                            float* out, void* stream);
 
 /*
  * Per-edge messages, without the destination sum (the page's fused kernel,

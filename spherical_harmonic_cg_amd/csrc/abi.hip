@@ -4,10 +4,19 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/eqtp.h"
 #include "eqtp_device.hpp"
 #include "eqtp_kernels.hpp"
 #include "generated/so2_tables.inc"
+
+// The static scratch of eqtp_conv_fused_noalloc: the workspace of the grouping
+// by destination, one array per device (each GPU holds its own copy for the
+// life of the process).  Host code never uses this name as an address: the
+// device address comes from hipGetSymbolAddress, once per device.
+constexpr int64_t kScratchBytes = (int64_t)128 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 namespace {
 
@@ -229,6 +238,47 @@ int eqtp_conv_fused_ws(const eqtp_conv_desc* d, int64_t N, int64_t E, const floa
   return conv_ws_impl(d, N, E, vec, src, dst, row_ptr, x, weights, out, workspace, workspace_bytes, stream);
 }
 
+}  // extern "C"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// device address of the current device's scratch array, looked up on the first call on that device
+int scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return EQTP_EHIP;
+  if (dev < 0 || dev >= kMaxDevices) return EQTP_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return EQTP_EHIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return EQTP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int eqtp_conv_fused_noalloc(const eqtp_conv_desc* d, int64_t N, int64_t E, const float* vec, const int32_t* src,
+                            const int32_t* dst, const int32_t* row_ptr, const void* x, const float* weights,
+                            float* out, void* stream) {
+  const int64_t need = eqtp_conv_workspace_bytes(d, N, E);
+  if (need < 0) return (int)-need;
+  if (need > kScratchBytes) return EQTP_ETOOLARGE;
+  void* ws = nullptr;
+  if (need > 0) {
+    const int rc = scratch_address(&ws);
+    if (rc != EQTP_OK) return rc;
+  }
+  return conv_ws_impl(d, N, E, vec, src, dst, row_ptr, x, weights, out, ws, kScratchBytes, stream);
+}
+
 int eqtp_conv_messages(const eqtp_conv_desc* d, int64_t N, int64_t E, const float* vec, const int32_t* src,
                        const float* x, const float* weights, float* messages, void* stream) {
   if (!desc_ok(d)) return EQTP_EINVAL;
@@ -401,6 +451,7 @@ const char* eqtp_status_string(int status) {
     case EQTP_EINVAL: return "EQTP_EINVAL: invalid argument";
     case EQTP_EUNSUPPORTED: return "EQTP_EUNSUPPORTED: request not supported by this build";
     case EQTP_EHIP: return "EQTP_EHIP: HIP runtime error at launch";
+    case EQTP_ETOOLARGE: return "EQTP_ETOOLARGE: the request needs more than the library's static scratch";
     default: return "unknown status";
   }
 }

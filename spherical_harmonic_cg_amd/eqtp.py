@@ -17,7 +17,7 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libeqtp.so")
 
-EQTP_OK, EQTP_EINVAL, EQTP_EUNSUPPORTED, EQTP_EHIP = 0, 1, 2, 3
+EQTP_OK, EQTP_EINVAL, EQTP_EUNSUPPORTED, EQTP_EHIP, EQTP_ETOOLARGE = 0, 1, 2, 3, 4
 EQTP_PATHS_PARITY, EQTP_PATHS_SO3 = 0, 1
 EQTP_W_FIXED, EQTP_W_RADIAL = 0, 1
 EQTP_EDGES_DST_SORTED, EQTP_EDGES_UNSORTED = 0, 1
@@ -25,7 +25,7 @@ EQTP_ALGO_AUTO, EQTP_ALGO_NODE_MFMA, EQTP_ALGO_EDGE_VALU, EQTP_ALGO_EDGE_SO2 = 0
 EQTP_F32, EQTP_BF16, EQTP_F32_BF16 = 0, 1, 2
 
 EXPORTED = ("eqtp_num_paths", "eqtp_path_table", "eqtp_sh", "eqtp_conv_fused", "eqtp_conv_workspace_bytes",
-            "eqtp_conv_fused_ws", "eqtp_conv_messages",
+            "eqtp_conv_fused_ws", "eqtp_conv_fused_noalloc", "eqtp_conv_messages",
             "eqtp_conv_backward", "eqtp_conv_backward_by_source", "eqtp_edge_rows", "eqtp_sort_edges",
             "eqtp_linear",
             "eqtp_status_string", "eqtp_test_segment_probe")
@@ -69,6 +69,8 @@ def load_library(path: str = LIB_PATH):
             lib.eqtp_conv_workspace_bytes.restype = i64
             lib.eqtp_conv_fused_ws.argtypes = [ctypes.POINTER(_ConvDesc), i64, i64] + [vp] * 8 + [i64, vp]
             lib.eqtp_conv_fused_ws.restype = i32
+            lib.eqtp_conv_fused_noalloc.argtypes = [ctypes.POINTER(_ConvDesc), i64, i64] + [vp] * 8
+            lib.eqtp_conv_fused_noalloc.restype = i32
             lib.eqtp_conv_messages.argtypes = [ctypes.POINTER(_ConvDesc), i64, i64] + [vp] * 6
             lib.eqtp_conv_messages.restype = i32
             lib.eqtp_conv_backward.argtypes = [ctypes.POINTER(_ConvDesc), i64, i64] + [vp] * 11
@@ -239,6 +241,19 @@ def eqtp_conv_fused_ws(vec, src, x, weights, lmax: int, row_ptr=None, dst=None, 
                                            _ptr(x), _ptr(weights), _ptr(out), _ptr(workspace), workspace.numel(),
                                            _stream())
     _raise(rc, "eqtp_conv_fused_ws")
+    return out
+
+
+def eqtp_conv_fused_noalloc(vec, src, x, weights, lmax: int, row_ptr=None, dst=None,
+                            path_set: int = EQTP_PATHS_PARITY, weight_mode: int = EQTP_W_FIXED, r_cut: float = 0.0,
+                            n_basis: int = 8, algo: int = EQTP_ALGO_AUTO, out=None):
+    """eqtp_conv_fused_ws with the library's static scratch as the workspace (no device allocation by
+    the library; ``out`` must be given for a call that allocates nothing at all)."""
+    d, N, E, out = _conv_args(vec, src, x, weights, lmax, row_ptr, dst, path_set, weight_mode, r_cut, n_basis, algo,
+                              out)
+    rc = load_library().eqtp_conv_fused_noalloc(ctypes.byref(d), N, E, _ptr(vec), _ptr(src), _ptr(dst),
+                                                _ptr(row_ptr), _ptr(x), _ptr(weights), _ptr(out), _stream())
+    _raise(rc, "eqtp_conv_fused_noalloc")
     return out
 
 

@@ -263,3 +263,15 @@ def test_conv_ws_validation():
     assert call(ctypes.c_void_p(0x10008), need) == 1              # misaligned workspace
     assert lib.eqtp_conv_fused_ws(ctypes.byref(d), 100, 1000, FAKE, FAKE, NULL, NULL, FAKE, FAKE, FAKE, FAKE, need,
                                   NULL) == 1                      # no dst
+
+
+def test_noalloc_refuses_beyond_its_scratch():
+    e = _lib()
+    lib = e.load_library()
+    d = _desc(e, edge_order=1)
+    assert lib.eqtp_conv_workspace_bytes(ctypes.byref(d), 100000, 10000000) > (128 << 20)
+    assert lib.eqtp_conv_fused_noalloc(ctypes.byref(d), 100000, 10000000, FAKE, FAKE, FAKE, NULL, FAKE, FAKE, FAKE,
+                                       NULL) == e.EQTP_ETOOLARGE
+    assert lib.eqtp_conv_fused_noalloc(ctypes.byref(d), -1, 10, FAKE, FAKE, FAKE, NULL, FAKE, FAKE, FAKE,
+                                       NULL) == 1
+    assert b"scratch" in lib.eqtp_status_string(e.EQTP_ETOOLARGE)
