@@ -79,6 +79,13 @@ def _load():
             lib.oracle_conv_backward.restype = i32
             lib.oracle_conv_backward_f64.argtypes = [i64, i64, i32, i32, i32] + [vp] * 9
             lib.oracle_conv_backward_f64.restype = i32
+            for fn in (lib.oracle_conv_backward_radial, lib.oracle_conv_backward_radial_f64):
+                fn.argtypes = [i64, i64, i32, i32, i32, f64, i32] + [vp] * 9
+                fn.restype = i32
+            lib.oracle_envelope_deriv.argtypes = [f64]
+            lib.oracle_envelope_deriv.restype = f64
+            lib.oracle_radial_basis_deriv.argtypes = [f64, f64, i32, vp]
+            lib.oracle_radial_basis_deriv.restype = None
             lib.oracle_set_threads.argtypes = [i32]
             lib.oracle_set_threads.restype = None
             lib.oracle_num_threads.argtypes = []
@@ -275,6 +282,48 @@ def conv_backward(N, vec, src, dst, x, w, gout, lmax, path_set=PATHS_PARITY):
     if rc != 0:
         raise ValueError("oracle_conv_backward failed (rc=%d)" % rc)
     return gx, gw, gv
+
+
+def envelope_deriv(d: float) -> float:
+    return _load().oracle_envelope_deriv(float(d))
+
+
+def radial_basis_deriv(r: float, r_cut: float, n_basis: int = 8) -> np.ndarray:
+    dR = np.empty(n_basis, dtype=np.float64)
+    _load().oracle_radial_basis_deriv(float(r), float(r_cut), n_basis, _p(dR))
+    return dR
+
+
+def conv_backward_radial(N, vec, src, dst, x, W, gout, lmax, r_cut, path_set=PATHS_PARITY, n_basis=8,
+                         need=(True, True, True)):
+    """(gx [N,C,K], gW [n_basis, P*C], gvec [E,3]) fp64: gradients of
+    sum(gout * out) for the radial-weight convolution (see
+    oracle_conv_backward_radial in the C source); an output not in ``need``
+    (x, W, vec) is None.  float64 ``x`` selects the double entry point."""
+    lib = _load()
+    is64 = np.asarray(x).dtype == np.float64
+    cast = _f64 if is64 else _f32
+    v = cast(vec).reshape(-1, 3)
+    s = _i32(src)
+    d = _i32(dst)
+    xx, ww, gg = cast(x), cast(W), cast(gout)
+    E = v.shape[0]
+    C = xx.shape[1]
+    K = (lmax + 1) ** 2
+    P = paths(lmax, path_set).shape[0]
+    if (xx.shape != (N, C, K) or gg.shape != (N, C, K) or ww.shape != (n_basis, P * C) or s.shape != (E,)
+            or d.shape != (E,)):
+        raise ValueError("shape mismatch")
+    gx = np.empty((N, C, K), dtype=np.float64) if need[0] else None
+    gW = np.empty((n_basis, P * C), dtype=np.float64) if need[1] else None
+    gv = np.empty((E, 3), dtype=np.float64) if need[2] else None
+    fn = lib.oracle_conv_backward_radial_f64 if is64 else lib.oracle_conv_backward_radial
+    rc = fn(N, E, lmax, C, path_set, float(r_cut), n_basis, _p(v), _p(s), _p(d), _p(xx), _p(ww), _p(gg),
+            _p(gx) if gx is not None else None, _p(gW) if gW is not None else None,
+            _p(gv) if gv is not None else None)
+    if rc != 0:
+        raise ValueError("oracle_conv_backward_radial failed (rc=%d)" % rc)
+    return gx, gW, gv
 
 
 def messages(N, vec, src, x, w, lmax, path_set=PATHS_PARITY, weight_mode=0, r_cut=0.0, n_basis=8) -> np.ndarray:

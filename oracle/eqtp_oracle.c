@@ -32,6 +32,9 @@
  *     by a path index (34 entries, i.e. every (l1,l2,l3<=3) triangle triple);
  *   - section "3. operator fusion": edge vectors [E,3], node features
  *     [N,C,16], source indices [E]; one message per edge.
+ * The gradients (fixed and radial weights) are those of L = sum gout * out,
+ * written out term by term from the forward's definition; the radial ones
+ * add the derivative of the radial basis (product and chain rule).
  * Readings where the page is silent (all stated in the design notes):
  *   path weights are per path and per channel (channel-wise "uvu" product),
  *   messages are summed into dst with no normalisation, a zero-length edge
@@ -675,6 +678,203 @@ int oracle_conv_backward(int64_t N, int64_t E, int lmax, int C, int path_set, co
   double* ww = widen(w, (int64_t)P * C);
   double* gg = widen(gout, N * C * K);
   int rc = oracle_conv_backward_f64(N, E, lmax, C, path_set, v, src, dst, xx, ww, gg, gx, gw, gvec);
+  free(v);
+  free(xx);
+  free(ww);
+  free(gg);
+  return rc;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Gradients of the convolution with radial weights                          */
+/* ------------------------------------------------------------------------ */
+
+/* Derivative of the p = 6 envelope: u'(d) = -168 d^5 + 336 d^6 - 168 d^7 for
+ * d < 1, else 0 (u, u' and u'' all vanish at d = 1). */
+double oracle_envelope_deriv(double d) {
+  if (d >= 1.0) return 0.0;
+  double d5 = d * d * d * d * d;
+  return -168.0 * d5 + 336.0 * d5 * d - 168.0 * d5 * d * d;
+}
+
+/* dR_n/dr of oracle_radial_basis, n = 1..n_basis: with a = n pi / r_c,
+ *   d/dr [sin(a r)/r u(r/r_c)] = (a r cos(a r) - sin(a r)) / r^2 u(r/r_c) + sin(a r)/r u'(r/r_c) / r_c.
+ * For a r < 1e-2 the first quotient (a difference of nearly equal terms over
+ * a vanishing r^2) is taken from its Taylor series
+ * -a^3 r / 3 + a^5 r^3 / 30 - a^7 r^5 / 840 (next term a^9 r^7 / 45360, below
+ * 1e-16 relative there); at r = 0 it is 0, and so is u'(0), so dR = 0.
+ * Likewise sin(a r)/r is taken as a for r = 0. */
+void oracle_radial_basis_deriv(double r, double r_cut, int n_basis, double* dR) {
+  double d = r / r_cut;
+  double u = oracle_envelope(d), du = oracle_envelope_deriv(d) / r_cut;
+  for (int n = 1; n <= n_basis; ++n) {
+    double a = (double)n * M_PI / r_cut;
+    double ar = a * r;
+    double ds, s;
+    if (ar < 1e-2) {
+      double a3r = a * a * a * r, ar2 = ar * ar;
+      ds = -a3r / 3.0 + a3r * ar2 / 30.0 - a3r * ar2 * ar2 / 840.0;
+      s = r == 0.0 ? a : sin(ar) / r;
+    } else {
+      ds = (ar * cos(ar) - sin(ar)) / (r * r);
+      s = sin(ar) / r;
+    }
+    dR[n - 1] = ds * u + s * du;
+  }
+}
+
+#define OR_BWD_BLOCK 1024 /* source nodes per partial sum of grad_W */
+
+/* Gradients of L = sum_{n,c,k} gout[n,c,k] out[n,c,k] for the radial-weight
+ * convolution (weight_mode 1 of oracle_conv_f64), where edge e = (s -> d) has
+ * the path weights w_e[p,c] = sum_b R_b(r_e) W[b, p*C + c], r_e = |vec_e|:
+ *   gx[s,c,l1 m1]  = sum_{e: src_e = s} sum_p w_e[p,c] sum_{m2,m3} C^p Y_e[l2 m2] gout[d,c,l3 m3]
+ *   T_e[p,c]       = sum_{m1,m2,m3} C^p x[s,c,l1 m1] Y_e[l2 m2] gout[d,c,l3 m3]   (dL/dw_e[p,c])
+ *   gW[b, p*C + c] = sum_e R_b(r_e) T_e[p,c]
+ *   dL/dY_e[l2 m2] = sum_c sum_p w_e[p,c] sum_{m1,m3} C^p x[s,c,l1 m1] gout[d,c,l3 m3]
+ *   dL/dR_b(e)     = sum_{p,c} W[b, p*C + c] T_e[p,c]
+ *   gvec[e]        = sum_k dL/dY_e[k] dY_k/dvec_e + (sum_b dL/dR_b(e) R_b'(r_e)) vec_e / r_e
+ * (the last term is 0 for a zero-length edge).  gW is [n_basis, P*C].  The
+ * edges are grouped by source, stably; blocks of OR_BWD_BLOCK source nodes are
+ * shared out over the threads, each block sums its edges' gW terms in order
+ * into a partial of its own, and the partials are added in block order, so
+ * the result does not depend on the thread count.  Any of gx, gW, gvec may
+ * be NULL.  Returns 0, 1 on bad arguments, 2 if an index is out of range
+ * (the requested outputs are then zero). */
+int oracle_conv_backward_radial_f64(int64_t N, int64_t E, int lmax, int C, int path_set, double r_cut,
+                                    int n_basis, const double* vec, const int32_t* src, const int32_t* dst,
+                                    const double* x, const double* W, const double* gout, double* gx, double* gW,
+                                    double* gvec) {
+  if (lmax < 0 || lmax > OR_MAX_L || C <= 0 || N < 0 || E < 0) return 1;
+  if (n_basis <= 0 || n_basis > 64 || !(r_cut > 0.0)) return 1;
+  int K = (lmax + 1) * (lmax + 1);
+  path_blocks pb;
+  if (path_blocks_make(lmax, path_set, &pb)) return 1;
+  int P = pb.P;
+  int64_t PC = (int64_t)P * C;
+  if (gx)
+    for (int64_t i = 0; i < N * C * K; ++i) gx[i] = 0.0;
+  if (gW)
+    for (int64_t i = 0; i < n_basis * PC; ++i) gW[i] = 0.0;
+  if (gvec)
+    for (int64_t i = 0; i < 3 * E; ++i) gvec[i] = 0.0;
+  for (int64_t e = 0; e < E; ++e)
+    if (src[e] < 0 || src[e] >= N || dst[e] < 0 || dst[e] >= N) {
+      path_blocks_free(&pb);
+      return 2;
+    }
+  /* edges grouped by source, in their given order inside each group */
+  int64_t* start = (int64_t*)calloc((size_t)N + 1, sizeof(int64_t));
+  int64_t* order = (int64_t*)malloc(sizeof(int64_t) * (E > 0 ? E : 1));
+  int64_t* fill = (int64_t*)malloc(sizeof(int64_t) * (N > 0 ? N : 1));
+  for (int64_t e = 0; e < E; ++e) start[src[e] + 1]++;
+  for (int64_t n = 0; n < N; ++n) start[n + 1] += start[n];
+  for (int64_t n = 0; n < N; ++n) fill[n] = start[n];
+  for (int64_t e = 0; e < E; ++e) order[fill[src[e]]++] = e;
+  free(fill);
+  int64_t nblk = (N + OR_BWD_BLOCK - 1) / OR_BWD_BLOCK;
+  double* part = gW ? (double*)calloc((size_t)(nblk > 0 ? nblk : 1) * n_basis * PC, sizeof(double)) : NULL;
+#pragma omp parallel num_threads(oracle_num_threads())
+  {
+    double* Y = (double*)malloc(sizeof(double) * K);
+    double* Y2 = (double*)malloc(sizeof(double) * K);
+    double* G = (double*)malloc(sizeof(double) * K * 3);
+    double* dY = (double*)malloc(sizeof(double) * K);
+    double* we = (double*)malloc(sizeof(double) * PC);
+    double* T = (double*)malloc(sizeof(double) * PC);
+    double R[64], dR[64];
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t blk = 0; blk < nblk; ++blk) {
+      int64_t n_end = (blk + 1) * OR_BWD_BLOCK < N ? (blk + 1) * OR_BWD_BLOCK : N;
+      for (int64_t i = start[blk * OR_BWD_BLOCK]; i < start[n_end]; ++i) {
+        int64_t e = order[i];
+        int64_t s = src[e], d = dst[e];
+        double vx = vec[3 * e], vy = vec[3 * e + 1], vz = vec[3 * e + 2];
+        double r = sqrt(vx * vx + vy * vy + vz * vz);
+        /* radial functions, path weights and harmonics of the edge */
+        oracle_radial_basis(r, r_cut, n_basis, R);
+        oracle_radial_basis_deriv(r, r_cut, n_basis, dR);
+        for (int64_t q = 0; q < PC; ++q) {
+          double acc = 0.0;
+          for (int b = 0; b < n_basis; ++b) acc += R[b] * W[b * PC + q];
+          we[q] = acc;
+          T[q] = 0.0;
+        }
+        real_sh(lmax, vx, vy, vz, Y);
+        real_sh_grad(lmax, vx, vy, vz, Y2, G);
+        for (int k = 0; k < K; ++k) dY[k] = 0.0;
+        /* the coupling, term by term */
+        for (int p = 0; p < P; ++p) {
+          int l1 = pb.paths[3 * p], l2 = pb.paths[3 * p + 1], l3 = pb.paths[3 * p + 2];
+          int n1 = 2 * l1 + 1, n2 = 2 * l2 + 1, n3 = 2 * l3 + 1;
+          for (int a = 0; a < n1; ++a)
+            for (int b2 = 0; b2 < n2; ++b2)
+              for (int c3 = 0; c3 < n3; ++c3) {
+                double coef = pb.cg[p][(a * n2 + b2) * n3 + c3];
+                if (coef == 0.0) continue;
+                for (int ch = 0; ch < C; ++ch) {
+                  double xv = x[(s * C + ch) * K + l1 * l1 + a];
+                  double gv = gout[(d * C + ch) * K + l3 * l3 + c3];
+                  double yv = Y[l2 * l2 + b2];
+                  double wv = we[p * C + ch];
+                  if (gx) gx[(s * C + ch) * K + l1 * l1 + a] += wv * coef * yv * gv;
+                  T[p * C + ch] += coef * xv * yv * gv;
+                  dY[l2 * l2 + b2] += wv * coef * xv * gv;
+                }
+              }
+        }
+        /* grad_W: this block's partial */
+        if (part)
+          for (int b = 0; b < n_basis; ++b)
+            for (int64_t q = 0; q < PC; ++q) part[(blk * n_basis + b) * PC + q] += R[b] * T[q];
+        if (gvec) {
+          double dr = 0.0; /* dL/dr_e */
+          for (int b = 0; b < n_basis; ++b) {
+            double dLdR = 0.0;
+            for (int64_t q = 0; q < PC; ++q) dLdR += W[b * PC + q] * T[q];
+            dr += dLdR * dR[b];
+          }
+          for (int ax = 0; ax < 3; ++ax) {
+            double acc = 0.0;
+            for (int k = 0; k < K; ++k) acc += dY[k] * G[3 * k + ax];
+            if (r > 0.0) acc += dr * vec[3 * e + ax] / r;
+            gvec[3 * e + ax] = acc;
+          }
+        }
+      }
+    }
+    free(Y);
+    free(Y2);
+    free(G);
+    free(dY);
+    free(we);
+    free(T);
+  }
+  if (gW)
+    for (int64_t blk = 0; blk < nblk; ++blk)
+      for (int64_t q = 0; q < n_basis * PC; ++q) gW[q] += part[blk * n_basis * PC + q];
+  free(part);
+  free(start);
+  free(order);
+  path_blocks_free(&pb);
+  return 0;
+}
+
+/* float32 entry point: inputs widened exactly to double. */
+int oracle_conv_backward_radial(int64_t N, int64_t E, int lmax, int C, int path_set, double r_cut, int n_basis,
+                                const float* vec, const int32_t* src, const int32_t* dst, const float* x,
+                                const float* W, const float* gout, double* gx, double* gW, double* gvec) {
+  if (lmax < 0 || lmax > OR_MAX_L || C <= 0 || N < 0 || E < 0) return 1;
+  if (n_basis <= 0 || n_basis > 64) return 1;
+  int K = (lmax + 1) * (lmax + 1);
+  int P = oracle_paths(lmax, path_set, NULL);
+  if (P <= 0) return 1;
+  double* v = widen(vec, 3 * E);
+  double* xx = widen(x, N * C * K);
+  double* ww = widen(W, (int64_t)n_basis * P * C);
+  double* gg = widen(gout, N * C * K);
+  int rc = oracle_conv_backward_radial_f64(N, E, lmax, C, path_set, r_cut, n_basis, v, src, dst, xx, ww, gg, gx,
+                                           gW, gvec);
   free(v);
   free(xx);
   free(ww);

@@ -42,6 +42,15 @@ int oracle_conv_backward_f64(int64_t N, int64_t E, int lmax, int C, int path_set
 int oracle_conv_backward(int64_t N, int64_t E, int lmax, int C, int path_set, const float* vec, const int32_t* src,
                          const int32_t* dst, const float* x, const float* w, const float* gout, double* gx,
                          double* gw, double* gvec);
+double oracle_envelope_deriv(double d);
+void oracle_radial_basis_deriv(double r, double r_cut, int n_basis, double* dR);
+int oracle_conv_backward_radial_f64(int64_t N, int64_t E, int lmax, int C, int path_set, double r_cut,
+                                    int n_basis, const double* vec, const int32_t* src, const int32_t* dst,
+                                    const double* x, const double* W, const double* gout, double* gx, double* gW,
+                                    double* gvec);
+int oracle_conv_backward_radial(int64_t N, int64_t E, int lmax, int C, int path_set, double r_cut, int n_basis,
+                                const float* vec, const int32_t* src, const int32_t* dst, const float* x,
+                                const float* W, const float* gout, double* gx, double* gW, double* gvec);
 float oracle_round_bf16(float f);
 int oracle_linear_f64(int64_t N, int C, int lmax, const double* h, const double* W, double* out);
 int oracle_linear(int64_t N, int C, int lmax, int bf16, const float* h, const float* W, double* out);
@@ -152,10 +161,14 @@ static void test_radial(void) {
     for (int nb = 1; nb <= 64; nb *= 2) {
       oracle_radial_basis(rs[i], 5.0, nb, R);
       for (int b = 0; b < nb; ++b) EXPECT(isfinite(R[b]));
+      oracle_radial_basis_deriv(rs[i], 5.0, nb, R);
+      for (int b = 0; b < nb; ++b) EXPECT(isfinite(R[b]));
     }
   EXPECT(oracle_envelope(1.0) == 0.0);
   EXPECT(oracle_envelope(0.0) == 1.0);
   EXPECT(oracle_envelope(2.0) == 0.0);
+  EXPECT(oracle_envelope_deriv(0.0) == 0.0);
+  EXPECT(oracle_envelope_deriv(1.5) == 0.0);
 }
 
 /* one convolution case: forward (fp64 and fp32 entry points), messages and,
@@ -192,6 +205,32 @@ static void conv_case(int64_t N, int64_t E, int lmax, int C, int ps, int wm, int
   EXPECT(oracle_conv(N, E, lmax, C, ps, wm, 5.0, NB, vf, src, dst, xf, wf, out) == want);
   EXPECT(oracle_messages_f64(N, E, lmax, C, ps, wm, 5.0, NB, v, src, x, w, msg) == want);
   EXPECT(oracle_messages(N, E, lmax, C, ps, wm, 5.0, NB, vf, src, xf, wf, msg) == want);
+  {
+    /* radial-weight gradients (their own weights [8, P*C]), every subset of outputs */
+    const int64_t nr = (int64_t)NB * P * C;
+    double* Wr = (double*)xmalloc(sizeof(double) * nr);
+    float* Wrf = (float*)xmalloc(sizeof(float) * nr);
+    double* gout = (double*)xmalloc(sizeof(double) * N * C * K);
+    float* goutf = (float*)xmalloc(sizeof(float) * N * C * K);
+    double* gx = (double*)xmalloc(sizeof(double) * N * C * K);
+    double* gW = (double*)xmalloc(sizeof(double) * nr);
+    double* gvec = (double*)xmalloc(sizeof(double) * 3 * E);
+    for (int64_t i = 0; i < nr; ++i) Wrf[i] = (float)(Wr[i] = uniform(-1.0, 1.0));
+    for (int64_t i = 0; i < N * C * K; ++i) goutf[i] = (float)(gout[i] = uniform(-1.0, 1.0));
+    for (int mask = 0; mask < 8; ++mask)
+      EXPECT(oracle_conv_backward_radial_f64(N, E, lmax, C, ps, 5.0, NB, v, src, dst, x, Wr, gout,
+                                             (mask & 1) ? gx : NULL, (mask & 2) ? gW : NULL,
+                                             (mask & 4) ? gvec : NULL) == want);
+    EXPECT(oracle_conv_backward_radial(N, E, lmax, C, ps, 5.0, NB, vf, src, dst, xf, Wrf, goutf, gx, gW, gvec) ==
+           want);
+    free(Wr);
+    free(Wrf);
+    free(gout);
+    free(goutf);
+    free(gx);
+    free(gW);
+    free(gvec);
+  }
   if (!wm) {
     double* gout = (double*)xmalloc(sizeof(double) * N * C * K);
     float* goutf = (float*)xmalloc(sizeof(float) * N * C * K);
@@ -240,6 +279,10 @@ static void test_conv(void) {
   EXPECT(oracle_conv(1, 0, 2, 1, 3, 0, 5.0, 8, NULL, NULL, NULL, NULL, NULL, NULL) == 1);
   EXPECT(oracle_messages(-1, 0, 2, 1, 0, 0, 5.0, 8, NULL, NULL, NULL, NULL, NULL) == 1);
   EXPECT(oracle_conv_backward(1, 0, 2, 1, 5, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL) == 1);
+  EXPECT(oracle_conv_backward_radial_f64(1, 0, 2, 1, 0, 0.0, 8, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL,
+                                         NULL) == 1);
+  EXPECT(oracle_conv_backward_radial(1, 0, 2, 1, 0, 5.0, 65, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL) ==
+         1);
 }
 
 static void test_linear(void) {
