@@ -393,8 +393,36 @@ def main():
 
     backward = None
     if args.backward:
-        if wl.weight_mode != 0 or args.x_bf16:
-            log("backward: fp32 features and fixed weights only; skipped for this workload")
+        if args.x_bf16:
+            log("backward: fp32 features only; skipped for this workload")
+        elif wl.weight_mode == 1:
+            gout = torch.randn(out.shape, dtype=torch.float32, device=dev)
+            bkw = dict(dst=dst) if args.unsorted else dict(row_ptr=row_ptr)
+            bvec, bsrc = vec, src
+            if sort_out is not None:
+                bkw = dict(row_ptr=sort_out[0])
+                bvec, bsrc = sort_out[2], sort_out[3]
+
+            def bwd_rad():
+                eq.eqtp_conv_backward(bvec, bsrc, x, w, gout, wl.lmax, path_set=wl.path_set, weight_mode=1,
+                                      r_cut=wl.r_cut, **bkw)
+
+            for _ in range(3):
+                bwd_rad()
+            torch.cuda.synchronize()
+            kb = max(5, K // 4)
+            b0 = torch.cuda.Event(enable_timing=True)
+            b1 = torch.cuda.Event(enable_timing=True)
+            b0.record(stream)
+            for _ in range(kb):
+                bwd_rad()
+            b1.record(stream)
+            torch.cuda.synchronize()
+            rms = b0.elapsed_time(b1) / kb
+            backward = {"ms": round(rms, 5), "edges_per_s": round(wl.E / (rms * 1e-3), 1), "launches": kb,
+                        "what": "grad_x, grad_W [8, P*C] and grad_vec of the radial-weight conv "
+                                "(eqtp_conv_backward with EQTP_W_RADIAL: zero fills + one kernel)"}
+            log("backward (radial weights): %.4f ms (%.3e edges/s)" % (rms, wl.E / (rms * 1e-3)))
         else:
             gout = torch.randn(out.shape, dtype=torch.float32, device=dev)
             bkw = dict(dst=dst) if args.unsorted else dict(row_ptr=row_ptr)

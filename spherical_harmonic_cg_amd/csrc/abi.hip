@@ -339,7 +339,11 @@ int eqtp_conv_backward(const eqtp_conv_desc* d, int64_t N, int64_t E, const floa
   if (d->edge_order != EQTP_EDGES_DST_SORTED && d->edge_order != EQTP_EDGES_UNSORTED) return EQTP_EINVAL;
   if (d->C <= 0) return EQTP_EINVAL;
   if (!valid_c(d->C)) return EQTP_EUNSUPPORTED;
-  if (d->weight_mode == EQTP_W_RADIAL) return EQTP_EUNSUPPORTED;
+  const bool radial = d->weight_mode == EQTP_W_RADIAL;
+  if (radial) {
+    if (!(d->r_cut > 0.0f)) return EQTP_EINVAL;
+    if (d->n_basis != 8 || d->C % 16 != 0) return EQTP_EUNSUPPORTED;
+  }
   if (N < 0 || E < 0 || N > kMaxIndex || E > kMaxIndex) return EQTP_EINVAL;
   if (E > 0 && N == 0) return EQTP_EINVAL;
   if (!grad_x && !grad_w && !grad_vec) return EQTP_EINVAL;
@@ -369,8 +373,9 @@ int eqtp_conv_backward(const eqtp_conv_desc* d, int64_t N, int64_t E, const floa
   a.gw = grad_w;
   a.gvec = grad_vec;
   a.algo = d->algo;
+  a.r_cut = d->r_cut;
   a.stream = (hipStream_t)stream;
-  return status_of(eqtp::launch_conv_backward(a));
+  return status_of(radial ? eqtp::launch_conv_backward_radial(a) : eqtp::launch_conv_backward(a));
 }
 
 int eqtp_conv_backward_by_source(const eqtp_conv_desc* d, int64_t N, int64_t E, const float* vec_s,

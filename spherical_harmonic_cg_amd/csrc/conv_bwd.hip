@@ -113,6 +113,10 @@ struct TermOrder {
   static constexpr const eqtp_gen::CgTerm& term(int j) { return T::by_out[order.v[j]]; }
   static constexpr bool first(int j) { return j == 0 || key(order.v[j - 1]) != key(order.v[j]); }
   static constexpr bool last(int j) { return j + 1 == T::NT || key(order.v[j + 1]) != key(order.v[j]); }
+  // the terms of one path are contiguous too (the key is path-major)
+  static constexpr int path(int j) { return T::by_out[order.v[j]].p; }
+  static constexpr bool path_first(int j) { return j == 0 || path(j - 1) != path(j); }
+  static constexpr bool path_last(int j) { return j + 1 == T::NT || path(j + 1) != path(j); }
 };
 
 
@@ -571,6 +575,383 @@ hipError_t launch_conv_backward(const BwdArgs& a) {
     case 5: return dispatch_bwd_c<2, 1>(a);
     case 6: return dispatch_bwd_c<3, 0>(a);
     case 7: return dispatch_bwd_c<3, 1>(a);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// The radial basis and its derivative in r:
+//   dR_n/dr = (a cos(a r) - sin(a r)/r) / r * u + sin(a r)/r * u'(d) / r_c,  a = n pi / r_c,
+// with u'(d) = -168 d^5 + 336 d^6 - 168 d^7.  For a r < 1/2 the first term's
+// difference of nearly equal quotients is replaced by its Taylor series
+// -a^3 r / 3 (1 - t/10 + t^2/280 - t^3/15120), t = (a r)^2 (truncation below
+// 3e-9 relative there).  Zero for d >= 1 and at r = 0.
+template <int NB>
+__device__ __forceinline__ void radial_basis_grad(float r, float inv_rc, float (&R)[NB], float (&dR)[NB]) {
+  // branch-free (selects only): early returns that fill the arrays on several paths make the
+  // compiler keep them in private memory
+  const float d = r * inv_rc;
+  const bool inside = d < 1.0f, at_zero = r == 0.0f;
+  const float d2 = d * d, d4 = d2 * d2, d6 = d4 * d2;
+  const float env = 1.0f + d6 * (-28.0f + d * (48.0f - 21.0f * d));
+  const float denv = d4 * d * (-168.0f + d * (336.0f - 168.0f * d)) * inv_rc;  // du/dr
+  const float theta = eqtp_gen::kPiF * (inside ? d : 0.0f);  // in [0, pi)
+  // sin and cos of theta from their Taylor series on [0, pi/2] (terms to u^13 and u^14, truncation
+  // below 3e-8), folded by sin(pi - u) = sin u, cos(pi - u) = -cos u
+  const bool upper = theta > 0.5f * eqtp_gen::kPiF;
+  const float u = upper ? eqtp_gen::kPiF - theta : theta, u2 = u * u;
+  const float s1 =
+      u * (1.0f + u2 * (-1.0f / 6 + u2 * (1.0f / 120 + u2 * (-1.0f / 5040 + u2 * (1.0f / 362880 +
+          u2 * (-1.0f / 39916800 + u2 * (1.0f / 6227020800.0f)))))));
+  const float cu =
+      1.0f + u2 * (-0.5f + u2 * (1.0f / 24 + u2 * (-1.0f / 720 + u2 * (1.0f / 40320 + u2 * (-1.0f / 3628800 +
+          u2 * (1.0f / 479001600 - u2 * (1.0f / 87178291200.0f)))))));
+  const float c1 = upper ? -cu : cu;
+  const float inv_r = at_zero ? 0.0f : 1.0f / r;
+  float sm1 = 0.0f, s = s1, cm1 = 1.0f, c = c1;  // sin, cos of n theta by the Chebyshev recurrence
+  const float c2 = 2.0f * c1;
+#pragma unroll
+  for (int n = 0; n < NB; ++n) {
+    const float a = (float)(n + 1) * eqtp_gen::kPiF * inv_rc;
+    const float ar = (float)(n + 1) * theta;
+    const float f = at_zero ? a : s * inv_r;  // sin(a r) / r, its limit a at r = 0
+    const float t = ar * ar;
+    const float series = -(a * a * a * r) * (1.0f / 3.0f) *
+                         (1.0f + t * (-0.1f + t * (1.0f / 280.0f - t * (1.0f / 15120.0f))));
+    const float df = ar < 0.5f ? series : (a * c - f) * inv_r;
+    R[n] = inside ? f * env : 0.0f;
+    dR[n] = inside ? df * env + f * denv : 0.0f;
+    const float sn = c2 * s - sm1, cn = c2 * c - cm1;
+    sm1 = s;
+    s = sn;
+    cm1 = c;
+    c = cn;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Gradients with radial weights, w_e[p,c] = sum_b R_b(r_e) W[b, p*C + c]
+// (the radial basis above, 8 functions; r_e = |vec_e|).  Per edge e = (s -> d)
+// and channel c, with s1 and s2 the coupling sums of the fixed-weight walk:
+//   grad_x[s,c,mu1]  += sum_p w_e[p,c] s1[p,mu1]
+//   T_e[p,c]          = sum_mu1 x[s,c,mu1] s1[p,mu1]        (dL/dw_e[p,c])
+//   grad_W[b,p*C+c]  += R_b(r_e) T_e[p,c]
+//   dL/dY_e[mu2]     += w_e[p,c] s2[p,mu2]
+//   dL/dr_e          += sum_b R_b'(r_e) sum_p W[b,p*C+c] T_e[p,c]
+//   grad_vec[e]       = sum_mu2 dL/dY_e[mu2] dY_mu2/dvec_e + dL/dr_e vec_e / r_e.
+// Lane layout: a workgroup works on one block of 16 channels (lane j of each
+// 16-lane group), its four waves on edges of their own (sorted: one row per
+// wave, rows strided over the block's workgroups; unsorted: runs of 64 edges),
+// four edges per round (lane group kq takes edge kq).  The block's slice of W
+// sits in LDS as [p][j][b] (two 16-byte reads give a lane the 8 weights of a
+// path), read one path ahead of its use.
+// Pass 1 walks the coupling in (path, mu1) order; after each path's runs the
+// lane adds w_p s1 into its grad_x sums, keeps (sum_b R_b' W_b) T_p for dL/dr
+// and stages T_p in LDS.  After the walk, per path, D[b][j] = sum_kq R_b(edge
+// kq) T_p(edge kq, j) is one v_mfma_f32_16x16x4_f32 (A rows = b, 8 of 16 used;
+// k = the round's four edges; B = the staged T_p), added into an LDS copy of
+// the block's grad_W slice with LDS atomics; the slice goes to memory once per
+// workgroup.  grad_x goes out as in the fixed-weight walk (the round's
+// 4 x 16 x K contributions through LDS, 64 contiguous floats per atomic
+// instruction).  Pass 2 walks in (path, mu2) order for dL/dY.  Each pass adds
+// its part of grad_vec (pass 1: dL/dr vec / r; pass 2: the harmonics' part),
+// reduced over the block's 16 channels, with fp32 atomics.  Lanes of a round
+// past the last edge load an in-range edge and zero its radial functions,
+// which zeroes all their contributions.
+// The walks are kept free of branches, and the running sums of each path are
+// settled (an empty asm that takes them as operands) before the next path
+// starts: otherwise the compiler is free to leave sums to the end of the walk
+// with all their inputs live, several hundred registers at lmax 3.
+// ---------------------------------------------------------------------------
+constexpr int kRbNB = 8;     // radial functions
+constexpr int kRbWaves = 4;  // waves per workgroup
+constexpr int kRbChunk = 64; // edges per run, unsorted edges
+
+template <int L, int PS, bool SORTED, int PASS>
+__global__ __launch_bounds__(kRbWaves * kWave) void conv_bwd_radial_kernel(
+    int N, int E, int C, int nwg, const int* __restrict__ row_ptr, const float* __restrict__ vec,
+    const int* __restrict__ src, const int* __restrict__ dst, const float* __restrict__ x,
+    const float* __restrict__ W, const float* __restrict__ gout, float* __restrict__ gx, float* __restrict__ gW,
+    float* __restrict__ gvec, float inv_rc) {
+  using T = Tables<L, PS>;
+  using O1 = TermOrder<L, PS, 1>;
+  using O2 = TermOrder<L, PS, 2>;
+  constexpr int K = num_comp(L);
+  constexpr int P = T::P;
+  constexpr int NB = kRbNB;
+  constexpr int XB = 16 * K;  // floats of one edge's block of 16 channels
+  __shared__ __attribute__((aligned(16))) float wt[P * 16 * NB];  // W slice, [p][j][b]
+  constexpr int GWL = PASS == 1 ? NB * P * 16 : 1;
+  __shared__ float gwl[GWL];  // pass 1: grad_W slice, [b][p][j]
+  // pass 1, per wave: the round's T_p (P x 64) during the walk, then its grad_x exchange (4 x XB)
+  constexpr int XCH = PASS == 1 ? (64 * P > 4 * XB ? 64 * P : 4 * XB) : 1;
+  __shared__ __attribute__((aligned(16))) float xch[kRbWaves][XCH];
+  __shared__ int xsrc[kRbWaves][4];
+  const int cb = (int)(blockIdx.x / nwg) * 16;
+  const int wg = (int)(blockIdx.x % nwg);
+  for (int i = threadIdx.x; i < P * 16 * NB; i += kRbWaves * kWave) {
+    const int b = i % NB, jj = (i / NB) % 16, p = i / (NB * 16);
+    wt[i] = W[(size_t)b * P * C + (size_t)p * C + cb + jj];
+    if constexpr (PASS == 1) gwl[i] = 0.0f;
+  }
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int j = lane & 15;   // channel cb + j
+  const int kq = lane >> 4;  // edge of the round
+  // pass 1: grad_x, grad_W and the radial part of grad_vec; pass 2: the harmonics' part of grad_vec
+  const bool want_x = PASS == 1 && gx != nullptr, want_w = PASS == 1 && gW != nullptr;
+  const bool want_v = gvec != nullptr;
+  float* const xw = xch[wv];
+
+  // one round: lane group kq takes edge e (valid) or, if past the end, edge e_alt with no weight
+  auto round = [&](int e, bool valid, int e_alt, const float (&grow)[K]) {
+    const int ec = valid ? e : e_alt;
+    const float vx = vec[3 * (size_t)ec], vy = vec[3 * (size_t)ec + 1], vz = vec[3 * (size_t)ec + 2];
+    const int s = clamp_index(src[ec], N);
+    float xv[K], gv[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) xv[k] = x[((size_t)s * C + cb + j) * K + k];
+    if constexpr (SORTED) {
+#pragma unroll
+      for (int k = 0; k < K; ++k) gv[k] = grow[k];
+    } else {
+      const int d = clamp_index(dst[ec], N);
+#pragma unroll
+      for (int k = 0; k < K; ++k) gv[k] = gout[((size_t)d * C + cb + j) * K + k];
+    }
+    float Y[16];
+    sh_eval<L>(vx, vy, vz, Y);
+    const float r = sqrtf(vx * vx + vy * vy + vz * vz);
+    float R[NB], dR[NB];
+    radial_basis_grad<NB>(r, inv_rc, R, dR);
+    if (!valid) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b) R[b] = dR[b] = 0.0f;
+    }
+    float g0 = 0.0f, g1 = 0.0f, g2 = 0.0f;  // this lane's part of grad_vec
+    // The lane's 8 weights of path p are read from LDS one path ahead.  The offset of each read passes
+    // through an empty asm that takes the previous path's w_p as input: the read can then not be issued
+    // before that path starts, so at most two paths' weights are held in registers at a time (the
+    // compiler would otherwise issue all 2 P reads up front).
+    int woff = j * NB;
+    asm volatile("" : "+v"(woff));
+    f4 nlo = reinterpret_cast<const f4*>(wt + woff)[0], nhi = reinterpret_cast<const f4*>(wt + woff)[1];
+    auto settle = [&](float (&v)[K]) {
+#pragma unroll
+      for (int k = 0; k < K; ++k) asm volatile("" : "+v"(v[k]));
+    };
+    auto prefetch = [&](int p_next, float after, float& settle) {
+      // settle: a running sum that must be complete here (else the compiler may leave its terms, and
+      // their inputs, live until the end of the walk)
+      asm volatile("" : "+v"(woff), "+v"(settle) : "v"(after));
+      const f4* wr = reinterpret_cast<const f4*>(wt + p_next * 16 * NB + woff);
+      nlo = wr[0];
+      nhi = wr[1];
+    };
+
+    if constexpr (PASS == 1) {
+      float aR = 0.0f;  // MFMA A operand: R_j of this lane's edge (rows j >= 8 are zero)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) aR = j == b ? R[b] : aR;
+      // (path, mu1) walk: grad_x, T_p -> grad_W and dL/dr
+      float mx[K];
+#pragma unroll
+      for (int k = 0; k < K; ++k) mx[k] = 0.0f;
+      // wp = sum_b R_b W_b (the path weight), wd = sum_b R_b' W_b (its derivative in r)
+      float wp = 0.0f, wd = 0.0f, tp = 0.0f, s1 = 0.0f, dr = 0.0f;
+      static_for<0, T::NT>([&](auto jj) {
+        constexpr int q = decltype(jj)::value;
+        constexpr eqtp_gen::CgTerm tm = O1::term(q);
+        if constexpr (O1::path_first(q)) {
+          wp = wd = 0.0f;
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            wp = fmaf(R[b], nlo[b], wp);
+            wp = fmaf(R[4 + b], nhi[b], wp);
+            wd = fmaf(dR[b], nlo[b], wd);
+            wd = fmaf(dR[4 + b], nhi[b], wd);
+          }
+          if constexpr (tm.p + 1 < P) {
+            prefetch(tm.p + 1, wp, dr);
+            settle(mx);  // likewise the grad_x sums: each path's terms are added before the next starts
+          }
+          tp = 0.0f;
+        }
+        const float cy = tm.c * Y[tm.mu2];
+        s1 = O1::first(q) ? cy * gv[tm.mu3] : fmaf(cy, gv[tm.mu3], s1);
+        if constexpr (O1::last(q)) {
+          mx[tm.mu1] = fmaf(wp, s1, mx[tm.mu1]);
+          tp = fmaf(xv[tm.mu1], s1, tp);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if constexpr (O1::path_last(q)) {
+          // (no branches in the walk: a branch per path splits it into blocks across which the compiler
+          // keeps common products live, several hundred registers at lmax 3)
+          dr = fmaf(wd, tp, dr);                // dL/dr += sum_b R_b' W_b T_p
+          xw[tm.p * kWave + lane] = tp;         // T_p of the round, for the grad_W products below
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      });
+      if (want_w) {
+        // grad_W: per path, D[b][j] = sum_kq R_b(edge kq) T_p(edge kq, j) on the matrix cores
+        wave_lds_sync();
+        for (int p = 0; p < P; ++p) {
+          const f4 dd = __builtin_amdgcn_mfma_f32_16x16x4f32(aR, xw[p * kWave + lane], f4{0.f, 0.f, 0.f, 0.f}, 0,
+                                                             0, 0);
+          if (lane < 32) {  // rows b = 4 kq + r < 8
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr)
+              __hip_atomic_fetch_add(&gwl[((4 * kq + rr) * P + p) * 16 + j], dd[rr], __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_WORKGROUP);
+          }
+        }
+        wave_lds_sync();
+      }
+      if (want_x) {
+#pragma unroll
+        for (int k = 0; k < K; ++k) xw[(kq * 16 + j) * K + k] = mx[k];
+        if (j == 0) xsrc[wv][kq] = valid ? s : -1;
+        wave_lds_sync();
+#pragma unroll
+        for (int t = 0; t < K; ++t) {  // 4 * XB floats = K instructions of 64
+          const int f = kWave * t + lane;
+          const int sd = xsrc[wv][f / XB];
+          if (sd >= 0) unsafeAtomicAdd(gx + ((size_t)sd * C + cb) * K + f % XB, xw[f]);
+        }
+        wave_lds_sync();
+      }
+      if (want_v && r > 0.0f) {  // the radial part: dL/dr along vec / r
+        const float qr = dr / r;
+        g0 = qr * vx;
+        g1 = qr * vy;
+        g2 = qr * vz;
+      }
+    } else {
+      // (path, mu2) walk: dL/dY, then through the harmonics' Jacobian
+      float dy[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) dy[k] = 0.0f;
+      float wp = 0.0f, s2 = 0.0f;
+      static_for<0, T::NT>([&](auto jj) {
+        constexpr int q = decltype(jj)::value;
+        constexpr eqtp_gen::CgTerm tm = O2::term(q);
+        if constexpr (O2::path_first(q)) {
+          wp = 0.0f;
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            wp = fmaf(R[b], nlo[b], wp);
+            wp = fmaf(R[4 + b], nhi[b], wp);
+          }
+          if constexpr (tm.p + 1 < P) {
+            float none = 0.0f;
+            prefetch(tm.p + 1, wp, none);
+          }
+        }
+        const float cx = tm.c * xv[tm.mu1];
+        s2 = O2::first(q) ? cx * gv[tm.mu3] : fmaf(cx, gv[tm.mu3], s2);
+        if constexpr (O2::last(q)) {
+          dy[tm.mu2] = fmaf(wp, s2, dy[tm.mu2]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      });
+      float Y2[16], Gm[16][3];
+      sh_grad_eval<L>(vx, vy, vz, Y2, Gm);
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        g0 = fmaf(dy[k], Gm[k][0], g0);
+        g1 = fmaf(dy[k], Gm[k][1], g1);
+        g2 = fmaf(dy[k], Gm[k][2], g2);
+      }
+    }
+    if (want_v) {  // the block's 16 channels, then one atomic per component
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) {
+        g0 += __shfl_xor(g0, off);
+        g1 += __shfl_xor(g1, off);
+        g2 += __shfl_xor(g2, off);
+      }
+      if (j == 0 && valid) {
+        unsafeAtomicAdd(gvec + 3 * (size_t)e, g0);
+        unsafeAtomicAdd(gvec + 3 * (size_t)e + 1, g1);
+        unsafeAtomicAdd(gvec + 3 * (size_t)e + 2, g2);
+      }
+    }
+  };
+
+  if constexpr (SORTED) {
+    for (int row = wg * kRbWaves + wv; row < N; row += nwg * kRbWaves) {
+      const int e_beg = min(max(row_ptr[row], 0), E);
+      const int e_end = min(max(row_ptr[row + 1], e_beg), E);
+      if (e_beg == e_end) continue;
+      float grow[K];
+#pragma unroll
+      for (int k = 0; k < K; ++k) grow[k] = gout[((size_t)row * C + cb + j) * K + k];
+      for (int e0 = e_beg; e0 < e_end; e0 += 4) round(e0 + kq, e0 + kq < e_end, e_beg, grow);
+    }
+  } else {
+    const int nchunk = (E + kRbChunk - 1) / kRbChunk;
+    float none[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) none[k] = 0.0f;
+    for (int ch = wg * kRbWaves + wv; ch < nchunk; ch += nwg * kRbWaves) {
+      const int e_first = ch * kRbChunk;
+      const int e_last = min(E, e_first + kRbChunk);
+      for (int e0 = e_first; e0 < e_last; e0 += 4) round(e0 + kq, e0 + kq < e_last, e_first, none);
+    }
+  }
+  __syncthreads();
+  if (PASS == 1 && want_w) {
+    for (int i = threadIdx.x; i < GWL; i += kRbWaves * kWave) {
+      const int b = i / (P * 16), p = (i / 16) % P, jj = i % 16;
+      unsafeAtomicAdd(gW + (size_t)b * P * C + (size_t)p * C + cb + jj, gwl[i]);
+    }
+  }
+}
+
+template <int L, int PS>
+static hipError_t launch_bwd_radial_t(const BwdArgs& a) {
+  constexpr int K = num_comp(L);
+  constexpr int P = Tables<L, PS>::P;
+  hipError_t err;
+  if (a.gx && a.N > 0 && (err = launch_fill_zero(a.gx, a.N * a.C * K, a.stream)) != hipSuccess) return err;
+  if (a.gw && (err = launch_fill_zero(a.gw, (int64_t)kRbNB * P * a.C, a.stream)) != hipSuccess) return err;
+  if (a.gvec && a.E > 0 && (err = launch_fill_zero(a.gvec, a.E * 3, a.stream)) != hipSuccess) return err;
+  if (a.N == 0 || a.E == 0) return hipSuccess;
+  const bool sorted = a.row_ptr != nullptr;
+  const int nblk = a.C / 16;
+  // about four resident workgroups per CU over the whole grid; each wave walks rows or runs strided
+  const int64_t units = sorted ? a.N : (a.E + kRbChunk - 1) / kRbChunk;
+  const int64_t want = (4LL * num_cus() + nblk - 1) / nblk;
+  const int64_t cap = (units + kRbWaves - 1) / kRbWaves;
+  const int nwg = (int)(want < cap ? want : cap);
+  const unsigned grid = (unsigned)(nblk * nwg);
+  const float inv_rc = 1.0f / a.r_cut;
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(kRbWaves * kWave), 0, a.stream, (int)a.N, (int)a.E, a.C, nwg,
+                       a.row_ptr, a.vec, a.src, a.dst, a.x, a.w, a.gout, a.gx, a.gw, a.gvec, inv_rc);
+  };
+  if (a.gx || a.gw || a.gvec) {
+    if (sorted) go(conv_bwd_radial_kernel<L, PS, true, 1>);
+    else go(conv_bwd_radial_kernel<L, PS, false, 1>);
+  }
+  if (a.gvec) {
+    if (sorted) go(conv_bwd_radial_kernel<L, PS, true, 2>);
+    else go(conv_bwd_radial_kernel<L, PS, false, 2>);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_conv_backward_radial(const BwdArgs& a) {
+  if (a.C % 16 != 0) return hipErrorInvalidValue;
+  switch (a.lmax * 2 + a.path_set) {
+    case 0: return launch_bwd_radial_t<0, 0>(a);
+    case 1: return launch_bwd_radial_t<0, 1>(a);
+    case 2: return launch_bwd_radial_t<1, 0>(a);
+    case 3: return launch_bwd_radial_t<1, 1>(a);
+    case 4: return launch_bwd_radial_t<2, 0>(a);
+    case 5: return launch_bwd_radial_t<2, 1>(a);
+    case 6: return launch_bwd_radial_t<3, 0>(a);
+    case 7: return launch_bwd_radial_t<3, 1>(a);
     default: return hipErrorInvalidValue;
   }
 }

@@ -48,6 +48,7 @@ struct BwdArgs {
   float* gw;    // or nullptr
   float* gvec;  // or nullptr
   int algo = 0;  // grad_vec of sorted edges: 2 = vector-ALU walk, else matrix cores
+  float r_cut = 0.0f;  // radial weights: w is [8, P*C] and gw [8, P*C]
   hipStream_t stream;
 };
 
@@ -64,6 +65,7 @@ hipError_t launch_linear(int64_t N, int C, int lmax, int mode, const void* h, co
 int num_cus();
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t stream);
 hipError_t launch_conv_backward(const BwdArgs& a);   // fixed weights, vector ALUs
+hipError_t launch_conv_backward_radial(const BwdArgs& a);  // radial weights, lmax <= 3, C a multiple of 16
 // edge-aligned (SO(2)) form, lmax 0..6, fixed fp32 weights; C = 128 only up to kSo2MaxLC128
 constexpr int kSo2MaxL = 6;
 constexpr int kSo2MaxLC128 = 4;

@@ -289,9 +289,12 @@ def eqtp_conv_messages(vec, src, x, weights, lmax: int, path_set: int = EQTP_PAT
 
 def eqtp_conv_backward(vec, src, x, weights, grad_out, lmax: int, row_ptr=None, dst=None,
                        path_set: int = EQTP_PATHS_PARITY, need_x: bool = True, need_w: bool = True,
-                       need_vec: bool = True, algo: int = EQTP_ALGO_AUTO):
-    """(grad_x [N,C,K] | None, grad_w [P,C] | None, grad_vec [E,3] | None) of
-    sum(grad_out * eqtp_conv_fused(...)) for fixed weights [P, C]."""
+                       need_vec: bool = True, algo: int = EQTP_ALGO_AUTO, weight_mode: int = EQTP_W_FIXED,
+                       r_cut: float = 0.0, n_basis: int = 8):
+    """(grad_x [N,C,K] | None, grad_w | None, grad_vec [E,3] | None) of
+    sum(grad_out * eqtp_conv_fused(...)) for fixed weights [P, C] (grad_w
+    [P, C]) or, with weight_mode=EQTP_W_RADIAL, radial weights
+    [n_basis, P*C] (grad_w of the same shape)."""
     import torch
 
     _check(x, "x", torch.float32)
@@ -313,13 +316,14 @@ def eqtp_conv_backward(vec, src, x, weights, grad_out, lmax: int, row_ptr=None, 
         _check(dst, "dst", torch.int32, (E,))
         order = EQTP_EDGES_UNSORTED
     P = eqtp_num_paths(lmax, path_set)
-    _check(weights, "weights", torch.float32, (P, C))
+    _check(weights, "weights", torch.float32, (P, C) if weight_mode == EQTP_W_FIXED else (n_basis, P * C))
     if not (need_x or need_w or need_vec):
         raise ValueError("request at least one gradient")
     gx = torch.empty_like(x) if need_x else None
     gw = torch.empty_like(weights) if need_w else None
     gv = torch.empty((E, 3), dtype=torch.float32, device=x.device) if need_vec else None
-    d = _ConvDesc(ctypes.sizeof(_ConvDesc), lmax, C, path_set, EQTP_W_FIXED, order, algo, 0.0, 8, EQTP_F32)
+    d = _ConvDesc(ctypes.sizeof(_ConvDesc), lmax, C, path_set, weight_mode, order, algo, float(r_cut), n_basis,
+                  EQTP_F32)
     rc = load_library().eqtp_conv_backward(ctypes.byref(d), N, E, _ptr(vec), _ptr(src), _ptr(dst), _ptr(row_ptr),
                                            _ptr(x), _ptr(weights), _ptr(grad_out), _ptr(gx), _ptr(gw), _ptr(gv),
                                            _stream())

@@ -133,7 +133,12 @@ def test_conv_backward_validation():
              gv=FAKE):
         return lib.eqtp_conv_backward(ctypes.byref(d), N, E, vec, src, dst, rp, x, w, g, gx, gw, gv, NULL)
 
-    assert call(_desc(e, weight_mode=1, r_cut=5.0)) == 2                 # radial weights: not implemented
+    assert call(_desc(e, weight_mode=1, r_cut=0.0)) == 1                 # radial weights need r_cut > 0
+    assert call(_desc(e, weight_mode=1, r_cut=5.0, n_basis=6)) == 2      # radial: 8 basis functions only
+    assert call(_desc(e, weight_mode=1, r_cut=5.0, C=8)) == 2            # radial: C a multiple of 16
+    assert call(_desc(e, weight_mode=1, r_cut=5.0), x=NULL) == 1
+    assert call(_desc(e, weight_mode=1, r_cut=5.0, edge_order=1), rp=NULL) == 1
+    assert call(_desc(e, weight_mode=2)) == 1
     assert call(_desc(e, lmax=4)) == 2
     assert call(_desc(e, C=48)) == 2
     assert call(_desc(e, path_set=2)) == 1
