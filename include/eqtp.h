@@ -236,30 +236,39 @@ int eqtp_conv_messages(const eqtp_conv_desc* d, int64_t N, int64_t E, const floa
                        const float* x, const float* weights, float* messages, void* stream);
 
 /*
- * Gradients of the fused convolution with fixed weights: for a scalar loss L
- * with grad_out = dL/dout,
+ * Gradients of the fused convolution: for a scalar loss L with
+ * grad_out = dL/dout, with fixed weights,
  *   grad_x[s, c, l1 m1] = sum_{e: src_e = s} sum_p w[p, c] sum_{m2, m3} C^p[m1, m2, m3] Y_{l2 m2}(vec_e)
  *                         grad_out[dst_e, c, l3 m3]
  *   grad_w[p, c]        = sum_e sum_{m1, m2, m3} C^p x[src_e, c, l1 m1] Y_{l2 m2}(vec_e) grad_out[dst_e, c, l3 m3]
  *   grad_vec[e]         = sum_{l2 m2} dL/dY_{l2 m2}(vec_e) * dY_{l2 m2}/dvec_e
  * (the forces of an interatomic potential are built from grad_vec; the page
  * names a PyTorch autograd function with a backward as the integration path,
- * section "extension possibilities").  A zero-length edge vector has
- * grad_vec = 0.
+ * section "extension possibilities").  With radial weights
+ * (d->weight_mode = EQTP_W_RADIAL, w_e[p,c] = sum_b R_b(|vec_e|) W[b, p*C+c]
+ * as in eqtp_conv_fused) w becomes w_e in grad_x and dL/dY, and
+ *   grad_W[b, p*C + c] = sum_e R_b(r_e) T_e[p, c],
+ *   T_e[p, c] = sum C^p x[src_e, c, l1 m1] Y_{l2 m2}(vec_e) grad_out[dst_e, c, l3 m3],
+ *   grad_vec[e] += (sum_b R_b'(r_e) sum_{p,c} W[b, p*C+c] T_e[p, c]) vec_e / r_e
+ * (the product and chain rule through the radial basis; R_b' = dR_b/dr).
+ * A zero-length edge vector has grad_vec = 0.
  *   d, N, E, vec, src, dst, row_ptr, x, weights: as for eqtp_conv_fused
- *            (x fp32, 16-byte aligned); d->weight_mode must be EQTP_W_FIXED
- *            (radial weights: EQTP_EUNSUPPORTED).
+ *            (x fp32, 16-byte aligned).  Radial weights: lmax 0..3, C a
+ *            multiple of 16, n_basis 8, r_cut > 0 (else EQTP_EUNSUPPORTED /
+ *            EQTP_EINVAL); weights [8, P*C] fp32.
  *   grad_out [N, C, K] fp32, 16-byte aligned.
  *   grad_x   [N, C, K] fp32, 16-byte aligned, or NULL (not computed).
- *   grad_w   [P, C] fp32, or NULL.
+ *   grad_w   [P, C] fp32 (fixed weights) or [8, P*C] (radial), or NULL.
  *   grad_vec [E, 3] fp32, or NULL.
  * Each requested output is fully overwritten; outputs must not alias inputs
  * or each other.  grad_x and grad_w are sums of fp32 atomics (their
- * summation order varies from run to run); grad_vec is written once per
- * edge.  Errors as for eqtp_conv_fused.  d->algo: for dst-sorted edges,
- * grad_vec runs on the matrix cores (dL/dY_e = x[src_e] contracted with a
- * per-node B_d built from grad_out) unless d->algo = EQTP_ALGO_EDGE_VALU,
- * which walks the coupling per edge on the vector ALUs.
+ * summation order varies from run to run); with fixed weights grad_vec is
+ * written once per edge, with radial weights it is a sum of fp32 atomics
+ * (two per 16-channel block).  Errors as for eqtp_conv_fused.  d->algo
+ * (fixed weights): for dst-sorted edges, grad_vec runs on the matrix cores
+ * (dL/dY_e = x[src_e] contracted with a per-node B_d built from grad_out)
+ * unless d->algo = EQTP_ALGO_EDGE_VALU, which walks the coupling per edge on
+ * the vector ALUs.  Radial weights ignore d->algo.
  */
 int eqtp_conv_backward(const eqtp_conv_desc* d, int64_t N, int64_t E, const float* vec, const int32_t* src,
                        const int32_t* dst, const int32_t* row_ptr, const float* x, const float* weights,
