@@ -702,23 +702,25 @@ __global__ __launch_bounds__(kRbWaves * kWave) void conv_bwd_radial_kernel(
   const bool want_x = PASS == 1 && gx != nullptr, want_w = PASS == 1 && gW != nullptr;
   const bool want_v = gvec != nullptr;
   float* const xw = xch[wv];
+  // pass 1: the wave's grad_W sums, D_p[b][j] of path p in lane (j, rows 4 kq .. 4 kq + 3), b < 8 in lanes < 32
+  f4 gacc[PASS == 1 ? P : 1];
+#pragma unroll
+  for (int p = 0; p < (PASS == 1 ? P : 1); ++p) gacc[p] = f4{0.f, 0.f, 0.f, 0.f};
 
   // one round: lane group kq takes edge e (valid) or, if past the end, edge e_alt with no weight
-  auto round = [&](int e, bool valid, int e_alt, const float (&grow)[K]) {
+  auto round = [&](int e, bool valid, int e_alt, int row) {
     const int ec = valid ? e : e_alt;
     const float vx = vec[3 * (size_t)ec], vy = vec[3 * (size_t)ec + 1], vz = vec[3 * (size_t)ec + 2];
     const int s = clamp_index(src[ec], N);
     float xv[K], gv[K];
 #pragma unroll
     for (int k = 0; k < K; ++k) xv[k] = x[((size_t)s * C + cb + j) * K + k];
-    if constexpr (SORTED) {
+    // the destination's grad_out (sorted edges: the row's, read again each round from the cache
+    // rather than held in registers across the row)
+    int d = SORTED ? row : clamp_index(dst[ec], N);
+    if constexpr (SORTED) asm volatile("" : "+v"(d));  // a new value each round: not hoisted out of the row
 #pragma unroll
-      for (int k = 0; k < K; ++k) gv[k] = grow[k];
-    } else {
-      const int d = clamp_index(dst[ec], N);
-#pragma unroll
-      for (int k = 0; k < K; ++k) gv[k] = gout[((size_t)d * C + cb + j) * K + k];
-    }
+    for (int k = 0; k < K; ++k) gv[k] = gout[((size_t)d * C + cb + j) * K + k];
     float Y[16];
     sh_eval<L>(vx, vy, vz, Y);
     const float r = sqrtf(vx * vx + vy * vy + vz * vz);
@@ -793,18 +795,13 @@ __global__ __launch_bounds__(kRbWaves * kWave) void conv_bwd_radial_kernel(
         }
       });
       if (want_w) {
-        // grad_W: per path, D[b][j] = sum_kq R_b(edge kq) T_p(edge kq, j) on the matrix cores
+        // grad_W: per path, D[b][j] += sum_kq R_b(edge kq) T_p(edge kq, j) on the matrix cores, into the
+        // wave's accumulators
         wave_lds_sync();
-        for (int p = 0; p < P; ++p) {
-          const f4 dd = __builtin_amdgcn_mfma_f32_16x16x4f32(aR, xw[p * kWave + lane], f4{0.f, 0.f, 0.f, 0.f}, 0,
-                                                             0, 0);
-          if (lane < 32) {  // rows b = 4 kq + r < 8
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr)
-              __hip_atomic_fetch_add(&gwl[((4 * kq + rr) * P + p) * 16 + j], dd[rr], __ATOMIC_RELAXED,
-                                     __HIP_MEMORY_SCOPE_WORKGROUP);
-          }
-        }
+        static_for<0, P>([&](auto pp) {
+          constexpr int p = decltype(pp)::value;
+          gacc[p] = __builtin_amdgcn_mfma_f32_16x16x4f32(aR, xw[p * kWave + lane], gacc[p], 0, 0, 0);
+        });
         wave_lds_sync();
       }
       if (want_x) {
@@ -882,21 +879,24 @@ __global__ __launch_bounds__(kRbWaves * kWave) void conv_bwd_radial_kernel(
     for (int row = wg * kRbWaves + wv; row < N; row += nwg * kRbWaves) {
       const int e_beg = min(max(row_ptr[row], 0), E);
       const int e_end = min(max(row_ptr[row + 1], e_beg), E);
-      if (e_beg == e_end) continue;
-      float grow[K];
-#pragma unroll
-      for (int k = 0; k < K; ++k) grow[k] = gout[((size_t)row * C + cb + j) * K + k];
-      for (int e0 = e_beg; e0 < e_end; e0 += 4) round(e0 + kq, e0 + kq < e_end, e_beg, grow);
+      for (int e0 = e_beg; e0 < e_end; e0 += 4) round(e0 + kq, e0 + kq < e_end, e_beg, row);
     }
   } else {
     const int nchunk = (E + kRbChunk - 1) / kRbChunk;
-    float none[K];
-#pragma unroll
-    for (int k = 0; k < K; ++k) none[k] = 0.0f;
     for (int ch = wg * kRbWaves + wv; ch < nchunk; ch += nwg * kRbWaves) {
       const int e_first = ch * kRbChunk;
       const int e_last = min(E, e_first + kRbChunk);
-      for (int e0 = e_first; e0 < e_last; e0 += 4) round(e0 + kq, e0 + kq < e_last, e_first, none);
+      for (int e0 = e_first; e0 < e_last; e0 += 4) round(e0 + kq, e0 + kq < e_last, e_first, 0);
+    }
+  }
+  if constexpr (PASS == 1) {
+    if (want_w && lane < 32) {  // the wave's sums into the workgroup's slice (rows b = 4 kq + r < 8)
+#pragma unroll
+      for (int p = 0; p < P; ++p)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr)
+          __hip_atomic_fetch_add(&gwl[((4 * kq + rr) * P + p) * 16 + j], gacc[p][rr], __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_WORKGROUP);
     }
   }
   __syncthreads();
