@@ -86,6 +86,15 @@ def _load():
             lib.oracle_envelope_deriv.restype = f64
             lib.oracle_radial_basis_deriv.argtypes = [f64, f64, i32, vp]
             lib.oracle_radial_basis_deriv.restype = None
+            lib.oracle_silu.argtypes = [f64]
+            lib.oracle_silu.restype = f64
+            lib.oracle_radial_mlp_f64.argtypes = [i64, vp, f64, i32, i32, vp, vp, vp]
+            lib.oracle_radial_mlp_f64.restype = i32
+            lib.oracle_conv_basis_f64.argtypes = [i64, i64, i32, i32, i32, i32] + [vp] * 7
+            lib.oracle_conv_basis_f64.restype = i32
+            for fn in (lib.oracle_interaction_f64, lib.oracle_interaction):
+                fn.argtypes = [i64, i64, i32, i32, i32, f64, i32, i32] + [vp] * 9 + [f64, vp]
+                fn.restype = i32
             lib.oracle_set_threads.argtypes = [i32]
             lib.oracle_set_threads.restype = None
             lib.oracle_num_threads.argtypes = []
@@ -346,4 +355,68 @@ def messages(N, vec, src, x, w, lmax, path_set=PATHS_PARITY, weight_mode=0, r_cu
     rc = fn(N, E, lmax, C, path_set, weight_mode, float(r_cut), n_basis, _p(v), _p(s), _p(xx), _p(ww), _p(out))
     if rc != 0:
         raise ValueError("oracle_messages failed (rc=%d)" % rc)
+    return out
+
+
+def silu(t: float) -> float:
+    return _load().oracle_silu(float(t))
+
+
+def radial_mlp(vec, r_cut: float, W1, W2, n_basis: int = 8) -> np.ndarray:
+    """phi [E, H] fp64: the radial network of every edge (see oracle_radial_mlp_f64)."""
+    v = _f64(vec).reshape(-1, 3)
+    w1, w2 = _f64(W1), _f64(W2)
+    H = w2.shape[0]
+    if w1.shape != (n_basis, H) or w2.shape != (H, H):
+        raise ValueError("shape mismatch")
+    phi = np.empty((v.shape[0], H), dtype=np.float64)
+    if _load().oracle_radial_mlp_f64(v.shape[0], _p(v), float(r_cut), n_basis, H, _p(w1), _p(w2), _p(phi)) != 0:
+        raise ValueError("oracle_radial_mlp_f64: bad arguments")
+    return phi
+
+
+def conv_basis(N, vec, src, dst, x, phi, W3, lmax, path_set=PATHS_PARITY) -> np.ndarray:
+    """fp64 convolution [N, C, K] with per-edge weights w_e = phi_e W3 (see oracle_conv_basis_f64)."""
+    v = _f64(vec).reshape(-1, 3)
+    s, d = _i32(src), _i32(dst)
+    xx, ph, w3 = _f64(x), _f64(phi), _f64(W3)
+    E = v.shape[0]
+    C = xx.shape[1]
+    K = (lmax + 1) ** 2
+    H = ph.shape[1] if ph.ndim == 2 else 0
+    P = paths(lmax, path_set).shape[0]
+    if xx.shape != (N, C, K) or ph.shape != (E, H) or w3.shape != (H, P * C):
+        raise ValueError("shape mismatch")
+    out = np.empty((N, C, K), dtype=np.float64)
+    rc = _load().oracle_conv_basis_f64(N, E, lmax, C, path_set, H, _p(v), _p(s), _p(d), _p(xx), _p(ph), _p(w3),
+                                       _p(out))
+    if rc != 0:
+        raise ValueError("oracle_conv_basis_f64 failed (rc=%d)" % rc)
+    return out
+
+
+def interaction(N, vec, src, dst, h, W_up, W1, W2, W3, W_out, lmax, r_cut, norm=1.0, path_set=PATHS_PARITY,
+                n_basis=8) -> np.ndarray:
+    """fp64 interaction layer output [N, C, K] (see oracle_interaction_f64); float64 ``h`` selects the
+    double entry point (all weights taken as float64)."""
+    lib = _load()
+    is64 = np.asarray(h).dtype == np.float64
+    cast = _f64 if is64 else _f32
+    v = cast(vec).reshape(-1, 3)
+    s, d = _i32(src), _i32(dst)
+    hh, wu, w1, w2, w3, wo = cast(h), cast(W_up), cast(W1), cast(W2), cast(W3), cast(W_out)
+    E = v.shape[0]
+    C = hh.shape[1]
+    K = (lmax + 1) ** 2
+    H = w2.shape[0]
+    P = paths(lmax, path_set).shape[0]
+    if (hh.shape != (N, C, K) or wu.shape != (lmax + 1, C, C) or wo.shape != (lmax + 1, C, C)
+            or w1.shape != (n_basis, H) or w2.shape != (H, H) or w3.shape != (H, P * C)):
+        raise ValueError("shape mismatch")
+    out = np.empty((N, C, K), dtype=np.float64)
+    fn = lib.oracle_interaction_f64 if is64 else lib.oracle_interaction
+    rc = fn(N, E, lmax, C, path_set, float(r_cut), n_basis, H, _p(v), _p(s), _p(d), _p(hh), _p(wu), _p(w1),
+            _p(w2), _p(w3), _p(wo), float(norm), _p(out))
+    if rc != 0:
+        raise ValueError("oracle_interaction failed (rc=%d)" % rc)
     return out

@@ -322,10 +322,12 @@ static void path_blocks_free(path_blocks* pb) {
  * the edge's own message block):
  *   o[c, l3 mu3] += sum_p w_e[p,c] sum_{mu1,mu2} C^p[mu1,mu2,mu3] x[src_e, c, l1 mu1] Y_{l2 mu2}(vec_e)
  * in the order: harmonics, per-edge path weights, then paths, mu1, mu2, mu3,
- * channel.  Y [K] and we [P*C] are the caller's work space. */
+ * channel.  Y [K] and we [P*C] are the caller's work space.  The path
+ * weights: weight_mode 0 w[p*C+c]; 1 sum_n R_n(|vec_e|) w[n*P*C + p*C+c];
+ * 2 sum_n phi[e*n_basis + n] w[n*P*C + p*C+c] (a given per-edge basis). */
 static void edge_message_add(const path_blocks* pb, int lmax, int C, int weight_mode, double r_cut, int n_basis,
                              const double* vec, int64_t e, int64_t s, const double* x, const double* w, double* Y,
-                             double* we, double* o) {
+                             double* we, double* o, const double* phi) {
   int K = (lmax + 1) * (lmax + 1);
   int P = pb->P;
   double R[64];
@@ -335,6 +337,12 @@ static void edge_message_add(const path_blocks* pb, int lmax, int C, int weight_
   /* 2. per-edge path weights */
   if (weight_mode == 0) {
     for (int i = 0; i < P * C; ++i) we[i] = w[i];
+  } else if (weight_mode == 2) {
+    for (int i = 0; i < P * C; ++i) {
+      double acc = 0.0;
+      for (int n = 0; n < n_basis; ++n) acc += phi[e * n_basis + n] * w[(int64_t)n * P * C + i];
+      we[i] = acc;
+    }
   } else {
     double r = sqrt(vx * vx + vy * vy + vz * vz);
     oracle_radial_basis(r, r_cut, n_basis, R);
@@ -371,12 +379,23 @@ static void edge_message_add(const path_blocks* pb, int lmax, int C, int weight_
  * in the order given (the edges are grouped by destination, stably, and the
  * destinations are shared out over the threads).  Returns 0 on success,
  * 1 on bad arguments, 2 if an index is out of range (out is then all zero). */
+static int conv_core(int64_t N, int64_t E, int lmax, int C, int path_set, int weight_mode, double r_cut,
+                     int n_basis, const double* vec, const int32_t* src, const int32_t* dst, const double* x,
+                     const double* w, double* out, const double* phi);
+
 int oracle_conv_f64(int64_t N, int64_t E, int lmax, int C, int path_set, int weight_mode, double r_cut,
                     int n_basis, const double* vec, const int32_t* src, const int32_t* dst, const double* x,
                     const double* w, double* out) {
-  if (lmax < 0 || lmax > OR_MAX_L || C <= 0 || N < 0 || E < 0) return 1;
   if (weight_mode != 0 && weight_mode != 1) return 1;
+  return conv_core(N, E, lmax, C, path_set, weight_mode, r_cut, n_basis, vec, src, dst, x, w, out, NULL);
+}
+
+static int conv_core(int64_t N, int64_t E, int lmax, int C, int path_set, int weight_mode, double r_cut,
+                     int n_basis, const double* vec, const int32_t* src, const int32_t* dst, const double* x,
+                     const double* w, double* out, const double* phi) {
+  if (lmax < 0 || lmax > OR_MAX_L || C <= 0 || N < 0 || E < 0) return 1;
   if (weight_mode == 1 && (n_basis <= 0 || n_basis > 64 || !(r_cut > 0.0))) return 1;
+  if (weight_mode == 2 && (n_basis <= 0 || (E > 0 && !phi))) return 1;
   int K = (lmax + 1) * (lmax + 1);
   for (int64_t i = 0; i < N * C * K; ++i) out[i] = 0.0;
   for (int64_t e = 0; e < E; ++e)
@@ -402,7 +421,7 @@ int oracle_conv_f64(int64_t N, int64_t E, int lmax, int C, int path_set, int wei
       for (int64_t i = start[n]; i < start[n + 1]; ++i) {
         int64_t e = order[i];
         edge_message_add(&pb, lmax, C, weight_mode, r_cut, n_basis, vec, e, src[e], x, w, Y, we,
-                         out + n * C * K);
+                         out + n * C * K, phi);
       }
     free(Y);
     free(we);
@@ -437,7 +456,8 @@ int oracle_messages_f64(int64_t N, int64_t E, int lmax, int C, int path_set, int
     double* we = (double*)malloc(sizeof(double) * P * C);
 #pragma omp for schedule(dynamic, 256)
     for (int64_t e = 0; e < E; ++e)
-      edge_message_add(&pb, lmax, C, weight_mode, r_cut, n_basis, vec, e, src[e], x, w, Y, we, msg + e * C * K);
+      edge_message_add(&pb, lmax, C, weight_mode, r_cut, n_basis, vec, e, src[e], x, w, Y, we, msg + e * C * K,
+                       NULL);
     free(Y);
     free(we);
   }
@@ -947,4 +967,107 @@ int oracle_linear(int64_t N, int C, int lmax, int bf16, const float* h, const fl
           out[(n * C + co) * K + mu] = acc;
         }
   return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Interaction layer: channel linear, radial MLP, convolution, channel linear */
+/* ------------------------------------------------------------------------ */
+
+/* SiLU(t) = t / (1 + exp(-t)). */
+double oracle_silu(double t) { return t / (1.0 + exp(-t)); }
+
+/* The radial network of an edge: R = radial basis of |vec_e| (n_basis
+ * functions, as in the radial weights), then two hidden layers of width H
+ * with SiLU and no bias:
+ *   a[k]      = SiLU(sum_b R_b W1[b*H + k]),
+ *   phi[e, k] = SiLU(sum_j a[j] W2[j*H + k]).
+ * phi is [E, H]. */
+int oracle_radial_mlp_f64(int64_t E, const double* vec, double r_cut, int n_basis, int H, const double* W1,
+                          const double* W2, double* phi) {
+  if (E < 0 || n_basis <= 0 || n_basis > 64 || H <= 0 || !(r_cut > 0.0)) return 1;
+#pragma omp parallel num_threads(oracle_num_threads())
+  {
+    double R[64];
+    double* a = (double*)malloc(sizeof(double) * H);
+#pragma omp for schedule(static)
+    for (int64_t e = 0; e < E; ++e) {
+      double vx = vec[3 * e], vy = vec[3 * e + 1], vz = vec[3 * e + 2];
+      oracle_radial_basis(sqrt(vx * vx + vy * vy + vz * vz), r_cut, n_basis, R);
+      for (int k = 0; k < H; ++k) {
+        double acc = 0.0;
+        for (int b = 0; b < n_basis; ++b) acc += R[b] * W1[(int64_t)b * H + k];
+        a[k] = oracle_silu(acc);
+      }
+      for (int k = 0; k < H; ++k) {
+        double acc = 0.0;
+        for (int j = 0; j < H; ++j) acc += a[j] * W2[(int64_t)j * H + k];
+        phi[e * H + k] = oracle_silu(acc);
+      }
+    }
+    free(a);
+  }
+  return 0;
+}
+
+/* The convolution of oracle_conv_f64 with per-edge path weights from a given
+ * per-edge basis phi [E, H]: w_e[p,c] = sum_k phi[e,k] W3[k, p*C + c]. */
+int oracle_conv_basis_f64(int64_t N, int64_t E, int lmax, int C, int path_set, int H, const double* vec,
+                          const int32_t* src, const int32_t* dst, const double* x, const double* phi,
+                          const double* W3, double* out) {
+  return conv_core(N, E, lmax, C, path_set, 2, 0.0, H, vec, src, dst, x, W3, out, phi);
+}
+
+/* One interaction layer on node features h [N, C, K]:
+ *   h1  = linear(h, W_up)                       (per-l channel linear, W_up [lmax+1, C, C])
+ *   phi = radial MLP of the edge lengths        (oracle_radial_mlp_f64: W1 [n_basis, H], W2 [H, H])
+ *   m   = conv of h1 with w_e = phi_e W3        (oracle_conv_basis_f64: W3 [H, P*C])
+ *   out = linear(m, W_out) / norm               (W_out [lmax+1, C, C]; norm > 0, e.g. the mean degree)
+ * out is [N, C, K]. */
+int oracle_interaction_f64(int64_t N, int64_t E, int lmax, int C, int path_set, double r_cut, int n_basis, int H,
+                           const double* vec, const int32_t* src, const int32_t* dst, const double* h,
+                           const double* W_up, const double* W1, const double* W2, const double* W3,
+                           const double* W_out, double norm, double* out) {
+  if (lmax < 0 || lmax > OR_MAX_L || C <= 0 || N < 0 || E < 0 || !(norm > 0.0)) return 1;
+  int K = (lmax + 1) * (lmax + 1);
+  double* h1 = (double*)malloc(sizeof(double) * (N * C * K > 0 ? N * C * K : 1));
+  double* m = (double*)malloc(sizeof(double) * (N * C * K > 0 ? N * C * K : 1));
+  double* phi = (double*)malloc(sizeof(double) * (E * H > 0 ? E * H : 1));
+  int rc = oracle_linear_f64(N, C, lmax, h, W_up, h1);
+  if (!rc) rc = oracle_radial_mlp_f64(E, vec, r_cut, n_basis, H, W1, W2, phi);
+  if (!rc) rc = oracle_conv_basis_f64(N, E, lmax, C, path_set, H, vec, src, dst, h1, phi, W3, m);
+  if (!rc) rc = oracle_linear_f64(N, C, lmax, m, W_out, out);
+  if (!rc)
+    for (int64_t i = 0; i < N * C * K; ++i) out[i] /= norm;
+  free(h1);
+  free(m);
+  free(phi);
+  return rc;
+}
+
+/* float32 entry point: inputs widened exactly to double. */
+int oracle_interaction(int64_t N, int64_t E, int lmax, int C, int path_set, double r_cut, int n_basis, int H,
+                       const float* vec, const int32_t* src, const int32_t* dst, const float* h, const float* W_up,
+                       const float* W1, const float* W2, const float* W3, const float* W_out, double norm,
+                       double* out) {
+  if (lmax < 0 || lmax > OR_MAX_L || C <= 0 || N < 0 || E < 0 || H <= 0 || n_basis <= 0) return 1;
+  int K = (lmax + 1) * (lmax + 1);
+  int P = oracle_paths(lmax, path_set, NULL);
+  if (P <= 0) return 1;
+  double* v = widen(vec, 3 * E);
+  double* hh = widen(h, N * C * K);
+  double* wu = widen(W_up, (int64_t)(lmax + 1) * C * C);
+  double* w1 = widen(W1, (int64_t)n_basis * H);
+  double* w2 = widen(W2, (int64_t)H * H);
+  double* w3 = widen(W3, (int64_t)H * P * C);
+  double* wo = widen(W_out, (int64_t)(lmax + 1) * C * C);
+  int rc = oracle_interaction_f64(N, E, lmax, C, path_set, r_cut, n_basis, H, v, src, dst, hh, wu, w1, w2, w3, wo,
+                                  norm, out);
+  free(v);
+  free(hh);
+  free(wu);
+  free(w1);
+  free(w2);
+  free(w3);
+  free(wo);
+  return rc;
 }

@@ -24,7 +24,10 @@ bottleneck": 1000 atoms, 32 channels, about 20 neighbours per atom; section
 * features are N(0, 1) float32 with layout [N, C, (L+1)^2];
 * path weights are N(0, 1/P) float32 with layout [P, C];
 * radial weights are N(0, 1/8) float32 with layout [8, P*C];
-* linear weights are N(0, 1/C) float32 with layout [L+1, C_out, C_in].
+* linear weights are N(0, 1/C) float32 with layout [L+1, C_out, C_in];
+* interaction-layer weights (``interaction_weights``): W_up and W_out as the
+  linear weights, radial MLP W1 [8, H] N(0, 1/8), W2 [H, H] N(0, 1/H) and
+  W3 [H, P*C] N(0, 1/H), float32, from their own seed.
 """
 from __future__ import annotations
 
@@ -300,3 +303,22 @@ def small_graph(n: int, e_per_row: int, C: int, lmax: int, seed: int, path_set: 
     return Workload(name="small", N=n, lmax=lmax, C=C, pos=np.zeros((n, 3)), box=None, src=src.astype(np.int32),
                     dst=dst.astype(np.int32), vec=vec, row_ptr=row_ptr.astype(np.int32), x=x, w=w,
                     path_set=path_set, weight_mode=1 if radial else 0, r_cut=r_cut, w_rad=w_rad, w_lin=w_lin)
+
+
+@dataclasses.dataclass
+class InteractionWeights:
+    W_up: np.ndarray    # [L+1, C, C]
+    W1: np.ndarray      # [n_basis, H]
+    W2: np.ndarray      # [H, H]
+    W3: np.ndarray      # [H, P*C]
+    W_out: np.ndarray   # [L+1, C, C]
+
+
+def interaction_weights(lmax: int, C: int, path_set: int = 0, H: int = 64, n_basis: int = 8,
+                        seed: int = 2026) -> InteractionWeights:
+    """Seeded weights of one interaction layer (see the module docstring)."""
+    rng = np.random.default_rng(np.random.SeedSequence([seed, 7000 + lmax, C, H, path_set]))
+    P = num_paths(lmax, path_set)
+    f = lambda shape, var: (rng.standard_normal(shape) * np.sqrt(var)).astype(np.float32)
+    return InteractionWeights(W_up=f((lmax + 1, C, C), 1.0 / C), W1=f((n_basis, H), 1.0 / n_basis),
+                              W2=f((H, H), 1.0 / H), W3=f((H, P * C), 1.0 / H), W_out=f((lmax + 1, C, C), 1.0 / C))
