@@ -217,6 +217,9 @@ def main():
                     help="also time eqtp_conv_backward (all three gradients) on the same inputs (an extra field)")
     ap.add_argument("--messages", action="store_true",
                     help="also time eqtp_conv_messages (per-edge [E,C,K] output, the page's kernel) (an extra field)")
+    ap.add_argument("--interaction", action="store_true",
+                    help="also time eqtp_interaction (channel linear, radial network, convolution with the "
+                         "network's path weights, channel linear) on the same graph and features (an extra field)")
     ap.add_argument("--sh", action="store_true",
                     help="also time eqtp_sh (standalone harmonics [E,K] of the workload's edges) (an extra field)")
     ap.add_argument("--calib-copy", action="store_true",
@@ -473,6 +476,43 @@ def main():
                         "edge_path_what": "all three from eqtp_conv_backward (fp32 atomics for grad_x)"}
             log("backward: by source %.4f ms (%.3e edges/s); edge path %.4f ms" % (sms, wl.E / (sms * 1e-3), bms))
 
+    interaction = None
+    if args.interaction:
+        if args.unsorted or args.x_bf16 or wl.lmax > 3 or wl.C % 16 != 0:
+            log("interaction: dst-sorted fp32 features, lmax <= 3, C a multiple of 16 only; skipped")
+        else:
+            iw = synth.interaction_weights(wl.lmax, wl.C, wl.path_set)
+            it = [T(a) for a in (iw.W_up, iw.W1, iw.W2, iw.W3, iw.W_out)]
+            norm = wl.E / wl.N
+            ix_r_cut = wl.r_cut if wl.r_cut > 0 else 5.0
+            ws = torch.empty(eq.eqtp_interaction_workspace_bytes(wl.N, wl.E, wl.lmax, wl.C, ix_r_cut, norm,
+                                                                 wl.path_set), dtype=torch.uint8, device=dev)
+            ix_out = torch.empty_like(x)
+
+            def ix():
+                eq.eqtp_interaction(vec, src, row_ptr, x, *it, wl.lmax, ix_r_cut, norm=norm, path_set=wl.path_set,
+                                    workspace=ws, out=ix_out)
+
+            for _ in range(3):
+                ix()
+            torch.cuda.synchronize()
+            kb = max(5, K // 4)
+            b0 = torch.cuda.Event(enable_timing=True)
+            b1 = torch.cuda.Event(enable_timing=True)
+            b0.record(stream)
+            for _ in range(kb):
+                ix()
+            b1.record(stream)
+            torch.cuda.synchronize()
+            ims = b0.elapsed_time(b1) / kb
+            P_ = wl.P
+            interaction = {"ms": round(ims, 5), "edges_per_s": round(wl.E / (ims * 1e-3), 1), "launches": kb,
+                           "hidden": 64, "r_cut": ix_r_cut, "norm": round(norm, 4),
+                           "path_weight_tflops": round(2.0 * 64 * P_ * wl.C * wl.E / (ims * 1e-3) / 1e12, 3),
+                           "what": "eqtp_interaction: linear_up, radial network 8->64->64 (SiLU), convolution with "
+                                   "path weights phi_e W3 (last layer on the matrix cores), linear_out / norm"}
+            log("interaction layer: %.4f ms (%.3e edges/s)" % (ims, wl.E / (ims * 1e-3)))
+
     messages = None
     if args.messages and args.x_bf16:
         log("messages: fp32 features only; skipped")
@@ -609,6 +649,8 @@ def main():
         rec["backward"] = backward
     if messages is not None:
         rec["messages"] = messages
+    if interaction is not None:
+        rec["interaction"] = interaction
     if sh is not None:
         rec["sh"] = sh
     print(json.dumps(rec), flush=True)

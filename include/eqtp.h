@@ -358,6 +358,53 @@ int eqtp_sort_edges(int64_t N, int64_t E, const int32_t* dst, const float* vec, 
  */
 int eqtp_linear(int64_t N, int C, int lmax, int dtype, const void* h, const void* W, float* out, void* stream);
 
+/*
+ * One interaction layer of an equivariant interatomic potential on node
+ * features h, around the fused convolution.  The page names an end-to-end
+ * layer benchmark (section "deployment", benchmark of an end-to-end MACE
+ * layer) but not its parts; this is the plainest layer built from what the
+ * page and this library define, in this order:
+ *   h1  = linear(h, W_up)                 per-l channel linear (eqtp_linear), W_up [lmax+1, C, C]
+ *   R_b = radial basis of |vec_e|         the 8 functions of the radial weights (cut-off r_cut)
+ *   a   = SiLU(R W1),  phi_e = SiLU(a W2) radial network, W1 [8, H], W2 [H, H], no bias,
+ *                                         SiLU(t) = t / (1 + exp(-t))
+ *   w_e = phi_e W3                        per-edge path weights, W3 [H, P*C]
+ *   m   = conv(h1; w_e)                   the fused convolution with the per-edge weights w_e
+ *   out = linear(m, W_out) / norm         W_out [lmax+1, C, C]; norm > 0 (e.g. the mean degree)
+ * H = 64.  Edges dst-sorted (row_ptr), lmax 0..3, C 16, 32, 64 or 128,
+ * any path set.  The last network layer (w_e) is applied on the matrix cores
+ * inside the convolution kernel; w_e never reaches memory.
+ *   d          lmax, C, path_set, r_cut (> 0), n_basis (must be 8), hidden
+ *              (must be 64), norm (> 0).
+ *   vec, src, row_ptr  as for eqtp_conv_fused with dst-sorted edges.
+ *   h, out     [N, C, K] fp32, 16-byte aligned; out must not alias an input.
+ *   W_up, W_out [lmax+1, C, C] fp32, 16-byte aligned (output channel major).
+ *   W1 [8, 64], W2 [64, 64], W3 [64, P*C] fp32, 4-byte aligned.
+ *   workspace  device memory of at least eqtp_interaction_workspace_bytes
+ *              bytes, 16-byte aligned, owned by the caller (h1, m and phi).
+ * Errors as for eqtp_conv_fused (EQTP_EINVAL / EQTP_EUNSUPPORTED before any
+ * launch, EQTP_EHIP at launch).  Asynchronous on stream; deterministic.
+ */
+typedef struct eqtp_interaction_desc {
+  int32_t struct_size; /* = sizeof(eqtp_interaction_desc) */
+  int32_t lmax;        /* 0..3 */
+  int32_t C;           /* 16, 32, 64 or 128 */
+  int32_t path_set;    /* EQTP_PATHS_* */
+  float r_cut;         /* cut-off radius of the radial basis (> 0) */
+  int32_t n_basis;     /* must be 8 */
+  int32_t hidden;      /* must be 64 */
+  float norm;          /* the output is divided by it (> 0) */
+} eqtp_interaction_desc;
+
+/* Workspace bytes of eqtp_interaction for N nodes and E edges (a negative
+ * status for invalid arguments). */
+int64_t eqtp_interaction_workspace_bytes(const eqtp_interaction_desc* d, int64_t N, int64_t E);
+
+int eqtp_interaction(const eqtp_interaction_desc* d, int64_t N, int64_t E, const float* vec, const int32_t* src,
+                     const int32_t* row_ptr, const float* h, const float* W_up, const float* W1, const float* W2,
+                     const float* W3, const float* W_out, float* out, void* workspace, int64_t workspace_bytes,
+                     void* stream);
+
 /* Static description of a status code (never NULL). */
 const char* eqtp_status_string(int status);
 

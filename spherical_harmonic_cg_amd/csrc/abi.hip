@@ -70,6 +70,34 @@ int status_of(hipError_t e) { return e == hipSuccess ? EQTP_OK : EQTP_EHIP; }
 
 }  // namespace
 
+namespace {
+struct IxLayout {
+  size_t m, phi, total;
+};
+IxLayout ix_layout(int64_t N, int64_t E, int lmax, int C) {
+  auto al = [](int64_t b) { return (size_t)((b + 255) & ~(int64_t)255); };
+  const int64_t nodes = N * C * (int64_t)(lmax + 1) * (lmax + 1) * 4;
+  IxLayout w;
+  w.m = al(nodes);
+  w.phi = w.m + al(nodes);
+  w.total = w.phi + al(E * 64 * 4);
+  return w;
+}
+bool ix_desc_ok(const eqtp_interaction_desc* d) {
+  return d && d->struct_size >= (int32_t)sizeof(eqtp_interaction_desc);
+}
+// EQTP_OK, or the status of an invalid / unsupported descriptor
+int ix_check(const eqtp_interaction_desc* d, int64_t N, int64_t E) {
+  if (!ix_desc_ok(d)) return EQTP_EINVAL;
+  if (d->lmax < 0 || d->C <= 0 || !(d->r_cut > 0.0f) || !(d->norm > 0.0f)) return EQTP_EINVAL;
+  if (d->path_set != EQTP_PATHS_PARITY && d->path_set != EQTP_PATHS_SO3) return EQTP_EINVAL;
+  if (d->lmax > 3 || d->C % 16 != 0 || !valid_c(d->C) || d->n_basis != 8 || d->hidden != 64)
+    return EQTP_EUNSUPPORTED;
+  if (N < 0 || E < 0 || N > kMaxIndex || E > kMaxIndex || (E > 0 && N == 0)) return EQTP_EINVAL;
+  return EQTP_OK;
+}
+}  // namespace
+
 extern "C" {
 
 int eqtp_num_paths(int lmax, int path_set) { return num_paths_host(lmax, path_set); }
@@ -448,6 +476,59 @@ int eqtp_linear(int64_t N, int C, int lmax, int dtype, const void* h, const void
   if (!h || !W || !out || !aligned16(h) || !aligned16(W) || !aligned16(out)) return EQTP_EINVAL;
   const int mode = dtype == EQTP_F32 ? 0 : (dtype == EQTP_BF16 ? 1 : 2);
   return status_of(eqtp::launch_linear(N, C, lmax, mode, h, W, out, (hipStream_t)stream));
+}
+
+
+int64_t eqtp_interaction_workspace_bytes(const eqtp_interaction_desc* d, int64_t N, int64_t E) {
+  const int rc = ix_check(d, N, E);
+  if (rc != EQTP_OK) return -rc;
+  return (int64_t)ix_layout(N, E, d->lmax, d->C).total;
+}
+
+int eqtp_interaction(const eqtp_interaction_desc* d, int64_t N, int64_t E, const float* vec, const int32_t* src,
+                     const int32_t* row_ptr, const float* h, const float* W_up, const float* W1, const float* W2,
+                     const float* W3, const float* W_out, float* out, void* workspace, int64_t workspace_bytes,
+                     void* stream) {
+  const int rc = ix_check(d, N, E);
+  if (rc != EQTP_OK) return rc;
+  if (N == 0) return EQTP_OK;
+  const IxLayout L = ix_layout(N, E, d->lmax, d->C);
+  if (!workspace || !aligned16(workspace) || workspace_bytes < (int64_t)L.total) return EQTP_EINVAL;
+  if (!h || !out || !W_up || !W_out || !aligned16(h) || !aligned16(out) || !aligned16(W_up) || !aligned16(W_out))
+    return EQTP_EINVAL;
+  if (!W1 || !W2 || !W3 || !aligned4(W1) || !aligned4(W2) || !aligned4(W3)) return EQTP_EINVAL;
+  if (!row_ptr || !aligned4(row_ptr)) return EQTP_EINVAL;
+  if (E > 0 && (!vec || !src || !aligned4(vec) || !aligned4(src))) return EQTP_EINVAL;
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  float* h1 = reinterpret_cast<float*>(ws);
+  float* m = reinterpret_cast<float*>(ws + L.m);
+  float* phi = reinterpret_cast<float*>(ws + L.phi);
+  const hipStream_t st = (hipStream_t)stream;
+  int s = status_of(eqtp::launch_linear(N, d->C, d->lmax, 0, h, W_up, h1, st));
+  if (s != EQTP_OK) return s;
+  s = status_of(eqtp::launch_radial_mlp(E, vec, d->r_cut, W1, W2, phi, 1.0f / d->norm, st));
+  if (s != EQTP_OK) return s;
+  eqtp::ConvArgs a;
+  a.N = N;
+  a.E = E;
+  a.lmax = d->lmax;
+  a.C = d->C;
+  a.path_set = d->path_set;
+  a.weight_mode = EQTP_W_RADIAL;
+  a.edge_order = EQTP_EDGES_DST_SORTED;
+  a.r_cut = d->r_cut;
+  a.vec = vec;
+  a.src = src;
+  a.dst = nullptr;
+  a.row_ptr = row_ptr;
+  a.x = h1;
+  a.w = W3;
+  a.out = m;
+  a.stream = st;
+  a.phi = phi;
+  s = status_of(eqtp::launch_conv_so2_radial(a));
+  if (s != EQTP_OK) return s;
+  return status_of(eqtp::launch_linear(N, d->C, d->lmax, 0, m, W_out, out, st));
 }
 
 const char* eqtp_status_string(int status) {

@@ -490,34 +490,51 @@ __global__ __launch_bounds__(So2Cfg<C>::THREADS) void conv_so2_msg_kernel(int N,
 // parity path set fits 168 VGPRs (3 waves per SIMD); the SO(3) set keeps 2.
 // ---------------------------------------------------------------------------
 constexpr int kSo2RadialBasis = 8;
+// Per-edge basis of width 64 (the hidden layer of a radial network, given by
+// the caller in memory): w_e[p,c] = sum_k phi_e[k] W[k, p*C + c] is the same
+// product with K = 64, 16 MFMAs per path.  phi is stored per edge as [4][16]:
+// hidden unit k = 4 i + q sits at q * 16 + i, so lane group q reads its 16
+// A values of an edge as 4 contiguous 16-byte loads.  The workgroup holds the
+// block's 64 x P x 16 slice of W (94 KB at P = 23) and runs 8 waves, two per
+// SIMD, on it.
+constexpr int kSo2BasisWidth = 64;
 
-template <int L, int PS, int C>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PS == 0 ? 3 : 2))) void conv_so2_radial_kernel(
+template <int NB>
+struct So2RadialCfg {
+  static constexpr int WAVES = NB == kSo2RadialBasis ? 4 : 8;
+};
+
+template <int L, int PS, int C, int NB>
+__global__ __launch_bounds__(So2RadialCfg<NB>::WAVES * 64) __attribute__((amdgpu_waves_per_eu(
+    NB == kSo2RadialBasis ? (PS == 0 ? 3 : 2) : (PS == 0 ? 2 : 1)))) void conv_so2_radial_kernel(
     int N, int E, const int* __restrict__ row_ptr, const float* __restrict__ vec, const int* __restrict__ src,
-    const float* __restrict__ x, const float* __restrict__ w, float* __restrict__ out, float inv_rc) {
+    const float* __restrict__ x, const float* __restrict__ w, float* __restrict__ out, float inv_rc,
+    const float* __restrict__ phi) {
   using T = So2Tables<L, PS>;
   constexpr int K = num_comp(L);
   constexpr int P = T::P;
-  constexpr int NB = kSo2RadialBasis;
   constexpr int NBLK = C / 16;
+  constexpr int WAVES = So2RadialCfg<NB>::WAVES;
+  constexpr bool BASIS = NB != kSo2RadialBasis;
   static_assert(C % 16 == 0 && L <= 3, "radial edge-aligned kernel: C multiple of 16, lmax <= 3");
+  static_assert(NB == kSo2RadialBasis || NB == kSo2BasisWidth, "basis width 8 (radial functions) or 64");
   using Frame = So2Frame<L>;
   __shared__ float wl[NB * P * 16];  // [b][p][channel of the block]
   // the current batch's 16 edge frames and sources, per wave (computed once per batch, read by every
   // channel lane)
-  __shared__ __attribute__((aligned(16))) float frm[4][16 * Frame::FS];
+  __shared__ __attribute__((aligned(16))) float frm[WAVES][16 * Frame::FS];
   // block-major order: the workgroups in flight at any time share one channel
   // block, so the gathered slice of x (N * 16 * K floats) is what the caches
   // must hold, not all of x
-  const int ngrp = (N + 3) / 4;
+  const int ngrp = (N + WAVES - 1) / WAVES;
   const int cb = (int)(blockIdx.x / ngrp) * 16;
-  for (int i = threadIdx.x; i < NB * P * 16; i += 256) {
+  for (int i = threadIdx.x; i < NB * P * 16; i += WAVES * 64) {
     const int bp = i >> 4;  // b * P + p
     wl[i] = w[(size_t)bp * C + cb + (i & 15)];
   }
   __syncthreads();
   const int lane = threadIdx.x & 63;
-  const int row = (int)(blockIdx.x % ngrp) * 4 + (threadIdx.x >> 6);
+  const int row = (int)(blockIdx.x % ngrp) * WAVES + (threadIdx.x >> 6);
   if (row >= N) return;
   const int j = lane & 15;   // channel cb + j; A row (edge e0 + j) for the radial product
   const int kq = lane >> 4;  // edge group: edges kq + 4 i of each batch; A/B k index
@@ -530,10 +547,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PS == 0 ? 3
 #pragma unroll
   for (int k = 0; k < K; ++k) acc[k] = 0.0f;
   for (int e0 = e_beg; e0 < e_end; e0 += 16) {
-    // A operand of lane (j, kq): R_{kq}, R_{4+kq} of the edge of A row j, e0 + (j >> 2) + 4 (j & 3)
-    // (zeros past the row)
-    // and the frame and source of that edge, written by the lanes of group 0 to the wave's LDS
-    float a0 = 0.0f, a1 = 0.0f;
+    // A operand of lane (j, kq): basis functions kq, 4 + kq, ... of the edge of A row j,
+    // e0 + (j >> 2) + 4 (j & 3) (zeros past the row), and the frame and source of that edge, written by
+    // the lanes of group 0 to the wave's LDS
+    float av[NB / 4];
+#pragma unroll
+    for (int i = 0; i < NB / 4; ++i) av[i] = 0.0f;
     const int ar = (j >> 2) | ((j & 3) << 2);
     const int ea = e0 + ar;
     float ax = 0.0f, ay = 0.0f, az = 0.0f;
@@ -543,10 +562,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PS == 0 ? 3
       ay = vec[3 * (size_t)ea + 1];
       az = vec[3 * (size_t)ea + 2];
       sa = clamp_index(src[ea], N);
-      float R[NB];
-      radial_basis<NB>(sqrtf(ax * ax + ay * ay + az * az), inv_rc, R);
-      a0 = kq == 0 ? R[0] : (kq == 1 ? R[1] : (kq == 2 ? R[2] : R[3]));
-      a1 = kq == 0 ? R[4] : (kq == 1 ? R[5] : (kq == 2 ? R[6] : R[7]));
+      if constexpr (BASIS) {
+        const f4* pr = reinterpret_cast<const f4*>(phi + (size_t)ea * NB + kq * (NB / 4));
+#pragma unroll
+        for (int q = 0; q < NB / 16; ++q) {
+          const f4 v4 = pr[q];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) av[4 * q + r] = v4[r];
+        }
+      } else {
+        float R[NB];
+        radial_basis<NB>(sqrtf(ax * ax + ay * ay + az * az), inv_rc, R);
+        av[0] = kq == 0 ? R[0] : (kq == 1 ? R[1] : (kq == 2 ? R[2] : R[3]));
+        av[1] = kq == 0 ? R[4] : (kq == 1 ? R[5] : (kq == 2 ? R[6] : R[7]));
+      }
     }
     float* const wf = frm[threadIdx.x >> 6];
     wave_lds_sync();  // the previous batch's frames have been read
@@ -557,13 +586,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PS == 0 ? 3
     wave_lds_sync();
     // w of edges e0 + kq + 4 i, channel cb + j: wp[p][i]
     f4 wp[P];
-    // basis functions 0..3 for every path, then 4..7 accumulated (no back-to-back dependent products)
+    // basis functions 0..3 for every path first, then the next four accumulated (no back-to-back dependent
+    // products)
 #pragma unroll
     for (int p = 0; p < P; ++p)
-      wp[p] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, wl[(kq * P + p) * 16 + j], f4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+      wp[p] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[0], wl[(kq * P + p) * 16 + j], f4{0.f, 0.f, 0.f, 0.f}, 0, 0,
+                                                   0);
 #pragma unroll
-    for (int p = 0; p < P; ++p)
-      wp[p] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, wl[((4 + kq) * P + p) * 16 + j], wp[p], 0, 0, 0);
+    for (int i = 1; i < NB / 4; ++i)
+#pragma unroll
+      for (int p = 0; p < P; ++p)
+        wp[p] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[i], wl[((4 * i + kq) * P + p) * 16 + j], wp[p], 0, 0, 0);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if (e0 + 4 * i >= e_end) break;  // no edge left for any lane (wave-uniform)
@@ -599,9 +632,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PS == 0 ? 3
 template <int L, int PS, int C>
 static hipError_t launch_so2_radial_t(const ConvArgs& a) {
   if (a.N == 0) return hipSuccess;
-  const long long blocks = (a.N + 3) / 4 * (C / 16);
-  hipLaunchKernelGGL((conv_so2_radial_kernel<L, PS, C>), dim3((unsigned)blocks), dim3(256), 0, a.stream, (int)a.N,
-                     (int)a.E, a.row_ptr, a.vec, a.src, (const float*)a.x, a.w, a.out, 1.0f / a.r_cut);
+  if (a.phi != nullptr) {  // per-edge basis of width 64
+    constexpr int WV = So2RadialCfg<kSo2BasisWidth>::WAVES;
+    const long long blocks = (a.N + WV - 1) / WV * (C / 16);
+    hipLaunchKernelGGL((conv_so2_radial_kernel<L, PS, C, kSo2BasisWidth>), dim3((unsigned)blocks), dim3(WV * 64), 0,
+                       a.stream, (int)a.N, (int)a.E, a.row_ptr, a.vec, a.src, (const float*)a.x, a.w, a.out, 0.0f,
+                       a.phi);
+    return hipGetLastError();
+  }
+  constexpr int WV = So2RadialCfg<kSo2RadialBasis>::WAVES;
+  const long long blocks = (a.N + WV - 1) / WV * (C / 16);
+  hipLaunchKernelGGL((conv_so2_radial_kernel<L, PS, C, kSo2RadialBasis>), dim3((unsigned)blocks), dim3(WV * 64), 0,
+                     a.stream, (int)a.N, (int)a.E, a.row_ptr, a.vec, a.src, (const float*)a.x, a.w, a.out,
+                     1.0f / a.r_cut, nullptr);
   return hipGetLastError();
 }
 

@@ -11,8 +11,8 @@ namespace eqtp {
 struct ConvArgs {
   int64_t N, E;
   int lmax, C, path_set, weight_mode, edge_order;
-  int x_bf16 = 0;
-  int messages = 0;  // edge-aligned kernel: per-edge messages [E, C, K] into out instead of the sum  // x holds bfloat16 features (node algorithm only)
+  int x_bf16 = 0;     // x holds bfloat16 features
+  int messages = 0;   // edge-aligned kernel: per-edge messages [E, C, K] into out instead of the sum
   float r_cut;
   const float* vec;
   const int32_t* src;
@@ -22,6 +22,9 @@ struct ConvArgs {
   const float* w;
   float* out;
   hipStream_t stream;
+  // radial edge-aligned kernel: a per-edge basis [E, 64] (stored [E][4][16], hidden unit 4 i + q at
+  // q * 16 + i) in place of the radial functions, with w [64, P*C]; else nullptr
+  const float* phi = nullptr;
 };
 
 struct ProbeArgs {
@@ -66,6 +69,9 @@ int num_cus();
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t stream);
 hipError_t launch_conv_backward(const BwdArgs& a);   // fixed weights, vector ALUs
 hipError_t launch_conv_backward_radial(const BwdArgs& a);  // radial weights, lmax <= 3, C a multiple of 16
+// the interaction layer's radial network: phi [E][4][16] (scaled by scale) from the edge lengths
+hipError_t launch_radial_mlp(int64_t E, const float* vec, float r_cut, const float* W1, const float* W2, float* phi,
+                             float scale, hipStream_t stream);
 // edge-aligned (SO(2)) form, lmax 0..6, fixed fp32 weights; C = 128 only up to kSo2MaxLC128
 constexpr int kSo2MaxL = 6;
 constexpr int kSo2MaxLC128 = 4;

@@ -27,7 +27,7 @@ EQTP_F32, EQTP_BF16, EQTP_F32_BF16 = 0, 1, 2
 EXPORTED = ("eqtp_num_paths", "eqtp_path_table", "eqtp_sh", "eqtp_conv_fused", "eqtp_conv_workspace_bytes",
             "eqtp_conv_fused_ws", "eqtp_conv_fused_noalloc", "eqtp_conv_messages",
             "eqtp_conv_backward", "eqtp_conv_backward_by_source", "eqtp_edge_rows", "eqtp_sort_edges",
-            "eqtp_linear",
+            "eqtp_linear", "eqtp_interaction_workspace_bytes", "eqtp_interaction",
             "eqtp_status_string", "eqtp_test_segment_probe")
 
 
@@ -42,6 +42,12 @@ class _ConvDesc(ctypes.Structure):
                 ("path_set", ctypes.c_int32), ("weight_mode", ctypes.c_int32), ("edge_order", ctypes.c_int32),
                 ("algo", ctypes.c_int32), ("r_cut", ctypes.c_float), ("n_basis", ctypes.c_int32),
                 ("x_dtype", ctypes.c_int32)]
+
+
+class _InteractionDesc(ctypes.Structure):
+    _fields_ = [("struct_size", ctypes.c_int32), ("lmax", ctypes.c_int32), ("C", ctypes.c_int32),
+                ("path_set", ctypes.c_int32), ("r_cut", ctypes.c_float), ("n_basis", ctypes.c_int32),
+                ("hidden", ctypes.c_int32), ("norm", ctypes.c_float)]
 
 
 _lib = None
@@ -83,6 +89,10 @@ def load_library(path: str = LIB_PATH):
             lib.eqtp_sort_edges.restype = i32
             lib.eqtp_linear.argtypes = [i64, i32, i32, i32, vp, vp, vp, vp]
             lib.eqtp_linear.restype = i32
+            lib.eqtp_interaction_workspace_bytes.argtypes = [ctypes.POINTER(_InteractionDesc), i64, i64]
+            lib.eqtp_interaction_workspace_bytes.restype = i64
+            lib.eqtp_interaction.argtypes = [ctypes.POINTER(_InteractionDesc), i64, i64] + [vp] * 11 + [i64, vp]
+            lib.eqtp_interaction.restype = i32
             lib.eqtp_status_string.argtypes = [i32]
             lib.eqtp_status_string.restype = ctypes.c_char_p
             lib.eqtp_test_segment_probe.argtypes = [vp, vp, i64, i64, i32, i32, i32, vp, vp, vp]
@@ -428,6 +438,58 @@ def eqtp_linear(h, W, lmax: int, dtype: int = EQTP_F32, out=None):
         out = torch.empty((N, C, K), dtype=torch.float32, device=h.device)
     _check(out, "out", torch.float32, (N, C, K))
     _raise(load_library().eqtp_linear(N, C, lmax, cdt, _ptr(h), _ptr(W), _ptr(out), _stream()), "eqtp_linear")
+    return out
+
+
+def _ix_desc(lmax, C, path_set, r_cut, norm):
+    return _InteractionDesc(ctypes.sizeof(_InteractionDesc), lmax, C, path_set, float(r_cut), 8, 64, float(norm))
+
+
+def eqtp_interaction_workspace_bytes(N: int, E: int, lmax: int, C: int, r_cut: float = 1.0, norm: float = 1.0,
+                                     path_set: int = EQTP_PATHS_PARITY) -> int:
+    d = _ix_desc(lmax, C, path_set, r_cut, norm)
+    n = load_library().eqtp_interaction_workspace_bytes(ctypes.byref(d), N, E)
+    if n < 0:
+        _raise(int(-n), "eqtp_interaction_workspace_bytes")
+    return int(n)
+
+
+def eqtp_interaction(vec, src, row_ptr, h, W_up, W1, W2, W3, W_out, lmax: int, r_cut: float, norm: float = 1.0,
+                     path_set: int = EQTP_PATHS_PARITY, workspace=None, out=None):
+    """One interaction layer (see include/eqtp.h): out [N, C, K] fp32 from node features h [N, C, K],
+    dst-sorted edges (vec, src, row_ptr) and the weights W_up, W_out [lmax+1, C, C], W1 [8, 64],
+    W2 [64, 64], W3 [64, P*C].  ``workspace``: a uint8 tensor of at least
+    eqtp_interaction_workspace_bytes bytes, or None to allocate one here."""
+    import torch
+
+    _check(h, "h", torch.float32)
+    if h.dim() != 3:
+        raise ValueError("h must be [N, C, K]")
+    N, C, K = h.shape
+    if K != (lmax + 1) ** 2:
+        raise ValueError("h has %d components, lmax %d needs %d" % (K, lmax, (lmax + 1) ** 2))
+    _check(vec, "vec", torch.float32)
+    E = vec.shape[0]
+    _check(src, "src", torch.int32, (E,))
+    _check(row_ptr, "row_ptr", torch.int32, (N + 1,))
+    P = eqtp_num_paths(lmax, path_set)
+    _check(W_up, "W_up", torch.float32, (lmax + 1, C, C))
+    _check(W_out, "W_out", torch.float32, (lmax + 1, C, C))
+    _check(W1, "W1", torch.float32, (8, 64))
+    _check(W2, "W2", torch.float32, (64, 64))
+    _check(W3, "W3", torch.float32, (64, P * C))
+    d = _ix_desc(lmax, C, path_set, r_cut, norm)
+    need = eqtp_interaction_workspace_bytes(N, E, lmax, C, r_cut, norm, path_set)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=h.device)
+    _check(workspace, "workspace", torch.uint8)
+    if out is None:
+        out = torch.empty((N, C, K), dtype=torch.float32, device=h.device)
+    _check(out, "out", torch.float32, (N, C, K))
+    rc = load_library().eqtp_interaction(ctypes.byref(d), N, E, _ptr(vec), _ptr(src), _ptr(row_ptr), _ptr(h),
+                                         _ptr(W_up), _ptr(W1), _ptr(W2), _ptr(W3), _ptr(W_out), _ptr(out),
+                                         _ptr(workspace), workspace.numel(), _stream())
+    _raise(rc, "eqtp_interaction")
     return out
 
 

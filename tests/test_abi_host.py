@@ -280,3 +280,41 @@ def test_noalloc_refuses_beyond_its_scratch():
     assert lib.eqtp_conv_fused_noalloc(ctypes.byref(d), -1, 10, FAKE, FAKE, FAKE, NULL, FAKE, FAKE, FAKE,
                                        NULL) == 1
     assert b"scratch" in lib.eqtp_status_string(e.EQTP_ETOOLARGE)
+
+
+def test_interaction_validation():
+    e = _lib()
+    lib = e.load_library()
+
+    def desc(**kw):
+        d = dict(lmax=3, C=64, path_set=0, r_cut=5.0, n_basis=8, hidden=64, norm=1.0)
+        d.update(kw)
+        return e._InteractionDesc(ctypes.sizeof(e._InteractionDesc), d["lmax"], d["C"], d["path_set"], d["r_cut"],
+                                  d["n_basis"], d["hidden"], d["norm"])
+
+    def call(d, N=10, E=20, vec=FAKE, src=FAKE, rp=FAKE, h=FAKE, ws=FAKE, wsb=1 << 40, out=FAKE):
+        return lib.eqtp_interaction(ctypes.byref(d), N, E, vec, src, rp, h, FAKE, FAKE, FAKE, FAKE, FAKE, out, ws,
+                                    wsb, NULL)
+
+    assert call(desc(lmax=4)) == 2
+    assert call(desc(C=48)) == 2
+    assert call(desc(C=8)) == 2               # C a multiple of 16
+    assert call(desc(hidden=32)) == 2
+    assert call(desc(n_basis=6)) == 2
+    assert call(desc(norm=0.0)) == 1
+    assert call(desc(r_cut=0.0)) == 1
+    assert call(desc(path_set=2)) == 1
+    assert call(desc(), ws=NULL) == 1
+    assert call(desc(), wsb=100) == 1         # workspace too small
+    assert call(desc(), h=NULL) == 1
+    assert call(desc(), rp=NULL) == 1
+    assert call(desc(), vec=NULL) == 1
+    assert call(desc(), out=ctypes.c_void_p(0x10004)) == 1
+    assert call(desc(), N=0) == 1             # edges without nodes
+    assert call(desc(), N=0, E=0) == 0        # nothing to do
+    bad = desc()
+    bad.struct_size = 8
+    assert call(bad) == 1
+    assert lib.eqtp_interaction_workspace_bytes(ctypes.byref(desc(lmax=4)), 10, 20) == -2
+    n = lib.eqtp_interaction_workspace_bytes(ctypes.byref(desc()), 10, 20)
+    assert n >= 2 * 10 * 64 * 16 * 4 + 20 * 64 * 4 and n % 256 == 0
