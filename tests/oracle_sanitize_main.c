@@ -52,6 +52,16 @@ int oracle_conv_backward_radial(int64_t N, int64_t E, int lmax, int C, int path_
                                 const float* vec, const int32_t* src, const int32_t* dst, const float* x,
                                 const float* W, const float* gout, double* gx, double* gW, double* gvec);
 float oracle_round_bf16(float f);
+double oracle_silu(double t);
+int oracle_radial_mlp_f64(int64_t E, const double* vec, double r_cut, int n_basis, int H, const double* W1,
+                          const double* W2, double* phi);
+int oracle_conv_basis_f64(int64_t N, int64_t E, int lmax, int C, int path_set, int H, const double* vec,
+                          const int32_t* src, const int32_t* dst, const double* x, const double* phi,
+                          const double* W3, double* out);
+int oracle_interaction(int64_t N, int64_t E, int lmax, int C, int path_set, double r_cut, int n_basis, int H,
+                       const float* vec, const int32_t* src, const int32_t* dst, const float* h, const float* W_up,
+                       const float* W1, const float* W2, const float* W3, const float* W_out, double norm,
+                       double* out);
 int oracle_linear_f64(int64_t N, int C, int lmax, const double* h, const double* W, double* out);
 int oracle_linear(int64_t N, int C, int lmax, int bf16, const float* h, const float* W, double* out);
 
@@ -285,6 +295,62 @@ static void test_conv(void) {
          1);
 }
 
+static void test_interaction(void) {
+  const int H = 5, NB = 8;
+  for (int lmax = 0; lmax <= 3; ++lmax) {
+    const int64_t N = 6, E = 14;
+    const int C = 2, K = (lmax + 1) * (lmax + 1), P = oracle_paths(lmax, 0, NULL);
+    float* vec = (float*)xmalloc(sizeof(float) * 3 * E);
+    double* vd = (double*)xmalloc(sizeof(double) * 3 * E);
+    int32_t* src = (int32_t*)xmalloc(sizeof(int32_t) * E);
+    int32_t* dst = (int32_t*)xmalloc(sizeof(int32_t) * E);
+    float* h = (float*)xmalloc(sizeof(float) * N * C * K);
+    float* wu = (float*)xmalloc(sizeof(float) * (lmax + 1) * C * C);
+    float* wo = (float*)xmalloc(sizeof(float) * (lmax + 1) * C * C);
+    float* w1 = (float*)xmalloc(sizeof(float) * NB * H);
+    float* w2 = (float*)xmalloc(sizeof(float) * H * H);
+    float* w3 = (float*)xmalloc(sizeof(float) * H * P * C);
+    double* out = (double*)xmalloc(sizeof(double) * N * C * K);
+    double* phi = (double*)xmalloc(sizeof(double) * E * H);
+    double* w1d = (double*)xmalloc(sizeof(double) * NB * H);
+    double* w2d = (double*)xmalloc(sizeof(double) * H * H);
+    fill_vectors(E, vd);
+    for (int64_t i = 0; i < 3 * E; ++i) vec[i] = (float)vd[i];
+    for (int64_t e = 0; e < E; ++e) {
+      src[e] = index_below(N);
+      dst[e] = index_below(N);
+    }
+    for (int64_t i = 0; i < N * C * K; ++i) h[i] = (float)uniform(-1, 1);
+    for (int64_t i = 0; i < (lmax + 1) * C * C; ++i) {
+      wu[i] = (float)uniform(-1, 1);
+      wo[i] = (float)uniform(-1, 1);
+    }
+    for (int64_t i = 0; i < NB * H; ++i) w1d[i] = w1[i] = (float)uniform(-1, 1);
+    for (int64_t i = 0; i < H * H; ++i) w2d[i] = w2[i] = (float)uniform(-1, 1);
+    for (int64_t i = 0; i < H * P * C; ++i) w3[i] = (float)uniform(-1, 1);
+    EXPECT(oracle_interaction(N, E, lmax, C, 0, 5.0, NB, H, vec, src, dst, h, wu, w1, w2, w3, wo, 2.0, out) == 0);
+    EXPECT(oracle_interaction(N, 0, lmax, C, 0, 5.0, NB, H, vec, src, dst, h, wu, w1, w2, w3, wo, 2.0, out) == 0);
+    EXPECT(oracle_radial_mlp_f64(E, vd, 5.0, NB, H, w1d, w2d, phi) == 0);
+    EXPECT(oracle_interaction(N, E, lmax, C, 0, 5.0, NB, H, vec, src, dst, h, wu, w1, w2, w3, wo, 0.0, out) == 1);
+    free(vec);
+    free(vd);
+    free(src);
+    free(dst);
+    free(h);
+    free(wu);
+    free(wo);
+    free(w1);
+    free(w2);
+    free(w3);
+    free(out);
+    free(phi);
+    free(w1d);
+    free(w2d);
+  }
+  EXPECT(oracle_silu(0.0) == 0.0);
+  EXPECT(oracle_conv_basis_f64(1, 1, 2, 1, 0, 4, NULL, NULL, NULL, NULL, NULL, NULL, NULL) == 1);
+}
+
 static void test_linear(void) {
   for (int lmax = 0; lmax <= 6; ++lmax) {
     const int C = 5;
@@ -324,10 +390,12 @@ int main(void) {
   test_radial();
   test_conv();
   test_linear();
+  test_interaction();
   /* the row-, edge- and node-parallel loops with several threads */
   oracle_set_threads(3);
   test_conv();
   test_linear();
+  test_interaction();
   if (failures) {
     fprintf(stderr, "%d checks failed\n", failures);
     return 1;
