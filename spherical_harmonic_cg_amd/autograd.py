@@ -1,6 +1,9 @@
-"""PyTorch autograd wrapper of the fused convolution (fixed path weights).
+"""PyTorch autograd wrapper of the fused convolution.
 
-The forward calls eqtp_conv_fused.  The backward computes
+The forward calls eqtp_conv_fused.  With radial weights (weight_mode =
+EQTP_W_RADIAL) the backward is eqtp_conv_backward with radial weights (all
+three gradients; grad_x_mode does not apply).  With fixed weights the
+backward computes
   * grad_x and grad_w with eqtp_conv_backward_by_source, on a copy of the edges
     grouped by source node that eqtp_sort_edges builds on the GPU (the adjoint
     of the node-factored forward, on the matrix cores), and
@@ -30,12 +33,16 @@ class EquivariantConvFunction(torch.autograd.Function):
     """out = conv(vec, x, weights) over dst-sorted (row_ptr) or unsorted (dst) edges."""
 
     @staticmethod
-    def forward(ctx, vec, x, weights, src, row_ptr, dst, lmax, path_set, grad_x_mode):
-        out = _eq.eqtp_conv_fused(vec, src, x, weights, lmax, row_ptr=row_ptr, dst=dst, path_set=path_set)
+    def forward(ctx, vec, x, weights, src, row_ptr, dst, lmax, path_set, grad_x_mode, weight_mode=_eq.EQTP_W_FIXED,
+                r_cut=0.0):
+        out = _eq.eqtp_conv_fused(vec, src, x, weights, lmax, row_ptr=row_ptr, dst=dst, path_set=path_set,
+                                  weight_mode=weight_mode, r_cut=r_cut)
         ctx.save_for_backward(vec, x, weights, src, row_ptr, dst)
         ctx.lmax = lmax
         ctx.path_set = path_set
         ctx.grad_x_mode = grad_x_mode
+        ctx.weight_mode = weight_mode
+        ctx.r_cut = r_cut
         return out
 
     @staticmethod
@@ -44,7 +51,13 @@ class EquivariantConvFunction(torch.autograd.Function):
         need_vec, need_x, need_w = ctx.needs_input_grad[0], ctx.needs_input_grad[1], ctx.needs_input_grad[2]
         g = grad_out.contiguous()
         gx = gw = gv = None
-        if ctx.grad_x_mode == "edge":
+        if ctx.weight_mode == _eq.EQTP_W_RADIAL:
+            if need_vec or need_x or need_w:
+                gx, gw, gv = _eq.eqtp_conv_backward(vec, src, x, weights, g, ctx.lmax, row_ptr=row_ptr, dst=dst,
+                                                    path_set=ctx.path_set, need_x=need_x, need_w=need_w,
+                                                    need_vec=need_vec, weight_mode=ctx.weight_mode,
+                                                    r_cut=ctx.r_cut)
+        elif ctx.grad_x_mode == "edge":
             if need_vec or need_x or need_w:
                 gx, gw, gv = _eq.eqtp_conv_backward(vec, src, x, weights, g, ctx.lmax, row_ptr=row_ptr, dst=dst,
                                                     path_set=ctx.path_set, need_x=need_x, need_w=need_w,
@@ -57,13 +70,15 @@ class EquivariantConvFunction(torch.autograd.Function):
             if need_vec:
                 _, _, gv = _eq.eqtp_conv_backward(vec, src, x, weights, g, ctx.lmax, row_ptr=row_ptr, dst=dst,
                                                   path_set=ctx.path_set, need_x=False, need_w=False, need_vec=True)
-        return gv, gx, gw, None, None, None, None, None, None
+        return gv, gx, gw, None, None, None, None, None, None, None, None
 
 
 def equivariant_conv(vec, x, weights, src, lmax: int, row_ptr=None, dst=None, path_set: int = _eq.EQTP_PATHS_PARITY,
-                     grad_x_mode: str = "by_source"):
+                     grad_x_mode: str = "by_source", weight_mode: int = _eq.EQTP_W_FIXED, r_cut: float = 0.0):
     """Differentiable fused convolution (see eqtp_conv_fused for the layouts).
-    grad_x_mode: "by_source" (default) or "edge" (see the module docstring)."""
+    grad_x_mode: "by_source" (default) or "edge" (see the module docstring; fixed weights).
+    weight_mode=EQTP_W_RADIAL: weights [8, P*C] applied through the radial basis of cut-off r_cut."""
     if grad_x_mode not in ("by_source", "edge"):
         raise ValueError("grad_x_mode must be 'by_source' or 'edge'")
-    return EquivariantConvFunction.apply(vec, x, weights, src, row_ptr, dst, lmax, path_set, grad_x_mode)
+    return EquivariantConvFunction.apply(vec, x, weights, src, row_ptr, dst, lmax, path_set, grad_x_mode,
+                                         weight_mode, r_cut)

@@ -27,6 +27,8 @@ constexpr int kMlpRun = 32;  // edges per wave and run
 
 __device__ __forceinline__ float silu(float t) { return t / (1.0f + __expf(-t)); }
 
+constexpr int kMlpIlp = 4;  // edges in flight per lane (independent FMA chains)
+
 __global__ __launch_bounds__(kMlpWaves * kWave) void radial_mlp_kernel(int E, const float* __restrict__ vec,
                                                                        const float* __restrict__ W1,
                                                                        const float* __restrict__ W2,
@@ -44,19 +46,30 @@ __global__ __launch_bounds__(kMlpWaves * kWave) void radial_mlp_kernel(int E, co
   const int nwaves = gridDim.x * kMlpWaves;
   for (int run = wave; run < nruns; run += nwaves) {
     const int e_end = min(E, (run + 1) * kMlpRun);
-    for (int e = run * kMlpRun; e < e_end; ++e) {
-      const float vx = vec[3 * (size_t)e], vy = vec[3 * (size_t)e + 1], vz = vec[3 * (size_t)e + 2];
-      float R[kMlpBasis];
-      radial_basis<kMlpBasis>(sqrtf(vx * vx + vy * vy + vz * vz), inv_rc, R);
-      float a = 0.0f;
+    // kMlpIlp edges at a time; slots past the run's end repeat its last edge and are not stored
+    for (int e0 = run * kMlpRun; e0 < e_end; e0 += kMlpIlp) {
+      float a[kMlpIlp], t[kMlpIlp];
 #pragma unroll
-      for (int b = 0; b < kMlpBasis; ++b) a = fmaf(R[b], w1[b], a);
-      a = silu(a);
-      float t = 0.0f;
+      for (int u = 0; u < kMlpIlp; ++u) {
+        const int e = min(e0 + u, e_end - 1);
+        const float vx = vec[3 * (size_t)e], vy = vec[3 * (size_t)e + 1], vz = vec[3 * (size_t)e + 2];
+        float R[kMlpBasis];
+        radial_basis<kMlpBasis>(sqrtf(vx * vx + vy * vy + vz * vz), inv_rc, R);
+        float acc = 0.0f;
+#pragma unroll
+        for (int b = 0; b < kMlpBasis; ++b) acc = fmaf(R[b], w1[b], acc);
+        a[u] = silu(acc);
+        t[u] = 0.0f;
+      }
 #pragma unroll
       for (int jj = 0; jj < kMlpHidden; ++jj)
-        t = fmaf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, a), jj)), w2[jj], t);
-      phi[(size_t)e * kMlpHidden + slot] = silu(t) * scale;
+#pragma unroll
+        for (int u = 0; u < kMlpIlp; ++u)
+          t[u] = fmaf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, a[u]), jj)), w2[jj],
+                      t[u]);
+#pragma unroll
+      for (int u = 0; u < kMlpIlp; ++u)
+        if (e0 + u < e_end) phi[(size_t)(e0 + u) * kMlpHidden + slot] = silu(t[u]) * scale;
     }
   }
 }

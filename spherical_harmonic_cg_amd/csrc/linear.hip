@@ -18,6 +18,8 @@
 // is reused as the fp32 output tile in the global layout and the tile leaves
 // with coalesced 16-byte stores.  Bytes per node: C K (h once, 4 or 2 bytes
 // each) + 4 C K (out once); flops 2 C^2 K: bound by HBM bandwidth.
+#include <type_traits>
+
 #include "eqtp_device.hpp"
 #include "eqtp_kernels.hpp"
 
@@ -109,10 +111,16 @@ __global__ __launch_bounds__(256) void linear_kernel(int N, const S* __restrict_
   //    issued before the first LDS store so their latencies overlap.
   constexpr int WF4 = Cfg::W_LDS ? (L + 1) * C * C / 4 : 0;
   constexpr int W_IT = (WF4 + 255) / 256;
-  constexpr int HU = (K % 4 == 0) ? TN * (C / 2) * (K / 4) : 0;  // (node, channel pair, m quad) units
+  // bf16 in memory and in LDS, K a multiple of 8: units of (node, channel pair, 8 components), one
+  // 16-byte load per channel, the bits stored as they are (two channels per 4-byte LDS store)
+  constexpr bool OCT = std::is_same<S, __bf16>::value && BF16 && K % 8 == 0;
+  constexpr int HU8 = OCT ? TN * (C / 2) * (K / 8) : 0;
+  constexpr int H8_IT = (HU8 + 255) / 256;
+  constexpr int HU = (!OCT && K % 4 == 0) ? TN * (C / 2) * (K / 4) : 0;  // (node, channel pair, m quad) units
   constexpr int H_IT = (HU + 255) / 256;
   f4 wbuf[W_IT > 0 ? W_IT : 1];
   f4 ha[H_IT > 0 ? H_IT : 1], hb[H_IT > 0 ? H_IT : 1];
+  uint4 h8a[H8_IT > 0 ? H8_IT : 1], h8b[H8_IT > 0 ? H8_IT : 1];
 #pragma unroll
   for (int it = 0; it < W_IT; ++it) {
     const int i = tid + it * 256;
@@ -129,6 +137,21 @@ __global__ __launch_bounds__(256) void linear_kernel(int N, const S* __restrict_
       const S* src = h + base + ((size_t)n * C + 2 * cp) * K + 4 * mq;
       ha[it] = ld4s(src);
       hb[it] = ld4s(src + K);
+    }
+  }
+  if constexpr (OCT) {
+#pragma unroll
+    for (int it = 0; it < H8_IT; ++it) {
+      const int u = tid + it * 256;
+      const int mo = u % (K / 8);
+      const int cp = (u / (K / 8)) % (C / 2);
+      const int n = u / ((K / 8) * (C / 2));
+      h8a[it] = h8b[it] = uint4{0u, 0u, 0u, 0u};
+      if (u < HU8 && n < nv) {
+        const S* src = h + base + ((size_t)n * C + 2 * cp) * K + 8 * mo;
+        h8a[it] = *reinterpret_cast<const uint4*>(src);
+        h8b[it] = *reinterpret_cast<const uint4*>(src + K);
+      }
     }
   }
 #pragma unroll
@@ -154,6 +177,26 @@ __global__ __launch_bounds__(256) void linear_kernel(int N, const S* __restrict_
         T* d = hT + (4 * mq + q) * Cfg::PLANE + n * RS + 2 * cp;
         d[0] = to_op<T>(ha[it][q]);
         d[1] = to_op<T>(hb[it][q]);
+      }
+    }
+  }
+  if constexpr (OCT) {
+#pragma unroll
+    for (int it = 0; it < H8_IT; ++it) {
+      const int u = tid + it * 256;
+      if (u < HU8) {
+        const int mo = u % (K / 8);
+        const int cp = (u / (K / 8)) % (C / 2);
+        const int n = u / ((K / 8) * (C / 2));
+        const uint32_t wa[4] = {h8a[it].x, h8a[it].y, h8a[it].z, h8a[it].w};
+        const uint32_t wb[4] = {h8b[it].x, h8b[it].y, h8b[it].z, h8b[it].w};
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          // component 8 mo + q of channels 2cp (low half) and 2cp + 1 (high half)
+          const uint32_t a = q & 1 ? wa[q >> 1] >> 16 : wa[q >> 1] & 0xffffu;
+          const uint32_t b = q & 1 ? wb[q >> 1] & 0xffff0000u : wb[q >> 1] << 16;
+          *reinterpret_cast<uint32_t*>(hT + (8 * mo + q) * Cfg::PLANE + n * RS + 2 * cp) = a | b;
+        }
       }
     }
   }

@@ -131,3 +131,29 @@ def test_radial_backward_radial_workload_full():
     _say("radial backward radial workload E=%d" % wl.src.shape[0])
     errs = _check(eq, wl, gout, what="radial workload")
     _say("radial workload rel errors %s" % (errs,))
+
+
+@pytest.mark.parametrize("unsorted", [False, True])
+def test_radial_autograd_function(unsorted):
+    """equivariant_conv with radial weights: forward and the three gradients through torch.autograd."""
+    import torch
+
+    eq = _eq()
+    from spherical_harmonic_cg_amd.autograd import equivariant_conv
+
+    wl = synth.small_graph(19, 7, 32, 3, 990 + int(unsorted), radial=True, r_cut=5.0, zero_vec_edges=1)
+    gout = _gout(wl, 15)
+    vec = _t(wl.vec).requires_grad_(True)
+    x = _t(wl.x).requires_grad_(True)
+    W = _t(wl.w_rad).requires_grad_(True)
+    kw = dict(dst=_t(wl.dst)) if unsorted else dict(row_ptr=_t(wl.row_ptr))
+    _say("radial autograd unsorted=%s" % unsorted)
+    out = equivariant_conv(vec, x, W, _t(wl.src), 3, weight_mode=RAD, r_cut=wl.r_cut, **kw)
+    ref_out = oracle.conv(wl.N, wl.vec, wl.src, wl.dst, wl.x, wl.w_rad, 3, weight_mode=1, r_cut=wl.r_cut)
+    _assert_close(_np(out.detach()), ref_out, TOL, "radial autograd forward")
+    (out * _t(gout)).sum().backward()
+    torch.cuda.synchronize()
+    ref = oracle.conv_backward_radial(wl.N, wl.vec, wl.src, wl.dst, wl.x, wl.w_rad, gout, 3, wl.r_cut)
+    _assert_close(_np(x.grad), ref[0], TOL, "radial autograd grad_x")
+    _assert_close(_np(W.grad), ref[1], TOL, "radial autograd grad_W")
+    _assert_close(_np(vec.grad), ref[2], TOL, "radial autograd grad_vec")
