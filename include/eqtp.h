@@ -172,8 +172,9 @@ int eqtp_conv_fused(const eqtp_conv_desc* d, int64_t N, int64_t E, const float* 
 /*
  * Bytes of device workspace eqtp_conv_fused_ws needs for (d, N, E): for
  * EQTP_EDGES_UNSORTED with N > 0, 256-byte aligned regions for row pointers
- * [N+1], staged edge indices [E], grouped vectors [E,3] and sources [E] (about
- * 20 bytes per edge); 0 for dst-sorted edges.  Negative status for a bad
+ * [N+1], five int arrays [E] (the sort's keys and edge indices, later the
+ * grouped vectors [E,3] and sources [E]) and the sort's digit counts (about
+ * 20.5 bytes per edge); 0 for dst-sorted edges.  Negative status for a bad
  * descriptor or sizes.
  */
 int64_t eqtp_conv_workspace_bytes(const eqtp_conv_desc* d, int64_t N, int64_t E);
@@ -182,9 +183,9 @@ int64_t eqtp_conv_workspace_bytes(const eqtp_conv_desc* d, int64_t N, int64_t E)
  * The fused convolution of eqtp_conv_fused with a caller-given workspace.
  * Dst-sorted edges: exactly eqtp_conv_fused (the workspace is not touched).
  * Edges in any order (d->edge_order = EQTP_EDGES_UNSORTED, dst given): the
- * edges are first grouped by destination in the workspace -- a counting sort
- * on the GPU whose rows keep the edges' input order, so the grouping does not
- * depend on the order of hardware atomics -- and the call then runs as for
+ * edges are first grouped by destination in the workspace -- a stable radix
+ * sort on the GPU, so every row keeps its edges' input order and the grouping
+ * does not depend on the order of hardware atomics -- and the call then runs as for
  * dst-sorted edges (d->algo as there; row_ptr is ignored).  The result is
  * deterministic (bit-identical from call to call) and no atomics touch out.
  * The grouping is layout preparation for the destination sum of the

@@ -199,19 +199,24 @@ int conv_impl(const eqtp_conv_desc* d, int64_t N, int64_t E, const float* vec, c
   return status_of(use_node ? eqtp::launch_conv_node(a) : eqtp::launch_conv_edge(a));
 }
 
-// Workspace of the grouping by destination: row pointers [N+1], the scatter's
-// staged edge indices [E], and the grouped vectors [E,3] and sources [E],
-// each region 256-byte aligned.
+// Workspace of the grouping by destination: row pointers [N+1]; five regions of
+// E ints R0..R4 (the radix sort's keys and edge indices: the last pass leaves
+// them in R0 and R4); the sort's digit counts.  After the sort the grouped
+// vectors [E,3] overwrite R0..R2 (contiguous, 12 E bytes) and the grouped
+// sources R3.  Every region 256-byte aligned.
 struct WsLayout {
-  size_t staged, vec, src, total;
+  size_t r[5], hist, total;
 };
 WsLayout ws_layout(int64_t N, int64_t E) {
   auto al = [](int64_t b) { return (size_t)((b + 255) & ~(int64_t)255); };
   WsLayout w;
-  w.staged = al((N + 1) * 4);
-  w.vec = w.staged + al(E * 4);
-  w.src = w.vec + al(E * 12);
-  w.total = w.src + al(E * 4);
+  size_t o = al((N + 1) * 4);
+  for (int i = 0; i < 5; ++i) {
+    w.r[i] = o;
+    o += al(E * 4);
+  }
+  w.hist = o;
+  w.total = o + al(eqtp::radix_hist_entries(E) * 4);
   return w;
 }
 
@@ -229,9 +234,11 @@ int conv_ws_impl(const eqtp_conv_desc* d, int64_t N, int64_t E, const float* vec
   if (E > 0 && (!dst || !aligned4(dst))) return EQTP_EINVAL;
   unsigned char* ws = static_cast<unsigned char*>(workspace);
   int32_t* rp = reinterpret_cast<int32_t*>(ws);
-  int32_t* staged = reinterpret_cast<int32_t*>(ws + L.staged);
-  float* vec_s = reinterpret_cast<float*>(ws + L.vec);
-  int32_t* src_s = reinterpret_cast<int32_t*>(ws + L.src);
+  int32_t* R[5];
+  for (int i = 0; i < 5; ++i) R[i] = reinterpret_cast<int32_t*>(ws + L.r[i]);
+  int32_t* hist = reinterpret_cast<int32_t*>(ws + L.hist);
+  float* vec_s = reinterpret_cast<float*>(R[0]);  // spans R0..R2
+  int32_t* src_s = R[3];
   // the call as it runs after the grouping: dst-sorted edges
   eqtp_conv_desc ds{};
   memcpy(&ds, d, (size_t)d->struct_size);  // a descriptor of the earlier size ends before x_dtype
@@ -240,7 +247,8 @@ int conv_ws_impl(const eqtp_conv_desc* d, int64_t N, int64_t E, const float* vec
   ds.edge_order = EQTP_EDGES_DST_SORTED;
   int rc = conv_impl(&ds, N, E, vec, src, nullptr, rp, x, weights, out, stream, false);
   if (rc != EQTP_OK) return rc;
-  rc = status_of(eqtp::launch_sort_edges_ordered(N, E, dst, vec, src, rp, staged, vec_s, src_s, (hipStream_t)stream));
+  rc = status_of(eqtp::launch_sort_edges_stable(N, E, dst, vec, src, rp, R[0], R[4], R[1], R[2], hist, vec_s, src_s,
+                                                (hipStream_t)stream));
   if (rc != EQTP_OK) return rc;
   return conv_impl(&ds, N, E, vec_s, src_s, nullptr, rp, x, weights, out, stream, true);
 }

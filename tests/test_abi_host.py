@@ -257,7 +257,12 @@ def test_conv_ws_validation():
     d = _desc(e, edge_order=1)
     need = lib.eqtp_conv_workspace_bytes(ctypes.byref(d), 100, 1000)
     al = lambda b: (b + 255) // 256 * 256
-    assert need == al(101 * 4) + al(1000 * 4) + al(1000 * 12) + al(1000 * 4)
+    # row pointers, five E-int regions of the radix sort, its digit counts (512 bins x (tiles + 1) + 1;
+    # tiles of 256 x rounds edges, rounds = E / (256 * 512) clamped to 1..16)
+    assert need == al(101 * 4) + 5 * al(1000 * 4) + al((512 * (4 + 1) + 1) * 4)
+    big = lib.eqtp_conv_workspace_bytes(ctypes.byref(d), 100000, 5239100)
+    assert big == al(100001 * 4) + 5 * al(5239100 * 4) + al((512 * ((5239100 + 4095) // 4096 + 1) + 1) * 4)
+    assert big < (128 << 20)     # the large workload in random order fits the no-allocation scratch
     assert lib.eqtp_conv_workspace_bytes(ctypes.byref(_desc(e)), 100, 1000) == 0   # dst-sorted: none
     assert lib.eqtp_conv_workspace_bytes(ctypes.byref(d), -1, 10) == -1
     assert lib.eqtp_conv_workspace_bytes(ctypes.byref(d), 0, 0) == 0
