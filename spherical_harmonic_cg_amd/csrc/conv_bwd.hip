@@ -27,6 +27,7 @@
 // both needs about 300 registers at lmax 3, which leaves one wave per SIMD.
 #include "eqtp_device.hpp"
 #include "eqtp_kernels.hpp"
+#include "so2_device.hpp"
 
 namespace eqtp {
 
@@ -662,6 +663,18 @@ __device__ __forceinline__ void radial_basis_grad(float r, float inv_rc, float (
 // starts: otherwise the compiler is free to leave sums to the end of the walk
 // with all their inputs live, several hundred registers at lmax 3.
 // ---------------------------------------------------------------------------
+// true if the edge-aligned terms hold every path 0..P-1, in path order (the walk below reads the next
+// path's weights one path ahead)
+template <class S>
+constexpr bool so2_paths_in_order() {
+  int expect = 0;
+  for (int i = 0; i < S::NT; ++i) {
+    if (S::terms[i].p == expect) ++expect;
+    else if (S::terms[i].p != expect - 1) return false;
+  }
+  return expect == S::P;
+}
+
 constexpr int kRbNB = 8;     // radial functions
 constexpr int kRbWaves = 4;  // waves per workgroup
 constexpr int kRbChunk = 64; // edges per run, unsorted edges
@@ -673,11 +686,12 @@ __global__ __launch_bounds__(kRbWaves * kWave) void conv_bwd_radial_kernel(
     const float* __restrict__ W, const float* __restrict__ gout, float* __restrict__ gx, float* __restrict__ gW,
     float* __restrict__ gvec, float inv_rc) {
   using T = Tables<L, PS>;
-  using O1 = TermOrder<L, PS, 1>;
   using O2 = TermOrder<L, PS, 2>;
+  using S = So2Tables<L, PS>;
   constexpr int K = num_comp(L);
   constexpr int P = T::P;
   constexpr int NB = kRbNB;
+  static_assert(S::P == P && so2_paths_in_order<S>(), "edge-aligned terms: every path, in path order");
   constexpr int XB = 16 * K;  // floats of one edge's block of 16 channels
   __shared__ __attribute__((aligned(16))) float wt[P * 16 * NB];  // W slice, [p][j][b]
   constexpr int GWL = PASS == 1 ? NB * P * 16 : 1;
@@ -721,8 +735,6 @@ __global__ __launch_bounds__(kRbWaves * kWave) void conv_bwd_radial_kernel(
     if constexpr (SORTED) asm volatile("" : "+v"(d));  // a new value each round: not hoisted out of the row
 #pragma unroll
     for (int k = 0; k < K; ++k) gv[k] = gout[((size_t)d * C + cb + j) * K + k];
-    float Y[16];
-    sh_eval<L>(vx, vy, vz, Y);
     const float r = sqrtf(vx * vx + vy * vy + vz * vz);
     float R[NB], dR[NB];
     radial_basis_grad<NB>(r, inv_rc, R, dR);
@@ -755,16 +767,29 @@ __global__ __launch_bounds__(kRbWaves * kWave) void conv_bwd_radial_kernel(
       float aR = 0.0f;  // MFMA A operand: R_j of this lane's edge (rows j >= 8 are zero)
 #pragma unroll
       for (int b = 0; b < NB; ++b) aR = j == b ? R[b] : aR;
-      // (path, mu1) walk: grad_x, T_p -> grad_W and dL/dr
-      float mx[K];
+      // The walk in the edge frame (the edge-aligned form of the coupling): with D = D(R_e),
+      // message_e = D^T P(w_e) D x, so grad_x = D^T P(w_e)^T D g and T_p = (D g) . P_p (D x); x and g are
+      // rotated in, the sparse terms (by (path, mu3) runs) give both, the grad_x sums are rotated back.
+      const So2Frame<L> fr(vx, vy, vz);
+      float xr[K], gr[K], mx[K];
 #pragma unroll
-      for (int k = 0; k < K; ++k) mx[k] = 0.0f;
+      for (int k = 0; k < K; ++k) {
+        xr[k] = xv[k];
+        gr[k] = gv[k];
+        mx[k] = 0.0f;
+      }
+      so2_rotate_in<L>(xr, fr);
+      so2_rotate_in<L>(gr, fr);
       // wp = sum_b R_b W_b (the path weight), wd = sum_b R_b' W_b (its derivative in r)
-      float wp = 0.0f, wd = 0.0f, tp = 0.0f, s1 = 0.0f, dr = 0.0f;
-      static_for<0, T::NT>([&](auto jj) {
-        constexpr int q = decltype(jj)::value;
-        constexpr eqtp_gen::CgTerm tm = O1::term(q);
-        if constexpr (O1::path_first(q)) {
+      float wp = 0.0f, wd = 0.0f, tp = 0.0f, t = 0.0f, qg = 0.0f, dr = 0.0f;
+      static_for<0, S::NT>([&](auto ii) {
+        constexpr int i = decltype(ii)::value;
+        constexpr eqtp_gen::So2Term tm = S::terms[i];
+        constexpr bool p_first = i == 0 || S::terms[i - 1].p != tm.p;
+        constexpr bool p_last = i + 1 == S::NT || S::terms[i + 1].p != tm.p;
+        constexpr bool run_first = p_first || S::terms[i - 1].mu3 != tm.mu3;
+        constexpr bool run_last = p_last || S::terms[i + 1].mu3 != tm.mu3;
+        if constexpr (p_first) {
           wp = wd = 0.0f;
 #pragma unroll
           for (int b = 0; b < 4; ++b) {
@@ -777,23 +802,26 @@ __global__ __launch_bounds__(kRbWaves * kWave) void conv_bwd_radial_kernel(
             prefetch(tm.p + 1, wp, dr);
             settle(mx);  // likewise the grad_x sums: each path's terms are added before the next starts
           }
+          if constexpr (tm.l2 > 0) wp *= fr.keep;  // a zero vector drops the paths with l2 > 0
           tp = 0.0f;
         }
-        const float cy = tm.c * Y[tm.mu2];
-        s1 = O1::first(q) ? cy * gv[tm.mu3] : fmaf(cy, gv[tm.mu3], s1);
-        if constexpr (O1::last(q)) {
-          mx[tm.mu1] = fmaf(wp, s1, mx[tm.mu1]);
-          tp = fmaf(xv[tm.mu1], s1, tp);
+        if constexpr (run_first) qg = wp * gr[tm.mu3];
+        mx[tm.mu1] = fmaf(tm.c, qg, mx[tm.mu1]);
+        t = run_first ? tm.c * xr[tm.mu1] : fmaf(tm.c, xr[tm.mu1], t);
+        if constexpr (run_last) {
+          tp = fmaf(gr[tm.mu3], t, tp);
           __builtin_amdgcn_sched_barrier(0);
         }
-        if constexpr (O1::path_last(q)) {
+        if constexpr (p_last) {
           // (no branches in the walk: a branch per path splits it into blocks across which the compiler
-          // keeps common products live, several hundred registers at lmax 3)
+          // keeps common products live)
+          if constexpr (tm.l2 > 0) tp *= fr.keep;
           dr = fmaf(wd, tp, dr);                // dL/dr += sum_b R_b' W_b T_p
           xw[tm.p * kWave + lane] = tp;         // T_p of the round, for the grad_W products below
           __builtin_amdgcn_sched_barrier(0);
         }
       });
+      so2_rotate_out<L>(mx, fr);
       if (want_w) {
         // grad_W: per path, D[b][j] += sum_kq R_b(edge kq) T_p(edge kq, j) on the matrix cores, into the
         // wave's accumulators
