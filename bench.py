@@ -437,6 +437,10 @@ def main():
             def bwd():
                 eq.eqtp_conv_backward(bvec, bsrc, x, w, gout, wl.lmax, path_set=wl.path_set, **bkw)
 
+            def bwd_so2():
+                eq.eqtp_conv_backward(bvec, bsrc, x, w, gout, wl.lmax, path_set=wl.path_set,
+                                      algo=eq.EQTP_ALGO_EDGE_SO2, **bkw)
+
             # by source: destinations of the CSR, sort by source, grad_x and grad_w on
             # the matrix cores, grad_vec edge by edge (what the autograd wrapper runs)
             E_ = wl.E
@@ -466,15 +470,27 @@ def main():
                 torch.cuda.synchronize()
                 return b0.elapsed_time(b1) / kb, kb
 
-            bms, kb = timed(bwd)
-            sms, _ = timed(bwd_src)
-            backward = {"ms": round(sms, 5), "edges_per_s": round(wl.E / (sms * 1e-3), 1), "launches": kb,
-                        "what": "grad_x, grad_w and grad_vec of the conv: source grouping on the GPU "
-                                "(eqtp_edge_rows + eqtp_sort_edges), eqtp_conv_backward_by_source (grad_x, grad_w), "
-                                "eqtp_conv_backward (grad_vec)",
-                        "edge_path_ms": round(bms, 5),
-                        "edge_path_what": "all three from eqtp_conv_backward (fp32 atomics for grad_x)"}
-            log("backward: by source %.4f ms (%.3e edges/s); edge path %.4f ms" % (sms, wl.E / (sms * 1e-3), bms))
+            if wl.lmax > 3:
+                oms, kb = timed(bwd_so2)
+                backward = {"ms": round(oms, 5), "edges_per_s": round(wl.E / (oms * 1e-3), 1), "launches": kb,
+                            "what": "grad_x, grad_w and grad_vec of the conv in the edge-aligned form "
+                                    "(eqtp_conv_backward above lmax 3: zero fills + one kernel, fp32 atomics "
+                                    "for grad_x)"}
+                log("backward (edge-aligned form): %.4f ms (%.3e edges/s)" % (oms, wl.E / (oms * 1e-3)))
+            else:
+                bms, kb = timed(bwd)
+                sms, _ = timed(bwd_src)
+                oms, _ = timed(bwd_so2)
+                backward = {"ms": round(sms, 5), "edges_per_s": round(wl.E / (sms * 1e-3), 1), "launches": kb,
+                            "what": "grad_x, grad_w and grad_vec of the conv: source grouping on the GPU "
+                                    "(eqtp_edge_rows + eqtp_sort_edges), eqtp_conv_backward_by_source (grad_x, "
+                                    "grad_w), eqtp_conv_backward (grad_vec)",
+                            "edge_path_ms": round(bms, 5),
+                            "edge_path_what": "all three from eqtp_conv_backward (fp32 atomics for grad_x)",
+                            "edge_aligned_ms": round(oms, 5),
+                            "edge_aligned_what": "all three from eqtp_conv_backward with EQTP_ALGO_EDGE_SO2"}
+                log("backward: by source %.4f ms (%.3e edges/s); edge path %.4f ms; edge-aligned %.4f ms" % (
+                    sms, wl.E / (sms * 1e-3), bms, oms))
 
     interaction = None
     if args.interaction:

@@ -253,10 +253,16 @@ int eqtp_conv_messages(const eqtp_conv_desc* d, int64_t N, int64_t E, const floa
  *   grad_vec[e] += (sum_b R_b'(r_e) sum_{p,c} W[b, p*C+c] T_e[p, c]) vec_e / r_e
  * (the product and chain rule through the radial basis; R_b' = dR_b/dr).
  * A zero-length edge vector has grad_vec = 0.
+ * Fixed weights at lmax 4..6, or with d->algo = EQTP_ALGO_EDGE_SO2 at any
+ * lmax: the edge-aligned form (E2Former-V2 page, section 2.1), where grad_x
+ * and grad_w come from the sparse coupling in each edge's frame and grad_vec
+ * from the generators of rotations about the frame's x and y axes acting on
+ * the rotated features (same formulas as above, to rounding); C = 128 only
+ * up to lmax 4.
  *   d, N, E, vec, src, dst, row_ptr, x, weights: as for eqtp_conv_fused
- *            (x fp32, 16-byte aligned).  Radial weights: lmax 0..3, C a
- *            multiple of 16, n_basis 8, r_cut > 0 (else EQTP_EUNSUPPORTED /
- *            EQTP_EINVAL); weights [8, P*C] fp32.
+ *            (x fp32, 16-byte aligned; lmax 0..6).  Radial weights: lmax
+ *            0..3, C a multiple of 16, n_basis 8, r_cut > 0 (else
+ *            EQTP_EUNSUPPORTED / EQTP_EINVAL); weights [8, P*C] fp32.
  *   grad_out [N, C, K] fp32, 16-byte aligned.
  *   grad_x   [N, C, K] fp32, 16-byte aligned, or NULL (not computed).
  *   grad_w   [P, C] fp32 (fixed weights) or [8, P*C] (radial), or NULL.
@@ -266,10 +272,11 @@ int eqtp_conv_messages(const eqtp_conv_desc* d, int64_t N, int64_t E, const floa
  * summation order varies from run to run); with fixed weights grad_vec is
  * written once per edge, with radial weights it is a sum of fp32 atomics
  * (two per 16-channel block).  Errors as for eqtp_conv_fused.  d->algo
- * (fixed weights): for dst-sorted edges, grad_vec runs on the matrix cores
- * (dL/dY_e = x[src_e] contracted with a per-node B_d built from grad_out)
- * unless d->algo = EQTP_ALGO_EDGE_VALU, which walks the coupling per edge on
- * the vector ALUs.  Radial weights ignore d->algo.
+ * (fixed weights, lmax <= 3): for dst-sorted edges, grad_vec runs on the
+ * matrix cores (dL/dY_e = x[src_e] contracted with a per-node B_d built from
+ * grad_out) unless d->algo = EQTP_ALGO_EDGE_VALU, which walks the coupling
+ * per edge on the vector ALUs, or EQTP_ALGO_EDGE_SO2 (the edge-aligned form
+ * above).  Radial weights ignore d->algo.
  */
 int eqtp_conv_backward(const eqtp_conv_desc* d, int64_t N, int64_t E, const float* vec, const int32_t* src,
                        const int32_t* dst, const int32_t* row_ptr, const float* x, const float* weights,

@@ -369,13 +369,20 @@ int eqtp_conv_backward(const eqtp_conv_desc* d, int64_t N, int64_t E, const floa
   if (!desc_ok(d)) return EQTP_EINVAL;
   if (desc_x_dtype(d) != EQTP_F32) return desc_x_dtype(d) == EQTP_BF16 ? EQTP_EUNSUPPORTED : EQTP_EINVAL;
   if (d->lmax < 0) return EQTP_EINVAL;
-  if (d->lmax > 3) return EQTP_EUNSUPPORTED;
+  if (d->lmax > eqtp::kSo2MaxL) return EQTP_EUNSUPPORTED;
   if (d->path_set != EQTP_PATHS_PARITY && d->path_set != EQTP_PATHS_SO3) return EQTP_EINVAL;
   if (d->weight_mode != EQTP_W_FIXED && d->weight_mode != EQTP_W_RADIAL) return EQTP_EINVAL;
   if (d->edge_order != EQTP_EDGES_DST_SORTED && d->edge_order != EQTP_EDGES_UNSORTED) return EQTP_EINVAL;
+  if (d->algo != EQTP_ALGO_AUTO && d->algo != EQTP_ALGO_NODE_MFMA && d->algo != EQTP_ALGO_EDGE_VALU &&
+      d->algo != EQTP_ALGO_EDGE_SO2)
+    return EQTP_EINVAL;
   if (d->C <= 0) return EQTP_EINVAL;
   if (!valid_c(d->C)) return EQTP_EUNSUPPORTED;
   const bool radial = d->weight_mode == EQTP_W_RADIAL;
+  // fixed weights above lmax 3, or when asked for: the edge-aligned form
+  const bool use_so2 = !radial && (d->lmax > 3 || d->algo == EQTP_ALGO_EDGE_SO2);
+  if (d->lmax > 3 && !use_so2) return EQTP_EUNSUPPORTED;
+  if (use_so2 && d->C == 128 && d->lmax > eqtp::kSo2MaxLC128) return EQTP_EUNSUPPORTED;
   if (radial) {
     if (!(d->r_cut > 0.0f)) return EQTP_EINVAL;
     if (d->n_basis != 8 || d->C % 16 != 0) return EQTP_EUNSUPPORTED;
@@ -411,7 +418,9 @@ int eqtp_conv_backward(const eqtp_conv_desc* d, int64_t N, int64_t E, const floa
   a.algo = d->algo;
   a.r_cut = d->r_cut;
   a.stream = (hipStream_t)stream;
-  return status_of(radial ? eqtp::launch_conv_backward_radial(a) : eqtp::launch_conv_backward(a));
+  return status_of(radial    ? eqtp::launch_conv_backward_radial(a)
+                   : use_so2 ? eqtp::launch_conv_backward_so2(a)
+                             : eqtp::launch_conv_backward(a));
 }
 
 int eqtp_conv_backward_by_source(const eqtp_conv_desc* d, int64_t N, int64_t E, const float* vec_s,

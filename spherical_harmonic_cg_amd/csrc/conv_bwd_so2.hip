@@ -1,0 +1,323 @@
+// conv_bwd_so2.hip -- gradients of the fixed-weight convolution in the
+// edge-aligned (SO(2)) form, for lmax 0..6 (E2Former-V2 page, section 2.1
+// "derivation of EAAS"; the page names a PyTorch autograd function with a
+// backward as the integration path, section "extension possibilities").
+//
+// For L = sum grad_out * out with out[d] = sum_{e: dst_e = d} D^T P_w(D x[src_e])
+// (D = D(R_e) the action on the real harmonics of the rotation R_e that takes
+// the edge direction to the z axis, P_w the coupling with the harmonics of the
+// z axis and per-path weights w[p, c]; see conv_so2.hip), per edge and
+// channel, with x' = D x[src_e] and g' = D grad_out[dst_e] in the edge frame:
+//   grad_x[src_e] += D^T v',          v' = P_w^T g'
+//   grad_w[p, c]  += g' . P_p x'      (P_p: path p's part of the coupling)
+// and for the edge vector: dL/dvec = sum_mu dL/dY_mu dY_mu/dvec.  At the z
+// axis only the m = +-1 harmonics have a tangential derivative, and
+//   dY(z)/dx = L_y Y(z),   dY(z)/dy = -L_x Y(z)
+// with L_a the generator of rotations about axis a (L_a = d/de D(R_a(e)) at
+// e = 0).  The coupling is invariant under rotations, so for every generator
+//   C(L a, Y, b) + C(a, L Y, b) + C(a, Y, L b) = 0,
+// which moves the derivative off the harmonics onto x' and g':
+//   G_x = -(v' . L_y x' + u' . L_y g'),   G_y = v' . L_x x' + u' . L_x g',
+//   dL/dvec = R_e^T (G_x, G_y, 0) / |vec|        (summed over channels),
+// with u' = P_w x' the message in the frame.  So the whole gradient costs two
+// rotations in, one walk of the sparse coupling (624 terms at lmax 6, not the
+// 6460 of the full coupling), four products with the 72-entry generators
+// and one rotation back.  A zero edge vector drops the paths with l2 > 0 (as
+// the forward does) and has grad_vec = 0.  L_x, L_y and the identity above
+// are generated and checked in gen_so2_table.py.
+//
+// Lane mapping as in the forward: lane = channel (C <= 64: 64/C edges per
+// wave round; C = 128: two channels per lane).  Persistent waves take
+// destination rows (dst-sorted edges) or runs of edges (any order, dst[]).
+// grad_x: fp32 atomics after an LDS exchange (each instruction adds 64
+// consecutive floats of one source's row); grad_w: LDS atomics into the
+// workgroup's [P][C] sums, added to memory once per workgroup; grad_vec: the
+// channel sum by xor shuffles, one store per edge.
+#include "eqtp_device.hpp"
+#include "eqtp_kernels.hpp"
+#include "so2_device.hpp"
+
+namespace eqtp {
+
+template <int C>
+struct So2BwdCfg {
+  static constexpr int CPL = C > 64 ? C / 64 : 1;  // channels per lane
+  static constexpr int CL = C / CPL;               // lanes per edge group
+  static constexpr int G = kWave / CL;             // edge groups per wave
+  static constexpr int WAVES = 4;
+  static constexpr int THREADS = WAVES * kWave;
+  static constexpr int EPW = 8 * G;                // edges per task, any order
+};
+
+// sum_r a[r] (L v)[r] for the generator L = L_x (LX) or L_y, rows of the table
+// walked with the entries as instruction immediates
+template <int K, bool LX>
+__device__ __forceinline__ float gen_form(const float (&a)[K], const float (&v)[K]) {
+  constexpr int NE = LX ? eqtp_gen::kLxRowStart[K] : eqtp_gen::kLyRowStart[K];
+  float acc = 0.0f, t = 0.0f;
+  static_for<0, NE>([&](auto ii) {
+    constexpr int i = decltype(ii)::value;
+    constexpr eqtp_gen::JEntry je = LX ? eqtp_gen::kLx[i] : eqtp_gen::kLy[i];
+    constexpr bool first = i == 0 || (LX ? eqtp_gen::kLx[i - 1].row : eqtp_gen::kLy[i - 1].row) != je.row;
+    constexpr bool last = i + 1 == NE || (LX ? eqtp_gen::kLx[i + 1].row : eqtp_gen::kLy[i + 1].row) != je.row;
+    t = first ? je.v * v[je.col] : fmaf(je.v, v[je.col], t);
+    if constexpr (last) acc = fmaf(a[je.row], t, acc);
+  });
+  return acc;
+}
+
+template <int K>
+__device__ __forceinline__ void load_vec(const float* __restrict__ p, float (&v)[K]) {
+  if constexpr (K % 4 == 0) {
+#pragma unroll
+    for (int q = 0; q < K / 4; ++q) {
+      const f4 t4 = reinterpret_cast<const f4*>(p)[q];
+      v[4 * q] = t4[0];
+      v[4 * q + 1] = t4[1];
+      v[4 * q + 2] = t4[2];
+      v[4 * q + 3] = t4[3];
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < K; ++k) v[k] = p[k];
+  }
+}
+
+// the path of the first term after path p's terms (which start at term i), or -1
+template <class T>
+constexpr int next_path_after(int i) {
+  for (int k = i; k < T::NT; ++k)
+    if (T::terms[k].p != T::terms[i].p) return T::terms[k].p;
+  return -1;
+}
+
+// ntasks: rows (row_ptr != nullptr) or runs of EPW edges
+template <int L, int PS, int C>
+__global__ __launch_bounds__(So2BwdCfg<C>::THREADS) __attribute__((amdgpu_waves_per_eu(L <= 4 ? 2 : 1))) void conv_bwd_so2_kernel(
+    int N, int E, long long ntasks, const int* __restrict__ row_ptr, const float* __restrict__ vec,
+    const int* __restrict__ src, const int* __restrict__ dst, const float* __restrict__ x,
+    const float* __restrict__ w, const float* __restrict__ gout, float* __restrict__ gx, float* __restrict__ gw,
+    float* __restrict__ gvec) {
+  using Cfg = So2BwdCfg<C>;
+  using T = So2Tables<L, PS>;
+  constexpr int K = num_comp(L);
+  constexpr int MSG = C * K;        // floats of one source row
+  constexpr int NI = Cfg::CPL * K;  // floats per lane of one round's grad_x rows
+  __shared__ float wl[T::P * C];
+  __shared__ float gwl[T::P * C];
+  __shared__ float xch[Cfg::WAVES][kWave * NI];
+  __shared__ int xsrc[Cfg::WAVES][Cfg::G];
+  for (int i = threadIdx.x; i < T::P * C; i += Cfg::THREADS) {
+    wl[i] = w[i];
+    gwl[i] = 0.0f;
+  }
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int g = lane / Cfg::CL;
+  const int cl = lane % Cfg::CL;
+  const bool sorted = row_ptr != nullptr;
+  float* const xw = xch[wv];
+
+  for (long long task = (long long)blockIdx.x * Cfg::WAVES + wv; task < ntasks;
+       task += (long long)gridDim.x * Cfg::WAVES) {
+    int e_beg = 0, e_end = 0, d_row = 0;
+    if (sorted) {
+      d_row = (int)task;
+      if (E > 0) {
+        e_beg = min(max(row_ptr[d_row], 0), E);
+        e_end = min(max(row_ptr[d_row + 1], e_beg), E);
+      }
+    } else {
+      e_beg = (int)(task * Cfg::EPW);
+      e_end = (int)min((long long)E, task * Cfg::EPW + Cfg::EPW);
+    }
+#pragma clang loop unroll(disable)
+    for (int e0 = e_beg; e0 < e_end; e0 += Cfg::G) {  // wave-uniform rounds of G edges
+      const int e = e0 + g;
+      const bool valid = e < e_end;
+      const int ee = valid ? e : e0;  // e0 < e_end: a real edge for the idle slots
+      const float vx = vec[3 * (size_t)ee], vy = vec[3 * (size_t)ee + 1], vz = vec[3 * (size_t)ee + 2];
+      const int s = clamp_index(src[ee], N);
+      const int d = sorted ? d_row : clamp_index(dst[ee], N);
+      const So2Frame<L> f(vx, vy, vz);
+      const float on = valid ? 1.0f : 0.0f;  // idle slots add nothing
+      float gxe = 0.0f, gye = 0.0f;
+#pragma clang loop unroll(disable)
+      for (int j = 0; j < Cfg::CPL; ++j) {
+        const int c = cl + j * Cfg::CL;
+        float xr[K], gr[K];
+        load_vec<K>(x + ((size_t)s * C + c) * K, xr);
+        load_vec<K>(gout + ((size_t)d * C + c) * K, gr);
+        so2_rotate_in<L, K>(xr, f);
+        so2_rotate_in<L, K>(gr, f);
+        // two walks of the sparse coupling (by path, then output component), so that at most three
+        // K-vectors are live: A: t = (P_p x')[mu3], u'[mu3] += w_p t, grad_w[p] += g'[mu3] t;
+        // B: v'[mu1] += w_p c g'[mu3]
+        {
+          float u[K];
+#pragma unroll
+          for (int k = 0; k < K; ++k) u[k] = 0.0f;
+          // each path's weight is read from LDS one path ahead; the scheduling barriers at the path
+          // boundaries keep the compiler from hoisting all P reads (P registers) to the top
+          float wp = 0.0f, kp = 0.0f, t = 0.0f, tp = 0.0f, wn = wl[T::terms[0].p * C + c];
+          static_for<0, T::NT>([&](auto ii) {
+            constexpr int i = decltype(ii)::value;
+            constexpr eqtp_gen::So2Term tm = T::terms[i];
+            constexpr bool p_first = i == 0 || T::terms[i - 1].p != tm.p;
+            constexpr bool p_last = i + 1 == T::NT || T::terms[i + 1].p != tm.p;
+            constexpr bool run_first = p_first || T::terms[i - 1].mu3 != tm.mu3;
+            constexpr bool run_last = p_last || T::terms[i + 1].mu3 != tm.mu3;
+            if constexpr (p_first) {
+              __builtin_amdgcn_sched_barrier(0);
+              kp = tm.l2 > 0 ? f.keep * on : on;  // a zero vector drops the paths with l2 > 0
+              wp = wn * kp;
+              tp = 0.0f;
+              constexpr int np = next_path_after<T>(i);
+              if constexpr (np >= 0) wn = wl[np * C + c];
+            }
+            t = run_first ? tm.c * xr[tm.mu1] : fmaf(tm.c, xr[tm.mu1], t);
+            if constexpr (run_last) {
+              u[tm.mu3] = fmaf(wp, t, u[tm.mu3]);
+              tp = fmaf(gr[tm.mu3], t, tp);
+            }
+            if constexpr (p_last) {
+              if (gw != nullptr) atomicAdd(&gwl[tm.p * C + c], kp * tp);
+            }
+          });
+          gxe -= gen_form<K, false>(u, gr);
+          gye += gen_form<K, true>(u, gr);
+        }
+        __builtin_amdgcn_sched_barrier(0);  // walk B's loads stay after walk A (bounded live range)
+        float v[K];
+#pragma unroll
+        for (int k = 0; k < K; ++k) v[k] = 0.0f;
+        {
+          float wp = 0.0f, qg = 0.0f, wn = wl[T::terms[0].p * C + c];
+          static_for<0, T::NT>([&](auto ii) {
+            constexpr int i = decltype(ii)::value;
+            constexpr eqtp_gen::So2Term tm = T::terms[i];
+            constexpr bool p_first = i == 0 || T::terms[i - 1].p != tm.p;
+            constexpr bool run_first = p_first || T::terms[i - 1].mu3 != tm.mu3;
+            if constexpr (p_first) {
+              __builtin_amdgcn_sched_barrier(0);
+              wp = wn * (tm.l2 > 0 ? f.keep * on : on);
+              constexpr int np = next_path_after<T>(i);
+              if constexpr (np >= 0) wn = wl[np * C + c];
+            }
+            if constexpr (run_first) qg = wp * gr[tm.mu3];
+            v[tm.mu1] = fmaf(tm.c, qg, v[tm.mu1]);
+          });
+        }
+        gxe -= gen_form<K, false>(v, xr);
+        gye += gen_form<K, true>(v, xr);
+        if (gx != nullptr) {
+          so2_rotate_out<L, K>(v, f);
+#pragma unroll
+          for (int k = 0; k < K; ++k) xw[(g * C + c) * K + k] = v[k];
+        }
+      }
+      if (gvec != nullptr) {
+#pragma unroll
+        for (int off = 1; off < Cfg::CL; off <<= 1) {
+          gxe += __shfl_xor(gxe, off);
+          gye += __shfl_xor(gye, off);
+        }
+        if (valid && cl == 0) {
+          // R_e^T (G_x, G_y, 0) / r, R_e = R_y(-theta) R_z(-phi); zero for a zero vector
+          const float r2 = vx * vx + vy * vy + vz * vz;
+          const float ir = r2 > 0.0f ? rsqrtf(r2) : 0.0f;
+          const float a = gxe * ir, b = gye * ir;
+          const float cph = f.cp[1 <= L ? 1 : 0], sph = f.sp[1 <= L ? 1 : 0];
+          const float cth = f.ct[1 <= L ? 1 : 0], sth = f.st[1 <= L ? 1 : 0];
+          float* gv = gvec + 3 * (size_t)e;
+          if constexpr (L >= 1) {
+            gv[0] = fmaf(a * cth, cph, -b * sph);
+            gv[1] = fmaf(a * cth, sph, b * cph);
+            gv[2] = -a * sth;
+          } else {
+            gv[0] = gv[1] = gv[2] = 0.0f;
+          }
+        }
+      }
+      if (gx != nullptr) {
+        if (cl == 0) xsrc[wv][g] = valid ? s : -1;
+        wave_lds_sync();
+        // the lane index passes through an empty asm statement so that the NI addresses below are
+        // formed here, not hoisted out of the edge loop (NI more live registers for the whole kernel)
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+          const int fi = kWave * i + ln;
+          const int sr = xsrc[wv][fi / MSG];
+          if (sr >= 0) unsafeAtomicAdd(gx + (size_t)sr * MSG + fi % MSG, xw[fi]);
+        }
+        wave_lds_sync();
+      }
+    }
+  }
+  if (gw != nullptr) {
+    __syncthreads();
+    for (int i = threadIdx.x; i < T::P * C; i += Cfg::THREADS) unsafeAtomicAdd(gw + i, gwl[i]);
+  }
+}
+
+template <int L, int PS, int C>
+static hipError_t launch_bwd_so2_t(const BwdArgs& a) {
+  using Cfg = So2BwdCfg<C>;
+  using T = So2Tables<L, PS>;
+  constexpr int K = num_comp(L);
+  hipError_t err;
+  if (a.gx && (err = launch_fill_zero(a.gx, a.N * C * K, a.stream)) != hipSuccess) return err;
+  if (a.gw && (err = launch_fill_zero(a.gw, (int64_t)T::P * C, a.stream)) != hipSuccess) return err;
+  const bool sorted = a.row_ptr != nullptr;
+  const long long ntasks = sorted ? a.N : (a.E + Cfg::EPW - 1) / Cfg::EPW;
+  if (ntasks == 0 || a.E == 0) return hipGetLastError();
+  // LDS per workgroup: weights and grad_w sums [P][C] each, the grad_x exchange
+  constexpr int64_t lds = (2LL * T::P * C + (int64_t)Cfg::WAVES * kWave * Cfg::CPL * K) * 4;
+  static_assert(lds <= 160 * 1024, "LDS budget");
+  const int64_t per_cu = lds * 2 <= 160 * 1024 ? 2 : 1;
+  const int64_t want = (int64_t)num_cus() * per_cu;
+  const int64_t need = (ntasks + Cfg::WAVES - 1) / Cfg::WAVES;
+  hipLaunchKernelGGL((conv_bwd_so2_kernel<L, PS, C>), dim3((unsigned)(need < want ? need : want)),
+                     dim3(Cfg::THREADS), 0, a.stream, (int)a.N, (int)a.E, ntasks, a.row_ptr, a.vec, a.src, a.dst,
+                     a.x, a.w, a.gout, a.gx, a.gw, a.gvec);
+  return hipGetLastError();
+}
+
+template <int L, int PS>
+static hipError_t dispatch_bwd_so2_c(const BwdArgs& a) {
+  switch (a.C) {
+    case 8: return launch_bwd_so2_t<L, PS, 8>(a);
+    case 16: return launch_bwd_so2_t<L, PS, 16>(a);
+    case 32: return launch_bwd_so2_t<L, PS, 32>(a);
+    case 64: return launch_bwd_so2_t<L, PS, 64>(a);
+    case 128:
+      if constexpr (L <= kSo2MaxLC128) return launch_bwd_so2_t<L, PS, 128>(a);
+      return hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_conv_backward_so2(const BwdArgs& a) {
+  switch (a.lmax * 2 + a.path_set) {
+    case 0: return dispatch_bwd_so2_c<0, 0>(a);
+    case 1: return dispatch_bwd_so2_c<0, 1>(a);
+    case 2: return dispatch_bwd_so2_c<1, 0>(a);
+    case 3: return dispatch_bwd_so2_c<1, 1>(a);
+    case 4: return dispatch_bwd_so2_c<2, 0>(a);
+    case 5: return dispatch_bwd_so2_c<2, 1>(a);
+    case 6: return dispatch_bwd_so2_c<3, 0>(a);
+    case 7: return dispatch_bwd_so2_c<3, 1>(a);
+    case 8: return dispatch_bwd_so2_c<4, 0>(a);
+    case 9: return dispatch_bwd_so2_c<4, 1>(a);
+    case 10: return dispatch_bwd_so2_c<5, 0>(a);
+    case 11: return dispatch_bwd_so2_c<5, 1>(a);
+    case 12: return dispatch_bwd_so2_c<6, 0>(a);
+    case 13: return dispatch_bwd_so2_c<6, 1>(a);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace eqtp

@@ -76,6 +76,8 @@ hipError_t launch_radial_mlp(int64_t E, const float* vec, float r_cut, const flo
 constexpr int kSo2MaxL = 6;
 constexpr int kSo2MaxLC128 = 4;
 hipError_t launch_conv_so2(const ConvArgs& a);
+// gradients in the edge-aligned form: fixed weights, lmax 0..6, any edge order (row_ptr or dst)
+hipError_t launch_conv_backward_so2(const BwdArgs& a);
 // edge-aligned form with radial weights on dst-sorted edges: lmax 0..3, C = 16, 32, 64 or 128
 hipError_t launch_conv_so2_radial(const ConvArgs& a);
 // grad_x / grad_w on the matrix cores from edges grouped by source: row_ptr =

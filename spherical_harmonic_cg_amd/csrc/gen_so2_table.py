@@ -27,6 +27,13 @@ receives at most a couple of input components of the same |m|.
 * Harmonic prefactors for degrees up to 6 (standalone evaluation by the
   Legendre-derivative recurrence): sqrt((2l+1)/(4 pi) (l-m)!/(l+m)!), times
   sqrt2 (-1)^m for m > 0.
+* Rotation generators for the gradient with respect to the edge vector:
+  L_a = d/de D(R_a(e)) at e = 0 for a = x, y (antisymmetric, block diagonal,
+  sparse), from L_z (each (m cos, m sin) pair: (-m v_s, m v_c)) as
+  L_y = J^T L_z J and L_x = D_y L_z D_y^T with D_y = D(R_y(pi/2)) =
+  J^T D(R_z(pi/2)) J.  Checked against central differences of fitted D, and
+  the identity the gradient kernel uses is checked against finite
+  differences of the harmonics (see check_gradient).
 """
 from __future__ import annotations
 
@@ -127,6 +134,27 @@ def z_rot(a, lmax):
     return D
 
 
+def gen_z(lmax):
+    """L_z = d/da D(R_z(a)) at a = 0."""
+    K = (lmax + 1) ** 2
+    G = np.zeros((K, K))
+    for l in range(lmax + 1):
+        for m in range(1, l + 1):
+            c, s = l * l + 2 * m - 1, l * l + 2 * m
+            G[c, s] = -m
+            G[s, c] = m
+    return G
+
+
+def generators(J, lmax):
+    """(L_x, L_y) in the real-harmonic basis, from J and L_z."""
+    Lz = gen_z(lmax)
+    Ly = J.T @ Lz @ J
+    Dy = J.T @ z_rot(math.pi / 2, lmax) @ J
+    Lx = Dy @ Lz @ Dy.T
+    return Lx, Ly
+
+
 def full_cg(lmax, path_set):
     """[(l1, l2, l3, dense real block as float64)] from the exact tables."""
     out = []
@@ -197,6 +225,79 @@ def check(lmax, path_set, J, cgl, terms):
         assert np.abs(Dr.T @ mt - full).max() < 1e-5 * max(1.0, np.abs(full).max()), "edge-aligned product"
 
 
+def check_generators(J, lmax):
+    K = (lmax + 1) ** 2
+    Lx, Ly = generators(J, lmax)
+    eps = 1e-4
+    for G, rot in ((Lx, rot_x), (Ly, rot_y)):
+        fd = (wigner_fit(rot(eps), lmax) - wigner_fit(rot(-eps), lmax)) / (2 * eps)
+        assert np.abs(G - fd).max() < 1e-6, "generator against central differences"
+        assert np.abs(G + G.T).max() < 1e-12, "generator not antisymmetric"
+    # L_z itself, and the pole derivatives: d/dx Y(z axis) = L_y Y(z axis), d/dy Y(z axis) = -L_x Y(z axis)
+    fd = (wigner_fit(rot_z(eps), lmax) - wigner_fit(rot_z(-eps), lmax)) / (2 * eps)
+    assert np.abs(gen_z(lmax) - fd).max() < 1e-6
+    y0 = real_sh(np.array([[0.0, 0.0, 1.0]]), lmax)[0]
+    h = 1e-4  # the harmonics' own evaluation limits the difference quotient near the pole to ~1e-7
+    for a, want in ((0, Ly @ y0), (1, -(Lx @ y0))):
+        e = np.zeros(3)
+        e[a] = h
+        up, dn = np.array([[0.0, 0.0, 1.0]]) + e, np.array([[0.0, 0.0, 1.0]]) - e
+        d = (real_sh(up / np.linalg.norm(up), lmax)[0] - real_sh(dn / np.linalg.norm(dn), lmax)[0]) / (2 * h)
+        assert np.abs(d - want).max() < 1e-6 * max(1.0, np.abs(want).max()), "pole derivative"
+    return Lx, Ly
+
+
+def check_gradient(lmax, J, Lx, Ly, cgl, terms):
+    """The gradient of L = g . out_e with respect to the edge vector, computed
+    in the edge frame as the kernel does, against central differences of the
+    full coupling: with x' = D x, g' = D g (D = D(R_e)), u' = P_w x' (the
+    message in the frame) and v' = P_w^T g',
+        G_x = -(v' . L_y x' + u' . L_y g'),  G_y = v' . L_x x' + u' . L_x g',
+        dL/dvec = R_e^T (G_x, G_y, 0) / |vec|."""
+    K = (lmax + 1) ** 2
+    rng = np.random.default_rng(11)
+
+    def loss(vec, x, g, w):
+        u = vec / np.linalg.norm(vec)
+        Y = real_sh(u[None, :], lmax)[0]
+        out = np.zeros(K)
+        for p, (l1, l2, l3, _, M) in enumerate(cgl):
+            out[l3 * l3:(l3 + 1) ** 2] += w[p] * np.einsum("ijk,i,j->k", M, x[l1 * l1:(l1 + 1) ** 2],
+                                                           Y[l2 * l2:(l2 + 1) ** 2])
+        return g @ out
+
+    for trial in range(4):
+        vec = rng.standard_normal(3) * 2.0
+        x, g, w = rng.standard_normal(K), rng.standard_normal(K), rng.standard_normal(len(cgl))
+        r = np.linalg.norm(vec)
+        theta = math.acos(vec[2] / r)
+        phi = math.atan2(vec[1], vec[0])
+        Dr = J.T @ z_rot(-theta, lmax) @ J @ z_rot(-phi, lmax)
+        xt, gt = Dr @ x, Dr @ g
+        P = np.zeros((K, K))  # P_w[mu3, mu1]
+        for (p, mu1, mu3, l2, c, _) in terms:
+            P[mu3, mu1] += w[p] * c
+        ut, vt = P @ xt, P.T @ gt
+        gx = -(vt @ (Ly @ xt) + ut @ (Ly @ gt))
+        gy = vt @ (Lx @ xt) + ut @ (Lx @ gt)
+        Re = rot_y(-theta) @ rot_z(-phi)
+        grad = Re.T @ np.array([gx, gy, 0.0]) / r
+        h = 1e-6
+        fd = np.array([(loss(vec + h * np.eye(3)[a], x, g, w) - loss(vec - h * np.eye(3)[a], x, g, w)) / (2 * h)
+                       for a in range(3)])
+        assert np.abs(grad - fd).max() < 1e-6 * max(1.0, np.abs(fd).max()), ("edge-frame gradient", lmax, grad, fd)
+
+
+def sparse_rows(M):
+    ent = []
+    for r in range(M.shape[0]):
+        for c in range(M.shape[1]):
+            if abs(M[r, c]) > 1e-12:
+                ent.append((r, c, float(np.float32(M[r, c]))))
+    starts = [next((i for i, e in enumerate(ent) if e[0] >= r), len(ent)) for r in range(M.shape[0] + 1)]
+    return ent, starts
+
+
 def main(out_path: str = OUT):
     src_hash = hashlib.sha256(open(os.path.abspath(__file__), "rb").read()).hexdigest()[:16]
     lines = []
@@ -244,6 +345,17 @@ def main(out_path: str = OUT):
     startsT = [next((i for i, e in enumerate(JTent) if e[0] >= r), len(JTent)) for r in range(nrow + 1)]
     w("constexpr short kJTRowStart[%d] = {%s};" % (nrow + 1, ", ".join(str(s) for s in startsT)))
     w("")
+    Lx, Ly = check_generators(Jfull, LMAX_SO2)
+    for name, G, axis in (("kLx", Lx, "x"), ("kLy", Ly, "y")):
+        ent, st = sparse_rows(G)
+        w("// L_%s = d/de D(R_%s(e)) at e = 0 for l <= %d (antisymmetric), non-zero entries by row" % (
+            axis, axis, LMAX_SO2))
+        w("constexpr JEntry %s[%d] = {" % (name, len(ent)))
+        for (r, c, v) in ent:
+            w("    {%d, %d, %s}," % (r, c, cg.f32_literal(v)))
+        w("};")
+        w("constexpr short %sRowStart[%d] = {%s};" % (name, nrow + 1, ", ".join(str(x) for x in st)))
+    w("")
     # harmonics of degree up to LMAX_SO2 for the standalone evaluation:
     #   Y_l0 = N_l0 Q_l^0(z),  Y_lm,c/s = sqrt2 (-1)^m N_lm Q_l^m(z) Re/Im (x + i y)^m
     # with Q_l^m = d^m P_l / dz^m and N_lm = sqrt((2l+1)/(4 pi) (l-m)!/(l+m)!)
@@ -269,6 +381,7 @@ def main(out_path: str = OUT):
             terms = so2_terms(cgl)
             K = (lmax + 1) ** 2
             check(lmax, path_set, Jfull[:K, :K], cgl, terms)
+            check_gradient(lmax, Jfull[:K, :K], Lx[:K, :K], Ly[:K, :K], cgl, terms)
             tag = "L%d_%s" % (lmax, psname)
             nnz_full = sum(len(c[3]) for c in cgl)
             summary.append((tag, len(cgl), len(terms), nnz_full))

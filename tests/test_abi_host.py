@@ -139,7 +139,10 @@ def test_conv_backward_validation():
     assert call(_desc(e, weight_mode=1, r_cut=5.0), x=NULL) == 1
     assert call(_desc(e, weight_mode=1, r_cut=5.0, edge_order=1), rp=NULL) == 1
     assert call(_desc(e, weight_mode=2)) == 1
-    assert call(_desc(e, lmax=4)) == 2
+    assert call(_desc(e, lmax=7)) == 2                                   # above lmax 6
+    assert call(_desc(e, lmax=4, weight_mode=1, r_cut=5.0)) == 2         # radial weights: lmax 0..3
+    assert call(_desc(e, lmax=5, C=128)) == 2                            # edge-aligned form: C = 128 to lmax 4
+    assert call(_desc(e, algo=7)) == 1                                   # unknown algorithm
     assert call(_desc(e, C=48)) == 2
     assert call(_desc(e, path_set=2)) == 1
     assert call(_desc(e), gx=NULL, gw=NULL, gv=NULL) == 1                 # nothing requested

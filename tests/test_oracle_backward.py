@@ -39,7 +39,7 @@ def test_sh_grad_second_route_values(lmax):
     np.testing.assert_allclose(Y, oracle.sh(v, lmax), rtol=0, atol=1e-13)
 
 
-@pytest.mark.parametrize("lmax", [1, 2, 3])
+@pytest.mark.parametrize("lmax", [1, 2, 3, 4, 6])
 def test_sh_grad_finite_differences(lmax):
     rng = np.random.default_rng(5 + lmax)
     v = rng.standard_normal((30, 3)) * rng.uniform(0.3, 4.0, (30, 1))
@@ -67,7 +67,7 @@ def test_sh_grad_zero_vector():
     assert np.all(Y[0, 1:] == 0.0) and np.all(G == 0.0)
 
 
-@pytest.mark.parametrize("lmax,ps", [(1, 0), (2, 0), (3, 0), (2, 1), (3, 1)])
+@pytest.mark.parametrize("lmax,ps", [(1, 0), (2, 0), (3, 0), (2, 1), (3, 1), (4, 0), (5, 1), (6, 0)])
 def test_backward_x_adjoint(lmax, ps):
     N, vec, src, dst, x, w, gout = _case(lmax, ps, 21 + lmax)
     gx, _, _ = oracle.conv_backward(N, vec, src, dst, x, w, gout, lmax, ps)
@@ -79,7 +79,7 @@ def test_backward_x_adjoint(lmax, ps):
         assert abs(lhs - rhs) <= 1e-12 * max(1.0, abs(rhs))
 
 
-@pytest.mark.parametrize("lmax,ps", [(1, 0), (3, 0), (3, 1)])
+@pytest.mark.parametrize("lmax,ps", [(1, 0), (3, 0), (3, 1), (4, 1), (6, 0)])
 def test_backward_w_linear(lmax, ps):
     N, vec, src, dst, x, w, gout = _case(lmax, ps, 31 + lmax)
     _, gw, _ = oracle.conv_backward(N, vec, src, dst, x, w, gout, lmax, ps)
@@ -91,7 +91,7 @@ def test_backward_w_linear(lmax, ps):
         assert abs(lhs - rhs) <= 1e-12 * max(1.0, abs(rhs))
 
 
-@pytest.mark.parametrize("lmax,ps", [(1, 0), (2, 0), (3, 0), (3, 1)])
+@pytest.mark.parametrize("lmax,ps", [(1, 0), (2, 0), (3, 0), (3, 1), (4, 0), (5, 1), (6, 0)])
 def test_backward_vec_finite_differences(lmax, ps):
     N, vec, src, dst, x, w, gout = _case(lmax, ps, 41 + lmax)
     _, _, gv = oracle.conv_backward(N, vec, src, dst, x, w, gout, lmax, ps)
