@@ -30,8 +30,9 @@
 // wave round; C = 128: two channels per lane).  Persistent waves take
 // destination rows (dst-sorted edges) or runs of edges (any order, dst[]).
 // grad_x: fp32 atomics after an LDS exchange (each instruction adds 64
-// consecutive floats of one source's row); grad_w: LDS atomics into the
-// workgroup's [P][C] sums, added to memory once per workgroup; grad_vec: the
+// consecutive floats of one source's row); grad_w: per-lane sums in
+// registers over all of the wave's edges, then LDS atomics into the
+// workgroup's [P][C] sums and one add to memory per workgroup; grad_vec: the
 // channel sum by xor shuffles, one store per edge.
 #include "eqtp_device.hpp"
 #include "eqtp_kernels.hpp"
@@ -39,14 +40,33 @@
 
 namespace eqtp {
 
-template <int C>
+template <int L, int PS, int C>
 struct So2BwdCfg {
+  static constexpr int K = num_comp(L);
+  static constexpr int P = So2Tables<L, PS>::P;
   static constexpr int CPL = C > 64 ? C / 64 : 1;  // channels per lane
   static constexpr int CL = C / CPL;               // lanes per edge group
   static constexpr int G = kWave / CL;             // edge groups per wave
-  static constexpr int WAVES = 4;
-  static constexpr int THREADS = WAVES * kWave;
   static constexpr int EPW = 8 * G;                // edges per task, any order
+  // grad_w sums over the wave's edges: per-lane registers when there are few
+  // of them, else lane-private LDS slots (a plain read-add-write per path and
+  // edge: LDS float atomics there cost far more)
+  static constexpr bool GW_REG = P * CPL <= 34;
+  static constexpr int64_t lds_bytes(int waves, bool wl) {
+    return 4LL * ((GW_REG ? (int64_t)P * C : (int64_t)waves * P * kWave * CPL) +  // grad_w sums
+                  (int64_t)waves * kWave * CPL * K +                             // grad_x exchange
+                  (wl ? (int64_t)P * C : 0) + waves * G);                        // weights, sources
+  }
+  static constexpr int64_t kLds = 160 * 1024;
+  // waves per workgroup: as many as fit (up to 4) without the weights in LDS;
+  // the weights are staged there too if they still fit, else read through the caches
+  static constexpr int WAVES = lds_bytes(4, false) <= kLds ? 4 : lds_bytes(3, false) <= kLds ? 3
+                             : lds_bytes(2, false) <= kLds ? 2 : 1;
+  static constexpr bool WL_LDS = lds_bytes(WAVES, true) <= kLds;
+  static constexpr int64_t LDS = lds_bytes(WAVES, WL_LDS);
+  static constexpr int PER_CU = LDS * 2 <= kLds ? 2 : 1;  // workgroups per compute unit
+  static constexpr int THREADS = WAVES * kWave;
+  static_assert(LDS <= kLds, "LDS budget");
 };
 
 // sum_r a[r] (L v)[r] for the generator L = L_x (LX) or L_y, rows of the table
@@ -93,24 +113,30 @@ constexpr int next_path_after(int i) {
 
 // ntasks: rows (row_ptr != nullptr) or runs of EPW edges
 template <int L, int PS, int C>
-__global__ __launch_bounds__(So2BwdCfg<C>::THREADS) __attribute__((amdgpu_waves_per_eu(L <= 4 ? 2 : 1))) void conv_bwd_so2_kernel(
+constexpr int kBwdSo2Threads = So2BwdCfg<L, PS, C>::THREADS;
+template <int L, int PS, int C>  // waves per SIMD that the LDS allows (the register budget follows)
+constexpr int kBwdSo2Occ = So2BwdCfg<L, PS, C>::WAVES * So2BwdCfg<L, PS, C>::PER_CU >= 8 ? 2 : 1;
+
+template <int L, int PS, int C>
+__global__ __launch_bounds__((kBwdSo2Threads<L, PS, C>)) __attribute__((amdgpu_waves_per_eu(
+    kBwdSo2Occ<L, PS, C>))) void conv_bwd_so2_kernel(
     int N, int E, long long ntasks, const int* __restrict__ row_ptr, const float* __restrict__ vec,
     const int* __restrict__ src, const int* __restrict__ dst, const float* __restrict__ x,
     const float* __restrict__ w, const float* __restrict__ gout, float* __restrict__ gx, float* __restrict__ gw,
     float* __restrict__ gvec) {
-  using Cfg = So2BwdCfg<C>;
+  using Cfg = So2BwdCfg<L, PS, C>;
   using T = So2Tables<L, PS>;
   constexpr int K = num_comp(L);
   constexpr int MSG = C * K;        // floats of one source row
   constexpr int NI = Cfg::CPL * K;  // floats per lane of one round's grad_x rows
-  __shared__ float wl[T::P * C];
-  __shared__ float gwl[T::P * C];
+  constexpr int GWS = Cfg::GW_REG ? T::P * C : Cfg::WAVES * T::P * kWave * Cfg::CPL;
+  __shared__ float wl[Cfg::WL_LDS ? T::P * C : 1];
+  __shared__ float gws[GWS];
   __shared__ float xch[Cfg::WAVES][kWave * NI];
   __shared__ int xsrc[Cfg::WAVES][Cfg::G];
-  for (int i = threadIdx.x; i < T::P * C; i += Cfg::THREADS) {
-    wl[i] = w[i];
-    gwl[i] = 0.0f;
-  }
+  if constexpr (Cfg::WL_LDS)
+    for (int i = threadIdx.x; i < T::P * C; i += Cfg::THREADS) wl[i] = w[i];
+  for (int i = threadIdx.x; i < GWS; i += Cfg::THREADS) gws[i] = 0.0f;
   __syncthreads();
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
@@ -118,6 +144,21 @@ __global__ __launch_bounds__(So2BwdCfg<C>::THREADS) __attribute__((amdgpu_waves_
   const int cl = lane % Cfg::CL;
   const bool sorted = row_ptr != nullptr;
   float* const xw = xch[wv];
+  // path weight of channel c (LDS copy or through the caches)
+  auto wld = [&](int p, int c) -> float {
+    if constexpr (Cfg::WL_LDS) return wl[p * C + c];
+    else return w[p * C + c];
+  };
+  // grad_w sums of this lane's channels over all its edges: registers, or the wave's slots
+  // [P][CPL][64] (slot of path p, channel c = cl + j CL at (p CPL + j) 64 + lane)
+  float gacc[Cfg::GW_REG ? Cfg::CPL : 1][Cfg::GW_REG ? T::P : 1];
+  if constexpr (Cfg::GW_REG) {
+#pragma unroll
+    for (int j = 0; j < Cfg::CPL; ++j)
+#pragma unroll
+      for (int p = 0; p < T::P; ++p) gacc[j][p] = 0.0f;
+  }
+  float* const gslot = gws + (Cfg::GW_REG ? 0 : wv * T::P * kWave * Cfg::CPL + lane);
 
   for (long long task = (long long)blockIdx.x * Cfg::WAVES + wv; task < ntasks;
        task += (long long)gridDim.x * Cfg::WAVES) {
@@ -143,8 +184,9 @@ __global__ __launch_bounds__(So2BwdCfg<C>::THREADS) __attribute__((amdgpu_waves_
       const So2Frame<L> f(vx, vy, vz);
       const float on = valid ? 1.0f : 0.0f;  // idle slots add nothing
       float gxe = 0.0f, gye = 0.0f;
-#pragma clang loop unroll(disable)
-      for (int j = 0; j < Cfg::CPL; ++j) {
+      static_for<0, Cfg::CPL>([&](auto jj) {
+        constexpr int j = decltype(jj)::value;
+        if constexpr (j > 0) __builtin_amdgcn_sched_barrier(0);  // one channel at a time
         const int c = cl + j * Cfg::CL;
         float xr[K], gr[K];
         load_vec<K>(x + ((size_t)s * C + c) * K, xr);
@@ -160,7 +202,7 @@ __global__ __launch_bounds__(So2BwdCfg<C>::THREADS) __attribute__((amdgpu_waves_
           for (int k = 0; k < K; ++k) u[k] = 0.0f;
           // each path's weight is read from LDS one path ahead; the scheduling barriers at the path
           // boundaries keep the compiler from hoisting all P reads (P registers) to the top
-          float wp = 0.0f, kp = 0.0f, t = 0.0f, tp = 0.0f, wn = wl[T::terms[0].p * C + c];
+          float wp = 0.0f, kp = 0.0f, t = 0.0f, tp = 0.0f, wn = wld(T::terms[0].p, c);
           static_for<0, T::NT>([&](auto ii) {
             constexpr int i = decltype(ii)::value;
             constexpr eqtp_gen::So2Term tm = T::terms[i];
@@ -174,18 +216,24 @@ __global__ __launch_bounds__(So2BwdCfg<C>::THREADS) __attribute__((amdgpu_waves_
               wp = wn * kp;
               tp = 0.0f;
               constexpr int np = next_path_after<T>(i);
-              if constexpr (np >= 0) wn = wl[np * C + c];
+              if constexpr (np >= 0) wn = wld(np, c);
             }
             t = run_first ? tm.c * xr[tm.mu1] : fmaf(tm.c, xr[tm.mu1], t);
             if constexpr (run_last) {
               u[tm.mu3] = fmaf(wp, t, u[tm.mu3]);
+              // the empty asm keeps each update where it is: sunk to their use after the walk, the
+              // updates would hold every run's partial sum and weight live until then
+              asm volatile("" : "+v"(u[tm.mu3]));
               tp = fmaf(gr[tm.mu3], t, tp);
             }
             if constexpr (p_last) {
-              if (gw != nullptr) atomicAdd(&gwl[tm.p * C + c], kp * tp);
+              if constexpr (Cfg::GW_REG) gacc[j][tm.p] = fmaf(kp, tp, gacc[j][tm.p]);
+              else gslot[(tm.p * Cfg::CPL + j) * kWave] = fmaf(kp, tp, gslot[(tm.p * Cfg::CPL + j) * kWave]);
             }
           });
+          __builtin_amdgcn_sched_barrier(0);
           gxe -= gen_form<K, false>(u, gr);
+          __builtin_amdgcn_sched_barrier(0);
           gye += gen_form<K, true>(u, gr);
         }
         __builtin_amdgcn_sched_barrier(0);  // walk B's loads stay after walk A (bounded live range)
@@ -193,7 +241,9 @@ __global__ __launch_bounds__(So2BwdCfg<C>::THREADS) __attribute__((amdgpu_waves_
 #pragma unroll
         for (int k = 0; k < K; ++k) v[k] = 0.0f;
         {
-          float wp = 0.0f, qg = 0.0f, wn = wl[T::terms[0].p * C + c];
+          int co = c;  // opaque: walk B reloads the weights instead of keeping walk A's P values live
+          asm volatile("" : "+v"(co));
+          float wp = 0.0f, qg = 0.0f, wn = wld(T::terms[0].p, co);
           static_for<0, T::NT>([&](auto ii) {
             constexpr int i = decltype(ii)::value;
             constexpr eqtp_gen::So2Term tm = T::terms[i];
@@ -203,20 +253,24 @@ __global__ __launch_bounds__(So2BwdCfg<C>::THREADS) __attribute__((amdgpu_waves_
               __builtin_amdgcn_sched_barrier(0);
               wp = wn * (tm.l2 > 0 ? f.keep * on : on);
               constexpr int np = next_path_after<T>(i);
-              if constexpr (np >= 0) wn = wl[np * C + c];
+              if constexpr (np >= 0) wn = wld(np, co);
             }
             if constexpr (run_first) qg = wp * gr[tm.mu3];
             v[tm.mu1] = fmaf(tm.c, qg, v[tm.mu1]);
+            asm volatile("" : "+v"(v[tm.mu1]));
           });
         }
+        __builtin_amdgcn_sched_barrier(0);
         gxe -= gen_form<K, false>(v, xr);
+        __builtin_amdgcn_sched_barrier(0);
         gye += gen_form<K, true>(v, xr);
+        __builtin_amdgcn_sched_barrier(0);
         if (gx != nullptr) {
           so2_rotate_out<L, K>(v, f);
 #pragma unroll
           for (int k = 0; k < K; ++k) xw[(g * C + c) * K + k] = v[k];
         }
-      }
+      });
       if (gvec != nullptr) {
 #pragma unroll
         for (int off = 1; off < Cfg::CL; off <<= 1) {
@@ -258,14 +312,30 @@ __global__ __launch_bounds__(So2BwdCfg<C>::THREADS) __attribute__((amdgpu_waves_
     }
   }
   if (gw != nullptr) {
-    __syncthreads();
-    for (int i = threadIdx.x; i < T::P * C; i += Cfg::THREADS) unsafeAtomicAdd(gw + i, gwl[i]);
+    if constexpr (Cfg::GW_REG) {
+#pragma unroll
+      for (int j = 0; j < Cfg::CPL; ++j)
+#pragma unroll
+        for (int p = 0; p < T::P; ++p) atomicAdd(&gws[p * C + cl + j * Cfg::CL], gacc[j][p]);
+      __syncthreads();
+      for (int i = threadIdx.x; i < T::P * C; i += Cfg::THREADS) unsafeAtomicAdd(gw + i, gws[i]);
+    } else {
+      __syncthreads();
+      for (int i = threadIdx.x; i < T::P * C; i += Cfg::THREADS) {
+        const int p = i / C, c = i % C, j = c / Cfg::CL, cc = c % Cfg::CL;
+        float sum = 0.0f;
+        for (int ww = 0; ww < Cfg::WAVES; ++ww)
+          for (int gg = 0; gg < Cfg::G; ++gg)
+            sum += gws[ww * T::P * kWave * Cfg::CPL + (p * Cfg::CPL + j) * kWave + gg * Cfg::CL + cc];
+        unsafeAtomicAdd(gw + i, sum);
+      }
+    }
   }
 }
 
 template <int L, int PS, int C>
 static hipError_t launch_bwd_so2_t(const BwdArgs& a) {
-  using Cfg = So2BwdCfg<C>;
+  using Cfg = So2BwdCfg<L, PS, C>;
   using T = So2Tables<L, PS>;
   constexpr int K = num_comp(L);
   hipError_t err;
@@ -274,11 +344,7 @@ static hipError_t launch_bwd_so2_t(const BwdArgs& a) {
   const bool sorted = a.row_ptr != nullptr;
   const long long ntasks = sorted ? a.N : (a.E + Cfg::EPW - 1) / Cfg::EPW;
   if (ntasks == 0 || a.E == 0) return hipGetLastError();
-  // LDS per workgroup: weights and grad_w sums [P][C] each, the grad_x exchange
-  constexpr int64_t lds = (2LL * T::P * C + (int64_t)Cfg::WAVES * kWave * Cfg::CPL * K) * 4;
-  static_assert(lds <= 160 * 1024, "LDS budget");
-  const int64_t per_cu = lds * 2 <= 160 * 1024 ? 2 : 1;
-  const int64_t want = (int64_t)num_cus() * per_cu;
+  const int64_t want = (int64_t)num_cus() * Cfg::PER_CU;
   const int64_t need = (ntasks + Cfg::WAVES - 1) / Cfg::WAVES;
   hipLaunchKernelGGL((conv_bwd_so2_kernel<L, PS, C>), dim3((unsigned)(need < want ? need : want)),
                      dim3(Cfg::THREADS), 0, a.stream, (int)a.N, (int)a.E, ntasks, a.row_ptr, a.vec, a.src, a.dst,
