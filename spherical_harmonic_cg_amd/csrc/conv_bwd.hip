@@ -632,33 +632,36 @@ __device__ __forceinline__ void radial_basis_grad(float r, float inv_rc, float (
 // ---------------------------------------------------------------------------
 // Gradients with radial weights, w_e[p,c] = sum_b R_b(r_e) W[b, p*C + c]
 // (the radial basis above, 8 functions; r_e = |vec_e|).  Per edge e = (s -> d)
-// and channel c, with s1 and s2 the coupling sums of the fixed-weight walk:
-//   grad_x[s,c,mu1]  += sum_p w_e[p,c] s1[p,mu1]
-//   T_e[p,c]          = sum_mu1 x[s,c,mu1] s1[p,mu1]        (dL/dw_e[p,c])
-//   grad_W[b,p*C+c]  += R_b(r_e) T_e[p,c]
-//   dL/dY_e[mu2]     += w_e[p,c] s2[p,mu2]
-//   dL/dr_e          += sum_b R_b'(r_e) sum_p W[b,p*C+c] T_e[p,c]
-//   grad_vec[e]       = sum_mu2 dL/dY_e[mu2] dY_mu2/dvec_e + dL/dr_e vec_e / r_e.
+// and channel c, in the edge frame (the edge-aligned form of the coupling,
+// E2Former-V2 page, section 2.1): with D = D(R_e), x' = D x[s], g' = D g[d]
+// and P_p the sparse coupling of path p at the frame's pole,
+//   v' = sum_p w_e[p,c] P_p^T g',  grad_x[s,c] += D^T v'
+//   T_e[p,c] = g' . P_p x'                                  (dL/dw_e[p,c])
+//   grad_W[b,p*C+c] += R_b(r_e) T_e[p,c]
+//   dL/dr_e += sum_b R_b'(r_e) sum_p W[b,p*C+c] T_e[p,c]
+//   u' = sum_p w_e[p,c] P_p x',  G_x = -(v' . L_y x' + u' . L_y g'),
+//   G_y = v' . L_x x' + u' . L_x g'  (the harmonics' part, by the rotation
+//   generators; so2_device.hpp, gen_form)
+//   grad_vec[e] = R_e^T (G_x, G_y, 0) / r_e + dL/dr_e vec_e / r_e.
 // Lane layout: a workgroup works on one block of 16 channels (lane j of each
 // 16-lane group), its four waves on edges of their own (sorted: one row per
 // wave, rows strided over the block's workgroups; unsorted: runs of 64 edges),
 // four edges per round (lane group kq takes edge kq).  The block's slice of W
 // sits in LDS as [p][j][b] (two 16-byte reads give a lane the 8 weights of a
 // path), read one path ahead of its use.
-// Pass 1 walks the coupling in (path, mu1) order; after each path's runs the
-// lane adds w_p s1 into its grad_x sums, keeps (sum_b R_b' W_b) T_p for dL/dr
-// and stages T_p in LDS.  After the walk, per path, D[b][j] = sum_kq R_b(edge
-// kq) T_p(edge kq, j) is one v_mfma_f32_16x16x4_f32 (A rows = b, 8 of 16 used;
-// k = the round's four edges; B = the staged T_p), added into an LDS copy of
-// the block's grad_W slice with LDS atomics; the slice goes to memory once per
-// workgroup.  grad_x goes out as in the fixed-weight walk (the round's
-// 4 x 16 x K contributions through LDS, 64 contiguous floats per atomic
-// instruction).  Pass 2 walks in (path, mu2) order for dL/dY.  Each pass adds
-// its part of grad_vec (pass 1: dL/dr vec / r; pass 2: the harmonics' part),
-// reduced over the block's 16 channels, with fp32 atomics.  Lanes of a round
-// past the last edge load an in-range edge and zero its radial functions,
-// which zeroes all their contributions.
-// The walks are kept free of branches, and the running sums of each path are
+// One walk of the sparse terms by (path, mu3) runs gives v', u' and T_p; per
+// path the lane keeps (sum_b R_b' W_b) T_p for dL/dr and stages T_p in LDS.
+// After the walk, per path, D[b][j] = sum_kq R_b(edge kq) T_p(edge kq, j) is
+// one v_mfma_f32_16x16x4_f32 (A rows = b, 8 of 16 used; k = the round's four
+// edges; B = the staged T_p), accumulated in the wave's matrix-core result
+// registers over its whole run of edges; the sums go into an LDS copy of the
+// block's grad_W slice once per wave and to memory once per workgroup.  grad_x
+// goes out as in the fixed-weight walk (the round's 4 x 16 x K contributions
+// through LDS, 64 contiguous floats per atomic instruction); grad_vec is
+// reduced over the block's 16 channels and added with fp32 atomics (one per
+// block and component).  Lanes of a round past the last edge load an in-range
+// edge and zero its radial functions, which zeroes all their contributions.
+// The walk is kept free of branches, and the running sums of each path are
 // settled (an empty asm that takes them as operands) before the next path
 // starts: otherwise the compiler is free to leave sums to the end of the walk
 // with all their inputs live, several hundred registers at lmax 3.
@@ -679,14 +682,13 @@ constexpr int kRbNB = 8;     // radial functions
 constexpr int kRbWaves = 4;  // waves per workgroup
 constexpr int kRbChunk = 64; // edges per run, unsorted edges
 
-template <int L, int PS, bool SORTED, int PASS>
+template <int L, int PS, bool SORTED>
 __global__ __launch_bounds__(kRbWaves * kWave) void conv_bwd_radial_kernel(
     int N, int E, int C, int nwg, const int* __restrict__ row_ptr, const float* __restrict__ vec,
     const int* __restrict__ src, const int* __restrict__ dst, const float* __restrict__ x,
     const float* __restrict__ W, const float* __restrict__ gout, float* __restrict__ gx, float* __restrict__ gW,
     float* __restrict__ gvec, float inv_rc) {
   using T = Tables<L, PS>;
-  using O2 = TermOrder<L, PS, 2>;
   using S = So2Tables<L, PS>;
   constexpr int K = num_comp(L);
   constexpr int P = T::P;
@@ -694,10 +696,10 @@ __global__ __launch_bounds__(kRbWaves * kWave) void conv_bwd_radial_kernel(
   static_assert(S::P == P && so2_paths_in_order<S>(), "edge-aligned terms: every path, in path order");
   constexpr int XB = 16 * K;  // floats of one edge's block of 16 channels
   __shared__ __attribute__((aligned(16))) float wt[P * 16 * NB];  // W slice, [p][j][b]
-  constexpr int GWL = PASS == 1 ? NB * P * 16 : 1;
-  __shared__ float gwl[GWL];  // pass 1: grad_W slice, [b][p][j]
-  // pass 1, per wave: the round's T_p (P x 64) during the walk, then its grad_x exchange (4 x XB)
-  constexpr int XCH = PASS == 1 ? (64 * P > 4 * XB ? 64 * P : 4 * XB) : 1;
+  constexpr int GWL = NB * P * 16;
+  __shared__ float gwl[GWL];  // grad_W slice, [b][p][j]
+  // per wave: the round's T_p (P x 64) during the walk, then its grad_x exchange (4 x XB)
+  constexpr int XCH = 64 * P > 4 * XB ? 64 * P : 4 * XB;
   __shared__ __attribute__((aligned(16))) float xch[kRbWaves][XCH];
   __shared__ int xsrc[kRbWaves][4];
   const int cb = (int)(blockIdx.x / nwg) * 16;
@@ -705,21 +707,20 @@ __global__ __launch_bounds__(kRbWaves * kWave) void conv_bwd_radial_kernel(
   for (int i = threadIdx.x; i < P * 16 * NB; i += kRbWaves * kWave) {
     const int b = i % NB, jj = (i / NB) % 16, p = i / (NB * 16);
     wt[i] = W[(size_t)b * P * C + (size_t)p * C + cb + jj];
-    if constexpr (PASS == 1) gwl[i] = 0.0f;
+    gwl[i] = 0.0f;
   }
   __syncthreads();
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
   const int j = lane & 15;   // channel cb + j
   const int kq = lane >> 4;  // edge of the round
-  // pass 1: grad_x, grad_W and the radial part of grad_vec; pass 2: the harmonics' part of grad_vec
-  const bool want_x = PASS == 1 && gx != nullptr, want_w = PASS == 1 && gW != nullptr;
+  const bool want_x = gx != nullptr, want_w = gW != nullptr;
   const bool want_v = gvec != nullptr;
   float* const xw = xch[wv];
-  // pass 1: the wave's grad_W sums, D_p[b][j] of path p in lane (j, rows 4 kq .. 4 kq + 3), b < 8 in lanes < 32
-  f4 gacc[PASS == 1 ? P : 1];
+  // the wave's grad_W sums, D_p[b][j] of path p in lane (j, rows 4 kq .. 4 kq + 3), b < 8 in lanes < 32
+  f4 gacc[P];
 #pragma unroll
-  for (int p = 0; p < (PASS == 1 ? P : 1); ++p) gacc[p] = f4{0.f, 0.f, 0.f, 0.f};
+  for (int p = 0; p < P; ++p) gacc[p] = f4{0.f, 0.f, 0.f, 0.f};
 
   // one round: lane group kq takes edge e (valid) or, if past the end, edge e_alt with no weight
   auto round = [&](int e, bool valid, int e_alt, int row) {
@@ -763,7 +764,7 @@ __global__ __launch_bounds__(kRbWaves * kWave) void conv_bwd_radial_kernel(
       nhi = wr[1];
     };
 
-    if constexpr (PASS == 1) {
+    {
       float aR = 0.0f;  // MFMA A operand: R_j of this lane's edge (rows j >= 8 are zero)
 #pragma unroll
       for (int b = 0; b < NB; ++b) aR = j == b ? R[b] : aR;
@@ -771,12 +772,13 @@ __global__ __launch_bounds__(kRbWaves * kWave) void conv_bwd_radial_kernel(
       // message_e = D^T P(w_e) D x, so grad_x = D^T P(w_e)^T D g and T_p = (D g) . P_p (D x); x and g are
       // rotated in, the sparse terms (by (path, mu3) runs) give both, the grad_x sums are rotated back.
       const So2Frame<L> fr(vx, vy, vz);
-      float xr[K], gr[K], mx[K];
+      float xr[K], gr[K], mx[K], ux[K];  // mx: v' = P_w^T g' (grad_x in the frame); ux: u' = P_w x'
 #pragma unroll
       for (int k = 0; k < K; ++k) {
         xr[k] = xv[k];
         gr[k] = gv[k];
         mx[k] = 0.0f;
+        ux[k] = 0.0f;
       }
       so2_rotate_in<L>(xr, fr);
       so2_rotate_in<L>(gr, fr);
@@ -801,6 +803,7 @@ __global__ __launch_bounds__(kRbWaves * kWave) void conv_bwd_radial_kernel(
           if constexpr (tm.p + 1 < P) {
             prefetch(tm.p + 1, wp, dr);
             settle(mx);  // likewise the grad_x sums: each path's terms are added before the next starts
+            settle(ux);
           }
           if constexpr (tm.l2 > 0) wp *= fr.keep;  // a zero vector drops the paths with l2 > 0
           tp = 0.0f;
@@ -810,6 +813,7 @@ __global__ __launch_bounds__(kRbWaves * kWave) void conv_bwd_radial_kernel(
         t = run_first ? tm.c * xr[tm.mu1] : fmaf(tm.c, xr[tm.mu1], t);
         if constexpr (run_last) {
           tp = fmaf(gr[tm.mu3], t, tp);
+          ux[tm.mu3] = fmaf(wp, t, ux[tm.mu3]);
           __builtin_amdgcn_sched_barrier(0);
         }
         if constexpr (p_last) {
@@ -821,6 +825,17 @@ __global__ __launch_bounds__(kRbWaves * kWave) void conv_bwd_radial_kernel(
           __builtin_amdgcn_sched_barrier(0);
         }
       });
+      // the harmonics' part of grad_vec, in the frame: the generators of rotations about its x and y
+      // axes act on the rotated features (so2_device.hpp, gen_form); with dL/dr, along vec / r below
+      float ga0 = 0.0f, ga1 = 0.0f, ga2 = 0.0f;
+      if (want_v && r > 0.0f) {
+        __builtin_amdgcn_sched_barrier(0);
+        const float gxe = -(gen_form<K, false>(mx, xr) + gen_form<K, false>(ux, gr));
+        __builtin_amdgcn_sched_barrier(0);
+        const float gye = gen_form<K, true>(mx, xr) + gen_form<K, true>(ux, gr);
+        __builtin_amdgcn_sched_barrier(0);
+        frame_gradient<L>(fr, gxe, gye, 1.0f / r, ga0, ga1, ga2);
+      }
       so2_rotate_out<L>(mx, fr);
       if (want_w) {
         // grad_W: per path, D[b][j] += sum_kq R_b(edge kq) T_p(edge kq, j) on the matrix cores, into the
@@ -847,45 +862,9 @@ __global__ __launch_bounds__(kRbWaves * kWave) void conv_bwd_radial_kernel(
       }
       if (want_v && r > 0.0f) {  // the radial part: dL/dr along vec / r
         const float qr = dr / r;
-        g0 = qr * vx;
-        g1 = qr * vy;
-        g2 = qr * vz;
-      }
-    } else {
-      // (path, mu2) walk: dL/dY, then through the harmonics' Jacobian
-      float dy[16];
-#pragma unroll
-      for (int k = 0; k < 16; ++k) dy[k] = 0.0f;
-      float wp = 0.0f, s2 = 0.0f;
-      static_for<0, T::NT>([&](auto jj) {
-        constexpr int q = decltype(jj)::value;
-        constexpr eqtp_gen::CgTerm tm = O2::term(q);
-        if constexpr (O2::path_first(q)) {
-          wp = 0.0f;
-#pragma unroll
-          for (int b = 0; b < 4; ++b) {
-            wp = fmaf(R[b], nlo[b], wp);
-            wp = fmaf(R[4 + b], nhi[b], wp);
-          }
-          if constexpr (tm.p + 1 < P) {
-            float none = 0.0f;
-            prefetch(tm.p + 1, wp, none);
-          }
-        }
-        const float cx = tm.c * xv[tm.mu1];
-        s2 = O2::first(q) ? cx * gv[tm.mu3] : fmaf(cx, gv[tm.mu3], s2);
-        if constexpr (O2::last(q)) {
-          dy[tm.mu2] = fmaf(wp, s2, dy[tm.mu2]);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      });
-      float Y2[16], Gm[16][3];
-      sh_grad_eval<L>(vx, vy, vz, Y2, Gm);
-#pragma unroll
-      for (int k = 0; k < K; ++k) {
-        g0 = fmaf(dy[k], Gm[k][0], g0);
-        g1 = fmaf(dy[k], Gm[k][1], g1);
-        g2 = fmaf(dy[k], Gm[k][2], g2);
+        g0 = fmaf(qr, vx, ga0);
+        g1 = fmaf(qr, vy, ga1);
+        g2 = fmaf(qr, vz, ga2);
       }
     }
     if (want_v) {  // the block's 16 channels, then one atomic per component
@@ -917,7 +896,7 @@ __global__ __launch_bounds__(kRbWaves * kWave) void conv_bwd_radial_kernel(
       for (int e0 = e_first; e0 < e_last; e0 += 4) round(e0 + kq, e0 + kq < e_last, e_first, 0);
     }
   }
-  if constexpr (PASS == 1) {
+  {
     if (want_w && lane < 32) {  // the wave's sums into the workgroup's slice (rows b = 4 kq + r < 8)
 #pragma unroll
       for (int p = 0; p < P; ++p)
@@ -928,7 +907,7 @@ __global__ __launch_bounds__(kRbWaves * kWave) void conv_bwd_radial_kernel(
     }
   }
   __syncthreads();
-  if (PASS == 1 && want_w) {
+  if (want_w) {
     for (int i = threadIdx.x; i < GWL; i += kRbWaves * kWave) {
       const int b = i / (P * 16), p = (i / 16) % P, jj = i % 16;
       unsafeAtomicAdd(gW + (size_t)b * P * C + (size_t)p * C + cb + jj, gwl[i]);
@@ -958,14 +937,8 @@ static hipError_t launch_bwd_radial_t(const BwdArgs& a) {
     hipLaunchKernelGGL(kernel, dim3(grid), dim3(kRbWaves * kWave), 0, a.stream, (int)a.N, (int)a.E, a.C, nwg,
                        a.row_ptr, a.vec, a.src, a.dst, a.x, a.w, a.gout, a.gx, a.gw, a.gvec, inv_rc);
   };
-  if (a.gx || a.gw || a.gvec) {
-    if (sorted) go(conv_bwd_radial_kernel<L, PS, true, 1>);
-    else go(conv_bwd_radial_kernel<L, PS, false, 1>);
-  }
-  if (a.gvec) {
-    if (sorted) go(conv_bwd_radial_kernel<L, PS, true, 2>);
-    else go(conv_bwd_radial_kernel<L, PS, false, 2>);
-  }
+  if (sorted) go(conv_bwd_radial_kernel<L, PS, true>);
+  else go(conv_bwd_radial_kernel<L, PS, false>);
   return hipGetLastError();
 }
 

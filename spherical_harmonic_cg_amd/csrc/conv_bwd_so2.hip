@@ -69,23 +69,6 @@ struct So2BwdCfg {
   static_assert(LDS <= kLds, "LDS budget");
 };
 
-// sum_r a[r] (L v)[r] for the generator L = L_x (LX) or L_y, rows of the table
-// walked with the entries as instruction immediates
-template <int K, bool LX>
-__device__ __forceinline__ float gen_form(const float (&a)[K], const float (&v)[K]) {
-  constexpr int NE = LX ? eqtp_gen::kLxRowStart[K] : eqtp_gen::kLyRowStart[K];
-  float acc = 0.0f, t = 0.0f;
-  static_for<0, NE>([&](auto ii) {
-    constexpr int i = decltype(ii)::value;
-    constexpr eqtp_gen::JEntry je = LX ? eqtp_gen::kLx[i] : eqtp_gen::kLy[i];
-    constexpr bool first = i == 0 || (LX ? eqtp_gen::kLx[i - 1].row : eqtp_gen::kLy[i - 1].row) != je.row;
-    constexpr bool last = i + 1 == NE || (LX ? eqtp_gen::kLx[i + 1].row : eqtp_gen::kLy[i + 1].row) != je.row;
-    t = first ? je.v * v[je.col] : fmaf(je.v, v[je.col], t);
-    if constexpr (last) acc = fmaf(a[je.row], t, acc);
-  });
-  return acc;
-}
-
 template <int K>
 __device__ __forceinline__ void load_vec(const float* __restrict__ p, float (&v)[K]) {
   if constexpr (K % 4 == 0) {
@@ -277,21 +260,14 @@ __global__ __launch_bounds__((kBwdSo2Threads<L, PS, C>)) __attribute__((amdgpu_w
           gxe += __shfl_xor(gxe, off);
           gye += __shfl_xor(gye, off);
         }
-        if (valid && cl == 0) {
-          // R_e^T (G_x, G_y, 0) / r, R_e = R_y(-theta) R_z(-phi); zero for a zero vector
+        if (valid && cl == 0) {  // zero for a zero vector
           const float r2 = vx * vx + vy * vy + vz * vz;
-          const float ir = r2 > 0.0f ? rsqrtf(r2) : 0.0f;
-          const float a = gxe * ir, b = gye * ir;
-          const float cph = f.cp[1 <= L ? 1 : 0], sph = f.sp[1 <= L ? 1 : 0];
-          const float cth = f.ct[1 <= L ? 1 : 0], sth = f.st[1 <= L ? 1 : 0];
+          float g0, g1, g2;
+          frame_gradient<L>(f, gxe, gye, r2 > 0.0f ? rsqrtf(r2) : 0.0f, g0, g1, g2);
           float* gv = gvec + 3 * (size_t)e;
-          if constexpr (L >= 1) {
-            gv[0] = fmaf(a * cth, cph, -b * sph);
-            gv[1] = fmaf(a * cth, sph, b * cph);
-            gv[2] = -a * sth;
-          } else {
-            gv[0] = gv[1] = gv[2] = 0.0f;
-          }
+          gv[0] = g0;
+          gv[1] = g1;
+          gv[2] = g2;
         }
       }
       if (gx != nullptr) {

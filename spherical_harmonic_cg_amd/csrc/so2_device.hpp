@@ -1,7 +1,7 @@
 // so2_device.hpp -- device pieces of the edge-aligned (SO(2)) form shared by
-// the forward kernels (conv_so2.hip) and the radial-weight gradients
-// (conv_bwd.hip): the sparse coupling tables, the constant rotation J and
-// the pair rotations Z, and the edge frame.  With R_e taking the edge
+// the forward kernels (conv_so2.hip) and the gradients (conv_bwd_so2.hip,
+// conv_bwd.hip): the sparse coupling tables, the constant rotation J and the
+// pair rotations Z, the edge frame, and the rotation generators.  With R_e taking the edge
 // direction to the z axis, D(R_e) = J^T Z(-theta) J Z(-phi) and
 // D(R_e)^T = Z(phi) J^T Z(theta) J (E2Former-V2 page, section 2.1, and
 // conv_so2.hip).
@@ -144,6 +144,42 @@ __device__ __forceinline__ void so2_rotate_out(float (&v)[K], const So2Frame<L>&
   apply_z<L>(v, f.ct, f.st, 1.0f);
   apply_j<K, true>(v);
   apply_z<L>(v, f.cp, f.sp, 1.0f);
+}
+
+// sum_r a[r] (L v)[r] for the generator of rotations L = L_x (LX) or L_y
+// (L_a = d/de D(R_a(e)) at e = 0), rows of the table walked with the entries
+// as instruction immediates.  With x', g' the features in the edge frame,
+// u' = P_w x' and v' = P_w^T g', the loss's tangential derivatives at the
+// frame's pole are G_x = -(v' . L_y x' + u' . L_y g') and
+// G_y = v' . L_x x' + u' . L_x g' (the coupling's invariance moves the
+// derivative of the harmonics onto x' and g'; conv_bwd_so2.hip)
+template <int K, bool LX>
+__device__ __forceinline__ float gen_form(const float (&a)[K], const float (&v)[K]) {
+  constexpr int NE = LX ? eqtp_gen::kLxRowStart[K] : eqtp_gen::kLyRowStart[K];
+  float acc = 0.0f, t = 0.0f;
+  static_for<0, NE>([&](auto ii) {
+    constexpr int i = decltype(ii)::value;
+    constexpr eqtp_gen::JEntry je = LX ? eqtp_gen::kLx[i] : eqtp_gen::kLy[i];
+    constexpr bool first = i == 0 || (LX ? eqtp_gen::kLx[i - 1].row : eqtp_gen::kLy[i - 1].row) != je.row;
+    constexpr bool last = i + 1 == NE || (LX ? eqtp_gen::kLx[i + 1].row : eqtp_gen::kLy[i + 1].row) != je.row;
+    t = first ? je.v * v[je.col] : fmaf(je.v, v[je.col], t);
+    if constexpr (last) acc = fmaf(a[je.row], t, acc);
+  });
+  return acc;
+}
+
+// dL/dvec = R_e^T (G_x, G_y, 0) / |vec| for the edge frame f (R_e = R_y(-theta) R_z(-phi))
+template <int L>
+__device__ __forceinline__ void frame_gradient(const So2Frame<L>& f, float gxe, float gye, float inv_r, float& g0,
+                                               float& g1, float& g2) {
+  if constexpr (L >= 1) {
+    const float a = gxe * inv_r, b = gye * inv_r;
+    g0 = fmaf(a * f.ct[1], f.cp[1], -b * f.sp[1]);
+    g1 = fmaf(a * f.ct[1], f.sp[1], b * f.cp[1]);
+    g2 = -a * f.st[1];
+  } else {
+    g0 = g1 = g2 = 0.0f;
+  }
 }
 
 }  // namespace eqtp
