@@ -8,8 +8,9 @@ backward computes
     grouped by source node that eqtp_sort_edges builds on the GPU (the adjoint
     of the node-factored forward, on the matrix cores), and
   * grad_vec (for forces) with eqtp_conv_backward, edge by edge.
-``grad_x_mode="edge"`` takes all three from eqtp_conv_backward instead.  All
-arithmetic runs in the HIP library; this module only marshals arguments.
+``grad_x_mode="edge"`` takes all three from eqtp_conv_backward instead, as
+does lmax above 3 (the edge-aligned gradients).  All arithmetic runs in the
+HIP library; this module only marshals arguments.
 """
 from __future__ import annotations
 
@@ -57,7 +58,7 @@ class EquivariantConvFunction(torch.autograd.Function):
                                                     path_set=ctx.path_set, need_x=need_x, need_w=need_w,
                                                     need_vec=need_vec, weight_mode=ctx.weight_mode,
                                                     r_cut=ctx.r_cut)
-        elif ctx.grad_x_mode == "edge":
+        elif ctx.grad_x_mode == "edge" or ctx.lmax > 3:
             if need_vec or need_x or need_w:
                 gx, gw, gv = _eq.eqtp_conv_backward(vec, src, x, weights, g, ctx.lmax, row_ptr=row_ptr, dst=dst,
                                                     path_set=ctx.path_set, need_x=need_x, need_w=need_w,

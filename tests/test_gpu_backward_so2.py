@@ -147,3 +147,25 @@ def test_so2_backward_lmax6_graph_full():
     inv = np.empty_like(perm)
     inv[perm] = np.arange(wl.E)
     _compare((gx, gw, _np(gv)[inv]), ref, (True, True, True), "so2 bwd L6 graph unsorted")
+
+
+@pytest.mark.parametrize("L,csr", [(4, True), (6, False)])
+def test_so2_autograd_high_lmax(L, csr):
+    """equivariant_conv above lmax 3: the edge-aligned forward and gradients through torch.autograd
+    (the default source-grouped mode falls back to eqtp_conv_backward there)."""
+    eq = _eq()
+    from spherical_harmonic_cg_amd.autograd import equivariant_conv
+
+    wl = _graph(L, 0, 32, 2500 + L)
+    gout = _gout(wl.N, 32, L, 81)
+    kw = dict(row_ptr=_t(wl.row_ptr)) if csr else dict(dst=_t(wl.dst))
+    vec = _t(wl.vec).requires_grad_(True)
+    x = _t(wl.x).requires_grad_(True)
+    w = _t(wl.w).requires_grad_(True)
+    _say("so2 autograd L=%d csr=%s" % (L, csr))
+    out = equivariant_conv(vec, x, w, _t(wl.src), L, **kw)
+    _assert_close(_np(out.detach()), oracle.conv(wl.N, wl.vec, wl.src, wl.dst, wl.x, wl.w, L), TOL,
+                  "so2 autograd forward")
+    (out * _t(gout)).sum().backward()
+    ref = oracle.conv_backward(wl.N, wl.vec, wl.src, wl.dst, wl.x, wl.w, gout, L, 0)
+    _compare((x.grad, w.grad, vec.grad), ref, (True, True, True), "so2 autograd L%d" % L)
