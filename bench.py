@@ -410,22 +410,43 @@ def main():
                 eq.eqtp_conv_backward(bvec, bsrc, x, w, gout, wl.lmax, path_set=wl.path_set, weight_mode=1,
                                       r_cut=wl.r_cut, **bkw)
 
-            for _ in range(3):
-                bwd_rad()
-            torch.cuda.synchronize()
-            kb = max(5, K // 4)
-            b0 = torch.cuda.Event(enable_timing=True)
-            b1 = torch.cuda.Event(enable_timing=True)
-            b0.record(stream)
-            for _ in range(kb):
-                bwd_rad()
-            b1.record(stream)
-            torch.cuda.synchronize()
-            rms = b0.elapsed_time(b1) / kb
-            backward = {"ms": round(rms, 5), "edges_per_s": round(wl.E / (rms * 1e-3), 1), "launches": kb,
-                        "what": "grad_x, grad_W [8, P*C] and grad_vec of the radial-weight conv "
-                                "(eqtp_conv_backward with EQTP_W_RADIAL: zero fills + one kernel)"}
-            log("backward (radial weights): %.4f ms (%.3e edges/s)" % (rms, wl.E / (rms * 1e-3)))
+            # grouped by source on the GPU, then one pass for all three (what the autograd wrapper runs)
+            E_ = wl.E
+            rows = torch.empty(E_, dtype=torch.int32, device=dev) if "row_ptr" in bkw else None
+            grp = (torch.empty(wl.N + 1, dtype=torch.int32, device=dev), torch.empty(E_, dtype=torch.int32, device=dev),
+                   torch.empty((E_, 3), dtype=torch.float32, device=dev), torch.empty(E_, dtype=torch.int32, device=dev))
+
+            def bwd_rad_src():
+                d_ = eq.eqtp_edge_rows(bkw["row_ptr"], E_, out=rows) if "row_ptr" in bkw else bkw["dst"]
+                eq.eqtp_sort_edges(bsrc, wl.N, vec=bvec, src=d_, out=grp)
+                eq.eqtp_conv_backward_by_source(grp[2], grp[3], grp[0], x, w, gout, wl.lmax, path_set=wl.path_set,
+                                                need_vec=True, perm=grp[1], weight_mode=1, r_cut=wl.r_cut)
+
+            def timed_r(fn):
+                for _ in range(3):
+                    fn()
+                torch.cuda.synchronize()
+                kb = max(5, K // 4)
+                b0 = torch.cuda.Event(enable_timing=True)
+                b1 = torch.cuda.Event(enable_timing=True)
+                b0.record(stream)
+                for _ in range(kb):
+                    fn()
+                b1.record(stream)
+                torch.cuda.synchronize()
+                return b0.elapsed_time(b1) / kb, kb
+
+            rms, kb = timed_r(bwd_rad)
+            sms, _ = timed_r(bwd_rad_src)
+            backward = {"ms": round(sms, 5), "edges_per_s": round(wl.E / (sms * 1e-3), 1), "launches": kb,
+                        "what": "grad_x, grad_W [8, P*C] and grad_vec of the radial-weight conv: source grouping "
+                                "on the GPU (eqtp_edge_rows + eqtp_sort_edges), then eqtp_conv_backward_by_source "
+                                "with EQTP_W_RADIAL (one pass, grad_x without atomics)",
+                        "edge_path_ms": round(rms, 5),
+                        "edge_path_what": "eqtp_conv_backward with EQTP_W_RADIAL on the edges as given (zero fills "
+                                          "+ one kernel, grad_x by fp32 atomics)"}
+            log("backward (radial weights): by source %.4f ms (%.3e edges/s); edge path %.4f ms" % (
+                sms, wl.E / (sms * 1e-3), rms))
         else:
             gout = torch.randn(out.shape, dtype=torch.float32, device=dev)
             bkw = dict(dst=dst) if args.unsorted else dict(row_ptr=row_ptr)
@@ -471,12 +492,23 @@ def main():
                 return b0.elapsed_time(b1) / kb, kb
 
             if wl.lmax > 3:
+                def bwd_so2_src():
+                    d_ = eq.eqtp_edge_rows(bkw["row_ptr"], E_, out=rows) if "row_ptr" in bkw else bkw["dst"]
+                    eq.eqtp_sort_edges(bsrc, wl.N, vec=bvec, src=d_, out=grp)
+                    eq.eqtp_conv_backward_by_source(grp[2], grp[3], grp[0], x, w, gout, wl.lmax,
+                                                    path_set=wl.path_set, need_vec=True, perm=grp[1])
+
                 oms, kb = timed(bwd_so2)
-                backward = {"ms": round(oms, 5), "edges_per_s": round(wl.E / (oms * 1e-3), 1), "launches": kb,
-                            "what": "grad_x, grad_w and grad_vec of the conv in the edge-aligned form "
-                                    "(eqtp_conv_backward above lmax 3: zero fills + one kernel, fp32 atomics "
-                                    "for grad_x)"}
-                log("backward (edge-aligned form): %.4f ms (%.3e edges/s)" % (oms, wl.E / (oms * 1e-3)))
+                sms, _ = timed(bwd_so2_src)
+                backward = {"ms": round(sms, 5), "edges_per_s": round(wl.E / (sms * 1e-3), 1), "launches": kb,
+                            "what": "grad_x, grad_w and grad_vec of the conv in the edge-aligned form: source "
+                                    "grouping on the GPU (eqtp_edge_rows + eqtp_sort_edges), then "
+                                    "eqtp_conv_backward_by_source (one pass, grad_x without atomics)",
+                            "edge_path_ms": round(oms, 5),
+                            "edge_path_what": "eqtp_conv_backward on the edges as given (zero fills + one kernel, "
+                                              "fp32 atomics for grad_x)"}
+                log("backward (edge-aligned form): by source %.4f ms (%.3e edges/s); edge path %.4f ms" % (
+                    sms, wl.E / (sms * 1e-3), oms))
             else:
                 bms, kb = timed(bwd)
                 sms, _ = timed(bwd_src)

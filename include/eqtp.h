@@ -283,31 +283,43 @@ int eqtp_conv_backward(const eqtp_conv_desc* d, int64_t N, int64_t E, const floa
                        const float* grad_out, float* grad_x, float* grad_w, float* grad_vec, void* stream);
 
 /*
- * grad_x and grad_w as for eqtp_conv_backward (same formulas, fixed weights),
- * computed from a copy of the edges grouped by SOURCE node, on the matrix
- * cores and without atomics on grad_x:
- *   H_s[c, m3, m2] = sum_{e: src_e = s} grad_out[dst_e, c, m3] Y_m2(vec_e),
- *   grad_x[s, c, m1] = sum_p w[p, c] sum_{m2, m3} C^p[m1, m2, m3] H_s[c, m3, m2],
- *   grad_w[p, c] = sum_s sum_{m1} x[s, c, m1] sum_{m2, m3} C^p[m1, m2, m3] H_s[c, m3, m2].
+ * The gradients of eqtp_conv_backward (same formulas) from a copy of the edges
+ * grouped by SOURCE node, so that grad_x[s] is summed over the source's edges
+ * in one place and written once: no atomics on grad_x, deterministic.
  *   src_ptr [N+1] int32: CSR over source nodes (src_ptr[N] = E);
  *   vec_s   [E, 3] fp32 and dst_s [E] int32: each edge's vector (pointing
  *           from its source to its destination, as in the forward) and its
- *           destination, in source-grouped order.
+ *           destination, in source-grouped order;
+ *   perm    [E] int32: perm[i] = the index, in the caller's edge order, of
+ *           grouped edge i (needed with grad_vec only, else may be NULL).
  *   eqtp_sort_edges(N, E, src, vec, dst, src_ptr, perm, vec_s, dst_s, ...)
- *   produces these from the forward's arrays (eqtp_edge_rows gives dst from
+ *   produces all four from the forward's arrays (eqtp_edge_rows gives dst from
  *   a dst-sorted CSR).
- *   x [N, C, K] fp32 16-byte aligned (needed for grad_w only, else may be NULL);
- *   grad_out [N, C, K] fp32 16-byte aligned; weights [P, C] fp32.
- *   grad_x [N, C, K] fp32 16-byte aligned, fully overwritten (zeros for nodes
- *   that are no edge's source), deterministic; or NULL.
- *   grad_w [P, C] fp32, a sum of fp32 atomics; or NULL.  Not both NULL.
- * d: lmax, C, path_set, weight_mode (must be EQTP_W_FIXED), x_dtype (must be
- * EQTP_F32); edge_order and algo are ignored.  Errors as for
- * eqtp_conv_backward.
+ *   x [N, C, K] fp32 16-byte aligned (needed for grad_w and grad_vec, and
+ *   always with radial weights or the edge-aligned form; else may be NULL);
+ *   grad_out [N, C, K] fp32 16-byte aligned; weights [P, C] fp32 (fixed) or
+ *   [8, P*C] (radial).
+ *   grad_x   [N, C, K] fp32 16-byte aligned, fully overwritten (zeros for nodes
+ *            that are no edge's source), deterministic; or NULL.
+ *   grad_w   [P, C] or [8, P*C] fp32, a sum of fp32 atomics; or NULL.
+ *   grad_vec [E, 3] fp32 in the caller's edge order (entry perm[i] for grouped
+ *            edge i), fully overwritten; or NULL.  Not all three NULL.
+ * How: fixed weights at lmax <= 3 (the default): grad_x and grad_w by the
+ * adjoint of the node-factored forward on the matrix cores,
+ *   H_s[c, m3, m2] = sum_{e: src_e = s} grad_out[dst_e, c, m3] Y_m2(vec_e),
+ *   grad_x[s, c, m1] = sum_p w[p, c] sum_{m2, m3} C^p[m1, m2, m3] H_s[c, m3, m2],
+ *   grad_w[p, c] = sum_s sum_{m1} x[s, c, m1] sum_{m2, m3} C^p[m1, m2, m3] H_s[c, m3, m2],
+ * and grad_vec by a walk in the edge frame; fixed weights at lmax 4..6 (or
+ * d->algo = EQTP_ALGO_EDGE_SO2): all three by one walk in the edge frame (C =
+ * 128 only up to lmax 4); radial weights (lmax 0..3, C a multiple of 16,
+ * n_basis 8, r_cut > 0): all three by one walk in the edge frame.
+ * d: lmax, C, path_set, weight_mode, r_cut, n_basis, algo, x_dtype (must be
+ * EQTP_F32); edge_order is ignored.  Errors as for eqtp_conv_backward.
  */
 int eqtp_conv_backward_by_source(const eqtp_conv_desc* d, int64_t N, int64_t E, const float* vec_s,
                                  const int32_t* dst_s, const int32_t* src_ptr, const float* x, const float* weights,
-                                 const float* grad_out, float* grad_x, float* grad_w, void* stream);
+                                 const float* grad_out, float* grad_x, float* grad_w, const int32_t* perm,
+                                 float* grad_vec, void* stream);
 
 /*
  * rows[e] = the row n with row_ptr[n] <= e < row_ptr[n+1] (the destination of

@@ -425,26 +425,41 @@ int eqtp_conv_backward(const eqtp_conv_desc* d, int64_t N, int64_t E, const floa
 
 int eqtp_conv_backward_by_source(const eqtp_conv_desc* d, int64_t N, int64_t E, const float* vec_s,
                                  const int32_t* dst_s, const int32_t* src_ptr, const float* x, const float* weights,
-                                 const float* grad_out, float* grad_x, float* grad_w, void* stream) {
+                                 const float* grad_out, float* grad_x, float* grad_w, const int32_t* perm,
+                                 float* grad_vec, void* stream) {
   if (!desc_ok(d)) return EQTP_EINVAL;
   if (desc_x_dtype(d) != EQTP_F32) return desc_x_dtype(d) == EQTP_BF16 ? EQTP_EUNSUPPORTED : EQTP_EINVAL;
   if (d->lmax < 0) return EQTP_EINVAL;
-  if (d->lmax > 3) return EQTP_EUNSUPPORTED;
+  if (d->lmax > eqtp::kSo2MaxL) return EQTP_EUNSUPPORTED;
   if (d->path_set != EQTP_PATHS_PARITY && d->path_set != EQTP_PATHS_SO3) return EQTP_EINVAL;
   if (d->weight_mode != EQTP_W_FIXED && d->weight_mode != EQTP_W_RADIAL) return EQTP_EINVAL;
+  if (d->algo != EQTP_ALGO_AUTO && d->algo != EQTP_ALGO_NODE_MFMA && d->algo != EQTP_ALGO_EDGE_VALU &&
+      d->algo != EQTP_ALGO_EDGE_SO2)
+    return EQTP_EINVAL;
   if (d->C <= 0) return EQTP_EINVAL;
   if (!valid_c(d->C)) return EQTP_EUNSUPPORTED;
-  if (d->weight_mode == EQTP_W_RADIAL) return EQTP_EUNSUPPORTED;
+  const bool radial = d->weight_mode == EQTP_W_RADIAL;
+  // fixed weights: the node-factored adjoint (lmax <= 3) unless the edge-aligned form is asked for or needed
+  const bool use_so2 = !radial && (d->lmax > 3 || d->algo == EQTP_ALGO_EDGE_SO2);
+  if (d->lmax > 3 && !use_so2) return EQTP_EUNSUPPORTED;
+  if (!radial && d->C == 128 && d->lmax > eqtp::kSo2MaxLC128 && (use_so2 || grad_vec)) return EQTP_EUNSUPPORTED;
+  if (radial) {
+    if (!(d->r_cut > 0.0f)) return EQTP_EINVAL;
+    if (d->n_basis != 8 || d->C % 16 != 0) return EQTP_EUNSUPPORTED;
+  }
   if (N < 0 || E < 0 || N > kMaxIndex || E > kMaxIndex) return EQTP_EINVAL;
   if (E > 0 && N == 0) return EQTP_EINVAL;
-  if (!grad_x && !grad_w) return EQTP_EINVAL;
-  if ((grad_x && !aligned16(grad_x)) || (grad_w && !aligned4(grad_w))) return EQTP_EINVAL;
+  if (!grad_x && !grad_w && !grad_vec) return EQTP_EINVAL;
+  if ((grad_x && !aligned16(grad_x)) || (grad_w && !aligned4(grad_w)) || (grad_vec && !aligned4(grad_vec)))
+    return EQTP_EINVAL;
   if (!weights || !aligned4(weights)) return EQTP_EINVAL;
+  const bool edge_walk = radial || use_so2 || grad_vec;  // a walk over the edges reads x for every output
   if (N > 0) {
     if (!grad_out || !aligned16(grad_out) || !src_ptr || !aligned4(src_ptr)) return EQTP_EINVAL;
-    if (grad_w && (!x || !aligned16(x))) return EQTP_EINVAL;
+    if ((grad_w || edge_walk) && (!x || !aligned16(x))) return EQTP_EINVAL;
   }
   if (E > 0 && (!vec_s || !dst_s || !aligned4(vec_s) || !aligned4(dst_s))) return EQTP_EINVAL;
+  if (E > 0 && grad_vec && (!perm || !aligned4(perm))) return EQTP_EINVAL;
   eqtp::BwdArgs a;
   a.N = N;
   a.E = E;
@@ -460,9 +475,26 @@ int eqtp_conv_backward_by_source(const eqtp_conv_desc* d, int64_t N, int64_t E, 
   a.gout = grad_out;
   a.gx = grad_x;
   a.gw = grad_w;
-  a.gvec = nullptr;
+  a.gvec = grad_vec;
+  a.r_cut = d->r_cut;
+  a.by_src = true;
+  a.perm = perm;
   a.stream = (hipStream_t)stream;
-  return status_of(eqtp::launch_conv_backward_by_source(a));
+  if (radial) return status_of(eqtp::launch_conv_backward_radial(a));
+  if (use_so2) return status_of(eqtp::launch_conv_backward_so2(a));
+  // lmax <= 3, fixed weights: grad_x and grad_w by the node-factored adjoint, grad_vec by a walk in the edge
+  // frame over the same grouped edges
+  if (grad_x || grad_w) {
+    eqtp::BwdArgs b = a;
+    b.gvec = nullptr;
+    b.by_src = false;
+    b.perm = nullptr;
+    const int st = status_of(eqtp::launch_conv_backward_by_source(b));
+    if (st != EQTP_OK || !grad_vec) return st;
+  }
+  a.gx = nullptr;
+  a.gw = nullptr;
+  return status_of(eqtp::launch_conv_backward_so2(a));
 }
 
 int eqtp_edge_rows(int64_t N, int64_t E, const int32_t* row_ptr, int32_t* rows, void* stream) {

@@ -682,12 +682,15 @@ constexpr int kRbNB = 8;     // radial functions
 constexpr int kRbWaves = 4;  // waves per workgroup
 constexpr int kRbChunk = 64; // edges per run, unsorted edges
 
-template <int L, int PS, bool SORTED>
+// MODE 0: edges in any order (runs of kRbChunk; src, dst per edge); 1: dst-sorted (row_ptr over
+// destinations, src per edge); 2: grouped by source (row_ptr over sources, dst per edge, perm[i] = the
+// input index of grouped edge i for grad_vec): grad_x is summed per source row in LDS and written once.
+template <int L, int PS, int MODE>
 __global__ __launch_bounds__(kRbWaves * kWave) void conv_bwd_radial_kernel(
     int N, int E, int C, int nwg, const int* __restrict__ row_ptr, const float* __restrict__ vec,
-    const int* __restrict__ src, const int* __restrict__ dst, const float* __restrict__ x,
-    const float* __restrict__ W, const float* __restrict__ gout, float* __restrict__ gx, float* __restrict__ gW,
-    float* __restrict__ gvec, float inv_rc) {
+    const int* __restrict__ src, const int* __restrict__ dst, const int* __restrict__ perm,
+    const float* __restrict__ x, const float* __restrict__ W, const float* __restrict__ gout,
+    float* __restrict__ gx, float* __restrict__ gW, float* __restrict__ gvec, float inv_rc) {
   using T = Tables<L, PS>;
   using S = So2Tables<L, PS>;
   constexpr int K = num_comp(L);
@@ -702,6 +705,8 @@ __global__ __launch_bounds__(kRbWaves * kWave) void conv_bwd_radial_kernel(
   constexpr int XCH = 64 * P > 4 * XB ? 64 * P : 4 * XB;
   __shared__ __attribute__((aligned(16))) float xch[kRbWaves][XCH];
   __shared__ int xsrc[kRbWaves][4];
+  // grouped by source: the row's grad_x sums, lane (kq, j) owning floats (kq * 16 + j) * K .. + K - 1
+  __shared__ __attribute__((aligned(16))) float gxa[kRbWaves][MODE == 2 ? 4 * XB : 1];
   const int cb = (int)(blockIdx.x / nwg) * 16;
   const int wg = (int)(blockIdx.x % nwg);
   for (int i = threadIdx.x; i < P * 16 * NB; i += kRbWaves * kWave) {
@@ -726,14 +731,15 @@ __global__ __launch_bounds__(kRbWaves * kWave) void conv_bwd_radial_kernel(
   auto round = [&](int e, bool valid, int e_alt, int row) {
     const int ec = valid ? e : e_alt;
     const float vx = vec[3 * (size_t)ec], vy = vec[3 * (size_t)ec + 1], vz = vec[3 * (size_t)ec + 2];
-    const int s = clamp_index(src[ec], N);
+    // the row's node (dst-sorted: the destination, grouped by source: the source) is read again each
+    // round from the cache rather than held in registers across the row
+    int s = MODE == 2 ? row : clamp_index(src[ec], N);
+    if constexpr (MODE == 2) asm volatile("" : "+v"(s));  // a new value each round: not hoisted out of the row
     float xv[K], gv[K];
 #pragma unroll
     for (int k = 0; k < K; ++k) xv[k] = x[((size_t)s * C + cb + j) * K + k];
-    // the destination's grad_out (sorted edges: the row's, read again each round from the cache
-    // rather than held in registers across the row)
-    int d = SORTED ? row : clamp_index(dst[ec], N);
-    if constexpr (SORTED) asm volatile("" : "+v"(d));  // a new value each round: not hoisted out of the row
+    int d = MODE == 1 ? row : clamp_index(dst[ec], N);
+    if constexpr (MODE == 1) asm volatile("" : "+v"(d));
 #pragma unroll
     for (int k = 0; k < K; ++k) gv[k] = gout[((size_t)d * C + cb + j) * K + k];
     const float r = sqrtf(vx * vx + vy * vy + vz * vz);
@@ -847,7 +853,11 @@ __global__ __launch_bounds__(kRbWaves * kWave) void conv_bwd_radial_kernel(
         });
         wave_lds_sync();
       }
-      if (want_x) {
+      if (MODE == 2 && want_x) {  // grouped by source: into the row's sums (lane-private slots)
+        float* const ga = gxa[wv] + (kq * 16 + j) * K;
+#pragma unroll
+        for (int k = 0; k < K; ++k) ga[k] += mx[k];
+      } else if (want_x) {
 #pragma unroll
         for (int k = 0; k < K; ++k) xw[(kq * 16 + j) * K + k] = mx[k];
         if (j == 0) xsrc[wv][kq] = valid ? s : -1;
@@ -875,18 +885,39 @@ __global__ __launch_bounds__(kRbWaves * kWave) void conv_bwd_radial_kernel(
         g2 += __shfl_xor(g2, off);
       }
       if (j == 0 && valid) {
-        unsafeAtomicAdd(gvec + 3 * (size_t)e, g0);
-        unsafeAtomicAdd(gvec + 3 * (size_t)e + 1, g1);
-        unsafeAtomicAdd(gvec + 3 * (size_t)e + 2, g2);
+        const size_t ge = MODE == 2 ? (size_t)clamp_index(perm[e], E) : (size_t)e;
+        unsafeAtomicAdd(gvec + 3 * ge, g0);
+        unsafeAtomicAdd(gvec + 3 * ge + 1, g1);
+        unsafeAtomicAdd(gvec + 3 * ge + 2, g2);
       }
     }
   };
 
-  if constexpr (SORTED) {
+  if constexpr (MODE == 1) {
     for (int row = wg * kRbWaves + wv; row < N; row += nwg * kRbWaves) {
       const int e_beg = min(max(row_ptr[row], 0), E);
       const int e_end = min(max(row_ptr[row + 1], e_beg), E);
       for (int e0 = e_beg; e0 < e_end; e0 += 4) round(e0 + kq, e0 + kq < e_end, e_beg, row);
+    }
+  } else if constexpr (MODE == 2) {
+    float* const ga = gxa[wv];
+    for (int row = wg * kRbWaves + wv; row < N; row += nwg * kRbWaves) {
+      const int e_beg = min(max(row_ptr[row], 0), E);
+      const int e_end = min(max(row_ptr[row + 1], e_beg), E);
+      if (want_x) {
+#pragma unroll
+        for (int k = 0; k < K; ++k) ga[(kq * 16 + j) * K + k] = 0.0f;
+      }
+      for (int e0 = e_beg; e0 < e_end; e0 += 4) round(e0 + kq, e0 + kq < e_end, e_beg, row);
+      if (want_x) {  // the four edge groups' sums, one coalesced store of the row's block (zeros if no edges)
+        wave_lds_sync();
+#pragma unroll
+        for (int t = 0; t < (XB + kWave - 1) / kWave; ++t) {
+          const int f = kWave * t + lane;  // float f of the block's 16 x K
+          if (f < XB) gx[((size_t)row * C + cb) * K + f] = ga[f] + ga[XB + f] + ga[2 * XB + f] + ga[3 * XB + f];
+        }
+        wave_lds_sync();
+      }
     }
   } else {
     const int nchunk = (E + kRbChunk - 1) / kRbChunk;
@@ -920,9 +951,14 @@ static hipError_t launch_bwd_radial_t(const BwdArgs& a) {
   constexpr int K = num_comp(L);
   constexpr int P = Tables<L, PS>::P;
   hipError_t err;
-  if (a.gx && a.N > 0 && (err = launch_fill_zero(a.gx, a.N * a.C * K, a.stream)) != hipSuccess) return err;
+  // grouped by source every row's grad_x block is written once; else it is a sum of atomics
+  if (a.gx && a.N > 0 && !a.by_src && (err = launch_fill_zero(a.gx, a.N * a.C * K, a.stream)) != hipSuccess)
+    return err;
   if (a.gw && (err = launch_fill_zero(a.gw, (int64_t)kRbNB * P * a.C, a.stream)) != hipSuccess) return err;
   if (a.gvec && a.E > 0 && (err = launch_fill_zero(a.gvec, a.E * 3, a.stream)) != hipSuccess) return err;
+  if (a.N > 0 && a.E == 0 && a.by_src && a.gx &&
+      (err = launch_fill_zero(a.gx, a.N * a.C * K, a.stream)) != hipSuccess)
+    return err;
   if (a.N == 0 || a.E == 0) return hipSuccess;
   const bool sorted = a.row_ptr != nullptr;
   const int nblk = a.C / 16;
@@ -935,10 +971,11 @@ static hipError_t launch_bwd_radial_t(const BwdArgs& a) {
   const float inv_rc = 1.0f / a.r_cut;
   auto go = [&](auto kernel) {
     hipLaunchKernelGGL(kernel, dim3(grid), dim3(kRbWaves * kWave), 0, a.stream, (int)a.N, (int)a.E, a.C, nwg,
-                       a.row_ptr, a.vec, a.src, a.dst, a.x, a.w, a.gout, a.gx, a.gw, a.gvec, inv_rc);
+                       a.row_ptr, a.vec, a.src, a.dst, a.perm, a.x, a.w, a.gout, a.gx, a.gw, a.gvec, inv_rc);
   };
-  if (sorted) go(conv_bwd_radial_kernel<L, PS, true>);
-  else go(conv_bwd_radial_kernel<L, PS, false>);
+  if (a.by_src) go(conv_bwd_radial_kernel<L, PS, 2>);
+  else if (sorted) go(conv_bwd_radial_kernel<L, PS, 1>);
+  else go(conv_bwd_radial_kernel<L, PS, 0>);
   return hipGetLastError();
 }
 

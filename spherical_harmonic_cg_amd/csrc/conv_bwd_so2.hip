@@ -28,7 +28,8 @@
 //
 // Lane mapping as in the forward: lane = channel (C <= 64: 64/C edges per
 // wave round; C = 128: two channels per lane).  Persistent waves take
-// destination rows (dst-sorted edges) or runs of edges (any order, dst[]).
+// destination rows (dst-sorted edges), runs of edges (any order, dst[]) or
+// source rows (edges grouped by source: grad_x summed per row, no atomics).
 // grad_x: fp32 atomics after an LDS exchange (each instruction adds 64
 // consecutive floats of one source's row); grad_w: per-lane sums in
 // registers over all of the wave's edges, then LDS atomics into the
@@ -94,7 +95,10 @@ constexpr int next_path_after(int i) {
   return -1;
 }
 
-// ntasks: rows (row_ptr != nullptr) or runs of EPW edges
+// mode 0: edges in any order (runs of EPW edges; src, dst per edge); 1: dst-sorted (row_ptr over
+// destinations, src per edge); 2: grouped by source (row_ptr over sources, dst per edge, perm[i] = the
+// input index of grouped edge i for grad_vec): grad_x is summed per source row in the wave's LDS and
+// written once, no atomics.  ntasks: rows (modes 1, 2) or runs.
 template <int L, int PS, int C>
 constexpr int kBwdSo2Threads = So2BwdCfg<L, PS, C>::THREADS;
 template <int L, int PS, int C>  // waves per SIMD that the LDS allows (the register budget follows)
@@ -103,10 +107,10 @@ constexpr int kBwdSo2Occ = So2BwdCfg<L, PS, C>::WAVES * So2BwdCfg<L, PS, C>::PER
 template <int L, int PS, int C>
 __global__ __launch_bounds__((kBwdSo2Threads<L, PS, C>)) __attribute__((amdgpu_waves_per_eu(
     kBwdSo2Occ<L, PS, C>))) void conv_bwd_so2_kernel(
-    int N, int E, long long ntasks, const int* __restrict__ row_ptr, const float* __restrict__ vec,
-    const int* __restrict__ src, const int* __restrict__ dst, const float* __restrict__ x,
-    const float* __restrict__ w, const float* __restrict__ gout, float* __restrict__ gx, float* __restrict__ gw,
-    float* __restrict__ gvec) {
+    int N, int E, long long ntasks, int mode, const int* __restrict__ row_ptr, const float* __restrict__ vec,
+    const int* __restrict__ src, const int* __restrict__ dst, const int* __restrict__ perm,
+    const float* __restrict__ x, const float* __restrict__ w, const float* __restrict__ gout, float* __restrict__ gx,
+    float* __restrict__ gw, float* __restrict__ gvec) {
   using Cfg = So2BwdCfg<L, PS, C>;
   using T = So2Tables<L, PS>;
   constexpr int K = num_comp(L);
@@ -125,7 +129,7 @@ __global__ __launch_bounds__((kBwdSo2Threads<L, PS, C>)) __attribute__((amdgpu_w
   const int wv = threadIdx.x >> 6;
   const int g = lane / Cfg::CL;
   const int cl = lane % Cfg::CL;
-  const bool sorted = row_ptr != nullptr;
+  const bool rows = mode != 0, by_src = mode == 2;
   float* const xw = xch[wv];
   // path weight of channel c (LDS copy or through the caches)
   auto wld = [&](int p, int c) -> float {
@@ -145,12 +149,17 @@ __global__ __launch_bounds__((kBwdSo2Threads<L, PS, C>)) __attribute__((amdgpu_w
 
   for (long long task = (long long)blockIdx.x * Cfg::WAVES + wv; task < ntasks;
        task += (long long)gridDim.x * Cfg::WAVES) {
-    int e_beg = 0, e_end = 0, d_row = 0;
-    if (sorted) {
-      d_row = (int)task;
+    int e_beg = 0, e_end = 0, row = 0;
+    if (rows) {
+      row = (int)task;
       if (E > 0) {
-        e_beg = min(max(row_ptr[d_row], 0), E);
-        e_end = min(max(row_ptr[d_row + 1], e_beg), E);
+        e_beg = min(max(row_ptr[row], 0), E);
+        e_end = min(max(row_ptr[row + 1], e_beg), E);
+      }
+      if (by_src && gx != nullptr) {  // the row's grad_x sums (lane-private slots)
+#pragma unroll
+        for (int i = 0; i < NI; ++i) xw[kWave * i + lane] = 0.0f;
+        wave_lds_sync();
       }
     } else {
       e_beg = (int)(task * Cfg::EPW);
@@ -162,8 +171,8 @@ __global__ __launch_bounds__((kBwdSo2Threads<L, PS, C>)) __attribute__((amdgpu_w
       const bool valid = e < e_end;
       const int ee = valid ? e : e0;  // e0 < e_end: a real edge for the idle slots
       const float vx = vec[3 * (size_t)ee], vy = vec[3 * (size_t)ee + 1], vz = vec[3 * (size_t)ee + 2];
-      const int s = clamp_index(src[ee], N);
-      const int d = sorted ? d_row : clamp_index(dst[ee], N);
+      const int s = by_src ? row : clamp_index(src[ee], N);
+      const int d = mode == 1 ? row : clamp_index(dst[ee], N);
       const So2Frame<L> f(vx, vy, vz);
       const float on = valid ? 1.0f : 0.0f;  // idle slots add nothing
       float gxe = 0.0f, gye = 0.0f;
@@ -250,8 +259,14 @@ __global__ __launch_bounds__((kBwdSo2Threads<L, PS, C>)) __attribute__((amdgpu_w
         __builtin_amdgcn_sched_barrier(0);
         if (gx != nullptr) {
           so2_rotate_out<L, K>(v, f);
+          float* const xs = xw + (g * C + c) * K;
+          if (by_src) {
 #pragma unroll
-          for (int k = 0; k < K; ++k) xw[(g * C + c) * K + k] = v[k];
+            for (int k = 0; k < K; ++k) xs[k] += v[k];
+          } else {
+#pragma unroll
+            for (int k = 0; k < K; ++k) xs[k] = v[k];
+          }
         }
       });
       if (gvec != nullptr) {
@@ -264,13 +279,13 @@ __global__ __launch_bounds__((kBwdSo2Threads<L, PS, C>)) __attribute__((amdgpu_w
           const float r2 = vx * vx + vy * vy + vz * vz;
           float g0, g1, g2;
           frame_gradient<L>(f, gxe, gye, r2 > 0.0f ? rsqrtf(r2) : 0.0f, g0, g1, g2);
-          float* gv = gvec + 3 * (size_t)e;
+          float* gv = gvec + 3 * (by_src ? (size_t)clamp_index(perm[e], E) : (size_t)e);
           gv[0] = g0;
           gv[1] = g1;
           gv[2] = g2;
         }
       }
-      if (gx != nullptr) {
+      if (gx != nullptr && !by_src) {
         if (cl == 0) xsrc[wv][g] = valid ? s : -1;
         wave_lds_sync();
         // the lane index passes through an empty asm statement so that the NI addresses below are
@@ -285,6 +300,18 @@ __global__ __launch_bounds__((kBwdSo2Threads<L, PS, C>)) __attribute__((amdgpu_w
         }
         wave_lds_sync();
       }
+    }
+    if (by_src && gx != nullptr) {  // the edge groups' sums, one coalesced store of the row (zeros if no edges)
+      wave_lds_sync();
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      for (int f = ln; f < MSG; f += kWave) {
+        float t = 0.0f;
+#pragma unroll
+        for (int gg = 0; gg < Cfg::G; ++gg) t += xw[gg * MSG + f];
+        gx[(size_t)row * MSG + f] = t;
+      }
+      wave_lds_sync();
     }
   }
   if (gw != nullptr) {
@@ -315,16 +342,17 @@ static hipError_t launch_bwd_so2_t(const BwdArgs& a) {
   using T = So2Tables<L, PS>;
   constexpr int K = num_comp(L);
   hipError_t err;
-  if (a.gx && (err = launch_fill_zero(a.gx, a.N * C * K, a.stream)) != hipSuccess) return err;
+  // grouped by source every row's grad_x is written once (zeros without edges); else a sum of atomics
+  if (a.gx && !a.by_src && (err = launch_fill_zero(a.gx, a.N * C * K, a.stream)) != hipSuccess) return err;
   if (a.gw && (err = launch_fill_zero(a.gw, (int64_t)T::P * C, a.stream)) != hipSuccess) return err;
-  const bool sorted = a.row_ptr != nullptr;
-  const long long ntasks = sorted ? a.N : (a.E + Cfg::EPW - 1) / Cfg::EPW;
-  if (ntasks == 0 || a.E == 0) return hipGetLastError();
+  const int mode = a.by_src ? 2 : a.row_ptr != nullptr ? 1 : 0;
+  const long long ntasks = mode != 0 ? a.N : (a.E + Cfg::EPW - 1) / Cfg::EPW;
+  if (ntasks == 0 || (a.E == 0 && !(a.by_src && a.gx))) return hipGetLastError();
   const int64_t want = (int64_t)num_cus() * Cfg::PER_CU;
   const int64_t need = (ntasks + Cfg::WAVES - 1) / Cfg::WAVES;
   hipLaunchKernelGGL((conv_bwd_so2_kernel<L, PS, C>), dim3((unsigned)(need < want ? need : want)),
-                     dim3(Cfg::THREADS), 0, a.stream, (int)a.N, (int)a.E, ntasks, a.row_ptr, a.vec, a.src, a.dst,
-                     a.x, a.w, a.gout, a.gx, a.gw, a.gvec);
+                     dim3(Cfg::THREADS), 0, a.stream, (int)a.N, (int)a.E, ntasks, mode, a.row_ptr, a.vec, a.src,
+                     a.dst, a.perm, a.x, a.w, a.gout, a.gx, a.gw, a.gvec);
   return hipGetLastError();
 }
 

@@ -53,6 +53,10 @@ struct BwdArgs {
   int algo = 0;  // grad_vec of sorted edges: 2 = vector-ALU walk, else matrix cores
   float r_cut = 0.0f;  // radial weights: w is [8, P*C] and gw [8, P*C]
   hipStream_t stream;
+  // edges grouped by source: row_ptr is the CSR over sources, dst the destinations in that order,
+  // perm[i] the input index of grouped edge i (grad_vec is written there)
+  bool by_src = false;
+  const int32_t* perm = nullptr;
 };
 
 hipError_t launch_sh(const float* vec, int64_t E, int lmax, float* Y, hipStream_t stream);

@@ -81,7 +81,7 @@ def load_library(path: str = LIB_PATH):
             lib.eqtp_conv_messages.restype = i32
             lib.eqtp_conv_backward.argtypes = [ctypes.POINTER(_ConvDesc), i64, i64] + [vp] * 11
             lib.eqtp_conv_backward.restype = i32
-            lib.eqtp_conv_backward_by_source.argtypes = [ctypes.POINTER(_ConvDesc), i64, i64] + [vp] * 9
+            lib.eqtp_conv_backward_by_source.argtypes = [ctypes.POINTER(_ConvDesc), i64, i64] + [vp] * 11
             lib.eqtp_conv_backward_by_source.restype = i32
             lib.eqtp_edge_rows.argtypes = [i64, i64, vp, vp, vp]
             lib.eqtp_edge_rows.restype = i32
@@ -342,10 +342,15 @@ def eqtp_conv_backward(vec, src, x, weights, grad_out, lmax: int, row_ptr=None, 
 
 
 def eqtp_conv_backward_by_source(vec_s, dst_s, src_ptr, x, weights, grad_out, lmax: int,
-                                 path_set: int = EQTP_PATHS_PARITY, need_x: bool = True, need_w: bool = True):
-    """(grad_x [N,C,K] | None, grad_w [P,C] | None) from the edges grouped by
-    source node: src_ptr [N+1] CSR over sources, vec_s [E,3] / dst_s [E] in
-    that order (see eqtp_sort_edges)."""
+                                 path_set: int = EQTP_PATHS_PARITY, need_x: bool = True, need_w: bool = True,
+                                 need_vec: bool = False, perm=None, weight_mode: int = EQTP_W_FIXED,
+                                 r_cut: float = 0.0, n_basis: int = 8, algo: int = EQTP_ALGO_AUTO):
+    """(grad_x [N,C,K] | None, grad_w | None, grad_vec [E,3] | None) from the
+    edges grouped by source node: src_ptr [N+1] CSR over sources, vec_s [E,3] /
+    dst_s [E] in that order, perm [E] (needed for grad_vec) the caller's index of
+    each grouped edge (see eqtp_sort_edges).  grad_vec is in the caller's edge
+    order.  Fixed weights [P, C] or, with weight_mode=EQTP_W_RADIAL, radial
+    weights [n_basis, P*C] (grad_w of the same shape)."""
     import torch
 
     _check(grad_out, "grad_out", torch.float32)
@@ -358,21 +363,25 @@ def eqtp_conv_backward_by_source(vec_s, dst_s, src_ptr, x, weights, grad_out, lm
     E = vec_s.shape[0]
     _check(dst_s, "dst_s", torch.int32, (E,))
     _check(src_ptr, "src_ptr", torch.int32, (N + 1,))
-    if need_w:
-        _check(x, "x", torch.float32, (N, C, K))
+    _check(x, "x", torch.float32, (N, C, K))
     P = eqtp_num_paths(lmax, path_set)
-    _check(weights, "weights", torch.float32, (P, C))
-    if not (need_x or need_w):
+    _check(weights, "weights", torch.float32, (P, C) if weight_mode == EQTP_W_FIXED else (n_basis, P * C))
+    if not (need_x or need_w or need_vec):
         raise ValueError("request at least one gradient")
+    if need_vec:
+        if perm is None:
+            raise ValueError("grad_vec needs perm (the caller's index of each grouped edge)")
+        _check(perm, "perm", torch.int32, (E,))
     gx = torch.empty_like(grad_out) if need_x else None
     gw = torch.empty_like(weights) if need_w else None
-    d = _ConvDesc(ctypes.sizeof(_ConvDesc), lmax, C, path_set, EQTP_W_FIXED, EQTP_EDGES_DST_SORTED, EQTP_ALGO_AUTO,
-                  0.0, 8, EQTP_F32)
+    gv = torch.empty((E, 3), dtype=torch.float32, device=grad_out.device) if need_vec else None
+    d = _ConvDesc(ctypes.sizeof(_ConvDesc), lmax, C, path_set, weight_mode, EQTP_EDGES_DST_SORTED, algo,
+                  float(r_cut), n_basis, EQTP_F32)
     rc = load_library().eqtp_conv_backward_by_source(ctypes.byref(d), N, E, _ptr(vec_s), _ptr(dst_s), _ptr(src_ptr),
-                                                     _ptr(x if need_w else None), _ptr(weights), _ptr(grad_out),
-                                                     _ptr(gx), _ptr(gw), _stream())
+                                                     _ptr(x), _ptr(weights), _ptr(grad_out), _ptr(gx), _ptr(gw),
+                                                     _ptr(perm if need_vec else None), _ptr(gv), _stream())
     _raise(rc, "eqtp_conv_backward_by_source")
-    return gx, gw
+    return gx, gw, gv
 
 
 def eqtp_edge_rows(row_ptr, E: int, out=None):

@@ -222,15 +222,26 @@ def test_conv_backward_by_source_validation():
     e = _lib()
     lib = e.load_library()
 
-    def call(d, N=10, E=20, vec=FAKE, dst=FAKE, sp=FAKE, x=FAKE, w=FAKE, g=FAKE, gx=FAKE, gw=FAKE):
-        return lib.eqtp_conv_backward_by_source(ctypes.byref(d), N, E, vec, dst, sp, x, w, g, gx, gw, NULL)
+    def call(d, N=10, E=20, vec=FAKE, dst=FAKE, sp=FAKE, x=FAKE, w=FAKE, g=FAKE, gx=FAKE, gw=FAKE, perm=NULL,
+             gv=NULL):
+        return lib.eqtp_conv_backward_by_source(ctypes.byref(d), N, E, vec, dst, sp, x, w, g, gx, gw, perm, gv,
+                                                NULL)
 
-    assert call(_desc(e, weight_mode=1, r_cut=5.0)) == 2                 # radial weights: not implemented
-    assert call(_desc(e, lmax=4)) == 2
+    assert call(_desc(e, weight_mode=1, r_cut=0.0)) == 1                 # radial weights need r_cut > 0
+    assert call(_desc(e, weight_mode=1, r_cut=5.0, n_basis=6)) == 2      # radial: 8 basis functions only
+    assert call(_desc(e, weight_mode=1, r_cut=5.0, C=8)) == 2            # radial: C a multiple of 16
+    assert call(_desc(e, weight_mode=1, r_cut=5.0, lmax=4)) == 2         # radial: lmax 0..3
+    assert call(_desc(e, weight_mode=1, r_cut=5.0), x=NULL, gw=NULL) == 1  # the walk reads x
+    assert call(_desc(e, lmax=7)) == 2                                   # above lmax 6
+    assert call(_desc(e, lmax=5, C=128)) == 2                            # edge-aligned form: C = 128 to lmax 4
+    assert call(_desc(e, algo=7)) == 1                                   # unknown algorithm
     assert call(_desc(e, C=48)) == 2
     assert call(_desc(e, x_dtype=1)) == 2                                  # bf16 features
     assert call(_desc(e, path_set=2)) == 1
     assert call(_desc(e), gx=NULL, gw=NULL) == 1                          # nothing requested
+    assert call(_desc(e), gx=NULL, gw=NULL, gv=FAKE) == 1                 # grad_vec needs perm
+    assert call(_desc(e), gx=NULL, gw=NULL, gv=FAKE, perm=FAKE, x=NULL) == 1  # grad_vec needs x
+    assert call(_desc(e), gv=ctypes.c_void_p(0x10002), perm=FAKE) == 1    # grad_vec not 4-byte aligned
     assert call(_desc(e), x=NULL) == 1                                    # grad_w needs x
     assert call(_desc(e), g=NULL) == 1
     assert call(_desc(e), sp=NULL) == 1

@@ -146,7 +146,7 @@ def _by_source_numpy(wl):
 def _check_by_source(eq, wl, gout, grouping, need=(True, True), what=""):
     ref = oracle.conv_backward(wl.N, wl.vec, wl.src, wl.dst, wl.x, wl.w, gout, wl.lmax, wl.path_set)
     sp, vs, ds = grouping
-    gx, gw = eq.eqtp_conv_backward_by_source(vs if not isinstance(vs, np.ndarray) else _t(vs),
+    gx, gw, _ = eq.eqtp_conv_backward_by_source(vs if not isinstance(vs, np.ndarray) else _t(vs),
                                              ds if not isinstance(ds, np.ndarray) else _t(ds),
                                              sp if not isinstance(sp, np.ndarray) else _t(sp),
                                              _t(wl.x), _t(wl.w), _t(gout), wl.lmax, path_set=wl.path_set,
@@ -220,7 +220,7 @@ def test_backward_by_source_no_edges():
     x = torch.randn(N, C, 16, device="cuda")
     w = torch.randn(23, C, device="cuda")
     _say("backward by source, no edges")
-    gx, gw = eq.eqtp_conv_backward_by_source(torch.zeros(0, 3, device="cuda"),
+    gx, gw, _ = eq.eqtp_conv_backward_by_source(torch.zeros(0, 3, device="cuda"),
                                              torch.zeros(0, dtype=torch.int32, device="cuda"),
                                              torch.zeros(N + 1, dtype=torch.int32, device="cuda"), x, w, g, 3)
     assert float(_np(gx).__abs__().max()) == 0.0 and float(_np(gw).__abs__().max()) == 0.0
