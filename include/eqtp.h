@@ -19,7 +19,8 @@
  * Conventions shared by every entry point
  *   - All pointers not marked "host" are device pointers allocated and owned
  *     by the caller.  The library allocates no device memory, performs no
- *     host<->device copies and never synchronises.
+ *     host<->device copies and never synchronises (debug mode, below
+ *     eqtp_check_graph, is the one exception).
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Work is enqueued on it and the call returns immediately.
  *   - Return value: EQTP_OK (0) or an error code.  Argument errors are
@@ -27,7 +28,8 @@
  *     A failed launch returns EQTP_EHIP.  Device faults surface at the
  *     caller's next synchronisation.
  *   - Functions are thread-safe; the only mutable state is a per-device cache
- *     of the compute-unit count, read once through the HIP runtime.
+ *     of the compute-unit count, read once through the HIP runtime, and the
+ *     debug-mode switch.
  *   - Feature vectors use layout [N, C, K] with K = (lmax+1)^2: each
  *     channel's K components are contiguous, in the component order above.
  *   - Indices (src, dst, row_ptr) are int32.  Out-of-range index values are
@@ -49,6 +51,7 @@ extern "C" {
 #define EQTP_EUNSUPPORTED 2 /* valid request this build does not implement */
 #define EQTP_EHIP 3         /* the HIP runtime reported an error at launch */
 #define EQTP_ETOOLARGE 4    /* eqtp_conv_fused_noalloc: the call needs more than the static scratch */
+#define EQTP_EGRAPH 5       /* debug mode: the graph arrays fail eqtp_check_graph (nothing else launched) */
 
 /* coupling path sets (paths are (l1 = feature l, l2 = harmonic l, l3 = output l)) */
 #define EQTP_PATHS_PARITY 0 /* l1+l2+l3 even: 23 paths at lmax 3, 11 at lmax 2 */
@@ -427,6 +430,52 @@ int eqtp_interaction(const eqtp_interaction_desc* d, int64_t N, int64_t E, const
 
 /* Static description of a status code (never NULL). */
 const char* eqtp_status_string(int status);
+
+/*
+ * Graph checks, the debugging aid for the index arrays every kernel trusts
+ * (the PyTorch custom-operator tutorial page, chapter 5, debugging and best
+ * practices: look at the last launch error, run a memory checker, synchronise
+ * to find which launch went wrong).  The kernels clamp out-of-range indices
+ * so that no access leaves the buffers; this call says whether any clamp
+ * would act, and where.  Each array may be NULL (its checks are skipped):
+ *   row_ptr  [N+1] int32: CSR rows (row_ptr[0] = 0, non-decreasing,
+ *            row_ptr[N] = E); for edges grouped by source pass src_ptr here.
+ *   src      [E] int32, each in [0, N).
+ *   dst      [E] int32, each in [0, N); with row_ptr also given, each edge e
+ *            must lie in row dst[e] of the CSR.
+ *   vec      [E, 3] fp32, every component finite.
+ *   report   [EQTP_CHECK_WORDS] int32, device, out (the caller's; 4-byte
+ *            aligned); fully written:
+ *     [0] edges with src outside [0, N)       [1] edges with dst outside [0, N)
+ *     [2] rows with row_ptr[r+1] < row_ptr[r]  [3] endpoint faults (row_ptr[0]
+ *         != 0 and row_ptr[N] != E count one each)
+ *     [4] edges outside the row their dst names  [5] edges with a non-finite
+ *         vector component
+ *     [6] smallest edge index counted in [0], [1], [4] or [5], or -1
+ *     [7] smallest row index counted in [2], or -1
+ * The report is a set of counts, so it is the same from run to run.
+ * 0 <= N, E < 2^31.  EQTP_EINVAL for bad sizes or a NULL / misaligned report
+ * or array (before any launch), else the launch status.  Asynchronous on
+ * stream; reads only the arrays given.
+ */
+#define EQTP_CHECK_WORDS 8
+int eqtp_check_graph(int64_t N, int64_t E, const int32_t* row_ptr, const int32_t* src, const int32_t* dst,
+                     const float* vec, int32_t* report, void* stream);
+
+/*
+ * Debug mode.  When on, every entry point that takes a graph (the
+ * convolutions, messages, gradients, edge grouping and the interaction layer)
+ * first runs eqtp_check_graph on the arrays it will read (and on perm for the
+ * source-grouped gradients), waits for the report on its stream and returns
+ * EQTP_EGRAPH, with nothing else launched, if any count is non-zero.  Debug
+ * calls synchronise the stream and share one small static report per device
+ * (calls are serialised by a host lock), so they are for finding bad inputs,
+ * not for graph capture or timing.  The initial setting comes from the
+ * environment variable EQTP_DEBUG when the library is loaded (set and not
+ * "0" = on).  eqtp_set_debug(on) sets it for the whole process (on = 0 or 1;
+ * any other value leaves it unchanged) and returns the previous setting.
+ */
+int eqtp_set_debug(int on);
 
 /*
  * Test-only: walks the dst-sorted edges with exactly the row -> wave ->

@@ -17,7 +17,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libeqtp.so")
 ROOT = os.path.dirname(HERE)
 
-SOURCES = ["abi.hip", "sh.hip", "sort.hip", "conv_node.hip", "conv_edge.hip", "conv_bwd.hip", "conv_so2.hip", "conv_bwd_so2.hip", "linear.hip", "interaction.hip"]
+SOURCES = ["abi.hip", "sh.hip", "sort.hip", "conv_node.hip", "conv_edge.hip", "conv_bwd.hip", "conv_so2.hip", "conv_bwd_so2.hip", "linear.hip", "interaction.hip", "check.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

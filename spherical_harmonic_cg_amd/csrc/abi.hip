@@ -2,8 +2,10 @@
 // argument validation, kernel selection and launch on the caller's stream.
 #include <stddef.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
+#include <atomic>
 #include <mutex>
 
 #include "../../include/eqtp.h"
@@ -17,6 +19,11 @@
 // device address comes from hipGetSymbolAddress, once per device.
 constexpr int64_t kScratchBytes = (int64_t)128 << 20;
 static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// Debug mode's report: the graph check's words, then those of the check of a
+// permutation (source-grouped gradients); one array per device, used under
+// g_debug_mu only, addressed like the scratch above.
+static __device__ __align__(16) int32_t debug_report[2 * eqtp::kCheckWords];
 
 namespace {
 
@@ -67,6 +74,49 @@ const eqtp_gen::PathLs* path_list(int lmax, int path_set) {
 }
 
 int status_of(hipError_t e) { return e == hipSuccess ? EQTP_OK : EQTP_EHIP; }
+
+// ---- debug mode: graph checks before each launch (see eqtp_set_debug) ----
+int debug_from_env() {
+  const char* v = getenv("EQTP_DEBUG");
+  return (v != nullptr && v[0] != '\0' && strcmp(v, "0") != 0) ? 1 : 0;
+}
+std::atomic<int> g_debug{debug_from_env()};
+std::mutex g_debug_mu;
+constexpr int kMaxDebugDevices = 64;
+int32_t* g_debug_report[kMaxDebugDevices] = {};
+
+// Runs the graph check (and, with perm, the check that perm holds edge
+// indices in [0, E)) on the stream, waits for the report and returns
+// EQTP_EGRAPH if any count is non-zero.  A no-op returning EQTP_OK when debug
+// mode is off.  Arrays may be NULL (their checks are skipped).
+int debug_check(int64_t N, int64_t E, const int32_t* row_ptr, const int32_t* src, const int32_t* dst,
+                const float* vec, const int32_t* perm, void* stream) {
+  if (!g_debug.load(std::memory_order_relaxed)) return EQTP_OK;
+  if (N == 0 && E == 0) return EQTP_OK;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return EQTP_EHIP;
+  if (dev < 0 || dev >= kMaxDebugDevices) return EQTP_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_debug_mu);
+  if (g_debug_report[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(debug_report)) != hipSuccess || p == nullptr) return EQTP_EHIP;
+    g_debug_report[dev] = static_cast<int32_t*>(p);
+  }
+  int32_t* rep = g_debug_report[dev];
+  const hipStream_t st = (hipStream_t)stream;
+  if (E == 0) src = dst = perm = nullptr, vec = nullptr;
+  if (eqtp::launch_check_graph(N, E, row_ptr, src, dst, vec, rep, st) != hipSuccess) return EQTP_EHIP;
+  if (perm && eqtp::launch_check_graph(E, E, nullptr, perm, nullptr, nullptr, rep + eqtp::kCheckWords, st) !=
+                  hipSuccess)
+    return EQTP_EHIP;
+  int32_t host[2 * eqtp::kCheckWords] = {};
+  const int words = perm ? 2 * eqtp::kCheckWords : eqtp::kCheckWords;
+  if (hipMemcpyAsync(host, rep, words * sizeof(int32_t), hipMemcpyDeviceToHost, st) != hipSuccess) return EQTP_EHIP;
+  if (hipStreamSynchronize(st) != hipSuccess) return EQTP_EHIP;
+  for (int k = 0; k < words; ++k)
+    if (k % eqtp::kCheckWords < 6 && host[k] != 0) return EQTP_EGRAPH;
+  return EQTP_OK;
+}
 
 }  // namespace
 
@@ -199,6 +249,18 @@ int conv_impl(const eqtp_conv_desc* d, int64_t N, int64_t E, const float* vec, c
   return status_of(use_node ? eqtp::launch_conv_node(a) : eqtp::launch_conv_edge(a));
 }
 
+// conv_impl with debug mode's graph check between validation and launch
+int conv_checked(const eqtp_conv_desc* d, int64_t N, int64_t E, const float* vec, const int32_t* src,
+                 const int32_t* dst, const int32_t* row_ptr, const void* x, const float* weights, float* out,
+                 void* stream) {
+  int rc = conv_impl(d, N, E, vec, src, dst, row_ptr, x, weights, out, stream, false);
+  if (rc != EQTP_OK || N == 0) return rc;
+  const bool sorted = d->edge_order == EQTP_EDGES_DST_SORTED;
+  rc = debug_check(N, E, sorted ? row_ptr : nullptr, src, sorted ? nullptr : dst, vec, nullptr, stream);
+  if (rc != EQTP_OK) return rc;
+  return conv_impl(d, N, E, vec, src, dst, row_ptr, x, weights, out, stream, true);
+}
+
 // Workspace of the grouping by destination: row pointers [N+1]; five regions of
 // E ints R0..R4 (the radix sort's keys and edge indices: the last pass leaves
 // them in R0 and R4); the sort's digit counts.  After the sort the grouped
@@ -227,7 +289,7 @@ int conv_ws_impl(const eqtp_conv_desc* d, int64_t N, int64_t E, const float* vec
                  const int32_t* dst, const int32_t* row_ptr, const void* x, const float* weights, float* out,
                  void* workspace, int64_t workspace_bytes, void* stream) {
   if (!desc_ok(d)) return EQTP_EINVAL;
-  if (!groups_edges(d, N)) return conv_impl(d, N, E, vec, src, dst, row_ptr, x, weights, out, stream, true);
+  if (!groups_edges(d, N)) return conv_checked(d, N, E, vec, src, dst, row_ptr, x, weights, out, stream);
   if (N < 0 || E < 0 || N > kMaxIndex || E > kMaxIndex) return EQTP_EINVAL;
   const WsLayout L = ws_layout(N, E);
   if (!workspace || !aligned16(workspace) || workspace_bytes < (int64_t)L.total) return EQTP_EINVAL;
@@ -247,6 +309,8 @@ int conv_ws_impl(const eqtp_conv_desc* d, int64_t N, int64_t E, const float* vec
   ds.edge_order = EQTP_EDGES_DST_SORTED;
   int rc = conv_impl(&ds, N, E, vec, src, nullptr, rp, x, weights, out, stream, false);
   if (rc != EQTP_OK) return rc;
+  rc = debug_check(N, E, nullptr, src, dst, vec, nullptr, stream);
+  if (rc != EQTP_OK) return rc;
   rc = status_of(eqtp::launch_sort_edges_stable(N, E, dst, vec, src, rp, R[0], R[4], R[1], R[2], hist, vec_s, src_s,
                                                 (hipStream_t)stream));
   if (rc != EQTP_OK) return rc;
@@ -260,7 +324,7 @@ extern "C" {
 int eqtp_conv_fused(const eqtp_conv_desc* d, int64_t N, int64_t E, const float* vec, const int32_t* src,
                     const int32_t* dst, const int32_t* row_ptr, const void* x, const float* weights, float* out,
                     void* stream) {
-  return conv_impl(d, N, E, vec, src, dst, row_ptr, x, weights, out, stream, true);
+  return conv_checked(d, N, E, vec, src, dst, row_ptr, x, weights, out, stream);
 }
 
 int64_t eqtp_conv_workspace_bytes(const eqtp_conv_desc* d, int64_t N, int64_t E) {
@@ -356,6 +420,8 @@ int eqtp_conv_messages(const eqtp_conv_desc* d, int64_t N, int64_t E, const floa
   a.w = weights;
   a.out = messages;
   a.stream = (hipStream_t)stream;
+  const int chk = debug_check(N, E, nullptr, src, nullptr, vec, nullptr, stream);
+  if (chk != EQTP_OK) return chk;
   if (use_so2) {
     a.messages = 1;
     return status_of(eqtp::launch_conv_so2(a));
@@ -418,6 +484,10 @@ int eqtp_conv_backward(const eqtp_conv_desc* d, int64_t N, int64_t E, const floa
   a.algo = d->algo;
   a.r_cut = d->r_cut;
   a.stream = (hipStream_t)stream;
+  if (N > 0) {
+    const int chk = debug_check(N, E, a.row_ptr, src, a.dst, vec, nullptr, stream);
+    if (chk != EQTP_OK) return chk;
+  }
   return status_of(radial    ? eqtp::launch_conv_backward_radial(a)
                    : use_so2 ? eqtp::launch_conv_backward_so2(a)
                              : eqtp::launch_conv_backward(a));
@@ -480,6 +550,11 @@ int eqtp_conv_backward_by_source(const eqtp_conv_desc* d, int64_t N, int64_t E, 
   a.by_src = true;
   a.perm = perm;
   a.stream = (hipStream_t)stream;
+  if (N > 0) {
+    // rows are sources here: src_ptr is the CSR, dst_s is range-checked as an index array
+    const int chk = debug_check(N, E, src_ptr, dst_s, nullptr, vec_s, grad_vec ? perm : nullptr, stream);
+    if (chk != EQTP_OK) return chk;
+  }
   if (radial) return status_of(eqtp::launch_conv_backward_radial(a));
   if (use_so2) return status_of(eqtp::launch_conv_backward_so2(a));
   // lmax <= 3, fixed weights: grad_x and grad_w by the node-factored adjoint, grad_vec by a walk in the edge
@@ -500,6 +575,10 @@ int eqtp_conv_backward_by_source(const eqtp_conv_desc* d, int64_t N, int64_t E, 
 int eqtp_edge_rows(int64_t N, int64_t E, const int32_t* row_ptr, int32_t* rows, void* stream) {
   if (N < 0 || E < 0 || N > kMaxIndex || E > kMaxIndex) return EQTP_EINVAL;
   if (E > 0 && (N == 0 || !row_ptr || !rows || !aligned4(row_ptr) || !aligned4(rows))) return EQTP_EINVAL;
+  if (E > 0) {
+    const int chk = debug_check(N, E, row_ptr, nullptr, nullptr, nullptr, nullptr, stream);
+    if (chk != EQTP_OK) return chk;
+  }
   return status_of(eqtp::launch_edge_rows(N, E, row_ptr, rows, (hipStream_t)stream));
 }
 
@@ -512,6 +591,9 @@ int eqtp_sort_edges(int64_t N, int64_t E, const int32_t* dst, const float* vec, 
     if (!dst || !perm || !aligned4(dst) || !aligned4(perm)) return EQTP_EINVAL;
     if (vec_sorted && (!vec || !aligned4(vec) || !aligned4(vec_sorted))) return EQTP_EINVAL;
     if (src_sorted && (!src || !aligned4(src) || !aligned4(src_sorted))) return EQTP_EINVAL;
+    const int chk = debug_check(N, E, nullptr, src_sorted ? src : nullptr, dst, vec_sorted ? vec : nullptr, nullptr,
+                                stream);
+    if (chk != EQTP_OK) return chk;
   }
   return status_of(eqtp::launch_sort_edges(N, E, dst, vec, src, row_ptr, perm, vec_sorted, src_sorted,
                                            (hipStream_t)stream));
@@ -548,6 +630,8 @@ int eqtp_interaction(const eqtp_interaction_desc* d, int64_t N, int64_t E, const
   if (!W1 || !W2 || !W3 || !aligned4(W1) || !aligned4(W2) || !aligned4(W3)) return EQTP_EINVAL;
   if (!row_ptr || !aligned4(row_ptr)) return EQTP_EINVAL;
   if (E > 0 && (!vec || !src || !aligned4(vec) || !aligned4(src))) return EQTP_EINVAL;
+  const int chk = debug_check(N, E, row_ptr, src, nullptr, vec, nullptr, stream);
+  if (chk != EQTP_OK) return chk;
   unsigned char* ws = static_cast<unsigned char*>(workspace);
   float* h1 = reinterpret_cast<float*>(ws);
   float* m = reinterpret_cast<float*>(ws + L.m);
@@ -587,8 +671,25 @@ const char* eqtp_status_string(int status) {
     case EQTP_EUNSUPPORTED: return "EQTP_EUNSUPPORTED: request not supported by this build";
     case EQTP_EHIP: return "EQTP_EHIP: HIP runtime error at launch";
     case EQTP_ETOOLARGE: return "EQTP_ETOOLARGE: the request needs more than the library's static scratch";
+    case EQTP_EGRAPH: return "EQTP_EGRAPH: the graph arrays fail the debug-mode checks";
     default: return "unknown status";
   }
+}
+
+int eqtp_check_graph(int64_t N, int64_t E, const int32_t* row_ptr, const int32_t* src, const int32_t* dst,
+                     const float* vec, int32_t* report, void* stream) {
+  if (N < 0 || E < 0 || N > kMaxIndex || E > kMaxIndex) return EQTP_EINVAL;
+  if (!report || !aligned4(report)) return EQTP_EINVAL;
+  if ((row_ptr && !aligned4(row_ptr)) || (src && !aligned4(src)) || (dst && !aligned4(dst)) ||
+      (vec && !aligned4(vec)))
+    return EQTP_EINVAL;
+  if (E == 0) src = dst = nullptr, vec = nullptr;
+  return status_of(eqtp::launch_check_graph(N, E, row_ptr, src, dst, vec, report, (hipStream_t)stream));
+}
+
+int eqtp_set_debug(int on) {
+  if (on != 0 && on != 1) return g_debug.load();
+  return g_debug.exchange(on);
 }
 
 int eqtp_test_segment_probe(const int32_t* row_ptr, const int32_t* src, int64_t N, int64_t E, int C, int lmax,

@@ -71,6 +71,10 @@ hipError_t launch_linear(int64_t N, int C, int lmax, int mode, const void* h, co
 // compute units of the current device (cached per device)
 int num_cus();
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t stream);
+// graph checks: kCheckWords int32 of counts and first offending indices into report (check.hip)
+constexpr int kCheckWords = 8;
+hipError_t launch_check_graph(int64_t N, int64_t E, const int32_t* row_ptr, const int32_t* src, const int32_t* dst,
+                              const float* vec, int32_t* report, hipStream_t stream);
 hipError_t launch_conv_backward(const BwdArgs& a);   // fixed weights, vector ALUs
 hipError_t launch_conv_backward_radial(const BwdArgs& a);  // radial weights, lmax <= 3, C a multiple of 16
 // the interaction layer's radial network: phi [E][4][16] (scaled by scale) from the edge lengths

@@ -17,7 +17,8 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libeqtp.so")
 
-EQTP_OK, EQTP_EINVAL, EQTP_EUNSUPPORTED, EQTP_EHIP, EQTP_ETOOLARGE = 0, 1, 2, 3, 4
+EQTP_OK, EQTP_EINVAL, EQTP_EUNSUPPORTED, EQTP_EHIP, EQTP_ETOOLARGE, EQTP_EGRAPH = 0, 1, 2, 3, 4, 5
+EQTP_CHECK_WORDS = 8
 EQTP_PATHS_PARITY, EQTP_PATHS_SO3 = 0, 1
 EQTP_W_FIXED, EQTP_W_RADIAL = 0, 1
 EQTP_EDGES_DST_SORTED, EQTP_EDGES_UNSORTED = 0, 1
@@ -28,7 +29,7 @@ EXPORTED = ("eqtp_num_paths", "eqtp_path_table", "eqtp_sh", "eqtp_conv_fused", "
             "eqtp_conv_fused_ws", "eqtp_conv_fused_noalloc", "eqtp_conv_messages",
             "eqtp_conv_backward", "eqtp_conv_backward_by_source", "eqtp_edge_rows", "eqtp_sort_edges",
             "eqtp_linear", "eqtp_interaction_workspace_bytes", "eqtp_interaction",
-            "eqtp_status_string", "eqtp_test_segment_probe")
+            "eqtp_status_string", "eqtp_check_graph", "eqtp_set_debug", "eqtp_test_segment_probe")
 
 
 class EqtpError(RuntimeError):
@@ -95,6 +96,10 @@ def load_library(path: str = LIB_PATH):
             lib.eqtp_interaction.restype = i32
             lib.eqtp_status_string.argtypes = [i32]
             lib.eqtp_status_string.restype = ctypes.c_char_p
+            lib.eqtp_check_graph.argtypes = [i64, i64] + [vp] * 6
+            lib.eqtp_check_graph.restype = i32
+            lib.eqtp_set_debug.argtypes = [i32]
+            lib.eqtp_set_debug.restype = i32
             lib.eqtp_test_segment_probe.argtypes = [vp, vp, i64, i64, i32, i32, i32, vp, vp, vp]
             lib.eqtp_test_segment_probe.restype = i32
             _lib = lib
@@ -382,6 +387,29 @@ def eqtp_conv_backward_by_source(vec_s, dst_s, src_ptr, x, weights, grad_out, lm
                                                      _ptr(perm if need_vec else None), _ptr(gv), _stream())
     _raise(rc, "eqtp_conv_backward_by_source")
     return gx, gw, gv
+
+
+def eqtp_check_graph(N: int, E: int, row_ptr=None, src=None, dst=None, vec=None, report=None):
+    """Graph checks on the GPU: report [EQTP_CHECK_WORDS] int32 (counts of out-of-range src / dst,
+    decreasing row_ptr steps, row_ptr endpoint faults, edges outside their dst's row, non-finite
+    vectors; then the first offending edge and row, -1 if none).  Any array may be None."""
+    import torch
+
+    for t, name, dt, shape in ((row_ptr, "row_ptr", torch.int32, (N + 1,)), (src, "src", torch.int32, (E,)),
+                               (dst, "dst", torch.int32, (E,)), (vec, "vec", torch.float32, (E, 3))):
+        if t is not None:
+            _check(t, name, dt, shape)
+    dev = next((t.device for t in (row_ptr, src, dst, vec) if t is not None), torch.device("cuda"))
+    rep = report if report is not None else torch.empty(EQTP_CHECK_WORDS, dtype=torch.int32, device=dev)
+    _check(rep, "report", torch.int32, (EQTP_CHECK_WORDS,))
+    rc = load_library().eqtp_check_graph(N, E, _ptr(row_ptr), _ptr(src), _ptr(dst), _ptr(vec), _ptr(rep), _stream())
+    _raise(rc, "eqtp_check_graph")
+    return rep
+
+
+def eqtp_set_debug(on: bool) -> bool:
+    """Switch the library's debug mode (graph checks before every launch); returns the previous setting."""
+    return bool(load_library().eqtp_set_debug(1 if on else 0))
 
 
 def eqtp_edge_rows(row_ptr, E: int, out=None):

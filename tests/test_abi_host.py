@@ -53,9 +53,53 @@ def test_num_paths_and_table_match_oracle():
 
 def test_status_strings():
     e = _lib()
-    for s in range(5):
+    for s in range(6):
         assert isinstance(e.eqtp_status_string(s), str)
     assert e.eqtp_status_string(1).startswith("EQTP_EINVAL")
+    assert e.eqtp_status_string(e.EQTP_EGRAPH).startswith("EQTP_EGRAPH")
+
+
+def test_check_graph_rejects_bad_arguments():
+    e = _lib()
+    lib = e.load_library()
+    rep = FAKE
+    assert lib.eqtp_check_graph(-1, 0, NULL, NULL, NULL, NULL, rep, NULL) == e.EQTP_EINVAL
+    assert lib.eqtp_check_graph(4, -2, NULL, NULL, NULL, NULL, rep, NULL) == e.EQTP_EINVAL
+    assert lib.eqtp_check_graph(1 << 31, 4, NULL, NULL, NULL, NULL, rep, NULL) == e.EQTP_EINVAL
+    assert lib.eqtp_check_graph(4, 4, NULL, NULL, NULL, NULL, NULL, NULL) == e.EQTP_EINVAL
+    assert lib.eqtp_check_graph(4, 4, NULL, NULL, NULL, NULL, ctypes.c_void_p(0x10002), NULL) == e.EQTP_EINVAL
+    odd = ctypes.c_void_p(0x10001)
+    for k in range(4):
+        arrs = [NULL] * 4
+        arrs[k] = odd
+        assert lib.eqtp_check_graph(4, 4, *arrs, rep, NULL) == e.EQTP_EINVAL
+
+
+def test_debug_switch_and_environment():
+    import subprocess
+    import sys
+
+    e = _lib()
+    was = e.eqtp_set_debug(True)
+    try:
+        assert e.eqtp_set_debug(True) is True
+        lib = e.load_library()
+        assert lib.eqtp_set_debug(7) == 1      # not 0 or 1: unchanged
+        assert e.eqtp_set_debug(False) is True
+        assert lib.eqtp_set_debug(-1) == 0
+    finally:
+        e.eqtp_set_debug(was)
+    # the initial setting comes from EQTP_DEBUG when the library is loaded
+    code = "import ctypes,sys; l=ctypes.CDLL(sys.argv[1]); print(l.eqtp_set_debug(0))"
+    for val, want in (("1", "1"), ("yes", "1"), ("0", "0"), ("", "0"), (None, "0")):
+        env = dict(os.environ)
+        env.pop("EQTP_DEBUG", None)
+        if val is not None:
+            env["EQTP_DEBUG"] = val
+        out = subprocess.run([sys.executable, "-c", code, e.LIB_PATH], env=env, capture_output=True, text=True,
+                             timeout=120)
+        assert out.returncode == 0, out.stderr
+        assert out.stdout.strip() == want, (val, out.stdout)
 
 
 def _desc(e, **kw):
