@@ -202,6 +202,9 @@ def main():
                     help="'cell': spatially coherent atom numbering (a labelled extra, not the headline)")
     ap.add_argument("--path-set", default="parity", choices=("parity", "so3"),
                     help="'so3': the 34-path SO(3) set (a labelled extra, not the headline)")
+    ap.add_argument("--out-bf16", action="store_true",
+                    help="with --unsorted: bfloat16 conv output summed with packed bf16 atomics; the linear then "
+                         "reads it in bf16 storage")
     ap.add_argument("--x-bf16", action="store_true",
                     help="bfloat16 node features (a labelled extra: halves the gathered bytes)")
     ap.add_argument("--lmax", type=int, default=None,
@@ -230,6 +233,8 @@ def main():
         ap.error("--sort-edges needs --unsorted")
     if args.ws and (not args.unsorted or args.sort_edges):
         ap.error("--ws needs --unsorted (and replaces --sort-edges)")
+    if args.out_bf16 and (not args.unsorted or args.sort_edges or args.ws):
+        ap.error("--out-bf16 needs --unsorted (atomics into the output; not with --sort-edges or --ws)")
     if args.graph and args.unsorted:
         ap.error("--graph times dst-sorted edges only")
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -268,10 +273,13 @@ def main():
     if args.x_bf16:
         x = x.to(torch.bfloat16)
     w = T(wl.weights)
-    out = torch.empty(x.shape, dtype=torch.float32, device=dev)
+    out = torch.empty(x.shape, dtype=torch.bfloat16 if args.out_bf16 else torch.float32, device=dev)
     w_lin = T(wl.w_lin) if wl.w_lin is not None else None
-    out2 = torch.empty_like(out) if w_lin is not None else None
-    lin_dtype = eq.EQTP_BF16 if wl.linear_bf16 else eq.EQTP_F32
+    out2 = torch.empty(x.shape, dtype=torch.float32, device=dev) if w_lin is not None else None
+    lin_dtype = eq.EQTP_BF16 if (wl.linear_bf16 or args.out_bf16) else eq.EQTP_F32
+    if args.out_bf16 and w_lin is not None:
+        w_lin = w_lin.to(torch.bfloat16)  # bf16 h needs bf16 W (bf16 storage for both)
+    out_dtype = eq.EQTP_BF16 if args.out_bf16 else eq.EQTP_F32
     stream = torch.cuda.current_stream()
 
     sort_out = None
@@ -299,7 +307,7 @@ def main():
                                weight_mode=wl.weight_mode, r_cut=wl.r_cut, algo=args.algo, out=out)
             return
         eq.eqtp_conv_fused(vec, src, x, w, wl.lmax, row_ptr=row_ptr, dst=dst, path_set=wl.path_set,
-                           weight_mode=wl.weight_mode, r_cut=wl.r_cut, algo=args.algo, out=out)
+                           weight_mode=wl.weight_mode, r_cut=wl.r_cut, algo=args.algo, out=out, out_dtype=out_dtype)
 
     def linear():
         if w_lin is not None:
@@ -635,8 +643,9 @@ def main():
     node_kernel = wl.weight_mode == 0 and sorted_edges and wl.lmax <= 3 and args.algo in (0, 1)
     roofline = {"bound": "mfma" if node_kernel else "alu", "achieved": round(achieved_tflops, 3),
                 "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved_tflops / PEAK_FP32_TFLOPS, 4),
-                "traffic": measured_traffic(cfg_key, args.atom_order, args.unsorted, args.algo, args.path_set,
-                                            args.x_bf16, args.sort_edges)}
+                "traffic": None if args.out_bf16 else measured_traffic(cfg_key, args.atom_order, args.unsorted,
+                                                                        args.algo, args.path_set, args.x_bf16,
+                                                                        args.sort_edges)}
     if wl.weight_mode == 1:
         roofline["counted"] = ("2*nnz*C coupling flop (nnz=%d) + 2*8*P*C radial flop per edge, whichever form "
                                "the kernel computes them in" % nnz)
@@ -680,6 +689,8 @@ def main():
                    + (" (cell-sorted atom numbering)" if args.atom_order == "cell" else "")
                    + (" (SO(3) path set)" if args.path_set == "so3" else "")
                    + (" (bfloat16 node features)" if args.x_bf16 else "")
+                   + (" (bfloat16 output, packed bf16 atomics; the linear reads it in bf16)" if args.out_bf16
+                      else "")
                    + (" (step replayed as one HIP graph)" if args.graph else ""),
                    "atoms": wl.N, "edges": wl.E, "channels": wl.C, "lmax": wl.lmax, "paths": wl.P,
                    "coupling_nnz": nnz, "algo": args.algo},

@@ -128,10 +128,17 @@ typedef struct eqtp_conv_desc {
                           same [N, C, K] layout, 2 bytes each (eqtp_conv_fused at
                           lmax <= 3).  A descriptor whose struct_size ends before
                           this field is read as EQTP_F32. */
+  int32_t out_dtype;   /* EQTP_F32 (default) or EQTP_BF16: eqtp_conv_fused writes a
+                          bfloat16 out, summed with packed bf16 atomics (edges in
+                          any order, lmax <= 3; see eqtp_conv_fused).  A descriptor
+                          whose struct_size ends before this field is read as
+                          EQTP_F32. */
 } eqtp_conv_desc;
 
 /* struct_size of a descriptor without the x_dtype field (still accepted) */
 #define EQTP_CONV_DESC_SIZE_V1 36
+/* struct_size of a descriptor without the out_dtype field (still accepted) */
+#define EQTP_CONV_DESC_SIZE_V2 40
 
 /*
  * Fused convolution: spherical harmonics -> coupling with the source
@@ -161,6 +168,14 @@ typedef struct eqtp_conv_desc {
  *            (limit n pi / r_cut at r = 0).
  *   out      [N, C, K] fp32, 16-byte aligned, fully overwritten (nodes with
  *            no incoming edge get zeros); must not alias any input.
+ *            d->out_dtype = EQTP_BF16 (EQTP_EDGES_UNSORTED, lmax <= 3,
+ *            EQTP_ALGO_AUTO or EQTP_ALGO_EDGE_VALU; EQTP_EUNSUPPORTED
+ *            otherwise): out is [N, C, K] bfloat16, zero-filled, and every
+ *            edge's message -- computed in fp32 -- is rounded to bf16 (nearest
+ *            even) and added with packed two-element bf16 atomics, so each
+ *            partial sum is rounded to bf16 as well: half the atomic
+ *            operations and output bytes, at bf16 accuracy (the Batmobile
+ *            page's extensions, mixed precision).
  * Sorted edges: deterministic (bit-identical from run to run).  Unsorted
  * edges: summation order varies from run to run.
  * lmax 4..6 (EQTP_ALGO_EDGE_SO2): fixed weights and fp32 features only
@@ -169,7 +184,7 @@ typedef struct eqtp_conv_desc {
  * lmax <= 3 and C a multiple of 16 only.
  */
 int eqtp_conv_fused(const eqtp_conv_desc* d, int64_t N, int64_t E, const float* vec, const int32_t* src,
-                    const int32_t* dst, const int32_t* row_ptr, const void* x, const float* weights, float* out,
+                    const int32_t* dst, const int32_t* row_ptr, const void* x, const float* weights, void* out,
                     void* stream);
 
 /*
@@ -234,7 +249,7 @@ int eqtp_conv_fused_noalloc(const eqtp_conv_desc* d, int64_t N, int64_t E, const
  * or d->algo = EQTP_ALGO_EDGE_SO2, use the edge-aligned form (fixed weights
  * only, C = 128 up to lmax 4); otherwise the coupling form.
  *   messages [E, C, K] fp32, 16-byte aligned, fully overwritten; must not
- *            alias an input.  Deterministic.
+ *            alias an input (d->out_dtype must be EQTP_F32).  Deterministic.
  */
 int eqtp_conv_messages(const eqtp_conv_desc* d, int64_t N, int64_t E, const float* vec, const int32_t* src,
                        const float* x, const float* weights, float* messages, void* stream);
@@ -279,7 +294,8 @@ int eqtp_conv_messages(const eqtp_conv_desc* d, int64_t N, int64_t E, const floa
  * matrix cores (dL/dY_e = x[src_e] contracted with a per-node B_d built from
  * grad_out) unless d->algo = EQTP_ALGO_EDGE_VALU, which walks the coupling
  * per edge on the vector ALUs, or EQTP_ALGO_EDGE_SO2 (the edge-aligned form
- * above).  Radial weights ignore d->algo.
+ * above).  Radial weights ignore d->algo.  d->x_dtype and d->out_dtype must
+ * be EQTP_F32 (EQTP_EUNSUPPORTED for EQTP_BF16).
  */
 int eqtp_conv_backward(const eqtp_conv_desc* d, int64_t N, int64_t E, const float* vec, const int32_t* src,
                        const int32_t* dst, const int32_t* row_ptr, const float* x, const float* weights,
@@ -316,8 +332,9 @@ int eqtp_conv_backward(const eqtp_conv_desc* d, int64_t N, int64_t E, const floa
  * d->algo = EQTP_ALGO_EDGE_SO2): all three by one walk in the edge frame (C =
  * 128 only up to lmax 4); radial weights (lmax 0..3, C a multiple of 16,
  * n_basis 8, r_cut > 0): all three by one walk in the edge frame.
- * d: lmax, C, path_set, weight_mode, r_cut, n_basis, algo, x_dtype (must be
- * EQTP_F32); edge_order is ignored.  Errors as for eqtp_conv_backward.
+ * d: lmax, C, path_set, weight_mode, r_cut, n_basis, algo, x_dtype and
+ * out_dtype (both must be EQTP_F32); edge_order is ignored.  Errors as for
+ * eqtp_conv_backward.
  */
 int eqtp_conv_backward_by_source(const eqtp_conv_desc* d, int64_t N, int64_t E, const float* vec_s,
                                  const int32_t* dst_s, const int32_t* src_ptr, const float* x, const float* weights,

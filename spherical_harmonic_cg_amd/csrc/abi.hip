@@ -32,13 +32,23 @@ bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0
 bool valid_c(int C) { return C == 8 || C == 16 || C == 32 || C == 64 || C == 128; }
 
 static_assert(offsetof(eqtp_conv_desc, x_dtype) == EQTP_CONV_DESC_SIZE_V1, "descriptor layout");
+static_assert(offsetof(eqtp_conv_desc, out_dtype) == EQTP_CONV_DESC_SIZE_V2, "descriptor layout");
 
-// descriptor version check: the current size, or the size before x_dtype
+// descriptor version check: the current size, or the size before out_dtype, or before x_dtype
 bool desc_ok(const eqtp_conv_desc* d) {
-  return d && (d->struct_size == (int32_t)sizeof(eqtp_conv_desc) || d->struct_size == EQTP_CONV_DESC_SIZE_V1);
+  return d && (d->struct_size == (int32_t)sizeof(eqtp_conv_desc) || d->struct_size == EQTP_CONV_DESC_SIZE_V2 ||
+               d->struct_size == EQTP_CONV_DESC_SIZE_V1);
 }
 int desc_x_dtype(const eqtp_conv_desc* d) {
-  return d->struct_size >= (int32_t)sizeof(eqtp_conv_desc) ? d->x_dtype : EQTP_F32;
+  return d->struct_size >= EQTP_CONV_DESC_SIZE_V2 ? d->x_dtype : EQTP_F32;
+}
+int desc_out_dtype(const eqtp_conv_desc* d) {
+  return d->struct_size >= (int32_t)sizeof(eqtp_conv_desc) ? d->out_dtype : EQTP_F32;
+}
+// status for the entry points whose outputs are fp32 only
+int out_f32_only(const eqtp_conv_desc* d) {
+  const int o = desc_out_dtype(d);
+  return o == EQTP_F32 ? EQTP_OK : (o == EQTP_BF16 ? EQTP_EUNSUPPORTED : EQTP_EINVAL);
 }
 constexpr int64_t kMaxIndex = (int64_t(1) << 31) - 1;
 
@@ -179,11 +189,13 @@ namespace {
 
 // Validation and dispatch of the fused convolution; nothing is launched when launch is false.
 int conv_impl(const eqtp_conv_desc* d, int64_t N, int64_t E, const float* vec, const int32_t* src,
-              const int32_t* dst, const int32_t* row_ptr, const void* x, const float* weights, float* out,
+              const int32_t* dst, const int32_t* row_ptr, const void* x, const float* weights, void* out,
               void* stream, bool launch) {
   if (!desc_ok(d)) return EQTP_EINVAL;
   const int x_dtype = desc_x_dtype(d);
   if (x_dtype != EQTP_F32 && x_dtype != EQTP_BF16) return EQTP_EINVAL;
+  const int out_dtype = desc_out_dtype(d);
+  if (out_dtype != EQTP_F32 && out_dtype != EQTP_BF16) return EQTP_EINVAL;
   if (d->lmax < 0) return EQTP_EINVAL;
   if (d->lmax > eqtp::kSo2MaxL) return EQTP_EUNSUPPORTED;
   if (d->path_set != EQTP_PATHS_PARITY && d->path_set != EQTP_PATHS_SO3) return EQTP_EINVAL;
@@ -205,6 +217,11 @@ int conv_impl(const eqtp_conv_desc* d, int64_t N, int64_t E, const float* vec, c
   if (d->lmax > 3 && !use_so2) return EQTP_EUNSUPPORTED;
   if (use_so2 && (d->weight_mode != EQTP_W_FIXED || x_dtype != EQTP_F32)) return EQTP_EUNSUPPORTED;
   if (use_so2 && d->C == 128 && d->lmax > eqtp::kSo2MaxLC128) return EQTP_EUNSUPPORTED;
+  // bf16 output: packed bf16 atomics of the per-edge walk, edges in any order
+  if (out_dtype == EQTP_BF16 &&
+      (d->edge_order != EQTP_EDGES_UNSORTED || use_so2 || use_radial_so2 ||
+       (d->algo != EQTP_ALGO_AUTO && d->algo != EQTP_ALGO_EDGE_VALU)))
+    return EQTP_EUNSUPPORTED;
   if (d->weight_mode == EQTP_W_RADIAL) {
     if (!(d->r_cut > 0.0f)) return EQTP_EINVAL;
     if (d->n_basis != 8) return EQTP_EUNSUPPORTED;
@@ -240,7 +257,8 @@ int conv_impl(const eqtp_conv_desc* d, int64_t N, int64_t E, const float* vec, c
   a.x = static_cast<const float*>(x);
   a.x_bf16 = x_dtype == EQTP_BF16;
   a.w = weights;
-  a.out = out;
+  a.out = static_cast<float*>(out);
+  a.out_bf16 = out_dtype == EQTP_BF16;
   a.stream = (hipStream_t)stream;
   if (!launch) return EQTP_OK;
   if (use_radial_so2) return status_of(eqtp::launch_conv_so2_radial(a));
@@ -251,7 +269,7 @@ int conv_impl(const eqtp_conv_desc* d, int64_t N, int64_t E, const float* vec, c
 
 // conv_impl with debug mode's graph check between validation and launch
 int conv_checked(const eqtp_conv_desc* d, int64_t N, int64_t E, const float* vec, const int32_t* src,
-                 const int32_t* dst, const int32_t* row_ptr, const void* x, const float* weights, float* out,
+                 const int32_t* dst, const int32_t* row_ptr, const void* x, const float* weights, void* out,
                  void* stream) {
   int rc = conv_impl(d, N, E, vec, src, dst, row_ptr, x, weights, out, stream, false);
   if (rc != EQTP_OK || N == 0) return rc;
@@ -303,9 +321,10 @@ int conv_ws_impl(const eqtp_conv_desc* d, int64_t N, int64_t E, const float* vec
   int32_t* src_s = R[3];
   // the call as it runs after the grouping: dst-sorted edges
   eqtp_conv_desc ds{};
-  memcpy(&ds, d, (size_t)d->struct_size);  // a descriptor of the earlier size ends before x_dtype
+  memcpy(&ds, d, (size_t)d->struct_size);  // a descriptor of an earlier size ends before x_dtype or out_dtype
   ds.struct_size = (int32_t)sizeof(eqtp_conv_desc);
   ds.x_dtype = desc_x_dtype(d);
+  ds.out_dtype = desc_out_dtype(d);
   ds.edge_order = EQTP_EDGES_DST_SORTED;
   int rc = conv_impl(&ds, N, E, vec, src, nullptr, rp, x, weights, out, stream, false);
   if (rc != EQTP_OK) return rc;
@@ -322,7 +341,7 @@ int conv_ws_impl(const eqtp_conv_desc* d, int64_t N, int64_t E, const float* vec
 extern "C" {
 
 int eqtp_conv_fused(const eqtp_conv_desc* d, int64_t N, int64_t E, const float* vec, const int32_t* src,
-                    const int32_t* dst, const int32_t* row_ptr, const void* x, const float* weights, float* out,
+                    const int32_t* dst, const int32_t* row_ptr, const void* x, const float* weights, void* out,
                     void* stream) {
   return conv_checked(d, N, E, vec, src, dst, row_ptr, x, weights, out, stream);
 }
@@ -383,6 +402,7 @@ int eqtp_conv_messages(const eqtp_conv_desc* d, int64_t N, int64_t E, const floa
                        const float* x, const float* weights, float* messages, void* stream) {
   if (!desc_ok(d)) return EQTP_EINVAL;
   if (desc_x_dtype(d) != EQTP_F32) return desc_x_dtype(d) == EQTP_BF16 ? EQTP_EUNSUPPORTED : EQTP_EINVAL;
+  if (out_f32_only(d) != EQTP_OK) return out_f32_only(d);
   if (d->lmax < 0) return EQTP_EINVAL;
   if (d->lmax > eqtp::kSo2MaxL) return EQTP_EUNSUPPORTED;
   // lmax above 3 (or algo = EDGE_SO2): the edge-aligned form, fixed weights
@@ -434,6 +454,7 @@ int eqtp_conv_backward(const eqtp_conv_desc* d, int64_t N, int64_t E, const floa
                        const float* grad_out, float* grad_x, float* grad_w, float* grad_vec, void* stream) {
   if (!desc_ok(d)) return EQTP_EINVAL;
   if (desc_x_dtype(d) != EQTP_F32) return desc_x_dtype(d) == EQTP_BF16 ? EQTP_EUNSUPPORTED : EQTP_EINVAL;
+  if (out_f32_only(d) != EQTP_OK) return out_f32_only(d);
   if (d->lmax < 0) return EQTP_EINVAL;
   if (d->lmax > eqtp::kSo2MaxL) return EQTP_EUNSUPPORTED;
   if (d->path_set != EQTP_PATHS_PARITY && d->path_set != EQTP_PATHS_SO3) return EQTP_EINVAL;
@@ -499,6 +520,7 @@ int eqtp_conv_backward_by_source(const eqtp_conv_desc* d, int64_t N, int64_t E, 
                                  float* grad_vec, void* stream) {
   if (!desc_ok(d)) return EQTP_EINVAL;
   if (desc_x_dtype(d) != EQTP_F32) return desc_x_dtype(d) == EQTP_BF16 ? EQTP_EUNSUPPORTED : EQTP_EINVAL;
+  if (out_f32_only(d) != EQTP_OK) return out_f32_only(d);
   if (d->lmax < 0) return EQTP_EINVAL;
   if (d->lmax > eqtp::kSo2MaxL) return EQTP_EUNSUPPORTED;
   if (d->path_set != EQTP_PATHS_PARITY && d->path_set != EQTP_PATHS_SO3) return EQTP_EINVAL;

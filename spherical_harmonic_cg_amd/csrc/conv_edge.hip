@@ -22,6 +22,9 @@
 // radial basis of eqtp_device.hpp.
 // XB: the node features are bfloat16 in memory (widened exactly to fp32 on
 // load); every product and sum, and the atomics, stay fp32.
+// OB (unsorted edges only): out is bfloat16; each message is rounded to bf16
+// (nearest even) and added with packed two-element bf16 atomics, half the
+// atomic operations of the fp32 output.
 #include <type_traits>
 
 #include "eqtp_device.hpp"
@@ -131,7 +134,9 @@ struct EdgeMsg {
   }
 };
 
-template <int L, int PS, int C, bool RADIAL, bool ATOMIC, bool XB>
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+template <int L, int PS, int C, bool RADIAL, bool ATOMIC, bool XB, bool OB = false>
 __global__ __launch_bounds__(EdgeCfg<C>::THREADS) void conv_edge_kernel(
     int N, int E, const int* __restrict__ row_ptr, const float* __restrict__ vec, const int* __restrict__ src,
     const int* __restrict__ dst, const typename EdgeMsg<L, PS, C, RADIAL, XB>::XT* __restrict__ x,
@@ -214,11 +219,31 @@ __global__ __launch_bounds__(EdgeCfg<C>::THREADS) void conv_edge_kernel(
         for (int k = 0; k < K; ++k) xw[(g * C + cl + j * Cfg::CL) * K + k] = acc[j][k];
       if (cl == 0) xdst[wv][g] = valid ? clamp_index(dst[e], N) : -1;  // -1: no edge in this slot
       wave_lds_sync();
+      if constexpr (OB) {
+        // lane pairs of consecutive floats (MSG is even, so a pair never straddles two messages): one
+        // packed atomic covers 4 bytes of out, an instruction 256 contiguous bytes
+        constexpr int NPAIR = kWave * NI / 2;
+        bf16x2_t* const ob = reinterpret_cast<bf16x2_t*>(out);
 #pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        const int f = kWave * i + lane;      // float index in the wave's messages
-        const int d = xdst[wv][f / MSG];
-        if (d >= 0) unsafeAtomicAdd(out + (size_t)d * MSG + f % MSG, xw[f]);  // hardware fp32 atomic
+        for (int i = 0; i < (NPAIR + kWave - 1) / kWave; ++i) {
+          const int pr = kWave * i + lane;
+          if (pr < NPAIR) {
+            const int f = 2 * pr;
+            const int d = xdst[wv][f / MSG];
+            if (d >= 0) {
+              const bf16x2_t v = {to_bf16(xw[f]), to_bf16(xw[f + 1])};
+              __builtin_amdgcn_global_atomic_fadd_v2bf16(
+                  (__attribute__((address_space(1))) bf16x2_t*)(ob + ((size_t)d * MSG + f % MSG) / 2), v);
+            }
+          }
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+          const int f = kWave * i + lane;      // float index in the wave's messages
+          const int d = xdst[wv][f / MSG];
+          if (d >= 0) unsafeAtomicAdd(out + (size_t)d * MSG + f % MSG, xw[f]);  // hardware fp32 atomic
+        }
       }
       wave_lds_sync();
     }
@@ -349,21 +374,21 @@ __global__ __launch_bounds__(EdgeCfg<C>::THREADS) void probe_edge_kernel(int N, 
   }
 }
 
-template <int L, int PS, int C, bool RADIAL, bool ATOMIC, bool XB>
+template <int L, int PS, int C, bool RADIAL, bool ATOMIC, bool XB, bool OB = false>
 static hipError_t launch_edge_t(const ConvArgs& a) {
   using Cfg = EdgeCfg<C>;
   using XT = typename EdgeMsg<L, PS, C, RADIAL, XB>::XT;
   const XT* x = reinterpret_cast<const XT*>(a.x);
   const float inv_rc = RADIAL ? 1.0f / a.r_cut : 0.0f;
   if constexpr (ATOMIC) {
-    if (a.N > 0) {
-      hipError_t err = launch_fill_zero(a.out, a.N * a.C * num_comp(L), a.stream);
+    if (a.N > 0) {  // zero bits are 0.0 in either type; a bf16 out is N C K / 2 floats (C is even)
+      hipError_t err = launch_fill_zero(a.out, a.N * a.C * num_comp(L) / (OB ? 2 : 1), a.stream);
       if (err != hipSuccess) return err;
     }
     if (a.E == 0) return hipSuccess;
     const long long per_block = (long long)Cfg::WAVES * Cfg::EPW;
     const unsigned blocks = (unsigned)((a.E + per_block - 1) / per_block);
-    hipLaunchKernelGGL((conv_edge_kernel<L, PS, C, RADIAL, true, XB>), dim3(blocks), dim3(Cfg::THREADS), 0,
+    hipLaunchKernelGGL((conv_edge_kernel<L, PS, C, RADIAL, true, XB, OB>), dim3(blocks), dim3(Cfg::THREADS), 0,
                        a.stream, (int)a.N, (int)a.E, a.row_ptr, a.vec, a.src, a.dst, x, a.w, a.out, inv_rc);
   } else {
     if (a.N == 0) return hipSuccess;
@@ -377,6 +402,8 @@ static hipError_t launch_edge_t(const ConvArgs& a) {
 template <int L, int PS, int C, bool XB>
 static hipError_t dispatch_edge_mode_x(const ConvArgs& a) {
   const bool radial = a.weight_mode == 1, atomic = a.edge_order == 1;
+  if (atomic && a.out_bf16)
+    return radial ? launch_edge_t<L, PS, C, true, true, XB, true>(a) : launch_edge_t<L, PS, C, false, true, XB, true>(a);
   if (radial)
     return atomic ? launch_edge_t<L, PS, C, true, true, XB>(a) : launch_edge_t<L, PS, C, true, false, XB>(a);
   return atomic ? launch_edge_t<L, PS, C, false, true, XB>(a) : launch_edge_t<L, PS, C, false, false, XB>(a);

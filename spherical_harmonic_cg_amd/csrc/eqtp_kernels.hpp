@@ -13,6 +13,7 @@ struct ConvArgs {
   int lmax, C, path_set, weight_mode, edge_order;
   int x_bf16 = 0;     // x holds bfloat16 features
   int messages = 0;   // edge-aligned kernel: per-edge messages [E, C, K] into out instead of the sum
+  bool out_bf16 = false;  // out holds bfloat16 (edges in any order: packed bf16 atomics)
   float r_cut;
   const float* vec;
   const int32_t* src;

@@ -42,7 +42,7 @@ class _ConvDesc(ctypes.Structure):
     _fields_ = [("struct_size", ctypes.c_int32), ("lmax", ctypes.c_int32), ("C", ctypes.c_int32),
                 ("path_set", ctypes.c_int32), ("weight_mode", ctypes.c_int32), ("edge_order", ctypes.c_int32),
                 ("algo", ctypes.c_int32), ("r_cut", ctypes.c_float), ("n_basis", ctypes.c_int32),
-                ("x_dtype", ctypes.c_int32)]
+                ("x_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32)]
 
 
 class _InteractionDesc(ctypes.Structure):
@@ -172,7 +172,8 @@ def eqtp_sh(vec, lmax: int, Y=None):
     return Y
 
 
-def _conv_args(vec, src, x, weights, lmax, row_ptr, dst, path_set, weight_mode, r_cut, n_basis, algo, out):
+def _conv_args(vec, src, x, weights, lmax, row_ptr, dst, path_set, weight_mode, r_cut, n_basis, algo, out,
+               out_dtype=EQTP_F32):
     """Checks the fused convolution's tensors; returns (descriptor, N, E, out)."""
     import torch
 
@@ -199,26 +200,28 @@ def _conv_args(vec, src, x, weights, lmax, row_ptr, dst, path_set, weight_mode, 
     wshape = (P, C) if weight_mode == EQTP_W_FIXED else (n_basis, P * C)
     if tuple(weights.shape) != wshape:
         raise ValueError("weights has shape %s, expected %s" % (tuple(weights.shape), wshape))
+    odt = torch.bfloat16 if out_dtype == EQTP_BF16 else torch.float32
     if out is None:
-        out = torch.empty((N, C, K), dtype=torch.float32, device=x.device)
-    _check(out, "out", torch.float32, (N, C, K))
+        out = torch.empty((N, C, K), dtype=odt, device=x.device)
+    _check(out, "out", odt, (N, C, K))
     d = _ConvDesc(ctypes.sizeof(_ConvDesc), lmax, C, path_set, weight_mode, order, algo, float(r_cut), n_basis,
-                  x_dtype)
+                  x_dtype, out_dtype)
     return d, N, E, out
 
 
 def eqtp_conv_fused(vec, src, x, weights, lmax: int, row_ptr=None, dst=None, path_set: int = EQTP_PATHS_PARITY,
                     weight_mode: int = EQTP_W_FIXED, r_cut: float = 0.0, n_basis: int = 8,
-                    algo: int = EQTP_ALGO_AUTO, out=None):
+                    algo: int = EQTP_ALGO_AUTO, out=None, out_dtype: int = EQTP_F32):
     """out [N, C, K] = fused harmonics -> coupling -> sum into dst.
 
     Give ``row_ptr`` [N+1] for dst-sorted edges, or ``dst`` [E] for any order
     (atomic accumulation).  ``weights`` is [P, C] (fixed) or [8, P*C] (radial).
     ``x`` is float32, or bfloat16 (lmax <= 3, any edge order or weights); ``out``
-    is float32.
+    is float32, or bfloat16 with ``out_dtype=EQTP_BF16`` (edges in any order:
+    packed bf16 atomics).
     """
     d, N, E, out = _conv_args(vec, src, x, weights, lmax, row_ptr, dst, path_set, weight_mode, r_cut, n_basis, algo,
-                              out)
+                              out, out_dtype)
     rc = load_library().eqtp_conv_fused(ctypes.byref(d), N, E, _ptr(vec), _ptr(src), _ptr(dst), _ptr(row_ptr),
                                         _ptr(x), _ptr(weights), _ptr(out), _stream())
     _raise(rc, "eqtp_conv_fused")

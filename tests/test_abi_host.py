@@ -103,10 +103,11 @@ def test_debug_switch_and_environment():
 
 
 def _desc(e, **kw):
-    d = dict(lmax=3, C=64, path_set=0, weight_mode=0, edge_order=0, algo=0, r_cut=0.0, n_basis=8, x_dtype=0)
+    d = dict(lmax=3, C=64, path_set=0, weight_mode=0, edge_order=0, algo=0, r_cut=0.0, n_basis=8, x_dtype=0,
+             out_dtype=0)
     d.update(kw)
     return e._ConvDesc(ctypes.sizeof(e._ConvDesc), d["lmax"], d["C"], d["path_set"], d["weight_mode"],
-                       d["edge_order"], d["algo"], d["r_cut"], d["n_basis"], d["x_dtype"])
+                       d["edge_order"], d["algo"], d["r_cut"], d["n_basis"], d["x_dtype"], d["out_dtype"])
 
 
 FAKE = ctypes.c_void_p(0x10000)  # never dereferenced: every call below is rejected first
@@ -121,6 +122,10 @@ NULL = ctypes.c_void_p(0)
     (dict(weight_mode=2), 1), (dict(edge_order=5), 1), (dict(algo=9), 1),
     (dict(weight_mode=1, r_cut=0.0), 1), (dict(weight_mode=1, r_cut=5.0, n_basis=6), 2),
     (dict(weight_mode=1, r_cut=5.0, algo=1), 2), (dict(edge_order=1, algo=1), 2),
+    # bf16 output: edges in any order on the per-edge walk only
+    (dict(out_dtype=1), 2), (dict(out_dtype=1, edge_order=1, lmax=4), 2), (dict(out_dtype=1, edge_order=1, algo=3), 2),
+    (dict(out_dtype=1, edge_order=1, algo=1), 2), (dict(out_dtype=1, weight_mode=1, r_cut=5.0), 2),
+    (dict(out_dtype=2, edge_order=1), 1), (dict(out_dtype=-1), 1),
 ])
 def test_conv_descriptor_validation(kw, want):
     e = _lib()
@@ -227,7 +232,7 @@ def test_conv_messages_validation():
 def test_descriptor_versions_and_feature_dtype():
     e = _lib()
     lib = e.load_library()
-    assert ctypes.sizeof(e._ConvDesc) == 40
+    assert ctypes.sizeof(e._ConvDesc) == 44
     conv = lambda d, **kw: lib.eqtp_conv_fused(ctypes.byref(d), 10, 20, FAKE, FAKE, kw.get("dst", NULL),
                                                kw.get("rp", FAKE), FAKE, FAKE, FAKE, NULL)
     v1 = _desc(e, lmax=7)
@@ -244,6 +249,25 @@ def test_descriptor_versions_and_feature_dtype():
     assert lib.eqtp_conv_messages(ctypes.byref(bf), 10, 20, FAKE, FAKE, FAKE, FAKE, FAKE, NULL) == 2
     assert lib.eqtp_conv_backward(ctypes.byref(bf), 10, 20, FAKE, FAKE, NULL, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                                   FAKE, NULL) == 2
+    # size 40: a descriptor from before out_dtype -- x_dtype is read, out_dtype is not
+    v2 = _desc(e, lmax=7, out_dtype=9)
+    v2.struct_size = 40
+    assert conv(v2) == 2
+    v2.x_dtype = 7
+    assert conv(v2) == 1
+    assert conv(_desc(e, lmax=7, out_dtype=9)) == 1                             # current size: out_dtype read
+    # bf16 output: the fused convolution with edges in any order only
+    ob = _desc(e, out_dtype=1)
+    assert lib.eqtp_conv_messages(ctypes.byref(ob), 10, 20, FAKE, FAKE, FAKE, FAKE, FAKE, NULL) == 2
+    assert lib.eqtp_conv_backward(ctypes.byref(ob), 10, 20, FAKE, FAKE, NULL, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                  FAKE, NULL) == 2
+    assert lib.eqtp_conv_backward_by_source(ctypes.byref(ob), 10, 20, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                            FAKE, FAKE, FAKE, NULL) == 2
+    ob5 = _desc(e, out_dtype=5)
+    assert lib.eqtp_conv_messages(ctypes.byref(ob5), 10, 20, FAKE, FAKE, FAKE, FAKE, FAKE, NULL) == 1
+    ws = _desc(e, out_dtype=1, edge_order=1)  # the workspace call groups the edges: dst-sorted, so fp32 only
+    assert lib.eqtp_conv_fused_ws(ctypes.byref(ws), 10, 20, FAKE, FAKE, FAKE, NULL, FAKE, FAKE, FAKE, FAKE,
+                                  1 << 20, NULL) == 2
 
 
 def test_sort_edges_validation():
