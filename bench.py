@@ -423,10 +423,11 @@ def main():
             rows = torch.empty(E_, dtype=torch.int32, device=dev) if "row_ptr" in bkw else None
             grp = (torch.empty(wl.N + 1, dtype=torch.int32, device=dev), torch.empty(E_, dtype=torch.int32, device=dev),
                    torch.empty((E_, 3), dtype=torch.float32, device=dev), torch.empty(E_, dtype=torch.int32, device=dev))
+            sws = torch.empty(max(16, eq.eqtp_sort_workspace_bytes(wl.N, E_)), dtype=torch.uint8, device=dev)
 
             def bwd_rad_src():
                 d_ = eq.eqtp_edge_rows(bkw["row_ptr"], E_, out=rows) if "row_ptr" in bkw else bkw["dst"]
-                eq.eqtp_sort_edges(bsrc, wl.N, vec=bvec, src=d_, out=grp)
+                eq.eqtp_sort_edges_stable(bsrc, wl.N, vec=bvec, src=d_, out=grp, workspace=sws)
                 eq.eqtp_conv_backward_by_source(grp[2], grp[3], grp[0], x, w, gout, wl.lmax, path_set=wl.path_set,
                                                 need_vec=True, perm=grp[1], weight_mode=1, r_cut=wl.r_cut)
 
@@ -448,7 +449,7 @@ def main():
             sms, _ = timed_r(bwd_rad_src)
             backward = {"ms": round(sms, 5), "edges_per_s": round(wl.E / (sms * 1e-3), 1), "launches": kb,
                         "what": "grad_x, grad_W [8, P*C] and grad_vec of the radial-weight conv: source grouping "
-                                "on the GPU (eqtp_edge_rows + eqtp_sort_edges), then eqtp_conv_backward_by_source "
+                                "on the GPU (eqtp_edge_rows + eqtp_sort_edges_stable), then eqtp_conv_backward_by_source "
                                 "with EQTP_W_RADIAL (one pass, grad_x without atomics)",
                         "edge_path_ms": round(rms, 5),
                         "edge_path_what": "eqtp_conv_backward with EQTP_W_RADIAL on the edges as given (zero fills "
@@ -477,10 +478,11 @@ def main():
                 rows = torch.empty(E_, dtype=torch.int32, device=dev)
             grp = (torch.empty(wl.N + 1, dtype=torch.int32, device=dev), torch.empty(E_, dtype=torch.int32, device=dev),
                    torch.empty((E_, 3), dtype=torch.float32, device=dev), torch.empty(E_, dtype=torch.int32, device=dev))
+            sws = torch.empty(max(16, eq.eqtp_sort_workspace_bytes(wl.N, E_)), dtype=torch.uint8, device=dev)
 
             def bwd_src():
                 d_ = eq.eqtp_edge_rows(bkw["row_ptr"], E_, out=rows) if "row_ptr" in bkw else bkw["dst"]
-                eq.eqtp_sort_edges(bsrc, wl.N, vec=bvec, src=d_, out=grp)
+                eq.eqtp_sort_edges_stable(bsrc, wl.N, vec=bvec, src=d_, out=grp, workspace=sws)
                 eq.eqtp_conv_backward_by_source(grp[2], grp[3], grp[0], x, w, gout, wl.lmax, path_set=wl.path_set)
                 eq.eqtp_conv_backward(bvec, bsrc, x, w, gout, wl.lmax, path_set=wl.path_set, need_x=False,
                                       need_w=False, need_vec=True, **bkw)
@@ -502,7 +504,7 @@ def main():
             if wl.lmax > 3:
                 def bwd_so2_src():
                     d_ = eq.eqtp_edge_rows(bkw["row_ptr"], E_, out=rows) if "row_ptr" in bkw else bkw["dst"]
-                    eq.eqtp_sort_edges(bsrc, wl.N, vec=bvec, src=d_, out=grp)
+                    eq.eqtp_sort_edges_stable(bsrc, wl.N, vec=bvec, src=d_, out=grp, workspace=sws)
                     eq.eqtp_conv_backward_by_source(grp[2], grp[3], grp[0], x, w, gout, wl.lmax,
                                                     path_set=wl.path_set, need_vec=True, perm=grp[1])
 
@@ -510,7 +512,7 @@ def main():
                 sms, _ = timed(bwd_so2_src)
                 backward = {"ms": round(sms, 5), "edges_per_s": round(wl.E / (sms * 1e-3), 1), "launches": kb,
                             "what": "grad_x, grad_w and grad_vec of the conv in the edge-aligned form: source "
-                                    "grouping on the GPU (eqtp_edge_rows + eqtp_sort_edges), then "
+                                    "grouping on the GPU (eqtp_edge_rows + eqtp_sort_edges_stable), then "
                                     "eqtp_conv_backward_by_source (one pass, grad_x without atomics)",
                             "edge_path_ms": round(oms, 5),
                             "edge_path_what": "eqtp_conv_backward on the edges as given (zero fills + one kernel, "
@@ -523,7 +525,7 @@ def main():
                 oms, _ = timed(bwd_so2)
                 backward = {"ms": round(sms, 5), "edges_per_s": round(wl.E / (sms * 1e-3), 1), "launches": kb,
                             "what": "grad_x, grad_w and grad_vec of the conv: source grouping on the GPU "
-                                    "(eqtp_edge_rows + eqtp_sort_edges), eqtp_conv_backward_by_source (grad_x, "
+                                    "(eqtp_edge_rows + eqtp_sort_edges_stable), eqtp_conv_backward_by_source (grad_x, "
                                     "grad_w), eqtp_conv_backward (grad_vec)",
                             "edge_path_ms": round(bms, 5),
                             "edge_path_what": "all three from eqtp_conv_backward (fp32 atomics for grad_x)",

@@ -374,6 +374,26 @@ int eqtp_sort_edges(int64_t N, int64_t E, const int32_t* dst, const float* vec, 
                     int32_t* perm, float* vec_sorted, int32_t* src_sorted, void* stream);
 
 /*
+ * eqtp_sort_edges with every row in input order: a stable LSD radix sort of
+ * (key, edge index) on the GPU (digits of up to 9 bits, per-tile digit
+ * counts in LDS, one scan per digit, ranks from wave ballots), so all
+ * outputs, perm included, are unique and the same from call to call -- what
+ * makes sums taken in the grouped order deterministic (grad_x of
+ * eqtp_conv_backward_by_source, which sums each source row's edges in that
+ * order and writes it once).  Same arguments, layouts
+ * and errors as eqtp_sort_edges, plus:
+ *   workspace        device memory of at least eqtp_sort_workspace_bytes(N, E)
+ *                    bytes (about 12 bytes per edge plus the digit counts),
+ *                    16-byte aligned, owned by the caller; its contents on
+ *                    entry do not matter.  May be NULL when E = 0.
+ *   workspace_bytes  its size (EQTP_EINVAL when short).
+ */
+int64_t eqtp_sort_workspace_bytes(int64_t N, int64_t E);
+int eqtp_sort_edges_stable(int64_t N, int64_t E, const int32_t* dst, const float* vec, const int32_t* src,
+                           int32_t* row_ptr, int32_t* perm, float* vec_sorted, int32_t* src_sorted, void* workspace,
+                           int64_t workspace_bytes, void* stream);
+
+/*
  * Per-l channel linear (channel mixing inside each irrep, no bias), the
  * channel-wise mixing that follows the convolution: the Batmobile page names
  * no such layer; its form (a C x C matrix per degree l, applied to every m of

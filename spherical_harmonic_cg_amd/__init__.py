@@ -10,5 +10,6 @@ from .eqtp import (EQTP_ALGO_AUTO, EQTP_ALGO_EDGE_SO2, EQTP_ALGO_EDGE_VALU, EQTP
                    eqtp_check_graph, eqtp_conv_backward_by_source, eqtp_conv_fused, eqtp_conv_fused_noalloc, eqtp_conv_fused_ws,
                    eqtp_conv_messages,
                    eqtp_conv_workspace_bytes, eqtp_edge_rows, eqtp_interaction, eqtp_interaction_workspace_bytes, eqtp_linear,
-                   eqtp_num_paths, eqtp_path_table, eqtp_set_debug, eqtp_sh, eqtp_sort_edges, eqtp_status_string,
+                   eqtp_num_paths, eqtp_path_table, eqtp_set_debug, eqtp_sh, eqtp_sort_edges, eqtp_sort_edges_stable, eqtp_sort_workspace_bytes,
+                   eqtp_status_string,
                    eqtp_test_segment_probe, load_library)

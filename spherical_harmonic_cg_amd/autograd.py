@@ -23,12 +23,13 @@ from . import eqtp as _eq
 def group_by_source(N: int, src, vec, dst=None, row_ptr=None, with_perm: bool = False):
     """(src_ptr [N+1], vec_s [E,3], dst_s [E]) and, with_perm, perm [E] (the
     caller's index of each grouped edge): the edges grouped by source node (the
-    input of eqtp_conv_backward_by_source).  Destinations come from dst, or from
-    a dst-sorted CSR (row_ptr)."""
+    input of eqtp_conv_backward_by_source), each source's edges in input order,
+    so grad_x, summed per source over them, is the same from call to call.
+    Destinations come from dst, or from a dst-sorted CSR (row_ptr)."""
     E = src.shape[0]
     if dst is None:
         dst = _eq.eqtp_edge_rows(row_ptr, E)
-    src_ptr, perm, vec_s, dst_s = _eq.eqtp_sort_edges(src, N, vec=vec, src=dst)
+    src_ptr, perm, vec_s, dst_s = _eq.eqtp_sort_edges_stable(src, N, vec=vec, src=dst)
     return (src_ptr, vec_s, dst_s, perm) if with_perm else (src_ptr, vec_s, dst_s)
 
 

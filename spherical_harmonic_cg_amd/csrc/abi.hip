@@ -621,6 +621,59 @@ int eqtp_sort_edges(int64_t N, int64_t E, const int32_t* dst, const float* vec, 
                                            (hipStream_t)stream));
 }
 
+}  // extern "C"
+
+namespace {
+// Workspace of eqtp_sort_edges_stable: the radix sort's second key buffer, both ping-pong buffers of the
+// other pass and its digit counts, each region 256-byte aligned (the caller's perm receives the edge
+// indices of the last pass)
+struct SortWs {
+  size_t keys_a, keys_b, vals_b, hist, total;
+};
+SortWs sort_ws_layout(int64_t E) {
+  auto al = [](int64_t b) { return (size_t)((b + 255) & ~(int64_t)255); };
+  SortWs w;
+  w.keys_a = 0;
+  w.keys_b = al(E * 4);
+  w.vals_b = w.keys_b + al(E * 4);
+  w.hist = w.vals_b + al(E * 4);
+  w.total = w.hist + al(eqtp::radix_hist_entries(E) * 4);
+  return w;
+}
+}  // namespace
+
+extern "C" {
+
+int64_t eqtp_sort_workspace_bytes(int64_t N, int64_t E) {
+  if (N < 0 || E < 0 || N > kMaxIndex - 1 || E > kMaxIndex) return -EQTP_EINVAL;
+  return (int64_t)sort_ws_layout(E).total;
+}
+
+int eqtp_sort_edges_stable(int64_t N, int64_t E, const int32_t* dst, const float* vec, const int32_t* src,
+                           int32_t* row_ptr, int32_t* perm, float* vec_sorted, int32_t* src_sorted, void* workspace,
+                           int64_t workspace_bytes, void* stream) {
+  if (N < 0 || E < 0 || N > kMaxIndex - 1 || E > kMaxIndex) return EQTP_EINVAL;
+  if (E > 0 && N == 0) return EQTP_EINVAL;
+  if (!row_ptr || !aligned4(row_ptr)) return EQTP_EINVAL;
+  const SortWs L = sort_ws_layout(E);
+  if (E > 0) {
+    if (!dst || !perm || !aligned4(dst) || !aligned4(perm)) return EQTP_EINVAL;
+    if (vec_sorted && (!vec || !aligned4(vec) || !aligned4(vec_sorted))) return EQTP_EINVAL;
+    if (src_sorted && (!src || !aligned4(src) || !aligned4(src_sorted))) return EQTP_EINVAL;
+    if (!workspace || !aligned16(workspace) || workspace_bytes < (int64_t)L.total) return EQTP_EINVAL;
+    const int chk = debug_check(N, E, nullptr, src_sorted ? src : nullptr, dst, vec_sorted ? vec : nullptr, nullptr,
+                                stream);
+    if (chk != EQTP_OK) return chk;
+  }
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  int32_t* keys_a = E > 0 ? reinterpret_cast<int32_t*>(ws + L.keys_a) : nullptr;
+  int32_t* keys_b = E > 0 ? reinterpret_cast<int32_t*>(ws + L.keys_b) : nullptr;
+  int32_t* vals_b = E > 0 ? reinterpret_cast<int32_t*>(ws + L.vals_b) : nullptr;
+  int32_t* hist = E > 0 ? reinterpret_cast<int32_t*>(ws + L.hist) : nullptr;
+  return status_of(eqtp::launch_sort_edges_stable(N, E, dst, vec, src, row_ptr, keys_a, perm, keys_b, vals_b, hist,
+                                                  vec_sorted, src_sorted, (hipStream_t)stream));
+}
+
 int eqtp_linear(int64_t N, int C, int lmax, int dtype, const void* h, const void* W, float* out, void* stream) {
   if (lmax < 0 || C <= 0 || N < 0 || N > kMaxIndex) return EQTP_EINVAL;
   if (lmax > eqtp::kSo2MaxL || !valid_c(C)) return EQTP_EUNSUPPORTED;

@@ -98,8 +98,8 @@ hipError_t launch_sort_edges(int64_t N, int64_t E, const int32_t* dst, const flo
 // grouping by destination with each row in input order: staged [E] int32 scratch; vec_out, src_out required
 // stable grouping by destination (LSD radix sort) for the workspace convolution: row_ptr [N+1], the sorted
 // keys and edge indices end in keys_a / vals_a (keys_b / vals_b: the other buffers of the passes, hist:
-// radix_hist_entries(E) ints); vec_out [E,3] / src_out [E] in that order (vec_out may span keys_a..vals_b
-// when they are laid out in that order and hold 12 E bytes; it must not overlap vals_a)
+// radix_hist_entries(E) ints); vec_out [E,3] / src_out [E] in that order, each may be null (vec_out may
+// span keys_a..vals_b when they are laid out in that order and hold 12 E bytes; it must not overlap vals_a)
 int64_t radix_hist_entries(int64_t E);
 hipError_t launch_sort_edges_stable(int64_t N, int64_t E, const int32_t* dst, const float* vec, const int32_t* src,
                                     int32_t* row_ptr, int32_t* keys_a, int32_t* vals_a, int32_t* keys_b,

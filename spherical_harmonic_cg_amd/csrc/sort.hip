@@ -330,12 +330,13 @@ __global__ __launch_bounds__(256) void gather_sorted_kernel(const int* __restric
   const int i = blockIdx.x * blockDim.x + threadIdx.x;  // one edge per thread (the grid covers E)
   if (i >= E) return;
   const int e = clamp_index(vals[i], E);
-  const float a = vec[3 * (size_t)e], b = vec[3 * (size_t)e + 1], c = vec[3 * (size_t)e + 2];
-  const int s = src[e];
-  vec_out[3 * (size_t)i] = a;
-  vec_out[3 * (size_t)i + 1] = b;
-  vec_out[3 * (size_t)i + 2] = c;
-  src_out[i] = s;
+  if (vec_out != nullptr) {
+    const float a = vec[3 * (size_t)e], b = vec[3 * (size_t)e + 1], c = vec[3 * (size_t)e + 2];
+    vec_out[3 * (size_t)i] = a;
+    vec_out[3 * (size_t)i + 1] = b;
+    vec_out[3 * (size_t)i + 2] = c;
+  }
+  if (src_out != nullptr) src_out[i] = src[e];
 }
 
 hipError_t launch_sort_edges_stable(int64_t N, int64_t E, const int32_t* dst, const float* vec, const int32_t* src,
@@ -371,8 +372,9 @@ hipError_t launch_sort_edges_stable(int64_t N, int64_t E, const int32_t* dst, co
   }
   hipLaunchKernelGGL(rows_from_sorted_kernel, dim3(grid_for(E + 1)), dim3(256), 0, stream, keys_a, (int)E, (int)N,
                      row_ptr);
-  hipLaunchKernelGGL(gather_sorted_kernel, dim3((unsigned)((E + 255) / 256)), dim3(256), 0, stream, vals_a, (int)E,
-                     vec, src, vec_out, src_out);
+  if (vec_out != nullptr || src_out != nullptr)
+    hipLaunchKernelGGL(gather_sorted_kernel, dim3((unsigned)((E + 255) / 256)), dim3(256), 0, stream, vals_a,
+                       (int)E, vec, src, vec_out, src_out);
   return hipGetLastError();
 }
 

@@ -28,6 +28,7 @@ EQTP_F32, EQTP_BF16, EQTP_F32_BF16 = 0, 1, 2
 EXPORTED = ("eqtp_num_paths", "eqtp_path_table", "eqtp_sh", "eqtp_conv_fused", "eqtp_conv_workspace_bytes",
             "eqtp_conv_fused_ws", "eqtp_conv_fused_noalloc", "eqtp_conv_messages",
             "eqtp_conv_backward", "eqtp_conv_backward_by_source", "eqtp_edge_rows", "eqtp_sort_edges",
+            "eqtp_sort_workspace_bytes", "eqtp_sort_edges_stable",
             "eqtp_linear", "eqtp_interaction_workspace_bytes", "eqtp_interaction",
             "eqtp_status_string", "eqtp_check_graph", "eqtp_set_debug", "eqtp_test_segment_probe")
 
@@ -88,6 +89,10 @@ def load_library(path: str = LIB_PATH):
             lib.eqtp_edge_rows.restype = i32
             lib.eqtp_sort_edges.argtypes = [i64, i64] + [vp] * 8
             lib.eqtp_sort_edges.restype = i32
+            lib.eqtp_sort_workspace_bytes.argtypes = [i64, i64]
+            lib.eqtp_sort_workspace_bytes.restype = i64
+            lib.eqtp_sort_edges_stable.argtypes = [i64, i64] + [vp] * 8 + [i64, vp]
+            lib.eqtp_sort_edges_stable.restype = i32
             lib.eqtp_linear.argtypes = [i64, i32, i32, i32, vp, vp, vp, vp]
             lib.eqtp_linear.restype = i32
             lib.eqtp_interaction_workspace_bytes.argtypes = [ctypes.POINTER(_InteractionDesc), i64, i64]
@@ -453,6 +458,47 @@ def eqtp_sort_edges(dst, N: int, vec=None, src=None, out=None):
                                         _ptr(vs if vec is not None else None), _ptr(ss if src is not None else None),
                                         _stream())
     _raise(rc, "eqtp_sort_edges")
+    return row_ptr, perm, (vs if vec is not None else None), (ss if src is not None else None)
+
+
+def eqtp_sort_workspace_bytes(N: int, E: int) -> int:
+    """Device workspace eqtp_sort_edges_stable needs (bytes)."""
+    n = load_library().eqtp_sort_workspace_bytes(N, E)
+    if n < 0:
+        raise EqtpError(-n, "eqtp_sort_workspace_bytes")
+    return int(n)
+
+
+def eqtp_sort_edges_stable(dst, N: int, vec=None, src=None, out=None, workspace=None):
+    """eqtp_sort_edges with every row in input order (stable radix sort): the same four outputs, unique
+    and identical from call to call.  ``workspace`` is a uint8 CUDA tensor of at least
+    eqtp_sort_workspace_bytes bytes (allocated here if None)."""
+    import torch
+
+    _check(dst, "dst", torch.int32)
+    E = dst.shape[0]
+    dev = dst.device
+    if out is None:
+        out = (torch.empty(N + 1, dtype=torch.int32, device=dev), torch.empty(E, dtype=torch.int32, device=dev),
+               torch.empty_like(vec) if vec is not None else None, torch.empty_like(src) if src is not None else None)
+    row_ptr, perm, vs, ss = out
+    _check(row_ptr, "row_ptr", torch.int32, (N + 1,))
+    _check(perm, "perm", torch.int32, (E,))
+    if vec is not None:
+        _check(vec, "vec", torch.float32, (E, 3))
+        _check(vs, "vec_sorted", torch.float32, (E, 3))
+    if src is not None:
+        _check(src, "src", torch.int32, (E,))
+        _check(ss, "src_sorted", torch.int32, (E,))
+    need = eqtp_sort_workspace_bytes(N, E)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    _check(workspace, "workspace", torch.uint8)
+    rc = load_library().eqtp_sort_edges_stable(N, E, _ptr(dst), _ptr(vec), _ptr(src), _ptr(row_ptr), _ptr(perm),
+                                               _ptr(vs if vec is not None else None),
+                                               _ptr(ss if src is not None else None), _ptr(workspace),
+                                               workspace.numel(), _stream())
+    _raise(rc, "eqtp_sort_edges_stable")
     return row_ptr, perm, (vs if vec is not None else None), (ss if src is not None else None)
 
 

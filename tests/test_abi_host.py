@@ -270,6 +270,27 @@ def test_descriptor_versions_and_feature_dtype():
                                   1 << 20, NULL) == 2
 
 
+def test_stable_sort_validation():
+    e = _lib()
+    lib = e.load_library()
+    assert lib.eqtp_sort_workspace_bytes(-1, 5) == -e.EQTP_EINVAL
+    assert lib.eqtp_sort_workspace_bytes(5, -1) == -e.EQTP_EINVAL
+    need = lib.eqtp_sort_workspace_bytes(1000, 20000)
+    assert need >= 3 * 20000 * 4 and need % 256 == 0
+    call = lambda N, E, dst=FAKE, vec=NULL, src=NULL, rp=FAKE, perm=FAKE, vs=NULL, ss=NULL, ws=FAKE, nb=need: \
+        lib.eqtp_sort_edges_stable(N, E, dst, vec, src, rp, perm, vs, ss, ws, nb, NULL)
+    assert call(1000, 20000, nb=need - 1) == 1                  # short workspace
+    assert call(1000, 20000, ws=NULL) == 1                      # no workspace
+    assert call(1000, 20000, ws=ctypes.c_void_p(0x10004)) == 1  # workspace not 16-byte aligned
+    assert call(1000, 20000, perm=NULL) == 1
+    assert call(1000, 20000, dst=NULL) == 1
+    assert call(1000, 20000, rp=NULL) == 1
+    assert call(1000, 20000, vs=FAKE) == 1                      # vec_sorted without vec
+    assert call(1000, 20000, ss=FAKE) == 1                      # src_sorted without src
+    assert call(0, 5) == 1                                      # edges without nodes
+    assert call(-1, 0) == 1
+
+
 def test_sort_edges_validation():
     e = _lib()
     lib = e.load_library()

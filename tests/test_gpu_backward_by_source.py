@@ -136,6 +136,26 @@ def test_by_source_gpu_grouping_and_determinism(radial):
     assert np.array_equal(_np(a[0]), _np(b[0]))
 
 
+@pytest.mark.parametrize("radial,L", [(True, 3), (False, 3), (False, 5)])
+def test_by_source_stable_grouping_deterministic(radial, L):
+    """The stable GPU grouping (eqtp_sort_edges_stable) equals the host's stable argsort exactly, so two
+    groupings and backward passes give bit-identical grad_x (summed per source row in the grouped order and
+    written once); grad_w and grad_vec, whose partial sums meet in fp32 atomics, agree with the oracle."""
+    eq = _eq()
+    wl = synth.small_graph(67, 15, 64, L, 3451 + L, radial=radial, r_cut=5.0, long_rows=(5,), long_len=150,
+                           zero_vec_edges=1)
+    gout = _gout(wl, 13)
+    _say("by source stable grouping radial=%s L=%d" % (radial, L))
+    runs = []
+    for _ in range(2):
+        rows = eq.eqtp_edge_rows(_t(wl.row_ptr), wl.src.shape[0])
+        src_ptr, perm, vec_s, dst_s = eq.eqtp_sort_edges_stable(_t(wl.src), wl.N, vec=_t(wl.vec), src=rows)
+        assert np.array_equal(_np(perm), np.argsort(wl.src, kind="stable").astype(np.int32))
+        runs.append(_run(eq, wl, (src_ptr, vec_s, dst_s, perm), gout, radial=radial))
+    _compare(runs[0], _ref(wl, gout, radial), (True, True, True), "by source stable grouping")
+    assert np.array_equal(_np(runs[0][0]), _np(runs[1][0]))
+
+
 def test_by_source_no_edges():
     eq = _eq()
     for radial, L in ((True, 3), (False, 5)):

@@ -214,3 +214,64 @@ def test_conv_ws_workloads(name):
     out = _np(eq.eqtp_conv_fused_ws(_t(pvec), _t(psrc), _t(wl.x), _t(wl.weights), wl.lmax, dst=_t(pdst),
                                     path_set=wl.path_set, weight_mode=wl.weight_mode, r_cut=wl.r_cut))
     _assert_close(out, _oracle_full(name), TOL, name + " conv ws")
+
+
+# ---- eqtp_sort_edges_stable: every output unique, so all of them are compared exactly ----
+
+def _check_stable(eq, N, dst, vec=None, src=None, reuse=None):
+    E = dst.shape[0]
+    key = np.clip(dst, 0, max(N - 1, 0))  # out-of-range keys are clamped, as the kernels do
+    order = np.argsort(key, kind="stable").astype(np.int32)
+    got = eq.eqtp_sort_edges_stable(_t(dst), N, vec=_t(vec) if vec is not None else None,
+                                    src=_t(src) if src is not None else None, out=reuse)
+    rp, perm = _np(got[0]), _np(got[1])
+    want_rp = np.concatenate([[0], np.cumsum(np.bincount(key, minlength=N))]).astype(np.int32)
+    assert np.array_equal(rp, want_rp), "row_ptr differs"
+    assert np.array_equal(perm, order), "perm differs from the stable order"
+    if vec is not None:
+        assert np.array_equal(_np(got[2]), vec[order])
+    if src is not None:
+        assert np.array_equal(_np(got[3]), src[order])
+    return got
+
+
+@pytest.mark.parametrize("N,E,seed", [(1, 1, 20), (1, 500, 21), (7, 3, 22), (512, 5000, 23), (513, 5000, 24),
+                                      (10000, 266116, 25), (262144, 40000, 26), (300000, 50000, 27),
+                                      (5000, 2, 28)])
+def test_stable_sort_random(N, E, seed):
+    """One, two and three radix passes (keys of up to 9, 18 and 27 bits), tiny and mid-sized inputs."""
+    eq = _eq()
+    rng = np.random.default_rng(seed)
+    dst = rng.integers(0, N, size=E).astype(np.int32)
+    _say("stable sort N=%d E=%d" % (N, E))
+    _check_stable(eq, N, dst, rng.standard_normal((E, 3)).astype(np.float32),
+                  rng.integers(0, N, size=E).astype(np.int32))
+
+
+def test_stable_sort_skewed_clamped_and_repeated():
+    eq = _eq()
+    rng = np.random.default_rng(29)
+    N, E = 3000, 60000
+    dst = np.where(rng.random(E) < 0.5, 1234, rng.integers(0, N, size=E) // 7 * 7).astype(np.int32)
+    dst[:4] = (0, N - 1, -5, N + 9)  # the last two are clamped to rows 0 and N - 1
+    vec = rng.standard_normal((E, 3)).astype(np.float32)
+    _say("stable sort skewed + clamped")
+    first = _check_stable(eq, N, dst, vec, None)
+    again = _check_stable(eq, N, dst, vec, None)
+    assert np.array_equal(_np(first[1]), _np(again[1]))
+    d2 = rng.integers(0, N // 3, size=E).astype(np.int32)  # same buffers, other edges
+    _check_stable(eq, N, d2, None, None, reuse=(first[0], first[1], None, None))
+
+
+def test_stable_sort_no_edges_and_validation():
+    import torch
+
+    eq = _eq()
+    _say("stable sort no edges")
+    for N in (0, 1, 777):
+        rp, perm, _, _ = eq.eqtp_sort_edges_stable(torch.zeros(0, dtype=torch.int32, device="cuda"), N)
+        assert np.array_equal(_np(rp), np.zeros(N + 1, dtype=np.int32)) and perm.numel() == 0
+    dst = _t(np.zeros(100, np.int32))
+    short = torch.empty(eq.eqtp_sort_workspace_bytes(10, 100) - 256, dtype=torch.uint8, device="cuda")
+    with pytest.raises(eq.EqtpError):
+        eq.eqtp_sort_edges_stable(dst, 10, workspace=short)
