@@ -9,12 +9,18 @@
 // memory.  phi is written as [E][4][16] (unit k = 4 i + q at q * 16 + i),
 // the order in which that kernel's lane groups read it.
 //
-// Lane k of a wave is hidden unit k; the wave walks a run of edges one at a
-// time.  W1's column and W2's column of the lane's unit are held in
-// registers (8 + 64 values); a[j] reaches every lane through v_readlane, so
-// the second layer is 64 FMAs per lane with a wave-uniform operand.  The
-// network is a small fraction of the layer's work (about 4.6k FMAs per edge
-// against the path weights' 94k at P = 23, C = 64).
+// Both layers are products with the edges as rows, so a wave takes 16 edges
+// at a time and runs them on v_mfma_f32_16x16x4_f32 (fp32 products and
+// sums): layer 1 is [16 x 8] x [8 x 64] (8 products), layer 2 [16 x 64] x
+// [64 x 64] (64 products), with W1 and W2 held in registers as B operands
+// for the whole kernel.  Lane (i, g) of the A operand supplies edge i and
+// inputs g, g + 4, ...; the radial functions of edge i are evaluated by the
+// four lanes that feed its row.  Between the layers, and before the store,
+// the results go through a 16 x 64 LDS tile in the order unit 4 s + q at
+// q * 16 + s, which is both the layout the second layer's A operand reads
+// contiguously and the phi layout above, so every global store is a
+// coalesced 16-byte one.  About 4.6k multiply-adds per edge against the path
+// weights' 94k at P = 23, C = 64.
 #include "eqtp_device.hpp"
 #include "eqtp_kernels.hpp"
 
@@ -23,53 +29,84 @@ namespace eqtp {
 constexpr int kMlpHidden = 64;
 constexpr int kMlpBasis = 8;
 constexpr int kMlpWaves = 4;
-constexpr int kMlpRun = 32;  // edges per wave and run
+constexpr int kMlpRow = kMlpHidden + 4;  // LDS row stride (floats): rows start 4 banks apart
 
 __device__ __forceinline__ float silu(float t) { return t / (1.0f + __expf(-t)); }
 
-constexpr int kMlpIlp = 4;  // edges in flight per lane (independent FMA chains)
+// position of hidden unit h = 4 s + q in an LDS row and in phi: q * 16 + s
+__device__ __forceinline__ int mlp_slot(int h) { return (h & 3) * 16 + (h >> 2); }
 
 __global__ __launch_bounds__(kMlpWaves * kWave) void radial_mlp_kernel(int E, const float* __restrict__ vec,
                                                                        const float* __restrict__ W1,
                                                                        const float* __restrict__ W2,
                                                                        float* __restrict__ phi, float inv_rc,
                                                                        float scale) {
-  const int k = threadIdx.x & 63;  // hidden unit
-  float w1[kMlpBasis], w2[kMlpHidden];
+  __shared__ __attribute__((aligned(16))) float tile[kMlpWaves][16 * kMlpRow];
+  const int lane = threadIdx.x & 63;
+  const int i16 = lane & 15;  // A row (edge) / B and D column
+  const int kq = lane >> 4;   // A / B k group; D rows 4 kq .. 4 kq + 3
+  float* const t = tile[threadIdx.x >> 6];
+  // B operands: w1b[s][j] = W1[4 s + kq, 16 j + i16], w2b[s][j] = W2[4 s + kq, 16 j + i16]
+  float w1b[2][4], w2b[16][4];
 #pragma unroll
-  for (int b = 0; b < kMlpBasis; ++b) w1[b] = W1[b * kMlpHidden + k];
+  for (int s = 0; s < 2; ++s)
 #pragma unroll
-  for (int jj = 0; jj < kMlpHidden; ++jj) w2[jj] = W2[jj * kMlpHidden + k];
-  const int slot = (k & 3) * 16 + (k >> 2);  // where unit k = 4 i + q is stored: q * 16 + i
-  const int nruns = (E + kMlpRun - 1) / kMlpRun;
-  const int wave = blockIdx.x * kMlpWaves + (threadIdx.x >> 6);
+    for (int j = 0; j < 4; ++j) w1b[s][j] = W1[(4 * s + kq) * kMlpHidden + 16 * j + i16];
+#pragma unroll
+  for (int s = 0; s < 16; ++s)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w2b[s][j] = W2[(4 * s + kq) * kMlpHidden + 16 * j + i16];
+  const int nbatch = (E + 15) / 16;
   const int nwaves = gridDim.x * kMlpWaves;
-  for (int run = wave; run < nruns; run += nwaves) {
-    const int e_end = min(E, (run + 1) * kMlpRun);
-    // kMlpIlp edges at a time; slots past the run's end repeat its last edge and are not stored
-    for (int e0 = run * kMlpRun; e0 < e_end; e0 += kMlpIlp) {
-      float a[kMlpIlp], t[kMlpIlp];
+  for (int b = blockIdx.x * kMlpWaves + (threadIdx.x >> 6); b < nbatch; b += nwaves) {
+    const int e = 16 * b + i16;
+    float R[kMlpBasis];
 #pragma unroll
-      for (int u = 0; u < kMlpIlp; ++u) {
-        const int e = min(e0 + u, e_end - 1);
-        const float vx = vec[3 * (size_t)e], vy = vec[3 * (size_t)e + 1], vz = vec[3 * (size_t)e + 2];
-        float R[kMlpBasis];
-        radial_basis<kMlpBasis>(sqrtf(vx * vx + vy * vy + vz * vz), inv_rc, R);
-        float acc = 0.0f;
+    for (int k = 0; k < kMlpBasis; ++k) R[k] = 0.0f;
+    if (e < E) {
+      const float vx = vec[3 * (size_t)e], vy = vec[3 * (size_t)e + 1], vz = vec[3 * (size_t)e + 2];
+      radial_basis<kMlpBasis>(sqrtf(vx * vx + vy * vy + vz * vz), inv_rc, R);
+    }
+    const float r0 = kq == 0 ? R[0] : (kq == 1 ? R[1] : (kq == 2 ? R[2] : R[3]));
+    const float r1 = kq == 0 ? R[4] : (kq == 1 ? R[5] : (kq == 2 ? R[6] : R[7]));
+    // layer 1: a[edge 4 kq + v][unit 16 j + i16] = SiLU(acc[j][v]) -> LDS
+    f4 acc[4];
 #pragma unroll
-        for (int b = 0; b < kMlpBasis; ++b) acc = fmaf(R[b], w1[b], acc);
-        a[u] = silu(acc);
-        t[u] = 0.0f;
-      }
+    for (int j = 0; j < 4; ++j) {
+      acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(r0, w1b[0][j], f4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+      acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(r1, w1b[1][j], acc[j], 0, 0, 0);
+    }
+    wave_lds_sync();  // the previous batch's tile has been read
 #pragma unroll
-      for (int jj = 0; jj < kMlpHidden; ++jj)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int u = 0; u < kMlpIlp; ++u)
-          t[u] = fmaf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, a[u]), jj)), w2[jj],
-                      t[u]);
+      for (int v = 0; v < 4; ++v) t[(4 * kq + v) * kMlpRow + mlp_slot(16 * j + i16)] = silu(acc[j][v]);
+    wave_lds_sync();
+    // layer 2: A operand of lane (edge i16, kq) = units kq, 4 + kq, ..., 60 + kq: 16 contiguous floats
+    f4 av[4];
 #pragma unroll
-      for (int u = 0; u < kMlpIlp; ++u)
-        if (e0 + u < e_end) phi[(size_t)(e0 + u) * kMlpHidden + slot] = silu(t[u]) * scale;
+    for (int q = 0; q < 4; ++q) av[q] = *reinterpret_cast<const f4*>(t + i16 * kMlpRow + kq * 16 + 4 * q);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[j] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 16; ++s)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[s >> 2][s & 3], w2b[s][j], acc[j], 0, 0, 0);
+    wave_lds_sync();  // every lane has read its A operands
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) t[(4 * kq + v) * kMlpRow + mlp_slot(16 * j + i16)] = silu(acc[j][v]) * scale;
+    wave_lds_sync();
+    // 16 rows of 64 floats leave as 256 coalesced 16-byte stores (four per lane)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int f = 64 * q + lane;  // 16-byte piece f: row f / 16, columns 4 (f % 16) .. 4 (f % 16) + 3
+      const int r = f >> 4, c4 = f & 15;
+      if (16 * b + r < E)
+        *reinterpret_cast<f4*>(phi + (size_t)(16 * b + r) * kMlpHidden + 4 * c4) =
+            *reinterpret_cast<const f4*>(t + r * kMlpRow + 4 * c4);
     }
   }
 }
@@ -77,9 +114,10 @@ __global__ __launch_bounds__(kMlpWaves * kWave) void radial_mlp_kernel(int E, co
 hipError_t launch_radial_mlp(int64_t E, const float* vec, float r_cut, const float* W1, const float* W2, float* phi,
                              float scale, hipStream_t stream) {
   if (E == 0) return hipSuccess;
-  const int64_t runs = (E + kMlpRun - 1) / kMlpRun;
-  const int64_t want = 8LL * num_cus();  // two workgroups of four waves per CU
-  const int64_t blocks = (runs + kMlpWaves - 1) / kMlpWaves < want ? (runs + kMlpWaves - 1) / kMlpWaves : want;
+  const int64_t nbatch = (E + 15) / 16;
+  const int64_t want = 8LL * num_cus();  // workgroups of four waves, eight per CU at most
+  const int64_t need = (nbatch + kMlpWaves - 1) / kMlpWaves;
+  const int64_t blocks = need < want ? need : want;
   hipLaunchKernelGGL(radial_mlp_kernel, dim3((unsigned)blocks), dim3(kMlpWaves * kWave), 0, stream, (int)E, vec, W1,
                      W2, phi, 1.0f / r_cut, scale);
   return hipGetLastError();
