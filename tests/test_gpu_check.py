@@ -210,3 +210,53 @@ def test_debug_mode_same_results_on_clean_graphs():
     finally:
         eq.eqtp_set_debug(was)
     assert np.array_equal(got, ref) and np.array_equal(got_u, ref_u)
+
+
+def test_debug_mode_other_entry_points():
+    """Debug mode in the interaction layer, eqtp_edge_rows, eqtp_sort_edges_stable and
+    eqtp_conv_fused_noalloc: a faulty graph is refused with EQTP_EGRAPH and nothing written."""
+    import torch
+
+    eq = _eq()
+    wl = synth.small_graph(39, 8, 32, 3, 4105, empty_rows=(6,))
+    iw = synth.interaction_weights(3, 32)
+    bad_src = wl.src.copy()
+    bad_src[11] = wl.N + 4
+    bad_rp = wl.row_ptr.copy()
+    bad_rp[10] = bad_rp[11] + 1  # decreasing
+    was = eq.eqtp_set_debug(True)
+    try:
+        _say("debug mode: interaction layer with src out of range")
+        out = torch.full((wl.N, 32, 16), 3.5, dtype=torch.float32, device="cuda")
+        with pytest.raises(eq.EqtpError) as ei:
+            eq.eqtp_interaction(_t(wl.vec), _t(bad_src), _t(wl.row_ptr), _t(wl.x), _t(iw.W_up), _t(iw.W1),
+                                _t(iw.W2), _t(iw.W3), _t(iw.W_out), 3, r_cut=5.0, norm=8.0, out=out)
+        assert ei.value.status == eq.EQTP_EGRAPH and bool((out == 3.5).all())
+        _say("debug mode: edge rows with a decreasing row_ptr")
+        rows = torch.full((wl.E,), -7, dtype=torch.int32, device="cuda")
+        with pytest.raises(eq.EqtpError) as ei:
+            eq.eqtp_edge_rows(_t(bad_rp), wl.E, out=rows)
+        assert ei.value.status == eq.EQTP_EGRAPH and bool((rows == -7).all())
+        _say("debug mode: stable sort with a key out of range")
+        bad_dst = wl.dst.copy()
+        bad_dst[0] = -1
+        with pytest.raises(eq.EqtpError) as ei:
+            eq.eqtp_sort_edges_stable(_t(bad_dst), wl.N)
+        assert ei.value.status == eq.EQTP_EGRAPH
+        _say("debug mode: no-alloc convolution with a NaN vector")
+        bad_vec = wl.vec.copy()
+        bad_vec[2, 1] = np.inf
+        out2 = torch.full((wl.N, 32, 16), 1.25, dtype=torch.float32, device="cuda")
+        with pytest.raises(eq.EqtpError) as ei:
+            eq.eqtp_conv_fused_noalloc(_t(bad_vec), _t(wl.src), _t(wl.x), _t(wl.w), 3, dst=_t(wl.dst), out=out2)
+        assert ei.value.status == eq.EQTP_EGRAPH and bool((out2 == 1.25).all())
+        _say("debug mode: the same calls on the clean graph succeed")
+        eq.eqtp_interaction(_t(wl.vec), _t(wl.src), _t(wl.row_ptr), _t(wl.x), _t(iw.W_up), _t(iw.W1), _t(iw.W2),
+                            _t(iw.W3), _t(iw.W_out), 3, r_cut=5.0, norm=8.0, out=out)
+        eq.eqtp_edge_rows(_t(wl.row_ptr), wl.E, out=rows)
+        eq.eqtp_sort_edges_stable(_t(wl.dst), wl.N)
+        eq.eqtp_conv_fused_noalloc(_t(wl.vec), _t(wl.src), _t(wl.x), _t(wl.w), 3, dst=_t(wl.dst), out=out2)
+        torch.cuda.synchronize()
+        assert np.array_equal(_np(rows), wl.dst.astype(np.int32))
+    finally:
+        eq.eqtp_set_debug(was)
