@@ -245,9 +245,11 @@ int eqtp_conv_fused_noalloc(const eqtp_conv_desc* d, int64_t N, int64_t E, const
  * source indices [E] in, messages [E,C,16] out):
  *   messages[e, c, l3 m3] = sum_p w_e[p, c] sum_{m1, m2} C^p[m1, m2, m3] x[src_e, c, l1 m1] Y_{l2 m2}(vec_e)
  * d: lmax, C, path_set, weight_mode, r_cut, n_basis as for eqtp_conv_fused
- * (edge_order is ignored); N, E, vec, src, x, weights as there.  lmax 4..6,
- * or d->algo = EQTP_ALGO_EDGE_SO2, use the edge-aligned form (fixed weights
- * only, C = 128 up to lmax 4); otherwise the coupling form.
+ * (edge_order is ignored); N, E, vec, src, x, weights as there.  Fixed
+ * weights use the edge-aligned form (C = 128 up to lmax 4) unless d->algo =
+ * EQTP_ALGO_EDGE_VALU asks for the coupling form (lmax <= 3); radial weights
+ * use the coupling form (lmax <= 3; EQTP_ALGO_EDGE_SO2 gives
+ * EQTP_EUNSUPPORTED).  Both forms give the same messages to rounding.
  *   messages [E, C, K] fp32, 16-byte aligned, fully overwritten; must not
  *            alias an input (d->out_dtype must be EQTP_F32).  Deterministic.
  */

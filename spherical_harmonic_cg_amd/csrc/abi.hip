@@ -405,8 +405,10 @@ int eqtp_conv_messages(const eqtp_conv_desc* d, int64_t N, int64_t E, const floa
   if (out_f32_only(d) != EQTP_OK) return out_f32_only(d);
   if (d->lmax < 0) return EQTP_EINVAL;
   if (d->lmax > eqtp::kSo2MaxL) return EQTP_EUNSUPPORTED;
-  // lmax above 3 (or algo = EDGE_SO2): the edge-aligned form, fixed weights
-  const bool use_so2 = d->lmax > 3 || d->algo == EQTP_ALGO_EDGE_SO2;
+  // fixed weights: the edge-aligned form unless the per-edge coupling walk (EQTP_ALGO_EDGE_VALU) is asked for
+  // (the same messages with fewer operations per edge); radial weights at lmax <= 3: the coupling walk
+  const bool use_so2 = d->lmax > 3 || d->algo == EQTP_ALGO_EDGE_SO2 ||
+                       (d->algo != EQTP_ALGO_EDGE_VALU && d->weight_mode == EQTP_W_FIXED);
   if (use_so2 && d->weight_mode != EQTP_W_FIXED) return EQTP_EUNSUPPORTED;
   if (use_so2 && d->C == 128 && d->lmax > eqtp::kSo2MaxLC128) return EQTP_EUNSUPPORTED;
   if (d->path_set != EQTP_PATHS_PARITY && d->path_set != EQTP_PATHS_SO3) return EQTP_EINVAL;

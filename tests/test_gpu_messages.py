@@ -11,23 +11,24 @@ from test_gpu_parity import TOL, _assert_close, _eq, _np, _say, _t
 pytestmark = pytest.mark.gpu
 
 
-def _run(eq, wl, radial):
+def _run(eq, wl, radial, algo=0):
     w = wl.w_rad if radial else wl.w
     kw = dict(path_set=wl.path_set, weight_mode=1 if radial else 0, r_cut=wl.r_cut)
-    got = eq.eqtp_conv_messages(_t(wl.vec), _t(wl.src), _t(wl.x), _t(w), wl.lmax, **kw)
+    got = eq.eqtp_conv_messages(_t(wl.vec), _t(wl.src), _t(wl.x), _t(w), wl.lmax, algo=algo, **kw)
     ref = oracle.messages(wl.N, wl.vec, wl.src, wl.x, w, wl.lmax, **kw)
     return _np(got), ref
 
 
+@pytest.mark.parametrize("algo", [0, 2])  # default (edge-aligned form) and the coupling walk
 @pytest.mark.parametrize("lmax", [0, 1, 2, 3])
 @pytest.mark.parametrize("ps", [0, 1])
 @pytest.mark.parametrize("C", [8, 16, 32, 64, 128])
-def test_messages_fixed(lmax, ps, C):
+def test_messages_fixed(lmax, ps, C, algo):
     eq = _eq()
     wl = synth.small_graph(29, 7, C, lmax, 900 + lmax * 10 + C, path_set=ps, zero_vec_edges=1)
-    _say("messages fixed lmax=%d ps=%d C=%d E=%d" % (lmax, ps, C, wl.src.shape[0]))
-    got, ref = _run(eq, wl, False)
-    _assert_close(got, ref, TOL, "messages L%d ps%d C%d" % (lmax, ps, C))
+    _say("messages fixed lmax=%d ps=%d C=%d algo=%d E=%d" % (lmax, ps, C, algo, wl.src.shape[0]))
+    got, ref = _run(eq, wl, False, algo)
+    _assert_close(got, ref, TOL, "messages L%d ps%d C%d algo%d" % (lmax, ps, C, algo))
 
 
 @pytest.mark.parametrize("lmax,ps,C", [(3, 0, 64), (3, 0, 128), (2, 1, 16), (1, 0, 8)])
@@ -45,6 +46,8 @@ def test_messages_typical_workload_and_sum():
     _say("messages typical E=%d" % wl.src.shape[0])
     got, ref = _run(eq, wl, False)
     _assert_close(got, ref, TOL, "messages typical")
+    got2, _ = _run(eq, wl, False, algo=2)
+    _assert_close(got2, ref, TOL, "messages typical, coupling walk")
     # summing the GPU messages into the destinations gives the GPU convolution
     conv = _np(eq.eqtp_conv_fused(_t(wl.vec), _t(wl.src), _t(wl.x), _t(wl.w), 3, row_ptr=_t(wl.row_ptr)))
     summed = np.zeros_like(conv, dtype=np.float64)
