@@ -9,6 +9,7 @@ raises -- there is no fallback.
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
 import threading
 
@@ -59,6 +60,8 @@ _lock = threading.Lock()
 def load_library(path: str = LIB_PATH):
     """Load libeqtp.so (raises if it has not been built)."""
     global _lib
+    if _lib is not None and path == LIB_PATH:
+        return _lib
     with _lock:
         if _lib is None:
             if not os.path.exists(path):
@@ -111,17 +114,37 @@ def load_library(path: str = LIB_PATH):
     return _lib
 
 
-def _stream():
-    import torch
+# The per-call marshalling is on the host's critical path for small graphs (a launch takes a few µs), so
+# the helpers below take the cheap route first: the raw current stream of the current device, pointers as
+# plain ints (ctypes converts them for c_void_p arguments), and one combined test per tensor before the
+# detailed checks that name what is wrong.
+_raw_stream = None
 
-    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+def _stream():
+    global _raw_stream
+    if _raw_stream is None:
+        import torch
+
+        get_raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+        get_dev = getattr(torch._C, "_cuda_getDevice", None)
+        if get_raw is not None and get_dev is not None:
+            _raw_stream = lambda: get_raw(get_dev())
+        else:
+            _raw_stream = lambda: torch.cuda.current_stream().cuda_stream
+    return _raw_stream()
 
 
 def _ptr(t):
-    return ctypes.c_void_p(t.data_ptr()) if t is not None and t.numel() > 0 else ctypes.c_void_p(0)
+    return t.data_ptr() if t is not None and t.numel() > 0 else None
 
 
 def _check(t, name, dtype, shape=None):
+    try:
+        if t.is_cuda and t.dtype is dtype and t.is_contiguous() and (shape is None or t.shape == tuple(shape)):
+            return
+    except AttributeError:
+        pass
     import torch
 
     if not isinstance(t, torch.Tensor):
@@ -145,11 +168,23 @@ def eqtp_status_string(status: int) -> str:
     return load_library().eqtp_status_string(int(status)).decode()
 
 
+@functools.lru_cache(maxsize=None)
+def _num_paths(lmax: int, path_set: int) -> int:
+    return load_library().eqtp_num_paths(lmax, path_set)
+
+
 def eqtp_num_paths(lmax: int, path_set: int = EQTP_PATHS_PARITY) -> int:
-    P = load_library().eqtp_num_paths(lmax, path_set)
+    P = _num_paths(int(lmax), int(path_set))
     if P < 0:
         raise EqtpError(-P, "eqtp_num_paths")
     return P
+
+
+@functools.lru_cache(maxsize=256)
+def _conv_desc(lmax, C, path_set, weight_mode, order, algo, r_cut, n_basis, x_dtype, out_dtype):
+    # read by the library during a call only, so one instance per distinct descriptor is shared
+    return _ConvDesc(ctypes.sizeof(_ConvDesc), lmax, C, path_set, weight_mode, order, algo, r_cut, n_basis, x_dtype,
+                     out_dtype)
 
 
 def eqtp_path_table(lmax: int, path_set: int = EQTP_PATHS_PARITY) -> np.ndarray:
@@ -209,8 +244,7 @@ def _conv_args(vec, src, x, weights, lmax, row_ptr, dst, path_set, weight_mode, 
     if out is None:
         out = torch.empty((N, C, K), dtype=odt, device=x.device)
     _check(out, "out", odt, (N, C, K))
-    d = _ConvDesc(ctypes.sizeof(_ConvDesc), lmax, C, path_set, weight_mode, order, algo, float(r_cut), n_basis,
-                  x_dtype, out_dtype)
+    d = _conv_desc(lmax, C, path_set, weight_mode, order, algo, float(r_cut), n_basis, x_dtype, out_dtype)
     return d, N, E, out
 
 
