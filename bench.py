@@ -464,12 +464,12 @@ def main():
                 bkw = dict(row_ptr=sort_out[0])
                 bvec, bsrc = sort_out[2], sort_out[3]
 
-            def bwd():
-                eq.eqtp_conv_backward(bvec, bsrc, x, w, gout, wl.lmax, path_set=wl.path_set, **bkw)
-
-            def bwd_so2():
+            def bwd():  # the coupling walk (grad_vec of sorted edges on the matrix cores)
                 eq.eqtp_conv_backward(bvec, bsrc, x, w, gout, wl.lmax, path_set=wl.path_set,
-                                      algo=eq.EQTP_ALGO_EDGE_SO2, **bkw)
+                                      algo=eq.EQTP_ALGO_NODE_MFMA, **bkw)
+
+            def bwd_so2():  # the default: the edge-aligned form
+                eq.eqtp_conv_backward(bvec, bsrc, x, w, gout, wl.lmax, path_set=wl.path_set, **bkw)
 
             # by source: destinations of the CSR, sort by source, grad_x and grad_w on
             # the matrix cores, grad_vec edge by edge (what the autograd wrapper runs)
@@ -527,12 +527,13 @@ def main():
                             "what": "grad_x, grad_w and grad_vec of the conv: source grouping on the GPU "
                                     "(eqtp_edge_rows + eqtp_sort_edges_stable), eqtp_conv_backward_by_source (grad_x, "
                                     "grad_w), eqtp_conv_backward (grad_vec)",
-                            "edge_path_ms": round(bms, 5),
-                            "edge_path_what": "all three from eqtp_conv_backward (fp32 atomics for grad_x)",
-                            "edge_aligned_ms": round(oms, 5),
-                            "edge_aligned_what": "all three from eqtp_conv_backward with EQTP_ALGO_EDGE_SO2"}
-                log("backward: by source %.4f ms (%.3e edges/s); edge path %.4f ms; edge-aligned %.4f ms" % (
-                    sms, wl.E / (sms * 1e-3), bms, oms))
+                            "edge_path_ms": round(oms, 5),
+                            "edge_path_what": "all three from eqtp_conv_backward with the default algorithm (the "
+                                              "edge-aligned form, fp32 atomics for grad_x)",
+                            "coupling_walk_ms": round(bms, 5),
+                            "coupling_walk_what": "all three from eqtp_conv_backward with EQTP_ALGO_NODE_MFMA"}
+                log("backward: by source %.4f ms (%.3e edges/s); edge path (edge-aligned) %.4f ms; coupling walk "
+                    "%.4f ms" % (sms, wl.E / (sms * 1e-3), oms, bms))
 
     interaction = None
     if args.interaction:

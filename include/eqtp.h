@@ -273,8 +273,9 @@ int eqtp_conv_messages(const eqtp_conv_desc* d, int64_t N, int64_t E, const floa
  *   grad_vec[e] += (sum_b R_b'(r_e) sum_{p,c} W[b, p*C+c] T_e[p, c]) vec_e / r_e
  * (the product and chain rule through the radial basis; R_b' = dR_b/dr).
  * A zero-length edge vector has grad_vec = 0.
- * Fixed weights at lmax 4..6, or with d->algo = EQTP_ALGO_EDGE_SO2 at any
- * lmax: the edge-aligned form (E2Former-V2 page, section 2.1), where grad_x
+ * Fixed weights (d->algo = EQTP_ALGO_AUTO -- see below -- or
+ * EQTP_ALGO_EDGE_SO2, and always at lmax 4..6): the edge-aligned form
+ * (E2Former-V2 page, section 2.1), where grad_x
  * and grad_w come from the sparse coupling in each edge's frame and grad_vec
  * from the generators of rotations about the frame's x and y axes acting on
  * the rotated features (same formulas as above, to rounding); C = 128 only
@@ -292,11 +293,17 @@ int eqtp_conv_messages(const eqtp_conv_desc* d, int64_t N, int64_t E, const floa
  * summation order varies from run to run); with fixed weights grad_vec is
  * written once per edge, with radial weights it is a sum of fp32 atomics
  * (two per 16-channel block).  Errors as for eqtp_conv_fused.  d->algo
- * (fixed weights, lmax <= 3): for dst-sorted edges, grad_vec runs on the
- * matrix cores (dL/dY_e = x[src_e] contracted with a per-node B_d built from
- * grad_out) unless d->algo = EQTP_ALGO_EDGE_VALU, which walks the coupling
- * per edge on the vector ALUs, or EQTP_ALGO_EDGE_SO2 (the edge-aligned form
- * above).  Radial weights ignore d->algo.  d->x_dtype and d->out_dtype must
+ * (fixed weights, lmax <= 3): EQTP_ALGO_AUTO takes the edge-aligned form
+ * when grad_x or grad_w is requested (it is the faster one there at every
+ * lmax and channel count), and the coupling form for grad_vec alone (the
+ * faster one there: for dst-sorted edges the per-edge walk below lmax 3 and
+ * the matrix cores at lmax 3).  EQTP_ALGO_NODE_MFMA and EQTP_ALGO_EDGE_VALU
+ * always select the coupling form -- grad_x and grad_w by a walk of the
+ * coupling per edge on the vector ALUs, and grad_vec, for dst-sorted edges,
+ * on the matrix cores (dL/dY_e = x[src_e] contracted with a per-node B_d
+ * built from grad_out; EQTP_ALGO_NODE_MFMA) or by the same per-edge walk
+ * (EQTP_ALGO_EDGE_VALU, and for edges in any order).  Radial weights ignore
+ * d->algo.  d->x_dtype and d->out_dtype must
  * be EQTP_F32 (EQTP_EUNSUPPORTED for EQTP_BF16).
  */
 int eqtp_conv_backward(const eqtp_conv_desc* d, int64_t N, int64_t E, const float* vec, const int32_t* src,

@@ -468,8 +468,12 @@ int eqtp_conv_backward(const eqtp_conv_desc* d, int64_t N, int64_t E, const floa
   if (d->C <= 0) return EQTP_EINVAL;
   if (!valid_c(d->C)) return EQTP_EUNSUPPORTED;
   const bool radial = d->weight_mode == EQTP_W_RADIAL;
-  // fixed weights above lmax 3, or when asked for: the edge-aligned form
-  const bool use_so2 = !radial && (d->lmax > 3 || d->algo == EQTP_ALGO_EDGE_SO2);
+  // fixed weights, lmax <= 3, EQTP_ALGO_AUTO: the edge-aligned form when grad_x or grad_w is wanted (faster
+  // than the coupling walk at every lmax and channel count measured); grad_vec alone by the coupling walk,
+  // which is faster there (dst-sorted edges: the vector-ALU walk below lmax 3, the matrix cores at 3)
+  const bool vec_only = !grad_x && !grad_w;
+  const bool use_so2 = !radial && (d->lmax > 3 || d->algo == EQTP_ALGO_EDGE_SO2 ||
+                                   (d->algo == EQTP_ALGO_AUTO && !vec_only));
   if (d->lmax > 3 && !use_so2) return EQTP_EUNSUPPORTED;
   if (use_so2 && d->C == 128 && d->lmax > eqtp::kSo2MaxLC128) return EQTP_EUNSUPPORTED;
   if (radial) {
@@ -504,7 +508,7 @@ int eqtp_conv_backward(const eqtp_conv_desc* d, int64_t N, int64_t E, const floa
   a.gx = grad_x;
   a.gw = grad_w;
   a.gvec = grad_vec;
-  a.algo = d->algo;
+  a.algo = d->algo == EQTP_ALGO_AUTO && vec_only && d->lmax < 3 ? EQTP_ALGO_EDGE_VALU : d->algo;
   a.r_cut = d->r_cut;
   a.stream = (hipStream_t)stream;
   if (N > 0) {

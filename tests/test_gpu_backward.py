@@ -19,21 +19,22 @@ def _gout(wl, seed):
     return np.random.default_rng(seed).standard_normal((wl.N, wl.C, K)).astype(np.float32)
 
 
-def _check(eq, wl, gout, unsorted=False, perm_seed=2026, need=(True, True, True), what=""):
+def _check(eq, wl, gout, unsorted=False, perm_seed=2026, need=(True, True, True), what="", algo=0):
     ref = oracle.conv_backward(wl.N, wl.vec, wl.src, wl.dst, wl.x, wl.w, gout, wl.lmax, wl.path_set)
     if unsorted:
         rng = np.random.default_rng(perm_seed)
         perm = rng.permutation(wl.src.shape[0])
         vec, src, dst = wl.vec[perm], wl.src[perm], wl.dst[perm]
         gx, gw, gv = eq.eqtp_conv_backward(_t(vec), _t(src), _t(wl.x), _t(wl.w), _t(gout), wl.lmax, dst=_t(dst),
-                                           path_set=wl.path_set, need_x=need[0], need_w=need[1], need_vec=need[2])
+                                           path_set=wl.path_set, need_x=need[0], need_w=need[1], need_vec=need[2],
+                                           algo=algo)
         inv = np.empty_like(perm)
         inv[perm] = np.arange(perm.shape[0])
         gv_np = _np(gv)[inv] if gv is not None else None
     else:
         gx, gw, gv = eq.eqtp_conv_backward(_t(wl.vec), _t(wl.src), _t(wl.x), _t(wl.w), _t(gout), wl.lmax,
                                            row_ptr=_t(wl.row_ptr), path_set=wl.path_set, need_x=need[0],
-                                           need_w=need[1], need_vec=need[2])
+                                           need_w=need[1], need_vec=need[2], algo=algo)
         gv_np = _np(gv) if gv is not None else None
     for got, r, name, want in ((gx, ref[0], "grad_x", need[0]), (gw, ref[1], "grad_w", need[1]),
                                (gv_np, ref[2], "grad_vec", need[2])):
@@ -44,32 +45,39 @@ def _check(eq, wl, gout, unsorted=False, perm_seed=2026, need=(True, True, True)
         _assert_close(got, r, TOL, what + " " + name)
 
 
+# algo 0: the default (the edge-aligned form when grad_x or grad_w is wanted); 1: the coupling walk with
+# grad_vec on the matrix cores
+@pytest.mark.parametrize("algo", [0, 1])
 @pytest.mark.parametrize("lmax", [0, 1, 2, 3])
 @pytest.mark.parametrize("ps", [0, 1])
 @pytest.mark.parametrize("C", [8, 16, 32, 64, 128])
-def test_backward_small_sorted(lmax, ps, C):
+def test_backward_small_sorted(lmax, ps, C, algo):
     eq = _eq()
     wl = synth.small_graph(37, 9, C, lmax, 300 + lmax * 10 + C, path_set=ps, empty_rows=(3,), long_rows=(5,),
                            long_len=70, zero_vec_edges=1)
-    _say("backward sorted lmax=%d ps=%d C=%d E=%d" % (lmax, ps, C, wl.src.shape[0]))
-    _check(eq, wl, _gout(wl, 7), what="sorted L%d ps%d C%d" % (lmax, ps, C))
+    _say("backward sorted lmax=%d ps=%d C=%d algo=%d E=%d" % (lmax, ps, C, algo, wl.src.shape[0]))
+    _check(eq, wl, _gout(wl, 7), what="sorted L%d ps%d C%d algo%d" % (lmax, ps, C, algo), algo=algo)
 
 
+@pytest.mark.parametrize("algo", [0, 1])
 @pytest.mark.parametrize("lmax,ps,C", [(3, 0, 64), (3, 1, 32), (2, 0, 8), (1, 0, 128), (3, 0, 128)])
-def test_backward_small_unsorted(lmax, ps, C):
+def test_backward_small_unsorted(lmax, ps, C, algo):
     eq = _eq()
     wl = synth.small_graph(41, 10, C, lmax, 500 + lmax + C, path_set=ps, empty_rows=(0,), zero_vec_edges=2)
-    _say("backward unsorted lmax=%d ps=%d C=%d E=%d" % (lmax, ps, C, wl.src.shape[0]))
-    _check(eq, wl, _gout(wl, 8), unsorted=True, what="unsorted L%d ps%d C%d" % (lmax, ps, C))
+    _say("backward unsorted lmax=%d ps=%d C=%d algo=%d E=%d" % (lmax, ps, C, algo, wl.src.shape[0]))
+    _check(eq, wl, _gout(wl, 8), unsorted=True, what="unsorted L%d ps%d C%d algo%d" % (lmax, ps, C, algo),
+           algo=algo)
 
 
 @pytest.mark.parametrize("need", [(True, False, False), (False, True, False), (False, False, True),
                                   (True, False, True)])
-def test_backward_partial_requests(need):
+@pytest.mark.parametrize("lmax,unsorted", [(3, False), (1, False), (2, True)])
+def test_backward_partial_requests(need, lmax, unsorted):
+    """Each subset of outputs under the default algorithm (grad_vec alone goes to the coupling walk)."""
     eq = _eq()
-    wl = synth.small_graph(23, 8, 32, 3, 77)
-    _say("backward partial %s" % (need,))
-    _check(eq, wl, _gout(wl, 9), need=need, what="partial")
+    wl = synth.small_graph(23, 8, 32, lmax, 77 + lmax)
+    _say("backward partial %s lmax=%d unsorted=%s" % (need, lmax, unsorted))
+    _check(eq, wl, _gout(wl, 9), unsorted=unsorted, need=need, what="partial L%d" % lmax)
 
 
 def test_backward_typical_workload():
@@ -258,15 +266,16 @@ def test_autograd_modes(mode, csr):
 
 @pytest.mark.parametrize("lmax,ps,C", [(3, 0, 64), (3, 1, 128), (2, 0, 16), (1, 1, 8), (0, 0, 32), (3, 0, 8)])
 def test_grad_vec_both_walks(lmax, ps, C):
-    """grad_vec of dst-sorted edges: the matrix-core kernel (default) and the
-    vector-ALU walk (algo = EDGE_VALU), both against the oracle; rows longer
-    than 64 edges (several chunks) and empty rows included."""
+    """grad_vec alone of dst-sorted edges: the default (the vector-ALU walk below lmax 3,
+    the matrix cores at 3), the matrix-core kernel (algo = NODE_MFMA), the vector-ALU walk
+    (algo = EDGE_VALU) and the edge-aligned form (algo = EDGE_SO2), all against the oracle;
+    rows longer than 64 edges (several chunks) and empty rows included."""
     eq = _eq()
     wl = synth.small_graph(31, 12, C, lmax, 610 + lmax + C + ps, path_set=ps, empty_rows=(1, 2), long_rows=(7, 8),
                            long_len=150, zero_vec_edges=2)
     gout = _gout(wl, 33)
     ref = oracle.conv_backward(wl.N, wl.vec, wl.src, wl.dst, wl.x, wl.w, gout, lmax, ps)[2]
-    for algo in (0, 2):
+    for algo in (0, 1, 2, 3):
         _say("grad_vec walk algo=%d lmax=%d ps=%d C=%d" % (algo, lmax, ps, C))
         _, _, gv = eq.eqtp_conv_backward(_t(wl.vec), _t(wl.src), _t(wl.x), _t(wl.w), _t(gout), lmax,
                                          row_ptr=_t(wl.row_ptr), path_set=ps, need_x=False, need_w=False,
@@ -280,6 +289,7 @@ def test_grad_vec_mid_workload():
     gout = _gout(wl, 34)
     _say("grad_vec mid E=%d" % wl.src.shape[0])
     ref = oracle.conv_backward(wl.N, wl.vec, wl.src, wl.dst, wl.x, wl.w, gout, 3)[2]
-    _, _, gv = eq.eqtp_conv_backward(_t(wl.vec), _t(wl.src), _t(wl.x), _t(wl.w), _t(gout), 3,
-                                     row_ptr=_t(wl.row_ptr), need_x=False, need_w=False)
-    _assert_close(_np(gv), ref, TOL, "grad_vec mid")
+    for algo in (0, 1):
+        _, _, gv = eq.eqtp_conv_backward(_t(wl.vec), _t(wl.src), _t(wl.x), _t(wl.w), _t(gout), 3,
+                                         row_ptr=_t(wl.row_ptr), need_x=False, need_w=False, algo=algo)
+        _assert_close(_np(gv), ref, TOL, "grad_vec mid algo %d" % algo)
