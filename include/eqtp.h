@@ -77,7 +77,8 @@ extern "C" {
                                  "EAAS"): rotate x[src] so that the edge is the z axis, where the
                                  harmonics keep only m = 0 and the coupling is a sparse re-indexing,
                                  rotate back; vector ALUs; fixed weights, fp32 features; lmax 0..6
-                                 (C = 128 up to lmax 4).  Same result as the coupling form. */
+                                 (gradients: C = 128 up to lmax 4).  Same result as the coupling
+                                 form. */
 
 /* element types: node features (eqtp_conv_desc.x_dtype) and the channel
    linear's operands (eqtp_linear's dtype) */
@@ -179,7 +180,8 @@ typedef struct eqtp_conv_desc {
  * Sorted edges: deterministic (bit-identical from run to run).  Unsorted
  * edges: summation order varies from run to run.
  * lmax 4..6 (EQTP_ALGO_EDGE_SO2): fixed weights and fp32 features only
- * (EQTP_EUNSUPPORTED otherwise), C = 128 up to lmax 4; both edge orders.
+ * (EQTP_EUNSUPPORTED otherwise), any C (C = 128 above lmax 4 runs as two
+ * launches over 64-channel halves); both edge orders.
  * EQTP_ALGO_EDGE_SO2 with radial weights: dst-sorted edges, fp32 features,
  * lmax <= 3 and C a multiple of 16 only.
  */
@@ -246,7 +248,7 @@ int eqtp_conv_fused_noalloc(const eqtp_conv_desc* d, int64_t N, int64_t E, const
  *   messages[e, c, l3 m3] = sum_p w_e[p, c] sum_{m1, m2} C^p[m1, m2, m3] x[src_e, c, l1 m1] Y_{l2 m2}(vec_e)
  * d: lmax, C, path_set, weight_mode, r_cut, n_basis as for eqtp_conv_fused
  * (edge_order is ignored); N, E, vec, src, x, weights as there.  Fixed
- * weights use the edge-aligned form (C = 128 up to lmax 4) unless d->algo =
+ * weights use the edge-aligned form (any C) unless d->algo =
  * EQTP_ALGO_EDGE_VALU asks for the coupling form (lmax <= 3); radial weights
  * use the coupling form (lmax <= 3; EQTP_ALGO_EDGE_SO2 gives
  * EQTP_EUNSUPPORTED).  Both forms give the same messages to rounding.

@@ -216,7 +216,6 @@ int conv_impl(const eqtp_conv_desc* d, int64_t N, int64_t E, const float* vec, c
       !use_radial_so2 && (d->algo == EQTP_ALGO_EDGE_SO2 || (d->algo == EQTP_ALGO_AUTO && d->lmax > 3));
   if (d->lmax > 3 && !use_so2) return EQTP_EUNSUPPORTED;
   if (use_so2 && (d->weight_mode != EQTP_W_FIXED || x_dtype != EQTP_F32)) return EQTP_EUNSUPPORTED;
-  if (use_so2 && d->C == 128 && d->lmax > eqtp::kSo2MaxLC128) return EQTP_EUNSUPPORTED;
   // bf16 output: packed bf16 atomics of the per-edge walk, edges in any order
   if (out_dtype == EQTP_BF16 &&
       (d->edge_order != EQTP_EDGES_UNSORTED || use_so2 || use_radial_so2 ||
@@ -410,7 +409,6 @@ int eqtp_conv_messages(const eqtp_conv_desc* d, int64_t N, int64_t E, const floa
   const bool use_so2 = d->lmax > 3 || d->algo == EQTP_ALGO_EDGE_SO2 ||
                        (d->algo != EQTP_ALGO_EDGE_VALU && d->weight_mode == EQTP_W_FIXED);
   if (use_so2 && d->weight_mode != EQTP_W_FIXED) return EQTP_EUNSUPPORTED;
-  if (use_so2 && d->C == 128 && d->lmax > eqtp::kSo2MaxLC128) return EQTP_EUNSUPPORTED;
   if (d->path_set != EQTP_PATHS_PARITY && d->path_set != EQTP_PATHS_SO3) return EQTP_EINVAL;
   if (d->weight_mode != EQTP_W_FIXED && d->weight_mode != EQTP_W_RADIAL) return EQTP_EINVAL;
   if (d->C <= 0) return EQTP_EINVAL;

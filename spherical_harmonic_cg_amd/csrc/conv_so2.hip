@@ -105,7 +105,9 @@ __device__ __forceinline__ void load_feat(const float* __restrict__ xp, float (&
   }
 }
 
-template <int L, int PS, int C>
+// CT: channels per node row of x (C, or 128 when a C = 128 problem runs as two
+// 64-channel halves, x and w then pointing at the half's first channel)
+template <int L, int PS, int C, int CT = C>
 struct So2Msg {
   using T = So2Tables<L, PS>;
   using Cfg = So2Cfg<C>;
@@ -134,7 +136,7 @@ struct So2Msg {
 #pragma unroll
     for (int j = 0; j < Cfg::CPL; ++j) {
       float v[K];
-      const float* xp = x + ((size_t)s * C + cl + j * Cfg::CL) * K;
+      const float* xp = x + ((size_t)s * CT + cl + j * Cfg::CL) * K;
       if constexpr (K % 4 == 0) {
 #pragma unroll
         for (int q = 0; q < K / 4; ++q) {
@@ -182,7 +184,7 @@ struct So2Msg {
   }
 };
 
-template <int L, int PS, int C, bool ATOMIC>
+template <int L, int PS, int C, bool ATOMIC, int CT = C>
 __global__ __launch_bounds__(So2Cfg<C>::THREADS) void conv_so2_kernel(int N, int E, const int* __restrict__ row_ptr,
                                                                       const float* __restrict__ vec,
                                                                       const int* __restrict__ src,
@@ -192,17 +194,17 @@ __global__ __launch_bounds__(So2Cfg<C>::THREADS) void conv_so2_kernel(int N, int
                                                                       float* __restrict__ out) {
   using Cfg = So2Cfg<C>;
   using T = So2Tables<L, PS>;
-  using M = So2Msg<L, PS, C>;
+  using M = So2Msg<L, PS, C, CT>;
   constexpr int K = num_comp(L);
   __shared__ float wl[T::P * C];
-  for (int i = threadIdx.x; i < T::P * C; i += Cfg::THREADS) wl[i] = w[i];
+  for (int i = threadIdx.x; i < T::P * C; i += Cfg::THREADS) wl[i] = w[(i / C) * CT + i % C];
   __syncthreads();
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
   const int g = lane / Cfg::CL;
   const int cl = lane % Cfg::CL;
 
-  constexpr int MSG = C * K;        // floats per edge message
+  constexpr int MSG = C * K;        // floats per edge message (of this kernel's channels)
   constexpr int NI = Cfg::CPL * K;  // floats per lane of one round's messages
   // sorted rows at lmax >= 4 sum the messages in LDS (the lane's own slots)
   // rather than in registers, which the rotations and the coupling need
@@ -264,7 +266,7 @@ __global__ __launch_bounds__(So2Cfg<C>::THREADS) void conv_so2_kernel(int N, int
     if (g == 0) {
 #pragma unroll
       for (int j = 0; j < Cfg::CPL; ++j) {
-        float* op = out + ((size_t)row * C + cl + j * Cfg::CL) * K;
+        float* op = out + ((size_t)row * CT + cl + j * Cfg::CL) * K;
         if constexpr (K % 4 == 0) {
 #pragma unroll
           for (int q = 0; q < K / 4; ++q)
@@ -299,7 +301,7 @@ __global__ __launch_bounds__(So2Cfg<C>::THREADS) void conv_so2_kernel(int N, int
       for (int i = 0; i < NI; ++i) {
         const int f = kWave * i + lane;
         const int d = xdst[wv][f / MSG];
-        if (d >= 0) unsafeAtomicAdd(out + (size_t)d * MSG + f % MSG, xw[f]);
+        if (d >= 0) unsafeAtomicAdd(out + (size_t)d * (CT * K) + f % MSG, xw[f]);
       }
       wave_lds_sync();
     }
@@ -309,7 +311,7 @@ __global__ __launch_bounds__(So2Cfg<C>::THREADS) void conv_so2_kernel(int N, int
 // Per-edge messages in the edge-aligned form (the page's fused-kernel output
 // [E, C, K], no destination sum): the wave's store of one edge covers its
 // C*K*4 contiguous bytes.
-template <int L, int PS, int C>
+template <int L, int PS, int C, int CT = C>
 __global__ __launch_bounds__(So2Cfg<C>::THREADS) void conv_so2_msg_kernel(int N, int E, const float* __restrict__ vec,
                                                                           const int* __restrict__ src,
                                                                           const float* __restrict__ x,
@@ -317,10 +319,10 @@ __global__ __launch_bounds__(So2Cfg<C>::THREADS) void conv_so2_msg_kernel(int N,
                                                                           float* __restrict__ msg) {
   using Cfg = So2Cfg<C>;
   using T = So2Tables<L, PS>;
-  using M = So2Msg<L, PS, C>;
+  using M = So2Msg<L, PS, C, CT>;
   constexpr int K = num_comp(L);
   __shared__ float wl[T::P * C];
-  for (int i = threadIdx.x; i < T::P * C; i += Cfg::THREADS) wl[i] = w[i];
+  for (int i = threadIdx.x; i < T::P * C; i += Cfg::THREADS) wl[i] = w[(i / C) * CT + i % C];
   __syncthreads();
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
@@ -338,7 +340,7 @@ __global__ __launch_bounds__(So2Cfg<C>::THREADS) void conv_so2_msg_kernel(int N,
     M::run(e, N, cl, vec, src, x, wl, acc);
 #pragma unroll
     for (int j = 0; j < Cfg::CPL; ++j) {
-      float* op = msg + ((size_t)e * C + cl + j * Cfg::CL) * K;
+      float* op = msg + ((size_t)e * CT + cl + j * Cfg::CL) * K;
       if constexpr (K % 4 == 0) {
 #pragma unroll
         for (int q = 0; q < K / 4; ++q)
@@ -557,31 +559,37 @@ hipError_t launch_conv_so2_radial(const ConvArgs& a) {
   }
 }
 
-template <int L, int PS, int C>
-static hipError_t launch_so2_t(const ConvArgs& a) {
+// c0: the first channel this launch covers (x, w and out offset by it; rows CT channels wide)
+template <int L, int PS, int C, int CT = C>
+static hipError_t launch_so2_t(const ConvArgs& a, int c0 = 0) {
   using Cfg = So2Cfg<C>;
   constexpr int K = num_comp(L);
   if (a.N == 0) return hipSuccess;
+  const float* const x = (const float*)a.x + (size_t)c0 * K;
+  const float* const w = a.w + c0;
+  float* const out = a.out + (size_t)c0 * K;
   if (a.messages) {
     if (a.E == 0) return hipSuccess;
     const long long per_block = (long long)Cfg::WAVES * Cfg::EPW;
     const unsigned blocks = (unsigned)((a.E + per_block - 1) / per_block);
-    hipLaunchKernelGGL((conv_so2_msg_kernel<L, PS, C>), dim3(blocks), dim3(Cfg::THREADS), 0, a.stream, (int)a.N,
-                       (int)a.E, a.vec, a.src, (const float*)a.x, a.w, a.out);
+    hipLaunchKernelGGL((conv_so2_msg_kernel<L, PS, C, CT>), dim3(blocks), dim3(Cfg::THREADS), 0, a.stream, (int)a.N,
+                       (int)a.E, a.vec, a.src, x, w, out);
     return hipGetLastError();
   }
   if (a.row_ptr != nullptr) {
     const unsigned blocks = (unsigned)((a.N + Cfg::WAVES - 1) / Cfg::WAVES);
-    hipLaunchKernelGGL((conv_so2_kernel<L, PS, C, false>), dim3(blocks), dim3(Cfg::THREADS), 0, a.stream, (int)a.N,
-                       (int)a.E, a.row_ptr, a.vec, a.src, a.dst, (const float*)a.x, a.w, a.out);
+    hipLaunchKernelGGL((conv_so2_kernel<L, PS, C, false, CT>), dim3(blocks), dim3(Cfg::THREADS), 0, a.stream,
+                       (int)a.N, (int)a.E, a.row_ptr, a.vec, a.src, a.dst, x, w, out);
   } else {
-    hipError_t err = launch_fill_zero(a.out, a.N * C * K, a.stream);
-    if (err != hipSuccess) return err;
+    if (c0 == 0) {  // the whole output (every half) once
+      hipError_t err = launch_fill_zero(a.out, a.N * CT * K, a.stream);
+      if (err != hipSuccess) return err;
+    }
     if (a.E == 0) return hipSuccess;
     const long long per_block = (long long)Cfg::WAVES * Cfg::EPW;
     const unsigned blocks = (unsigned)((a.E + per_block - 1) / per_block);
-    hipLaunchKernelGGL((conv_so2_kernel<L, PS, C, true>), dim3(blocks), dim3(Cfg::THREADS), 0, a.stream, (int)a.N,
-                       (int)a.E, a.row_ptr, a.vec, a.src, a.dst, (const float*)a.x, a.w, a.out);
+    hipLaunchKernelGGL((conv_so2_kernel<L, PS, C, true, CT>), dim3(blocks), dim3(Cfg::THREADS), 0, a.stream,
+                       (int)a.N, (int)a.E, a.row_ptr, a.vec, a.src, a.dst, x, w, out);
   }
   return hipGetLastError();
 }
@@ -594,8 +602,12 @@ static hipError_t dispatch_so2_c(const ConvArgs& a) {
     case 32: return launch_so2_t<L, PS, 32>(a);
     case 64: return launch_so2_t<L, PS, 64>(a);
     case 128:
-      if constexpr (L <= kSo2MaxLC128) return launch_so2_t<L, PS, 128>(a);
-      else return hipErrorInvalidValue;
+      if constexpr (L <= kSo2MaxLC128) {
+        return launch_so2_t<L, PS, 128>(a);
+      } else {  // two 64-channel halves (two channels per lane do not fit the registers above lmax 4)
+        const hipError_t err = launch_so2_t<L, PS, 64, 128>(a, 0);
+        return err != hipSuccess ? err : launch_so2_t<L, PS, 64, 128>(a, 64);
+      }
     default: return hipErrorInvalidValue;
   }
 }

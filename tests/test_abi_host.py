@@ -116,8 +116,8 @@ NULL = ctypes.c_void_p(0)
 
 @pytest.mark.parametrize("kw,want", [
     (dict(lmax=7), 2), (dict(lmax=-1), 1), (dict(lmax=4, algo=1), 2), (dict(lmax=4, algo=2), 2),
-    (dict(lmax=4, weight_mode=1, r_cut=5.0), 2), (dict(lmax=4, x_dtype=1), 2), (dict(lmax=5, C=128), 2),
-    (dict(lmax=6, C=128, algo=3), 2), (dict(algo=3, weight_mode=1, r_cut=5.0, edge_order=1), 2), (dict(algo=3, weight_mode=1, r_cut=5.0, C=8), 2),
+    (dict(lmax=4, weight_mode=1, r_cut=5.0), 2), (dict(lmax=4, x_dtype=1), 2), (dict(lmax=5, C=128, x_dtype=1), 2),
+    (dict(lmax=6, C=128, algo=3, weight_mode=1, r_cut=5.0), 2), (dict(algo=3, weight_mode=1, r_cut=5.0, edge_order=1), 2), (dict(algo=3, weight_mode=1, r_cut=5.0, C=8), 2),
     (dict(lmax=4, algo=3, weight_mode=1, r_cut=5.0), 2), (dict(algo=3, x_dtype=1), 2), (dict(C=48), 2), (dict(C=0), 1), (dict(path_set=3), 1),
     (dict(weight_mode=2), 1), (dict(edge_order=5), 1), (dict(algo=9), 1),
     (dict(weight_mode=1, r_cut=0.0), 1), (dict(weight_mode=1, r_cut=5.0, n_basis=6), 2),
@@ -142,6 +142,8 @@ def test_conv_pointer_and_size_validation():
     call = lambda N, E, vec, src, dst, rp, x, w, out: lib.eqtp_conv_fused(ctypes.byref(d), N, E, vec, src, dst, rp,
                                                                           x, w, out, NULL)
     assert call(10, 20, FAKE, FAKE, NULL, FAKE, NULL, FAKE, FAKE) == 1      # x missing
+    d5 = _desc(e, lmax=5, C=128)  # C = 128 above lmax 4 (two 64-channel halves) gets past the descriptor checks
+    assert lib.eqtp_conv_fused(ctypes.byref(d5), 10, 20, FAKE, FAKE, NULL, FAKE, NULL, FAKE, FAKE, NULL) == 1
     assert call(10, 20, FAKE, FAKE, NULL, NULL, FAKE, FAKE, FAKE) == 1      # row_ptr missing (sorted)
     assert call(10, 20, NULL, FAKE, NULL, FAKE, FAKE, FAKE, FAKE) == 1      # vec missing
     assert call(-1, 20, FAKE, FAKE, NULL, FAKE, FAKE, FAKE, FAKE) == 1      # negative N
@@ -190,7 +192,7 @@ def test_conv_backward_validation():
     assert call(_desc(e, weight_mode=2)) == 1
     assert call(_desc(e, lmax=7)) == 2                                   # above lmax 6
     assert call(_desc(e, lmax=4, weight_mode=1, r_cut=5.0)) == 2         # radial weights: lmax 0..3
-    assert call(_desc(e, lmax=5, C=128)) == 2                            # edge-aligned form: C = 128 to lmax 4
+    assert call(_desc(e, lmax=5, C=128)) == 2                            # gradients: C = 128 to lmax 4
     assert call(_desc(e, algo=7)) == 1                                   # unknown algorithm
     assert call(_desc(e, C=48)) == 2
     assert call(_desc(e, path_set=2)) == 1
@@ -217,7 +219,7 @@ def test_conv_messages_validation():
     assert call(_desc(e, lmax=7)) == 2
     assert call(_desc(e, lmax=4, weight_mode=1, r_cut=4.0)) == 2          # edge-aligned form: fixed weights
     assert call(_desc(e, algo=3, weight_mode=1, r_cut=4.0)) == 2
-    assert call(_desc(e, lmax=5, C=128)) == 2
+    assert call(_desc(e, lmax=5, C=128), m=NULL) == 1                     # C = 128 at lmax 5 is supported
     assert call(_desc(e, lmax=5), m=NULL) == 1
     assert call(_desc(e, C=24)) == 2
     assert call(_desc(e, weight_mode=1, r_cut=0.0)) == 1
@@ -322,7 +324,7 @@ def test_conv_backward_by_source_validation():
     assert call(_desc(e, weight_mode=1, r_cut=5.0, lmax=4)) == 2         # radial: lmax 0..3
     assert call(_desc(e, weight_mode=1, r_cut=5.0), x=NULL, gw=NULL) == 1  # the walk reads x
     assert call(_desc(e, lmax=7)) == 2                                   # above lmax 6
-    assert call(_desc(e, lmax=5, C=128)) == 2                            # edge-aligned form: C = 128 to lmax 4
+    assert call(_desc(e, lmax=5, C=128)) == 2                            # gradients: C = 128 to lmax 4
     assert call(_desc(e, algo=7)) == 1                                   # unknown algorithm
     assert call(_desc(e, C=48)) == 2
     assert call(_desc(e, x_dtype=1)) == 2                                  # bf16 features

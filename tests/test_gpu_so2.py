@@ -39,7 +39,8 @@ def _run(eq, wl, unsorted, algo=SO2, perm_seed=3):
     return eq.eqtp_conv_fused(_t(wl.vec), _t(wl.src), _t(wl.x), _t(wl.w), wl.lmax, row_ptr=_t(wl.row_ptr), **kw)
 
 
-CASES = [(L, ps, C) for L in range(7) for ps in (0, 1) for C in (8, 16, 32, 64, 128) if not (C == 128 and L > 4)]
+# C = 128 above lmax 4 runs as two launches over 64-channel halves
+CASES = [(L, ps, C) for L in range(7) for ps in (0, 1) for C in (8, 16, 32, 64, 128)]
 
 
 @pytest.mark.parametrize("L,ps,C", CASES)
@@ -67,8 +68,8 @@ def test_so2_rejects_unsupported():
     eq = _eq()
     wl = _graph(5, 0, 128, 5)
     _say("so2 unsupported combinations")
-    with pytest.raises(eq.EqtpError):
-        _run(eq, wl, False)                      # C = 128 above lmax 4
+    with pytest.raises(eq.EqtpError):            # gradients: C = 128 only up to lmax 4
+        eq.eqtp_conv_backward(_t(wl.vec), _t(wl.src), _t(wl.x), _t(wl.w), _t(wl.x), 5, row_ptr=_t(wl.row_ptr))
     wl = _graph(4, 0, 32, 6)
     with pytest.raises(eq.EqtpError):
         _run(eq, wl, False, algo=1)              # lmax 4 has no node-factored form
@@ -112,7 +113,8 @@ def test_so2_lmax6_graph_full():
     _assert_close(outu, ref, TOL, "so2 L6 unsorted")
 
 
-@pytest.mark.parametrize("L,ps,C", [(4, 0, 32), (5, 1, 16), (6, 0, 64), (6, 1, 8), (4, 1, 128), (3, 0, 64), (2, 1, 32)])
+@pytest.mark.parametrize("L,ps,C", [(4, 0, 32), (5, 1, 16), (6, 0, 64), (6, 1, 8), (4, 1, 128), (5, 1, 128), (6, 0, 128),
+                                    (3, 0, 64), (2, 1, 32)])
 def test_so2_messages(L, ps, C):
     """Per-edge messages [E, C, K] in the edge-aligned form (lmax > 3, or
     algo = EDGE_SO2 at lmax <= 3) against the oracle's messages."""
