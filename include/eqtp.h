@@ -77,8 +77,8 @@ extern "C" {
                                  "EAAS"): rotate x[src] so that the edge is the z axis, where the
                                  harmonics keep only m = 0 and the coupling is a sparse re-indexing,
                                  rotate back; vector ALUs; fixed weights, fp32 features; lmax 0..6
-                                 (gradients: C = 128 up to lmax 4).  Same result as the coupling
-                                 form. */
+                                 (C = 128 above lmax 4 as two 64-channel halves).  Same result as
+                                 the coupling form. */
 
 /* element types: node features (eqtp_conv_desc.x_dtype) and the channel
    linear's operands (eqtp_linear's dtype) */
@@ -280,8 +280,9 @@ int eqtp_conv_messages(const eqtp_conv_desc* d, int64_t N, int64_t E, const floa
  * (E2Former-V2 page, section 2.1), where grad_x
  * and grad_w come from the sparse coupling in each edge's frame and grad_vec
  * from the generators of rotations about the frame's x and y axes acting on
- * the rotated features (same formulas as above, to rounding); C = 128 only
- * up to lmax 4.
+ * the rotated features (same formulas as above, to rounding); C = 128 above
+ * lmax 4 runs as two launches over 64-channel halves (the second adds its
+ * channels' share of grad_vec).
  *   d, N, E, vec, src, dst, row_ptr, x, weights: as for eqtp_conv_fused
  *            (x fp32, 16-byte aligned; lmax 0..6).  Radial weights: lmax
  *            0..3, C a multiple of 16, n_basis 8, r_cut > 0 (else
@@ -341,7 +342,7 @@ int eqtp_conv_backward(const eqtp_conv_desc* d, int64_t N, int64_t E, const floa
  *   grad_w[p, c] = sum_s sum_{m1} x[s, c, m1] sum_{m2, m3} C^p[m1, m2, m3] H_s[c, m3, m2],
  * and grad_vec by a walk in the edge frame; fixed weights at lmax 4..6 (or
  * d->algo = EQTP_ALGO_EDGE_SO2): all three by one walk in the edge frame (C =
- * 128 only up to lmax 4); radial weights (lmax 0..3, C a multiple of 16,
+ * 128 above lmax 4 as two 64-channel halves); radial weights (lmax 0..3, C a multiple of 16,
  * n_basis 8, r_cut > 0): all three by one walk in the edge frame.
  * d: lmax, C, path_set, weight_mode, r_cut, n_basis, algo, x_dtype and
  * out_dtype (both must be EQTP_F32); edge_order is ignored.  Errors as for

@@ -473,7 +473,6 @@ int eqtp_conv_backward(const eqtp_conv_desc* d, int64_t N, int64_t E, const floa
   const bool use_so2 = !radial && (d->lmax > 3 || d->algo == EQTP_ALGO_EDGE_SO2 ||
                                    (d->algo == EQTP_ALGO_AUTO && !vec_only));
   if (d->lmax > 3 && !use_so2) return EQTP_EUNSUPPORTED;
-  if (use_so2 && d->C == 128 && d->lmax > eqtp::kSo2MaxLC128) return EQTP_EUNSUPPORTED;
   if (radial) {
     if (!(d->r_cut > 0.0f)) return EQTP_EINVAL;
     if (d->n_basis != 8 || d->C % 16 != 0) return EQTP_EUNSUPPORTED;
@@ -538,7 +537,6 @@ int eqtp_conv_backward_by_source(const eqtp_conv_desc* d, int64_t N, int64_t E, 
   // fixed weights: the node-factored adjoint (lmax <= 3) unless the edge-aligned form is asked for or needed
   const bool use_so2 = !radial && (d->lmax > 3 || d->algo == EQTP_ALGO_EDGE_SO2);
   if (d->lmax > 3 && !use_so2) return EQTP_EUNSUPPORTED;
-  if (!radial && d->C == 128 && d->lmax > eqtp::kSo2MaxLC128 && (use_so2 || grad_vec)) return EQTP_EUNSUPPORTED;
   if (radial) {
     if (!(d->r_cut > 0.0f)) return EQTP_EINVAL;
     if (d->n_basis != 8 || d->C % 16 != 0) return EQTP_EUNSUPPORTED;

@@ -104,7 +104,10 @@ constexpr int kBwdSo2Threads = So2BwdCfg<L, PS, C>::THREADS;
 template <int L, int PS, int C>  // waves per SIMD that the LDS allows (the register budget follows)
 constexpr int kBwdSo2Occ = So2BwdCfg<L, PS, C>::WAVES * So2BwdCfg<L, PS, C>::PER_CU >= 8 ? 2 : 1;
 
-template <int L, int PS, int C>
+// CT: channels per node row of x, grad_out and grad_x and per path row of w and grad_w (C, or 128 when a
+// C = 128 problem runs as two 64-channel halves, the pointers then offset to the half's first channel);
+// GV_ADD: grad_vec adds to what the first half wrote instead of storing
+template <int L, int PS, int C, int CT = C, bool GV_ADD = false>
 __global__ __launch_bounds__((kBwdSo2Threads<L, PS, C>)) __attribute__((amdgpu_waves_per_eu(
     kBwdSo2Occ<L, PS, C>))) void conv_bwd_so2_kernel(
     int N, int E, long long ntasks, int mode, const int* __restrict__ row_ptr, const float* __restrict__ vec,
@@ -122,7 +125,7 @@ __global__ __launch_bounds__((kBwdSo2Threads<L, PS, C>)) __attribute__((amdgpu_w
   __shared__ float xch[Cfg::WAVES][kWave * NI];
   __shared__ int xsrc[Cfg::WAVES][Cfg::G];
   if constexpr (Cfg::WL_LDS)
-    for (int i = threadIdx.x; i < T::P * C; i += Cfg::THREADS) wl[i] = w[i];
+    for (int i = threadIdx.x; i < T::P * C; i += Cfg::THREADS) wl[i] = w[(i / C) * CT + i % C];
   for (int i = threadIdx.x; i < GWS; i += Cfg::THREADS) gws[i] = 0.0f;
   __syncthreads();
   const int lane = threadIdx.x & 63;
@@ -134,7 +137,7 @@ __global__ __launch_bounds__((kBwdSo2Threads<L, PS, C>)) __attribute__((amdgpu_w
   // path weight of channel c (LDS copy or through the caches)
   auto wld = [&](int p, int c) -> float {
     if constexpr (Cfg::WL_LDS) return wl[p * C + c];
-    else return w[p * C + c];
+    else return w[p * CT + c];
   };
   // grad_w sums of this lane's channels over all its edges: registers, or the wave's slots
   // [P][CPL][64] (slot of path p, channel c = cl + j CL at (p CPL + j) 64 + lane)
@@ -181,8 +184,8 @@ __global__ __launch_bounds__((kBwdSo2Threads<L, PS, C>)) __attribute__((amdgpu_w
         if constexpr (j > 0) __builtin_amdgcn_sched_barrier(0);  // one channel at a time
         const int c = cl + j * Cfg::CL;
         float xr[K], gr[K];
-        load_vec<K>(x + ((size_t)s * C + c) * K, xr);
-        load_vec<K>(gout + ((size_t)d * C + c) * K, gr);
+        load_vec<K>(x + ((size_t)s * CT + c) * K, xr);
+        load_vec<K>(gout + ((size_t)d * CT + c) * K, gr);
         so2_rotate_in<L, K>(xr, f);
         so2_rotate_in<L, K>(gr, f);
         // two walks of the sparse coupling (by path, then output component), so that at most three
@@ -280,9 +283,15 @@ __global__ __launch_bounds__((kBwdSo2Threads<L, PS, C>)) __attribute__((amdgpu_w
           float g0, g1, g2;
           frame_gradient<L>(f, gxe, gye, r2 > 0.0f ? rsqrtf(r2) : 0.0f, g0, g1, g2);
           float* gv = gvec + 3 * (by_src ? (size_t)clamp_index(perm[e], E) : (size_t)e);
-          gv[0] = g0;
-          gv[1] = g1;
-          gv[2] = g2;
+          if constexpr (GV_ADD) {
+            gv[0] += g0;
+            gv[1] += g1;
+            gv[2] += g2;
+          } else {
+            gv[0] = g0;
+            gv[1] = g1;
+            gv[2] = g2;
+          }
         }
       }
       if (gx != nullptr && !by_src) {
@@ -296,7 +305,7 @@ __global__ __launch_bounds__((kBwdSo2Threads<L, PS, C>)) __attribute__((amdgpu_w
         for (int i = 0; i < NI; ++i) {
           const int fi = kWave * i + ln;
           const int sr = xsrc[wv][fi / MSG];
-          if (sr >= 0) unsafeAtomicAdd(gx + (size_t)sr * MSG + fi % MSG, xw[fi]);
+          if (sr >= 0) unsafeAtomicAdd(gx + (size_t)sr * (CT * K) + fi % MSG, xw[fi]);
         }
         wave_lds_sync();
       }
@@ -309,7 +318,7 @@ __global__ __launch_bounds__((kBwdSo2Threads<L, PS, C>)) __attribute__((amdgpu_w
         float t = 0.0f;
 #pragma unroll
         for (int gg = 0; gg < Cfg::G; ++gg) t += xw[gg * MSG + f];
-        gx[(size_t)row * MSG + f] = t;
+        gx[(size_t)row * (CT * K) + f] = t;
       }
       wave_lds_sync();
     }
@@ -321,7 +330,7 @@ __global__ __launch_bounds__((kBwdSo2Threads<L, PS, C>)) __attribute__((amdgpu_w
 #pragma unroll
         for (int p = 0; p < T::P; ++p) atomicAdd(&gws[p * C + cl + j * Cfg::CL], gacc[j][p]);
       __syncthreads();
-      for (int i = threadIdx.x; i < T::P * C; i += Cfg::THREADS) unsafeAtomicAdd(gw + i, gws[i]);
+      for (int i = threadIdx.x; i < T::P * C; i += Cfg::THREADS) unsafeAtomicAdd(gw + (i / C) * CT + i % C, gws[i]);
     } else {
       __syncthreads();
       for (int i = threadIdx.x; i < T::P * C; i += Cfg::THREADS) {
@@ -330,29 +339,39 @@ __global__ __launch_bounds__((kBwdSo2Threads<L, PS, C>)) __attribute__((amdgpu_w
         for (int ww = 0; ww < Cfg::WAVES; ++ww)
           for (int gg = 0; gg < Cfg::G; ++gg)
             sum += gws[ww * T::P * kWave * Cfg::CPL + (p * Cfg::CPL + j) * kWave + gg * Cfg::CL + cc];
-        unsafeAtomicAdd(gw + i, sum);
+        unsafeAtomicAdd(gw + p * CT + c, sum);
       }
     }
   }
 }
 
-template <int L, int PS, int C>
-static hipError_t launch_bwd_so2_t(const BwdArgs& a) {
+// c0: the first channel this launch covers (rows CT channels wide; the zero fills cover every half and run
+// with the first)
+template <int L, int PS, int C, int CT = C>
+static hipError_t launch_bwd_so2_t(const BwdArgs& a, int c0 = 0) {
   using Cfg = So2BwdCfg<L, PS, C>;
   using T = So2Tables<L, PS>;
   constexpr int K = num_comp(L);
   hipError_t err;
-  // grouped by source every row's grad_x is written once (zeros without edges); else a sum of atomics
-  if (a.gx && !a.by_src && (err = launch_fill_zero(a.gx, a.N * C * K, a.stream)) != hipSuccess) return err;
-  if (a.gw && (err = launch_fill_zero(a.gw, (int64_t)T::P * C, a.stream)) != hipSuccess) return err;
+  if (c0 == 0) {
+    // grouped by source every row's grad_x is written once (zeros without edges); else a sum of atomics
+    if (a.gx && !a.by_src && (err = launch_fill_zero(a.gx, a.N * CT * K, a.stream)) != hipSuccess) return err;
+    if (a.gw && (err = launch_fill_zero(a.gw, (int64_t)T::P * CT, a.stream)) != hipSuccess) return err;
+  }
   const int mode = a.by_src ? 2 : a.row_ptr != nullptr ? 1 : 0;
   const long long ntasks = mode != 0 ? a.N : (a.E + Cfg::EPW - 1) / Cfg::EPW;
   if (ntasks == 0 || (a.E == 0 && !(a.by_src && a.gx))) return hipGetLastError();
   const int64_t want = (int64_t)num_cus() * Cfg::PER_CU;
   const int64_t need = (ntasks + Cfg::WAVES - 1) / Cfg::WAVES;
-  hipLaunchKernelGGL((conv_bwd_so2_kernel<L, PS, C>), dim3((unsigned)(need < want ? need : want)),
-                     dim3(Cfg::THREADS), 0, a.stream, (int)a.N, (int)a.E, ntasks, mode, a.row_ptr, a.vec, a.src,
-                     a.dst, a.perm, a.x, a.w, a.gout, a.gx, a.gw, a.gvec);
+  const size_t ko = (size_t)c0 * K;
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, dim3((unsigned)(need < want ? need : want)), dim3(Cfg::THREADS), 0, a.stream,
+                       (int)a.N, (int)a.E, ntasks, mode, a.row_ptr, a.vec, a.src, a.dst, a.perm,
+                       a.x ? a.x + ko : nullptr, a.w + c0, a.gout + ko, a.gx ? a.gx + ko : nullptr,
+                       a.gw ? a.gw + c0 : nullptr, a.gvec);
+  };
+  if (c0 == 0) go(conv_bwd_so2_kernel<L, PS, C, CT, false>);
+  else go(conv_bwd_so2_kernel<L, PS, C, CT, true>);
   return hipGetLastError();
 }
 
@@ -364,8 +383,13 @@ static hipError_t dispatch_bwd_so2_c(const BwdArgs& a) {
     case 32: return launch_bwd_so2_t<L, PS, 32>(a);
     case 64: return launch_bwd_so2_t<L, PS, 64>(a);
     case 128:
-      if constexpr (L <= kSo2MaxLC128) return launch_bwd_so2_t<L, PS, 128>(a);
-      return hipErrorInvalidValue;
+      if constexpr (L <= 2) {
+        return launch_bwd_so2_t<L, PS, 128>(a);
+      } else {  // two 64-channel halves: two channels per lane do not fit the registers above lmax 4, and from
+                // lmax 3 they hold one wave per SIMD where the halves keep two
+        const hipError_t err = launch_bwd_so2_t<L, PS, 64, 128>(a, 0);
+        return err != hipSuccess ? err : launch_bwd_so2_t<L, PS, 64, 128>(a, 64);
+      }
     default: return hipErrorInvalidValue;
   }
 }

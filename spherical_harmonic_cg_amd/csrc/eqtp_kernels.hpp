@@ -82,6 +82,7 @@ hipError_t launch_conv_backward_radial(const BwdArgs& a);  // radial weights, lm
 hipError_t launch_radial_mlp(int64_t E, const float* vec, float r_cut, const float* W1, const float* W2, float* phi,
                              float scale, hipStream_t stream);
 // edge-aligned (SO(2)) form, lmax 0..6, fixed fp32 weights; C = 128 above kSo2MaxLC128 as two 64-channel halves
+// (forward, messages and gradients)
 constexpr int kSo2MaxL = 6;
 constexpr int kSo2MaxLC128 = 4;
 hipError_t launch_conv_so2(const ConvArgs& a);

@@ -192,7 +192,7 @@ def test_conv_backward_validation():
     assert call(_desc(e, weight_mode=2)) == 1
     assert call(_desc(e, lmax=7)) == 2                                   # above lmax 6
     assert call(_desc(e, lmax=4, weight_mode=1, r_cut=5.0)) == 2         # radial weights: lmax 0..3
-    assert call(_desc(e, lmax=5, C=128)) == 2                            # gradients: C = 128 to lmax 4
+    assert call(_desc(e, lmax=5, C=128), x=NULL) == 1                    # C = 128 at lmax 5 (two halves) passes
     assert call(_desc(e, algo=7)) == 1                                   # unknown algorithm
     assert call(_desc(e, C=48)) == 2
     assert call(_desc(e, path_set=2)) == 1
@@ -324,7 +324,7 @@ def test_conv_backward_by_source_validation():
     assert call(_desc(e, weight_mode=1, r_cut=5.0, lmax=4)) == 2         # radial: lmax 0..3
     assert call(_desc(e, weight_mode=1, r_cut=5.0), x=NULL, gw=NULL) == 1  # the walk reads x
     assert call(_desc(e, lmax=7)) == 2                                   # above lmax 6
-    assert call(_desc(e, lmax=5, C=128)) == 2                            # gradients: C = 128 to lmax 4
+    assert call(_desc(e, lmax=5, C=128), x=NULL) == 1                    # C = 128 at lmax 5 (two halves) passes
     assert call(_desc(e, algo=7)) == 1                                   # unknown algorithm
     assert call(_desc(e, C=48)) == 2
     assert call(_desc(e, x_dtype=1)) == 2                                  # bf16 features

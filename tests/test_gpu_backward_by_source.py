@@ -81,8 +81,8 @@ def test_radial_by_source_small(lmax, ps, C):
              "radial by source L%d ps%d C%d" % (lmax, ps, C))
 
 
-@pytest.mark.parametrize("L,ps,C", [(4, 0, 32), (4, 1, 128), (5, 1, 16), (6, 0, 64), (6, 1, 8), (3, 0, 64),
-                                    (2, 1, 32), (0, 0, 16)])
+@pytest.mark.parametrize("L,ps,C", [(4, 0, 32), (4, 1, 128), (5, 1, 16), (6, 0, 64), (6, 1, 8), (5, 0, 128),
+                                    (6, 1, 128), (3, 0, 64), (2, 1, 32), (0, 0, 16)])
 def test_so2_by_source_small(L, ps, C):
     """Fixed weights in the edge-aligned form (lmax 4..6, and lmax <= 3 with EQTP_ALGO_EDGE_SO2)."""
     eq = _eq()

@@ -66,10 +66,7 @@ def test_so2_rejects_unsupported():
     import torch
 
     eq = _eq()
-    wl = _graph(5, 0, 128, 5)
     _say("so2 unsupported combinations")
-    with pytest.raises(eq.EqtpError):            # gradients: C = 128 only up to lmax 4
-        eq.eqtp_conv_backward(_t(wl.vec), _t(wl.src), _t(wl.x), _t(wl.w), _t(wl.x), 5, row_ptr=_t(wl.row_ptr))
     wl = _graph(4, 0, 32, 6)
     with pytest.raises(eq.EqtpError):
         _run(eq, wl, False, algo=1)              # lmax 4 has no node-factored form
