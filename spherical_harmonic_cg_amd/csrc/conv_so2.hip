@@ -602,9 +602,10 @@ static hipError_t dispatch_so2_c(const ConvArgs& a) {
     case 32: return launch_so2_t<L, PS, 32>(a);
     case 64: return launch_so2_t<L, PS, 64>(a);
     case 128:
-      if constexpr (L <= kSo2MaxLC128) {
+      if constexpr (L <= 3) {
         return launch_so2_t<L, PS, 128>(a);
-      } else {  // two 64-channel halves (two channels per lane do not fit the registers above lmax 4)
+      } else {  // two 64-channel halves: two channels per lane do not fit the registers above lmax 4, and at
+                // lmax 4 the halves are faster for dst-sorted edges and messages
         const hipError_t err = launch_so2_t<L, PS, 64, 128>(a, 0);
         return err != hipSuccess ? err : launch_so2_t<L, PS, 64, 128>(a, 64);
       }

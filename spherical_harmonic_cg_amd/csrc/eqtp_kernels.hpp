@@ -81,10 +81,9 @@ hipError_t launch_conv_backward_radial(const BwdArgs& a);  // radial weights, lm
 // the interaction layer's radial network: phi [E][4][16] (scaled by scale) from the edge lengths
 hipError_t launch_radial_mlp(int64_t E, const float* vec, float r_cut, const float* W1, const float* W2, float* phi,
                              float scale, hipStream_t stream);
-// edge-aligned (SO(2)) form, lmax 0..6, fixed fp32 weights; C = 128 above kSo2MaxLC128 as two 64-channel halves
-// (forward, messages and gradients)
+// edge-aligned (SO(2)) form, lmax 0..6, fixed fp32 weights, any C; C = 128 runs as two 64-channel halves from
+// lmax 4 (forward, messages) or lmax 3 (gradients)
 constexpr int kSo2MaxL = 6;
-constexpr int kSo2MaxLC128 = 4;
 hipError_t launch_conv_so2(const ConvArgs& a);
 // gradients in the edge-aligned form: fixed weights, lmax 0..6, any edge order (row_ptr or dst)
 hipError_t launch_conv_backward_so2(const BwdArgs& a);
